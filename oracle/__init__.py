@@ -1,0 +1,13 @@
+"""CPU oracle for the bitwise-deterministic MoE expert layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package's smoke check and
+the benchmark's CPU-baseline leg may import anything in this package.  The
+HIP library never calls it, and it shares no code, headers, tables or
+helpers with the HIP path; both sides only consume the same seeded inputs
+(package ``synth``).
+"""
+from .moe import (  # noqa: F401
+    decode, route, permute, expert_forward, expert_backward, forward, backward,
+    combine_rows, layer_loss,
+)
+from .fingerprint import fingerprint, mix64, DTYPE_CODE  # noqa: F401
