@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the bitwise-deterministic MoE grouped-GEMM backward on one
+MI355X.
+
+A step is one backward of the expert layer: moe_bwd_dgrad_dprob followed by
+moe_bwd_wgrad (fc2 dgrad with the dprob partial epilogue, the fixed-order
+dprob combine, fc1 dgrad, the fixed-order dx combine, both split-K weight
+gradients and their ordered reduction) on the default workload: 4096 tokens,
+d_model 1024, 8 experts, top-2, expert MLP 1024 -> 2048 -> 1024 with ReLU^2,
+bf16 storage, float32 accumulation and float32 dprob / dW.  The inputs are
+seeded synthetic tensors already resident in HBM, and routing and the saved h
+come from one untimed moe_fwd.
+
+Prints one JSON line.  ``value`` is 8*R*D*F / (time of one deterministic
+step), in TFLOP/s.  The determinism tax compares deterministic with atomic
+steps, which are interleaved step by step.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA, vendor figure
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="bf16_e8k2")
+    ap.add_argument("--stage-reps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="run warmup + timed steps only (for rocprofv3 runs)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import bitwise_deterministic_moe_amd as moe
+    from synth import CONFIGS, make_inputs
+
+    moe.load_library()
+    cfg = CONFIGS[args.config]
+    prob = moe.Problem.from_config(cfg)
+    host = make_inputs(cfg)
+    dev = "cuda"
+
+    def up(a, dt):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    logits = torch.from_numpy(host["logits"]).to(dev)
+    x, w1, w2, dy = (up(host[n], cfg.dtype) for n in ("x", "w1", "w2", "dy"))
+    routing, h, _ = moe.moe_fwd(prob, logits, x, w1, w2, moe.DETERMINISTIC)
+    torch.cuda.synchronize()
+    R = routing.rows
+    D, F, el = cfg.d_model, cfg.d_ffn, cfg.num_local
+    flops = 8.0 * R * D * F
+    gemm_flops = 2.0 * R * D * F
+    dt = moe.TORCH_DTYPE[cfg.dtype]
+    out_rows = cfg.tokens if cfg.combine else prob.rows_cap
+
+    class Bufs:
+        def __init__(self, mode):
+            self.mode = mode
+            self.dx = torch.empty((out_rows, D), dtype=dt, device=dev)
+            self.dprob = torch.empty((cfg.tokens, cfg.top_k), dtype=torch.float32, device=dev)
+            self.dh = torch.empty((prob.rows_cap, F), dtype=dt, device=dev)
+            self.dw1 = torch.empty((el, D, F), dtype=torch.float32, device=dev)
+            self.dw2 = torch.empty((el, F, D), dtype=torch.float32, device=dev)
+            sz = moe.moe_workspace_size(prob, mode)
+            self.ws1 = torch.empty(max(sz[1], 1), dtype=torch.uint8, device=dev)
+            self.ws2 = torch.empty(max(sz[2], 1), dtype=torch.uint8, device=dev)
+
+    def step(b, ev1=None, ev2=None):
+        moe.moe_bwd_dgrad_dprob(prob, routing, dy, w1, w2, h, b.mode, dx=b.dx, dprob=b.dprob, dh=b.dh,
+                                ws=b.ws1, events=ev1)
+        moe.moe_bwd_wgrad(prob, routing, x, dy, h, b.dh, b.mode, dw1=b.dw1, dw2=b.dw2, ws=b.ws2, events=ev2)
+
+    det, atom = Bufs(moe.DETERMINISTIC), Bufs(moe.ATOMIC)
+    for _ in range(args.warmup):
+        step(det)
+        step(atom)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K deterministic steps back to back
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    t0, t1 = E(), E()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step(det)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_det = t0.elapsed_time(t1) / args.steps
+    if args.profile_only:
+        print(json.dumps({"profile_only": True, "ms_per_step": ms_det}))
+        return
+
+    # ---- determinism tax: det and atomic steps interleaved, per-step events
+    td, ta = [], []
+    for _ in range(args.steps):
+        e = [E() for _ in range(3)]
+        e[0].record()
+        step(det)
+        e[1].record()
+        step(atom)
+        e[2].record()
+        torch.cuda.synchronize()
+        td.append(e[0].elapsed_time(e[1]))
+        ta.append(e[1].elapsed_time(e[2]))
+    med_d, med_a = statistics.median(td), statistics.median(ta)
+
+    def iqr(v):
+        q = statistics.quantiles(v, n=4)
+        return q[2] - q[0]
+
+    # ---- per-kernel times through the library's stage-event hook
+    def stage_times(mode, b):
+        names1 = moe.moe_stage_names(prob, mode, 1)
+        names2 = moe.moe_stage_names(prob, mode, 2)
+        acc = {}
+        for _ in range(args.stage_reps):
+            ev1 = [E() for _ in range(len(names1) + 1)]
+            ev2 = [E() for _ in range(len(names2) + 1)]
+            for e in ev1 + ev2:   # materialise the events before handing them to the library
+                e.record()
+            step(b, ev1, ev2)
+            torch.cuda.synchronize()
+            for names, ev in ((names1, ev1), (names2, ev2)):
+                for i, n in enumerate(names):
+                    acc.setdefault(n, []).append(ev[i].elapsed_time(ev[i + 1]))
+        return {n: statistics.mean(v) for n, v in acc.items()}
+
+    st_det = stage_times(moe.DETERMINISTIC, det)
+    st_atom = stage_times(moe.ATOMIC, atom)
+    gemm_stages = ("fc2_dgrad_dprob_partials", "fc1_dgrad", "wgrad_fc1", "wgrad_fc2")
+    dom = max(gemm_stages, key=lambda n: st_det[n])
+    dom_ms = st_det[dom]
+    achieved = gemm_flops / (dom_ms * 1e-3) / 1e12
+
+    value = flops / (ms_det * 1e-3) / 1e12
+    result = {
+        "metric": "MoE grouped-GEMM bwd TFLOP/s (det mode), % bf16 peak; determinism tax vs atomic",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_det, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.tokens} tokens, d_model {D}, {cfg.num_experts} experts top-{cfg.top_k}, "
+                               f"expert MLP {D}->{F}->{D} ReLU^2, {cfg.dtype} storage, fp32 dprob/dW",
+                   "tokens": cfg.tokens, "d_model": D, "d_ffn": F, "experts": cfg.num_experts,
+                   "top_k": cfg.top_k, "routed_rows": R, "mode": "deterministic", "parallelism": "single GPU"},
+        "pct_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
+        "determinism_tax": {
+            "tax": round(med_d / med_a - 1.0, 4),
+            "det_ms_median": round(med_d, 5), "det_ms_iqr": round(iqr(td), 5),
+            "atomic_ms_median": round(med_a, 5), "atomic_ms_iqr": round(iqr(ta), 5),
+            "interleaved_pairs": args.steps,
+        },
+        "stages_ms_det": {k: round(v, 5) for k, v in st_det.items()},
+        "stages_ms_atomic": {k: round(v, 5) for k, v in st_atom.items()},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": gemm_flops},
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, host, flops)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, host, gpu_flops):
+    """The oracle's backward (float64 numpy, as it stands) on the same inputs."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    import oracle
+    idx, p = oracle.route(host["logits"], cfg.top_k)
+    perm = oracle.permute(idx, cfg.expert_begin, cfg.num_local)
+    x, w1, w2, dy = (oracle.decode(host[n], cfg.dtype) for n in ("x", "w1", "w2", "dy"))
+    h = oracle.forward(x, w1, w2, p, perm, cfg.top_k, combine=bool(cfg.combine))["h"]
+    times = []
+    t_end = time.perf_counter() + 10.0
+    while len(times) < 3 and (not times or time.perf_counter() < t_end):
+        t = time.perf_counter()
+        oracle.backward(x, w1, w2, h, dy, p, perm, cfg.top_k, combine=bool(cfg.combine))
+        times.append(time.perf_counter() - t)
+    sec = statistics.median(times)
+    R = int(perm["offsets"][-1])
+    fl = 8.0 * R * cfg.d_model * cfg.d_ffn
+    return {"value": round(fl / sec / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"full float64 oracle backward of {cfg.name} (all {cfg.num_local} experts, {R} rows), "
+                      f"median of {len(times)} runs, {sec:.2f} s each",
+            "seconds_per_step": round(sec, 3)}
+
+
+if __name__ == "__main__":
+    main()

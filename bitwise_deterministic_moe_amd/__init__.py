@@ -1,0 +1,287 @@
+"""Python binding of libmoedet: the bitwise-deterministic MoE expert layer
+for MI355X (gfx950).
+
+Argument marshalling only.  Every step of the layer runs in the HIP kernels
+of ``libmoedet.so``; PyTorch supplies device memory and the current stream.
+The functions carry the names of the C ABI (include/moedet.h).  There is no
+fallback: a missing library raises ``MoeLibraryMissing``.
+"""
+import ctypes
+import os
+from dataclasses import dataclass, replace
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "DETERMINISTIC", "ATOMIC", "Problem", "Routing", "MoeError", "MoeLibraryMissing",
+    "load_library", "library_path", "moe_workspace_size", "moe_rows_cap", "moe_stage_names",
+    "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad", "moe_fingerprint", "EXPORTED_SYMBOLS",
+]
+
+DETERMINISTIC = 0
+ATOMIC = 1
+DTYPE_CODE = {"f32": 0, "bf16": 1, "i32": 2, "u8": 3, "i64": 4, "f64": 5}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+_TORCH_TO_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.int32: 2, torch.uint8: 3,
+                  torch.int64: 4, torch.float64: 5}
+EXPORTED_SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_rows_cap", "moe_workspace_size",
+                    "moe_stage_names", "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad",
+                    "moe_fingerprint")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+class MoeLibraryMissing(MoeError):
+    pass
+
+
+class _CProblem(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("d_model", ctypes.c_int32), ("d_ffn", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("expert_begin", ctypes.c_int32), ("num_local", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("combine", ctypes.c_int32),
+                ("debug_shuffle_seed", ctypes.c_uint64), ("stage_events", ctypes.c_void_p),
+                ("n_stage_events", ctypes.c_int32)]
+
+
+class _CRouting(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("topk_idx", "topk_prob", "counts", "offsets",
+                                                "row_src", "row_tok", "row_prob", "slot_row")]
+
+
+def library_path() -> str:
+    return os.environ.get("MOEDET_LIB", os.path.join(_HERE, "libmoedet.so"))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libmoedet.so (build it with ``python -m bitwise_deterministic_moe_amd.build``)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise MoeLibraryMissing(f"{path} not found; build it with python -m bitwise_deterministic_moe_amd.build")
+    lib = ctypes.CDLL(path)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    P = ctypes.POINTER(_CProblem)
+    R = ctypes.POINTER(_CRouting)
+    lib.moe_abi_version.restype = ctypes.c_int
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_rows_cap.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+    lib.moe_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(sz), ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.moe_stage_names.restype = ctypes.c_char_p
+    lib.moe_stage_names.argtypes = [P, ctypes.c_int, ctypes.c_int]
+    lib.moe_fwd.argtypes = [P, vp, vp, vp, vp, R, vp, vp, vp, sz, ctypes.c_int, vp]
+    lib.moe_bwd_dgrad_dprob.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
+    lib.moe_bwd_wgrad.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
+    lib.moe_fingerprint.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
+                                    vp, vp, vp]
+    for f in ("moe_rows_cap", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad",
+              "moe_fingerprint"):
+        getattr(lib, f).restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = load_library().moe_status_string(status).decode()
+        raise MoeError(f"{what}: status {status} ({msg})")
+
+
+@dataclass(frozen=True)
+class Problem:
+    """Mirror of ``moe_problem``."""
+    tokens: int
+    d_model: int
+    d_ffn: int
+    num_experts: int
+    top_k: int
+    expert_begin: int = 0
+    num_local: Optional[int] = None
+    dtype: str = "bf16"
+    combine: int = 1
+    shuffle_seed: int = 0
+
+    @property
+    def local(self) -> int:
+        return self.num_experts if self.num_local is None else self.num_local
+
+    @property
+    def rows_cap(self) -> int:
+        return self.tokens * min(self.top_k, self.local)
+
+    def with_seed(self, seed: int) -> "Problem":
+        return replace(self, shuffle_seed=seed)
+
+    def c(self, events=None) -> _CProblem:
+        p = _CProblem(self.tokens, self.d_model, self.d_ffn, self.num_experts, self.top_k,
+                      self.expert_begin, self.local, DTYPE_CODE[self.dtype], self.combine,
+                      self.shuffle_seed & 0xFFFFFFFFFFFFFFFF, None, 0)
+        if events:
+            arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+            p.stage_events = ctypes.cast(arr, ctypes.c_void_p)
+            p.n_stage_events = len(events)
+            p._keep = arr
+        return p
+
+    @classmethod
+    def from_config(cls, cfg, shuffle_seed: int = 0) -> "Problem":
+        return cls(cfg.tokens, cfg.d_model, cfg.d_ffn, cfg.num_experts, cfg.top_k, cfg.expert_begin,
+                   cfg.num_local, cfg.dtype, cfg.combine, shuffle_seed)
+
+
+@dataclass
+class Routing:
+    """Device routing state (mirror of ``moe_routing``)."""
+    topk_idx: torch.Tensor
+    topk_prob: torch.Tensor
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    row_src: torch.Tensor
+    row_tok: torch.Tensor
+    row_prob: torch.Tensor
+    slot_row: torch.Tensor
+
+    @classmethod
+    def empty(cls, prob: Problem, device="cuda") -> "Routing":
+        i32 = dict(dtype=torch.int32, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        T, k, el, rc = prob.tokens, prob.top_k, prob.local, prob.rows_cap
+        return cls(torch.empty((T, k), **i32), torch.empty((T, k), **f32), torch.empty(el, **i32),
+                   torch.empty(el + 1, **i32), torch.empty(rc, **i32), torch.empty(rc, **i32),
+                   torch.empty(rc, **f32), torch.empty(T * k, **i32))
+
+    def c(self) -> _CRouting:
+        return _CRouting(*[_ptr(getattr(self, n)) for n, _ in _CRouting._fields_])
+
+    @property
+    def rows(self) -> int:
+        """R (synchronises: reads offsets[-1] to the host)."""
+        return int(self.offsets[-1].item())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    return t.data_ptr() or None
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ws(nbytes: int, ws: Optional[torch.Tensor], device) -> torch.Tensor:
+    if ws is not None:
+        return ws
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def moe_rows_cap(prob: Problem) -> int:
+    v = ctypes.c_int64()
+    _check(load_library().moe_rows_cap(ctypes.byref(prob.c()), ctypes.byref(v)), "moe_rows_cap")
+    return v.value
+
+
+def moe_workspace_size(prob: Problem, mode: int = DETERMINISTIC):
+    """Bytes of workspace for (moe_fwd, moe_bwd_dgrad_dprob, moe_bwd_wgrad)."""
+    a, b, c = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load_library().moe_workspace_size(ctypes.byref(prob.c()), mode, ctypes.byref(a), ctypes.byref(b),
+                                             ctypes.byref(c)), "moe_workspace_size")
+    return a.value, b.value, c.value
+
+
+def moe_stage_names(prob: Problem, mode: int, call: int):
+    s = load_library().moe_stage_names(ctypes.byref(prob.c()), mode, call)
+    return s.decode().split(",") if s else None
+
+
+def moe_fwd(prob: Problem, logits, x, w1, w2, mode: int = DETERMINISTIC, routing: Routing = None,
+            h=None, y=None, ws=None, events=None):
+    """Routing + expert MLP + combine.  Returns (routing, h, y_or_rows)."""
+    lib = load_library()
+    dev = x.device
+    dt = TORCH_DTYPE[prob.dtype]
+    routing = routing or Routing.empty(prob, dev)
+    if h is None:
+        h = torch.empty((prob.rows_cap, prob.d_ffn), dtype=dt, device=dev)
+    if y is None:
+        y = torch.empty((prob.tokens if prob.combine else prob.rows_cap, prob.d_model), dtype=dt, device=dev)
+    need = moe_workspace_size(prob, mode)[0]
+    ws = _ws(need, ws, dev)
+    cp, cr = prob.c(events), routing.c()
+    _check(lib.moe_fwd(ctypes.byref(cp), _ptr(logits), _ptr(x), _ptr(w1), _ptr(w2), ctypes.byref(cr), _ptr(h),
+                       _ptr(y), _ptr(ws), ws.numel(), mode, _stream()), "moe_fwd")
+    return routing, h, y
+
+
+def moe_bwd_dgrad_dprob(prob: Problem, routing: Routing, dy, w1, w2, h, mode: int = DETERMINISTIC,
+                        dx=None, dprob=None, dh=None, ws=None, events=None):
+    """fc2 dgrad with dprob + fc1 dgrad + dx combine.  Returns (dx_or_rows, dprob, dh)."""
+    lib = load_library()
+    dev = h.device
+    dt = TORCH_DTYPE[prob.dtype]
+    if dx is None:
+        dx = torch.empty((prob.tokens if prob.combine else prob.rows_cap, prob.d_model), dtype=dt, device=dev)
+    if dprob is None:
+        dprob = torch.empty((prob.tokens, prob.top_k), dtype=torch.float32, device=dev)
+    if dh is None:
+        dh = torch.empty((prob.rows_cap, prob.d_ffn), dtype=dt, device=dev)
+    need = moe_workspace_size(prob, mode)[1]
+    ws = _ws(need, ws, dev)
+    cp, cr = prob.c(events), routing.c()
+    _check(lib.moe_bwd_dgrad_dprob(ctypes.byref(cp), ctypes.byref(cr), _ptr(dy), _ptr(w1), _ptr(w2), _ptr(h),
+                                   _ptr(dx), _ptr(dprob), _ptr(dh), _ptr(ws), ws.numel(), mode, _stream()),
+           "moe_bwd_dgrad_dprob")
+    return dx, dprob, dh
+
+
+def moe_bwd_wgrad(prob: Problem, routing: Routing, x, dy, h, dh, mode: int = DETERMINISTIC, dw1=None, dw2=None,
+                  ws=None, events=None):
+    """Expert weight gradients (float32).  Returns (dw1, dw2)."""
+    lib = load_library()
+    dev = h.device
+    el, D, F = prob.local, prob.d_model, prob.d_ffn
+    if dw1 is None:
+        dw1 = torch.empty((el, D, F), dtype=torch.float32, device=dev)
+    if dw2 is None:
+        dw2 = torch.empty((el, F, D), dtype=torch.float32, device=dev)
+    need = moe_workspace_size(prob, mode)[2]
+    ws = _ws(need, ws, dev)
+    cp, cr = prob.c(events), routing.c()
+    _check(lib.moe_bwd_wgrad(ctypes.byref(cp), ctypes.byref(cr), _ptr(x), _ptr(dy), _ptr(h), _ptr(dh), _ptr(dw1),
+                             _ptr(dw2), _ptr(ws), ws.numel(), mode, _stream()), "moe_bwd_wgrad")
+    return dw1, dw2
+
+
+def moe_fingerprint(t: torch.Tensor, dtype: Optional[str] = None, chunk_elems: int = 65536,
+                    shape=None, sync: bool = True):
+    """Chunk hashes (device uint64 as int64 tensor) and the total.
+
+    ``dtype`` names the element type ("f32", "bf16", "i32", ...); by default
+    it follows the tensor.  With ``sync`` the 8-byte total is copied to the
+    host and returned as a Python int; otherwise the device tensor."""
+    lib = load_library()
+    if not t.is_contiguous():
+        raise MoeError("fingerprint needs a contiguous tensor")
+    code = DTYPE_CODE[dtype] if dtype else _TORCH_TO_CODE[t.dtype]
+    shape = tuple(t.shape) if shape is None else tuple(shape)
+    n = 1
+    for s in shape:
+        n *= s
+    m = (n + chunk_elems - 1) // chunk_elems
+    hashes = torch.empty(max(m, 1), dtype=torch.int64, device=t.device)
+    total = torch.empty(1, dtype=torch.int64, device=t.device)
+    arr = (ctypes.c_int64 * max(len(shape), 1))(*shape)
+    _check(lib.moe_fingerprint(_ptr(t), code, len(shape), arr, chunk_elems, _ptr(hashes), _ptr(total), _stream()),
+           "moe_fingerprint")
+    if not sync:
+        return hashes[:m], total
+    return hashes[:m], int(total.item()) & 0xFFFFFFFFFFFFFFFF

@@ -1,0 +1,148 @@
+// Device helpers shared by the gfx950 kernels of libmoedet.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define DEV __device__ __forceinline__
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+namespace moedet {
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator dies, workgroups dealt round-robin
+
+// ------------------------------------------------------------------ bf16
+DEV float bf16_to_f32(uint32_t u16) { return __uint_as_float(u16 << 16); }
+
+// float32 -> bf16, round to nearest even (NaN kept quiet).
+DEV uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+DEV uint32_t pack_bf16x2(float lo, float hi) { return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16); }
+
+DEV float relu(float v) { return v > 0.f ? v : 0.f; }
+
+// ------------------------------------------------------------------ hashing
+// SplitMix64 output finalizer (Steele, Lea, Flood 2014).
+DEV uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+
+// ------------------------------------------------------- work-unit mapping
+DEV uint64_t gcd_u64(uint64_t a, uint64_t b) {
+  while (b) {
+    uint64_t t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+// Test-only launch-order perturbation: a seeded affine bijection of [0, U)
+// plus a seeded delay for some workgroups.
+DEV int64_t shuffle_unit(int64_t L, int64_t U, uint64_t seed) {
+  uint64_t h = mix64(seed);
+  uint64_t a = (h % (uint64_t)U) | 1ull;
+  while (gcd_u64(a, (uint64_t)U) != 1ull) a += 2;
+  uint64_t c = mix64(h ^ kGamma) % (uint64_t)U;
+  return (int64_t)((a * (uint64_t)L + c) % (uint64_t)U);
+}
+
+DEV void shuffle_delay(uint64_t seed, int64_t b) {
+  uint64_t h = mix64(seed ^ ((uint64_t)b * kGamma));
+  if ((h & 3u) == 0) {
+    int n = (int)((h >> 8) & 15u);
+    for (int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(32);
+  }
+}
+
+// Maps the physical workgroup index b to a logical work unit in [0, U), or
+// -1 when this workgroup has no unit.  Workgroups are dealt round-robin to
+// the 8 XCDs, so unit ranges are laid out per XCD: XCD x takes the
+// consecutive units [x*per, (x+1)*per), which keeps units that share
+// operands in one L2.  With a nonzero seed the units are permuted instead.
+DEV int64_t map_unit(int64_t b, int64_t U, uint64_t seed) {
+  if (U <= 0) return -1;
+  const int64_t per = (U + kNumXcd - 1) / kNumXcd;
+  const int64_t x = b % kNumXcd, q = b / kNumXcd;
+  if (q >= per) return -1;
+  int64_t L = x * per + q;
+  if (L >= U) return -1;
+  if (seed) {
+    shuffle_delay(seed, b);
+    L = shuffle_unit(L, U, seed);
+  }
+  return L;
+}
+
+// ------------------------------------------------------------ block scans
+// Exclusive prefix over G values computed by val(g), written to s_pre[0..G]
+// (s_pre[G] = total).  All NT threads of the block must call it; ends with a
+// barrier.  Integer arithmetic: exact and order-independent.
+template <int NT, class F>
+DEV void block_exclusive_scan(int* s_pre, int* s_tmp, int G, F val) {
+  const int tid = threadIdx.x;
+  const int per = (G + NT - 1) / NT;
+  const int g0 = tid * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i) {
+    int g = g0 + i;
+    if (g < G) local += val(g);
+  }
+  // wave inclusive scan of per-thread sums
+  const int lane = tid & (kWave - 1), w = tid / kWave;
+  int incl = local;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int o = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += o;
+  }
+  if (lane == kWave - 1) s_tmp[w] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int i = 0; i < w; ++i) wbase += s_tmp[i];
+  int run = wbase + incl - local;
+  for (int i = 0; i < per; ++i) {
+    int g = g0 + i;
+    if (g < G) {
+      s_pre[g] = run;
+      run += val(g);
+    }
+  }
+  if (tid == NT - 1) {
+    int tot = 0;
+    for (int i = 0; i < NT / kWave; ++i) tot += s_tmp[i];
+    s_pre[G] = tot;
+  }
+  __syncthreads();
+}
+
+// Largest g in [0, G) with pre[g] <= L (pre non-decreasing, pre[0] = 0,
+// L < pre[G]); skips empty groups.
+DEV int find_group(const int* pre, int G, int64_t L) {
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= L)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace moedet

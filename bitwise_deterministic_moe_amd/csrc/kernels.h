@@ -1,0 +1,124 @@
+// Internal kernel parameter blocks and host-side launchers of libmoedet.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moedet {
+
+constexpr int kMaxExperts = 1024;     // router width handled by the routing kernels
+constexpr int kMaxTopK = 64;          // one lane per selected expert
+constexpr int kRouteChunk = 64;       // tokens per routing/permutation chunk
+constexpr int kMaxChunkRows = 2048;   // upper bound on the wgrad K chunk (rows)
+
+// Grid size (a multiple of the 8 XCDs) for an upper bound on work units.
+inline int64_t grid_for_units(int64_t U_max) { return ((U_max + 7) / 8) * 8; }
+
+enum { kEpiStore = 0, kEpiDgrad2 = 1 };
+enum { kGemmFc1Fwd = 0, kGemmFc2Fwd = 1, kGemmFc2Dgrad = 2, kGemmFc1Dgrad = 3 };
+
+struct RowGemmParams {
+  const int32_t* counts;
+  const int32_t* offsets;
+  int groups;
+  int N, K;
+  const void* a;
+  int64_t lda;
+  const int32_t* a_rows;  // A row r reads a[a_rows[r]] when set, a[r] otherwise
+  const void* b;
+  int64_t b_gstride;
+  int64_t ldb;
+  void* c;
+  int64_t ldc;
+  // fc2 dgrad epilogue
+  const void* h;
+  int64_t ldh;
+  const float* row_prob;
+  const int32_t* row_src;
+  float* part;  // [rows_cap][n_tiles]
+  int n_tiles;
+  float* dprob;
+  int atomic;
+  uint64_t seed;
+};
+
+struct WgradParams {
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* row_tok;
+  const float* row_prob;
+  const int32_t* sched;  // unit_start[G+1], slot_base[G+1]
+  int groups;
+  int M, N;
+  const void* a;
+  int64_t lda;
+  const void* b;
+  int64_t ldb;
+  float* dw;
+  float* slots;
+  int kc;
+  int atomic;
+  uint64_t seed;
+};
+
+struct WgradPrepParams {
+  const int32_t* counts;
+  int32_t* sched;
+  int groups;
+  int M, N;
+  int kc;
+  int atomic;
+  float* dw1;
+  float* dw2;
+  const float* slots1;
+  const float* slots2;
+};
+
+struct RouteParams {
+  const float* logits;
+  int64_t T;
+  int E, k, eb, el;
+  int32_t* topk_idx;
+  float* topk_prob;
+  int32_t* hist;  // [nchunk][el]
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* cursor;  // [el] (atomic mode)
+  int32_t* row_src;
+  int32_t* row_tok;
+  float* row_prob;
+  int32_t* slot_row;
+  int nchunk;
+  int atomic;
+  uint64_t seed;
+};
+
+hipError_t launch_route(const RouteParams& P, hipStream_t st);
+hipError_t launch_permute_scan(const RouteParams& P, hipStream_t st);
+hipError_t launch_permute_scatter(const RouteParams& P, hipStream_t st);
+
+hipError_t launch_rowgemm(const RowGemmParams& P, int kind, bool bf16, int64_t grid, hipStream_t st);
+hipError_t launch_wgrad(const WgradParams& P, int which, bool bf16, int64_t grid, hipStream_t st);
+hipError_t launch_wgrad_prep(const WgradPrepParams& P, int64_t grid, hipStream_t st);
+hipError_t launch_wgrad_reduce(const WgradPrepParams& P, int64_t grid, hipStream_t st);
+int gemm_tile_m(bool bf16);
+int gemm_tile_n(bool bf16);
+
+// combine / dprob kernels
+hipError_t launch_gather_combine(const void* rows, const int32_t* slot_row, const float* weights,
+                                 int64_t T, int k, int D, void* out, bool bf16, uint64_t seed,
+                                 hipStream_t st);
+hipError_t launch_scatter_add(const void* rows, const int32_t* offsets, int el,
+                              const int32_t* row_tok, const float* row_prob, int64_t rows_cap, int D,
+                              float* out32, bool bf16, uint64_t seed, hipStream_t st);
+hipError_t launch_cast(const float* in32, void* out, int64_t n, bool bf16, hipStream_t st);
+hipError_t launch_zero(float* p, int64_t n, hipStream_t st);
+hipError_t launch_dprob_combine(const float* part, const int32_t* slot_row, int64_t nslots, int n_tiles,
+                                float* dprob, uint64_t seed, hipStream_t st);
+
+// fingerprint
+hipError_t launch_fingerprint(const void* data, int width, int64_t n, int64_t chunk,
+                              const uint64_t* words, int nwords, uint64_t* chunk_hashes,
+                              uint64_t* total, hipStream_t st);
+
+}  // namespace moedet

@@ -1,0 +1,543 @@
+// Host side of libmoedet: argument validation, workspace planning and the
+// launch sequence of each C-ABI call (declared in include/moedet.h).
+//
+// Work decompositions that depend on routing (rows per expert, split-K
+// chunks) are derived on the device from counts[]; the host sizes grids and
+// workspaces from shape upper bounds only, so nothing here waits for the GPU.
+#include <string.h>
+
+#include "../../include/moedet.h"
+#include "kernels.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace moedet {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  bool bf16;
+  int64_t T;
+  int D, F, E, k, eb, el;
+  int64_t rows_cap;
+  int64_t nslot;      // T*k
+  int nchunk;         // routing chunks
+  int bm, bn;         // GEMM tile
+  int n_tiles;        // fc2-dgrad N-tiles (dprob partials per row)
+  int kc;             // wgrad K chunk (rows)
+  int64_t wslots;     // wgrad partial slots per dW
+  size_t esize;
+};
+
+moe_status validate(const moe_problem* p, Plan* pl) {
+  if (!p) return MOE_ERR_NULL;
+  if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (p->combine != 0 && p->combine != 1) return MOE_ERR_MODE;
+  if (p->tokens < 0 || p->tokens >= (int64_t)1 << 31) return MOE_ERR_SHAPE;
+  if (p->num_experts < 1 || p->num_experts > kMaxExperts) return MOE_ERR_SHAPE;
+  if (p->top_k < 1 || p->top_k > p->num_experts || p->top_k > kMaxTopK) return MOE_ERR_SHAPE;
+  if (p->expert_begin < 0 || p->num_local < 1 || p->expert_begin + p->num_local > p->num_experts)
+    return MOE_ERR_SHAPE;
+  if (p->combine == 1 && (p->expert_begin != 0 || p->num_local != p->num_experts)) return MOE_ERR_SHAPE;
+  if (p->tokens * p->top_k >= (int64_t)1 << 31) return MOE_ERR_SHAPE;
+  const bool bf16 = p->dtype == MOE_BF16;
+  const int bm = gemm_tile_m(bf16), bn = gemm_tile_n(bf16);
+  const int align = bf16 ? 256 : 64;
+  if (p->d_model <= 0 || p->d_ffn <= 0 || p->d_model % align || p->d_ffn % align) return MOE_ERR_SHAPE;
+  if (p->d_ffn / bn > 64) return MOE_ERR_SHAPE;  // dprob partials per row
+  if ((int64_t)p->d_model * p->d_ffn >= (int64_t)1 << 31) return MOE_ERR_SHAPE;
+  if (p->n_stage_events < 0 || (p->n_stage_events > 0 && !p->stage_events)) return MOE_ERR_NULL;
+  if (pl) {
+    pl->bf16 = bf16;
+    pl->T = p->tokens;
+    pl->D = p->d_model;
+    pl->F = p->d_ffn;
+    pl->E = p->num_experts;
+    pl->k = p->top_k;
+    pl->eb = p->expert_begin;
+    pl->el = p->num_local;
+    pl->rows_cap = p->tokens * (int64_t)(p->top_k < p->num_local ? p->top_k : p->num_local);
+    pl->nslot = p->tokens * (int64_t)p->top_k;
+    pl->nchunk = (int)((p->tokens + kRouteChunk - 1) / kRouteChunk);
+    pl->bm = bm;
+    pl->bn = bn;
+    pl->n_tiles = p->d_ffn / bn;
+    // wgrad K chunk: twice the mean rows per expert of the whole layer,
+    // rounded up to 256, clamped to [512, 2048]; a pure function of shapes.
+    const double mean = (double)p->tokens * p->top_k / p->num_experts;
+    int64_t kc = 256 * (int64_t)((2.0 * mean + 255.0) / 256.0);
+    if (kc < 512) kc = 512;
+    if (kc > kMaxChunkRows) kc = kMaxChunkRows;
+    pl->kc = (int)kc;
+    pl->wslots = pl->rows_cap / kc;
+    pl->esize = bf16 ? 2 : 4;
+  }
+  return MOE_OK;
+}
+
+// Workspace layout of each call: a list of aligned regions.
+struct FwdWs {
+  size_t hist, cursor, orows, y32, total;
+};
+struct DgradWs {
+  size_t part, dxrows, dx32, total;
+};
+struct WgradWs {
+  size_t sched, slots1, slots2, total;
+};
+
+FwdWs fwd_layout(const Plan& pl, int combine, bool atomic) {
+  FwdWs w{};
+  size_t o = 0;
+  w.hist = o;
+  o += align_up((size_t)pl.nchunk * pl.el * 4);
+  w.cursor = o;
+  o += align_up((size_t)pl.el * 4);
+  w.orows = o;
+  if (combine) o += align_up((size_t)pl.rows_cap * pl.D * pl.esize);
+  w.y32 = o;
+  if (combine && atomic) o += align_up((size_t)pl.T * pl.D * 4);
+  w.total = o;
+  return w;
+}
+
+DgradWs dgrad_layout(const Plan& pl, int combine, bool atomic) {
+  DgradWs w{};
+  size_t o = 0;
+  w.part = o;
+  if (!atomic) o += align_up((size_t)pl.rows_cap * pl.n_tiles * 4);
+  w.dxrows = o;
+  if (combine) o += align_up((size_t)pl.rows_cap * pl.D * pl.esize);
+  w.dx32 = o;
+  if (combine && atomic) o += align_up((size_t)pl.T * pl.D * 4);
+  w.total = o;
+  return w;
+}
+
+WgradWs wgrad_layout(const Plan& pl, bool atomic) {
+  WgradWs w{};
+  size_t o = 0;
+  w.sched = o;
+  o += align_up((size_t)2 * (pl.el + 1) * 4);
+  const size_t slot_bytes = align_up((size_t)pl.wslots * pl.D * pl.F * 4);
+  w.slots1 = o;
+  if (!atomic) o += slot_bytes;
+  w.slots2 = o;
+  if (!atomic) o += slot_bytes;
+  w.total = o;
+  return w;
+}
+
+moe_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (need > 0 && (!ws || ((uintptr_t)ws % kAlign))) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+// Records the caller's stage events around each kernel of a call.
+struct Stager {
+  const moe_problem* p;
+  hipStream_t st;
+  int i = 0;
+  hipError_t err = hipSuccess;
+  void mark() {
+    if (p->stage_events && i < p->n_stage_events) {
+      hipError_t e = hipEventRecord((hipEvent_t)p->stage_events[i], st);
+      if (e != hipSuccess && err == hipSuccess) err = e;
+    }
+    ++i;
+  }
+};
+
+int64_t rowgemm_grid(const Plan& pl, int N) {
+  const int64_t mtiles = (pl.rows_cap + pl.bm - 1) / pl.bm + pl.el;
+  return grid_for_units(mtiles * (N / pl.bn));
+}
+
+int64_t wgrad_grid(const Plan& pl, int M, int N) {
+  const int64_t units = (int64_t)(pl.el + pl.wslots) * (M / pl.bm) * (N / pl.bn);
+  return grid_for_units(units);
+}
+
+#define HIP_TRY(expr)                          \
+  do {                                         \
+    hipError_t e_ = (expr);                    \
+    if (e_ != hipSuccess) return MOE_ERR_HIP;  \
+  } while (0)
+
+}  // namespace
+}  // namespace moedet
+
+using namespace moedet;
+
+MOE_API int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+MOE_API const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "null pointer argument";
+    case MOE_ERR_SHAPE: return "invalid shape, alignment or expert range";
+    case MOE_ERR_DTYPE: return "unsupported dtype";
+    case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MOE_ERR_MODE: return "invalid mode or combine flag";
+    case MOE_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+MOE_API moe_status moe_rows_cap(const moe_problem* p, int64_t* rows_cap) {
+  Plan pl;
+  moe_status s = validate(p, &pl);
+  if (s != MOE_OK) return s;
+  if (!rows_cap) return MOE_ERR_NULL;
+  *rows_cap = pl.rows_cap;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_workspace_size(const moe_problem* p, moe_mode mode, size_t* fwd_bytes,
+                                      size_t* dgrad_bytes, size_t* wgrad_bytes) {
+  Plan pl;
+  moe_status s = validate(p, &pl);
+  if (s != MOE_OK) return s;
+  if (mode != MOE_DETERMINISTIC && mode != MOE_ATOMIC) return MOE_ERR_MODE;
+  const bool at = mode == MOE_ATOMIC;
+  if (fwd_bytes) *fwd_bytes = fwd_layout(pl, p->combine, at).total;
+  if (dgrad_bytes) *dgrad_bytes = dgrad_layout(pl, p->combine, at).total;
+  if (wgrad_bytes) *wgrad_bytes = wgrad_layout(pl, at).total;
+  return MOE_OK;
+}
+
+MOE_API const char* moe_stage_names(const moe_problem* p, moe_mode mode, int call) {
+  if (validate(p, nullptr) != MOE_OK) return nullptr;
+  const bool at = mode == MOE_ATOMIC;
+  const bool cb = p->combine == 1;
+  switch (call) {
+    case 0:
+      if (!at) return cb ? "route,permute_scan,permute_scatter,fc1_fwd,fc2_fwd,combine_gather"
+                         : "route,permute_scan,permute_scatter,fc1_fwd,fc2_fwd";
+      return cb ? "route,permute_scan,permute_scatter_atomic,fc1_fwd,fc2_fwd,zero,combine_scatter,cast"
+                : "route,permute_scan,permute_scatter_atomic,fc1_fwd,fc2_fwd";
+    case 1:
+      if (!at) return cb ? "fc2_dgrad_dprob_partials,dprob_combine,fc1_dgrad,dx_combine_gather"
+                         : "fc2_dgrad_dprob_partials,dprob_combine,fc1_dgrad";
+      return cb ? "zero,fc2_dgrad_dprob_atomic,fc1_dgrad,dx_combine_scatter,cast"
+                : "zero,fc2_dgrad_dprob_atomic,fc1_dgrad";
+    case 2:
+      return at ? "wgrad_prep_zero,wgrad_fc1,wgrad_fc2" : "wgrad_prep,wgrad_fc1,wgrad_fc2,wgrad_reduce";
+  }
+  return nullptr;
+}
+
+MOE_API moe_status moe_fwd(const moe_problem* p, const float* logits, const void* x, const void* w1,
+                           const void* w2, const moe_routing* routing, void* h, void* y_or_rows,
+                           void* ws, size_t ws_bytes, moe_mode mode, void* stream) {
+  Plan pl;
+  moe_status s = validate(p, &pl);
+  if (s != MOE_OK) return s;
+  if (mode != MOE_DETERMINISTIC && mode != MOE_ATOMIC) return MOE_ERR_MODE;
+  const bool at = mode == MOE_ATOMIC;
+  const bool has_tok = pl.T > 0, has_rows = pl.rows_cap > 0;
+  if (!routing || !w1 || !w2 || !routing->counts || !routing->offsets) return MOE_ERR_NULL;
+  if (has_tok && (!logits || !x || !y_or_rows || !routing->topk_idx || !routing->topk_prob ||
+                  !routing->slot_row))
+    return MOE_ERR_NULL;
+  if (has_rows && (!h || !routing->row_src || !routing->row_tok || !routing->row_prob)) return MOE_ERR_NULL;
+  const FwdWs L = fwd_layout(pl, p->combine, at);
+  s = check_ws(ws, ws_bytes, L.total);
+  if (s != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  const uint64_t seed = p->debug_shuffle_seed;
+  Stager sg{p, st};
+
+  RouteParams R{};
+  R.logits = logits;
+  R.T = pl.T;
+  R.E = pl.E;
+  R.k = pl.k;
+  R.eb = pl.eb;
+  R.el = pl.el;
+  R.topk_idx = routing->topk_idx;
+  R.topk_prob = routing->topk_prob;
+  R.hist = (int32_t*)(wsb + L.hist);
+  R.counts = routing->counts;
+  R.offsets = routing->offsets;
+  R.cursor = (int32_t*)(wsb + L.cursor);
+  R.row_src = routing->row_src;
+  R.row_tok = routing->row_tok;
+  R.row_prob = routing->row_prob;
+  R.slot_row = routing->slot_row;
+  R.nchunk = pl.nchunk;
+  R.atomic = at;
+  R.seed = seed;
+  sg.mark();
+  HIP_TRY(launch_route(R, st));
+  sg.mark();
+  HIP_TRY(launch_permute_scan(R, st));
+  sg.mark();
+  HIP_TRY(launch_permute_scatter(R, st));
+
+  void* orows = p->combine ? (void*)(wsb + L.orows) : y_or_rows;
+  RowGemmParams G{};
+  G.counts = routing->counts;
+  G.offsets = routing->offsets;
+  G.groups = pl.el;
+  G.seed = seed;
+  // fc1: h = x[row_tok] W1_g, W1 [D][F]
+  G.N = pl.F;
+  G.K = pl.D;
+  G.a = x;
+  G.lda = pl.D;
+  G.a_rows = routing->row_tok;
+  G.b = w1;
+  G.b_gstride = (int64_t)pl.D * pl.F;
+  G.ldb = pl.F;
+  G.c = h;
+  G.ldc = pl.F;
+  sg.mark();
+  HIP_TRY(launch_rowgemm(G, kGemmFc1Fwd, pl.bf16, rowgemm_grid(pl, pl.F), st));
+  // fc2: o = relu(h)^2 W2_g, W2 [F][D]
+  G.N = pl.D;
+  G.K = pl.F;
+  G.a = h;
+  G.lda = pl.F;
+  G.a_rows = nullptr;
+  G.b = w2;
+  G.b_gstride = (int64_t)pl.F * pl.D;
+  G.ldb = pl.D;
+  G.c = orows;
+  G.ldc = pl.D;
+  sg.mark();
+  HIP_TRY(launch_rowgemm(G, kGemmFc2Fwd, pl.bf16, rowgemm_grid(pl, pl.D), st));
+
+  if (p->combine) {
+    if (!at) {
+      sg.mark();
+      HIP_TRY(launch_gather_combine(orows, routing->slot_row, routing->topk_prob, pl.T, pl.k, pl.D, y_or_rows,
+                                    pl.bf16, seed, st));
+    } else {
+      float* y32 = (float*)(wsb + L.y32);
+      sg.mark();
+      HIP_TRY(launch_zero(y32, pl.T * pl.D, st));
+      sg.mark();
+      HIP_TRY(launch_scatter_add(orows, routing->offsets, pl.el, routing->row_tok, routing->row_prob, pl.rows_cap,
+                                 pl.D, y32, pl.bf16, seed, st));
+      sg.mark();
+      HIP_TRY(launch_cast(y32, y_or_rows, pl.T * pl.D, pl.bf16, st));
+    }
+  }
+  sg.mark();
+  return sg.err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* routing, const void* dy,
+                                       const void* w1, const void* w2, const void* h, void* dx_or_rows,
+                                       float* dprob, void* dh, void* ws, size_t ws_bytes, moe_mode mode,
+                                       void* stream) {
+  Plan pl;
+  moe_status s = validate(p, &pl);
+  if (s != MOE_OK) return s;
+  if (mode != MOE_DETERMINISTIC && mode != MOE_ATOMIC) return MOE_ERR_MODE;
+  const bool at = mode == MOE_ATOMIC;
+  const bool has_tok = pl.T > 0, has_rows = pl.rows_cap > 0;
+  if (!routing || !w1 || !w2 || !routing->counts || !routing->offsets) return MOE_ERR_NULL;
+  if (has_tok && (!dy || !dx_or_rows || !dprob || !routing->slot_row || !routing->topk_prob)) return MOE_ERR_NULL;
+  if (has_rows && (!h || !dh || !routing->row_src || !routing->row_tok || !routing->row_prob)) return MOE_ERR_NULL;
+  const DgradWs L = dgrad_layout(pl, p->combine, at);
+  s = check_ws(ws, ws_bytes, L.total);
+  if (s != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  const uint64_t seed = p->debug_shuffle_seed;
+  Stager sg{p, st};
+  float* part = (float*)(wsb + L.part);
+  float* dx32 = (float*)(wsb + L.dx32);
+  void* dxrows = p->combine ? (void*)(wsb + L.dxrows) : dx_or_rows;
+
+  if (at) {
+    sg.mark();
+    HIP_TRY(launch_zero(dprob, pl.nslot, st));
+    if (p->combine) HIP_TRY(launch_zero(dx32, pl.T * pl.D, st));
+  }
+  RowGemmParams G{};
+  G.counts = routing->counts;
+  G.offsets = routing->offsets;
+  G.groups = pl.el;
+  G.seed = seed;
+  // fc2 dgrad: G = dy[row_tok] W2_g^T; W2 [F][D] read as [N=F][K=D].
+  G.N = pl.F;
+  G.K = pl.D;
+  G.a = dy;
+  G.lda = pl.D;
+  G.a_rows = routing->row_tok;
+  G.b = w2;
+  G.b_gstride = (int64_t)pl.F * pl.D;
+  G.ldb = pl.D;
+  G.c = dh;
+  G.ldc = pl.F;
+  G.h = h;
+  G.ldh = pl.F;
+  G.row_prob = routing->row_prob;
+  G.row_src = routing->row_src;
+  G.part = part;
+  G.n_tiles = pl.n_tiles;
+  G.dprob = dprob;
+  G.atomic = at;
+  sg.mark();
+  HIP_TRY(launch_rowgemm(G, kGemmFc2Dgrad, pl.bf16, rowgemm_grid(pl, pl.F), st));
+  if (!at) {
+    sg.mark();
+    HIP_TRY(launch_dprob_combine(part, routing->slot_row, pl.nslot, pl.n_tiles, dprob, seed, st));
+  }
+  // fc1 dgrad: dx_rows = dh W1_g^T; W1 [D][F] read as [N=D][K=F].
+  RowGemmParams G2{};
+  G2.counts = routing->counts;
+  G2.offsets = routing->offsets;
+  G2.groups = pl.el;
+  G2.seed = seed;
+  G2.N = pl.D;
+  G2.K = pl.F;
+  G2.a = dh;
+  G2.lda = pl.F;
+  G2.a_rows = nullptr;
+  G2.b = w1;
+  G2.b_gstride = (int64_t)pl.D * pl.F;
+  G2.ldb = pl.F;
+  G2.c = dxrows;
+  G2.ldc = pl.D;
+  sg.mark();
+  HIP_TRY(launch_rowgemm(G2, kGemmFc1Dgrad, pl.bf16, rowgemm_grid(pl, pl.D), st));
+  if (p->combine) {
+    if (!at) {
+      sg.mark();
+      HIP_TRY(launch_gather_combine(dxrows, routing->slot_row, nullptr, pl.T, pl.k, pl.D, dx_or_rows, pl.bf16,
+                                    seed, st));
+    } else {
+      sg.mark();
+      HIP_TRY(launch_scatter_add(dxrows, routing->offsets, pl.el, routing->row_tok, nullptr, pl.rows_cap, pl.D,
+                                 dx32, pl.bf16, seed, st));
+      sg.mark();
+      HIP_TRY(launch_cast(dx32, dx_or_rows, pl.T * pl.D, pl.bf16, st));
+    }
+  }
+  sg.mark();
+  return sg.err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routing, const void* x,
+                                 const void* dy, const void* h, const void* dh, float* dw1, float* dw2,
+                                 void* ws, size_t ws_bytes, moe_mode mode, void* stream) {
+  Plan pl;
+  moe_status s = validate(p, &pl);
+  if (s != MOE_OK) return s;
+  if (mode != MOE_DETERMINISTIC && mode != MOE_ATOMIC) return MOE_ERR_MODE;
+  const bool at = mode == MOE_ATOMIC;
+  const bool has_tok = pl.T > 0, has_rows = pl.rows_cap > 0;
+  if (!routing || !dw1 || !dw2 || !routing->counts || !routing->offsets) return MOE_ERR_NULL;
+  if (has_tok && (!x || !dy)) return MOE_ERR_NULL;
+  if (has_rows && (!h || !dh || !routing->row_tok || !routing->row_prob)) return MOE_ERR_NULL;
+  const WgradWs L = wgrad_layout(pl, at);
+  s = check_ws(ws, ws_bytes, L.total);
+  if (s != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  const uint64_t seed = p->debug_shuffle_seed;
+  Stager sg{p, st};
+  int32_t* sched = (int32_t*)(wsb + L.sched);
+  float* slots1 = (float*)(wsb + L.slots1);
+  float* slots2 = (float*)(wsb + L.slots2);
+
+  WgradPrepParams Q{};
+  Q.counts = routing->counts;
+  Q.sched = sched;
+  Q.groups = pl.el;
+  Q.M = pl.D;
+  Q.N = pl.F;
+  Q.kc = pl.kc;
+  Q.atomic = at;
+  Q.dw1 = dw1;
+  Q.dw2 = dw2;
+  Q.slots1 = slots1;
+  Q.slots2 = slots2;
+  sg.mark();
+  HIP_TRY(launch_wgrad_prep(Q, at ? 1024 : 1, st));
+
+  WgradParams W{};
+  W.counts = routing->counts;
+  W.offsets = routing->offsets;
+  W.row_tok = routing->row_tok;
+  W.row_prob = routing->row_prob;
+  W.sched = sched;
+  W.groups = pl.el;
+  W.kc = pl.kc;
+  W.atomic = at;
+  W.seed = seed;
+  // dW1_g [D][F] = x[row_tok]^T dh
+  W.M = pl.D;
+  W.N = pl.F;
+  W.a = x;
+  W.lda = pl.D;
+  W.b = dh;
+  W.ldb = pl.F;
+  W.dw = dw1;
+  W.slots = slots1;
+  sg.mark();
+  HIP_TRY(launch_wgrad(W, 1, pl.bf16, wgrad_grid(pl, pl.D, pl.F), st));
+  // dW2_g [F][D] = relu(h)^2^T (p * dy[row_tok])
+  W.M = pl.F;
+  W.N = pl.D;
+  W.a = h;
+  W.lda = pl.F;
+  W.b = dy;
+  W.ldb = pl.D;
+  W.dw = dw2;
+  W.slots = slots2;
+  sg.mark();
+  HIP_TRY(launch_wgrad(W, 2, pl.bf16, wgrad_grid(pl, pl.F, pl.D), st));
+  if (!at) {
+    sg.mark();
+    HIP_TRY(launch_wgrad_reduce(Q, 1024, st));
+  }
+  sg.mark();
+  return sg.err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+MOE_API moe_status moe_fingerprint(const void* data, moe_dtype dtype, int ndim, const int64_t* shape,
+                                   int64_t chunk_elems, uint64_t* chunk_hashes, uint64_t* total,
+                                   void* stream) {
+  int width;
+  switch (dtype) {
+    case MOE_U8: width = 1; break;
+    case MOE_BF16: width = 2; break;
+    case MOE_F32:
+    case MOE_I32: width = 4; break;
+    case MOE_I64:
+    case MOE_F64: width = 8; break;
+    default: return MOE_ERR_DTYPE;
+  }
+  if (ndim < 0 || ndim > 8 || chunk_elems <= 0) return MOE_ERR_SHAPE;
+  if (ndim > 0 && !shape) return MOE_ERR_NULL;
+  if (!total) return MOE_ERR_NULL;
+  int64_t n = 1;
+  for (int i = 0; i < ndim; ++i) {
+    if (shape[i] < 0) return MOE_ERR_SHAPE;
+    if (shape[i] > 0 && n > ((int64_t)1 << 62) / shape[i]) return MOE_ERR_SHAPE;
+    n *= shape[i];
+  }
+  const int64_t m = (n + chunk_elems - 1) / chunk_elems;
+  if (m >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
+  if (n > 0 && (!data || !chunk_hashes)) return MOE_ERR_NULL;
+  uint64_t words[12];
+  int nw = 0;
+  words[nw++] = (uint64_t)dtype;
+  words[nw++] = (uint64_t)ndim;
+  for (int i = 0; i < ndim; ++i) words[nw++] = (uint64_t)shape[i];
+  words[nw++] = (uint64_t)n;
+  words[nw++] = (uint64_t)chunk_elems;
+  hipError_t e = launch_fingerprint(data, width, n, chunk_elems, words, nw, chunk_hashes, total,
+                                    (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}

@@ -1,0 +1,187 @@
+// Router top-k + softmax and the stable token permutation (counting sort by
+// local expert), integer-exact.
+//
+// Readings of the pages (which give no router details): experts are ranked
+// by descending float32 logit, equal logits go to the lower expert index
+// (-0.0 compares equal to +0.0), and the routing probabilities are the
+// softmax over the k selected logits.  The permutation is stable in the flat
+// slot index t*k+j, so the row order inside an expert -- the K order of the
+// weight-gradient reduction -- is fixed by the routing alone.
+//
+//  route_kernel    one wave per token: k rounds of a wave-wide argmax, then
+//                  the softmax; per-chunk histogram of local experts in LDS
+//                  (integer atomics: exact in any order).
+//  scan_kernel     per-expert exclusive bases of every chunk and the expert
+//                  offsets (one workgroup, sequential over chunks).
+//  scatter_kernel  one wave per chunk walks its slots in order, 64 at a
+//                  time; a lane's rank among equal experts comes from ballots,
+//                  so the result is the stable order.  Atomic mode claims rows
+//                  with global atomics instead (order not fixed).
+#include "common.h"
+#include "kernels.h"
+
+namespace moedet {
+
+namespace {
+
+struct Cand {
+  float v;
+  int e;  // INT_MAX: none
+};
+
+DEV bool better(const Cand& a, const Cand& b) {
+  if (b.e == 0x7fffffff) return a.e != 0x7fffffff;
+  if (a.e == 0x7fffffff) return false;
+  return a.v > b.v || (a.v == b.v && a.e < b.e);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void route_kernel(RouteParams P) {
+  __shared__ int s_hist[kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t b = blockIdx.x;  // chunk index (fixed: the histogram is per chunk)
+  if (P.seed) shuffle_delay(P.seed, b);
+  for (int i = tid; i < P.el; i += 256) s_hist[i] = 0;
+  __syncthreads();
+  const int E = P.E, k = P.k;
+  constexpr int PER = kMaxExperts / kWave;
+  for (int tt = w; tt < kRouteChunk; tt += 4) {
+    const int64_t t = b * kRouteChunk + tt;
+    if (t >= P.T) break;
+    const float* row = P.logits + t * E;
+    float v[PER];
+    uint32_t avail = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane + kWave * i;
+      v[i] = 0.f;
+      if (e < E) {
+        v[i] = row[e];
+        avail |= 1u << i;
+      }
+    }
+    float vmax = 0.f, my_v = 0.f;
+    int my_e = -1;
+    for (int j = 0; j < k; ++j) {
+      Cand best{0.f, 0x7fffffff};
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if ((avail >> i) & 1u) {
+          Cand c{v[i], lane + kWave * i};
+          if (better(c, best)) best = c;
+        }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        Cand o{__shfl_xor(best.v, off, 64), __shfl_xor(best.e, off, 64)};
+        if (better(o, best)) best = o;
+      }
+      // best is identical in every lane: (value, index) is a strict total order.
+      if ((best.e & (kWave - 1)) == lane) avail &= ~(1u << (best.e / kWave));
+      if (j == 0) vmax = best.v;
+      if (lane == j) {
+        my_v = best.v;
+        my_e = best.e;
+      }
+    }
+    float ex = lane < k ? expf(my_v - vmax) : 0.f;
+    float sum = ex;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum = sum + __shfl_xor(sum, off, 64);
+    if (lane < k) {
+      P.topk_idx[t * k + lane] = my_e;
+      P.topk_prob[t * k + lane] = ex / sum;
+      const int le = my_e - P.eb;
+      if (le >= 0 && le < P.el) atomicAdd(&s_hist[le], 1);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < P.el; i += 256) P.hist[b * P.el + i] = s_hist[i];
+}
+
+// hist[c][e] -> exclusive row base of chunk c for expert e; counts, offsets.
+__global__ __launch_bounds__(1024) void permute_scan_kernel(RouteParams P) {
+  __shared__ int s_pre[kMaxExperts + 1];
+  __shared__ int s_tmp[16];
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < P.el) {
+    for (int c = 0; c < P.nchunk; ++c) {
+      int32_t* h = P.hist + (int64_t)c * P.el + e;
+      const int v = *h;
+      *h = total;
+      total += v;
+    }
+    P.counts[e] = total;
+  }
+  block_exclusive_scan<1024>(s_pre, s_tmp, P.el, [&](int g) { return P.counts[g]; });
+  if (e <= P.el) P.offsets[e] = s_pre[e];
+  if (e < P.el) {
+    const int base = s_pre[e];
+    for (int c = 0; c < P.nchunk; ++c) P.hist[(int64_t)c * P.el + e] += base;
+    if (P.atomic) P.cursor[e] = base;
+  }
+}
+
+__global__ __launch_bounds__(64) void permute_scatter_kernel(RouteParams P) {
+  __shared__ int s_base[kMaxExperts];
+  const int lane = threadIdx.x;
+  const int64_t c = blockIdx.x;
+  if (P.seed) shuffle_delay(P.seed, c);
+  for (int e = lane; e < P.el; e += 64) s_base[e] = P.hist[c * P.el + e];
+  __syncthreads();
+  const int k = P.k;
+  const int64_t i_begin = c * kRouteChunk * k;
+  const int64_t i_end = min((c + 1) * kRouteChunk, P.T) * k;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  for (int64_t g0 = i_begin; g0 < i_end; g0 += 64) {
+    const int64_t i = g0 + lane;
+    const bool valid = i < i_end;
+    const int e = valid ? P.topk_idx[i] - P.eb : -1;
+    const bool loc = valid && e >= 0 && e < P.el;
+    int row = -1;
+    if (!P.atomic) {
+      uint64_t match = __ballot(loc);
+#pragma unroll
+      for (int bit = 0; bit < 10; ++bit) {
+        const bool my = (e >> bit) & 1;
+        const uint64_t m = __ballot(loc && my);
+        match &= my ? m : ~m;
+      }
+      const int rank = __popcll(match & lt_mask);
+      const int cnt = __popcll(match);
+      const int base = loc ? s_base[e] : 0;
+      __syncthreads();
+      if (loc && rank == 0) s_base[e] = base + cnt;
+      __syncthreads();
+      if (loc) row = base + rank;
+    } else if (loc) {
+      row = atomicAdd(&P.cursor[e], 1);
+    }
+    if (valid) P.slot_row[i] = loc ? row : -1;
+    if (loc) {
+      P.row_src[row] = (int32_t)i;
+      P.row_tok[row] = (int32_t)(i / k);
+      P.row_prob[row] = P.topk_prob[i];
+    }
+  }
+}
+
+hipError_t launch_route(const RouteParams& P, hipStream_t st) {
+  if (P.nchunk <= 0) return hipSuccess;
+  route_kernel<<<P.nchunk, 256, 0, st>>>(P);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_scan(const RouteParams& P, hipStream_t st) {
+  permute_scan_kernel<<<1, 1024, 0, st>>>(P);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_scatter(const RouteParams& P, hipStream_t st) {
+  if (P.nchunk <= 0) return hipSuccess;
+  permute_scatter_kernel<<<P.nchunk, 64, 0, st>>>(P);
+  return hipGetLastError();
+}
+
+}  // namespace moedet

@@ -1,0 +1,241 @@
+/*
+ * moedet.h -- bitwise-deterministic MoE expert layer for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libmoedet.so.  Every compute entry point takes a mode:
+ *   MOE_DETERMINISTIC  every reduction runs in an order fixed by indices and
+ *                      shapes only, so the output bits are a pure function of
+ *                      the input bits, the problem description, the library
+ *                      build and the GPU model;
+ *   MOE_ATOMIC         the same kernels, but the reduction sites add with
+ *                      floating-point atomics in arrival order (the fault the
+ *                      pages describe), for comparison and as a negative
+ *                      control.
+ *
+ * Sources (the pages):
+ *   - "Trillion-Parameter Pretraining Goes Bitwise-Deterministic" (English
+ *     digest), section "Interpretation": in the grouped-GEMM epilogue several
+ *     N-tiles added into the same dprob[token] address, so the result depended
+ *     on their arrival order; the fix gives every N-tile a private output slot
+ *     and combines the slots in a fixed order once all writers have finished.
+ *     The same section states the general rule (fix the reduction order, keep
+ *     a full-precision source of truth).
+ *   - The French article, section "Optimisation pour le Nemotron à mille
+ *     milliards de paramètres": private output slots for the grouped-GEMM
+ *     writers and a fixed reduction order that keeps the parallelism.
+ *   - The French article, section "Méthodologie de débogage du
+ *     non-déterminisme": GPU tensor fingerprints recording shape, dtype and
+ *     element count, chunk-wise for order-sensitive data (routing maps, MoE
+ *     dispatch outputs).
+ *   The same fixed-order rule is applied here to the split-K expert weight
+ *   gradient and to the top-k unpermute/combine.
+ *
+ * Conventions (all calls):
+ *   - Tensor arguments are DEVICE pointers to row-major contiguous arrays,
+ *     allocated and owned by the caller.  The library never allocates or
+ *     frees memory and keeps no state between calls.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = default
+ *     stream).  Calls return after enqueue, with no host synchronisation and
+ *     no device-to-host copies.
+ *   - Arguments are validated before anything is enqueued: a status other
+ *     than MOE_OK (except MOE_ERR_HIP) means no work was enqueued.
+ *     MOE_ERR_HIP reports a launch failure (hipGetLastError).
+ *   - Inputs are read-only.  Every element of every output is written on
+ *     every call, in both modes; outputs need no pre-zeroing.  Row-layout
+ *     outputs ([rows_cap, .]) are written for rows < R only, where
+ *     R = routing.offsets[num_local] (a device value).
+ *   - Workspace contents are undefined on entry and on exit.  Size it with
+ *     moe_workspace_size; it must be 256-byte aligned.
+ *   - Calls that share a workspace or outputs must be ordered on one stream.
+ *   - Storage dtype (problem.dtype) applies to x, W1, W2, dy, h, y, dh, dx
+ *     and the row-layout outputs.  Routing probabilities, dprob and dW are
+ *     always float32; accumulation is float32.
+ *   - Non-finite logits give undefined routing.
+ */
+#ifndef MOEDET_H
+#define MOEDET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,      /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,     /* invalid sizes, alignment or expert range */
+  MOE_ERR_DTYPE = 3,     /* unsupported dtype */
+  MOE_ERR_WORKSPACE = 4, /* workspace too small or misaligned */
+  MOE_ERR_MODE = 5,      /* unknown mode or combine flag */
+  MOE_ERR_HIP = 6        /* a HIP launch or event call failed */
+} moe_status;
+
+typedef enum moe_dtype {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_I32 = 2,
+  MOE_U8 = 3,
+  MOE_I64 = 4,
+  MOE_F64 = 5
+} moe_dtype;
+
+typedef enum moe_mode { MOE_DETERMINISTIC = 0, MOE_ATOMIC = 1 } moe_mode;
+
+/* Layer description.
+ *   tokens        T >= 0 tokens of this call
+ *   d_model       D, the expert input/output width (the LatentMoE latent)
+ *   d_ffn         F, the expert hidden width; expert MLP o = relu(x W1)^2 W2,
+ *                 no bias, W1 [D,F], W2 [F,D]
+ *   num_experts   E, router width (1..1024)
+ *   top_k         k, experts per token (1..min(E,64))
+ *   expert_begin, num_local
+ *                 the experts held here: [expert_begin, expert_begin+num_local)
+ *   dtype         MOE_F32 (D, F multiples of 64) or MOE_BF16 (multiples of 256)
+ *   combine       1: full layer, outputs in token layout ([T,D]; requires
+ *                 num_local == num_experts);
+ *                 0: expert shard, outputs in row layout ([rows_cap,D]) as an
+ *                 expert-parallel rank would send them back
+ *   debug_shuffle_seed
+ *                 0 = off.  Otherwise every kernel permutes the order in which
+ *                 its workgroups take work and delays some of them; in
+ *                 MOE_DETERMINISTIC mode the results do not change.  Testing only.
+ *   stage_events, n_stage_events
+ *                 optional timing hook: NULL/0 = off.  Otherwise an array of
+ *                 n_stage_events hipEvent_t handles owned by the caller; the
+ *                 library records event i just before the i-th kernel of the
+ *                 call and one more after its last kernel (events beyond
+ *                 n_stage_events are skipped).  moe_stage_names lists the
+ *                 kernels. */
+typedef struct moe_problem {
+  int64_t tokens;
+  int32_t d_model;
+  int32_t d_ffn;
+  int32_t num_experts;
+  int32_t top_k;
+  int32_t expert_begin;
+  int32_t num_local;
+  int32_t dtype;
+  int32_t combine;
+  uint64_t debug_shuffle_seed;
+  void* const* stage_events;
+  int32_t n_stage_events;
+} moe_problem;
+
+/* Routing state: written by moe_fwd, read by the backward calls.
+ * Flat slot index i = t*k + j.  rows_cap = T*min(k, num_local).
+ *   topk_idx  [T,k]  int32   slot j holds the j-th largest logit's expert;
+ *                            equal logits go to the lower expert index and
+ *                            -0.0 equals +0.0
+ *   topk_prob [T,k]  float   softmax over the k selected logits
+ *   counts    [El]   int32   routed rows per local expert
+ *   offsets   [El+1] int32   exclusive prefix of counts; offsets[El] = R
+ *   row_src   [rows_cap] int32  row -> flat slot i; rows are grouped by local
+ *                            expert and, in MOE_DETERMINISTIC mode, increasing
+ *                            in i inside each expert (stable).  MOE_ATOMIC mode
+ *                            claims rows with atomics, so the order inside an
+ *                            expert is not fixed.
+ *   row_tok   [rows_cap] int32  row -> token (= row_src / k)
+ *   row_prob  [rows_cap] float  row -> topk_prob of its slot
+ *   slot_row  [T*k]  int32   flat slot -> row, -1 when its expert is not local */
+typedef struct moe_routing {
+  int32_t* topk_idx;
+  float* topk_prob;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* row_src;
+  int32_t* row_tok;
+  float* row_prob;
+  int32_t* slot_row;
+} moe_routing;
+
+/* ABI version (MOE_ABI_VERSION of the build). */
+int moe_abi_version(void);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status s);
+
+/* rows_cap = tokens * min(top_k, num_local): leading size of row-layout buffers. */
+moe_status moe_rows_cap(const moe_problem* p, int64_t* rows_cap);
+
+/* Workspace bytes needed by each call for problem p in `mode` (upper bounds
+ * from shapes only).  Any of the output pointers may be NULL. */
+moe_status moe_workspace_size(const moe_problem* p, moe_mode mode, size_t* fwd_bytes,
+                              size_t* dgrad_bytes, size_t* wgrad_bytes);
+
+/* Names of the kernels a call enqueues, in order, comma-separated, for the
+ * stage_events hook.  call: 0 = moe_fwd, 1 = moe_bwd_dgrad_dprob,
+ * 2 = moe_bwd_wgrad.  Returns NULL for an invalid call or problem. */
+const char* moe_stage_names(const moe_problem* p, moe_mode mode, int call);
+
+/* Forward: routing, stable permute, expert MLP and (combine=1) weighted
+ * combine.
+ *   logits     [T,E] float32
+ *   x          [T,D] dtype
+ *   w1         [El,D,F] dtype (local experts in order)
+ *   w2         [El,F,D] dtype
+ *   routing    its arrays are outputs (see moe_routing)
+ *   h          [rows_cap,F] dtype  output: pre-activation h = x W1 per row,
+ *              saved for the backward
+ *   y_or_rows  combine=1: [T,D] y_t = sum_j p_tj o_(t,j), slots j ascending,
+ *              float32 accumulation, rounded once;
+ *              combine=0: [rows_cap,D] per-row expert outputs o
+ *   ws         workspace of at least moe_workspace_size(...).fwd_bytes */
+moe_status moe_fwd(const moe_problem* p, const float* logits, const void* x, const void* w1,
+                   const void* w2, const moe_routing* routing, void* h, void* y_or_rows,
+                   void* ws, size_t ws_bytes, moe_mode mode, void* stream);
+
+/* Backward, data path: fc2 dgrad with the dprob epilogue, fc1 dgrad and the
+ * dx combine.
+ *   dy         [T,D] dtype upstream gradient of y (token layout also for the
+ *              shard: row r reads dy[row_tok[r]])
+ *   h          [rows_cap,F] saved pre-activation from moe_fwd
+ *   dx_or_rows combine=1: [T,D] dx_t = sum_j dx_(t,j), slots ascending;
+ *              combine=0: [rows_cap,D] per-row dx
+ *   dprob      [T,k] float32 dL/dp_tj = <dy_t, o_(t,j)>; 0 for slots whose
+ *              expert is not local.  MOE_DETERMINISTIC: every N-tile of the
+ *              fc2 dgrad writes a private float32 partial and a separate pass
+ *              adds the partials in N-tile order.  MOE_ATOMIC: each N-tile
+ *              adds its partial atomically.
+ *   dh         [rows_cap,F] dtype output, p * (dy W2^T) * 2 relu(h); input of
+ *              moe_bwd_wgrad */
+moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* routing, const void* dy,
+                               const void* w1, const void* w2, const void* h, void* dx_or_rows,
+                               float* dprob, void* dh, void* ws, size_t ws_bytes, moe_mode mode,
+                               void* stream);
+
+/* Backward, weight gradients (float32 outputs, exact zeros for experts
+ * without rows):
+ *   dw1 [El,D,F] = sum over the expert's rows of x_row^T dh_row
+ *   dw2 [El,F,D] = sum over the expert's rows of relu(h_row)^2^T (p_row dy_row)
+ * An expert with many rows is split along its rows into chunks whose size is
+ * a function of the problem shapes only.  MOE_DETERMINISTIC: the chunk
+ * partials go to the workspace and are added in chunk order.  MOE_ATOMIC:
+ * they are added atomically. */
+moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routing, const void* x,
+                         const void* dy, const void* h, const void* dh, float* dw1, float* dw2,
+                         void* ws, size_t ws_bytes, moe_mode mode, void* stream);
+
+/* Chunk-wise tensor fingerprint (integer arithmetic; bit-exact).
+ *   data          device pointer to numel = prod(shape) elements of `dtype`
+ *   shape         HOST array of ndim (0..8) sizes >= 0
+ *   chunk_elems   C > 0 elements per chunk
+ *   chunk_hashes  DEVICE uint64[ceil(numel/C)] output
+ *   total         DEVICE uint64[1] output
+ * Definition (mix64 = SplitMix64 finalizer, GAMMA = 0x9E3779B97F4A7C15,
+ * arithmetic mod 2^64):
+ *   v_i = mix64(bits_i ^ (i * GAMMA)), bits zero-extended element bits
+ *   H_c = mix64((sum of v_i over chunk c) ^ c)
+ *   total: h = GAMMA; for w in [dtype, ndim, shape..., numel, C, H_0, ...]:
+ *          h = mix64(h ^ w) */
+moe_status moe_fingerprint(const void* data, moe_dtype dtype, int ndim, const int64_t* shape,
+                           int64_t chunk_elems, uint64_t* chunk_hashes, uint64_t* total,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEDET_H */

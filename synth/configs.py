@@ -28,6 +28,8 @@ class Config:
     combine: int          # 1: token-layout outputs (full layer); 0: row-layout (expert shard)
     seed: int
     skew: Optional[str] = None   # None or "zipf"
+    zipf_beta: Optional[float] = None  # None: the calibrated value (zipf_beta.json)
+    zipf_empty: int = 8          # lowest-ranked experts pushed to -30 (no tokens)
     x_std: float = 0.02
     w_std: float = 0.02
 

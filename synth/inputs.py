@@ -61,12 +61,12 @@ def zipf_beta(cfg: Config) -> float:
 
 def zipf_bias(cfg: Config, beta: float) -> np.ndarray:
     """Per-expert logit offset b_e = -beta * 1.1 * ln(rank_e), rank a seeded
-    permutation of 1..E; the 8 lowest-ranked experts get -30 so that they
-    receive no tokens.  Computed in float64, returned as float32."""
+    permutation of 1..E; the ``cfg.zipf_empty`` lowest-ranked experts get -30
+    so that they receive no tokens.  Computed in float64, returned as float32."""
     E = cfg.num_experts
     rank = _rng(cfg.seed, "zipf_rank").permutation(E).astype(np.float64) + 1.0
     b = -beta * 1.1 * np.log(rank)
-    b[rank > E - 8] = -30.0
+    b[rank > E - cfg.zipf_empty] = -30.0
     return b.astype(np.float32)
 
 
@@ -74,7 +74,7 @@ def make_logits(cfg: Config, beta: float = None) -> np.ndarray:
     logits = _rng(cfg.seed, "logits").standard_normal((cfg.tokens, cfg.num_experts), dtype=np.float32)
     if cfg.skew == "zipf":
         if beta is None:
-            beta = zipf_beta(cfg)
+            beta = cfg.zipf_beta if cfg.zipf_beta is not None else zipf_beta(cfg)
         logits += zipf_bias(cfg, beta)[None, :]
     return logits
 

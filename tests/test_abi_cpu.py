@@ -1,0 +1,105 @@
+"""The C-ABI library loads, exports every symbol declared in include/*.h, and
+rejects invalid arguments before enqueuing anything (no GPU needed: these
+paths return before any HIP call)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import bitwise_deterministic_moe_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for hdr in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(hdr).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(moe_\w+)\s*\(", src, flags=re.M))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return moe.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad", "moe_fingerprint"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert names == set(moe.EXPORTED_SYMBOLS)
+    assert lib.moe_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.moe_status_string(s)
+
+
+BASE = dict(tokens=4096, d_model=1024, d_ffn=2048, num_experts=8, top_k=2)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(top_k=0), dict(top_k=9), dict(num_experts=2000, top_k=2), dict(d_model=1000), dict(d_ffn=64),
+    dict(tokens=-1), dict(expert_begin=7, num_local=2, combine=0), dict(num_local=4),  # combine=1 needs all experts
+    dict(d_ffn=256 * 65), dict(top_k=65, num_experts=100),
+])
+def test_shape_validation(bad):
+    p = moe.Problem(**{**BASE, **bad})
+    with pytest.raises(moe.MoeError, match="status 2"):
+        moe.moe_workspace_size(p)
+
+
+def test_dtype_and_mode_validation(lib):
+    p = moe.Problem(**BASE)
+    cp = p.c()
+    cp.dtype = 7
+    sz = ctypes.c_size_t()
+    assert lib.moe_workspace_size(ctypes.byref(cp), 0, ctypes.byref(sz), None, None) == 3
+    assert lib.moe_workspace_size(ctypes.byref(p.c()), 2, ctypes.byref(sz), None, None) == 5
+    cp = p.c()
+    cp.combine = 2
+    assert lib.moe_workspace_size(ctypes.byref(cp), 0, ctypes.byref(sz), None, None) == 5
+
+
+def test_null_and_workspace_errors_return_before_enqueue(lib):
+    p = moe.Problem(**BASE)
+    cp = p.c()
+    fake = ctypes.c_void_p(0x1000)
+    r = moe._CRouting(*([0x2000] * 8))
+    # NULL x
+    assert lib.moe_fwd(ctypes.byref(cp), fake, None, fake, fake, ctypes.byref(r), fake, fake, fake, 1 << 30, 0,
+                       None) == 1
+    # workspace too small
+    assert lib.moe_fwd(ctypes.byref(cp), fake, fake, fake, fake, ctypes.byref(r), fake, fake, fake, 16, 0, None) == 4
+    # misaligned workspace
+    assert lib.moe_bwd_wgrad(ctypes.byref(cp), ctypes.byref(r), fake, fake, fake, fake, fake, fake,
+                             ctypes.c_void_p(0x1008), 1 << 40, 0, None) == 4
+    assert lib.moe_bwd_dgrad_dprob(None, ctypes.byref(r), fake, fake, fake, fake, fake, fake, fake, fake, 0, 0,
+                                   None) == 1
+    # fingerprint argument checks
+    shape = (ctypes.c_int64 * 1)(10)
+    assert lib.moe_fingerprint(fake, 9, 1, shape, 4, fake, fake, None) == 3
+    assert lib.moe_fingerprint(fake, 0, 1, shape, 0, fake, fake, None) == 2
+    assert lib.moe_fingerprint(fake, 0, 9, shape, 4, fake, fake, None) == 2
+    assert lib.moe_fingerprint(fake, 0, 1, shape, 4, fake, None, None) == 1
+
+
+def test_workspace_sizes_and_rows_cap():
+    p = moe.Problem(**BASE)
+    fwd, dg, wg = moe.moe_workspace_size(p, moe.DETERMINISTIC)
+    assert moe.moe_rows_cap(p) == 8192
+    # dprob partials: rows_cap x (F / 256) floats
+    assert dg >= 8192 * 8 * 4
+    fa, da, wa = moe.moe_workspace_size(p, moe.ATOMIC)
+    assert wa < wg and da >= 4096 * 1024 * 4
+    shard = moe.Problem(16384, 2048, 2048, 512, 22, 0, 4, "bf16", 0)
+    assert moe.moe_rows_cap(shard) == 16384 * 4
+    assert moe.moe_stage_names(p, 0, 1) == ["fc2_dgrad_dprob_partials", "dprob_combine", "fc1_dgrad",
+                                            "dx_combine_gather"]
+    assert moe.moe_stage_names(p, 1, 2) == ["wgrad_prep_zero", "wgrad_fc1", "wgrad_fc2"]
