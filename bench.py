@@ -83,6 +83,7 @@ def main():
             self.dx = torch.empty((out_rows, D), dtype=dt, device=dev)
             self.dprob = torch.empty((cfg.tokens, cfg.top_k), dtype=torch.float32, device=dev)
             self.dh = torch.empty((prob.rows_cap, F), dtype=dt, device=dev)
+            self.act_p = torch.empty((prob.rows_cap, F), dtype=dt, device=dev)
             self.dw1 = torch.empty((el, D, F), dtype=torch.float32, device=dev)
             self.dw2 = torch.empty((el, F, D), dtype=torch.float32, device=dev)
             sz = moe.moe_workspace_size(prob, mode)
@@ -91,8 +92,8 @@ def main():
 
     def step(b, ev1=None, ev2=None):
         moe.moe_bwd_dgrad_dprob(prob, routing, dy, w1, w2, h, b.mode, dx=b.dx, dprob=b.dprob, dh=b.dh,
-                                ws=b.ws1, events=ev1)
-        moe.moe_bwd_wgrad(prob, routing, x, dy, h, b.dh, b.mode, dw1=b.dw1, dw2=b.dw2, ws=b.ws2, events=ev2)
+                                act_p=b.act_p, ws=b.ws1, events=ev1)
+        moe.moe_bwd_wgrad(prob, routing, x, dy, b.dh, b.act_p, b.mode, dw1=b.dw1, dw2=b.dw2, ws=b.ws2, events=ev2)
 
     det, atom = Bufs(moe.DETERMINISTIC), Bufs(moe.ATOMIC)
     for _ in range(args.warmup):

@@ -79,7 +79,7 @@ def load_library() -> ctypes.CDLL:
     lib.moe_stage_names.restype = ctypes.c_char_p
     lib.moe_stage_names.argtypes = [P, ctypes.c_int, ctypes.c_int]
     lib.moe_fwd.argtypes = [P, vp, vp, vp, vp, R, vp, vp, vp, sz, ctypes.c_int, vp]
-    lib.moe_bwd_dgrad_dprob.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
+    lib.moe_bwd_dgrad_dprob.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
     lib.moe_bwd_wgrad.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
     lib.moe_fingerprint.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
                                     vp, vp, vp]
@@ -223,8 +223,9 @@ def moe_fwd(prob: Problem, logits, x, w1, w2, mode: int = DETERMINISTIC, routing
 
 
 def moe_bwd_dgrad_dprob(prob: Problem, routing: Routing, dy, w1, w2, h, mode: int = DETERMINISTIC,
-                        dx=None, dprob=None, dh=None, ws=None, events=None):
-    """fc2 dgrad with dprob + fc1 dgrad + dx combine.  Returns (dx_or_rows, dprob, dh)."""
+                        dx=None, dprob=None, dh=None, act_p=None, ws=None, events=None):
+    """fc2 dgrad with dprob + fc1 dgrad + dx combine.
+    Returns (dx_or_rows, dprob, dh, act_p)."""
     lib = load_library()
     dev = h.device
     dt = TORCH_DTYPE[prob.dtype]
@@ -234,20 +235,22 @@ def moe_bwd_dgrad_dprob(prob: Problem, routing: Routing, dy, w1, w2, h, mode: in
         dprob = torch.empty((prob.tokens, prob.top_k), dtype=torch.float32, device=dev)
     if dh is None:
         dh = torch.empty((prob.rows_cap, prob.d_ffn), dtype=dt, device=dev)
+    if act_p is None:
+        act_p = torch.empty((prob.rows_cap, prob.d_ffn), dtype=dt, device=dev)
     need = moe_workspace_size(prob, mode)[1]
     ws = _ws(need, ws, dev)
     cp, cr = prob.c(events), routing.c()
     _check(lib.moe_bwd_dgrad_dprob(ctypes.byref(cp), ctypes.byref(cr), _ptr(dy), _ptr(w1), _ptr(w2), _ptr(h),
-                                   _ptr(dx), _ptr(dprob), _ptr(dh), _ptr(ws), ws.numel(), mode, _stream()),
-           "moe_bwd_dgrad_dprob")
-    return dx, dprob, dh
+                                   _ptr(dx), _ptr(dprob), _ptr(dh), _ptr(act_p), _ptr(ws), ws.numel(), mode,
+                                   _stream()), "moe_bwd_dgrad_dprob")
+    return dx, dprob, dh, act_p
 
 
-def moe_bwd_wgrad(prob: Problem, routing: Routing, x, dy, h, dh, mode: int = DETERMINISTIC, dw1=None, dw2=None,
-                  ws=None, events=None):
+def moe_bwd_wgrad(prob: Problem, routing: Routing, x, dy, dh, act_p, mode: int = DETERMINISTIC, dw1=None,
+                  dw2=None, ws=None, events=None):
     """Expert weight gradients (float32).  Returns (dw1, dw2)."""
     lib = load_library()
-    dev = h.device
+    dev = dh.device
     el, D, F = prob.local, prob.d_model, prob.d_ffn
     if dw1 is None:
         dw1 = torch.empty((el, D, F), dtype=torch.float32, device=dev)
@@ -256,7 +259,7 @@ def moe_bwd_wgrad(prob: Problem, routing: Routing, x, dy, h, dh, mode: int = DET
     need = moe_workspace_size(prob, mode)[2]
     ws = _ws(need, ws, dev)
     cp, cr = prob.c(events), routing.c()
-    _check(lib.moe_bwd_wgrad(ctypes.byref(cp), ctypes.byref(cr), _ptr(x), _ptr(dy), _ptr(h), _ptr(dh), _ptr(dw1),
+    _check(lib.moe_bwd_wgrad(ctypes.byref(cp), ctypes.byref(cr), _ptr(x), _ptr(dy), _ptr(dh), _ptr(act_p), _ptr(dw1),
                              _ptr(dw2), _ptr(ws), ws.numel(), mode, _stream()), "moe_bwd_wgrad")
     return dw1, dw2
 

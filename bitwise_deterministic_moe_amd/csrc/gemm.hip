@@ -1,11 +1,16 @@
 // Expert grouped GEMMs for gfx950.
 //
-//  rowgemm  C[rows of expert g, N] = A[rows, K] * B_g, K = D or F.
-//           fc1 forward (x gathered, W1 [D][F]), fc2 forward (relu(h)^2,
-//           W2 [F][D]), fc2 dgrad (dy gathered, W2 read as [N=F][K=D]) with
-//           the dprob / dh epilogue, fc1 dgrad (dh, W1 read as [N=D][K=F]).
-//  wgrad    dW_g[M, N] = sum over the expert's rows of A_row^T B_row, the
-//           rows split into chunks whose size depends on shapes only.
+//  rowgemm  C[rows of expert g, N] = A[rows, K] * B_g, K = D or F:
+//           fc1 forward   A = x[row_tok] (K-contig), B = W1_g [D][F] (N-contig),
+//                         epilogue stores h and a = relu(h)^2;
+//           fc2 forward   A = a, B = W2_g [F][D];
+//           fc2 dgrad     A = dy[row_tok], B = W2_g read as [N=F][K=D],
+//                         epilogue: dprob partial, dh, p*relu(h)^2;
+//           fc1 dgrad     A = dh, B = W1_g read as [N=D][K=F].
+//  wgrad    dW_g[M, N] = sum over the expert's rows of A_row^T B_row (both
+//           operands contiguous along M/N), rows split into chunks whose size
+//           depends on shapes only:
+//           dW1 = x[row_tok]^T dh,   dW2 = (p relu(h)^2)^T dy[row_tok].
 //
 // Expert row counts live on the device, so every workgroup derives the
 // work decomposition itself from counts[] (no host synchronisation); the
@@ -19,287 +24,185 @@
 //  * wgrad split-K: chunk partials go to the output (chunk 0) and to
 //    workspace slots (chunks 1..S-1) and a later pass adds them in chunk
 //    order; the atomic mode adds all chunks atomically into a zeroed dW.
-#include "gemm.h"
+#include "gemm_bf16.h"
+#include "gemm_f32.h"
 #include "kernels.h"
 
 namespace moedet {
 
-// ---------------------------------------------------------------- rowgemm
-template <typename T, bool A_ACT, bool B_MNC, int EPI>
-__global__ __launch_bounds__(256) void rowgemm_kernel(RowGemmParams P) {
-  using C = Tile<T>;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
-  __shared__ int s_pre[kMaxExperts + 1];
-  __shared__ int s_tmp[8];
-  T* As0 = (T*)smem;
-  T* Bs0 = As0 + 2 * C::OPER_ELEMS;
+// ------------------------------------------------------------ element I/O
+template <typename T>
+DEV float round_t(float v);
+template <>
+DEV float round_t<uint16_t>(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+template <>
+DEV float round_t<float>(float v) { return v; }
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / C::WN, wn = wave % C::WN;
-  const int G = P.groups;
-  const int nN = P.N / C::BN;
+DEV void load4(const uint16_t* p, float (&v)[4]) {
+  u32x2_t x = *(const u32x2_t*)p;
+  v[0] = bf16_to_f32(x[0] & 0xffffu);
+  v[1] = bf16_to_f32(x[0] >> 16);
+  v[2] = bf16_to_f32(x[1] & 0xffffu);
+  v[3] = bf16_to_f32(x[1] >> 16);
+}
+DEV void load4(const float* p, float (&v)[4]) {
+  f32x4_t x = *(const f32x4_t*)p;
+  v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+}
+DEV void store4(uint16_t* p, const float (&v)[4]) {
+  *(u32x2_t*)p = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+DEV void store4(float* p, const float (&v)[4]) { *(f32x4_t*)p = f32x4_t{v[0], v[1], v[2], v[3]}; }
 
-  block_exclusive_scan<256>(s_pre, s_tmp, G, [&](int g) { return (P.counts[g] + C::BM - 1) / C::BM; });
-  const int64_t U = (int64_t)s_pre[G] * nN;
+// Buffer resource covering [p, p + 2^31): outputs and saved activations are
+// below 2 GiB (validated on the host); offsets >= 2^31 are dropped on store
+// and read as zero on load.
+DEV __amdgpu_buffer_rsrc_t buf(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7fffffff, 0x00020000);
+}
+constexpr uint32_t kNoRow = 0x80000000u;
+
+// Sum over the 4 lanes of each quad with two DPP butterflies (lane pairs
+// (0,1)(2,3), then (0,2)(1,3)); a + b == b + a, so all four lanes end with
+// the same bits.
+DEV float quad_sum(float v) {
+  v = v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v = v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  return v;
+}
+
+// ------------------------------------------------------------ row tiles
+struct RowTile {
+  int g, m0, n0, nt, mvalid;
+  int64_t off;
+};
+
+// Work unit of this workgroup: (expert g, m-tile, n-tile), or false.
+template <int BMv, int BNv>
+DEV bool row_tile(const RowGemmParams& P, int* s_pre, int* s_tmp, RowTile& t) {
+  block_exclusive_scan<256>(s_pre, s_tmp, P.groups, [&](int g) { return (P.counts[g] + BMv - 1) / BMv; });
+  const int nN = P.N / BNv;
+  const int64_t U = (int64_t)s_pre[P.groups] * nN;
   const int64_t L = map_unit(blockIdx.x, U, P.seed);
-  if (L < 0) return;
+  if (L < 0) return false;
   const int64_t mt_all = L / nN;
-  const int nt = (int)(L % nN);
-  const int g = find_group(s_pre, G, mt_all);
-  const int m0 = (int)(mt_all - s_pre[g]) * C::BM;
-  const int n0 = nt * C::BN;
-  const int cnt = P.counts[g];
-  const int64_t off = P.offsets[g];
-  const int mvalid = min(C::BM, cnt - m0);
+  t.nt = (int)(L % nN);
+  t.g = find_group(s_pre, P.groups, mt_all);
+  t.m0 = (int)(mt_all - s_pre[t.g]) * BMv;
+  t.n0 = t.nt * BNv;
+  t.off = P.offsets[t.g];
+  t.mvalid = min(BMv, P.counts[t.g] - t.m0);
+  // uniform across the workgroup: keep them in scalar registers
+  t.g = __builtin_amdgcn_readfirstlane(t.g);
+  t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
+  t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
+  t.nt = __builtin_amdgcn_readfirstlane(t.nt);
+  t.mvalid = __builtin_amdgcn_readfirstlane(t.mvalid);
+  t.off = (int64_t)__builtin_amdgcn_readfirstlane((int)t.off);
+  return true;
+}
 
-  // A rows: global rows off+m0 .. (gathered through a_rows when given)
-  KcLoader<T, A_ACT> la;
-  la.init(tid, (const T*)P.a, P.lda, P.a_rows, off + m0, mvalid, P.a_rows != nullptr);
-  const T* Bg = (const T*)P.b + (int64_t)g * P.b_gstride;
-
-  f32x16_t acc[C::MB][C::NB];
-  zero_acc<T>(acc);
-  const int nsteps = P.K / C::BK;
-
-  if constexpr (!B_MNC) {
-    KcLoader<T, false> lb;
-    lb.init(tid, Bg, P.ldb, nullptr, n0, C::BN, false);
-    la.load(0);
-    lb.load(0);
-    la.store(As0, tid);
-    lb.store(Bs0, tid);
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-      const int cur = s & 1;
-      if (s + 1 < nsteps) {
-        la.load((int64_t)(s + 1) * C::BK);
-        lb.load((int64_t)(s + 1) * C::BK);
-      }
-      mma_slice<T>(As0 + cur * C::OPER_ELEMS, Bs0 + cur * C::OPER_ELEMS, acc, wm, wn, lane);
-      if (s + 1 < nsteps) {
-        la.store(As0 + (cur ^ 1) * C::OPER_ELEMS, tid);
-        lb.store(Bs0 + (cur ^ 1) * C::OPER_ELEMS, tid);
-      }
-      __syncthreads();
-    }
-  } else {
-    // B_g stored [K][N]: K row k of slice s is Bg + (s*BK + k)*ldb + n0.
-    MncLoader<T, false, false> lb;
-    auto none = [](int) { return 1.f; };
-    auto rows_of = [&](int s) {
-      return [=](int k) { return Bg + ((int64_t)s * C::BK + k) * P.ldb + n0; };
-    };
-    la.load(0);
-    lb.load(tid, rows_of(0), none);
-    la.store(As0, tid);
-    lb.store(Bs0, tid);
-    __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-      const int cur = s & 1;
-      if (s + 1 < nsteps) {
-        la.load((int64_t)(s + 1) * C::BK);
-        lb.load(tid, rows_of(s + 1), none);
-      }
-      mma_slice<T>(As0 + cur * C::OPER_ELEMS, Bs0 + cur * C::OPER_ELEMS, acc, wm, wn, lane);
-      if (s + 1 < nsteps) {
-        la.store(As0 + (cur ^ 1) * C::OPER_ELEMS, tid);
-        lb.store(Bs0 + (cur ^ 1) * C::OPER_ELEMS, tid);
-      }
-      __syncthreads();
-    }
-  }
-
-  // ------------------------------------------------------------ epilogue
+// Epilogue over the accumulators (layout documented in gemm_bf16.h /
+// gemm_f32.h): acc[mb][nb] lane l holds row wm*WTM + mb*32 + l%32 and columns
+// wn*WTN + nb*32 + 8*i + 4*(l/32) + 0..3 in registers 4i..4i+3.
+template <typename T, int MB, int NB, int WTM, int WTN, int BMv, int WN, int EPI>
+DEV void row_epilogue(const RowGemmParams& P, const RowTile& t, f32x16_t (&acc)[MB][NB], float* s_part, int wm,
+                      int wn, int lane, int tid) {
   const int r32 = lane & 31, half = lane >> 5;
-  const int WTM = C::BM / C::WM, WTN = C::BN / C::WN;
-  if constexpr (EPI == kEpiStore) {
+  if constexpr (EPI == kEpiStore || EPI == kEpiStoreAct) {
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       const int m = wm * WTM + mb * 32 + r32;
-      if (m >= mvalid) continue;
-      T* crow = (T*)P.c + (off + m0 + m) * P.ldc + n0 + wn * WTN;
+      if (m >= t.mvalid) continue;
+      const int64_t grow = t.off + t.m0 + m;
+      T* crow = (T*)P.c + grow * P.ldc + t.n0 + wn * WTN;
+      T* arow = (T*)P.c2 + grow * P.ldc2 + t.n0 + wn * WTN;
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int n = nb * 32 + 8 * i + 4 * half;
-          const f32x16_t& a = acc[mb][nb];
-          if constexpr (sizeof(T) == 2) {
-            u32x2_t v = {pack_bf16x2(a[4 * i], a[4 * i + 1]), pack_bf16x2(a[4 * i + 2], a[4 * i + 3])};
-            *(u32x2_t*)(crow + n) = v;
-          } else {
-            *(f32x4_t*)(crow + n) = f32x4_t{a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3]};
+          float v[4] = {acc[mb][nb][4 * i], acc[mb][nb][4 * i + 1], acc[mb][nb][4 * i + 2], acc[mb][nb][4 * i + 3]};
+          store4(crow + n, v);
+          if constexpr (EPI == kEpiStoreAct) {
+            // activation of the stored (rounded) h, the value the backward sees
+            float a[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float r = relu(round_t<T>(v[q]));
+              a[q] = r * r;
+            }
+            store4(arow + n, a);
           }
         }
     }
   } else {
     // fc2 dgrad: acc = G = dy W2^T for rows m, columns f of this N-tile.
-    //   part[row][nt] = sum_f G * relu(h)^2   (fixed order: nb, i, q within
-    //                   a lane; then the lane pair; then wave wn = 0, 1)
-    //   dh = (2 p G) * relu(h)
-    float* s_part = (float*)smem;  // [WN][BM], operand buffers are free now
+    //   part[row][nt] = sum_f G * relu(h)^2   (fixed order: nb, i, q inside a
+    //                   lane; then the lane pair; then waves wn = 0, 1, ...)
+    //   dh = (2 p G) * relu(h);   pa = p * relu(h)^2
 #pragma unroll
-    for (int mb = 0; mb < C::MB; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       const int m = wm * WTM + mb * 32 + r32;
-      const bool valid = m < mvalid;
-      const int64_t grow = off + m0 + m;
       float part = 0.f;
-      if (valid) {
-        const float p2 = 2.f * P.row_prob[grow];
-        const T* hrow = (const T*)P.h + grow * P.ldh + n0 + wn * WTN;
-        T* drow = (T*)P.c + grow * P.ldc + n0 + wn * WTN;
+      if (m < t.mvalid) {
+        const int64_t grow = t.off + t.m0 + m;
+        const float p = P.row_prob[grow];
+        const float p2 = 2.f * p;
+        const int64_t col = t.n0 + wn * WTN;
+        const T* hrow = (const T*)P.h + grow * P.ldh + col;
+        T* drow = (T*)P.c + grow * P.ldc + col;
+        T* arow = (T*)P.c2 + grow * P.ldc2 + col;
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int n = nb * 32 + 8 * i + 4 * half;
-            const f32x16_t& a = acc[mb][nb];
-            float hv[4];
-            if constexpr (sizeof(T) == 2) {
-              u32x2_t hh = *(const u32x2_t*)(hrow + n);
-              hv[0] = bf16_to_f32(hh[0] & 0xffffu);
-              hv[1] = bf16_to_f32(hh[0] >> 16);
-              hv[2] = bf16_to_f32(hh[1] & 0xffffu);
-              hv[3] = bf16_to_f32(hh[1] >> 16);
-            } else {
-              f32x4_t hh = *(const f32x4_t*)(hrow + n);
-              hv[0] = hh[0]; hv[1] = hh[1]; hv[2] = hh[2]; hv[3] = hh[3];
-            }
-            float dh[4];
+            float hv[4], dh[4], pa[4];
+            load4(hrow + n, hv);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const float gq = a[4 * i + q];
+              const float gq = acc[mb][nb][4 * i + q];
               const float rh = relu(hv[q]);
-              part = __builtin_fmaf(gq, rh * rh, part);
+              const float a = rh * rh;
+              part = __builtin_fmaf(gq, a, part);
               dh[q] = (p2 * gq) * rh;
+              pa[q] = p * a;
             }
-            if constexpr (sizeof(T) == 2) {
-              *(u32x2_t*)(drow + n) = u32x2_t{pack_bf16x2(dh[0], dh[1]), pack_bf16x2(dh[2], dh[3])};
-            } else {
-              *(f32x4_t*)(drow + n) = f32x4_t{dh[0], dh[1], dh[2], dh[3]};
-            }
+            store4(drow + n, dh);
+            store4(arow + n, pa);
           }
       }
       // lanes l and l^32 hold the two column halves of the same row;
       // a + b == b + a, so both get the same bits.
       part = part + __shfl_xor(part, 32, 64);
-      if (half == 0) s_part[wn * C::BM + m] = part;
+      if (half == 0) s_part[wn * BMv + m] = part;
     }
     __syncthreads();
-    for (int m = tid; m < mvalid; m += 256) {
+    for (int m = tid; m < t.mvalid; m += 256) {
       float v = s_part[m];
 #pragma unroll
-      for (int w = 1; w < C::WN; ++w) v = v + s_part[w * C::BM + m];
-      const int64_t grow = off + m0 + m;
+      for (int w = 1; w < WN; ++w) v = v + s_part[w * BMv + m];
+      const int64_t grow = t.off + t.m0 + m;
       if (P.atomic)
         atomicAdd(P.dprob + P.row_src[grow], v);
       else
-        P.part[grow * P.n_tiles + nt] = v;
+        P.part[grow * P.n_tiles + t.nt] = v;
     }
   }
 }
 
-// ---------------------------------------------------------------- wgrad
-template <typename T, bool A_GATHER, bool A_ACT, bool B_GATHER, bool B_SCALE>
-__global__ __launch_bounds__(256) void wgrad_kernel(WgradParams P) {
-  using C = Tile<T>;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
-  __shared__ int s_tok[kMaxChunkRows];
-  __shared__ float s_prob[B_SCALE ? kMaxChunkRows : 1];
-  T* As0 = (T*)smem;
-  T* Bs0 = As0 + 2 * C::OPER_ELEMS;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / C::WN, wn = wave % C::WN;
-  const int G = P.groups;
-  const int nN = P.N / C::BN;
-  const int tiles = (P.M / C::BM) * nN;
-  const int32_t* unit_start = P.sched;
-  const int32_t* slot_base = P.sched + (G + 1);
-
-  const int64_t U = (int64_t)unit_start[G] * tiles;
-  const int64_t L = map_unit(blockIdx.x, U, P.seed);
-  if (L < 0) return;
-  const int64_t u = L / tiles;
-  const int tile = (int)(L % tiles);
-  const int g = find_group(unit_start, G, u);
-  const int s = (int)(u - unit_start[g]);
-  const int cnt = P.counts[g];
-  const int S = cnt > P.kc ? (cnt + P.kc - 1) / P.kc : 1;
-  const int k_lo = (int)((int64_t)s * cnt / S), k_hi = (int)((int64_t)(s + 1) * cnt / S);
-  const int klen = k_hi - k_lo;
-  const int64_t row0 = (int64_t)P.offsets[g] + k_lo;
-  const int m0 = (tile / nN) * C::BM, n0 = (tile % nN) * C::BN;
-
-  for (int i = tid; i < klen; i += 256) {
-    s_tok[i] = (A_GATHER || B_GATHER) ? P.row_tok[row0 + i] : 0;
-    if constexpr (B_SCALE) s_prob[i] = P.row_prob[row0 + i];
-  }
-  __syncthreads();
-
-  f32x16_t acc[C::MB][C::NB];
-  zero_acc<T>(acc);
-  const int nsteps = (klen + C::BK - 1) / C::BK;
-
-  MncLoader<T, A_ACT, false> la;
-  MncLoader<T, false, B_SCALE> lb;
-  const T* Ab = (const T*)P.a;
-  const T* Bb = (const T*)P.b;
-  auto a_rows = [&](int st) {
-    return [=](int k) -> const T* {
-      const int kk = st * C::BK + k;
-      if (kk >= klen) return nullptr;
-      const int64_t r = A_GATHER ? (int64_t)s_tok[kk] : row0 + kk;
-      return Ab + r * P.lda + m0;
-    };
-  };
-  auto b_rows = [&](int st) {
-    return [=](int k) -> const T* {
-      const int kk = st * C::BK + k;
-      if (kk >= klen) return nullptr;
-      const int64_t r = B_GATHER ? (int64_t)s_tok[kk] : row0 + kk;
-      return Bb + r * P.ldb + n0;
-    };
-  };
-  auto no_scale = [](int) { return 1.f; };
-  auto b_scale = [&](int st) {
-    return [=](int k) { return B_SCALE ? s_prob[st * C::BK + k] : 1.f; };
-  };
-
-  if (nsteps > 0) {
-    la.load(tid, a_rows(0), no_scale);
-    lb.load(tid, b_rows(0), b_scale(0));
-    la.store(As0, tid);
-    lb.store(Bs0, tid);
-    __syncthreads();
-    for (int st = 0; st < nsteps; ++st) {
-      const int cur = st & 1;
-      if (st + 1 < nsteps) {
-        la.load(tid, a_rows(st + 1), no_scale);
-        lb.load(tid, b_rows(st + 1), b_scale(st + 1));
-      }
-      mma_slice<T>(As0 + cur * C::OPER_ELEMS, Bs0 + cur * C::OPER_ELEMS, acc, wm, wn, lane);
-      if (st + 1 < nsteps) {
-        la.store(As0 + (cur ^ 1) * C::OPER_ELEMS, tid);
-        lb.store(Bs0 + (cur ^ 1) * C::OPER_ELEMS, tid);
-      }
-      __syncthreads();
-    }
-  }
-
-  // Destination: a single chunk (or chunk 0) writes dW directly; chunks
-  // 1..S-1 write workspace slots in det mode, or add atomically.
-  const bool atomic_add = P.atomic && S > 1;
-  float* dst = P.dw + (int64_t)g * P.M * P.N;
-  if (!P.atomic && s > 0) dst = P.slots + (int64_t)(slot_base[g] + s - 1) * P.M * P.N;
+// Stores of a wgrad tile: direct, into a workspace slot, or atomic adds.
+template <int MB, int NB, int WTM, int WTN>
+DEV void wgrad_store(float* dst, int ldd, bool atomic_add, int m0, int n0, f32x16_t (&acc)[MB][NB], int wm, int wn,
+                     int lane) {
   const int r32 = lane & 31, half = lane >> 5;
-  const int WTM = C::BM / C::WM, WTN = C::BN / C::WN;
 #pragma unroll
-  for (int mb = 0; mb < C::MB; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
     const int m = m0 + wm * WTM + mb * 32 + r32;
-    float* crow = dst + (int64_t)m * P.N + n0 + wn * WTN;
+    float* crow = dst + (int64_t)m * ldd + n0 + wn * WTN;
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int n = nb * 32 + 8 * i + 4 * half;
@@ -314,6 +217,392 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradParams P) {
   }
 }
 
+struct WgradTile {
+  int g, s, S, klen, m0, n0;
+  int64_t row0;
+};
+
+template <int BMv, int BNv>
+DEV bool wgrad_tile(const WgradParams& P, WgradTile& t) {
+  const int G = P.groups;
+  const int nN = P.N / BNv;
+  const int tiles = (P.M / BMv) * nN;
+  const int32_t* unit_start = P.sched;
+  const int64_t U = (int64_t)unit_start[G] * tiles;
+  const int64_t L = map_unit(blockIdx.x, U, P.seed);
+  if (L < 0) return false;
+  const int64_t u = L / tiles;
+  const int tile = (int)(L % tiles);
+  t.g = find_group(unit_start, G, u);
+  t.s = (int)(u - unit_start[t.g]);
+  const int cnt = P.counts[t.g];
+  t.S = cnt > P.kc ? (cnt + P.kc - 1) / P.kc : 1;
+  const int k_lo = (int)((int64_t)t.s * cnt / t.S), k_hi = (int)((int64_t)(t.s + 1) * cnt / t.S);
+  t.klen = k_hi - k_lo;
+  t.row0 = (int64_t)P.offsets[t.g] + k_lo;
+  t.m0 = (tile / nN) * BMv;
+  t.n0 = (tile % nN) * BNv;
+  return true;
+}
+
+DEV float* wgrad_dst(const WgradParams& P, const WgradTile& t) {
+  const int32_t* slot_base = P.sched + (P.groups + 1);
+  if (!P.atomic && t.s > 0) return P.slots + (int64_t)(slot_base[t.g] + t.s - 1) * P.M * P.N;
+  return P.dw + (int64_t)t.g * P.M * P.N;
+}
+
+// ================================================================= bf16
+// Epilogues of the bf16 kernels go through LDS so that every global load and
+// store is row-contiguous: the 256x256 float32 accumulator tile is written to
+// LDS in four passes of 64 rows (row stride 260 floats); after each pass all
+// 256 threads walk the 64 rows, four rows per step, each thread owning four
+// consecutive columns (a wave covers one full row).
+constexpr int kStageRow = 260;                       // floats per staged row
+constexpr int kStageBytes = 64 * kStageRow * 4;      // 66,560 bytes, inside the main-loop ring
+static_assert(kStageBytes <= bf::LDS_BYTES, "epilogue stage must fit in the ring");
+
+// Pass p covers tile rows 64p..64p+63.  In step st (0..15) of a pass, thread
+// tid owns row 64p + 4*st + tid/64 and columns 4*(tid%64)..+3, so each wave
+// handles one whole row per step and control flow is uniform per wave.
+// Between passes only LDS traffic has to be ordered, so the barriers wait on
+// LDS operations alone and global stores stay in flight.  Everything is fully
+// unrolled so that per-step data lives in registers.
+DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+DEV int staged_row(int p, int st, int tid) {
+  return 64 * p + 4 * st + __builtin_amdgcn_readfirstlane(tid >> 6);  // one row per wave
+}
+DEV int staged_col(int tid) { return (tid & 63) * 4; }
+
+// pre.load(d, p): issue this thread's global loads needed by pass p into d
+// (called one pass ahead); emit(row, col, v, d, st): consume one step.
+template <class Pre, class Emit>
+DEV void staged_epilogue(float* stage, f32x16_t (&acc)[4][4], int wm, int wn, int lane, int tid, Pre& pre, Emit emit) {
+  const int r32 = lane & 31, half = lane >> 5;
+  typename Pre::Data d[2];
+  pre.load(d[0], 0);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    if (wm == (p >> 1)) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int mb = 2 * (p & 1) + q;
+        const int m = q * 32 + r32;  // row within the pass
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int n = wn * 128 + nb * 32 + 8 * i + 4 * half;
+            const f32x16_t& a = acc[mb][nb];
+            *(f32x4_t*)(stage + m * kStageRow + n) = f32x4_t{a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3]};
+          }
+      }
+    }
+    lds_barrier();
+    if (p + 1 < 4) pre.load(d[(p + 1) & 1], p + 1);
+    f32x4_t v[16];
+#pragma unroll
+    for (int st = 0; st < 16; ++st) v[st] = *(const f32x4_t*)(stage + (4 * st + (tid >> 6)) * kStageRow + staged_col(tid));
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      float f[4] = {v[st][0], v[st][1], v[st][2], v[st][3]};
+      emit(staged_row(p, st, tid), staged_col(tid), f, d[p & 1], st);
+    }
+    lds_barrier();
+  }
+}
+
+struct NoPre {
+  struct Data {};
+  DEV void load(Data&, int) {}
+};
+
+template <int BL, int EPI>
+__global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
+  __shared__ int s_pre[kMaxExperts + 1];
+  __shared__ int s_tmp[8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  RowTile t;
+  if (!row_tile<bf::BM, bf::BN>(P, s_pre, s_tmp, t)) return;
+
+  bf::KcOperand oa;
+  oa.init(P.a, P.a_bytes, wave, lane, [&](int r) -> uint32_t {
+    if (r >= t.mvalid) return bf::kOOB;
+    const int64_t row = P.a_rows ? (int64_t)P.a_rows[t.off + t.m0 + r] : t.off + t.m0 + r;
+    return (uint32_t)(row * P.lda * 2);
+  });
+  const uint16_t* Bg = (const uint16_t*)P.b + (int64_t)t.g * P.b_gstride;
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  const int nsteps = P.K / bf::BK;
+  if constexpr (BL == bf::KC) {
+    bf::KcOperand ob;
+    ob.init(Bg, P.b_bytes, wave, lane, [&](int r) -> uint32_t { return (uint32_t)((t.n0 + r) * P.ldb * 2); });
+    bf::mainloop<bf::KC, bf::KC>(lds, nsteps, [&](int s, uint16_t* st) {
+      oa.issue(st, wave, s * bf::BK);
+      ob.issue(st + bf::OPER, wave, s * bf::BK);
+    }, acc, wm, wn, lane);
+  } else {
+    bf::MncOperand ob;
+    ob.init(Bg, P.b_bytes, wave, lane, t.n0);
+    bf::mainloop<bf::KC, bf::MNC>(lds, nsteps, [&](int s, uint16_t* st) {
+      oa.issue(st, wave, s * bf::BK);
+      ob.issue(st + bf::OPER, wave, lane,
+               [&](int k) -> uint32_t { return (uint32_t)((s * bf::BK + k) * P.ldb * 2); });
+    }, acc, wm, wn, lane);
+  }
+  float* stage = (float*)lds;
+  if constexpr (EPI == kEpiStore || EPI == kEpiStoreAct) {
+    NoPre none;
+    const __amdgpu_buffer_rsrc_t rc = buf(P.c), rc2 = buf(P.c2);
+    staged_epilogue(stage, acc, wm, wn, lane, tid, none, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
+      if (m >= t.mvalid) return;  // uniform per wave
+      const uint32_t grow = (uint32_t)(t.off + t.m0 + m);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rc,
+                                            (grow * (uint32_t)P.ldc + t.n0 + col) * 2u, 0, 0);
+      if constexpr (EPI == kEpiStoreAct) {
+        // activation of the stored (rounded) h, the value the backward sees
+        float a[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float r = relu(round_t<uint16_t>(v[q]));
+          a[q] = r * r;
+        }
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])}, rc2,
+                                              (grow * (uint32_t)P.ldc2 + t.n0 + col) * 2u, 0, 0);
+      }
+    });
+  } else {
+    // fc2 dgrad: v = G = dy W2^T at (row, columns col..col+3 of this N-tile).
+    //   part[row][nt] = sum over the tile's 256 columns of G * relu(h)^2:
+    //                   4 columns in order inside a lane, a DPP butterfly over
+    //                   the lane quad (16 columns), then the 16 quad sums of
+    //                   the row in quad order (through LDS);
+    //   dh = (2 p G) * relu(h);  act_p = p * relu(h)^2.
+    // h and the row probabilities of a pass are loaded one pass ahead.
+    struct HPre {
+      struct Data {
+        u32x2_t h[16];
+        float p[16];
+      };
+      const RowGemmParams& P;
+      const RowTile& t;
+      int tid;
+      DEV void load(Data& d, int p) {
+        const __amdgpu_buffer_rsrc_t rh = buf(P.h);
+#pragma unroll
+        for (int st = 0; st < 16; ++st) {
+          const int m = staged_row(p, st, tid);
+          const bool ok = m < t.mvalid;
+          const uint32_t grow = (uint32_t)(t.off + t.m0 + (ok ? m : 0));
+          d.h[st] = __builtin_amdgcn_raw_buffer_load_b64(
+              rh, ok ? (grow * (uint32_t)P.ldh + t.n0 + staged_col(tid)) * 2u : kNoRow, 0, 0);
+          d.p[st] = P.row_prob[grow];
+        }
+      }
+    } hpre{P, t, tid};
+    const __amdgpu_buffer_rsrc_t rc = buf(P.c), rc2 = buf(P.c2);
+    __shared__ float s_qsum[bf::BM * 16];  // [tile row][quad]
+    staged_epilogue(stage, acc, wm, wn, lane, tid, hpre, [&](int m, int col, float (&g)[4], typename HPre::Data& d, int st) {
+      const bool valid = m < t.mvalid;   // uniform across the wave (one row per wave)
+      if (!valid) return;
+      const int64_t grow = t.off + t.m0 + m;
+      const float p = d.p[st];
+      const float p2 = 2.f * p;
+      float hv[4], dh[4], pa[4];
+      hv[0] = bf16_to_f32(d.h[st][0] & 0xffffu);
+      hv[1] = bf16_to_f32(d.h[st][0] >> 16);
+      hv[2] = bf16_to_f32(d.h[st][1] & 0xffffu);
+      hv[3] = bf16_to_f32(d.h[st][1] >> 16);
+      float part = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float rh = relu(hv[q]);
+        const float a = rh * rh;
+        part = __builtin_fmaf(g[q], a, part);
+        dh[q] = (p2 * g[q]) * rh;
+        pa[q] = p * a;
+      }
+      const uint32_t o = (uint32_t)grow * 2u * (uint32_t)P.ldc + (t.n0 + col) * 2u;
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(dh[0], dh[1]), pack_bf16x2(dh[2], dh[3])}, rc, o, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(pa[0], pa[1]), pack_bf16x2(pa[2], pa[3])}, rc2,
+                                            (uint32_t)grow * 2u * (uint32_t)P.ldc2 + (t.n0 + col) * 2u, 0, 0);
+      part = quad_sum(part);
+      if ((lane & 3) == 0) s_qsum[m * 16 + (lane >> 2)] = part;
+    });
+    __syncthreads();
+    // one thread per tile row: the 16 quad sums in order
+    if (tid < t.mvalid) {
+      float v = s_qsum[tid * 16];
+#pragma unroll
+      for (int q = 1; q < 16; ++q) v = v + s_qsum[tid * 16 + q];
+      const int64_t grow = t.off + t.m0 + tid;
+      if (P.atomic)
+        atomicAdd(P.dprob + P.row_src[grow], v);
+      else
+        P.part[grow * P.n_tiles + t.nt] = v;
+    }
+  }
+}
+
+template <bool A_GATHER, bool B_GATHER>
+__global__ __launch_bounds__(256) void wgrad_bf16_kernel(WgradParams P) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
+  __shared__ int s_tok[kMaxChunkRows];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  WgradTile t;
+  if (!wgrad_tile<bf::BM, bf::BN>(P, t)) return;
+  for (int i = tid; i < t.klen; i += 256) s_tok[i] = P.row_tok[t.row0 + i];
+  __syncthreads();
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  bf::MncOperand oa, ob;
+  oa.init(P.a, P.a_bytes, wave, lane, t.m0);
+  ob.init(P.b, P.b_bytes, wave, lane, t.n0);
+  const int nsteps = (t.klen + bf::BK - 1) / bf::BK;
+  bf::mainloop<bf::MNC, bf::MNC>(lds, nsteps, [&](int s, uint16_t* st) {
+    auto rowoff = [&](int k, bool gather, int64_t ld) -> uint32_t {
+      const int kk = s * bf::BK + k;
+      if (kk >= t.klen) return bf::kOOB;
+      const int64_t r = gather ? (int64_t)s_tok[kk] : t.row0 + kk;
+      return (uint32_t)(r * ld * 2);
+    };
+    oa.issue(st, wave, lane, [&](int k) { return rowoff(k, A_GATHER, P.lda); });
+    ob.issue(st + bf::OPER, wave, lane, [&](int k) { return rowoff(k, B_GATHER, P.ldb); });
+  }, acc, wm, wn, lane);
+  float* dst = wgrad_dst(P, t);
+  const bool atomic_add = P.atomic && t.S > 1;
+  NoPre none;
+  const __amdgpu_buffer_rsrc_t rd = buf(dst);
+  staged_epilogue((float*)lds, acc, wm, wn, lane, tid, none, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
+    const uint32_t o = ((uint32_t)(t.m0 + m) * (uint32_t)P.N + t.n0 + col) * 4u;
+    if (atomic_add) {
+      float* po = dst + o / 4u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) atomicAdd(po + q, v[q]);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b128(f32x4_t{v[0], v[1], v[2], v[3]}, rd, o, 0, 0);
+    }
+  });
+}
+
+// ================================================================= fp32
+template <bool B_MNC, int EPI>
+__global__ __launch_bounds__(256) void rowgemm_f32_kernel(RowGemmParams P) {
+  __shared__ __attribute__((aligned(16))) float lds[f32::LDS_BYTES / 4];
+  __shared__ int s_pre[kMaxExperts + 1];
+  __shared__ int s_tmp[8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  RowTile t;
+  if (!row_tile<f32::BM, f32::BN>(P, s_pre, s_tmp, t)) return;
+  float* As0 = lds;
+  float* Bs0 = lds + 2 * f32::OPER;
+  f32::KcLoader la;
+  la.init(tid, (const float*)P.a, P.lda, P.a_rows, t.off + t.m0, t.mvalid);
+  const float* Bg = (const float*)P.b + (int64_t)t.g * P.b_gstride;
+  f32x16_t acc[1][1];
+  f32::zero_acc(acc[0][0]);
+  const int nsteps = P.K / f32::BK;
+  f32::KcLoader lbk;
+  f32::MncLoader lbm;
+  if (!B_MNC) lbk.init(tid, Bg, P.ldb, nullptr, t.n0, f32::BN);
+  auto loadB = [&](int s) {
+    if constexpr (B_MNC)
+      lbm.load(tid, [&](int k) { return Bg + ((int64_t)s * f32::BK + k) * P.ldb + t.n0; });
+    else
+      lbk.load((int64_t)s * f32::BK);
+  };
+  auto storeB = [&](float* dst) {
+    if constexpr (B_MNC)
+      lbm.store(dst, tid);
+    else
+      lbk.store(dst, tid);
+  };
+  la.load(0);
+  loadB(0);
+  la.store(As0, tid);
+  storeB(Bs0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < nsteps) {
+      la.load((int64_t)(s + 1) * f32::BK);
+      loadB(s + 1);
+    }
+    f32::mma_slice(As0 + cur * f32::OPER, Bs0 + cur * f32::OPER, acc[0][0], wm, wn, lane);
+    if (s + 1 < nsteps) {
+      la.store(As0 + (cur ^ 1) * f32::OPER, tid);
+      storeB(Bs0 + (cur ^ 1) * f32::OPER);
+    }
+    __syncthreads();
+  }
+  row_epilogue<float, 1, 1, 32, 32, f32::BM, 2, EPI>(P, t, acc, lds, wm, wn, lane, tid);
+}
+
+template <bool A_GATHER, bool B_GATHER>
+__global__ __launch_bounds__(256) void wgrad_f32_kernel(WgradParams P) {
+  __shared__ __attribute__((aligned(16))) float lds[f32::LDS_BYTES / 4];
+  __shared__ int s_tok[kMaxChunkRows];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  WgradTile t;
+  if (!wgrad_tile<f32::BM, f32::BN>(P, t)) return;
+  for (int i = tid; i < t.klen; i += 256) s_tok[i] = P.row_tok[t.row0 + i];
+  __syncthreads();
+  float* As0 = lds;
+  float* Bs0 = lds + 2 * f32::OPER;
+  f32x16_t acc[1][1];
+  f32::zero_acc(acc[0][0]);
+  const int nsteps = (t.klen + f32::BK - 1) / f32::BK;
+  f32::MncLoader la, lb;
+  const float* Ab = (const float*)P.a;
+  const float* Bb = (const float*)P.b;
+  auto rows = [&](int st, const float* base, bool gather, int64_t ld, int mn0) {
+    return [=, &t](int k) -> const float* {
+      const int kk = st * f32::BK + k;
+      if (kk >= t.klen) return nullptr;
+      const int64_t r = gather ? (int64_t)s_tok[kk] : t.row0 + kk;
+      return base + r * ld + mn0;
+    };
+  };
+  if (nsteps > 0) {
+    la.load(tid, rows(0, Ab, A_GATHER, P.lda, t.m0));
+    lb.load(tid, rows(0, Bb, B_GATHER, P.ldb, t.n0));
+    la.store(As0, tid);
+    lb.store(Bs0, tid);
+    __syncthreads();
+    for (int st = 0; st < nsteps; ++st) {
+      const int cur = st & 1;
+      if (st + 1 < nsteps) {
+        la.load(tid, rows(st + 1, Ab, A_GATHER, P.lda, t.m0));
+        lb.load(tid, rows(st + 1, Bb, B_GATHER, P.ldb, t.n0));
+      }
+      f32::mma_slice(As0 + cur * f32::OPER, Bs0 + cur * f32::OPER, acc[0][0], wm, wn, lane);
+      if (st + 1 < nsteps) {
+        la.store(As0 + (cur ^ 1) * f32::OPER, tid);
+        lb.store(Bs0 + (cur ^ 1) * f32::OPER, tid);
+      }
+      __syncthreads();
+    }
+  }
+  wgrad_store<1, 1, 32, 32>(wgrad_dst(P, t), P.N, P.atomic && t.S > 1, t.m0, t.n0, acc, wm, wn, lane);
+}
+
+// ============================================================ prep/reduce
 // Schedule for wgrad: unit_start[g] = sum_{g'<g} S_g' and slot_base[g] =
 // sum_{g'<g} (S_g' - 1), S_g = max(1, ceil(cnt_g / kc)).  Atomic mode also
 // zeroes dW of every expert that is split (S_g >= 2).
@@ -377,44 +666,40 @@ __global__ __launch_bounds__(256) void wgrad_reduce_kernel(WgradPrepParams P) {
 }
 
 // ---------------------------------------------------------------- launchers
-template <typename T>
-static hipError_t launch_rowgemm_t(const RowGemmParams& P, int kind, int64_t grid, hipStream_t st) {
-  switch (kind) {
-    case kGemmFc1Fwd:
-      rowgemm_kernel<T, false, true, kEpiStore><<<grid, 256, 0, st>>>(P);
-      break;
-    case kGemmFc2Fwd:
-      rowgemm_kernel<T, true, true, kEpiStore><<<grid, 256, 0, st>>>(P);
-      break;
-    case kGemmFc2Dgrad:
-      rowgemm_kernel<T, false, false, kEpiDgrad2><<<grid, 256, 0, st>>>(P);
-      break;
-    case kGemmFc1Dgrad:
-      rowgemm_kernel<T, false, false, kEpiStore><<<grid, 256, 0, st>>>(P);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
 hipError_t launch_rowgemm(const RowGemmParams& P, int kind, bool bf16, int64_t grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
-  return bf16 ? launch_rowgemm_t<uint16_t>(P, kind, grid, st) : launch_rowgemm_t<float>(P, kind, grid, st);
+  if (bf16) {
+    switch (kind) {
+      case kGemmFc1Fwd: rowgemm_bf16_kernel<bf::MNC, kEpiStoreAct><<<grid, 256, 0, st>>>(P); break;
+      case kGemmFc2Fwd: rowgemm_bf16_kernel<bf::MNC, kEpiStore><<<grid, 256, 0, st>>>(P); break;
+      case kGemmFc2Dgrad: rowgemm_bf16_kernel<bf::KC, kEpiDgrad2><<<grid, 256, 0, st>>>(P); break;
+      case kGemmFc1Dgrad: rowgemm_bf16_kernel<bf::KC, kEpiStore><<<grid, 256, 0, st>>>(P); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (kind) {
+      case kGemmFc1Fwd: rowgemm_f32_kernel<true, kEpiStoreAct><<<grid, 256, 0, st>>>(P); break;
+      case kGemmFc2Fwd: rowgemm_f32_kernel<true, kEpiStore><<<grid, 256, 0, st>>>(P); break;
+      case kGemmFc2Dgrad: rowgemm_f32_kernel<false, kEpiDgrad2><<<grid, 256, 0, st>>>(P); break;
+      case kGemmFc1Dgrad: rowgemm_f32_kernel<false, kEpiStore><<<grid, 256, 0, st>>>(P); break;
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_wgrad(const WgradParams& P, int which, bool bf16, int64_t grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   if (bf16) {
     if (which == 1)
-      wgrad_kernel<uint16_t, true, false, false, false><<<grid, 256, 0, st>>>(P);
+      wgrad_bf16_kernel<true, false><<<grid, 256, 0, st>>>(P);
     else
-      wgrad_kernel<uint16_t, false, true, true, true><<<grid, 256, 0, st>>>(P);
+      wgrad_bf16_kernel<false, true><<<grid, 256, 0, st>>>(P);
   } else {
     if (which == 1)
-      wgrad_kernel<float, true, false, false, false><<<grid, 256, 0, st>>>(P);
+      wgrad_f32_kernel<true, false><<<grid, 256, 0, st>>>(P);
     else
-      wgrad_kernel<float, false, true, true, true><<<grid, 256, 0, st>>>(P);
+      wgrad_f32_kernel<false, true><<<grid, 256, 0, st>>>(P);
   }
   return hipGetLastError();
 }
@@ -429,7 +714,7 @@ hipError_t launch_wgrad_reduce(const WgradPrepParams& P, int64_t grid, hipStream
   return hipGetLastError();
 }
 
-int gemm_tile_m(bool bf16) { return bf16 ? Tile<uint16_t>::BM : Tile<float>::BM; }
-int gemm_tile_n(bool bf16) { return bf16 ? Tile<uint16_t>::BN : Tile<float>::BN; }
+int gemm_tile_m(bool bf16) { return bf16 ? bf::BM : f32::BM; }
+int gemm_tile_n(bool bf16) { return bf16 ? bf::BN : f32::BN; }
 
 }  // namespace moedet

@@ -14,7 +14,7 @@ constexpr int kMaxChunkRows = 2048;   // upper bound on the wgrad K chunk (rows)
 // Grid size (a multiple of the 8 XCDs) for an upper bound on work units.
 inline int64_t grid_for_units(int64_t U_max) { return ((U_max + 7) / 8) * 8; }
 
-enum { kEpiStore = 0, kEpiDgrad2 = 1 };
+enum { kEpiStore = 0, kEpiDgrad2 = 1, kEpiStoreAct = 2 };
 enum { kGemmFc1Fwd = 0, kGemmFc2Fwd = 1, kGemmFc2Dgrad = 2, kGemmFc1Dgrad = 3 };
 
 struct RowGemmParams {
@@ -24,12 +24,16 @@ struct RowGemmParams {
   int N, K;
   const void* a;
   int64_t lda;
+  uint32_t a_bytes;       // extent of a (buffer range check)
   const int32_t* a_rows;  // A row r reads a[a_rows[r]] when set, a[r] otherwise
   const void* b;
-  int64_t b_gstride;
+  int64_t b_gstride;      // elements between consecutive experts' B
   int64_t ldb;
+  uint32_t b_bytes;       // extent of one expert's B
   void* c;
   int64_t ldc;
+  void* c2;               // second output (a = relu(h)^2, or p*relu(h)^2)
+  int64_t ldc2;
   // fc2 dgrad epilogue
   const void* h;
   int64_t ldh;
@@ -46,14 +50,15 @@ struct WgradParams {
   const int32_t* counts;
   const int32_t* offsets;
   const int32_t* row_tok;
-  const float* row_prob;
   const int32_t* sched;  // unit_start[G+1], slot_base[G+1]
   int groups;
   int M, N;
   const void* a;
   int64_t lda;
+  uint32_t a_bytes;
   const void* b;
   int64_t ldb;
+  uint32_t b_bytes;
   float* dw;
   float* slots;
   int kc;

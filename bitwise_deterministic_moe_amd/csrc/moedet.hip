@@ -49,6 +49,14 @@ moe_status validate(const moe_problem* p, Plan* pl) {
   if (p->d_model <= 0 || p->d_ffn <= 0 || p->d_model % align || p->d_ffn % align) return MOE_ERR_SHAPE;
   if (p->d_ffn / bn > 64) return MOE_ERR_SHAPE;  // dprob partials per row
   if ((int64_t)p->d_model * p->d_ffn >= (int64_t)1 << 31) return MOE_ERR_SHAPE;
+  {
+    // every operand is addressed with 32-bit buffer offsets below 2^31
+    const int64_t es = bf16 ? 2 : 4;
+    const int64_t rc = p->tokens * (int64_t)(p->top_k < p->num_local ? p->top_k : p->num_local);
+    const int64_t wmax = p->d_model > p->d_ffn ? p->d_model : p->d_ffn;
+    if (p->tokens * p->d_model * es >= ((int64_t)1 << 31) || rc * wmax * es >= ((int64_t)1 << 31))
+      return MOE_ERR_SHAPE;
+  }
   if (p->n_stage_events < 0 || (p->n_stage_events > 0 && !p->stage_events)) return MOE_ERR_NULL;
   if (pl) {
     pl->bf16 = bf16;
@@ -80,7 +88,7 @@ moe_status validate(const moe_problem* p, Plan* pl) {
 
 // Workspace layout of each call: a list of aligned regions.
 struct FwdWs {
-  size_t hist, cursor, orows, y32, total;
+  size_t hist, cursor, arows, orows, y32, total;
 };
 struct DgradWs {
   size_t part, dxrows, dx32, total;
@@ -96,6 +104,8 @@ FwdWs fwd_layout(const Plan& pl, int combine, bool atomic) {
   o += align_up((size_t)pl.nchunk * pl.el * 4);
   w.cursor = o;
   o += align_up((size_t)pl.el * 4);
+  w.arows = o;
+  o += align_up((size_t)pl.rows_cap * pl.F * pl.esize);
   w.orows = o;
   if (combine) o += align_up((size_t)pl.rows_cap * pl.D * pl.esize);
   w.y32 = o;
@@ -287,29 +297,37 @@ MOE_API moe_status moe_fwd(const moe_problem* p, const float* logits, const void
   G.groups = pl.el;
   G.seed = seed;
   // fc1: h = x[row_tok] W1_g, W1 [D][F]
+  void* arows = wsb + L.arows;
   G.N = pl.F;
   G.K = pl.D;
   G.a = x;
   G.lda = pl.D;
+  G.a_bytes = (uint32_t)(pl.T * pl.D * pl.esize);
   G.a_rows = routing->row_tok;
   G.b = w1;
   G.b_gstride = (int64_t)pl.D * pl.F;
   G.ldb = pl.F;
+  G.b_bytes = (uint32_t)(G.b_gstride * pl.esize);
   G.c = h;
   G.ldc = pl.F;
+  G.c2 = arows;
+  G.ldc2 = pl.F;
   sg.mark();
   HIP_TRY(launch_rowgemm(G, kGemmFc1Fwd, pl.bf16, rowgemm_grid(pl, pl.F), st));
-  // fc2: o = relu(h)^2 W2_g, W2 [F][D]
+  // fc2: o = a W2_g with a = relu(h)^2 from the fc1 epilogue, W2 [F][D]
   G.N = pl.D;
   G.K = pl.F;
-  G.a = h;
+  G.a = arows;
   G.lda = pl.F;
+  G.a_bytes = (uint32_t)(pl.rows_cap * pl.F * pl.esize);
   G.a_rows = nullptr;
   G.b = w2;
   G.b_gstride = (int64_t)pl.F * pl.D;
   G.ldb = pl.D;
+  G.b_bytes = (uint32_t)(G.b_gstride * pl.esize);
   G.c = orows;
   G.ldc = pl.D;
+  G.c2 = nullptr;
   sg.mark();
   HIP_TRY(launch_rowgemm(G, kGemmFc2Fwd, pl.bf16, rowgemm_grid(pl, pl.D), st));
 
@@ -335,8 +353,8 @@ MOE_API moe_status moe_fwd(const moe_problem* p, const float* logits, const void
 
 MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* routing, const void* dy,
                                        const void* w1, const void* w2, const void* h, void* dx_or_rows,
-                                       float* dprob, void* dh, void* ws, size_t ws_bytes, moe_mode mode,
-                                       void* stream) {
+                                       float* dprob, void* dh, void* act_p, void* ws, size_t ws_bytes,
+                                       moe_mode mode, void* stream) {
   Plan pl;
   moe_status s = validate(p, &pl);
   if (s != MOE_OK) return s;
@@ -345,7 +363,8 @@ MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* 
   const bool has_tok = pl.T > 0, has_rows = pl.rows_cap > 0;
   if (!routing || !w1 || !w2 || !routing->counts || !routing->offsets) return MOE_ERR_NULL;
   if (has_tok && (!dy || !dx_or_rows || !dprob || !routing->slot_row || !routing->topk_prob)) return MOE_ERR_NULL;
-  if (has_rows && (!h || !dh || !routing->row_src || !routing->row_tok || !routing->row_prob)) return MOE_ERR_NULL;
+  if (has_rows && (!h || !dh || !act_p || !routing->row_src || !routing->row_tok || !routing->row_prob))
+    return MOE_ERR_NULL;
   const DgradWs L = dgrad_layout(pl, p->combine, at);
   s = check_ws(ws, ws_bytes, L.total);
   if (s != MOE_OK) return s;
@@ -372,12 +391,16 @@ MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* 
   G.K = pl.D;
   G.a = dy;
   G.lda = pl.D;
+  G.a_bytes = (uint32_t)(pl.T * pl.D * pl.esize);
   G.a_rows = routing->row_tok;
   G.b = w2;
   G.b_gstride = (int64_t)pl.F * pl.D;
   G.ldb = pl.D;
+  G.b_bytes = (uint32_t)(G.b_gstride * pl.esize);
   G.c = dh;
   G.ldc = pl.F;
+  G.c2 = act_p;
+  G.ldc2 = pl.F;
   G.h = h;
   G.ldh = pl.F;
   G.row_prob = routing->row_prob;
@@ -402,10 +425,12 @@ MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* 
   G2.K = pl.F;
   G2.a = dh;
   G2.lda = pl.F;
+  G2.a_bytes = (uint32_t)(pl.rows_cap * pl.F * pl.esize);
   G2.a_rows = nullptr;
   G2.b = w1;
   G2.b_gstride = (int64_t)pl.D * pl.F;
   G2.ldb = pl.F;
+  G2.b_bytes = (uint32_t)(G2.b_gstride * pl.esize);
   G2.c = dxrows;
   G2.ldc = pl.D;
   sg.mark();
@@ -428,7 +453,7 @@ MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* 
 }
 
 MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routing, const void* x,
-                                 const void* dy, const void* h, const void* dh, float* dw1, float* dw2,
+                                 const void* dy, const void* dh, const void* act_p, float* dw1, float* dw2,
                                  void* ws, size_t ws_bytes, moe_mode mode, void* stream) {
   Plan pl;
   moe_status s = validate(p, &pl);
@@ -438,7 +463,7 @@ MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routin
   const bool has_tok = pl.T > 0, has_rows = pl.rows_cap > 0;
   if (!routing || !dw1 || !dw2 || !routing->counts || !routing->offsets) return MOE_ERR_NULL;
   if (has_tok && (!x || !dy)) return MOE_ERR_NULL;
-  if (has_rows && (!h || !dh || !routing->row_tok || !routing->row_prob)) return MOE_ERR_NULL;
+  if (has_rows && (!dh || !act_p || !routing->row_tok)) return MOE_ERR_NULL;
   const WgradWs L = wgrad_layout(pl, at);
   s = check_ws(ws, ws_bytes, L.total);
   if (s != MOE_OK) return s;
@@ -469,7 +494,6 @@ MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routin
   W.counts = routing->counts;
   W.offsets = routing->offsets;
   W.row_tok = routing->row_tok;
-  W.row_prob = routing->row_prob;
   W.sched = sched;
   W.groups = pl.el;
   W.kc = pl.kc;
@@ -478,21 +502,27 @@ MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routin
   // dW1_g [D][F] = x[row_tok]^T dh
   W.M = pl.D;
   W.N = pl.F;
+  const uint32_t rows_f_bytes = (uint32_t)(pl.rows_cap * pl.F * pl.esize);
+  const uint32_t tok_d_bytes = (uint32_t)(pl.T * pl.D * pl.esize);
   W.a = x;
   W.lda = pl.D;
+  W.a_bytes = tok_d_bytes;
   W.b = dh;
   W.ldb = pl.F;
+  W.b_bytes = rows_f_bytes;
   W.dw = dw1;
   W.slots = slots1;
   sg.mark();
   HIP_TRY(launch_wgrad(W, 1, pl.bf16, wgrad_grid(pl, pl.D, pl.F), st));
-  // dW2_g [F][D] = relu(h)^2^T (p * dy[row_tok])
+  // dW2_g [F][D] = (p relu(h)^2)^T dy[row_tok]
   W.M = pl.F;
   W.N = pl.D;
-  W.a = h;
+  W.a = act_p;
   W.lda = pl.F;
+  W.a_bytes = rows_f_bytes;
   W.b = dy;
   W.ldb = pl.D;
+  W.b_bytes = tok_d_bytes;
   W.dw = dw2;
   W.slots = slots2;
   sg.mark();

@@ -93,7 +93,8 @@ typedef enum moe_mode { MOE_DETERMINISTIC = 0, MOE_ATOMIC = 1 } moe_mode;
  *   top_k         k, experts per token (1..min(E,64))
  *   expert_begin, num_local
  *                 the experts held here: [expert_begin, expert_begin+num_local)
- *   dtype         MOE_F32 (D, F multiples of 64) or MOE_BF16 (multiples of 256)
+ *   dtype         MOE_F32 (D, F multiples of 64) or MOE_BF16 (multiples of 256);
+ *                 every [T,D] and [rows_cap,max(D,F)] array below 2 GiB
  *   combine       1: full layer, outputs in token layout ([T,D]; requires
  *                 num_local == num_experts);
  *                 0: expert shard, outputs in row layout ([rows_cap,D]) as an
@@ -200,22 +201,25 @@ moe_status moe_fwd(const moe_problem* p, const float* logits, const void* x, con
  *              adds the partials in N-tile order.  MOE_ATOMIC: each N-tile
  *              adds its partial atomically.
  *   dh         [rows_cap,F] dtype output, p * (dy W2^T) * 2 relu(h); input of
- *              moe_bwd_wgrad */
+ *              moe_bwd_wgrad
+ *   act_p      [rows_cap,F] dtype output, p * relu(h)^2 recomputed from h in
+ *              the same epilogue; input of moe_bwd_wgrad */
 moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* routing, const void* dy,
                                const void* w1, const void* w2, const void* h, void* dx_or_rows,
-                               float* dprob, void* dh, void* ws, size_t ws_bytes, moe_mode mode,
-                               void* stream);
+                               float* dprob, void* dh, void* act_p, void* ws, size_t ws_bytes,
+                               moe_mode mode, void* stream);
 
 /* Backward, weight gradients (float32 outputs, exact zeros for experts
- * without rows):
+ * without rows), from the outputs of moe_bwd_dgrad_dprob:
  *   dw1 [El,D,F] = sum over the expert's rows of x_row^T dh_row
- *   dw2 [El,F,D] = sum over the expert's rows of relu(h_row)^2^T (p_row dy_row)
+ *   dw2 [El,F,D] = sum over the expert's rows of act_p_row^T dy_row
+ *                  (act_p = p * relu(h)^2)
  * An expert with many rows is split along its rows into chunks whose size is
  * a function of the problem shapes only.  MOE_DETERMINISTIC: the chunk
  * partials go to the workspace and are added in chunk order.  MOE_ATOMIC:
  * they are added atomically. */
 moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routing, const void* x,
-                         const void* dy, const void* h, const void* dh, float* dw1, float* dw2,
+                         const void* dy, const void* dh, const void* act_p, float* dw1, float* dw2,
                          void* ws, size_t ws_bytes, moe_mode mode, void* stream);
 
 /* Chunk-wise tensor fingerprint (integer arithmetic; bit-exact).

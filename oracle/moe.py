@@ -108,13 +108,15 @@ def expert_backward(xr, dyr, pr, hr, w1e, w2e) -> dict:
       dx_r    = dh_r W1^T
       dW1     = x^T dh
       dW2     = relu(h)^2^T (p * dy)
+    and act_p = p * relu(h)^2, the activation weighted by the probability
+    (dW2 = act_p^T dy).
     """
     a = _act(hr)
     o = a @ w2e
     dprob = np.sum(dyr * o, axis=1)
     g = dyr @ w2e.T
     dh = pr[:, None] * g * _act_grad(hr)
-    return dict(dprob=dprob, dh=dh, dx_rows=dh @ w1e.T,
+    return dict(dprob=dprob, dh=dh, dx_rows=dh @ w1e.T, act_p=pr[:, None] * a,
                 dw1=xr.T @ dh, dw2=a.T @ (pr[:, None] * dyr))
 
 
@@ -153,7 +155,7 @@ def forward(x, w1, w2, topk_prob, perm, top_k, combine=True) -> dict:
 def backward(x, w1, w2, h, dy, topk_prob, perm, top_k, combine=True) -> dict:
     """Layer backward over the local experts, given the saved h [R,F].
 
-    Returns dprob [T,k] (0 for non-local slots), dh [R,F], dx_rows [R,D],
+    Returns dprob [T,k] (0 for non-local slots), dh [R,F], act_p [R,F], dx_rows [R,D],
     dW1 [El,D,F], dW2 [El,F,D] (exact zeros for empty experts) and, with
     ``combine``, dx [T,D] = sum over slots of dx_rows."""
     T = x.shape[0]
@@ -163,6 +165,7 @@ def backward(x, w1, w2, h, dy, topk_prob, perm, top_k, combine=True) -> dict:
     p_rows = topk_prob.reshape(-1)[row_src]
     dprob_rows = np.zeros(R)
     dh = np.zeros((R, F))
+    act_p = np.zeros((R, F))
     dx_rows = np.zeros((R, D))
     dw1 = np.zeros((El, D, F))
     dw2 = np.zeros((El, F, D))
@@ -173,10 +176,11 @@ def backward(x, w1, w2, h, dy, topk_prob, perm, top_k, combine=True) -> dict:
         rows = row_tok[s:t]
         g = expert_backward(x[rows], dy[rows], p_rows[s:t], h[s:t], w1[e], w2[e])
         dprob_rows[s:t], dh[s:t], dx_rows[s:t] = g["dprob"], g["dh"], g["dx_rows"]
+        act_p[s:t] = g["act_p"]
         dw1[e], dw2[e] = g["dw1"], g["dw2"]
     dprob = np.zeros(T * top_k)
     dprob[row_src] = dprob_rows
-    out = dict(dprob=dprob.reshape(T, top_k), dh=dh, dx_rows=dx_rows, dw1=dw1, dw2=dw2)
+    out = dict(dprob=dprob.reshape(T, top_k), dh=dh, act_p=act_p, dx_rows=dx_rows, dw1=dw1, dw2=dw2)
     if combine:
         out["dx"] = combine_rows(dx_rows, perm["slot_row"], np.ones((T, top_k)), T, top_k)
     return out

@@ -80,13 +80,13 @@ def run_layer(prob: moe.Problem, di: DeviceInputs, mode=moe.DETERMINISTIC, poiso
     out_rows = T if prob.combine else rc
     routing, h, y = moe.moe_fwd(prob, di.logits, di.x, di.w1, di.w2, mode, routing=r,
                                 h=mk((rc, F), dt), y=mk((out_rows, D), dt), ws=ws[0])
-    dx, dprob, dh = moe.moe_bwd_dgrad_dprob(prob, routing, di.dy, di.w1, di.w2, h, mode,
-                                            dx=mk((out_rows, D), dt), dprob=mk((T, k), torch.float32),
-                                            dh=mk((rc, F), dt), ws=ws[1])
-    dw1, dw2 = moe.moe_bwd_wgrad(prob, routing, di.x, di.dy, h, dh, mode, dw1=mk((el, D, F), torch.float32),
+    dx, dprob, dh, act_p = moe.moe_bwd_dgrad_dprob(prob, routing, di.dy, di.w1, di.w2, h, mode,
+                                                   dx=mk((out_rows, D), dt), dprob=mk((T, k), torch.float32),
+                                                   dh=mk((rc, F), dt), act_p=mk((rc, F), dt), ws=ws[1])
+    dw1, dw2 = moe.moe_bwd_wgrad(prob, routing, di.x, di.dy, dh, act_p, mode, dw1=mk((el, D, F), torch.float32),
                                  dw2=mk((el, F, D), torch.float32), ws=ws[2])
     torch.cuda.synchronize()
-    return dict(routing=routing, h=h, y=y, dx=dx, dprob=dprob, dh=dh, dw1=dw1, dw2=dw2)
+    return dict(routing=routing, h=h, y=y, dx=dx, dprob=dprob, dh=dh, act_p=act_p, dw1=dw1, dw2=dw2)
 
 
 def oracle_layer(cfg, host: dict) -> dict:
@@ -131,6 +131,7 @@ def compare_layer(cfg, out: dict, ref: dict, tol=None):
         errs["dx"] = rel_l2(to_host(out["dx"])[:R], ref["dx_rows"])
     errs["dprob"] = rel_l2(to_host(out["dprob"]), ref["dprob"])
     errs["dh"] = rel_l2(to_host(out["dh"])[:R], ref["dh"])
+    errs["act_p"] = rel_l2(to_host(out["act_p"])[:R], ref["act_p"])
     errs["dw1"] = rel_l2(to_host(out["dw1"]), ref["dw1"])
     errs["dw2"] = rel_l2(to_host(out["dw2"]), ref["dw2"])
     bad = {k: v for k, v in errs.items() if not v <= tol}
@@ -146,7 +147,7 @@ def compare_layer(cfg, out: dict, ref: dict, tol=None):
     return errs
 
 
-FP_OUTPUTS = ("h", "y", "dx", "dprob", "dh", "dw1", "dw2")
+FP_OUTPUTS = ("h", "y", "dx", "dprob", "dh", "act_p", "dw1", "dw2")
 FP_ROUTING = ("topk_idx", "topk_prob", "counts", "offsets", "row_src", "row_tok", "row_prob", "slot_row")
 
 
@@ -155,7 +156,7 @@ def fingerprints(out: dict, combine: int) -> dict:
     Row-layout tensors are hashed over their R written rows only."""
     r = out["routing"]
     R = r.rows
-    rowwise = {"h", "dh"} | (set() if combine else {"y", "dx"})
+    rowwise = {"h", "dh", "act_p"} | (set() if combine else {"y", "dx"})
     fp = {}
     for n in FP_OUTPUTS:
         t = out[n][:R] if n in rowwise else out[n]
@@ -183,6 +184,7 @@ def compare_layer_unordered(cfg, out: dict, ref: dict, tol=None):
     np.testing.assert_array_equal(to_host(r.slot_row)[src], np.arange(R))
     errs = dict(h=rel_l2(to_host(out["h"])[:R], ref["h"][ref_row]),
                 dh=rel_l2(to_host(out["dh"])[:R], ref["dh"][ref_row]),
+                act_p=rel_l2(to_host(out["act_p"])[:R], ref["act_p"][ref_row]),
                 dprob=rel_l2(to_host(out["dprob"]), ref["dprob"]),
                 dw1=rel_l2(to_host(out["dw1"]), ref["dw1"]), dw2=rel_l2(to_host(out["dw2"]), ref["dw2"]))
     if cfg.combine:

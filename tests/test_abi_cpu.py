@@ -80,8 +80,11 @@ def test_null_and_workspace_errors_return_before_enqueue(lib):
     # misaligned workspace
     assert lib.moe_bwd_wgrad(ctypes.byref(cp), ctypes.byref(r), fake, fake, fake, fake, fake, fake,
                              ctypes.c_void_p(0x1008), 1 << 40, 0, None) == 4
-    assert lib.moe_bwd_dgrad_dprob(None, ctypes.byref(r), fake, fake, fake, fake, fake, fake, fake, fake, 0, 0,
-                                   None) == 1
+    assert lib.moe_bwd_dgrad_dprob(None, ctypes.byref(r), fake, fake, fake, fake, fake, fake, fake, fake, fake, 0,
+                                   0, None) == 1
+    # NULL act_p
+    assert lib.moe_bwd_dgrad_dprob(ctypes.byref(cp), ctypes.byref(r), fake, fake, fake, fake, fake, fake, fake, None,
+                                   fake, 1 << 40, 0, None) == 1
     # fingerprint argument checks
     shape = (ctypes.c_int64 * 1)(10)
     assert lib.moe_fingerprint(fake, 9, 1, shape, 4, fake, fake, None) == 3

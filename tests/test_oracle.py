@@ -200,6 +200,18 @@ def test_gradients_finite_difference(name):
     np.testing.assert_allclose(ref, g, rtol=1e-6, atol=1e-7)
 
 
+def test_act_p_gives_dw2():
+    """dW2 of an expert equals act_p^T dy over its rows, act_p = p relu(h)^2."""
+    x, w1, w2, dy, idx, prob, perm, fwd, bwd = _setup_small(seed=13)
+    off = perm["offsets"]
+    p_rows = prob.reshape(-1)[perm["row_src"]]
+    np.testing.assert_allclose(bwd["act_p"], p_rows[:, None] * np.maximum(fwd["h"], 0) ** 2, rtol=1e-14)
+    for e in range(w1.shape[0]):
+        s, t = off[e], off[e + 1]
+        np.testing.assert_allclose(bwd["act_p"][s:t].T @ dy[perm["row_tok"][s:t]], bwd["dw2"][e], rtol=1e-12,
+                                   atol=1e-14)
+
+
 def test_dx_rows_sum_to_dx_and_empty_expert_zero():
     rng = np.random.default_rng(9)
     T, E, k = 10, 5, 2
