@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
                     help="run warmup + timed steps only (for rocprofv3 runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (calibrates the "
+                         "FETCH_SIZE / WRITE_SIZE counters against known bytes)")
     return ap.parse_args()
 
 
@@ -51,6 +54,16 @@ def main():
         sys.exit(2)
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4}))
+        return
 
     import bitwise_deterministic_moe_amd as moe
     from synth import CONFIGS, make_inputs
@@ -185,13 +198,41 @@ def main():
         "stages_ms_det": {k: round(v, 5) for k, v in st_det.items()},
         "stages_ms_atomic": {k: round(v, 5) for k, v in st_atom.items()},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "flops_per_launch": gemm_flops},
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(dom) if args.config == "bf16_e8k2" else None,
+                     "flops_per_launch": gemm_flops, "ms_per_launch": round(dom_ms, 5)},
     }
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, host, flops)
     print(json.dumps(result), flush=True)
+
+
+def measured_traffic(stage):
+    """HBM bytes per launch of `stage` from profiles/bench_bf16_e8k2_hbm_traffic.txt
+    (rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by a plain-copy calibration), or
+    None when the library source changed since those counters were taken."""
+    import glob
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "bench_bf16_e8k2_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    m = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "bitwise_deterministic_moe_amd", "csrc", "*"))):
+        m.update(os.path.basename(f).encode())
+        m.update(open(f, "rb").read())
+    fields = {}
+    for line in open(path):
+        parts = line.split()
+        if not parts or parts[0].startswith("#"):
+            continue
+        if parts[0] == "stage" and len(parts) >= 8:
+            fields[("stage", parts[1])] = float(parts[7])
+        elif len(parts) == 2:
+            fields[parts[0]] = parts[1]
+    if fields.get("csrc_sha256") != m.hexdigest()[:16]:
+        return None
+    return fields.get(("stage", stage))
 
 
 def cpu_baseline(cfg, host, gpu_flops):
