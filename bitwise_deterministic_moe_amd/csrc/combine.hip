@@ -76,27 +76,38 @@ __global__ __launch_bounds__(256) void gather_combine_kernel(const T* rows, cons
   Vec<T>::store(out + t * D + d, acc);
 }
 
+// One wave per (row, segment of 64*V elements); instruction q of the wave
+// adds elements q*64 + lane, so every atomic instruction covers 64
+// consecutive floats (256 bytes) and every load 64 consecutive elements.
 template <typename T>
 __global__ __launch_bounds__(256) void scatter_add_kernel(const T* rows, const int32_t* offsets, int el,
                                                           const int32_t* row_tok, const float* row_prob,
                                                           int64_t rows_cap, int D, float* out32,
                                                           uint64_t seed) {
-  constexpr int V = Vec<T>::N;
-  const int per_row = D / V;
+  constexpr int V = sizeof(T) == 2 ? 4 : 1;
+  const int per_row = D / (64 * V);
   const int64_t R = offsets[el];
-  const int64_t units = (R * per_row + 255) / 256;
+  const int64_t units = (rows_cap * per_row + 3) / 4;
   const int64_t u = map_unit(blockIdx.x, units, seed);
   if (u < 0) return;
-  const int64_t idx = u * 256 + threadIdx.x;
-  if (idx >= R * per_row) return;
-  const int64_t r = idx / per_row;
-  const int d = (int)(idx % per_row) * V;
+  const int lane = threadIdx.x & 63;
+  const int64_t wu = u * 4 + (threadIdx.x >> 6);
+  if (wu >= R * per_row) return;
+  const int64_t r = wu / per_row;
+  const int base = (int)(wu % per_row) * 64 * V + lane;
   const float w = row_prob ? row_prob[r] : 1.f;
+  const T* src = rows + r * D + base;
+  float* o = out32 + (int64_t)row_tok[r] * D + base;
   float f[V];
-  Vec<T>::load(rows + r * D + d, f);
-  float* o = out32 + (int64_t)row_tok[r] * D + d;
 #pragma unroll
-  for (int q = 0; q < V; ++q) atomicAdd(o + q, row_prob ? w * f[q] : f[q]);
+  for (int q = 0; q < V; ++q) {
+    if constexpr (sizeof(T) == 2)
+      f[q] = bf16_to_f32(src[q * 64]);
+    else
+      f[q] = src[q * 64];
+  }
+#pragma unroll
+  for (int q = 0; q < V; ++q) atomicAdd(o + q * 64, row_prob ? w * f[q] : f[q]);
 }
 
 template <typename T>
@@ -154,8 +165,8 @@ hipError_t launch_gather_combine(const void* rows, const int32_t* slot_row, cons
 hipError_t launch_scatter_add(const void* rows, const int32_t* offsets, int el, const int32_t* row_tok,
                               const float* row_prob, int64_t rows_cap, int D, float* out32, bool bf16,
                               uint64_t seed, hipStream_t st) {
-  const int V = bf16 ? 8 : 4;
-  const int64_t units = (rows_cap * (D / V) + 255) / 256;
+  const int per_row = D / (64 * (bf16 ? 4 : 1));
+  const int64_t units = (rows_cap * per_row + 3) / 4;
   if (units <= 0) return hipSuccess;
   const int64_t grid = grid_for_units(units);
   if (bf16)

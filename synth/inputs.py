@@ -15,6 +15,7 @@ Nothing here implements the method (routing, expert MLP, combine, hashing).
 """
 import json
 import os
+import threading
 from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
@@ -80,14 +81,36 @@ def make_logits(cfg: Config, beta: float = None) -> np.ndarray:
 
 
 def make_expert_weights(cfg: Config, which: str, experts) -> np.ndarray:
-    """Weights of the given global expert indices: w1 [n, D, F] or w2 [n, F, D]."""
+    """Weights of the given global expert indices: w1 [n, D, F] or w2 [n, F, D].
+
+    Same values as ``_draw`` on each expert's own stream; the draw and the
+    rounding run in per-thread scratch buffers so that large expert counts
+    do not spend their time allocating."""
     D, F = cfg.d_model, cfg.d_ffn
     shape = (D, F) if which == "w1" else (F, D)
     experts = list(experts)
     out = np.empty((len(experts),) + shape, dtype=np.uint16 if cfg.dtype == "bf16" else np.float32)
+    local = threading.local()
 
     def one(i):
-        out[i] = _draw(_rng(cfg.seed, which, experts[i]), shape, cfg.w_std, cfg.dtype)
+        if not hasattr(local, "f"):
+            local.f = np.empty(shape, dtype=np.float32)
+            local.u = np.empty(shape, dtype=np.uint32)
+        f, u = local.f, local.u
+        _rng(cfg.seed, which, experts[i]).standard_normal(dtype=np.float32, out=f)
+        if cfg.w_std != 1.0:
+            f *= np.float32(cfg.w_std)
+        if cfg.dtype != "bf16":
+            out[i] = f
+            return
+        # round to nearest even, as f32_to_bf16_bits
+        b = f.view(np.uint32)
+        np.right_shift(b, np.uint32(16), out=u)
+        u &= np.uint32(1)
+        u += np.uint32(0x7FFF)
+        u += b
+        u >>= np.uint32(16)
+        out[i] = u
 
     if len(experts) > 4:
         with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:

@@ -1,0 +1,205 @@
+"""Full-size workloads (LatentMoE 512 experts top-22, the skewed-routing
+variant, and one GPU's 4-expert shard of a 16384-token layer) against the
+oracle.
+
+At these sizes the fp64 oracle cannot evaluate the whole layer in seconds,
+so every check is one the oracle can do piecewise on the same inputs:
+  * routing state (top-k indices, counts, offsets, row maps) for the whole
+    layer, bit-exact; probabilities to 1e-5;
+  * sampled experts: every row of h, dh, act_p (and the row outputs of the
+    shard) plus the complete dW1/dW2 matrices of the expert;
+  * sampled tokens: y_t, dx_t and dprob_t of the token-layout workloads,
+    each evaluated through the token's k experts;
+  * every expert and every token through identities that hold at any size:
+    o is homogeneous of degree 2 in (x, W1) and of degree 1 in W2, so with
+    L_e = sum_{r in e} p_r dprob_r the outputs must satisfy
+    <dW1_e, W1_e> = 2 L_e, <dW2_e, W2_e> = L_e and
+    <dx_t, x_t> = 2 sum_j p_tj dprob_tj;
+  * empty experts exact zero dW, non-local dprob slots exact zero;
+  * bit-identical outputs (fingerprints) under a shuffled launch order.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bitwise_deterministic_moe_amd as moe
+import oracle
+from synth import CONFIGS, make_inputs
+from synth.inputs import make_expert_weights
+from harness import DeviceInputs, compare_routing, fingerprints, rel_l2, run_layer, to_host
+
+pytestmark = pytest.mark.gpu
+
+LARGE = ["latent_e512k22", "skewed_e512k22", "shard_e512k22_l4"]
+N_TOKENS = 48
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.load_library()
+
+
+def _sample_experts(counts: np.ndarray, rng) -> list:
+    """Heaviest, lightest non-empty, first, last, an empty one (if any) and two
+    random experts."""
+    el = len(counts)
+    nz = np.nonzero(counts)[0]
+    pick = {int(np.argmax(counts)), int(nz[np.argmin(counts[nz])]), 0, el - 1}
+    empty = np.nonzero(counts == 0)[0]
+    if len(empty):
+        pick.add(int(empty[0]))
+    pick.update(int(e) for e in rng.choice(el, size=min(2, el), replace=False))
+    return sorted(pick)
+
+
+def _weights(cfg, host, e_local):
+    """float64 weights of local expert e_local, drawn from the seeded generator
+    (the same stream the device copy came from)."""
+    g = cfg.expert_begin + e_local
+    w1 = oracle.decode(make_expert_weights(cfg, "w1", [g])[0], cfg.dtype)
+    w2 = oracle.decode(make_expert_weights(cfg, "w2", [g])[0], cfg.dtype)
+    return w1, w2
+
+
+def _expert_checks(cfg, host, perm, prob, out, experts):
+    """Oracle evaluation of every row and the full weight gradient of each
+    sampled expert; returns (gpu, ref) lists per quantity."""
+    x = oracle.decode(host["x"], cfg.dtype)
+    dy = oracle.decode(host["dy"], cfg.dtype)
+    off, row_tok, row_src = perm["offsets"], perm["row_tok"], perm["row_src"]
+    p_rows = prob.reshape(-1)[row_src]
+    acc = {n: ([], []) for n in ("h", "dh", "act_p", "dw1", "dw2", "rows_o", "rows_dx")}
+    for e in experts:
+        s, t = int(off[e]), int(off[e + 1])
+        g_dw1 = to_host(out["dw1"][e])
+        g_dw2 = to_host(out["dw2"][e])
+        if t == s:
+            assert np.all(g_dw1 == 0) and np.all(g_dw2 == 0), f"empty expert {e} must have exact zero dW"
+            continue
+        w1, w2 = _weights(cfg, host, e)
+        xr, dyr = x[row_tok[s:t]], dy[row_tok[s:t]]
+        h, o = oracle.expert_forward(xr, w1, w2)
+        b = oracle.expert_backward(xr, dyr, p_rows[s:t], h, w1, w2)
+        pairs = [("h", out["h"][s:t], h), ("dh", out["dh"][s:t], b["dh"]),
+                 ("act_p", out["act_p"][s:t], b["act_p"]), ("dw1", out["dw1"][e], b["dw1"]),
+                 ("dw2", out["dw2"][e], b["dw2"])]
+        if not cfg.combine:
+            pairs += [("rows_o", out["y"][s:t], o), ("rows_dx", out["dx"][s:t], b["dx_rows"])]
+        for n, gt, ref in pairs:
+            acc[n][0].append(to_host(gt).ravel())
+            acc[n][1].append(np.asarray(ref).ravel())
+    return acc
+
+
+def _token_checks(cfg, host, idx, prob, out, tokens):
+    """y_t, dx_t and dprob_t of sampled tokens through their k experts."""
+    x = oracle.decode(host["x"], cfg.dtype)
+    dy = oracle.decode(host["dy"], cfg.dtype)
+    cache = {}
+    ys, dxs, dps = [], [], []
+    for t in tokens:
+        y = np.zeros(cfg.d_model)
+        dx = np.zeros(cfg.d_model)
+        dp = np.zeros(cfg.top_k)
+        for j in range(cfg.top_k):
+            e = int(idx[t, j]) - cfg.expert_begin
+            if not 0 <= e < cfg.num_local:
+                continue
+            if e not in cache:
+                cache[e] = _weights(cfg, host, e)
+            w1, w2 = cache[e]
+            h, o = oracle.expert_forward(x[t:t + 1], w1, w2)
+            b = oracle.expert_backward(x[t:t + 1], dy[t:t + 1], prob[t, j:j + 1], h, w1, w2)
+            y += prob[t, j] * o[0]
+            dx += b["dx_rows"][0]
+            dp[j] = b["dprob"][0]
+        ys.append(y)
+        dxs.append(dx)
+        dps.append(dp)
+    got_dp = to_host(out["dprob"])[tokens]
+    res = dict(dprob=(got_dp.ravel(), np.concatenate(dps)))
+    if cfg.combine:
+        res["y"] = (to_host(out["y"])[tokens].ravel(), np.concatenate(ys))
+        res["dx"] = (to_host(out["dx"])[tokens].ravel(), np.concatenate(dxs))
+    return res
+
+
+def _euler(cfg, di, out, routing):
+    """Homogeneity identities over every expert (and token), evaluated in
+    float64 on the device from the outputs alone."""
+    R = routing.rows
+    counts = routing.counts.long()
+    offs = routing.offsets.long()
+    dprob_rows = out["dprob"].reshape(-1)[routing.row_src[:R].long()].double()
+    lp = dprob_rows * routing.row_prob[:R].double()
+    seg = torch.repeat_interleave(torch.arange(cfg.num_local, device=lp.device), counts)
+    L_e = torch.zeros(cfg.num_local, dtype=torch.float64, device=lp.device).index_add_(0, seg, lp)
+    assert int(offs[-1]) == R
+    lhs1 = torch.empty(cfg.num_local, dtype=torch.float64, device=lp.device)
+    lhs2 = torch.empty_like(lhs1)
+    for e in range(cfg.num_local):
+        lhs1[e] = (out["dw1"][e].double() * di.w1[e].double()).sum()
+        lhs2[e] = (out["dw2"][e].double() * di.w2[e].double()).sum()
+    res = dict(euler_w1=rel_l2(lhs1.cpu().numpy(), 2 * L_e.cpu().numpy()),
+               euler_w2=rel_l2(lhs2.cpu().numpy(), L_e.cpu().numpy()))
+    if cfg.combine:
+        xdx = (out["dx"].double() * di.x.double()).sum(dim=1)
+        pdp = 2 * (routing.topk_prob.double() * out["dprob"].double()).sum(dim=1)
+        res["euler_x"] = rel_l2(xdx.cpu().numpy(), pdp.cpu().numpy())
+    return res
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_large_parity_and_determinism(name):
+    cfg = CONFIGS[name]
+    print(f"[{name}] drawing inputs", flush=True)
+    host = make_inputs(cfg)
+    di = DeviceInputs(cfg, host)
+    prob = moe.Problem.from_config(cfg)
+    print(f"[{name}] HIP path (deterministic)", flush=True)
+    out = run_layer(prob, di)
+    r = out["routing"]
+
+    # routing, whole layer, bit-exact
+    idx, p = oracle.route(host["logits"], cfg.top_k)
+    perm = oracle.permute(idx, cfg.expert_begin, cfg.num_local)
+    compare_routing(r, dict(topk_idx=idx, topk_prob=p, perm=perm))
+    R = int(perm["offsets"][-1])
+    assert R == r.rows
+    if cfg.combine:
+        assert R == cfg.tokens * cfg.top_k
+
+    rng = np.random.default_rng([cfg.seed, 99])
+    experts = _sample_experts(perm["counts"], rng)
+    tokens = np.unique(np.concatenate([[0, cfg.tokens - 1], rng.choice(cfg.tokens, N_TOKENS, replace=False)]))
+    print(f"[{name}] oracle on experts {experts} and {len(tokens)} tokens", flush=True)
+    errs = {}
+    for n, (g, ref) in _expert_checks(cfg, host, perm, p, out, experts).items():
+        if g:
+            errs[n] = rel_l2(np.concatenate(g), np.concatenate(ref))
+    for n, (g, ref) in _token_checks(cfg, host, idx, p, out, tokens).items():
+        errs[n] = rel_l2(g, ref)
+    errs.update(_euler(cfg, di, out, r))
+    print(f"[{name}] rel-L2 {errs}", flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= 2e-2}
+    assert not bad, f"rel-L2 above 2e-2: {bad}"
+
+    dp = to_host(out["dprob"])
+    assert np.all(dp[perm["slot_row"].reshape(dp.shape) < 0] == 0)
+    empty = np.nonzero(perm["counts"] == 0)[0]
+    if name == "skewed_e512k22":
+        assert len(empty) > 0 and perm["counts"].max() > 4 * 512, "skewed workload must split and hold empty experts"
+    if len(empty):
+        ei = torch.as_tensor(empty, device="cuda")
+        assert torch.all(out["dw1"][ei] == 0) and torch.all(out["dw2"][ei] == 0)
+
+    # bit identity under a shuffled workgroup order with launch delays
+    fp0 = fingerprints(out, cfg.combine)
+    del out
+    torch.cuda.empty_cache()
+    print(f"[{name}] shuffled rerun", flush=True)
+    out2 = run_layer(prob.with_seed(0x5EED), di)
+    fp1 = fingerprints(out2, cfg.combine)
+    diff = [n for n in fp0 if fp0[n] != fp1[n]]
+    assert not diff, f"outputs differ under a shuffled launch order: {diff}"
