@@ -321,16 +321,19 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
   __shared__ int s_pre[kMaxExperts + 1];
   __shared__ int s_tmp[8];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t ring = bf::lds_base(lds);
   const int wm = wave >> 1, wn = wave & 1;
   RowTile t;
   if (!row_tile<bf::BM, bf::BN>(P, s_pre, s_tmp, t)) return;
 
   bf::KcOperand oa;
+  // Branch-free so that the four row-index loads of a thread are in flight
+  // together (the tile holds at least one valid row).
   oa.init(P.a, P.a_bytes, wave, lane, [&](int r) -> uint32_t {
-    if (r >= t.mvalid) return bf::kOOB;
-    const int64_t row = P.a_rows ? (int64_t)P.a_rows[t.off + t.m0 + r] : t.off + t.m0 + r;
-    return (uint32_t)(row * P.lda * 2);
+    const int rc = r < t.mvalid ? r : t.mvalid - 1;
+    const int64_t row = P.a_rows ? (int64_t)P.a_rows[t.off + t.m0 + rc] : t.off + t.m0 + rc;
+    return r < t.mvalid ? (uint32_t)(row * P.lda * 2) : bf::kOOB;
   });
   const uint16_t* Bg = (const uint16_t*)P.b + (int64_t)t.g * P.b_gstride;
   f32x16_t acc[4][4];
@@ -344,17 +347,24 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
   if constexpr (BL == bf::KC) {
     bf::KcOperand ob;
     ob.init(Bg, P.b_bytes, wave, lane, [&](int r) -> uint32_t { return (uint32_t)((t.n0 + r) * P.ldb * 2); });
-    bf::mainloop<bf::KC, bf::KC>(lds, nsteps, [&](int s, uint16_t* st) {
-      oa.issue(st, wave, s * bf::BK);
-      ob.issue(st + bf::OPER, wave, s * bf::BK);
+    bf::mainloop<bf::KC, bf::KC>(lds, ring, nsteps, [&](int s, uint32_t st, int i) {
+      if (i < bf::LOADS)
+        oa.issue1(st, wave, s * bf::BK, s < nsteps, i);
+      else
+        ob.issue1(st + bf::OPER * 2, wave, s * bf::BK, s < nsteps, i - bf::LOADS);
     }, acc, wm, wn, lane);
   } else {
     bf::MncOperand ob;
     ob.init(Bg, P.b_bytes, wave, lane, t.n0);
-    bf::mainloop<bf::KC, bf::MNC>(lds, nsteps, [&](int s, uint16_t* st) {
-      oa.issue(st, wave, s * bf::BK);
-      ob.issue(st + bf::OPER, wave, lane,
-               [&](int k) -> uint32_t { return (uint32_t)((s * bf::BK + k) * P.ldb * 2); });
+    bf::mainloop<bf::KC, bf::MNC>(lds, ring, nsteps, [&](int s, uint32_t st, int i) {
+      if (i < bf::LOADS) {
+        oa.issue1(st, wave, s * bf::BK, s < nsteps, i);
+      } else {
+        const int j = i - bf::LOADS;
+        const uint32_t ro =
+            s < nsteps ? (uint32_t)((s * bf::BK + bf::MncOperand::krow(wave, lane, j)) * P.ldb * 2) : bf::kOOB;
+        ob.issue1(st + bf::OPER * 2, wave, ro, j);
+      }
     }, acc, wm, wn, lane);
   }
   float* stage = (float*)lds;
@@ -455,7 +465,8 @@ template <bool A_GATHER, bool B_GATHER>
 __global__ __launch_bounds__(256) void wgrad_bf16_kernel(WgradParams P) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
   __shared__ int s_tok[kMaxChunkRows];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t ring = bf::lds_base(lds);
   const int wm = wave >> 1, wn = wave & 1;
   WgradTile t;
   if (!wgrad_tile<bf::BM, bf::BN>(P, t)) return;
@@ -473,15 +484,32 @@ __global__ __launch_bounds__(256) void wgrad_bf16_kernel(WgradParams P) {
   oa.init(P.a, P.a_bytes, wave, lane, t.m0);
   ob.init(P.b, P.b_bytes, wave, lane, t.n0);
   const int nsteps = (t.klen + bf::BK - 1) / bf::BK;
-  bf::mainloop<bf::MNC, bf::MNC>(lds, nsteps, [&](int s, uint16_t* st) {
-    auto rowoff = [&](int k, bool gather, int64_t ld) -> uint32_t {
-      const int kk = s * bf::BK + k;
-      if (kk >= t.klen) return bf::kOOB;
-      const int64_t r = gather ? (int64_t)s_tok[kk] : t.row0 + kk;
-      return (uint32_t)(r * ld * 2);
-    };
-    oa.issue(st, wave, lane, [&](int k) { return rowoff(k, A_GATHER, P.lda); });
-    ob.issue(st + bf::OPER, wave, lane, [&](int k) { return rowoff(k, B_GATHER, P.ldb); });
+  // Byte offsets of the k rows this lane loads.  The gathered operand's
+  // token index of slice s+1 is read from LDS while slice s is issued, so
+  // the issue never waits on that read.
+  // (Rows past the chunk read an in-range entry and are masked at issue.)
+  int tok[bf::LOADS];
+  auto fetch_tok = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < bf::LOADS; ++i) {
+      const int kk = s * bf::BK + bf::MncOperand::krow(wave, lane, i);
+      tok[i] = s_tok[kk < t.klen ? kk : (t.klen > 0 ? t.klen - 1 : 0)];
+    }
+  };
+  fetch_tok(0);
+  bf::mainloop<bf::MNC, bf::MNC>(lds, ring, nsteps, [&](int s, uint32_t st, int i) {
+    const int j = i & (bf::LOADS - 1);
+    const int kk = s * bf::BK + bf::MncOperand::krow(wave, lane, j);
+    const bool ok = kk < t.klen;
+    const uint32_t direct = (uint32_t)(t.row0 + kk);
+    if (i < bf::LOADS) {
+      const uint32_t r = A_GATHER ? (uint32_t)tok[j] : direct;
+      oa.issue1(st, wave, ok ? r * (uint32_t)P.lda * 2u : bf::kOOB, j);
+    } else {
+      const uint32_t r = B_GATHER ? (uint32_t)tok[j] : direct;
+      ob.issue1(st + bf::OPER * 2, wave, ok ? r * (uint32_t)P.ldb * 2u : bf::kOOB, j);
+    }
+    if (i == 2 * bf::LOADS - 1) fetch_tok(s + 1);
   }, acc, wm, wn, lane);
   float* dst = wgrad_dst(P, t);
   const bool atomic_add = P.atomic && t.S > 1;

@@ -56,16 +56,20 @@ DEV i32x4_t make_rsrc(const void* base, uint32_t bytes) {
   return i32x4_t{(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), (int)bytes, 0x00020000};
 }
 
-DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const LDS_AS void*)p; }
+// LDS byte address of a __shared__ object (a link-time constant).
+template <class T>
+DEV uint32_t lds_base(T* p) {
+  return (uint32_t)(uintptr_t)(LDS_AS T*)p;
+}
 
 // One 16-byte-per-lane DMA load HBM -> LDS: lane i's data lands at
 // lds + 16*i.  Issued through asm so that the compiler does not insert a
 // full vmcnt wait before every later LDS read; the main loop counts the
-// outstanding loads itself.
+// outstanding loads itself.  ``lds`` and ``soff`` are wave-uniform.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 DEV void dma16(i32x4_t rs, uint32_t lds, uint32_t voff, uint32_t soff) {
-  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform by construction
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
   const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
@@ -77,10 +81,14 @@ DEV void dma16(i32x4_t rs, uint32_t lds, uint32_t voff, uint32_t soff) {
 // Wait until at most N of this thread's DMA loads are outstanding, then
 // meet the other waves.  The asm keeps the compiler from moving LDS reads
 // across.
-DEV void wait_barrier(int n_outstanding) {
-  if (n_outstanding >= 16)
+template <int N>
+DEV void wait_barrier() {
+  static_assert(N == 0 || N == 8 || N == 12 || N == 16, "vmcnt");
+  if constexpr (N == 16)
     asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-  else if (n_outstanding >= 8)
+  else if constexpr (N == 12)
+    asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8)
     asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
@@ -123,6 +131,29 @@ DEV void load_frags(Frags& f, const uint16_t* st, int kk, int wm, int wn, int la
   for (int i = 0; i < 4; ++i) f.b[i] = frag<BL>(st + OPER, wn * 128 + i * 32, kk, lane);
 }
 
+// Fragment reads and MFMAs of a k-half in 8 groups.  Group g reads block
+// A0 B0 B1 A1 B2 B3 A2 A3 [g] and issues MFMA pair g:
+//   (A0;B0,B1) (A1;B0,B1) (A0;B2,B3) (A1;B2,B3) (A2;B0,B1) (A2;B2,B3) (A3;B0,B1) (A3;B2,B3)
+// so the pair of group g only needs blocks read by groups 0..g+1 of the
+// previous phase, never the reads issued last.
+template <int AL, int BL>
+DEV void load_frag(Frags& f, const uint16_t* st, int kk, int wm, int wn, int lane, int g) {
+  constexpr int kA[8] = {0, -1, -1, 1, -1, -1, 2, 3};
+  constexpr int kB[8] = {-1, 0, 1, -1, 2, 3, -1, -1};
+  if (kA[g] >= 0)
+    f.a[kA[g]] = frag<AL>(st, wm * 128 + kA[g] * 32, kk, lane);
+  else
+    f.b[kB[g]] = frag<BL>(st + OPER, wn * 128 + kB[g] * 32, kk, lane);
+}
+
+DEV void mma2(const Frags& f, f32x16_t (&acc)[4][4], int g) {
+  constexpr int kM[8] = {0, 1, 0, 1, 2, 2, 3, 3};
+  constexpr int kN[8] = {0, 0, 2, 2, 0, 2, 0, 2};
+  const int mb = kM[g], nb = kN[g];
+  acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[nb], f.a[mb], acc[mb][nb], 0, 0, 0);
+  acc[mb][nb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[nb + 1], f.a[mb], acc[mb][nb + 1], 0, 0, 0);
+}
+
 DEV void mma16(const Frags& f, f32x16_t (&acc)[4][4]) {
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -154,10 +185,11 @@ struct KcOperand {
       voff[i] = ro == kOOB ? kOOB : ro + (uint32_t)c * 16u;
     }
   }
-  DEV void issue(uint16_t* stage_base, int wave, int k0) const {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i)
-      dma16(rs, lds_addr(stage_base + (wave * LOADS + i) * 512), voff[i], (uint32_t)k0 * 2u);
+  // Load i of this operand for the slice at K offset k0; lds: byte address
+  // of the operand's tile in the slot (uniform); live == false issues the
+  // load past the buffer end.
+  DEV void issue1(uint32_t lds, int wave, int k0, bool live, int i) const {
+    dma16(rs, lds + (wave * LOADS + i) * 1024, live ? voff[i] : kOOB, live ? (uint32_t)k0 * 2u : 0u);
   }
 };
 
@@ -175,47 +207,73 @@ struct MncOperand {
     }
   }
   // krowoff(k) -> byte offset of k row (k relative to the stage start) or kOOB
-  template <class KRowOff>
-  DEV void issue(uint16_t* stage_base, int wave, int lane, KRowOff krowoff) const {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int k = 2 * (wave * LOADS + i) + (lane >> 5);
-      const uint32_t ro = krowoff(k);
-      dma16(rs, lds_addr(stage_base + (wave * LOADS + i) * 512), ro == kOOB ? kOOB : ro + mnoff[i], 0u);
-    }
+  // k row handled by this lane in load i
+  DEV static int krow(int wave, int lane, int i) { return 2 * (wave * LOADS + i) + (lane >> 5); }
+  // Load i; ro: byte offset of k row krow(i) of the slice, or kOOB.
+  DEV void issue1(uint32_t lds, int wave, uint32_t ro, int i) const {
+    dma16(rs, lds + (wave * LOADS + i) * 1024, ro == kOOB ? kOOB : ro + mnoff[i], 0u);
   }
 };
 
-// Pipelined main loop over nsteps K slices.  issue(s, stage_ptr) must issue
-// exactly 2*LOADS DMA loads per thread (A into stage_ptr, B into
-// stage_ptr + OPER).
+// Pipelined main loop over nsteps K slices through a ring of NSTAGE LDS
+// slots.  issue(s, lds, i) issues DMA load i (0..3 of A, 4..7 of B) of
+// slice s into the slot at LDS byte address lds; loads of a slice are
+// requested in order i = 0..7 and slices in increasing order.  For
+// s >= nsteps every load must carry an offset past the buffer end (no
+// memory traffic; zeros land in a slot that is never read again), which
+// keeps the outstanding-load count the same in every step.
 //
-// Iteration s: fragments of slice s / k-half 1 are read while the MFMAs of
-// k-half 0 run; then the wave waits for its DMA loads of slice s+1 and meets
-// the others at the barrier (which also proves every wave is done with
-// slice s-1, whose ring slot is refilled with slice s+3); then slice s+1 /
-// k-half 0 fragments are read while the MFMAs of k-half 1 run.  DMA loads
-// are therefore issued two iterations before they are needed.
+// A wave issues instructions in order, and a DMA load occupies the
+// per-CU address path for about 16 clocks, so loads are spread evenly over
+// the step (one per four MFMAs) instead of in a burst, and each LDS
+// fragment read sits next to the MFMAs it overlaps (scheduling barriers
+// pin the order):
+//  phase 1 of step s: fragments of slice s / k-half 1 are read and loads
+//    4..7 of slice s+2 issued, while the MFMAs of k-half 0 run;
+//  wait for this wave's loads of slice s+1, meet the other waves (every wave
+//    is then done with slice s-1, whose slot takes slice s+3);
+//  phase 2: fragments of slice s+1 / k-half 0 are read and loads 0..3 of
+//    slice s+3 issued, while the MFMAs of k-half 1 run.
 template <int AL, int BL, class Issue>
-DEV void mainloop(uint16_t* lds, int nsteps, Issue issue, f32x16_t (&acc)[4][4], int wm, int wn, int lane) {
+DEV void mainloop(const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f32x16_t (&acc)[4][4], int wm,
+                  int wn, int lane) {
   if (nsteps <= 0) return;
-  const int pre = nsteps < NSTAGE - 1 ? nsteps : NSTAGE - 1;
-  for (int s = 0; s < pre; ++s) issue(s, lds + s * STAGE);
-  wait_barrier(2 * LOADS * (pre - 1));
+  auto slot = [&](int s) { return lds + (s & (NSTAGE - 1)) * STAGE; };
+  auto slot_addr = [&](int s) { return ring + (uint32_t)(s & (NSTAGE - 1)) * (STAGE * 2); };
+#pragma unroll
+  for (int i = 0; i < 8; ++i) issue(0, slot_addr(0), i);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) issue(1, slot_addr(1), i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) issue(2, slot_addr(2), i);
+  wait_barrier<12>();  // slice 0 landed
   Frags f0, f1;
   load_frags<AL, BL>(f0, lds, 0, wm, wn, lane);
-  for (int s = 0; s < nsteps; ++s) {
-    const uint16_t* st = lds + (s % NSTAGE) * STAGE;
-    load_frags<AL, BL>(f1, st, 1, wm, wn, lane);
-    mma16(f0, acc);
-    if (s + 1 < nsteps) {
-      // outstanding after slice s+1: slice s+2 if it was issued
-      wait_barrier(s + 2 < nsteps ? 2 * LOADS : 0);
-      if (s + NSTAGE - 1 < nsteps) issue(s + NSTAGE - 1, lds + ((s + NSTAGE - 1) % NSTAGE) * STAGE);
-      load_frags<AL, BL>(f0, lds + ((s + 1) % NSTAGE) * STAGE, 0, wm, wn, lane);
+#pragma unroll 1
+  for (int s = 0; s < nsteps - 1; ++s) {
+    const uint16_t* cur = slot(s);
+    const uint16_t* nxt = slot(s + 1);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      if (g & 1) issue(s + 2, slot_addr(s + 2), 4 + (g >> 1));
+      load_frag<AL, BL>(f1, cur, 1, wm, wn, lane, g);
+      __builtin_amdgcn_sched_barrier(0);
+      mma2(f0, acc, g);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    mma16(f1, acc);
+    wait_barrier<8>();  // slice s+1 landed; slot of slice s-1 free
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      if (g & 1) issue(s + 3, slot_addr(s + 3), g >> 1);
+      load_frag<AL, BL>(f0, nxt, 0, wm, wn, lane, g);
+      __builtin_amdgcn_sched_barrier(0);
+      mma2(f1, acc, g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
+  load_frags<AL, BL>(f1, slot(nsteps - 1), 1, wm, wn, lane);
+  mma16(f0, acc);
+  mma16(f1, acc);
   block_barrier();
 }
 
