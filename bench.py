@@ -165,7 +165,8 @@ def main():
 
     st_det = stage_times(moe.DETERMINISTIC, det)
     st_atom = stage_times(moe.ATOMIC, atom)
-    gemm_stages = ("fc2_dgrad_dprob_partials", "fc1_dgrad", "wgrad_fc1", "wgrad_fc2")
+    gemm_stages = [n for n in ("fc2_dgrad_dprob_partials", "fc1_dgrad_dprob_combine", "fc1_dgrad", "wgrad_fc1",
+                               "wgrad_fc2") if n in st_det]
     dom = max(gemm_stages, key=lambda n: st_det[n])
     dom_ms = st_det[dom]
     achieved = gemm_flops / (dom_ms * 1e-3) / 1e12

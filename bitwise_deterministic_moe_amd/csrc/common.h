@@ -89,42 +89,72 @@ DEV int64_t map_unit(int64_t b, int64_t U, uint64_t seed) {
   return L;
 }
 
+// Work-unit mapping for kernels whose units are ordered most expensive
+// first and whose workgroups each fill a compute unit: the first round
+// (units [0, min(U, ncu))) and the remaining units are each laid out per XCD
+// as in map_unit, so the cheap units at the end of the order run last on
+// every XCD.  The grid must hold round_up8(min(U, ncu)) + round_up8(U - ncu)
+// workgroups (at most round_up8(U) + 8).
+DEV int64_t map_unit_rounds(int64_t b, int64_t U, int ncu, uint64_t seed) {
+  if (U <= 0) return -1;
+  const int64_t U1 = U < ncu ? U : ncu;
+  const int64_t per1 = (U1 + kNumXcd - 1) / kNumXcd;
+  int64_t L;
+  if (b < per1 * kNumXcd) {
+    const int64_t q = b / kNumXcd;
+    L = (b % kNumXcd) * per1 + q;
+    if (L >= U1) return -1;
+  } else {
+    const int64_t b2 = b - per1 * kNumXcd, U2 = U - U1;
+    const int64_t per2 = (U2 + kNumXcd - 1) / kNumXcd;
+    const int64_t q = b2 / kNumXcd;
+    if (q >= per2) return -1;
+    L = U1 + (b2 % kNumXcd) * per2 + q;
+    if (L >= U) return -1;
+  }
+  if (seed) {
+    shuffle_delay(seed, b);
+    L = shuffle_unit(L, U, seed);
+  }
+  return L;
+}
+
 // ------------------------------------------------------------ block scans
 // Exclusive prefix over G values computed by val(g), written to s_pre[0..G]
 // (s_pre[G] = total).  All NT threads of the block must call it; ends with a
 // barrier.  Integer arithmetic: exact and order-independent.
-template <int NT, class F>
-DEV void block_exclusive_scan(int* s_pre, int* s_tmp, int G, F val) {
+template <int NT, class F, class T = int>
+DEV void block_exclusive_scan(T* s_pre, T* s_tmp, int G, F val) {
   const int tid = threadIdx.x;
   const int per = (G + NT - 1) / NT;
   const int g0 = tid * per;
-  int local = 0;
+  T local = 0;
   for (int i = 0; i < per; ++i) {
     int g = g0 + i;
-    if (g < G) local += val(g);
+    if (g < G) local += (T)val(g);
   }
   // wave inclusive scan of per-thread sums
   const int lane = tid & (kWave - 1), w = tid / kWave;
-  int incl = local;
+  T incl = local;
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
-    int o = __shfl_up(incl, d, kWave);
+    T o = __shfl_up(incl, d, kWave);
     if (lane >= d) incl += o;
   }
   if (lane == kWave - 1) s_tmp[w] = incl;
   __syncthreads();
-  int wbase = 0;
+  T wbase = 0;
   for (int i = 0; i < w; ++i) wbase += s_tmp[i];
-  int run = wbase + incl - local;
+  T run = wbase + incl - local;
   for (int i = 0; i < per; ++i) {
     int g = g0 + i;
     if (g < G) {
       s_pre[g] = run;
-      run += val(g);
+      run += (T)val(g);
     }
   }
   if (tid == NT - 1) {
-    int tot = 0;
+    T tot = 0;
     for (int i = 0; i < NT / kWave; ++i) tot += s_tmp[i];
     s_pre[G] = tot;
   }
@@ -138,6 +168,20 @@ DEV int find_group(const int* pre, int G, int64_t L) {
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
     if (pre[mid] <= L)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// find_group over the values key(pre[g]).
+template <class T, class Key>
+DEV int find_group_by(const T* pre, int G, int64_t L, Key key) {
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (key(pre[mid]) <= L)
       lo = mid;
     else
       hi = mid - 1;

@@ -77,18 +77,59 @@ struct RowTile {
   int64_t off;
 };
 
-// Work unit of this workgroup: (expert g, m-tile, n-tile), or false.
+// Work unit of this workgroup: (expert g, m-tile, n-tile), a side unit, or
+// nothing.  M-tiles are ordered longest first: the full tiles (expert-major),
+// then each expert's partial last tile by descending row count (ties by
+// expert), so that when units outnumber compute units the last, short round
+// holds the smallest tiles.  The first scan packs, per expert, the number of
+// full tiles (high 32 bits) and of partial tiles (0 or 1, low bits).
+enum { kTileNone = 0, kTileGemm = 1, kTileSide = 2 };
 template <int BMv, int BNv>
-DEV bool row_tile(const RowGemmParams& P, int* s_pre, int* s_tmp, RowTile& t) {
-  block_exclusive_scan<256>(s_pre, s_tmp, P.groups, [&](int g) { return (P.counts[g] + BMv - 1) / BMv; });
+DEV int row_tile(const RowGemmParams& P, int64_t* s_pre, int64_t* s_tmp, RowTile& t) {
+  block_exclusive_scan<256>(s_pre, s_tmp, P.groups, [&](int g) {
+    const int c = P.counts[g];
+    return ((int64_t)(c / BMv) << 32) | (int64_t)(c % BMv != 0);
+  });
   const int nN = P.N / BNv;
-  const int64_t U = (int64_t)s_pre[P.groups] * nN;
-  const int64_t L = map_unit(blockIdx.x, U, P.seed);
-  if (L < 0) return false;
-  const int64_t mt_all = L / nN;
+  const int64_t tot = s_pre[P.groups];
+  const int64_t nfull = tot >> 32;
+  const int64_t U = (nfull + (tot & 0xffffffffll)) * nN;
+  const int64_t L = map_unit_rounds(blockIdx.x, U + P.side_units, P.ncu, P.seed);
+  if (L < 0) return kTileNone;
+  if (L >= U) {
+    t.nt = (int)(L - U);  // side unit index
+    return kTileSide;
+  }
+  const int64_t mt = L / nN;
   t.nt = (int)(L % nN);
-  t.g = find_group(s_pre, P.groups, mt_all);
-  t.m0 = (int)(mt_all - s_pre[t.g]) * BMv;
+  if (mt < nfull) {
+    t.g = find_group_by(s_pre, P.groups, mt, [](int64_t v) { return v >> 32; });
+    t.m0 = (int)(mt - (s_pre[t.g] >> 32)) * BMv;
+  } else {
+    // rank q among the partial tiles ordered by (BM - rows, expert):
+    // counting sort by key, then the (q - base)-th expert of the key's bin.
+    const int64_t q = mt - nfull;
+    static_assert(BMv <= 1024 && BMv <= kMaxExperts, "key bins fit the scan buffer");
+    int64_t* s_hist = s_pre + (kMaxExperts + 1) / 2;  // upper half, after the packed scan is consumed
+    __syncthreads();
+    for (int k = threadIdx.x; k <= BMv; k += blockDim.x) s_pre[k] = 0;
+    __syncthreads();
+    for (int g = threadIdx.x; g < P.groups; g += blockDim.x) {
+      const int r = P.counts[g] % BMv;
+      if (r) atomicAdd((unsigned long long*)&s_pre[BMv - r], 1ull);
+    }
+    __syncthreads();
+    block_exclusive_scan<256>(s_hist, s_tmp, BMv, [&](int k) { return s_pre[k]; });
+    const int key = find_group_by(s_hist, BMv, q, [](int64_t v) { return v; });
+    const int64_t rank = q - s_hist[key];
+    __syncthreads();
+    block_exclusive_scan<256>(s_pre, s_tmp, P.groups, [&](int g) {
+      const int r = P.counts[g] % BMv;
+      return (int64_t)(r != 0 && BMv - r == key);
+    });
+    t.g = find_group_by(s_pre, P.groups, rank, [](int64_t v) { return v; });
+    t.m0 = P.counts[t.g] / BMv * BMv;
+  }
   t.n0 = t.nt * BNv;
   t.off = P.offsets[t.g];
   t.mvalid = min(BMv, P.counts[t.g] - t.m0);
@@ -99,7 +140,28 @@ DEV bool row_tile(const RowGemmParams& P, int* s_pre, int* s_tmp, RowTile& t) {
   t.nt = __builtin_amdgcn_readfirstlane(t.nt);
   t.mvalid = __builtin_amdgcn_readfirstlane(t.mvalid);
   t.off = (int64_t)__builtin_amdgcn_readfirstlane((int)t.off);
-  return true;
+  return kTileGemm;
+}
+
+// Side unit u: the dprob combine of flat slots [u*kSideSlots, ...): groups of
+// GS = next_pow2(n_tiles) lanes, lane q loads partial q (0 for q >=
+// n_tiles) and the group folds with xor shuffles at distance 1, 2, 4, ...;
+// the tree depends on n_tiles only and a + b == b + a in IEEE arithmetic,
+// so every lane ends with the same bits.  Slots of non-local experts get 0.
+DEV void dprob_side(const RowGemmParams& P, int u) {
+  int gs = 1;
+  while (gs < P.n_tiles) gs <<= 1;
+  const int per = 256 / gs;
+  const int q = threadIdx.x % gs;
+  const int64_t s0 = (int64_t)u * kSideSlots;
+  for (int j = threadIdx.x / gs; j < kSideSlots; j += per) {
+    const int64_t i = s0 + j;
+    const bool valid = i < P.side_nslot;  // uniform per lane group
+    const int32_t r = valid ? P.side_slot_row[i] : -1;
+    float v = (r >= 0 && q < P.n_tiles) ? P.part[(int64_t)r * P.n_tiles + q] : 0.f;
+    for (int d = 1; d < gs; d <<= 1) v = v + __shfl_xor(v, d, 64);
+    if (valid && q == 0) P.dprob[i] = r >= 0 ? v : 0.f;
+  }
 }
 
 // Epilogue over the accumulators (layout documented in gemm_bf16.h /
@@ -319,13 +381,15 @@ struct NoPre {
 template <int BL, int EPI>
 __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
-  __shared__ int s_pre[kMaxExperts + 1];
-  __shared__ int s_tmp[8];
+  __shared__ int64_t s_pre[kMaxExperts + 1];
+  __shared__ int64_t s_tmp[8];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t ring = bf::lds_base(lds);
   const int wm = wave >> 1, wn = wave & 1;
   RowTile t;
-  if (!row_tile<bf::BM, bf::BN>(P, s_pre, s_tmp, t)) return;
+  const int kind = row_tile<bf::BM, bf::BN>(P, s_pre, s_tmp, t);
+  if (kind == kTileSide) dprob_side(P, t.nt);
+  if (kind != kTileGemm) return;
 
   bf::KcOperand oa;
   // Branch-free so that the four row-index loads of a thread are in flight
@@ -347,25 +411,30 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
   if constexpr (BL == bf::KC) {
     bf::KcOperand ob;
     ob.init(Bg, P.b_bytes, wave, lane, [&](int r) -> uint32_t { return (uint32_t)((t.n0 + r) * P.ldb * 2); });
-    bf::mainloop<bf::KC, bf::KC>(lds, ring, nsteps, [&](int s, uint32_t st, int i) {
+    auto issue = [&](int s, uint32_t st, int i) {
       if (i < bf::LOADS)
         oa.issue1(st, wave, s * bf::BK, s < nsteps, i);
       else
         ob.issue1(st + bf::OPER * 2, wave, s * bf::BK, s < nsteps, i - bf::LOADS);
-    }, acc, wm, wn, lane);
+    };
+    bf::mainloop<bf::KC, bf::KC>(lds, ring, nsteps, issue, acc, wm, wn, lane);
   } else {
     bf::MncOperand ob;
     ob.init(Bg, P.b_bytes, wave, lane, t.n0);
-    bf::mainloop<bf::KC, bf::MNC>(lds, ring, nsteps, [&](int s, uint32_t st, int i) {
+    // byte offset of this lane's k row of load j in slice 0
+    uint32_t kro[bf::LOADS];
+#pragma unroll
+    for (int j = 0; j < bf::LOADS; ++j) kro[j] = (uint32_t)(bf::MncOperand::krow(wave, lane, j) * P.ldb * 2);
+    const uint32_t slice_bytes = (uint32_t)(bf::BK * P.ldb * 2);
+    auto issue = [&](int s, uint32_t st, int i) {
       if (i < bf::LOADS) {
         oa.issue1(st, wave, s * bf::BK, s < nsteps, i);
       } else {
         const int j = i - bf::LOADS;
-        const uint32_t ro =
-            s < nsteps ? (uint32_t)((s * bf::BK + bf::MncOperand::krow(wave, lane, j)) * P.ldb * 2) : bf::kOOB;
-        ob.issue1(st + bf::OPER * 2, wave, ro, j);
+        ob.issue1(st + bf::OPER * 2, wave, s < nsteps ? kro[j] + (uint32_t)s * slice_bytes : bf::kOOB, j);
       }
-    }, acc, wm, wn, lane);
+    };
+    bf::mainloop<bf::KC, bf::MNC>(lds, ring, nsteps, issue, acc, wm, wn, lane);
   }
   float* stage = (float*)lds;
   if constexpr (EPI == kEpiStore || EPI == kEpiStoreAct) {
@@ -464,13 +533,16 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
 template <bool A_GATHER, bool B_GATHER>
 __global__ __launch_bounds__(256) void wgrad_bf16_kernel(WgradParams P) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
-  __shared__ int s_tok[kMaxChunkRows];
+  __shared__ uint32_t s_rowoff[kMaxChunkRows];  // byte offset of each gathered row of the chunk
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t ring = bf::lds_base(lds);
   const int wm = wave >> 1, wn = wave & 1;
   WgradTile t;
   if (!wgrad_tile<bf::BM, bf::BN>(P, t)) return;
-  for (int i = tid; i < t.klen; i += 256) s_tok[i] = P.row_tok[t.row0 + i];
+  static_assert(A_GATHER != B_GATHER, "exactly one operand is gathered by token");
+  const uint32_t ld_gather = (uint32_t)(A_GATHER ? P.lda : P.ldb) * 2u;
+  const uint32_t ld_direct = (uint32_t)(A_GATHER ? P.ldb : P.lda) * 2u;
+  for (int i = tid; i < t.klen; i += 256) s_rowoff[i] = (uint32_t)P.row_tok[t.row0 + i] * ld_gather;
   __syncthreads();
 
   f32x16_t acc[4][4];
@@ -484,32 +556,37 @@ __global__ __launch_bounds__(256) void wgrad_bf16_kernel(WgradParams P) {
   oa.init(P.a, P.a_bytes, wave, lane, t.m0);
   ob.init(P.b, P.b_bytes, wave, lane, t.n0);
   const int nsteps = (t.klen + bf::BK - 1) / bf::BK;
-  // Byte offsets of the k rows this lane loads.  The gathered operand's
-  // token index of slice s+1 is read from LDS while slice s is issued, so
-  // the issue never waits on that read.
-  // (Rows past the chunk read an in-range entry and are masked at issue.)
-  int tok[bf::LOADS];
-  auto fetch_tok = [&](int s) {
+  // Per load j of a slice, this lane's k row is krow(j) + 32 s.  The direct
+  // operand's row offset advances by a scalar per slice; the gathered
+  // operand's offsets of slice s+1 are read from LDS right after slice s is
+  // issued, so an issue never waits on that read.  (Rows past the chunk read
+  // an in-range entry and are masked at issue.)
+  uint32_t dir[bf::LOADS], gat[bf::LOADS];
+  int kr[bf::LOADS];
 #pragma unroll
-    for (int i = 0; i < bf::LOADS; ++i) {
-      const int kk = s * bf::BK + bf::MncOperand::krow(wave, lane, i);
-      tok[i] = s_tok[kk < t.klen ? kk : (t.klen > 0 ? t.klen - 1 : 0)];
+  for (int j = 0; j < bf::LOADS; ++j) {
+    kr[j] = bf::MncOperand::krow(wave, lane, j);
+    dir[j] = (uint32_t)(t.row0 + kr[j]) * ld_direct;
+  }
+  const int last = t.klen > 0 ? t.klen - 1 : 0;
+  auto fetch = [&](int s) {
+#pragma unroll
+    for (int j = 0; j < bf::LOADS; ++j) {
+      const int kk = s * bf::BK + kr[j];
+      gat[j] = s_rowoff[kk < t.klen ? kk : last];
     }
   };
-  fetch_tok(0);
+  fetch(0);
+  const uint32_t dir_step = (uint32_t)bf::BK * ld_direct;
   bf::mainloop<bf::MNC, bf::MNC>(lds, ring, nsteps, [&](int s, uint32_t st, int i) {
     const int j = i & (bf::LOADS - 1);
-    const int kk = s * bf::BK + bf::MncOperand::krow(wave, lane, j);
-    const bool ok = kk < t.klen;
-    const uint32_t direct = (uint32_t)(t.row0 + kk);
-    if (i < bf::LOADS) {
-      const uint32_t r = A_GATHER ? (uint32_t)tok[j] : direct;
-      oa.issue1(st, wave, ok ? r * (uint32_t)P.lda * 2u : bf::kOOB, j);
-    } else {
-      const uint32_t r = B_GATHER ? (uint32_t)tok[j] : direct;
-      ob.issue1(st + bf::OPER * 2, wave, ok ? r * (uint32_t)P.ldb * 2u : bf::kOOB, j);
-    }
-    if (i == 2 * bf::LOADS - 1) fetch_tok(s + 1);
+    const bool ok = kr[j] < t.klen - s * bf::BK;
+    const uint32_t d = dir[j] + (uint32_t)s * dir_step;
+    if (i < bf::LOADS)
+      oa.issue1(st, wave, ok ? (A_GATHER ? gat[j] : d) : bf::kOOB, j);
+    else
+      ob.issue1(st + bf::OPER * 2, wave, ok ? (B_GATHER ? gat[j] : d) : bf::kOOB, j);
+    if (i == 2 * bf::LOADS - 1) fetch(s + 1);
   }, acc, wm, wn, lane);
   float* dst = wgrad_dst(P, t);
   const bool atomic_add = P.atomic && t.S > 1;
@@ -531,12 +608,14 @@ __global__ __launch_bounds__(256) void wgrad_bf16_kernel(WgradParams P) {
 template <bool B_MNC, int EPI>
 __global__ __launch_bounds__(256) void rowgemm_f32_kernel(RowGemmParams P) {
   __shared__ __attribute__((aligned(16))) float lds[f32::LDS_BYTES / 4];
-  __shared__ int s_pre[kMaxExperts + 1];
-  __shared__ int s_tmp[8];
+  __shared__ int64_t s_pre[kMaxExperts + 1];
+  __shared__ int64_t s_tmp[8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   RowTile t;
-  if (!row_tile<f32::BM, f32::BN>(P, s_pre, s_tmp, t)) return;
+  const int kind = row_tile<f32::BM, f32::BN>(P, s_pre, s_tmp, t);
+  if (kind == kTileSide) dprob_side(P, t.nt);
+  if (kind != kTileGemm) return;
   float* As0 = lds;
   float* Bs0 = lds + 2 * f32::OPER;
   f32::KcLoader la;

@@ -136,20 +136,21 @@ DEV void load_frags(Frags& f, const uint16_t* st, int kk, int wm, int wn, int la
 //   (A0;B0,B1) (A1;B0,B1) (A0;B2,B3) (A1;B2,B3) (A2;B0,B1) (A2;B2,B3) (A3;B0,B1) (A3;B2,B3)
 // so the pair of group g only needs blocks read by groups 0..g+1 of the
 // previous phase, never the reads issued last.
+constexpr int kGrpA[8] = {0, -1, -1, 1, -1, -1, 2, 3};
+constexpr int kGrpB[8] = {-1, 0, 1, -1, 2, 3, -1, -1};
+constexpr int kGrpM[8] = {0, 1, 0, 1, 2, 2, 3, 3};
+constexpr int kGrpN[8] = {0, 0, 2, 2, 0, 2, 0, 2};
+
 template <int AL, int BL>
 DEV void load_frag(Frags& f, const uint16_t* st, int kk, int wm, int wn, int lane, int g) {
-  constexpr int kA[8] = {0, -1, -1, 1, -1, -1, 2, 3};
-  constexpr int kB[8] = {-1, 0, 1, -1, 2, 3, -1, -1};
-  if (kA[g] >= 0)
-    f.a[kA[g]] = frag<AL>(st, wm * 128 + kA[g] * 32, kk, lane);
+  if (kGrpA[g] >= 0)
+    f.a[kGrpA[g]] = frag<AL>(st, wm * 128 + kGrpA[g] * 32, kk, lane);
   else
-    f.b[kB[g]] = frag<BL>(st + OPER, wn * 128 + kB[g] * 32, kk, lane);
+    f.b[kGrpB[g]] = frag<BL>(st + OPER, wn * 128 + kGrpB[g] * 32, kk, lane);
 }
 
 DEV void mma2(const Frags& f, f32x16_t (&acc)[4][4], int g) {
-  constexpr int kM[8] = {0, 1, 0, 1, 2, 2, 3, 3};
-  constexpr int kN[8] = {0, 0, 2, 2, 0, 2, 0, 2};
-  const int mb = kM[g], nb = kN[g];
+  const int mb = kGrpM[g], nb = kGrpN[g];
   acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[nb], f.a[mb], acc[mb][nb], 0, 0, 0);
   acc[mb][nb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[nb + 1], f.a[mb], acc[mb][nb + 1], 0, 0, 0);
 }
@@ -248,7 +249,8 @@ DEV void mainloop(const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f
   for (int i = 0; i < 4; ++i) issue(2, slot_addr(2), i);
   wait_barrier<12>();  // slice 0 landed
   Frags f0, f1;
-  load_frags<AL, BL>(f0, lds, 0, wm, wn, lane);
+#pragma unroll
+  for (int g = 0; g < 8; ++g) load_frag<AL, BL>(f0, lds, 0, wm, wn, lane, g);
 #pragma unroll 1
   for (int s = 0; s < nsteps - 1; ++s) {
     const uint16_t* cur = slot(s);
@@ -271,9 +273,12 @@ DEV void mainloop(const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  load_frags<AL, BL>(f1, slot(nsteps - 1), 1, wm, wn, lane);
-  mma16(f0, acc);
-  mma16(f1, acc);
+#pragma unroll
+  for (int g = 0; g < 8; ++g) load_frag<AL, BL>(f1, slot(nsteps - 1), 1, wm, wn, lane, g);
+#pragma unroll
+  for (int g = 0; g < 8; ++g) mma2(f0, acc, g);
+#pragma unroll
+  for (int g = 0; g < 8; ++g) mma2(f1, acc, g);
   block_barrier();
 }
 

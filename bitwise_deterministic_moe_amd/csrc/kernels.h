@@ -9,10 +9,12 @@ namespace moedet {
 constexpr int kMaxExperts = 1024;     // router width handled by the routing kernels
 constexpr int kMaxTopK = 64;          // one lane per selected expert
 constexpr int kRouteChunk = 64;       // tokens per routing/permutation chunk
-constexpr int kMaxChunkRows = 2048;   // upper bound on the wgrad K chunk (rows)
+constexpr int kMaxChunkRows = 4096;   // upper bound on the wgrad K chunk (rows)
 
 // Grid size (a multiple of the 8 XCDs) for an upper bound on work units.
 inline int64_t grid_for_units(int64_t U_max) { return ((U_max + 7) / 8) * 8; }
+// grid for map_unit_rounds
+inline int64_t grid_for_unit_rounds(int64_t U_max) { return grid_for_units(U_max) + 8; }
 
 enum { kEpiStore = 0, kEpiDgrad2 = 1, kEpiStoreAct = 2 };
 enum { kGemmFc1Fwd = 0, kGemmFc2Fwd = 1, kGemmFc2Dgrad = 2, kGemmFc1Dgrad = 3 };
@@ -43,8 +45,17 @@ struct RowGemmParams {
   int n_tiles;
   float* dprob;
   int atomic;
+  int ncu;  // compute units of the device (work-unit rounds)
+  // Side job run by the workgroups after the GEMM tiles (fc1 dgrad, which
+  // leaves compute units idle at small shapes): the fixed-order dprob
+  // combine of part[] (n_tiles partials per row) for side_nslot flat slots.
+  const int32_t* side_slot_row;
+  int64_t side_nslot;
+  int side_units;
   uint64_t seed;
 };
+
+constexpr int kSideSlots = 1024;  // flat slots per side unit
 
 struct WgradParams {
   const int32_t* counts;

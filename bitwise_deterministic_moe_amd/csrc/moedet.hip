@@ -28,6 +28,7 @@ struct Plan {
   int bm, bn;         // GEMM tile
   int n_tiles;        // fc2-dgrad N-tiles (dprob partials per row)
   int kc;             // wgrad K chunk (rows)
+  bool may_split;     // some expert can hold more than kc rows
   int64_t wslots;     // wgrad partial slots per dW
   size_t esize;
 };
@@ -73,14 +74,18 @@ moe_status validate(const moe_problem* p, Plan* pl) {
     pl->bm = bm;
     pl->bn = bn;
     pl->n_tiles = p->d_ffn / bn;
-    // wgrad K chunk: twice the mean rows per expert of the whole layer,
-    // rounded up to 256, clamped to [512, 2048]; a pure function of shapes.
+    // wgrad K chunk: four times the mean rows per expert of the whole layer,
+    // rounded up to 256, clamped to [512, kMaxChunkRows]; a pure function of
+    // shapes.  Only experts holding more rows than that (skewed routing) are
+    // split.  An expert holds at most `tokens` rows, so with kc >= tokens no
+    // expert can split and the ordered reduction is not needed at all.
     const double mean = (double)p->tokens * p->top_k / p->num_experts;
-    int64_t kc = 256 * (int64_t)((2.0 * mean + 255.0) / 256.0);
+    int64_t kc = 256 * (int64_t)((4.0 * mean + 255.0) / 256.0);
     if (kc < 512) kc = 512;
     if (kc > kMaxChunkRows) kc = kMaxChunkRows;
     pl->kc = (int)kc;
-    pl->wslots = pl->rows_cap / kc;
+    pl->may_split = kc < p->tokens;
+    pl->wslots = pl->may_split ? pl->rows_cap / kc : 0;
     pl->esize = bf16 ? 2 : 4;
   }
   return MOE_OK;
@@ -162,9 +167,22 @@ struct Stager {
   }
 };
 
-int64_t rowgemm_grid(const Plan& pl, int N) {
+int64_t rowgemm_grid(const Plan& pl, int N, int64_t side_units = 0) {
   const int64_t mtiles = (pl.rows_cap + pl.bm - 1) / pl.bm + pl.el;
-  return grid_for_units(mtiles * (N / pl.bn));
+  return grid_for_unit_rounds(mtiles * (N / pl.bn) + side_units);
+}
+
+// Compute units of the current device (cached per device ordinal; the
+// value never changes, so a racing first fill writes the same number).
+int device_cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cache[dev] = n;
+  return n;
 }
 
 int64_t wgrad_grid(const Plan& pl, int M, int N) {
@@ -231,12 +249,16 @@ MOE_API const char* moe_stage_names(const moe_problem* p, moe_mode mode, int cal
       return cb ? "route,permute_scan,permute_scatter_atomic,fc1_fwd,fc2_fwd,zero,combine_scatter,cast"
                 : "route,permute_scan,permute_scatter_atomic,fc1_fwd,fc2_fwd";
     case 1:
-      if (!at) return cb ? "fc2_dgrad_dprob_partials,dprob_combine,fc1_dgrad,dx_combine_gather"
-                         : "fc2_dgrad_dprob_partials,dprob_combine,fc1_dgrad";
+      if (!at) return cb ? "fc2_dgrad_dprob_partials,fc1_dgrad_dprob_combine,dx_combine_gather"
+                         : "fc2_dgrad_dprob_partials,fc1_dgrad_dprob_combine";
       return cb ? "zero,fc2_dgrad_dprob_atomic,fc1_dgrad,dx_combine_scatter,cast"
                 : "zero,fc2_dgrad_dprob_atomic,fc1_dgrad";
-    case 2:
-      return at ? "wgrad_prep_zero,wgrad_fc1,wgrad_fc2" : "wgrad_prep,wgrad_fc1,wgrad_fc2,wgrad_reduce";
+    case 2: {
+      Plan pl;
+      validate(p, &pl);
+      if (at) return "wgrad_prep_zero,wgrad_fc1,wgrad_fc2";
+      return pl.may_split ? "wgrad_prep,wgrad_fc1,wgrad_fc2,wgrad_reduce" : "wgrad_prep,wgrad_fc1,wgrad_fc2";
+    }
   }
   return nullptr;
 }
@@ -295,6 +317,7 @@ MOE_API moe_status moe_fwd(const moe_problem* p, const float* logits, const void
   G.counts = routing->counts;
   G.offsets = routing->offsets;
   G.groups = pl.el;
+  G.ncu = device_cu_count();
   G.seed = seed;
   // fc1: h = x[row_tok] W1_g, W1 [D][F]
   void* arows = wsb + L.arows;
@@ -385,6 +408,7 @@ MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* 
   G.counts = routing->counts;
   G.offsets = routing->offsets;
   G.groups = pl.el;
+  G.ncu = device_cu_count();
   G.seed = seed;
   // fc2 dgrad: G = dy[row_tok] W2_g^T; W2 [F][D] read as [N=F][K=D].
   G.N = pl.F;
@@ -411,15 +435,12 @@ MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* 
   G.atomic = at;
   sg.mark();
   HIP_TRY(launch_rowgemm(G, kGemmFc2Dgrad, pl.bf16, rowgemm_grid(pl, pl.F), st));
-  if (!at) {
-    sg.mark();
-    HIP_TRY(launch_dprob_combine(part, routing->slot_row, pl.nslot, pl.n_tiles, dprob, seed, st));
-  }
   // fc1 dgrad: dx_rows = dh W1_g^T; W1 [D][F] read as [N=D][K=F].
   RowGemmParams G2{};
   G2.counts = routing->counts;
   G2.offsets = routing->offsets;
   G2.groups = pl.el;
+  G2.ncu = device_cu_count();
   G2.seed = seed;
   G2.N = pl.D;
   G2.K = pl.F;
@@ -433,8 +454,19 @@ MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* 
   G2.b_bytes = (uint32_t)(G2.b_gstride * pl.esize);
   G2.c = dxrows;
   G2.ldc = pl.D;
+  int64_t side = 0;
+  if (!at) {
+    // the fixed-order dprob combine rides along as side units of this launch
+    side = (pl.nslot + kSideSlots - 1) / kSideSlots;
+    G2.part = part;
+    G2.n_tiles = pl.n_tiles;
+    G2.dprob = dprob;
+    G2.side_slot_row = routing->slot_row;
+    G2.side_nslot = pl.nslot;
+    G2.side_units = (int)side;
+  }
   sg.mark();
-  HIP_TRY(launch_rowgemm(G2, kGemmFc1Dgrad, pl.bf16, rowgemm_grid(pl, pl.D), st));
+  HIP_TRY(launch_rowgemm(G2, kGemmFc1Dgrad, pl.bf16, rowgemm_grid(pl, pl.D, side), st));
   if (p->combine) {
     if (!at) {
       sg.mark();
@@ -527,7 +559,7 @@ MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routin
   W.slots = slots2;
   sg.mark();
   HIP_TRY(launch_wgrad(W, 2, pl.bf16, wgrad_grid(pl, pl.F, pl.D), st));
-  if (!at) {
+  if (!at && pl.may_split) {
     sg.mark();
     HIP_TRY(launch_wgrad_reduce(Q, 1024, st));
   }

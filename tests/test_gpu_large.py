@@ -189,7 +189,8 @@ def test_large_parity_and_determinism(name):
     assert np.all(dp[perm["slot_row"].reshape(dp.shape) < 0] == 0)
     empty = np.nonzero(perm["counts"] == 0)[0]
     if name == "skewed_e512k22":
-        assert len(empty) > 0 and perm["counts"].max() > 4 * 512, "skewed workload must split and hold empty experts"
+        # the weight-gradient chunk is 768 rows here (4 x the mean of 176, rounded up to 256)
+        assert len(empty) > 0 and perm["counts"].max() > 2 * 768, "skewed workload must split and hold empty experts"
     if len(empty):
         ei = torch.as_tensor(empty, device="cuda")
         assert torch.all(out["dw1"][ei] == 0) and torch.all(out["dw2"][ei] == 0)

@@ -21,8 +21,8 @@ EDGE = {
     "shard_bf16": Config("shard_bf16", 500, 256, 512, 16, 4, 5, 3, "bf16", 0, 16),
     "empty_experts_bf16": Config("empty_experts_bf16", 260, 256, 256, 16, 2, 0, 16, "bf16", 1, 17,
                                  skew="zipf", zipf_beta=0.3),
-    "split_k_bf16": Config("split_k_bf16", 2048, 256, 256, 8, 1, 0, 8, "bf16", 1, 18, skew="zipf",
-                           zipf_beta=1.5, zipf_empty=2),
+    "split_k_bf16": Config("split_k_bf16", 2048, 256, 256, 16, 1, 0, 16, "bf16", 1, 18, skew="zipf",
+                           zipf_beta=2.0, zipf_empty=2),
     "no_tokens_bf16": Config("no_tokens_bf16", 0, 256, 256, 4, 2, 0, 4, "bf16", 1, 19),
     "ragged_fp32": Config("ragged_fp32", 37, 64, 192, 3, 2, 0, 3, "f32", 1, 20),
     "shard_fp32": Config("shard_fp32", 90, 128, 64, 8, 3, 2, 4, "f32", 0, 21),
@@ -79,5 +79,5 @@ def test_split_config_really_splits():
     idx, _ = route(make_inputs(cfg, parts=("logits",))["logits"], cfg.top_k)
     import numpy as np
     counts = np.bincount(idx.reshape(-1), minlength=cfg.num_experts)
-    kc = 512  # chunk for this shape: 2 * mean rows (256) -> 512
+    kc = 512  # chunk for this shape: 4 * mean rows (128) -> 512
     assert counts.max() > 2 * kc, counts
