@@ -378,6 +378,21 @@ struct NoPre {
   DEV void load(Data&, int) {}
 };
 
+// Main loop instantiated for the number of the wave's A blocks that hold
+// rows, so that the waves of a partial tile skip MFMAs on zero rows while
+// every variant stays straight-line code.
+template <int AL, int BL, class Issue>
+DEV void run_mainloop(int nmb, const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f32x16_t (&acc)[4][4],
+                      int wm, int wn, int lane) {
+  switch (nmb) {
+    case 0: bf::mainloop<AL, BL, 0>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
+    case 1: bf::mainloop<AL, BL, 1>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
+    case 2: bf::mainloop<AL, BL, 2>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
+    case 3: bf::mainloop<AL, BL, 3>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
+    default: bf::mainloop<AL, BL, 4>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
+  }
+}
+
 template <int BL, int EPI>
 __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
@@ -408,6 +423,8 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
   const int nsteps = P.K / bf::BK;
+  // 32-row A blocks of this wave that hold rows (wave-uniform)
+  const int nmb = max(0, min(4, (t.mvalid - wm * 128 + 31) / 32));
   if constexpr (BL == bf::KC) {
     bf::KcOperand ob;
     ob.init(Bg, P.b_bytes, wave, lane, [&](int r) -> uint32_t { return (uint32_t)((t.n0 + r) * P.ldb * 2); });
@@ -417,7 +434,7 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
       else
         ob.issue1(st + bf::OPER * 2, wave, s * bf::BK, s < nsteps, i - bf::LOADS);
     };
-    bf::mainloop<bf::KC, bf::KC>(lds, ring, nsteps, issue, acc, wm, wn, lane);
+    run_mainloop<bf::KC, bf::KC>(nmb, lds, ring, nsteps, issue, acc, wm, wn, lane);
   } else {
     bf::MncOperand ob;
     ob.init(Bg, P.b_bytes, wave, lane, t.n0);
@@ -434,7 +451,7 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
         ob.issue1(st + bf::OPER * 2, wave, s < nsteps ? kro[j] + (uint32_t)s * slice_bytes : bf::kOOB, j);
       }
     };
-    bf::mainloop<bf::KC, bf::MNC>(lds, ring, nsteps, issue, acc, wm, wn, lane);
+    run_mainloop<bf::KC, bf::MNC>(nmb, lds, ring, nsteps, issue, acc, wm, wn, lane);
   }
   float* stage = (float*)lds;
   if constexpr (EPI == kEpiStore || EPI == kEpiStoreAct) {
@@ -530,15 +547,13 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
   }
 }
 
+// One weight-gradient tile: dW[m0:m0+256, n0:n0+256] of expert t.g over the
+// rows of chunk t.s, into dst (dW itself, or a split-K partial slot).
 template <bool A_GATHER, bool B_GATHER>
-__global__ __launch_bounds__(256) void wgrad_bf16_kernel(WgradParams P) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
-  __shared__ uint32_t s_rowoff[kMaxChunkRows];  // byte offset of each gathered row of the chunk
+DEV void wgrad_bf16_tile(const WgradParams& P, const WgradTile& t, float* dst, uint16_t* lds, uint32_t* s_rowoff) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t ring = bf::lds_base(lds);
   const int wm = wave >> 1, wn = wave & 1;
-  WgradTile t;
-  if (!wgrad_tile<bf::BM, bf::BN>(P, t)) return;
   static_assert(A_GATHER != B_GATHER, "exactly one operand is gathered by token");
   const uint32_t ld_gather = (uint32_t)(A_GATHER ? P.lda : P.ldb) * 2u;
   const uint32_t ld_direct = (uint32_t)(A_GATHER ? P.ldb : P.lda) * 2u;
@@ -588,7 +603,6 @@ __global__ __launch_bounds__(256) void wgrad_bf16_kernel(WgradParams P) {
       ob.issue1(st + bf::OPER * 2, wave, ok ? (B_GATHER ? gat[j] : d) : bf::kOOB, j);
     if (i == 2 * bf::LOADS - 1) fetch(s + 1);
   }, acc, wm, wn, lane);
-  float* dst = wgrad_dst(P, t);
   const bool atomic_add = P.atomic && t.S > 1;
   NoPre none;
   const __amdgpu_buffer_rsrc_t rd = buf(dst);
@@ -602,6 +616,70 @@ __global__ __launch_bounds__(256) void wgrad_bf16_kernel(WgradParams P) {
       __builtin_amdgcn_raw_buffer_store_b128(f32x4_t{v[0], v[1], v[2], v[3]}, rd, o, 0, 0);
     }
   });
+}
+
+template <bool A_GATHER, bool B_GATHER>
+__global__ __launch_bounds__(256) void wgrad_bf16_kernel(WgradParams P) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
+  __shared__ uint32_t s_rowoff[kMaxChunkRows];  // byte offset of each gathered row of the chunk
+  WgradTile t;
+  if (!wgrad_tile<bf::BM, bf::BN>(P, t)) return;
+  wgrad_bf16_tile<A_GATHER, B_GATHER>(P, t, wgrad_dst(P, t), lds, s_rowoff);
+}
+
+// Both weight gradients in one launch: units [0, U1) are dW1 tiles (rows of
+// x gathered by token, dh rows), [U1, U1 + U2) dW2 tiles (act_p rows, dy
+// gathered by token).  The chunk schedule is computed here from counts:
+// per expert S_g = max(1, ceil(cnt_g / kc)) chunks; one packed scan gives the
+// first unit (sum of S, high 32 bits) and the first partial slot (sum of
+// S - 1, low bits) of each expert.
+__global__ __launch_bounds__(256) void wgrad_pair_bf16_kernel(WgradParams P1, WgradParams P2, int ncu) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
+  __shared__ uint32_t s_rowoff[kMaxChunkRows];  // byte offset of each gathered row of the chunk
+  __shared__ int64_t s_tmp[8];
+  int64_t* s_pre = (int64_t*)lds;  // setup only, before the ring is used
+  const int G = P1.groups;
+  const int kc = P1.kc;
+  block_exclusive_scan<256>(s_pre, s_tmp, G, [&](int g) {
+    const int c = P1.counts[g];
+    const int64_t S = c > kc ? (c + kc - 1) / kc : 1;
+    return (S << 32) | (S - 1);
+  });
+  const int tiles1 = (P1.M / bf::BM) * (P1.N / bf::BN), tiles2 = (P2.M / bf::BM) * (P2.N / bf::BN);
+  const int64_t units = s_pre[G] >> 32;
+  const int64_t U1 = units * tiles1, U2 = units * tiles2;
+  int64_t L = map_unit_rounds(blockIdx.x, U1 + U2, ncu, P1.seed);
+  if (L < 0) return;
+  const bool second = L >= U1;
+  const WgradParams& P = second ? P2 : P1;
+  if (second) L -= U1;
+  const int tiles = second ? tiles2 : tiles1;
+  const int nN = P.N / bf::BN;
+  WgradTile t;
+  const int64_t u = L / tiles;
+  const int tile = (int)(L % tiles);
+  t.g = find_group_by(s_pre, G, u, [](int64_t v) { return v >> 32; });
+  t.s = (int)(u - (s_pre[t.g] >> 32));
+  const int64_t slot = (s_pre[t.g] & 0xffffffffll) + t.s - 1;
+  const int cnt = P.counts[t.g];
+  t.S = cnt > kc ? (cnt + kc - 1) / kc : 1;
+  const int k_lo = (int)((int64_t)t.s * cnt / t.S), k_hi = (int)((int64_t)(t.s + 1) * cnt / t.S);
+  t.klen = k_hi - k_lo;
+  t.row0 = (int64_t)P.offsets[t.g] + k_lo;
+  t.m0 = (tile / nN) * bf::BM;
+  t.n0 = (tile % nN) * bf::BN;
+  t.g = __builtin_amdgcn_readfirstlane(t.g);
+  t.s = __builtin_amdgcn_readfirstlane(t.s);
+  t.S = __builtin_amdgcn_readfirstlane(t.S);
+  t.klen = __builtin_amdgcn_readfirstlane(t.klen);
+  t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
+  t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
+  float* dst = (!P.atomic && t.s > 0) ? P.slots + slot * P.M * P.N : P.dw + (int64_t)t.g * P.M * P.N;
+  __syncthreads();  // the scan buffer aliases the ring
+  if (second)
+    wgrad_bf16_tile<false, true>(P2, t, dst, lds, s_rowoff);
+  else
+    wgrad_bf16_tile<true, false>(P1, t, dst, lds, s_rowoff);
 }
 
 // ================================================================= fp32
@@ -746,8 +824,13 @@ __global__ __launch_bounds__(256) void wgrad_prep_kernel(WgradPrepParams P) {
 //   dW_g = ((part_0 + part_1) + part_2) + ... + part_{S-1}
 // part_0 sits in dW_g itself, part_s (s >= 1) in slot slot_base[g] + s - 1.
 __global__ __launch_bounds__(256) void wgrad_reduce_kernel(WgradPrepParams P) {
+  __shared__ int slot_base[kMaxExperts + 1];  // sum over earlier experts of S - 1
+  __shared__ int s_tmp[8];
   const int G = P.groups;
-  const int32_t* slot_base = P.sched + (G + 1);
+  block_exclusive_scan<256>(slot_base, s_tmp, G, [&](int g) {
+    const int c = P.counts[g];
+    return c > P.kc ? (c + P.kc - 1) / P.kc - 1 : 0;
+  });
   const int64_t MN = (int64_t)P.M * P.N;
   const int64_t per = MN / 4;
   for (int g = 0; g < G; ++g) {
@@ -808,6 +891,12 @@ hipError_t launch_wgrad(const WgradParams& P, int which, bool bf16, int64_t grid
     else
       wgrad_f32_kernel<false, true><<<grid, 256, 0, st>>>(P);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad_pair(const WgradParams& P1, const WgradParams& P2, int ncu, int64_t grid, hipStream_t st) {
+  if (grid <= 0) return hipSuccess;
+  wgrad_pair_bf16_kernel<<<grid, 256, 0, st>>>(P1, P2, ncu);
   return hipGetLastError();
 }
 

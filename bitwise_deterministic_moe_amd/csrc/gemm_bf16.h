@@ -141,16 +141,22 @@ constexpr int kGrpB[8] = {-1, 0, 1, -1, 2, 3, -1, -1};
 constexpr int kGrpM[8] = {0, 1, 0, 1, 2, 2, 3, 3};
 constexpr int kGrpN[8] = {0, 0, 2, 2, 0, 2, 0, 2};
 
-template <int AL, int BL>
+// NMB: number of the wave's 32-row A blocks that hold rows (4 for a full
+// tile).  A wave of a partial tile skips the reads and MFMAs of the blocks
+// past the group end, which would only multiply zeros.
+template <int AL, int BL, int NMB = 4>
 DEV void load_frag(Frags& f, const uint16_t* st, int kk, int wm, int wn, int lane, int g) {
-  if (kGrpA[g] >= 0)
-    f.a[kGrpA[g]] = frag<AL>(st, wm * 128 + kGrpA[g] * 32, kk, lane);
-  else
+  if (kGrpA[g] >= 0) {
+    if (kGrpA[g] < NMB) f.a[kGrpA[g]] = frag<AL>(st, wm * 128 + kGrpA[g] * 32, kk, lane);
+  } else {
     f.b[kGrpB[g]] = frag<BL>(st + OPER, wn * 128 + kGrpB[g] * 32, kk, lane);
+  }
 }
 
+template <int NMB = 4>
 DEV void mma2(const Frags& f, f32x16_t (&acc)[4][4], int g) {
   const int mb = kGrpM[g], nb = kGrpN[g];
+  if (mb >= NMB) return;
   acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[nb], f.a[mb], acc[mb][nb], 0, 0, 0);
   acc[mb][nb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[nb + 1], f.a[mb], acc[mb][nb + 1], 0, 0, 0);
 }
@@ -235,7 +241,7 @@ struct MncOperand {
 //    is then done with slice s-1, whose slot takes slice s+3);
 //  phase 2: fragments of slice s+1 / k-half 0 are read and loads 0..3 of
 //    slice s+3 issued, while the MFMAs of k-half 1 run.
-template <int AL, int BL, class Issue>
+template <int AL, int BL, int NMB = 4, class Issue>
 DEV void mainloop(const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f32x16_t (&acc)[4][4], int wm,
                   int wn, int lane) {
   if (nsteps <= 0) return;
@@ -250,7 +256,7 @@ DEV void mainloop(const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f
   wait_barrier<12>();  // slice 0 landed
   Frags f0, f1;
 #pragma unroll
-  for (int g = 0; g < 8; ++g) load_frag<AL, BL>(f0, lds, 0, wm, wn, lane, g);
+  for (int g = 0; g < 8; ++g) load_frag<AL, BL, NMB>(f0, lds, 0, wm, wn, lane, g);
 #pragma unroll 1
   for (int s = 0; s < nsteps - 1; ++s) {
     const uint16_t* cur = slot(s);
@@ -258,27 +264,27 @@ DEV void mainloop(const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       if (g & 1) issue(s + 2, slot_addr(s + 2), 4 + (g >> 1));
-      load_frag<AL, BL>(f1, cur, 1, wm, wn, lane, g);
+      load_frag<AL, BL, NMB>(f1, cur, 1, wm, wn, lane, g);
       __builtin_amdgcn_sched_barrier(0);
-      mma2(f0, acc, g);
+      mma2<NMB>(f0, acc, g);
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_barrier<8>();  // slice s+1 landed; slot of slice s-1 free
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       if (g & 1) issue(s + 3, slot_addr(s + 3), g >> 1);
-      load_frag<AL, BL>(f0, nxt, 0, wm, wn, lane, g);
+      load_frag<AL, BL, NMB>(f0, nxt, 0, wm, wn, lane, g);
       __builtin_amdgcn_sched_barrier(0);
-      mma2(f1, acc, g);
+      mma2<NMB>(f1, acc, g);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
-  for (int g = 0; g < 8; ++g) load_frag<AL, BL>(f1, slot(nsteps - 1), 1, wm, wn, lane, g);
+  for (int g = 0; g < 8; ++g) load_frag<AL, BL, NMB>(f1, slot(nsteps - 1), 1, wm, wn, lane, g);
 #pragma unroll
-  for (int g = 0; g < 8; ++g) mma2(f0, acc, g);
+  for (int g = 0; g < 8; ++g) mma2<NMB>(f0, acc, g);
 #pragma unroll
-  for (int g = 0; g < 8; ++g) mma2(f1, acc, g);
+  for (int g = 0; g < 8; ++g) mma2<NMB>(f1, acc, g);
   block_barrier();
 }
 

@@ -117,6 +117,8 @@ hipError_t launch_rowgemm(const RowGemmParams& P, int kind, bool bf16, int64_t g
 hipError_t launch_wgrad(const WgradParams& P, int which, bool bf16, int64_t grid, hipStream_t st);
 hipError_t launch_wgrad_prep(const WgradPrepParams& P, int64_t grid, hipStream_t st);
 hipError_t launch_wgrad_reduce(const WgradPrepParams& P, int64_t grid, hipStream_t st);
+// bf16: both weight gradients (P1: dW1, P2: dW2) in one launch, schedule computed in-kernel
+hipError_t launch_wgrad_pair(const WgradParams& P1, const WgradParams& P2, int ncu, int64_t grid, hipStream_t st);
 int gemm_tile_m(bool bf16);
 int gemm_tile_n(bool bf16);
 

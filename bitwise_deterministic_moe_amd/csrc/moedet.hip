@@ -256,8 +256,12 @@ MOE_API const char* moe_stage_names(const moe_problem* p, moe_mode mode, int cal
     case 2: {
       Plan pl;
       validate(p, &pl);
-      if (at) return "wgrad_prep_zero,wgrad_fc1,wgrad_fc2";
-      return pl.may_split ? "wgrad_prep,wgrad_fc1,wgrad_fc2,wgrad_reduce" : "wgrad_prep,wgrad_fc1,wgrad_fc2";
+      if (!pl.bf16) {
+        if (at) return "wgrad_prep_zero,wgrad_fc1,wgrad_fc2";
+        return pl.may_split ? "wgrad_prep,wgrad_fc1,wgrad_fc2,wgrad_reduce" : "wgrad_prep,wgrad_fc1,wgrad_fc2";
+      }
+      if (at) return pl.may_split ? "wgrad_prep_zero,wgrad_fc1_fc2" : "wgrad_fc1_fc2";
+      return pl.may_split ? "wgrad_fc1_fc2,wgrad_reduce" : "wgrad_fc1_fc2";
     }
   }
   return nullptr;
@@ -519,46 +523,59 @@ MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routin
   Q.dw2 = dw2;
   Q.slots1 = slots1;
   Q.slots2 = slots2;
-  sg.mark();
-  HIP_TRY(launch_wgrad_prep(Q, at ? 1024 : 1, st));
 
-  WgradParams W{};
-  W.counts = routing->counts;
-  W.offsets = routing->offsets;
-  W.row_tok = routing->row_tok;
-  W.sched = sched;
-  W.groups = pl.el;
-  W.kc = pl.kc;
-  W.atomic = at;
-  W.seed = seed;
-  // dW1_g [D][F] = x[row_tok]^T dh
-  W.M = pl.D;
-  W.N = pl.F;
+  WgradParams W1{};
+  W1.counts = routing->counts;
+  W1.offsets = routing->offsets;
+  W1.row_tok = routing->row_tok;
+  W1.sched = sched;
+  W1.groups = pl.el;
+  W1.kc = pl.kc;
+  W1.atomic = at;
+  W1.seed = seed;
   const uint32_t rows_f_bytes = (uint32_t)(pl.rows_cap * pl.F * pl.esize);
   const uint32_t tok_d_bytes = (uint32_t)(pl.T * pl.D * pl.esize);
-  W.a = x;
-  W.lda = pl.D;
-  W.a_bytes = tok_d_bytes;
-  W.b = dh;
-  W.ldb = pl.F;
-  W.b_bytes = rows_f_bytes;
-  W.dw = dw1;
-  W.slots = slots1;
-  sg.mark();
-  HIP_TRY(launch_wgrad(W, 1, pl.bf16, wgrad_grid(pl, pl.D, pl.F), st));
+  WgradParams W2 = W1;
+  // dW1_g [D][F] = x[row_tok]^T dh
+  W1.M = pl.D;
+  W1.N = pl.F;
+  W1.a = x;
+  W1.lda = pl.D;
+  W1.a_bytes = tok_d_bytes;
+  W1.b = dh;
+  W1.ldb = pl.F;
+  W1.b_bytes = rows_f_bytes;
+  W1.dw = dw1;
+  W1.slots = slots1;
   // dW2_g [F][D] = (p relu(h)^2)^T dy[row_tok]
-  W.M = pl.F;
-  W.N = pl.D;
-  W.a = act_p;
-  W.lda = pl.F;
-  W.a_bytes = rows_f_bytes;
-  W.b = dy;
-  W.ldb = pl.D;
-  W.b_bytes = tok_d_bytes;
-  W.dw = dw2;
-  W.slots = slots2;
-  sg.mark();
-  HIP_TRY(launch_wgrad(W, 2, pl.bf16, wgrad_grid(pl, pl.F, pl.D), st));
+  W2.M = pl.F;
+  W2.N = pl.D;
+  W2.a = act_p;
+  W2.lda = pl.F;
+  W2.a_bytes = rows_f_bytes;
+  W2.b = dy;
+  W2.ldb = pl.D;
+  W2.b_bytes = tok_d_bytes;
+  W2.dw = dw2;
+  W2.slots = slots2;
+
+  if (pl.bf16) {
+    // atomic mode zeroes dW of split experts before their chunks add into it
+    if (at && pl.may_split) {
+      sg.mark();
+      HIP_TRY(launch_wgrad_prep(Q, 1024, st));
+    }
+    const int64_t units = (int64_t)(pl.el + pl.wslots) * (pl.D / pl.bm) * (pl.F / pl.bn);
+    sg.mark();
+    HIP_TRY(launch_wgrad_pair(W1, W2, device_cu_count(), grid_for_unit_rounds(2 * units), st));
+  } else {
+    sg.mark();
+    HIP_TRY(launch_wgrad_prep(Q, at ? 1024 : 1, st));
+    sg.mark();
+    HIP_TRY(launch_wgrad(W1, 1, pl.bf16, wgrad_grid(pl, pl.D, pl.F), st));
+    sg.mark();
+    HIP_TRY(launch_wgrad(W2, 2, pl.bf16, wgrad_grid(pl, pl.F, pl.D), st));
+  }
   if (!at && pl.may_split) {
     sg.mark();
     HIP_TRY(launch_wgrad_reduce(Q, 1024, st));

@@ -102,15 +102,16 @@ def test_workspace_sizes_and_rows_cap():
     fa, da, wa = moe.moe_workspace_size(p, moe.ATOMIC)
     # chunk 4 * mean rows = 4096 >= tokens: no expert can split, no partial slots
     assert wa == wg and da >= 4096 * 1024 * 4
-    assert moe.moe_stage_names(p, 0, 2) == ["wgrad_prep", "wgrad_fc1", "wgrad_fc2"]
+    assert moe.moe_stage_names(p, 0, 2) == ["wgrad_fc1_fc2"]
     # 512 experts top-22: chunk 768 rows < tokens, split slots in the deterministic workspace
     latent = moe.Problem(4096, 2048, 2048, 512, 22)
     _, _, wl = moe.moe_workspace_size(latent, moe.DETERMINISTIC)
     _, _, wla = moe.moe_workspace_size(latent, moe.ATOMIC)
     assert wl - wla >= 2 * (4096 * 22 // 768) * 2048 * 2048 * 4
-    assert moe.moe_stage_names(latent, 0, 2) == ["wgrad_prep", "wgrad_fc1", "wgrad_fc2", "wgrad_reduce"]
+    assert moe.moe_stage_names(latent, 0, 2) == ["wgrad_fc1_fc2", "wgrad_reduce"]
+    assert moe.moe_stage_names(latent, 1, 2) == ["wgrad_prep_zero", "wgrad_fc1_fc2"]
     shard = moe.Problem(16384, 2048, 2048, 512, 22, 0, 4, "bf16", 0)
     assert moe.moe_rows_cap(shard) == 16384 * 4
     assert moe.moe_stage_names(p, 0, 1) == ["fc2_dgrad_dprob_partials", "fc1_dgrad_dprob_combine",
                                             "dx_combine_gather"]
-    assert moe.moe_stage_names(p, 1, 2) == ["wgrad_prep_zero", "wgrad_fc1", "wgrad_fc2"]
+    assert moe.moe_stage_names(p, 1, 2) == ["wgrad_fc1_fc2"]
