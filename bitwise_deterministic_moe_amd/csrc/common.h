@@ -30,7 +30,9 @@ DEV uint32_t pack_bf16x2(float lo, float hi) {
 
 DEV uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
-DEV float relu(float v) { return v > 0.f ? v : 0.f; }
+// max(v, 0) with +0 for every v <= 0: as integers, the bit patterns of
+// negative floats (and -0) are negative, so one integer max does it.
+DEV float relu(float v) { return __int_as_float(max(__float_as_int(v), 0)); }
 
 // ------------------------------------------------------------------ hashing
 // SplitMix64 output finalizer (Steele, Lea, Flood 2014).

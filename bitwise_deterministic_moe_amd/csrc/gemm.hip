@@ -86,6 +86,10 @@ struct RowTile {
 enum { kTileNone = 0, kTileGemm = 1, kTileSide = 2 };
 template <int BMv, int BNv>
 DEV int row_tile(const RowGemmParams& P, int64_t* s_pre, int64_t* s_tmp, RowTile& t) {
+  if (P.side_units > 0 && (int64_t)blockIdx.x >= P.gemm_grid) {
+    t.nt = (int)(blockIdx.x - P.gemm_grid);  // side unit index
+    return t.nt < P.side_units ? kTileSide : kTileNone;
+  }
   block_exclusive_scan<256>(s_pre, s_tmp, P.groups, [&](int g) {
     const int c = P.counts[g];
     return ((int64_t)(c / BMv) << 32) | (int64_t)(c % BMv != 0);
@@ -94,12 +98,8 @@ DEV int row_tile(const RowGemmParams& P, int64_t* s_pre, int64_t* s_tmp, RowTile
   const int64_t tot = s_pre[P.groups];
   const int64_t nfull = tot >> 32;
   const int64_t U = (nfull + (tot & 0xffffffffll)) * nN;
-  const int64_t L = map_unit_rounds(blockIdx.x, U + P.side_units, P.ncu, P.seed);
+  const int64_t L = map_unit_rounds(blockIdx.x, U, P.ncu, P.seed);
   if (L < 0) return kTileNone;
-  if (L >= U) {
-    t.nt = (int)(L - U);  // side unit index
-    return kTileSide;
-  }
   const int64_t mt = L / nN;
   t.nt = (int)(L % nN);
   if (mt < nfull) {
@@ -143,24 +143,46 @@ DEV int row_tile(const RowGemmParams& P, int64_t* s_pre, int64_t* s_tmp, RowTile
   return kTileGemm;
 }
 
-// Side unit u: the dprob combine of flat slots [u*kSideSlots, ...): groups of
-// GS = next_pow2(n_tiles) lanes, lane q loads partial q (0 for q >=
-// n_tiles) and the group folds with xor shuffles at distance 1, 2, 4, ...;
-// the tree depends on n_tiles only and a + b == b + a in IEEE arithmetic,
-// so every lane ends with the same bits.  Slots of non-local experts get 0.
+// Side unit u: the dprob combine of flat slots [u*kSideSlots, ...), one
+// thread per slot.  The n_tiles partials of the slot's row are added as a
+// fixed pairwise tree over GS = next_pow2(n_tiles) positions (missing ones
+// are 0): level d adds position q + d into q for q = 0, 2d, 4d, ...  The
+// tree depends on n_tiles only.  Slots of non-local experts get 0.
+template <int GS>
+DEV float tree_sum(const float* pr, int n) {
+  float v[GS];
+#pragma unroll
+  for (int q = 0; q < GS; ++q) v[q] = q < n ? pr[q] : 0.f;
+#pragma unroll
+  for (int d = 1; d < GS; d <<= 1)
+#pragma unroll
+    for (int q = 0; q < GS; q += 2 * d) v[q] = v[q] + v[q + d];
+  return v[0];
+}
+
 DEV void dprob_side(const RowGemmParams& P, int u) {
   int gs = 1;
   while (gs < P.n_tiles) gs <<= 1;
-  const int per = 256 / gs;
-  const int q = threadIdx.x % gs;
   const int64_t s0 = (int64_t)u * kSideSlots;
-  for (int j = threadIdx.x / gs; j < kSideSlots; j += per) {
+#pragma unroll 4
+  for (int j = threadIdx.x; j < kSideSlots; j += 256) {
     const int64_t i = s0 + j;
-    const bool valid = i < P.side_nslot;  // uniform per lane group
-    const int32_t r = valid ? P.side_slot_row[i] : -1;
-    float v = (r >= 0 && q < P.n_tiles) ? P.part[(int64_t)r * P.n_tiles + q] : 0.f;
-    for (int d = 1; d < gs; d <<= 1) v = v + __shfl_xor(v, d, 64);
-    if (valid && q == 0) P.dprob[i] = r >= 0 ? v : 0.f;
+    if (i >= P.side_nslot) break;
+    const int32_t r = P.side_slot_row[i];
+    float out = 0.f;
+    if (r >= 0) {
+      const float* pr = P.part + (int64_t)r * P.n_tiles;
+      switch (gs) {
+        case 1: out = tree_sum<1>(pr, P.n_tiles); break;
+        case 2: out = tree_sum<2>(pr, P.n_tiles); break;
+        case 4: out = tree_sum<4>(pr, P.n_tiles); break;
+        case 8: out = tree_sum<8>(pr, P.n_tiles); break;
+        case 16: out = tree_sum<16>(pr, P.n_tiles); break;
+        case 32: out = tree_sum<32>(pr, P.n_tiles); break;
+        default: out = tree_sum<64>(pr, P.n_tiles); break;
+      }
+    }
+    P.dprob[i] = out;
   }
 }
 
@@ -323,12 +345,12 @@ constexpr int kStageRow = 260;                       // floats per staged row
 constexpr int kStageBytes = 64 * kStageRow * 4;      // 66,560 bytes, inside the main-loop ring
 static_assert(kStageBytes <= bf::LDS_BYTES, "epilogue stage must fit in the ring");
 
-// Pass p covers tile rows 64p..64p+63.  In step st (0..15) of a pass, thread
-// tid owns row 64p + 4*st + tid/64 and columns 4*(tid%64)..+3, so each wave
-// handles one whole row per step and control flow is uniform per wave.
-// Between passes only LDS traffic has to be ordered, so the barriers wait on
-// LDS operations alone and global stores stay in flight.  Everything is fully
-// unrolled so that per-step data lives in registers.
+// Pass p covers tile rows 64p..64p+63.  In step st (0..15) of a pass,
+// thread tid owns row 64p + 4*st + tid/64 and columns 4*(tid%64)..+3, so
+// each wave handles one whole row per step and control flow is uniform per
+// wave.  Between passes only LDS traffic has to be ordered, so the barriers
+// wait on LDS operations alone and global stores stay in flight.
+// Everything is fully unrolled so that per-step data lives in registers.
 DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 DEV int staged_row(int p, int st, int tid) {
   return 64 * p + 4 * st + __builtin_amdgcn_readfirstlane(tid >> 6);  // one row per wave
@@ -401,10 +423,13 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t ring = bf::lds_base(lds);
   const int wm = wave >> 1, wn = wave & 1;
+  __shared__ float s_prob[bf::BM];  // routing probability of each tile row (dgrad epilogue)
   RowTile t;
   const int kind = row_tile<bf::BM, bf::BN>(P, s_pre, s_tmp, t);
   if (kind == kTileSide) dprob_side(P, t.nt);
   if (kind != kTileGemm) return;
+  if constexpr (EPI == kEpiDgrad2)
+    s_prob[tid] = tid < t.mvalid ? P.row_prob[t.off + t.m0 + tid] : 0.f;  // read after the main loop's barriers
 
   bf::KcOperand oa;
   // Branch-free so that the four row-index loads of a thread are in flight
@@ -489,6 +514,7 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
       };
       const RowGemmParams& P;
       const RowTile& t;
+      const float* prob;
       int tid;
       DEV void load(Data& d, int p) {
         const __amdgpu_buffer_rsrc_t rh = buf(P.h);
@@ -499,10 +525,10 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
           const uint32_t grow = (uint32_t)(t.off + t.m0 + (ok ? m : 0));
           d.h[st] = __builtin_amdgcn_raw_buffer_load_b64(
               rh, ok ? (grow * (uint32_t)P.ldh + t.n0 + staged_col(tid)) * 2u : kNoRow, 0, 0);
-          d.p[st] = P.row_prob[grow];
+          d.p[st] = prob[m];
         }
       }
-    } hpre{P, t, tid};
+    } hpre{P, t, s_prob, tid};
     const __amdgpu_buffer_rsrc_t rc = buf(P.c), rc2 = buf(P.c2);
     __shared__ float s_qsum[bf::BM * 16];  // [tile row][quad]
     staged_epilogue(stage, acc, wm, wn, lane, tid, hpre, [&](int m, int col, float (&g)[4], typename HPre::Data& d, int st) {
@@ -627,33 +653,12 @@ __global__ __launch_bounds__(256) void wgrad_bf16_kernel(WgradParams P) {
   wgrad_bf16_tile<A_GATHER, B_GATHER>(P, t, wgrad_dst(P, t), lds, s_rowoff);
 }
 
-// Both weight gradients in one launch: units [0, U1) are dW1 tiles (rows of
-// x gathered by token, dh rows), [U1, U1 + U2) dW2 tiles (act_p rows, dy
-// gathered by token).  The chunk schedule is computed here from counts:
-// per expert S_g = max(1, ceil(cnt_g / kc)) chunks; one packed scan gives the
-// first unit (sum of S, high 32 bits) and the first partial slot (sum of
-// S - 1, low bits) of each expert.
-__global__ __launch_bounds__(256) void wgrad_pair_bf16_kernel(WgradParams P1, WgradParams P2, int ncu) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
-  __shared__ uint32_t s_rowoff[kMaxChunkRows];  // byte offset of each gathered row of the chunk
-  __shared__ int64_t s_tmp[8];
-  int64_t* s_pre = (int64_t*)lds;  // setup only, before the ring is used
-  const int G = P1.groups;
-  const int kc = P1.kc;
-  block_exclusive_scan<256>(s_pre, s_tmp, G, [&](int g) {
-    const int c = P1.counts[g];
-    const int64_t S = c > kc ? (c + kc - 1) / kc : 1;
-    return (S << 32) | (S - 1);
-  });
-  const int tiles1 = (P1.M / bf::BM) * (P1.N / bf::BN), tiles2 = (P2.M / bf::BM) * (P2.N / bf::BN);
-  const int64_t units = s_pre[G] >> 32;
-  const int64_t U1 = units * tiles1, U2 = units * tiles2;
-  int64_t L = map_unit_rounds(blockIdx.x, U1 + U2, ncu, P1.seed);
-  if (L < 0) return;
-  const bool second = L >= U1;
-  const WgradParams& P = second ? P2 : P1;
-  if (second) L -= U1;
-  const int tiles = second ? tiles2 : tiles1;
+// Unit L of one of the two weight gradients of the paired launch; s_pre
+// holds the packed chunk schedule (first unit, first partial slot).
+template <bool A_GATHER, bool B_GATHER>
+DEV void wgrad_pair_unit(const WgradParams& P, int64_t L, int tiles, const int64_t* s_pre, uint16_t* lds,
+                         uint32_t* s_rowoff) {
+  const int G = P.groups, kc = P.kc;
   const int nN = P.N / bf::BN;
   WgradTile t;
   const int64_t u = L / tiles;
@@ -676,10 +681,36 @@ __global__ __launch_bounds__(256) void wgrad_pair_bf16_kernel(WgradParams P1, Wg
   t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
   float* dst = (!P.atomic && t.s > 0) ? P.slots + slot * P.M * P.N : P.dw + (int64_t)t.g * P.M * P.N;
   __syncthreads();  // the scan buffer aliases the ring
-  if (second)
-    wgrad_bf16_tile<false, true>(P2, t, dst, lds, s_rowoff);
+  wgrad_bf16_tile<A_GATHER, B_GATHER>(P, t, dst, lds, s_rowoff);
+}
+
+// Both weight gradients in one launch: units [0, U1) are dW1 tiles (rows of
+// x gathered by token, dh rows), [U1, U1 + U2) dW2 tiles (act_p rows, dy
+// gathered by token).  The chunk schedule is computed here from counts:
+// per expert S_g = max(1, ceil(cnt_g / kc)) chunks; one packed scan gives the
+// first unit (sum of S, high 32 bits) and the first partial slot (sum of
+// S - 1, low bits) of each expert.
+__global__ __launch_bounds__(256) void wgrad_pair_bf16_kernel(WgradParams P1, WgradParams P2, int ncu) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
+  __shared__ uint32_t s_rowoff[kMaxChunkRows];  // byte offset of each gathered row of the chunk
+  __shared__ int64_t s_tmp[8];
+  int64_t* s_pre = (int64_t*)lds;  // setup only, before the ring is used
+  const int G = P1.groups;
+  const int kc = P1.kc;
+  block_exclusive_scan<256>(s_pre, s_tmp, G, [&](int g) {
+    const int c = P1.counts[g];
+    const int64_t S = c > kc ? (c + kc - 1) / kc : 1;
+    return (S << 32) | (S - 1);
+  });
+  const int tiles1 = (P1.M / bf::BM) * (P1.N / bf::BN), tiles2 = (P2.M / bf::BM) * (P2.N / bf::BN);
+  const int64_t units = s_pre[G] >> 32;
+  const int64_t U1 = units * tiles1, U2 = units * tiles2;
+  const int64_t L = map_unit_rounds(blockIdx.x, U1 + U2, ncu, P1.seed);
+  if (L < 0) return;
+  if (L >= U1)
+    wgrad_pair_unit<false, true>(P2, L - U1, tiles2, s_pre, lds, s_rowoff);
   else
-    wgrad_bf16_tile<true, false>(P1, t, dst, lds, s_rowoff);
+    wgrad_pair_unit<true, false>(P1, L, tiles1, s_pre, lds, s_rowoff);
 }
 
 // ================================================================= fp32

@@ -49,9 +49,13 @@ struct RowGemmParams {
   // Side job run by the workgroups after the GEMM tiles (fc1 dgrad, which
   // leaves compute units idle at small shapes): the fixed-order dprob
   // combine of part[] (n_tiles partials per row) for side_nslot flat slots.
+  // Workgroups [gemm_grid, gemm_grid + side_units) run the side units, after
+  // every GEMM workgroup in dispatch order, so the GEMM tiles keep their
+  // XCD-aware placement.
   const int32_t* side_slot_row;
   int64_t side_nslot;
   int side_units;
+  int64_t gemm_grid;
   uint64_t seed;
 };
 

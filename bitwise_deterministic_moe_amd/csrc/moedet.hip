@@ -167,9 +167,9 @@ struct Stager {
   }
 };
 
-int64_t rowgemm_grid(const Plan& pl, int N, int64_t side_units = 0) {
+int64_t rowgemm_grid(const Plan& pl, int N) {
   const int64_t mtiles = (pl.rows_cap + pl.bm - 1) / pl.bm + pl.el;
-  return grid_for_unit_rounds(mtiles * (N / pl.bn) + side_units);
+  return grid_for_unit_rounds(mtiles * (N / pl.bn));
 }
 
 // Compute units of the current device (cached per device ordinal; the
@@ -458,6 +458,7 @@ MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* 
   G2.b_bytes = (uint32_t)(G2.b_gstride * pl.esize);
   G2.c = dxrows;
   G2.ldc = pl.D;
+  const int64_t gemm_grid = rowgemm_grid(pl, pl.D);
   int64_t side = 0;
   if (!at) {
     // the fixed-order dprob combine rides along as side units of this launch
@@ -468,9 +469,10 @@ MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* 
     G2.side_slot_row = routing->slot_row;
     G2.side_nslot = pl.nslot;
     G2.side_units = (int)side;
+    G2.gemm_grid = gemm_grid;
   }
   sg.mark();
-  HIP_TRY(launch_rowgemm(G2, kGemmFc1Dgrad, pl.bf16, rowgemm_grid(pl, pl.D, side), st));
+  HIP_TRY(launch_rowgemm(G2, kGemmFc1Dgrad, pl.bf16, gemm_grid + side, st));
   if (p->combine) {
     if (!at) {
       sg.mark();
