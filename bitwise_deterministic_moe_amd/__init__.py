@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "DETERMINISTIC", "ATOMIC", "Problem", "Routing", "MoeError", "MoeLibraryMissing",
     "load_library", "library_path", "moe_workspace_size", "moe_rows_cap", "moe_stage_names",
-    "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad", "moe_fingerprint", "EXPORTED_SYMBOLS",
+    "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad", "moe_fingerprint", "moe_sched_elems", "EXPORTED_SYMBOLS",
 ]
 
 DETERMINISTIC = 0
@@ -25,8 +25,8 @@ DTYPE_CODE = {"f32": 0, "bf16": 1, "i32": 2, "u8": 3, "i64": 4, "f64": 5}
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 _TORCH_TO_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.int32: 2, torch.uint8: 3,
                   torch.int64: 4, torch.float64: 5}
-EXPORTED_SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_rows_cap", "moe_workspace_size",
-                    "moe_stage_names", "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad",
+EXPORTED_SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_rows_cap", "moe_sched_elems",
+                    "moe_workspace_size", "moe_stage_names", "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad",
                     "moe_fingerprint")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -52,7 +52,7 @@ class _CProblem(ctypes.Structure):
 
 class _CRouting(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("topk_idx", "topk_prob", "counts", "offsets",
-                                                "row_src", "row_tok", "row_prob", "slot_row")]
+                                                "row_src", "row_tok", "row_prob", "slot_row", "sched")]
 
 
 def library_path() -> str:
@@ -75,6 +75,7 @@ def load_library() -> ctypes.CDLL:
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_rows_cap.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+    lib.moe_sched_elems.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
     lib.moe_workspace_size.argtypes = [P, ctypes.c_int, ctypes.POINTER(sz), ctypes.POINTER(sz), ctypes.POINTER(sz)]
     lib.moe_stage_names.restype = ctypes.c_char_p
     lib.moe_stage_names.argtypes = [P, ctypes.c_int, ctypes.c_int]
@@ -83,8 +84,8 @@ def load_library() -> ctypes.CDLL:
     lib.moe_bwd_wgrad.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
     lib.moe_fingerprint.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
                                     vp, vp, vp]
-    for f in ("moe_rows_cap", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad",
-              "moe_fingerprint"):
+    for f in ("moe_rows_cap", "moe_sched_elems", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob",
+              "moe_bwd_wgrad", "moe_fingerprint"):
         getattr(lib, f).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -149,6 +150,7 @@ class Routing:
     row_tok: torch.Tensor
     row_prob: torch.Tensor
     slot_row: torch.Tensor
+    sched: torch.Tensor
 
     @classmethod
     def empty(cls, prob: Problem, device="cuda") -> "Routing":
@@ -157,7 +159,7 @@ class Routing:
         T, k, el, rc = prob.tokens, prob.top_k, prob.local, prob.rows_cap
         return cls(torch.empty((T, k), **i32), torch.empty((T, k), **f32), torch.empty(el, **i32),
                    torch.empty(el + 1, **i32), torch.empty(rc, **i32), torch.empty(rc, **i32),
-                   torch.empty(rc, **f32), torch.empty(T * k, **i32))
+                   torch.empty(rc, **f32), torch.empty(T * k, **i32), torch.empty(moe_sched_elems(prob), **i32))
 
     def c(self) -> _CRouting:
         return _CRouting(*[_ptr(getattr(self, n)) for n, _ in _CRouting._fields_])
@@ -187,6 +189,13 @@ def _ws(nbytes: int, ws: Optional[torch.Tensor], device) -> torch.Tensor:
 def moe_rows_cap(prob: Problem) -> int:
     v = ctypes.c_int64()
     _check(load_library().moe_rows_cap(ctypes.byref(prob.c()), ctypes.byref(v)), "moe_rows_cap")
+    return v.value
+
+
+def moe_sched_elems(prob: Problem) -> int:
+    """int32 elements of Routing.sched."""
+    v = ctypes.c_int64()
+    _check(load_library().moe_sched_elems(ctypes.byref(prob.c()), ctypes.byref(v)), "moe_sched_elems")
     return v.value
 
 

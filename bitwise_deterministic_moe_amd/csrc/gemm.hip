@@ -77,69 +77,30 @@ struct RowTile {
   int64_t off;
 };
 
-// Work unit of this workgroup: (expert g, m-tile, n-tile), a side unit, or
-// nothing.  M-tiles are ordered longest first: the full tiles (expert-major),
-// then each expert's partial last tile by descending row count (ties by
-// expert), so that when units outnumber compute units the last, short round
-// holds the smallest tiles.  The first scan packs, per expert, the number of
-// full tiles (high 32 bits) and of partial tiles (0 or 1, low bits).
+// Work unit of this workgroup: (row tile, n-tile), a side unit, or nothing.
+// Row tiles come from the routing work list (longest first: full tiles, then
+// partial tiles by descending rows), so when units outnumber compute units
+// the last, short round holds the smallest tiles.
 enum { kTileNone = 0, kTileGemm = 1, kTileSide = 2 };
 template <int BMv, int BNv>
-DEV int row_tile(const RowGemmParams& P, int64_t* s_pre, int64_t* s_tmp, RowTile& t) {
+DEV int row_tile(const RowGemmParams& P, RowTile& t) {
   if (P.side_units > 0 && (int64_t)blockIdx.x >= P.gemm_grid) {
     t.nt = (int)(blockIdx.x - P.gemm_grid);  // side unit index
     return t.nt < P.side_units ? kTileSide : kTileNone;
   }
-  block_exclusive_scan<256>(s_pre, s_tmp, P.groups, [&](int g) {
-    const int c = P.counts[g];
-    return ((int64_t)(c / BMv) << 32) | (int64_t)(c % BMv != 0);
-  });
   const int nN = P.N / BNv;
-  const int64_t tot = s_pre[P.groups];
-  const int64_t nfull = tot >> 32;
-  const int64_t U = (nfull + (tot & 0xffffffffll)) * nN;
+  const int64_t U = (int64_t)P.sched[0] * nN;
   const int64_t L = map_unit_rounds(blockIdx.x, U, P.ncu, P.seed);
   if (L < 0) return kTileNone;
   const int64_t mt = L / nN;
   t.nt = (int)(L % nN);
-  if (mt < nfull) {
-    t.g = find_group_by(s_pre, P.groups, mt, [](int64_t v) { return v >> 32; });
-    t.m0 = (int)(mt - (s_pre[t.g] >> 32)) * BMv;
-  } else {
-    // rank q among the partial tiles ordered by (BM - rows, expert):
-    // counting sort by key, then the (q - base)-th expert of the key's bin.
-    const int64_t q = mt - nfull;
-    static_assert(BMv <= 1024 && BMv <= kMaxExperts, "key bins fit the scan buffer");
-    int64_t* s_hist = s_pre + (kMaxExperts + 1) / 2;  // upper half, after the packed scan is consumed
-    __syncthreads();
-    for (int k = threadIdx.x; k <= BMv; k += blockDim.x) s_pre[k] = 0;
-    __syncthreads();
-    for (int g = threadIdx.x; g < P.groups; g += blockDim.x) {
-      const int r = P.counts[g] % BMv;
-      if (r) atomicAdd((unsigned long long*)&s_pre[BMv - r], 1ull);
-    }
-    __syncthreads();
-    block_exclusive_scan<256>(s_hist, s_tmp, BMv, [&](int k) { return s_pre[k]; });
-    const int key = find_group_by(s_hist, BMv, q, [](int64_t v) { return v; });
-    const int64_t rank = q - s_hist[key];
-    __syncthreads();
-    block_exclusive_scan<256>(s_pre, s_tmp, P.groups, [&](int g) {
-      const int r = P.counts[g] % BMv;
-      return (int64_t)(r != 0 && BMv - r == key);
-    });
-    t.g = find_group_by(s_pre, P.groups, rank, [](int64_t v) { return v; });
-    t.m0 = P.counts[t.g] / BMv * BMv;
-  }
-  t.n0 = t.nt * BNv;
-  t.off = P.offsets[t.g];
-  t.mvalid = min(BMv, P.counts[t.g] - t.m0);
-  // uniform across the workgroup: keep them in scalar registers
-  t.g = __builtin_amdgcn_readfirstlane(t.g);
-  t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
-  t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
+  const int4 en = ((const int4*)(P.sched + kSchedHeader))[mt];
+  t.g = __builtin_amdgcn_readfirstlane(en.x);
+  t.m0 = __builtin_amdgcn_readfirstlane(en.y);
+  t.off = (int64_t)__builtin_amdgcn_readfirstlane(en.z - en.y);
+  t.mvalid = __builtin_amdgcn_readfirstlane(en.w);
   t.nt = __builtin_amdgcn_readfirstlane(t.nt);
-  t.mvalid = __builtin_amdgcn_readfirstlane(t.mvalid);
-  t.off = (int64_t)__builtin_amdgcn_readfirstlane((int)t.off);
+  t.n0 = t.nt * BNv;
   return kTileGemm;
 }
 
@@ -418,14 +379,12 @@ DEV void run_mainloop(int nmb, const uint16_t* lds, uint32_t ring, int nsteps, I
 template <int BL, int EPI>
 __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
-  __shared__ int64_t s_pre[kMaxExperts + 1];
-  __shared__ int64_t s_tmp[8];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t ring = bf::lds_base(lds);
   const int wm = wave >> 1, wn = wave & 1;
   __shared__ float s_prob[bf::BM];  // routing probability of each tile row (dgrad epilogue)
   RowTile t;
-  const int kind = row_tile<bf::BM, bf::BN>(P, s_pre, s_tmp, t);
+  const int kind = row_tile<bf::BM, bf::BN>(P, t);
   if (kind == kTileSide) dprob_side(P, t.nt);
   if (kind != kTileGemm) return;
   if constexpr (EPI == kEpiDgrad2)
@@ -653,76 +612,53 @@ __global__ __launch_bounds__(256) void wgrad_bf16_kernel(WgradParams P) {
   wgrad_bf16_tile<A_GATHER, B_GATHER>(P, t, wgrad_dst(P, t), lds, s_rowoff);
 }
 
-// Unit L of one of the two weight gradients of the paired launch; s_pre
-// holds the packed chunk schedule (first unit, first partial slot).
+// Unit L of one of the two weight gradients of the paired launch: tile
+// L % tiles of weight-gradient unit L / tiles of the routing work list.
 template <bool A_GATHER, bool B_GATHER>
-DEV void wgrad_pair_unit(const WgradParams& P, int64_t L, int tiles, const int64_t* s_pre, uint16_t* lds,
-                         uint32_t* s_rowoff) {
-  const int G = P.groups, kc = P.kc;
+DEV void wgrad_pair_unit(const WgradParams& P, int64_t L, int tiles, uint16_t* lds, uint32_t* s_rowoff) {
   const int nN = P.N / bf::BN;
-  WgradTile t;
   const int64_t u = L / tiles;
   const int tile = (int)(L % tiles);
-  t.g = find_group_by(s_pre, G, u, [](int64_t v) { return v >> 32; });
-  t.s = (int)(u - (s_pre[t.g] >> 32));
-  const int64_t slot = (s_pre[t.g] & 0xffffffffll) + t.s - 1;
-  const int cnt = P.counts[t.g];
-  t.S = cnt > kc ? (cnt + kc - 1) / kc : 1;
-  const int k_lo = (int)((int64_t)t.s * cnt / t.S), k_hi = (int)((int64_t)(t.s + 1) * cnt / t.S);
-  t.klen = k_hi - k_lo;
-  t.row0 = (int64_t)P.offsets[t.g] + k_lo;
+  const int4 en = ((const int4*)(P.units + P.units_at))[u];
+  WgradTile t;
+  t.g = __builtin_amdgcn_readfirstlane(en.x & 0x3fffffff);
+  t.S = (en.x >> 30) ? 2 : 1;  // only "split or not" matters here
+  t.s = 0;
+  t.row0 = (int64_t)__builtin_amdgcn_readfirstlane(en.y);
+  t.klen = __builtin_amdgcn_readfirstlane(en.z);
+  const int slot = __builtin_amdgcn_readfirstlane(en.w);
   t.m0 = (tile / nN) * bf::BM;
   t.n0 = (tile % nN) * bf::BN;
-  t.g = __builtin_amdgcn_readfirstlane(t.g);
-  t.s = __builtin_amdgcn_readfirstlane(t.s);
-  t.S = __builtin_amdgcn_readfirstlane(t.S);
-  t.klen = __builtin_amdgcn_readfirstlane(t.klen);
-  t.m0 = __builtin_amdgcn_readfirstlane(t.m0);
-  t.n0 = __builtin_amdgcn_readfirstlane(t.n0);
-  float* dst = (!P.atomic && t.s > 0) ? P.slots + slot * P.M * P.N : P.dw + (int64_t)t.g * P.M * P.N;
-  __syncthreads();  // the scan buffer aliases the ring
+  float* dst = (!P.atomic && slot >= 0) ? P.slots + (int64_t)slot * P.M * P.N : P.dw + (int64_t)t.g * P.M * P.N;
   wgrad_bf16_tile<A_GATHER, B_GATHER>(P, t, dst, lds, s_rowoff);
 }
 
 // Both weight gradients in one launch: units [0, U1) are dW1 tiles (rows of
 // x gathered by token, dh rows), [U1, U1 + U2) dW2 tiles (act_p rows, dy
-// gathered by token).  The chunk schedule is computed here from counts:
-// per expert S_g = max(1, ceil(cnt_g / kc)) chunks; one packed scan gives the
-// first unit (sum of S, high 32 bits) and the first partial slot (sum of
-// S - 1, low bits) of each expert.
+// gathered by token), over the (expert, K chunk) units of the routing work
+// list.
 __global__ __launch_bounds__(256) void wgrad_pair_bf16_kernel(WgradParams P1, WgradParams P2, int ncu) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
   __shared__ uint32_t s_rowoff[kMaxChunkRows];  // byte offset of each gathered row of the chunk
-  __shared__ int64_t s_tmp[8];
-  int64_t* s_pre = (int64_t*)lds;  // setup only, before the ring is used
-  const int G = P1.groups;
-  const int kc = P1.kc;
-  block_exclusive_scan<256>(s_pre, s_tmp, G, [&](int g) {
-    const int c = P1.counts[g];
-    const int64_t S = c > kc ? (c + kc - 1) / kc : 1;
-    return (S << 32) | (S - 1);
-  });
   const int tiles1 = (P1.M / bf::BM) * (P1.N / bf::BN), tiles2 = (P2.M / bf::BM) * (P2.N / bf::BN);
-  const int64_t units = s_pre[G] >> 32;
+  const int64_t units = P1.units[1];
   const int64_t U1 = units * tiles1, U2 = units * tiles2;
   const int64_t L = map_unit_rounds(blockIdx.x, U1 + U2, ncu, P1.seed);
   if (L < 0) return;
   if (L >= U1)
-    wgrad_pair_unit<false, true>(P2, L - U1, tiles2, s_pre, lds, s_rowoff);
+    wgrad_pair_unit<false, true>(P2, L - U1, tiles2, lds, s_rowoff);
   else
-    wgrad_pair_unit<true, false>(P1, L, tiles1, s_pre, lds, s_rowoff);
+    wgrad_pair_unit<true, false>(P1, L, tiles1, lds, s_rowoff);
 }
 
 // ================================================================= fp32
 template <bool B_MNC, int EPI>
 __global__ __launch_bounds__(256) void rowgemm_f32_kernel(RowGemmParams P) {
   __shared__ __attribute__((aligned(16))) float lds[f32::LDS_BYTES / 4];
-  __shared__ int64_t s_pre[kMaxExperts + 1];
-  __shared__ int64_t s_tmp[8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   RowTile t;
-  const int kind = row_tile<f32::BM, f32::BN>(P, s_pre, s_tmp, t);
+  const int kind = row_tile<f32::BM, f32::BN>(P, t);
   if (kind == kTileSide) dprob_side(P, t.nt);
   if (kind != kTileGemm) return;
   float* As0 = lds;

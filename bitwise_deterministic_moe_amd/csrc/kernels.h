@@ -45,7 +45,8 @@ struct RowGemmParams {
   int n_tiles;
   float* dprob;
   int atomic;
-  int ncu;  // compute units of the device (work-unit rounds)
+  int ncu;                // compute units of the device (work-unit rounds)
+  const int32_t* sched;   // routing.sched (row-tile list)
   // Side job run by the workgroups after the GEMM tiles (fc1 dgrad, which
   // leaves compute units idle at small shapes): the fixed-order dprob
   // combine of part[] (n_tiles partials per row) for side_nslot flat slots.
@@ -65,6 +66,8 @@ struct WgradParams {
   const int32_t* counts;
   const int32_t* offsets;
   const int32_t* row_tok;
+  const int32_t* units;  // routing.sched: [1] = unit count; entries at `units_at`
+  int64_t units_at;
   const int32_t* sched;  // unit_start[G+1], slot_base[G+1]
   int groups;
   int M, N;
@@ -111,7 +114,18 @@ struct RouteParams {
   int nchunk;
   int atomic;
   uint64_t seed;
+  // backward work list (routing.sched), see sched_layout in moedet.hip
+  int32_t* sched;
+  int bm;          // row-tile height of the backward GEMMs
+  int kc;          // weight-gradient K chunk (rows)
+  int64_t mt_cap;  // capacity of the row-tile list
 };
+
+// routing.sched: [0] row tiles, [1] weight-gradient units, [2..3] 0, then
+// mt_cap row-tile entries {expert, first row in the expert, first row
+// overall, rows} and the weight-gradient unit entries {expert | split << 30,
+// first row, rows, partial slot or -1}, four int32 each.
+constexpr int kSchedHeader = 4;
 
 hipError_t launch_route(const RouteParams& P, hipStream_t st);
 hipError_t launch_permute_scan(const RouteParams& P, hipStream_t st);

@@ -30,6 +30,9 @@ struct Plan {
   int kc;             // wgrad K chunk (rows)
   bool may_split;     // some expert can hold more than kc rows
   int64_t wslots;     // wgrad partial slots per dW
+  int64_t mt_cap;     // routing.sched: row-tile entries
+  int64_t wu_cap;     // routing.sched: weight-gradient unit entries
+  int64_t sched_elems;
   size_t esize;
 };
 
@@ -86,6 +89,10 @@ moe_status validate(const moe_problem* p, Plan* pl) {
     pl->kc = (int)kc;
     pl->may_split = kc < p->tokens;
     pl->wslots = pl->may_split ? pl->rows_cap / kc : 0;
+    // sum over experts of ceil(cnt/BM) <= rows_cap/BM + El; of max(1, ceil(cnt/kc)) <= El + rows_cap/kc
+    pl->mt_cap = (pl->rows_cap + bm - 1) / bm + pl->el;
+    pl->wu_cap = pl->el + pl->rows_cap / kc + 1;
+    pl->sched_elems = kSchedHeader + 4 * (pl->mt_cap + pl->wu_cap);
     pl->esize = bf16 ? 2 : 4;
   }
   return MOE_OK;
@@ -238,6 +245,15 @@ MOE_API moe_status moe_workspace_size(const moe_problem* p, moe_mode mode, size_
   return MOE_OK;
 }
 
+MOE_API moe_status moe_sched_elems(const moe_problem* p, int64_t* elems) {
+  Plan pl;
+  const moe_status s = validate(p, &pl);
+  if (s != MOE_OK) return s;
+  if (!elems) return MOE_ERR_NULL;
+  *elems = pl.sched_elems;
+  return MOE_OK;
+}
+
 MOE_API const char* moe_stage_names(const moe_problem* p, moe_mode mode, int call) {
   if (validate(p, nullptr) != MOE_OK) return nullptr;
   const bool at = mode == MOE_ATOMIC;
@@ -276,7 +292,7 @@ MOE_API moe_status moe_fwd(const moe_problem* p, const float* logits, const void
   if (mode != MOE_DETERMINISTIC && mode != MOE_ATOMIC) return MOE_ERR_MODE;
   const bool at = mode == MOE_ATOMIC;
   const bool has_tok = pl.T > 0, has_rows = pl.rows_cap > 0;
-  if (!routing || !w1 || !w2 || !routing->counts || !routing->offsets) return MOE_ERR_NULL;
+  if (!routing || !w1 || !w2 || !routing->counts || !routing->offsets || !routing->sched) return MOE_ERR_NULL;
   if (has_tok && (!logits || !x || !y_or_rows || !routing->topk_idx || !routing->topk_prob ||
                   !routing->slot_row))
     return MOE_ERR_NULL;
@@ -306,6 +322,10 @@ MOE_API moe_status moe_fwd(const moe_problem* p, const float* logits, const void
   R.row_tok = routing->row_tok;
   R.row_prob = routing->row_prob;
   R.slot_row = routing->slot_row;
+  R.sched = routing->sched;
+  R.bm = pl.bm;
+  R.kc = pl.kc;
+  R.mt_cap = pl.mt_cap;
   R.nchunk = pl.nchunk;
   R.atomic = at;
   R.seed = seed;
@@ -322,6 +342,7 @@ MOE_API moe_status moe_fwd(const moe_problem* p, const float* logits, const void
   G.offsets = routing->offsets;
   G.groups = pl.el;
   G.ncu = device_cu_count();
+  G.sched = routing->sched;
   G.seed = seed;
   // fc1: h = x[row_tok] W1_g, W1 [D][F]
   void* arows = wsb + L.arows;
@@ -388,7 +409,7 @@ MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* 
   if (mode != MOE_DETERMINISTIC && mode != MOE_ATOMIC) return MOE_ERR_MODE;
   const bool at = mode == MOE_ATOMIC;
   const bool has_tok = pl.T > 0, has_rows = pl.rows_cap > 0;
-  if (!routing || !w1 || !w2 || !routing->counts || !routing->offsets) return MOE_ERR_NULL;
+  if (!routing || !w1 || !w2 || !routing->counts || !routing->offsets || !routing->sched) return MOE_ERR_NULL;
   if (has_tok && (!dy || !dx_or_rows || !dprob || !routing->slot_row || !routing->topk_prob)) return MOE_ERR_NULL;
   if (has_rows && (!h || !dh || !act_p || !routing->row_src || !routing->row_tok || !routing->row_prob))
     return MOE_ERR_NULL;
@@ -413,6 +434,7 @@ MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* 
   G.offsets = routing->offsets;
   G.groups = pl.el;
   G.ncu = device_cu_count();
+  G.sched = routing->sched;
   G.seed = seed;
   // fc2 dgrad: G = dy[row_tok] W2_g^T; W2 [F][D] read as [N=F][K=D].
   G.N = pl.F;
@@ -445,6 +467,7 @@ MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* 
   G2.offsets = routing->offsets;
   G2.groups = pl.el;
   G2.ncu = device_cu_count();
+  G2.sched = routing->sched;
   G2.seed = seed;
   G2.N = pl.D;
   G2.K = pl.F;
@@ -499,7 +522,7 @@ MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routin
   if (mode != MOE_DETERMINISTIC && mode != MOE_ATOMIC) return MOE_ERR_MODE;
   const bool at = mode == MOE_ATOMIC;
   const bool has_tok = pl.T > 0, has_rows = pl.rows_cap > 0;
-  if (!routing || !dw1 || !dw2 || !routing->counts || !routing->offsets) return MOE_ERR_NULL;
+  if (!routing || !dw1 || !dw2 || !routing->counts || !routing->offsets || !routing->sched) return MOE_ERR_NULL;
   if (has_tok && (!x || !dy)) return MOE_ERR_NULL;
   if (has_rows && (!dh || !act_p || !routing->row_tok)) return MOE_ERR_NULL;
   const WgradWs L = wgrad_layout(pl, at);
@@ -530,6 +553,8 @@ MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routin
   W1.counts = routing->counts;
   W1.offsets = routing->offsets;
   W1.row_tok = routing->row_tok;
+  W1.units = routing->sched;
+  W1.units_at = kSchedHeader + 4 * pl.mt_cap;
   W1.sched = sched;
   W1.groups = pl.el;
   W1.kc = pl.kc;

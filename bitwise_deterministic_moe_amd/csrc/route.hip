@@ -99,10 +99,21 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams P) {
   for (int i = tid; i < P.el; i += 256) P.hist[b * P.el + i] = s_hist[i];
 }
 
-// hist[c][e] -> exclusive row base of chunk c for expert e; counts, offsets.
+// hist[c][e] -> exclusive row base of chunk c for expert e; counts, offsets;
+// then the backward work list (routing.sched), from counts alone:
+//   row tiles of BM rows: every expert's full tiles (expert-major), then the
+//   partial last tiles ordered by descending rows (ties by expert), so that a
+//   GEMM whose tiles outnumber the compute units leaves the smallest tiles
+//   for its last round;
+//   weight-gradient units: expert g in S_g = max(1, ceil(cnt_g / kc)) chunks,
+//   chunk s covering rows [s cnt/S, (s+1) cnt/S); chunks s >= 1 of a split
+//   expert own partial slot sum_{g'<g} (S_g' - 1) + s - 1.
 __global__ __launch_bounds__(1024) void permute_scan_kernel(RouteParams P) {
   __shared__ int s_pre[kMaxExperts + 1];
   __shared__ int s_tmp[16];
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_off[kMaxExperts];
+  __shared__ uint32_t s_key[1024];
   const int e = threadIdx.x;
   int total = 0;
   if (e < P.el) {
@@ -113,14 +124,73 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(RouteParams P) {
       total += v;
     }
     P.counts[e] = total;
+    s_cnt[e] = total;
   }
-  block_exclusive_scan<1024>(s_pre, s_tmp, P.el, [&](int g) { return P.counts[g]; });
+  block_exclusive_scan<1024>(s_pre, s_tmp, P.el, [&](int g) { return s_cnt[g]; });
   if (e <= P.el) P.offsets[e] = s_pre[e];
+  const int off_e = e < P.el ? s_pre[e] : 0;
   if (e < P.el) {
-    const int base = s_pre[e];
-    for (int c = 0; c < P.nchunk; ++c) P.hist[(int64_t)c * P.el + e] += base;
-    if (P.atomic) P.cursor[e] = base;
+    s_off[e] = off_e;
+    for (int c = 0; c < P.nchunk; ++c) P.hist[(int64_t)c * P.el + e] += off_e;
+    if (P.atomic) P.cursor[e] = off_e;
   }
+  __syncthreads();
+
+  int4* mt = (int4*)(P.sched + kSchedHeader);
+  const int BM = P.bm;
+  // full row tiles, expert-major
+  block_exclusive_scan<1024>(s_pre, s_tmp, P.el, [&](int g) { return s_cnt[g] / BM; });
+  const int nfull = s_pre[P.el];
+  if (e < P.el)
+    for (int i = 0; i < total / BM; ++i) mt[s_pre[e] + i] = int4{e, i * BM, off_e + i * BM, BM};
+  // partial tiles: bitonic sort of (BM - rows) << 10 | expert
+  s_key[e] = (e < P.el && total % BM) ? ((uint32_t)(BM - total % BM) << 10) | (uint32_t)e : 0xffffffffu;
+  __syncthreads();
+  for (int k = 2; k <= 1024; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int o = e ^ j;
+      if (o > e) {
+        const uint32_t a = s_key[e], b = s_key[o];
+        if ((a > b) == ((e & k) == 0)) {
+          s_key[e] = b;
+          s_key[o] = a;
+        }
+      }
+      __syncthreads();
+    }
+  const uint32_t key = s_key[e];
+  if (key != 0xffffffffu) {
+    const int g = (int)(key & 1023u);
+    const int c = s_cnt[g];
+    const int m0 = c / BM * BM;
+    mt[nfull + e] = int4{g, m0, s_off[g] + m0, c - m0};
+  }
+  __syncthreads();
+  // number of partial tiles = sorted keys below the sentinel
+  block_exclusive_scan<1024>(s_pre, s_tmp, P.el, [&](int g) { return s_cnt[g] % BM != 0 ? 1 : 0; });
+  if (e == 0) {
+    P.sched[0] = nfull + s_pre[P.el];
+    P.sched[2] = 0;
+    P.sched[3] = 0;
+  }
+  __syncthreads();
+  // weight-gradient units: one packed scan of (S << 16 | (S - 1))
+  const int kc = P.kc;
+  auto nsplit = [&](int g) { const int c = s_cnt[g]; return c > kc ? (c + kc - 1) / kc : 1; };
+  block_exclusive_scan<1024>(s_pre, s_tmp, P.el, [&](int g) { return nsplit(g); });
+  const int ubase = e < P.el ? s_pre[e] : 0;
+  const int nunits = s_pre[P.el];
+  __syncthreads();
+  block_exclusive_scan<1024>(s_pre, s_tmp, P.el, [&](int g) { return nsplit(g) - 1; });
+  if (e < P.el) {
+    int4* wu = (int4*)(P.sched + kSchedHeader) + P.mt_cap;
+    const int S = nsplit(e);
+    for (int sc = 0; sc < S; ++sc) {
+      const int lo = (int)((int64_t)sc * total / S), hi = (int)((int64_t)(sc + 1) * total / S);
+      wu[ubase + sc] = int4{e | (S > 1 ? 1 << 30 : 0), off_e + lo, hi - lo, sc > 0 ? s_pre[e] + sc - 1 : -1};
+    }
+  }
+  if (e == 0) P.sched[1] = nunits;
 }
 
 __global__ __launch_bounds__(64) void permute_scatter_kernel(RouteParams P) {

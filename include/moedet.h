@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -140,7 +140,12 @@ typedef struct moe_problem {
  *                            expert is not fixed.
  *   row_tok   [rows_cap] int32  row -> token (= row_src / k)
  *   row_prob  [rows_cap] float  row -> topk_prob of its slot
- *   slot_row  [T*k]  int32   flat slot -> row, -1 when its expert is not local */
+ *   slot_row  [T*k]  int32   flat slot -> row, -1 when its expert is not local
+ *   sched     [moe_sched_elems] int32  work list of the backward GEMMs, derived
+ *                            from counts only (same in both modes): the row
+ *                            tiles of the expert GEMMs, longest first, and the
+ *                            (expert, K chunk) units of the weight gradients.
+ *                            Its contents are private to the library. */
 typedef struct moe_routing {
   int32_t* topk_idx;
   float* topk_prob;
@@ -150,6 +155,7 @@ typedef struct moe_routing {
   int32_t* row_tok;
   float* row_prob;
   int32_t* slot_row;
+  int32_t* sched;
 } moe_routing;
 
 /* ABI version (MOE_ABI_VERSION of the build). */
@@ -160,6 +166,9 @@ const char* moe_status_string(moe_status s);
 
 /* rows_cap = tokens * min(top_k, num_local): leading size of row-layout buffers. */
 moe_status moe_rows_cap(const moe_problem* p, int64_t* rows_cap);
+
+/* Number of int32 elements of routing.sched for problem p (from shapes only). */
+moe_status moe_sched_elems(const moe_problem* p, int64_t* elems);
 
 /* Workspace bytes needed by each call for problem p in `mode` (upper bounds
  * from shapes only).  Any of the output pointers may be NULL. */

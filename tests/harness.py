@@ -76,7 +76,7 @@ def run_layer(prob: moe.Problem, di: DeviceInputs, mode=moe.DETERMINISTIC, poiso
     ws = [mk((max(n, 1),), torch.uint8) for n in moe.moe_workspace_size(prob, mode)]
     r = moe.Routing(mk((T, k), torch.int32), mk((T, k), torch.float32), mk((el,), torch.int32),
                     mk((el + 1,), torch.int32), mk((rc,), torch.int32), mk((rc,), torch.int32),
-                    mk((rc,), torch.float32), mk((T * k,), torch.int32))
+                    mk((rc,), torch.float32), mk((T * k,), torch.int32), mk((moe.moe_sched_elems(prob),), torch.int32))
     out_rows = T if prob.combine else rc
     routing, h, y = moe.moe_fwd(prob, di.logits, di.x, di.w1, di.w2, mode, routing=r,
                                 h=mk((rc, F), dt), y=mk((out_rows, D), dt), ws=ws[0])

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert names == set(moe.EXPORTED_SYMBOLS)
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -71,7 +71,7 @@ def test_null_and_workspace_errors_return_before_enqueue(lib):
     p = moe.Problem(**BASE)
     cp = p.c()
     fake = ctypes.c_void_p(0x1000)
-    r = moe._CRouting(*([0x2000] * 8))
+    r = moe._CRouting(*([0x2000] * 9))
     # NULL x
     assert lib.moe_fwd(ctypes.byref(cp), fake, None, fake, fake, ctypes.byref(r), fake, fake, fake, 1 << 30, 0,
                        None) == 1
