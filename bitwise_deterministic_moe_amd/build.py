@@ -24,7 +24,24 @@ FLAGS = [
     "-Wall",
     "-Wno-unused-function",
     "-Wno-inline-asm",  # m0 is set inside the DMA asm and listed as clobbered
+    # per-kernel register / LDS / scratch report, checked below
+    "-Rpass-analysis=kernel-resource-usage",
+    "-fno-caret-diagnostics",
 ]
+
+
+def _scratch_kernels(stderr: str) -> list:
+    """Kernels whose resource report shows per-lane scratch (register spills
+    or stack), from the compiler's kernel-resource-usage remarks."""
+    bad, name = [], None
+    for line in stderr.splitlines():
+        if "remark: Function Name:" in line:
+            name = line.split("Function Name:")[1].split("[")[0].strip()
+        elif "ScratchSize [bytes/lane]:" in line and name:
+            n = int(line.split("ScratchSize [bytes/lane]:")[1].split("[")[0])
+            if n:
+                bad.append((name, n))
+    return bad
 
 
 def build(verbose: bool = False) -> str:
@@ -34,9 +51,13 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+    err = "\n".join(l for l in res.stderr.splitlines()
+                    if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    bad = _scratch_kernels(res.stderr)
+    if bad:
+        raise RuntimeError(f"kernels use per-lane scratch (spills): {bad}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
     os.replace(tmp, LIB)
