@@ -364,31 +364,52 @@ struct NoPre {
 // Main loop instantiated for the number of the wave's A blocks that hold
 // rows, so that the waves of a partial tile skip MFMAs on zero rows while
 // every variant stays straight-line code.
-template <int AL, int BL, class Issue>
+template <int AL, int BL, int NS, class Issue>
 DEV void run_mainloop(int nmb, const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f32x16_t (&acc)[4][4],
                       int wm, int wn, int lane) {
   switch (nmb) {
-    case 0: bf::mainloop<AL, BL, 0>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
-    case 1: bf::mainloop<AL, BL, 1>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
-    case 2: bf::mainloop<AL, BL, 2>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
-    case 3: bf::mainloop<AL, BL, 3>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
-    default: bf::mainloop<AL, BL, 4>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
+    case 0: bf::mainloop<AL, BL, 0, NS>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
+    case 1: bf::mainloop<AL, BL, 1, NS>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
+    case 2: bf::mainloop<AL, BL, 2, NS>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
+    case 3: bf::mainloop<AL, BL, 3, NS>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
+    default: bf::mainloop<AL, BL, 4, NS>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
   }
 }
 
+// Ring depth per tile (uniform over the workgroup): a tile with at most 128
+// rows has too few MFMAs per slice to cover the load latency with 4 slots
+// and takes 5; fuller tiles keep 4 (measured: the deeper ring slows them).
+template <int AL, int BL, class Issue>
+DEV void run_row_mainloop(int mvalid, int nmb, const uint16_t* lds, uint32_t ring, int nsteps, Issue issue,
+                          f32x16_t (&acc)[4][4], int wm, int wn, int lane) {
+  if (mvalid <= 128)
+    run_mainloop<AL, BL, 5>(nmb, lds, ring, nsteps, issue, acc, wm, wn, lane);
+  else
+    run_mainloop<AL, BL, 4>(nmb, lds, ring, nsteps, issue, acc, wm, wn, lane);
+}
+
+// Row GEMMs hold a 5-slot ring (all 160 KiB of LDS); after the main loop
+// the ring holds the epilogue stage, then the quad sums and row
+// probabilities of the fc2 dgrad epilogue.
+constexpr int kRowNS = 5;
+constexpr int kQsumOff = kStageBytes;                     // float [BM][16]
+constexpr int kProbOff = kQsumOff + bf::BM * 16 * 4;      // float [BM]
+static_assert(kProbOff + bf::BM * 4 <= bf::ring_bytes<kRowNS>, "epilogue scratch must fit in the ring");
+
 template <int BL, int EPI>
 __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[bf::ring_bytes<kRowNS> / 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t ring = bf::lds_base(lds);
   const int wm = wave >> 1, wn = wave & 1;
-  __shared__ float s_prob[bf::BM];  // routing probability of each tile row (dgrad epilogue)
   RowTile t;
   const int kind = row_tile<bf::BM, bf::BN>(P, t);
   if (kind == kTileSide) dprob_side(P, t.nt);
   if (kind != kTileGemm) return;
-  if constexpr (EPI == kEpiDgrad2)
-    s_prob[tid] = tid < t.mvalid ? P.row_prob[t.off + t.m0 + tid] : 0.f;  // read after the main loop's barriers
+  // routing probability of each tile row (fc2 dgrad epilogue); loaded now,
+  // stored to LDS once the ring is free
+  float my_prob = 0.f;
+  if constexpr (EPI == kEpiDgrad2) my_prob = tid < t.mvalid ? P.row_prob[t.off + t.m0 + tid] : 0.f;
 
   bf::KcOperand oa;
   // Branch-free so that the four row-index loads of a thread are in flight
@@ -418,7 +439,7 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
       else
         ob.issue1(st + bf::OPER * 2, wave, s * bf::BK, s < nsteps, i - bf::LOADS);
     };
-    run_mainloop<bf::KC, bf::KC>(nmb, lds, ring, nsteps, issue, acc, wm, wn, lane);
+    run_row_mainloop<bf::KC, bf::KC>(t.mvalid, nmb, lds, ring, nsteps, issue, acc, wm, wn, lane);
   } else {
     bf::MncOperand ob;
     ob.init(Bg, P.b_bytes, wave, lane, t.n0);
@@ -435,7 +456,7 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
         ob.issue1(st + bf::OPER * 2, wave, s < nsteps ? kro[j] + (uint32_t)s * slice_bytes : bf::kOOB, j);
       }
     };
-    run_mainloop<bf::KC, bf::MNC>(nmb, lds, ring, nsteps, issue, acc, wm, wn, lane);
+    run_row_mainloop<bf::KC, bf::MNC>(t.mvalid, nmb, lds, ring, nsteps, issue, acc, wm, wn, lane);
   }
   float* stage = (float*)lds;
   if constexpr (EPI == kEpiStore || EPI == kEpiStoreAct) {
@@ -487,9 +508,13 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
           d.p[st] = prob[m];
         }
       }
-    } hpre{P, t, s_prob, tid};
+    };
+    float* s_qsum = (float*)((char*)lds + kQsumOff);  // [tile row][quad]
+    float* s_prob = (float*)((char*)lds + kProbOff);
+    s_prob[tid] = my_prob;  // the main loop ended with a barrier: the ring is free
+    lds_barrier();
+    HPre hpre{P, t, s_prob, tid};
     const __amdgpu_buffer_rsrc_t rc = buf(P.c), rc2 = buf(P.c2);
-    __shared__ float s_qsum[bf::BM * 16];  // [tile row][quad]
     staged_epilogue(stage, acc, wm, wn, lane, tid, hpre, [&](int m, int col, float (&g)[4], typename HPre::Data& d, int st) {
       const bool valid = m < t.mvalid;   // uniform across the wave (one row per wave)
       if (!valid) return;

@@ -3,8 +3,8 @@
 // Tile 256x256, K slice 32, 4 waves in a 2x2 grid, each wave 128x128 as 4x4
 // blocks of v_mfma_f32_32x32x16_bf16 (accumulators in AGPRs).  Operands go
 // from HBM straight into LDS with buffer_load_dwordx4 ... lds (no VGPR
-// staging) through a 4-stage ring, so three K slices are in flight while
-// one is consumed.  Rows outside the group / K range are given an offset
+// staging) through a ring of 4 or 5 slots, so two and a half (three and a
+// half) K slices are in flight while one is consumed.  Rows outside the group / K range are given an offset
 // past the buffer's num_records, for which the hardware writes zeros.
 //
 // LDS layouts (bf16 elements):
@@ -36,6 +36,9 @@ constexpr int BM = 256, BN = 256, BK = 32, NSTAGE = 4, NT = 256;
 constexpr int OPER = BM * BK;                 // elements per operand per stage
 constexpr int STAGE = 2 * OPER;               // A then B
 constexpr int LDS_BYTES = NSTAGE * STAGE * 2; // 128 KiB
+// Ring of NS slots: NS = 5 fills the 160 KiB of LDS of a gfx950 CU.
+template <int NS>
+constexpr int ring_bytes = NS * STAGE * 2;
 constexpr int LOADS = 4;                      // 16-byte DMA loads per thread per operand per stage
 constexpr uint32_t kOOB = 0x80000000u;        // offset beyond any num_records: reads zeros
 
@@ -83,8 +86,10 @@ DEV void dma16(i32x4_t rs, uint32_t lds, uint32_t voff, uint32_t soff) {
 // across.
 template <int N>
 DEV void wait_barrier() {
-  static_assert(N == 0 || N == 8 || N == 12 || N == 16, "vmcnt");
-  if constexpr (N == 16)
+  static_assert(N == 0 || N == 8 || N == 12 || N == 16 || N == 20, "vmcnt");
+  if constexpr (N == 20)
+    asm volatile("s_waitcnt vmcnt(20)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 16)
     asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 12)
     asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
@@ -222,13 +227,15 @@ struct MncOperand {
   }
 };
 
-// Pipelined main loop over nsteps K slices through a ring of NSTAGE LDS
-// slots.  issue(s, lds, i) issues DMA load i (0..3 of A, 4..7 of B) of
-// slice s into the slot at LDS byte address lds; loads of a slice are
-// requested in order i = 0..7 and slices in increasing order.  For
+// Pipelined main loop over nsteps K slices through a ring of NS LDS slots
+// (slice s in slot s % NS).  issue(s, lds, i) issues DMA load i (0..3 of A,
+// 4..7 of B) of slice s into the slot at LDS byte address lds; loads of a
+// slice are requested in order i = 0..7 and slices in increasing order.  For
 // s >= nsteps every load must carry an offset past the buffer end (no
 // memory traffic; zeros land in a slot that is never read again), which
-// keeps the outstanding-load count the same in every step.
+// keeps the outstanding-load count the same in every step.  NS - 2 slices
+// and a half are in flight while one is consumed, which covers the HBM
+// latency of a loaded device with NS = 5.
 //
 // A wave issues instructions in order, and a DMA load occupies the
 // per-CU address path for about 16 clocks, so loads are spread evenly over
@@ -236,24 +243,25 @@ struct MncOperand {
 // fragment read sits next to the MFMAs it overlaps (scheduling barriers
 // pin the order):
 //  phase 1 of step s: fragments of slice s / k-half 1 are read and loads
-//    4..7 of slice s+2 issued, while the MFMAs of k-half 0 run;
+//    4..7 of slice s+NS-2 issued, while the MFMAs of k-half 0 run;
 //  wait for this wave's loads of slice s+1, meet the other waves (every wave
-//    is then done with slice s-1, whose slot takes slice s+3);
+//    is then done with slice s-1, whose slot takes slice s+NS-1);
 //  phase 2: fragments of slice s+1 / k-half 0 are read and loads 0..3 of
-//    slice s+3 issued, while the MFMAs of k-half 1 run.
-template <int AL, int BL, int NMB = 4, class Issue>
+//    slice s+NS-1 issued, while the MFMAs of k-half 1 run.
+template <int AL, int BL, int NMB = 4, int NS = NSTAGE, class Issue>
 DEV void mainloop(const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f32x16_t (&acc)[4][4], int wm,
                   int wn, int lane) {
+  static_assert(NS == 4 || NS == 5, "ring slots");
   if (nsteps <= 0) return;
-  auto slot = [&](int s) { return lds + (s & (NSTAGE - 1)) * STAGE; };
-  auto slot_addr = [&](int s) { return ring + (uint32_t)(s & (NSTAGE - 1)) * (STAGE * 2); };
+  auto slot = [&](int s) { return lds + (s % NS) * STAGE; };
+  auto slot_addr = [&](int s) { return ring + (uint32_t)(s % NS) * (STAGE * 2); };
 #pragma unroll
-  for (int i = 0; i < 8; ++i) issue(0, slot_addr(0), i);
+  for (int s = 0; s < NS - 2; ++s)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) issue(1, slot_addr(1), i);
+    for (int i = 0; i < 8; ++i) issue(s, slot_addr(s), i);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) issue(2, slot_addr(2), i);
-  wait_barrier<12>();  // slice 0 landed
+  for (int i = 0; i < 4; ++i) issue(NS - 2, slot_addr(NS - 2), i);
+  wait_barrier<8 * (NS - 3) + 4>();  // slice 0 landed
   Frags f0, f1;
 #pragma unroll
   for (int g = 0; g < 8; ++g) load_frag<AL, BL, NMB>(f0, lds, 0, wm, wn, lane, g);
@@ -263,16 +271,16 @@ DEV void mainloop(const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f
     const uint16_t* nxt = slot(s + 1);
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
-      if (g & 1) issue(s + 2, slot_addr(s + 2), 4 + (g >> 1));
+      if (g & 1) issue(s + NS - 2, slot_addr(s + NS - 2), 4 + (g >> 1));
       load_frag<AL, BL, NMB>(f1, cur, 1, wm, wn, lane, g);
       __builtin_amdgcn_sched_barrier(0);
       mma2<NMB>(f0, acc, g);
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_barrier<8>();  // slice s+1 landed; slot of slice s-1 free
+    wait_barrier<8 * (NS - 3)>();  // slice s+1 landed; slot of slice s-1 free
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
-      if (g & 1) issue(s + 3, slot_addr(s + 3), g >> 1);
+      if (g & 1) issue(s + NS - 1, slot_addr(s + NS - 1), g >> 1);
       load_frag<AL, BL, NMB>(f0, nxt, 0, wm, wn, lane, g);
       __builtin_amdgcn_sched_barrier(0);
       mma2<NMB>(f1, acc, g);
