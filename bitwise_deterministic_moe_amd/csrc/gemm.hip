@@ -319,40 +319,47 @@ DEV int staged_row(int p, int st, int tid) {
 DEV int staged_col(int tid) { return (tid & 63) * 4; }
 
 // pre.load(d, p): issue this thread's global loads needed by pass p into d
-// (called one pass ahead); emit(row, col, v, d, st): consume one step.
+// (called one pass ahead; pass 0's by the caller when first_loaded);
+// emit(row, col, v, d, st): consume one step.  Passes whose 64
+// rows are all past `rows` (the tile's valid rows) are skipped (the decision
+// is uniform over the workgroup).
 template <class Pre, class Emit>
-DEV void staged_epilogue(float* stage, f32x16_t (&acc)[4][4], int wm, int wn, int lane, int tid, Pre& pre, Emit emit) {
+DEV void staged_epilogue(float* stage, f32x16_t (&acc)[4][4], int wm, int wn, int lane, int tid, int rows, Pre& pre,
+                         typename Pre::Data (&d)[2], bool first_loaded, Emit emit) {
   const int r32 = lane & 31, half = lane >> 5;
-  typename Pre::Data d[2];
-  pre.load(d[0], 0);
+  const int npass = rows >= 256 ? 4 : (rows + 63) / 64;
+  if (npass > 0 && !first_loaded) pre.load(d[0], 0);
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    if (wm == (p >> 1)) {
+    if (p < npass) {
+      if (wm == (p >> 1)) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int mb = 2 * (p & 1) + q;
-        const int m = q * 32 + r32;  // row within the pass
+        for (int q = 0; q < 2; ++q) {
+          const int mb = 2 * (p & 1) + q;
+          const int m = q * 32 + r32;  // row within the pass
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+          for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int n = wn * 128 + nb * 32 + 8 * i + 4 * half;
-            const f32x16_t& a = acc[mb][nb];
-            *(f32x4_t*)(stage + m * kStageRow + n) = f32x4_t{a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3]};
-          }
+            for (int i = 0; i < 4; ++i) {
+              const int n = wn * 128 + nb * 32 + 8 * i + 4 * half;
+              const f32x16_t& a = acc[mb][nb];
+              *(f32x4_t*)(stage + m * kStageRow + n) = f32x4_t{a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3]};
+            }
+        }
       }
-    }
-    lds_barrier();
-    if (p + 1 < 4) pre.load(d[(p + 1) & 1], p + 1);
-    f32x4_t v[16];
+      lds_barrier();
+      if (p + 1 < npass) pre.load(d[(p + 1) & 1], p + 1);
+      f32x4_t v[16];
 #pragma unroll
-    for (int st = 0; st < 16; ++st) v[st] = *(const f32x4_t*)(stage + (4 * st + (tid >> 6)) * kStageRow + staged_col(tid));
+      for (int st = 0; st < 16; ++st)
+        v[st] = *(const f32x4_t*)(stage + (4 * st + (tid >> 6)) * kStageRow + staged_col(tid));
 #pragma unroll
-    for (int st = 0; st < 16; ++st) {
-      float f[4] = {v[st][0], v[st][1], v[st][2], v[st][3]};
-      emit(staged_row(p, st, tid), staged_col(tid), f, d[p & 1], st);
+      for (int st = 0; st < 16; ++st) {
+        float f[4] = {v[st][0], v[st][1], v[st][2], v[st][3]};
+        emit(staged_row(p, st, tid), staged_col(tid), f, d[p & 1], st);
+      }
+      lds_barrier();
     }
-    lds_barrier();
   }
 }
 
@@ -387,6 +394,29 @@ DEV void run_row_mainloop(int mvalid, int nmb, const uint16_t* lds, uint32_t rin
   else
     run_mainloop<AL, BL, 4>(nmb, lds, ring, nsteps, issue, acc, wm, wn, lane);
 }
+
+// Loads of h for the fc2 dgrad epilogue: pass p, step st reads the 4
+// columns of this thread in tile row staged_row(p, st) (rows past the tile's
+// valid rows read zeros).
+struct HPre {
+  struct Data {
+    u32x2_t h[16];
+  };
+  const RowGemmParams& P;
+  const RowTile& t;
+  int tid;
+  DEV void load(Data& d, int p) {
+    const __amdgpu_buffer_rsrc_t rh = buf(P.h);
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      const int m = staged_row(p, st, tid);
+      const bool ok = m < t.mvalid;
+      const uint32_t grow = (uint32_t)(t.off + t.m0 + (ok ? m : 0));
+      d.h[st] = __builtin_amdgcn_raw_buffer_load_b64(
+          rh, ok ? (grow * (uint32_t)P.ldh + t.n0 + staged_col(tid)) * 2u : kNoRow, 0, 0);
+    }
+  }
+};
 
 // Row GEMMs hold a 5-slot ring (all 160 KiB of LDS); after the main loop
 // the ring holds the epilogue stage, then the quad sums and row
@@ -461,8 +491,9 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
   float* stage = (float*)lds;
   if constexpr (EPI == kEpiStore || EPI == kEpiStoreAct) {
     NoPre none;
+    NoPre::Data nd[2];
     const __amdgpu_buffer_rsrc_t rc = buf(P.c), rc2 = buf(P.c2);
-    staged_epilogue(stage, acc, wm, wn, lane, tid, none, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
+    staged_epilogue(stage, acc, wm, wn, lane, tid, t.mvalid, none, nd, false, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
       if (m >= t.mvalid) return;  // uniform per wave
       const uint32_t grow = (uint32_t)(t.off + t.m0 + m);
       __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rc,
@@ -486,40 +517,20 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
     //                   the lane quad (16 columns), then the 16 quad sums of
     //                   the row in quad order (through LDS);
     //   dh = (2 p G) * relu(h);  act_p = p * relu(h)^2.
-    // h and the row probabilities of a pass are loaded one pass ahead.
-    struct HPre {
-      struct Data {
-        u32x2_t h[16];
-        float p[16];
-      };
-      const RowGemmParams& P;
-      const RowTile& t;
-      const float* prob;
-      int tid;
-      DEV void load(Data& d, int p) {
-        const __amdgpu_buffer_rsrc_t rh = buf(P.h);
-#pragma unroll
-        for (int st = 0; st < 16; ++st) {
-          const int m = staged_row(p, st, tid);
-          const bool ok = m < t.mvalid;
-          const uint32_t grow = (uint32_t)(t.off + t.m0 + (ok ? m : 0));
-          d.h[st] = __builtin_amdgcn_raw_buffer_load_b64(
-              rh, ok ? (grow * (uint32_t)P.ldh + t.n0 + staged_col(tid)) * 2u : kNoRow, 0, 0);
-          d.p[st] = prob[m];
-        }
-      }
-    };
+    // h of a pass is loaded one pass ahead; the row probabilities come from
+    // LDS.
     float* s_qsum = (float*)((char*)lds + kQsumOff);  // [tile row][quad]
     float* s_prob = (float*)((char*)lds + kProbOff);
     s_prob[tid] = my_prob;  // the main loop ended with a barrier: the ring is free
     lds_barrier();
-    HPre hpre{P, t, s_prob, tid};
+    HPre hpre{P, t, tid};
+    HPre::Data hd[2];
     const __amdgpu_buffer_rsrc_t rc = buf(P.c), rc2 = buf(P.c2);
-    staged_epilogue(stage, acc, wm, wn, lane, tid, hpre, [&](int m, int col, float (&g)[4], typename HPre::Data& d, int st) {
+    staged_epilogue(stage, acc, wm, wn, lane, tid, t.mvalid, hpre, hd, false, [&](int m, int col, float (&g)[4], HPre::Data& d, int st) {
       const bool valid = m < t.mvalid;   // uniform across the wave (one row per wave)
       if (!valid) return;
       const int64_t grow = t.off + t.m0 + m;
-      const float p = d.p[st];
+      const float p = s_prob[m];
       const float p2 = 2.f * p;
       float hv[4], dh[4], pa[4];
       hv[0] = bf16_to_f32(d.h[st][0] & 0xffffu);
@@ -616,7 +627,8 @@ DEV void wgrad_bf16_tile(const WgradParams& P, const WgradTile& t, float* dst, u
   const bool atomic_add = P.atomic && t.S > 1;
   NoPre none;
   const __amdgpu_buffer_rsrc_t rd = buf(dst);
-  staged_epilogue((float*)lds, acc, wm, wn, lane, tid, none, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
+  NoPre::Data nd[2];
+  staged_epilogue((float*)lds, acc, wm, wn, lane, tid, bf::BM, none, nd, false, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
     const uint32_t o = ((uint32_t)(t.m0 + m) * (uint32_t)P.N + t.n0 + col) * 4u;
     if (atomic_add) {
       float* po = dst + o / 4u;
