@@ -10,6 +10,7 @@ constexpr int kMaxExperts = 1024;     // router width handled by the routing ker
 constexpr int kMaxTopK = 64;          // one lane per selected expert
 constexpr int kRouteChunk = 64;       // tokens per routing/permutation chunk
 constexpr int kMaxChunkRows = 4096;   // upper bound on the wgrad K chunk (rows)
+constexpr int64_t kManyWgradTiles = 8192;  // weight-gradient tiles above which no expert is split
 
 // Grid size (a multiple of the 8 XCDs) for an upper bound on work units.
 inline int64_t grid_for_units(int64_t U_max) { return ((U_max + 7) / 8) * 8; }

@@ -82,10 +82,16 @@ moe_status validate(const moe_problem* p, Plan* pl) {
     // shapes.  Only experts holding more rows than that (skewed routing) are
     // split.  An expert holds at most `tokens` rows, so with kc >= tokens no
     // expert can split and the ordered reduction is not needed at all.
+    // Splitting only pays when the layer has few weight-gradient tiles (one
+    // per expert and 256x256 block of dW): with kManyWgradTiles or more every
+    // compute unit already runs many tiles, and a split would only add
+    // float32 partial writes and the ordered reduction, so the largest chunk
+    // is taken.
     const double mean = (double)p->tokens * p->top_k / p->num_experts;
     int64_t kc = 256 * (int64_t)((4.0 * mean + 255.0) / 256.0);
     if (kc < 512) kc = 512;
-    if (kc > kMaxChunkRows) kc = kMaxChunkRows;
+    const int64_t wtiles = (int64_t)p->num_local * (p->d_model / 256) * (p->d_ffn / 256);
+    if (wtiles >= kManyWgradTiles || kc > kMaxChunkRows) kc = kMaxChunkRows;
     pl->kc = (int)kc;
     pl->may_split = kc < p->tokens;
     pl->wslots = pl->may_split ? pl->rows_cap / kc : 0;

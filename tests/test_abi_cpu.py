@@ -103,13 +103,22 @@ def test_workspace_sizes_and_rows_cap():
     # chunk 4 * mean rows = 4096 >= tokens: no expert can split, no partial slots
     assert wa == wg and da >= 4096 * 1024 * 4
     assert moe.moe_stage_names(p, 0, 2) == ["wgrad_fc1_fc2"]
-    # 512 experts top-22: chunk 768 rows < tokens, split slots in the deterministic workspace
+    # 512 experts top-22: 32768 weight-gradient tiles, so no expert is split
+    # (chunk 4096 = tokens): no slots, no ordered reduction
     latent = moe.Problem(4096, 2048, 2048, 512, 22)
     _, _, wl = moe.moe_workspace_size(latent, moe.DETERMINISTIC)
     _, _, wla = moe.moe_workspace_size(latent, moe.ATOMIC)
-    assert wl - wla >= 2 * (4096 * 22 // 768) * 2048 * 2048 * 4
-    assert moe.moe_stage_names(latent, 0, 2) == ["wgrad_fc1_fc2", "wgrad_reduce"]
-    assert moe.moe_stage_names(latent, 1, 2) == ["wgrad_prep_zero", "wgrad_fc1_fc2"]
+    assert wl == wla
+    assert moe.moe_stage_names(latent, 0, 2) == ["wgrad_fc1_fc2"]
+    assert moe.moe_stage_names(latent, 1, 2) == ["wgrad_fc1_fc2"]
+    # 8 experts, 16384 tokens top-2: 128 tiles, chunk 4096 < tokens: split
+    # slots (rows_cap / chunk = 8 per weight gradient) in the deterministic workspace
+    wide = moe.Problem(16384, 1024, 1024, 8, 2)
+    _, _, ww = moe.moe_workspace_size(wide, moe.DETERMINISTIC)
+    _, _, wwa = moe.moe_workspace_size(wide, moe.ATOMIC)
+    assert ww - wwa >= 2 * 8 * 1024 * 1024 * 4
+    assert moe.moe_stage_names(wide, 0, 2) == ["wgrad_fc1_fc2", "wgrad_reduce"]
+    assert moe.moe_stage_names(wide, 1, 2) == ["wgrad_prep_zero", "wgrad_fc1_fc2"]
     shard = moe.Problem(16384, 2048, 2048, 512, 22, 0, 4, "bf16", 0)
     assert moe.moe_rows_cap(shard) == 16384 * 4
     assert moe.moe_stage_names(p, 0, 1) == ["fc2_dgrad_dprob_partials", "fc1_dgrad_dprob_combine",

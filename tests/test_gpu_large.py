@@ -189,8 +189,8 @@ def test_large_parity_and_determinism(name):
     assert np.all(dp[perm["slot_row"].reshape(dp.shape) < 0] == 0)
     empty = np.nonzero(perm["counts"] == 0)[0]
     if name == "skewed_e512k22":
-        # the weight-gradient chunk is 768 rows here (4 x the mean of 176, rounded up to 256)
-        assert len(empty) > 0 and perm["counts"].max() > 2 * 768, "skewed workload must split and hold empty experts"
+        # max/mean load about 12 (mean 176 rows) and some experts without rows
+        assert len(empty) > 0 and perm["counts"].max() > 8 * 176, "skewed workload must be skewed and hold empty experts"
     if len(empty):
         ei = torch.as_tensor(empty, device="cuda")
         assert torch.all(out["dw1"][ei] == 0) and torch.all(out["dw2"][ei] == 0)
