@@ -89,12 +89,12 @@ DEV int row_tile(const RowGemmParams& P, RowTile& t) {
     return t.nt < P.side_units ? kTileSide : kTileNone;
   }
   const int nN = P.N / BNv;
-  const int64_t U = (int64_t)P.sched[0] * nN;
+  const int64_t U = (int64_t)P.sched[P.list_hdr] * nN;
   const int64_t L = map_unit_rounds(blockIdx.x, U, P.ncu, P.seed);
   if (L < 0) return kTileNone;
   const int64_t mt = L / nN;
   t.nt = (int)(L % nN);
-  const int4 en = ((const int4*)(P.sched + kSchedHeader))[mt];
+  const int4 en = ((const int4*)(P.sched + P.list_at))[mt];
   t.g = __builtin_amdgcn_readfirstlane(en.x);
   t.m0 = __builtin_amdgcn_readfirstlane(en.y);
   t.off = (int64_t)__builtin_amdgcn_readfirstlane(en.z - en.y);
@@ -323,20 +323,22 @@ DEV int staged_col(int tid) { return (tid & 63) * 4; }
 // emit(row, col, v, d, st): consume one step.  Passes whose 64
 // rows are all past `rows` (the tile's valid rows) are skipped (the decision
 // is uniform over the workgroup).
-template <class Pre, class Emit>
+// WTM: rows of a wave's tile (128, or 96 for a 192-row tile); a wave's
+// 32-row block mb (tile rows wm*WTM + 32 mb ..) goes to the pass holding it.
+template <int WTM = 128, class Pre, class Emit>
 DEV void staged_epilogue(float* stage, f32x16_t (&acc)[4][4], int wm, int wn, int lane, int tid, int rows, Pre& pre,
                          typename Pre::Data (&d)[2], bool first_loaded, Emit emit) {
   const int r32 = lane & 31, half = lane >> 5;
-  const int npass = rows >= 256 ? 4 : (rows + 63) / 64;
+  const int npass = rows >= 2 * WTM ? 2 * WTM / 64 : (rows + 63) / 64;
   if (npass > 0 && !first_loaded) pre.load(d[0], 0);
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     if (p < npass) {
-      if (wm == (p >> 1)) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int mb = 2 * (p & 1) + q;
-          const int m = q * 32 + r32;  // row within the pass
+      for (int mb = 0; mb < WTM / 32; ++mb) {
+        const int r0 = wm * WTM + mb * 32 - 64 * p;  // block start within the pass (uniform)
+        if (r0 >= 0 && r0 < 64) {
+          const int m = r0 + r32;  // row within the pass
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -371,28 +373,30 @@ struct NoPre {
 // Main loop instantiated for the number of the wave's A blocks that hold
 // rows, so that the waves of a partial tile skip MFMAs on zero rows while
 // every variant stays straight-line code.
-template <int AL, int BL, int NS, class Issue>
+template <int AL, int BL, int NS, int WTM, class Issue>
 DEV void run_mainloop(int nmb, const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f32x16_t (&acc)[4][4],
                       int wm, int wn, int lane) {
   switch (nmb) {
-    case 0: bf::mainloop<AL, BL, 0, NS>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
-    case 1: bf::mainloop<AL, BL, 1, NS>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
-    case 2: bf::mainloop<AL, BL, 2, NS>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
-    case 3: bf::mainloop<AL, BL, 3, NS>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
-    default: bf::mainloop<AL, BL, 4, NS>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
+    case 0: bf::mainloop<AL, BL, 0, NS, WTM>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
+    case 1: bf::mainloop<AL, BL, 1, NS, WTM>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
+    case 2: bf::mainloop<AL, BL, 2, NS, WTM>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
+    case 3: bf::mainloop<AL, BL, 3, NS, WTM>(lds, ring, nsteps, issue, acc, wm, wn, lane); break;
+    default:
+      if constexpr (WTM >= 128) bf::mainloop<AL, BL, 4, NS, WTM>(lds, ring, nsteps, issue, acc, wm, wn, lane);
+      break;
   }
 }
 
 // Ring depth per tile (uniform over the workgroup): a tile with at most 128
 // rows has too few MFMAs per slice to cover the load latency with 4 slots
 // and takes 5; fuller tiles keep 4 (measured: the deeper ring slows them).
-template <int AL, int BL, class Issue>
+template <int AL, int BL, int WTM, class Issue>
 DEV void run_row_mainloop(int mvalid, int nmb, const uint16_t* lds, uint32_t ring, int nsteps, Issue issue,
                           f32x16_t (&acc)[4][4], int wm, int wn, int lane) {
   if (mvalid <= 128)
-    run_mainloop<AL, BL, 5>(nmb, lds, ring, nsteps, issue, acc, wm, wn, lane);
+    run_mainloop<AL, BL, 5, WTM>(nmb, lds, ring, nsteps, issue, acc, wm, wn, lane);
   else
-    run_mainloop<AL, BL, 4>(nmb, lds, ring, nsteps, issue, acc, wm, wn, lane);
+    run_mainloop<AL, BL, 4, WTM>(nmb, lds, ring, nsteps, issue, acc, wm, wn, lane);
 }
 
 // Loads of h for the fc2 dgrad epilogue: pass p, step st reads the 4
@@ -426,14 +430,16 @@ constexpr int kQsumOff = kStageBytes;                     // float [BM][16]
 constexpr int kProbOff = kQsumOff + bf::BM * 16 * 4;      // float [BM]
 static_assert(kProbOff + bf::BM * 4 <= bf::ring_bytes<kRowNS>, "epilogue scratch must fit in the ring");
 
-template <int BL, int EPI>
+// BMV: tile rows (256, or 192 as two wave rows of 96).
+template <int BL, int EPI, int BMV>
 __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
+  constexpr int WTM = BMV / 2;
   __shared__ __attribute__((aligned(16))) uint16_t lds[bf::ring_bytes<kRowNS> / 2];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t ring = bf::lds_base(lds);
   const int wm = wave >> 1, wn = wave & 1;
   RowTile t;
-  const int kind = row_tile<bf::BM, bf::BN>(P, t);
+  const int kind = row_tile<BMV, bf::BN>(P, t);
   if (kind == kTileSide) dprob_side(P, t.nt);
   if (kind != kTileGemm) return;
   // routing probability of each tile row (fc2 dgrad epilogue); loaded now,
@@ -459,7 +465,7 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
   const int nsteps = P.K / bf::BK;
   // 32-row A blocks of this wave that hold rows (wave-uniform)
-  const int nmb = max(0, min(4, (t.mvalid - wm * 128 + 31) / 32));
+  const int nmb = max(0, min(WTM / 32, (t.mvalid - wm * WTM + 31) / 32));
   if constexpr (BL == bf::KC) {
     bf::KcOperand ob;
     ob.init(Bg, P.b_bytes, wave, lane, [&](int r) -> uint32_t { return (uint32_t)((t.n0 + r) * P.ldb * 2); });
@@ -469,7 +475,7 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
       else
         ob.issue1(st + bf::OPER * 2, wave, s * bf::BK, s < nsteps, i - bf::LOADS);
     };
-    run_row_mainloop<bf::KC, bf::KC>(t.mvalid, nmb, lds, ring, nsteps, issue, acc, wm, wn, lane);
+    run_row_mainloop<bf::KC, bf::KC, WTM>(t.mvalid, nmb, lds, ring, nsteps, issue, acc, wm, wn, lane);
   } else {
     bf::MncOperand ob;
     ob.init(Bg, P.b_bytes, wave, lane, t.n0);
@@ -486,14 +492,14 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
         ob.issue1(st + bf::OPER * 2, wave, s < nsteps ? kro[j] + (uint32_t)s * slice_bytes : bf::kOOB, j);
       }
     };
-    run_row_mainloop<bf::KC, bf::MNC>(t.mvalid, nmb, lds, ring, nsteps, issue, acc, wm, wn, lane);
+    run_row_mainloop<bf::KC, bf::MNC, WTM>(t.mvalid, nmb, lds, ring, nsteps, issue, acc, wm, wn, lane);
   }
   float* stage = (float*)lds;
   if constexpr (EPI == kEpiStore || EPI == kEpiStoreAct) {
     NoPre none;
     NoPre::Data nd[2];
     const __amdgpu_buffer_rsrc_t rc = buf(P.c), rc2 = buf(P.c2);
-    staged_epilogue(stage, acc, wm, wn, lane, tid, t.mvalid, none, nd, false, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
+    staged_epilogue<WTM>(stage, acc, wm, wn, lane, tid, t.mvalid, none, nd, false, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
       if (m >= t.mvalid) return;  // uniform per wave
       const uint32_t grow = (uint32_t)(t.off + t.m0 + m);
       __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rc,
@@ -526,7 +532,7 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
     HPre hpre{P, t, tid};
     HPre::Data hd[2];
     const __amdgpu_buffer_rsrc_t rc = buf(P.c), rc2 = buf(P.c2);
-    staged_epilogue(stage, acc, wm, wn, lane, tid, t.mvalid, hpre, hd, false, [&](int m, int col, float (&g)[4], HPre::Data& d, int st) {
+    staged_epilogue<WTM>(stage, acc, wm, wn, lane, tid, t.mvalid, hpre, hd, false, [&](int m, int col, float (&g)[4], HPre::Data& d, int st) {
       const bool valid = m < t.mvalid;   // uniform across the wave (one row per wave)
       if (!valid) return;
       const int64_t grow = t.off + t.m0 + m;
@@ -864,10 +870,15 @@ hipError_t launch_rowgemm(const RowGemmParams& P, int kind, bool bf16, int64_t g
   if (grid <= 0) return hipSuccess;
   if (bf16) {
     switch (kind) {
-      case kGemmFc1Fwd: rowgemm_bf16_kernel<bf::MNC, kEpiStoreAct><<<grid, 256, 0, st>>>(P); break;
-      case kGemmFc2Fwd: rowgemm_bf16_kernel<bf::MNC, kEpiStore><<<grid, 256, 0, st>>>(P); break;
-      case kGemmFc2Dgrad: rowgemm_bf16_kernel<bf::KC, kEpiDgrad2><<<grid, 256, 0, st>>>(P); break;
-      case kGemmFc1Dgrad: rowgemm_bf16_kernel<bf::KC, kEpiStore><<<grid, 256, 0, st>>>(P); break;
+      case kGemmFc1Fwd: rowgemm_bf16_kernel<bf::MNC, kEpiStoreAct, 256><<<grid, 256, 0, st>>>(P); break;
+      case kGemmFc2Fwd: rowgemm_bf16_kernel<bf::MNC, kEpiStore, 256><<<grid, 256, 0, st>>>(P); break;
+      case kGemmFc2Dgrad: rowgemm_bf16_kernel<bf::KC, kEpiDgrad2, 256><<<grid, 256, 0, st>>>(P); break;
+      case kGemmFc1Dgrad:
+        if (P.list_hdr == 2)
+          rowgemm_bf16_kernel<bf::KC, kEpiStore, kRowTile2><<<grid, 256, 0, st>>>(P);
+        else
+          rowgemm_bf16_kernel<bf::KC, kEpiStore, 256><<<grid, 256, 0, st>>>(P);
+        break;
       default: return hipErrorInvalidValue;
     }
   } else {

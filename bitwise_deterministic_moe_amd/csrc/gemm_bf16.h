@@ -128,14 +128,6 @@ struct Frags {
   bf16x8_t a[4], b[4];
 };
 
-template <int AL, int BL>
-DEV void load_frags(Frags& f, const uint16_t* st, int kk, int wm, int wn, int lane) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = frag<AL>(st, wm * 128 + i * 32, kk, lane);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f.b[i] = frag<BL>(st + OPER, wn * 128 + i * 32, kk, lane);
-}
-
 // Fragment reads and MFMAs of a k-half in 8 groups.  Group g reads block
 // A0 B0 B1 A1 B2 B3 A2 A3 [g] and issues MFMA pair g:
 //   (A0;B0,B1) (A1;B0,B1) (A0;B2,B3) (A1;B2,B3) (A2;B0,B1) (A2;B2,B3) (A3;B0,B1) (A3;B2,B3)
@@ -149,10 +141,11 @@ constexpr int kGrpN[8] = {0, 0, 2, 2, 0, 2, 0, 2};
 // NMB: number of the wave's 32-row A blocks that hold rows (4 for a full
 // tile).  A wave of a partial tile skips the reads and MFMAs of the blocks
 // past the group end, which would only multiply zeros.
-template <int AL, int BL, int NMB = 4>
+// WTM: rows of the wave tile (128, or 96 for a 192-row tile).
+template <int AL, int BL, int NMB = 4, int WTM = 128>
 DEV void load_frag(Frags& f, const uint16_t* st, int kk, int wm, int wn, int lane, int g) {
   if (kGrpA[g] >= 0) {
-    if (kGrpA[g] < NMB) f.a[kGrpA[g]] = frag<AL>(st, wm * 128 + kGrpA[g] * 32, kk, lane);
+    if (kGrpA[g] < NMB) f.a[kGrpA[g]] = frag<AL>(st, wm * WTM + kGrpA[g] * 32, kk, lane);
   } else {
     f.b[kGrpB[g]] = frag<BL>(st + OPER, wn * 128 + kGrpB[g] * 32, kk, lane);
   }
@@ -248,7 +241,7 @@ struct MncOperand {
 //    is then done with slice s-1, whose slot takes slice s+NS-1);
 //  phase 2: fragments of slice s+1 / k-half 0 are read and loads 0..3 of
 //    slice s+NS-1 issued, while the MFMAs of k-half 1 run.
-template <int AL, int BL, int NMB = 4, int NS = NSTAGE, class Issue>
+template <int AL, int BL, int NMB = 4, int NS = NSTAGE, int WTM = 128, class Issue>
 DEV void mainloop(const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f32x16_t (&acc)[4][4], int wm,
                   int wn, int lane) {
   static_assert(NS == 4 || NS == 5, "ring slots");
@@ -264,7 +257,7 @@ DEV void mainloop(const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f
   wait_barrier<8 * (NS - 3) + 4>();  // slice 0 landed
   Frags f0, f1;
 #pragma unroll
-  for (int g = 0; g < 8; ++g) load_frag<AL, BL, NMB>(f0, lds, 0, wm, wn, lane, g);
+  for (int g = 0; g < 8; ++g) load_frag<AL, BL, NMB, WTM>(f0, lds, 0, wm, wn, lane, g);
 #pragma unroll 1
   for (int s = 0; s < nsteps - 1; ++s) {
     const uint16_t* cur = slot(s);
@@ -272,7 +265,7 @@ DEV void mainloop(const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       if (g & 1) issue(s + NS - 2, slot_addr(s + NS - 2), 4 + (g >> 1));
-      load_frag<AL, BL, NMB>(f1, cur, 1, wm, wn, lane, g);
+      load_frag<AL, BL, NMB, WTM>(f1, cur, 1, wm, wn, lane, g);
       __builtin_amdgcn_sched_barrier(0);
       mma2<NMB>(f0, acc, g);
       __builtin_amdgcn_sched_barrier(0);
@@ -281,14 +274,14 @@ DEV void mainloop(const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       if (g & 1) issue(s + NS - 1, slot_addr(s + NS - 1), g >> 1);
-      load_frag<AL, BL, NMB>(f0, nxt, 0, wm, wn, lane, g);
+      load_frag<AL, BL, NMB, WTM>(f0, nxt, 0, wm, wn, lane, g);
       __builtin_amdgcn_sched_barrier(0);
       mma2<NMB>(f1, acc, g);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
-  for (int g = 0; g < 8; ++g) load_frag<AL, BL, NMB>(f1, slot(nsteps - 1), 1, wm, wn, lane, g);
+  for (int g = 0; g < 8; ++g) load_frag<AL, BL, NMB, WTM>(f1, slot(nsteps - 1), 1, wm, wn, lane, g);
 #pragma unroll
   for (int g = 0; g < 8; ++g) mma2<NMB>(f0, acc, g);
 #pragma unroll

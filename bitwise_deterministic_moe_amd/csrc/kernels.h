@@ -47,7 +47,9 @@ struct RowGemmParams {
   float* dprob;
   int atomic;
   int ncu;                // compute units of the device (work-unit rounds)
-  const int32_t* sched;   // routing.sched (row-tile list)
+  const int32_t* sched;   // routing.sched
+  int list_hdr;           // header word holding the row-tile count (0 or 2)
+  int64_t list_at;        // int32 offset of the row-tile entries
   // Side job run by the workgroups after the GEMM tiles (fc1 dgrad, which
   // leaves compute units idle at small shapes): the fixed-order dprob
   // combine of part[] (n_tiles partials per row) for side_nslot flat slots.
@@ -115,18 +117,22 @@ struct RouteParams {
   int nchunk;
   int atomic;
   uint64_t seed;
-  // backward work list (routing.sched), see sched_layout in moedet.hip
+  // backward work list (routing.sched)
   int32_t* sched;
-  int bm;          // row-tile height of the backward GEMMs
-  int kc;          // weight-gradient K chunk (rows)
-  int64_t mt_cap;  // capacity of the row-tile list
+  int bm;            // row-tile height of the backward GEMMs
+  int bm2;           // row-tile height of the second list (fc1 dgrad)
+  int kc;            // weight-gradient K chunk (rows)
+  int64_t mt_cap;    // capacity of the row-tile list
+  int64_t list2_at;  // int32 offset of the second row-tile list
 };
 
-// routing.sched: [0] row tiles, [1] weight-gradient units, [2..3] 0, then
-// mt_cap row-tile entries {expert, first row in the expert, first row
-// overall, rows} and the weight-gradient unit entries {expert | split << 30,
-// first row, rows, partial slot or -1}, four int32 each.
+// routing.sched: [0] row tiles of bm rows, [1] weight-gradient units,
+// [2] row tiles of bm2 rows, [3] 0; then mt_cap row-tile entries {expert,
+// first row in the expert, first row overall, rows}, wu_cap weight-gradient
+// unit entries {expert | split << 30, first row, rows, partial slot or -1}
+// and mt_cap2 row-tile entries of bm2 rows, four int32 each.
 constexpr int kSchedHeader = 4;
+constexpr int kRowTile2 = 192;  // bf16 fc1 dgrad row tile: two waves of 96 rows
 
 hipError_t launch_route(const RouteParams& P, hipStream_t st);
 hipError_t launch_permute_scan(const RouteParams& P, hipStream_t st);

@@ -30,8 +30,12 @@ struct Plan {
   int kc;             // wgrad K chunk (rows)
   bool may_split;     // some expert can hold more than kc rows
   int64_t wslots;     // wgrad partial slots per dW
-  int64_t mt_cap;     // routing.sched: row-tile entries
+  int64_t mt_cap;     // routing.sched: row-tile entries (bm rows)
   int64_t wu_cap;     // routing.sched: weight-gradient unit entries
+  int bm2;            // height of the second row-tile list
+  int64_t mt_cap2;    // routing.sched: row-tile entries (bm2 rows)
+  int64_t list2_at;   // routing.sched: int32 offset of the bm2 list
+  bool fc1_list2;     // the fc1 dgrad runs the bm2 list
   int64_t sched_elems;
   size_t esize;
 };
@@ -98,7 +102,16 @@ moe_status validate(const moe_problem* p, Plan* pl) {
     // sum over experts of ceil(cnt/BM) <= rows_cap/BM + El; of max(1, ceil(cnt/kc)) <= El + rows_cap/kc
     pl->mt_cap = (pl->rows_cap + bm - 1) / bm + pl->el;
     pl->wu_cap = pl->el + pl->rows_cap / kc + 1;
-    pl->sched_elems = kSchedHeader + 4 * (pl->mt_cap + pl->wu_cap);
+    pl->bm2 = bf16 ? kRowTile2 : bm;
+    // fc1 dgrad tiles of 192 rows (two wave rows of 96): a 256-row list with
+    // few tiles per expert leaves compute units idle and splits waves 128 /
+    // <128, while with many experts of few rows the extra tiles of the
+    // 192-row list only re-read weights (which then bound that GEMM); so the
+    // 192-row list is used when the mean expert has at least 512 rows.
+    pl->fc1_list2 = bf16 && mean >= 512.0;
+    pl->mt_cap2 = (pl->rows_cap + pl->bm2 - 1) / pl->bm2 + pl->el;
+    pl->list2_at = kSchedHeader + 4 * (pl->mt_cap + pl->wu_cap);
+    pl->sched_elems = pl->list2_at + 4 * pl->mt_cap2;
     pl->esize = bf16 ? 2 : 4;
   }
   return MOE_OK;
@@ -180,8 +193,8 @@ struct Stager {
   }
 };
 
-int64_t rowgemm_grid(const Plan& pl, int N) {
-  const int64_t mtiles = (pl.rows_cap + pl.bm - 1) / pl.bm + pl.el;
+int64_t rowgemm_grid(const Plan& pl, int N, bool list2 = false) {
+  const int64_t mtiles = list2 ? pl.mt_cap2 : pl.mt_cap;
   return grid_for_unit_rounds(mtiles * (N / pl.bn));
 }
 
@@ -330,6 +343,8 @@ MOE_API moe_status moe_fwd(const moe_problem* p, const float* logits, const void
   R.slot_row = routing->slot_row;
   R.sched = routing->sched;
   R.bm = pl.bm;
+  R.bm2 = pl.bm2;
+  R.list2_at = pl.list2_at;
   R.kc = pl.kc;
   R.mt_cap = pl.mt_cap;
   R.nchunk = pl.nchunk;
@@ -349,6 +364,8 @@ MOE_API moe_status moe_fwd(const moe_problem* p, const float* logits, const void
   G.groups = pl.el;
   G.ncu = device_cu_count();
   G.sched = routing->sched;
+  G.list_hdr = 0;
+  G.list_at = kSchedHeader;
   G.seed = seed;
   // fc1: h = x[row_tok] W1_g, W1 [D][F]
   void* arows = wsb + L.arows;
@@ -441,6 +458,8 @@ MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* 
   G.groups = pl.el;
   G.ncu = device_cu_count();
   G.sched = routing->sched;
+  G.list_hdr = 0;
+  G.list_at = kSchedHeader;
   G.seed = seed;
   // fc2 dgrad: G = dy[row_tok] W2_g^T; W2 [F][D] read as [N=F][K=D].
   G.N = pl.F;
@@ -474,6 +493,8 @@ MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* 
   G2.groups = pl.el;
   G2.ncu = device_cu_count();
   G2.sched = routing->sched;
+  G2.list_hdr = pl.fc1_list2 ? 2 : 0;
+  G2.list_at = pl.fc1_list2 ? pl.list2_at : kSchedHeader;
   G2.seed = seed;
   G2.N = pl.D;
   G2.K = pl.F;
@@ -487,7 +508,7 @@ MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* 
   G2.b_bytes = (uint32_t)(G2.b_gstride * pl.esize);
   G2.c = dxrows;
   G2.ldc = pl.D;
-  const int64_t gemm_grid = rowgemm_grid(pl, pl.D);
+  const int64_t gemm_grid = rowgemm_grid(pl, pl.D, pl.fc1_list2);
   int64_t side = 0;
   if (!at) {
     // the fixed-order dprob combine rides along as side units of this launch

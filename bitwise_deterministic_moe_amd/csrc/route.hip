@@ -99,12 +99,53 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams P) {
   for (int i = tid; i < P.el; i += 256) P.hist[b * P.el + i] = s_hist[i];
 }
 
+// Row tiles of height BM over the experts' rows, longest first: the full
+// tiles expert-major, then the partial tiles by descending rows (bitonic sort
+// of (BM - rows) << 10 | expert).  Entries {expert, first row in the expert,
+// first row overall, rows}; returns the count (uniform).  One thread per
+// expert (e = threadIdx.x) with its row count `total` and offset `off_e`.
+DEV int row_tile_list(const RouteParams& P, int4* mt, int BM, const int* s_cnt, const int* s_off, int* s_pre,
+                      int* s_tmp, uint32_t* s_key, int total, int off_e) {
+  const int e = threadIdx.x;
+  block_exclusive_scan<1024>(s_pre, s_tmp, P.el, [&](int g) { return s_cnt[g] / BM; });
+  const int nfull = s_pre[P.el];
+  if (e < P.el)
+    for (int i = 0; i < total / BM; ++i) mt[s_pre[e] + i] = int4{e, i * BM, off_e + i * BM, BM};
+  s_key[e] = (e < P.el && total % BM) ? ((uint32_t)(BM - total % BM) << 10) | (uint32_t)e : 0xffffffffu;
+  __syncthreads();
+  for (int k = 2; k <= 1024; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int o = e ^ j;
+      if (o > e) {
+        const uint32_t a = s_key[e], b = s_key[o];
+        if ((a > b) == ((e & k) == 0)) {
+          s_key[e] = b;
+          s_key[o] = a;
+        }
+      }
+      __syncthreads();
+    }
+  const uint32_t key = s_key[e];
+  if (key != 0xffffffffu) {
+    const int g = (int)(key & 1023u);
+    const int c = s_cnt[g];
+    const int m0 = c / BM * BM;
+    mt[nfull + e] = int4{g, m0, s_off[g] + m0, c - m0};
+  }
+  __syncthreads();
+  // number of partial tiles = sorted keys below the sentinel
+  block_exclusive_scan<1024>(s_pre, s_tmp, P.el, [&](int g) { return s_cnt[g] % BM != 0 ? 1 : 0; });
+  const int n = nfull + s_pre[P.el];
+  __syncthreads();
+  return n;
+}
+
 // hist[c][e] -> exclusive row base of chunk c for expert e; counts, offsets;
 // then the backward work list (routing.sched), from counts alone:
-//   row tiles of BM rows: every expert's full tiles (expert-major), then the
-//   partial last tiles ordered by descending rows (ties by expert), so that a
-//   GEMM whose tiles outnumber the compute units leaves the smallest tiles
-//   for its last round;
+//   row tiles of bm and of bm2 rows (row_tile_list): every expert's full
+//   tiles (expert-major), then the partial last tiles ordered by descending
+//   rows (ties by expert), so that a GEMM whose tiles outnumber the compute
+//   units leaves the smallest tiles for its last round;
 //   weight-gradient units: expert g in S_g = max(1, ceil(cnt_g / kc)) chunks,
 //   chunk s covering rows [s cnt/S, (s+1) cnt/S); chunks s >= 1 of a split
 //   expert own partial slot sum_{g'<g} (S_g' - 1) + s - 1.
@@ -136,41 +177,12 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(RouteParams P) {
   }
   __syncthreads();
 
-  int4* mt = (int4*)(P.sched + kSchedHeader);
-  const int BM = P.bm;
-  // full row tiles, expert-major
-  block_exclusive_scan<1024>(s_pre, s_tmp, P.el, [&](int g) { return s_cnt[g] / BM; });
-  const int nfull = s_pre[P.el];
-  if (e < P.el)
-    for (int i = 0; i < total / BM; ++i) mt[s_pre[e] + i] = int4{e, i * BM, off_e + i * BM, BM};
-  // partial tiles: bitonic sort of (BM - rows) << 10 | expert
-  s_key[e] = (e < P.el && total % BM) ? ((uint32_t)(BM - total % BM) << 10) | (uint32_t)e : 0xffffffffu;
-  __syncthreads();
-  for (int k = 2; k <= 1024; k <<= 1)
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const int o = e ^ j;
-      if (o > e) {
-        const uint32_t a = s_key[e], b = s_key[o];
-        if ((a > b) == ((e & k) == 0)) {
-          s_key[e] = b;
-          s_key[o] = a;
-        }
-      }
-      __syncthreads();
-    }
-  const uint32_t key = s_key[e];
-  if (key != 0xffffffffu) {
-    const int g = (int)(key & 1023u);
-    const int c = s_cnt[g];
-    const int m0 = c / BM * BM;
-    mt[nfull + e] = int4{g, m0, s_off[g] + m0, c - m0};
-  }
-  __syncthreads();
-  // number of partial tiles = sorted keys below the sentinel
-  block_exclusive_scan<1024>(s_pre, s_tmp, P.el, [&](int g) { return s_cnt[g] % BM != 0 ? 1 : 0; });
+  // row tiles of height P.bm (header word 0) and P.bm2 (header word 2)
+  const int n1 = row_tile_list(P, (int4*)(P.sched + kSchedHeader), P.bm, s_cnt, s_off, s_pre, s_tmp, s_key, total, off_e);
+  const int n2 = row_tile_list(P, (int4*)(P.sched + P.list2_at), P.bm2, s_cnt, s_off, s_pre, s_tmp, s_key, total, off_e);
   if (e == 0) {
-    P.sched[0] = nfull + s_pre[P.el];
-    P.sched[2] = 0;
+    P.sched[0] = n1;
+    P.sched[2] = n2;
     P.sched[3] = 0;
   }
   __syncthreads();
