@@ -12,9 +12,11 @@
 //           depends on shapes only:
 //           dW1 = x[row_tok]^T dh,   dW2 = (p relu(h)^2)^T dy[row_tok].
 //
-// Expert row counts live on the device, so every workgroup derives the
-// work decomposition itself from counts[] (no host synchronisation); the
-// grid is an upper bound and surplus workgroups exit at once.
+// Expert row counts live on the device: the permute scan turns them into
+// the routing work list (row tiles longest first, weight-gradient units),
+// which the workgroups of the bf16 kernels read (no host synchronisation);
+// the grid is an upper bound and surplus workgroups exit at once.  The
+// float32 weight-gradient kernels derive their units from counts[].
 //
 // Deterministic reductions (the English digest "Trillion-Parameter
 // Pretraining Goes Bitwise-Deterministic", section "Interpretation"):
@@ -646,15 +648,6 @@ DEV void wgrad_bf16_tile(const WgradParams& P, const WgradTile& t, float* dst, u
   });
 }
 
-template <bool A_GATHER, bool B_GATHER>
-__global__ __launch_bounds__(256) void wgrad_bf16_kernel(WgradParams P) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
-  __shared__ uint32_t s_rowoff[kMaxChunkRows];  // byte offset of each gathered row of the chunk
-  WgradTile t;
-  if (!wgrad_tile<bf::BM, bf::BN>(P, t)) return;
-  wgrad_bf16_tile<A_GATHER, B_GATHER>(P, t, wgrad_dst(P, t), lds, s_rowoff);
-}
-
 // Unit L of one of the two weight gradients of the paired launch: tile
 // L % tiles of weight-gradient unit L / tiles of the routing work list.
 template <bool A_GATHER, bool B_GATHER>
@@ -895,17 +888,11 @@ hipError_t launch_rowgemm(const RowGemmParams& P, int kind, bool bf16, int64_t g
 
 hipError_t launch_wgrad(const WgradParams& P, int which, bool bf16, int64_t grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
-  if (bf16) {
-    if (which == 1)
-      wgrad_bf16_kernel<true, false><<<grid, 256, 0, st>>>(P);
-    else
-      wgrad_bf16_kernel<false, true><<<grid, 256, 0, st>>>(P);
-  } else {
-    if (which == 1)
-      wgrad_f32_kernel<true, false><<<grid, 256, 0, st>>>(P);
-    else
-      wgrad_f32_kernel<false, true><<<grid, 256, 0, st>>>(P);
-  }
+  if (bf16) return hipErrorInvalidValue;  // bf16 runs launch_wgrad_pair
+  if (which == 1)
+    wgrad_f32_kernel<true, false><<<grid, 256, 0, st>>>(P);
+  else
+    wgrad_f32_kernel<false, true><<<grid, 256, 0, st>>>(P);
   return hipGetLastError();
 }
 
