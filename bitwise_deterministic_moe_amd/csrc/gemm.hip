@@ -63,6 +63,11 @@ DEV __amdgpu_buffer_rsrc_t buf(const void* p) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7fffffff, 0x00020000);
 }
 constexpr uint32_t kNoRow = 0x80000000u;
+// Cache policy of the epilogue's loads and stores: non-temporal.  Each
+// output element is written once and each h element read once per launch;
+// streaming them keeps the L2 for the operand tiles that several workgroups
+// of an XCD share (measured: fc2 dgrad 85 -> 78 us on the bf16 8x2 workload).
+constexpr int kEpiNT = 2;
 
 // Sum over the 4 lanes of each quad with two DPP butterflies (lane pairs
 // (0,1)(2,3), then (0,2)(1,3)); a + b == b + a, so all four lanes end with
@@ -419,7 +424,7 @@ struct HPre {
       const bool ok = m < t.mvalid;
       const uint32_t grow = (uint32_t)(t.off + t.m0 + (ok ? m : 0));
       d.h[st] = __builtin_amdgcn_raw_buffer_load_b64(
-          rh, ok ? (grow * (uint32_t)P.ldh + t.n0 + staged_col(tid)) * 2u : kNoRow, 0, 0);
+          rh, ok ? (grow * (uint32_t)P.ldh + t.n0 + staged_col(tid)) * 2u : kNoRow, 0, kEpiNT);
     }
   }
 };
@@ -505,7 +510,7 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
       if (m >= t.mvalid) return;  // uniform per wave
       const uint32_t grow = (uint32_t)(t.off + t.m0 + m);
       __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rc,
-                                            (grow * (uint32_t)P.ldc + t.n0 + col) * 2u, 0, 0);
+                                            (grow * (uint32_t)P.ldc + t.n0 + col) * 2u, 0, kEpiNT);
       if constexpr (EPI == kEpiStoreAct) {
         // activation of the stored (rounded) h, the value the backward sees
         float a[4];
@@ -515,7 +520,7 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
           a[q] = r * r;
         }
         __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])}, rc2,
-                                              (grow * (uint32_t)P.ldc2 + t.n0 + col) * 2u, 0, 0);
+                                              (grow * (uint32_t)P.ldc2 + t.n0 + col) * 2u, 0, kEpiNT);
       }
     });
   } else {
@@ -555,9 +560,9 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
         pa[q] = p * a;
       }
       const uint32_t o = (uint32_t)grow * 2u * (uint32_t)P.ldc + (t.n0 + col) * 2u;
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(dh[0], dh[1]), pack_bf16x2(dh[2], dh[3])}, rc, o, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(dh[0], dh[1]), pack_bf16x2(dh[2], dh[3])}, rc, o, 0, kEpiNT);
       __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(pa[0], pa[1]), pack_bf16x2(pa[2], pa[3])}, rc2,
-                                            (uint32_t)grow * 2u * (uint32_t)P.ldc2 + (t.n0 + col) * 2u, 0, 0);
+                                            (uint32_t)grow * 2u * (uint32_t)P.ldc2 + (t.n0 + col) * 2u, 0, kEpiNT);
       part = quad_sum(part);
       if ((lane & 3) == 0) s_qsum[m * 16 + (lane >> 2)] = part;
     });
@@ -643,7 +648,7 @@ DEV void wgrad_bf16_tile(const WgradParams& P, const WgradTile& t, float* dst, u
 #pragma unroll
       for (int q = 0; q < 4; ++q) atomicAdd(po + q, v[q]);
     } else {
-      __builtin_amdgcn_raw_buffer_store_b128(f32x4_t{v[0], v[1], v[2], v[3]}, rd, o, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(f32x4_t{v[0], v[1], v[2], v[3]}, rd, o, 0, kEpiNT);
     }
   });
 }
