@@ -175,6 +175,7 @@ def main():
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
 
     value = flops / (ms_det * 1e-3) / 1e12
+    mfma_peak = measured_mfma_peak()
     result = {
         "metric": "MoE grouped-GEMM bwd TFLOP/s (det mode), % bf16 peak; determinism tax vs atomic",
         "value": round(value, 2),
@@ -193,6 +194,7 @@ def main():
                    "tokens": cfg.tokens, "d_model": D, "d_ffn": F, "experts": cfg.num_experts,
                    "top_k": cfg.top_k, "routed_rows": R, "mode": "deterministic", "parallelism": "single GPU"},
         "pct_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
+        "mfma_peak_measured": dict(mfma_peak, pct_of_measured=round(100.0 * value / mfma_peak["tflops"], 2)),
         "determinism_tax": {
             "tax": round(med_d / med_a - 1.0, 4),
             "det_ms_median": round(med_d, 5), "det_ms_iqr": round(iqr(td), 5),
@@ -210,6 +212,29 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, host, flops)
     print(json.dumps(result), flush=True)
+
+
+def measured_mfma_peak(iters=20000, reps=5):
+    """Attainable bf16 MFMA rate of this device: the library's register-only
+    MFMA loop (moe_mfma_rate) on two workgroups per compute unit, best of
+    `reps` timed launches.  The sink is checked against its closed form."""
+    import torch
+    import bitwise_deterministic_moe_amd as moe
+    blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    v = 0.125
+    sink = moe.moe_mfma_rate(blocks, 200, v)   # warm-up
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        moe.moe_mfma_rate(blocks, iters, v, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, blocks * 4 * iters * 8 * 32768 / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    expect = 2048.0 * v * v * iters
+    ok = bool(torch.all(sink == expect).item())
+    return {"tflops": round(best, 1), "kernel": "v_mfma_f32_32x32x16_bf16 register loop", "blocks": blocks,
+            "iters": iters, "sink_check": ok}
 
 
 def measured_traffic(stage):

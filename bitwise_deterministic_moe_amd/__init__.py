@@ -16,7 +16,8 @@ import torch
 __all__ = [
     "DETERMINISTIC", "ATOMIC", "Problem", "Routing", "MoeError", "MoeLibraryMissing",
     "load_library", "library_path", "moe_workspace_size", "moe_rows_cap", "moe_stage_names",
-    "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad", "moe_fingerprint", "moe_sched_elems", "EXPORTED_SYMBOLS",
+    "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad", "moe_fingerprint", "moe_sched_elems", "moe_mfma_rate",
+    "EXPORTED_SYMBOLS",
 ]
 
 DETERMINISTIC = 0
@@ -27,7 +28,7 @@ _TORCH_TO_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.int32: 2, torch.uin
                   torch.int64: 4, torch.float64: 5}
 EXPORTED_SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_rows_cap", "moe_sched_elems",
                     "moe_workspace_size", "moe_stage_names", "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad",
-                    "moe_fingerprint")
+                    "moe_fingerprint", "moe_mfma_rate")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -84,8 +85,9 @@ def load_library() -> ctypes.CDLL:
     lib.moe_bwd_wgrad.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
     lib.moe_fingerprint.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
                                     vp, vp, vp]
+    lib.moe_mfma_rate.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_float, vp, vp]
     for f in ("moe_rows_cap", "moe_sched_elems", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob",
-              "moe_bwd_wgrad", "moe_fingerprint"):
+              "moe_bwd_wgrad", "moe_fingerprint", "moe_mfma_rate"):
         getattr(lib, f).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -297,3 +299,13 @@ def moe_fingerprint(t: torch.Tensor, dtype: Optional[str] = None, chunk_elems: i
     if not sync:
         return hashes[:m], total
     return hashes[:m], int(total.item()) & 0xFFFFFFFFFFFFFFFF
+
+
+def moe_mfma_rate(blocks: int, iters: int, value: float = 0.125, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Enqueue the MFMA-rate loop on the current stream; returns the sink
+    (float32 [256 * blocks] on the current device)."""
+    lib = load_library()
+    if sink is None:
+        sink = torch.empty(256 * blocks, dtype=torch.float32, device="cuda")
+    _check(lib.moe_mfma_rate(blocks, iters, value, _ptr(sink), _stream()), "moe_mfma_rate")
+    return sink

@@ -160,6 +160,7 @@ hipError_t launch_dprob_combine(const float* part, const int32_t* slot_row, int6
                                 float* dprob, uint64_t seed, hipStream_t st);
 
 // fingerprint
+hipError_t launch_mfma_rate(int64_t blocks, int64_t iters, float v, float* sink, hipStream_t st);
 hipError_t launch_fingerprint(const void* data, int width, int64_t n, int64_t chunk,
                               const uint64_t* words, int nwords, uint64_t* chunk_hashes,
                               uint64_t* total, hipStream_t st);

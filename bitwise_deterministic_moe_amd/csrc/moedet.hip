@@ -674,3 +674,12 @@ MOE_API moe_status moe_fingerprint(const void* data, moe_dtype dtype, int ndim, 
                                     (hipStream_t)stream);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
+
+MOE_API moe_status moe_mfma_rate(int64_t blocks, int64_t iters, float value, float* sink, void* stream) {
+  if (blocks < 1 || blocks >= ((int64_t)1 << 31) || iters < 1) return MOE_ERR_SHAPE;
+  if (!sink) return MOE_ERR_NULL;
+  uint32_t bits;
+  memcpy(&bits, &value, 4);
+  if (bits & 0xffffu) return MOE_ERR_SHAPE;  // not a bf16 value
+  return launch_mfma_rate(blocks, iters, value, sink, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}

@@ -247,6 +247,23 @@ moe_status moe_fingerprint(const void* data, moe_dtype dtype, int ndim, const in
                            int64_t chunk_elems, uint64_t* chunk_hashes, uint64_t* total,
                            void* stream);
 
+/* Diagnostic for the measurement of the percent of bf16 dense peak: the
+ * attainable MFMA rate of the device.  Enqueues on `stream` one launch of
+ * `blocks` workgroups of 4 waves; every wave issues iters x 8 independent
+ * v_mfma_f32_32x32x16_bf16 on register operands that hold `value` in every
+ * element (no memory traffic in the loop), then thread t of block b writes
+ * the sum of its 128 accumulator elements to sink[256 b + t].  The launch
+ * performs blocks * 4 * iters * 8 * 32768 floating-point operations; the
+ * caller times it with events on the same stream.  Each sink element is
+ * 2048 * value^2 * iters while that is exact in float32.
+ *   blocks  1 .. 2^31-1 (two per compute unit fill every SIMD twice)
+ *   iters   >= 1
+ *   value   a float whose low 16 bits are zero (a bf16 value)
+ *   sink    DEVICE float[256 * blocks], caller-owned
+ * Errors: MOE_ERR_SHAPE (blocks, iters or value out of range), MOE_ERR_NULL
+ * (sink), MOE_ERR_HIP (launch failure).  Nothing is enqueued on error. */
+moe_status moe_mfma_rate(int64_t blocks, int64_t iters, float value, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -124,3 +124,12 @@ def test_workspace_sizes_and_rows_cap():
     assert moe.moe_stage_names(p, 0, 1) == ["fc2_dgrad_dprob_partials", "fc1_dgrad_dprob_combine",
                                             "dx_combine_gather"]
     assert moe.moe_stage_names(p, 1, 2) == ["wgrad_fc1_fc2"]
+
+
+def test_mfma_rate_validation_returns_before_enqueue(lib):
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.moe_mfma_rate(0, 10, 0.125, fake, None) == 2          # no blocks
+    assert lib.moe_mfma_rate(1 << 31, 10, 0.125, fake, None) == 2    # grid too large
+    assert lib.moe_mfma_rate(4, 0, 0.125, fake, None) == 2           # no iterations
+    assert lib.moe_mfma_rate(4, 10, 0.1, fake, None) == 2            # 0.1 is not a bf16 value
+    assert lib.moe_mfma_rate(4, 10, 0.125, None, None) == 1          # NULL sink
