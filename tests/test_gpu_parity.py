@@ -24,6 +24,9 @@ EDGE = {
     "split_k_bf16": Config("split_k_bf16", 2048, 256, 256, 16, 1, 0, 16, "bf16", 1, 18, skew="zipf",
                            zipf_beta=2.0, zipf_empty=2),
     "no_tokens_bf16": Config("no_tokens_bf16", 0, 256, 256, 4, 2, 0, 4, "bf16", 1, 19),
+    # mean 750 rows per expert: the fc1 dgrad runs the 192-row tile list
+    # (three full tiles and a ragged one per expert), the fc2 dgrad 256-row tiles
+    "rows192_bf16": Config("rows192_bf16", 1500, 256, 512, 4, 2, 0, 4, "bf16", 1, 22),
     "ragged_fp32": Config("ragged_fp32", 37, 64, 192, 3, 2, 0, 3, "f32", 1, 20),
     "shard_fp32": Config("shard_fp32", 90, 128, 64, 8, 3, 2, 4, "f32", 0, 21),
 }
