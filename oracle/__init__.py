@@ -11,3 +11,6 @@ from .moe import (  # noqa: F401
     combine_rows, layer_loss,
 )
 from .fingerprint import fingerprint, mix64, DTYPE_CODE  # noqa: F401
+from .router import (  # noqa: F401
+    router_logits, router_probs, router_dlogits, router_backward, router_loss,
+)

@@ -22,7 +22,7 @@ import numpy as np
 
 from .configs import Config
 
-_TENSOR_CODE = {"logits": 0, "x": 1, "w1": 2, "w2": 3, "dy": 4, "zipf_rank": 5}
+_TENSOR_CODE = {"logits": 0, "x": 1, "w1": 2, "w2": 3, "dy": 4, "zipf_rank": 5, "wr": 6, "dprob": 7}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -140,3 +140,14 @@ def make_inputs(cfg: Config, parts=("logits", "x", "w1", "w2", "dy"), experts=No
     if "dy" in parts:
         out["dy"] = _draw(_rng(cfg.seed, "dy"), (cfg.tokens, cfg.d_model), 1.0, cfg.dtype)
     return out
+
+
+def make_router_inputs(cfg: Config) -> dict:
+    """Router weights wr [E, D] (storage dtype, N(0, w_std)) and an upstream
+    gradient dprob [T, k] (float32, N(0, 1)) for exercising the router backward
+    on its own.  Drawn from streams of their own, so the layer's other inputs
+    are unchanged."""
+    return {
+        "wr": _draw(_rng(cfg.seed, "wr"), (cfg.num_experts, cfg.d_model), cfg.w_std, cfg.dtype),
+        "dprob": _draw(_rng(cfg.seed, "dprob"), (cfg.tokens, cfg.top_k), 1.0, "f32"),
+    }
