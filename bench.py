@@ -176,6 +176,7 @@ def main():
 
     value = flops / (ms_det * 1e-3) / 1e12
     mfma_peak = measured_mfma_peak()
+    router = measured_router_bwd(cfg, prob, routing, x, det.dprob) if cfg.combine and el == cfg.num_experts else None
     result = {
         "metric": "MoE grouped-GEMM bwd TFLOP/s (det mode), % bf16 peak; determinism tax vs atomic",
         "value": round(value, 2),
@@ -201,6 +202,7 @@ def main():
             "atomic_ms_median": round(med_a, 5), "atomic_ms_iqr": round(iqr(ta), 5),
             "interleaved_pairs": args.steps,
         },
+        "router_bwd": router,
         "stages_ms_det": {k: round(v, 5) for k, v in st_det.items()},
         "stages_ms_atomic": {k: round(v, 5) for k, v in st_atom.items()},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
@@ -235,6 +237,45 @@ def measured_mfma_peak(iters=20000, reps=5):
     ok = bool(torch.all(sink == expect).item())
     return {"tflops": round(best, 1), "kernel": "v_mfma_f32_32x32x16_bf16 register loop", "blocks": blocks,
             "iters": iters, "sink_check": ok}
+
+
+def measured_router_bwd(cfg, prob, routing, x, dprob, reps=20):
+    """The router backward (outside the step) on the same routing and the
+    step's dprob, with seeded router weights: average launch-sequence time over
+    `reps` back-to-back calls, against HBM for its algorithmic bytes (x and
+    the router weights read once, dlogits, dw_router and dx_router written once,
+    the routing's per-slot arrays read once)."""
+    import torch
+    import bitwise_deterministic_moe_amd as moe
+    from synth import make_router_inputs
+    import numpy as np
+    ri = make_router_inputs(cfg)
+    wr = torch.from_numpy(np.ascontiguousarray(ri["wr"]).view(np.int16 if cfg.dtype == "bf16" else np.float32))
+    wr = wr.cuda().view(torch.bfloat16) if cfg.dtype == "bf16" else wr.cuda()
+    outs = moe.moe_router_bwd(prob, routing, dprob, x, wr)
+    for mode in (moe.DETERMINISTIC, moe.ATOMIC):
+        moe.moe_router_bwd(prob, routing, dprob, x, wr, mode, *outs)
+    torch.cuda.synchronize()
+    res = {}
+    for name, mode in (("det", moe.DETERMINISTIC), ("atomic", moe.ATOMIC)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            moe.moe_router_bwd(prob, routing, dprob, x, wr, mode, *outs)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / reps
+    T, E, D, k = cfg.tokens, cfg.num_experts, cfg.d_model, cfg.top_k
+    es = 2 if cfg.dtype == "bf16" else 4
+    hbm = T * D * es + E * D * es + T * E * 4 + E * D * 4 + T * D * es + T * k * 12 + T * k * 4
+    # both reductions gather T*k rows of D elements (x rows for dw_router,
+    # router rows for dx_router), which the L2 serves
+    gather = 2 * T * k * D * es
+    sec = res["det"] * 1e-3
+    return {"ms_det": round(res["det"], 5), "ms_atomic": round(res["atomic"], 5),
+            "tax": round(res["det"] / res["atomic"] - 1.0, 4), "hbm_bytes": hbm,
+            "achieved_GBs": round(hbm / sec / 1e9, 1), "frac_hbm": round(hbm / sec / 1e9 / HBM_PEAK_GBS, 4),
+            "gather_bytes": gather, "gather_GBs": round(gather / sec / 1e9, 1)}
 
 
 def measured_traffic(stage):

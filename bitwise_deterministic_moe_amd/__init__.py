@@ -17,7 +17,7 @@ __all__ = [
     "DETERMINISTIC", "ATOMIC", "Problem", "Routing", "MoeError", "MoeLibraryMissing",
     "load_library", "library_path", "moe_workspace_size", "moe_rows_cap", "moe_stage_names",
     "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad", "moe_fingerprint", "moe_sched_elems", "moe_mfma_rate",
-    "EXPORTED_SYMBOLS",
+    "moe_router_bwd", "EXPORTED_SYMBOLS",
 ]
 
 DETERMINISTIC = 0
@@ -28,7 +28,7 @@ _TORCH_TO_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.int32: 2, torch.uin
                   torch.int64: 4, torch.float64: 5}
 EXPORTED_SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_rows_cap", "moe_sched_elems",
                     "moe_workspace_size", "moe_stage_names", "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad",
-                    "moe_fingerprint", "moe_mfma_rate")
+                    "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -86,8 +86,9 @@ def load_library() -> ctypes.CDLL:
     lib.moe_fingerprint.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
                                     vp, vp, vp]
     lib.moe_mfma_rate.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_float, vp, vp]
+    lib.moe_router_bwd.argtypes = [P, R, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp]
     for f in ("moe_rows_cap", "moe_sched_elems", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob",
-              "moe_bwd_wgrad", "moe_fingerprint", "moe_mfma_rate"):
+              "moe_bwd_wgrad", "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd"):
         getattr(lib, f).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -273,6 +274,25 @@ def moe_bwd_wgrad(prob: Problem, routing: Routing, x, dy, dh, act_p, mode: int =
     _check(lib.moe_bwd_wgrad(ctypes.byref(cp), ctypes.byref(cr), _ptr(x), _ptr(dy), _ptr(dh), _ptr(act_p), _ptr(dw1),
                              _ptr(dw2), _ptr(ws), ws.numel(), mode, _stream()), "moe_bwd_wgrad")
     return dw1, dw2
+
+
+def moe_router_bwd(prob: Problem, routing: Routing, dprob, x, w_router, mode: int = DETERMINISTIC, dlogits=None,
+                   dw_router=None, dx_router=None):
+    """Router backward (full layer only).  Returns (dlogits float32 [T,E],
+    dw_router float32 [E,D], dx_router [T,D] in the storage dtype)."""
+    lib = load_library()
+    dev = w_router.device
+    T, E, D = prob.tokens, prob.num_experts, prob.d_model
+    if dlogits is None:
+        dlogits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    if dw_router is None:
+        dw_router = torch.empty((E, D), dtype=torch.float32, device=dev)
+    if dx_router is None:
+        dx_router = torch.empty((T, D), dtype=TORCH_DTYPE[prob.dtype], device=dev)
+    cp, cr = prob.c(), routing.c()
+    _check(lib.moe_router_bwd(ctypes.byref(cp), ctypes.byref(cr), _ptr(dprob), _ptr(x), _ptr(w_router), _ptr(dlogits),
+                              _ptr(dw_router), _ptr(dx_router), mode, _stream()), "moe_router_bwd")
+    return dlogits, dw_router, dx_router
 
 
 def moe_fingerprint(t: torch.Tensor, dtype: Optional[str] = None, chunk_elems: int = 65536,

@@ -87,6 +87,25 @@ struct WgradParams {
   uint64_t seed;
 };
 
+struct RouterParams {
+  int64_t T;
+  int k, E, D;
+  const int32_t* topk_idx;
+  const float* topk_prob;
+  const float* dprob;
+  const int32_t* offsets;
+  const int32_t* counts;
+  const int32_t* row_tok;
+  const void* x;
+  const void* wr;
+  float* dlogits;
+  float* dwr;
+  void* dx;
+  int phases;  // dwr row phases: 8 or 64
+  int atomic;
+  uint64_t seed;
+};
+
 struct WgradPrepParams {
   const int32_t* counts;
   int32_t* sched;
@@ -156,6 +175,7 @@ hipError_t launch_scatter_add(const void* rows, const int32_t* offsets, int el,
                               float* out32, bool bf16, uint64_t seed, hipStream_t st);
 hipError_t launch_cast(const float* in32, void* out, int64_t n, bool bf16, hipStream_t st);
 hipError_t launch_zero(float* p, int64_t n, hipStream_t st);
+hipError_t launch_router_bwd(const RouterParams& P, bool bf16, hipStream_t st);
 hipError_t launch_dprob_combine(const float* part, const int32_t* slot_row, int64_t nslots, int n_tiles,
                                 float* dprob, uint64_t seed, hipStream_t st);
 

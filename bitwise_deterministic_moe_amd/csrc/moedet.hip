@@ -638,6 +638,44 @@ MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routin
   return sg.err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+MOE_API moe_status moe_router_bwd(const moe_problem* p, const moe_routing* routing, const float* dprob,
+                                  const void* x, const void* w_router, float* dlogits, float* dw_router,
+                                  void* dx_router, moe_mode mode, void* stream) {
+  Plan pl;
+  moe_status s = validate(p, &pl);
+  if (s != MOE_OK) return s;
+  if (mode != MOE_DETERMINISTIC && mode != MOE_ATOMIC) return MOE_ERR_MODE;
+  // the router backward needs every expert's routed rows: full layer only
+  if (p->combine != 1 || p->num_local != p->num_experts) return MOE_ERR_SHAPE;
+  if (!routing || !dw_router || !routing->counts || !routing->offsets) return MOE_ERR_NULL;
+  if (!w_router && pl.T > 0) return MOE_ERR_NULL;
+  if (pl.T > 0 && (!dprob || !x || !dlogits || !dx_router || !routing->topk_idx || !routing->topk_prob ||
+                   !routing->row_tok))
+    return MOE_ERR_NULL;
+  RouterParams R{};
+  R.T = pl.T;
+  R.k = pl.k;
+  R.E = pl.E;
+  R.D = pl.D;
+  R.topk_idx = routing->topk_idx;
+  R.topk_prob = routing->topk_prob;
+  R.dprob = dprob;
+  R.offsets = routing->offsets;
+  R.counts = routing->counts;
+  R.row_tok = routing->row_tok;
+  R.x = x;
+  R.wr = w_router;
+  R.dlogits = dlogits;
+  R.dwr = dw_router;
+  R.dx = dx_router;
+  // dw_router row phases: a function of the shapes only (the mean routed
+  // rows per expert and d_model), so the summation order is fixed
+  R.phases = ((double)pl.T * pl.k / pl.E < 512.0 && pl.D % 256 == 0) ? 8 : 64;
+  R.atomic = mode == MOE_ATOMIC;
+  R.seed = p->debug_shuffle_seed;
+  return launch_router_bwd(R, pl.bf16, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 MOE_API moe_status moe_fingerprint(const void* data, moe_dtype dtype, int ndim, const int64_t* shape,
                                    int64_t chunk_elems, uint64_t* chunk_hashes, uint64_t* total,
                                    void* stream) {

@@ -247,6 +247,35 @@ moe_status moe_fingerprint(const void* data, moe_dtype dtype, int ndim, const in
                            int64_t chunk_elems, uint64_t* chunk_hashes, uint64_t* total,
                            void* stream);
 
+/* Router backward, the step upstream of dprob ("Trillion-Parameter
+ * Pretraining Goes Bitwise-Deterministic", section "Interpretation": the
+ * grouped-GEMM epilogue produces dprob per token and selected expert; the
+ * router consumes it).  Router: logits[t,e] = <x_t, wr_e>, the k largest
+ * selected, p = softmax over them.
+ *   dprob      DEVICE float[T,k]: gradient of the loss w.r.t. topk_prob
+ *              (e.g. moe_bwd_dgrad_dprob's output)
+ *   x          DEVICE [T,D] storage dtype (the layer input)
+ *   w_router   DEVICE [E,D] storage dtype, row e = expert e's router vector
+ *   dlogits    DEVICE float[T,E] output: p_j (dprob_j - sum_i p_i dprob_i) at
+ *              the selected experts (sum over i ascending, float32), 0 elsewhere
+ *   dw_router  DEVICE float[E,D] output: dlogits^T x.  Deterministic mode sums
+ *              each expert's routed rows (routing order) in PH fixed row
+ *              phases and adds the phase sums in phase order (PH = 8 when
+ *              T*k/E < 512 and D is a multiple of 256, else 64); atomic mode
+ *              adds the phase sums with atomicAdd (the nondeterministic control)
+ *   dx_router  DEVICE [T,D] storage dtype output: dlogits wr, j ascending,
+ *              float32 accumulation, one rounding (the router's share of dx;
+ *              the caller adds it to the expert path's dx)
+ * routing: topk_idx, topk_prob, counts, offsets and row_tok as written by
+ * moe_fwd of the same problem.  Only the full layer is supported (combine = 1,
+ * num_local = num_experts), since dw_router needs every expert's rows:
+ * MOE_ERR_SHAPE otherwise.  Every output element is written.  Errors:
+ * MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_MODE before anything is
+ * enqueued; MOE_ERR_HIP for a launch failure. */
+moe_status moe_router_bwd(const moe_problem* p, const moe_routing* routing, const float* dprob,
+                          const void* x, const void* w_router, float* dlogits, float* dw_router,
+                          void* dx_router, moe_mode mode, void* stream);
+
 /* Diagnostic for the measurement of the percent of bf16 dense peak: the
  * attainable MFMA rate of the device.  Enqueues on `stream` one launch of
  * `blocks` workgroups of 4 waves; every wave issues iters x 8 independent

@@ -133,3 +133,21 @@ def test_mfma_rate_validation_returns_before_enqueue(lib):
     assert lib.moe_mfma_rate(4, 0, 0.125, fake, None) == 2           # no iterations
     assert lib.moe_mfma_rate(4, 10, 0.1, fake, None) == 2            # 0.1 is not a bf16 value
     assert lib.moe_mfma_rate(4, 10, 0.125, None, None) == 1          # NULL sink
+
+
+def test_router_bwd_validation_returns_before_enqueue(lib):
+    fake = ctypes.c_void_p(0x1000)
+    r = moe._CRouting(*([0x2000] * 9))
+    cp = moe.Problem(**BASE).c()
+    ok_args = lambda: [fake] * 6
+    # NULL dprob / x / outputs with tokens > 0
+    assert lib.moe_router_bwd(ctypes.byref(cp), ctypes.byref(r), None, *ok_args()[:5], 0, None) == 1
+    assert lib.moe_router_bwd(ctypes.byref(cp), ctypes.byref(r), fake, fake, fake, fake, None, fake, 0, None) == 1
+    # bad mode
+    assert lib.moe_router_bwd(ctypes.byref(cp), ctypes.byref(r), *ok_args(), 7, None) == 5
+    # a shard (num_local < num_experts, row layout) is rejected
+    sp = moe.Problem(**{**BASE, "expert_begin": 2, "num_local": 4, "combine": 0}).c()
+    assert lib.moe_router_bwd(ctypes.byref(sp), ctypes.byref(r), *ok_args(), 0, None) == 2
+    # NULL routing arrays
+    r0 = moe._CRouting(*([0x2000] * 2 + [0] + [0x2000] * 6))
+    assert lib.moe_router_bwd(ctypes.byref(cp), ctypes.byref(r0), *ok_args(), 0, None) == 1

@@ -24,9 +24,9 @@ import torch
 
 import bitwise_deterministic_moe_amd as moe
 import oracle
-from synth import CONFIGS, make_inputs
+from synth import CONFIGS, make_inputs, make_router_inputs
 from synth.inputs import make_expert_weights
-from harness import DeviceInputs, compare_routing, fingerprints, rel_l2, run_layer, to_host
+from harness import DeviceInputs, compare_routing, fingerprints, rel_l2, run_layer, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -194,6 +194,21 @@ def test_large_parity_and_determinism(name):
     if len(empty):
         ei = torch.as_tensor(empty, device="cuda")
         assert torch.all(out["dw1"][ei] == 0) and torch.all(out["dw2"][ei] == 0)
+
+    # router backward at full size (full-layer workloads): seeded dprob and
+    # router weights, the layer's routing, whole tensors against the oracle
+    if cfg.combine and cfg.num_local == cfg.num_experts:
+        ri = make_router_inputs(cfg)
+        dl, dwr, dxr = moe.moe_router_bwd(prob, r, torch.from_numpy(ri["dprob"]).cuda(), di.x,
+                                          to_dev(ri["wr"], cfg.dtype))
+        torch.cuda.synchronize()
+        ref = oracle.router_backward(idx, p, ri["dprob"], oracle.decode(host["x"], cfg.dtype),
+                                     oracle.decode(ri["wr"], cfg.dtype))
+        rerr = {"router_dlogits": rel_l2(to_host(dl), ref["dlogits"]), "router_dwr": rel_l2(to_host(dwr), ref["dwr"]),
+                "router_dx": rel_l2(to_host(dxr), ref["dx"])}
+        print(f"[{name}] router rel-L2 {rerr}", flush=True)
+        assert rerr["router_dlogits"] <= 1e-5 and rerr["router_dwr"] <= 1e-5 and rerr["router_dx"] <= 2e-2, rerr
+        del dl, dwr, dxr
 
     # bit identity under a shuffled workgroup order with launch delays
     fp0 = fingerprints(out, cfg.combine)
