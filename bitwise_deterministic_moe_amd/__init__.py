@@ -17,7 +17,7 @@ __all__ = [
     "DETERMINISTIC", "ATOMIC", "Problem", "Routing", "MoeError", "MoeLibraryMissing",
     "load_library", "library_path", "moe_workspace_size", "moe_rows_cap", "moe_stage_names",
     "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad", "moe_fingerprint", "moe_sched_elems", "moe_mfma_rate",
-    "moe_router_bwd", "EXPORTED_SYMBOLS",
+    "moe_router_bwd", "moe_router_fwd", "moe_sgd_step", "EXPORTED_SYMBOLS",
 ]
 
 DETERMINISTIC = 0
@@ -28,7 +28,7 @@ _TORCH_TO_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.int32: 2, torch.uin
                   torch.int64: 4, torch.float64: 5}
 EXPORTED_SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_rows_cap", "moe_sched_elems",
                     "moe_workspace_size", "moe_stage_names", "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad",
-                    "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd")
+                    "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd", "moe_sgd_step")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -87,8 +87,11 @@ def load_library() -> ctypes.CDLL:
                                     vp, vp, vp]
     lib.moe_mfma_rate.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_float, vp, vp]
     lib.moe_router_bwd.argtypes = [P, R, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp]
+    lib.moe_router_fwd.argtypes = [P, vp, vp, vp, vp]
+    lib.moe_sgd_step.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_float, vp, ctypes.c_int, vp]
     for f in ("moe_rows_cap", "moe_sched_elems", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob",
-              "moe_bwd_wgrad", "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd"):
+              "moe_bwd_wgrad", "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd",
+              "moe_sgd_step"):
         getattr(lib, f).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -293,6 +296,30 @@ def moe_router_bwd(prob: Problem, routing: Routing, dprob, x, w_router, mode: in
     _check(lib.moe_router_bwd(ctypes.byref(cp), ctypes.byref(cr), _ptr(dprob), _ptr(x), _ptr(w_router), _ptr(dlogits),
                               _ptr(dw_router), _ptr(dx_router), mode, _stream()), "moe_router_bwd")
     return dlogits, dw_router, dx_router
+
+
+def moe_router_fwd(prob: Problem, x, w_router, logits=None):
+    """Router logits float32 [T,E] = x w_router^T (d ascending, fp32 FMA)."""
+    lib = load_library()
+    if logits is None:
+        logits = torch.empty((prob.tokens, prob.num_experts), dtype=torch.float32, device=w_router.device)
+    cp = prob.c()
+    _check(lib.moe_router_fwd(ctypes.byref(cp), _ptr(x), _ptr(w_router), _ptr(logits), _stream()), "moe_router_fwd")
+    return logits
+
+
+def moe_sgd_step(master: torch.Tensor, grad: torch.Tensor, lr: float, runtime: torch.Tensor):
+    """master -= lr * grad (float32, in place); runtime = master rounded to
+    runtime's dtype.  All three tensors contiguous with the same element count."""
+    lib = load_library()
+    if not (master.is_contiguous() and grad.is_contiguous() and runtime.is_contiguous()):
+        raise MoeError("moe_sgd_step needs contiguous tensors")
+    n = master.numel()
+    if grad.numel() != n or runtime.numel() != n or master.dtype != torch.float32 or grad.dtype != torch.float32:
+        raise MoeError("moe_sgd_step: master and grad float32 with runtime's element count")
+    code = _TORCH_TO_CODE[runtime.dtype]
+    _check(lib.moe_sgd_step(_ptr(master), _ptr(grad), n, lr, _ptr(runtime), code, _stream()), "moe_sgd_step")
+    return master, runtime
 
 
 def moe_fingerprint(t: torch.Tensor, dtype: Optional[str] = None, chunk_elems: int = 65536,

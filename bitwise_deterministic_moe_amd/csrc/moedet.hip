@@ -676,6 +676,28 @@ MOE_API moe_status moe_router_bwd(const moe_problem* p, const moe_routing* routi
   return launch_router_bwd(R, pl.bf16, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+MOE_API moe_status moe_router_fwd(const moe_problem* p, const void* x, const void* w_router, float* logits,
+                                  void* stream) {
+  Plan pl;
+  moe_status s = validate(p, &pl);
+  if (s != MOE_OK) return s;
+  if (pl.T > 0 && (!x || !w_router || !logits)) return MOE_ERR_NULL;
+  return launch_router_fwd(x, w_router, pl.T, pl.E, pl.D, logits, pl.bf16, p->debug_shuffle_seed,
+                           (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+MOE_API moe_status moe_sgd_step(float* master, const float* grad, int64_t n, float lr, void* runtime,
+                                moe_dtype dtype, void* stream) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (n < 0 || n >= ((int64_t)1 << 40)) return MOE_ERR_SHAPE;
+  if (n > 0 && (!master || !grad || !runtime)) return MOE_ERR_NULL;
+  return launch_sgd(master, grad, n, lr, runtime, dtype == MOE_BF16, (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
 MOE_API moe_status moe_fingerprint(const void* data, moe_dtype dtype, int ndim, const int64_t* shape,
                                    int64_t chunk_elems, uint64_t* chunk_hashes, uint64_t* total,
                                    void* stream) {

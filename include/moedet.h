@@ -276,6 +276,32 @@ moe_status moe_router_bwd(const moe_problem* p, const moe_routing* routing, cons
                           const void* x, const void* w_router, float* dlogits, float* dw_router,
                           void* dx_router, moe_mode mode, void* stream);
 
+/* Router forward for a train step of the layer: logits[t,e] = sum over d
+ * ascending of x[t,d] * w_router[e,d] in float32 fused multiply-adds, one
+ * thread per logit (no reduction across threads, so bit-exact).  The router
+ * form is the reading stated at moe_router_bwd.
+ *   x         DEVICE [T,D] storage dtype;  w_router DEVICE [E,D] storage dtype
+ *   logits    DEVICE float[T,E] output (the input of moe_fwd)
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE (the problem's checks)
+ * before anything is enqueued; MOE_ERR_HIP for a launch failure. */
+moe_status moe_router_fwd(const moe_problem* p, const void* x, const void* w_router, float* logits,
+                          void* stream);
+
+/* Plain SGD step on a full-precision master copy, with the runtime copy
+ * rebuilt through the same conversion the layer uses ("Trillion-Parameter
+ * Pretraining Goes Bitwise-Deterministic", section "Interpretation": keep a
+ * full-precision source of truth and reconstruct the runtime representation
+ * through the training's conversion path):
+ *   master[i] = fma(-lr, grad[i], master[i])   (float32)
+ *   runtime[i] = master[i] rounded to `dtype` (RNE for MOE_BF16, copy for MOE_F32)
+ *   master    DEVICE float[n], updated in place;  grad DEVICE float[n]
+ *   runtime   DEVICE [n] of `dtype`, output
+ * Elementwise, so bit-exact.  Errors: MOE_ERR_DTYPE (dtype not F32/BF16),
+ * MOE_ERR_SHAPE (n < 0 or n >= 2^40), MOE_ERR_NULL; MOE_ERR_HIP for a launch
+ * failure. */
+moe_status moe_sgd_step(float* master, const float* grad, int64_t n, float lr, void* runtime, moe_dtype dtype,
+                        void* stream);
+
 /* Diagnostic for the measurement of the percent of bf16 dense peak: the
  * attainable MFMA rate of the device.  Enqueues on `stream` one launch of
  * `blocks` workgroups of 4 waves; every wave issues iters x 8 independent

@@ -151,3 +151,15 @@ def make_router_inputs(cfg: Config) -> dict:
         "wr": _draw(_rng(cfg.seed, "wr"), (cfg.num_experts, cfg.d_model), cfg.w_std, cfg.dtype),
         "dprob": _draw(_rng(cfg.seed, "dprob"), (cfg.tokens, cfg.top_k), 1.0, "f32"),
     }
+
+
+def make_batch(cfg: Config, step: int) -> dict:
+    """The batch of train step ``step``: x [T, D] (storage dtype, N(0, x_std))
+    and the upstream gradient dy [T, D] (storage dtype, N(0, 1)) of the loss
+    L = sum_t <dy_t, y_t>.  Streams keyed by the step, distinct from the
+    layer's fixed x and dy."""
+    key = 1_000_000 + int(step)
+    return {
+        "x": _draw(_rng(cfg.seed, "x", key), (cfg.tokens, cfg.d_model), cfg.x_std, cfg.dtype),
+        "dy": _draw(_rng(cfg.seed, "dy", key), (cfg.tokens, cfg.d_model), 1.0, cfg.dtype),
+    }

@@ -151,3 +151,15 @@ def test_router_bwd_validation_returns_before_enqueue(lib):
     # NULL routing arrays
     r0 = moe._CRouting(*([0x2000] * 2 + [0] + [0x2000] * 6))
     assert lib.moe_router_bwd(ctypes.byref(cp), ctypes.byref(r0), *ok_args(), 0, None) == 1
+
+
+def test_router_fwd_and_sgd_validation_return_before_enqueue(lib):
+    fake = ctypes.c_void_p(0x1000)
+    cp = moe.Problem(**BASE).c()
+    assert lib.moe_router_fwd(ctypes.byref(cp), None, fake, fake, None) == 1
+    bad = moe.Problem(**{**BASE, "top_k": 0}).c()
+    assert lib.moe_router_fwd(ctypes.byref(bad), fake, fake, fake, None) == 2
+    assert lib.moe_sgd_step(fake, fake, 10, 0.1, fake, 7, None) == 3      # dtype
+    assert lib.moe_sgd_step(fake, fake, -1, 0.1, fake, 1, None) == 2      # n < 0
+    assert lib.moe_sgd_step(None, fake, 10, 0.1, fake, 1, None) == 1      # NULL master
+    assert lib.moe_sgd_step(None, None, 0, 0.1, None, 1, None) == 0       # nothing to do
