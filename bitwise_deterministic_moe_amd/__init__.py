@@ -17,7 +17,7 @@ __all__ = [
     "DETERMINISTIC", "ATOMIC", "Problem", "Routing", "MoeError", "MoeLibraryMissing",
     "load_library", "library_path", "moe_workspace_size", "moe_rows_cap", "moe_stage_names",
     "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad", "moe_fingerprint", "moe_sched_elems", "moe_mfma_rate",
-    "moe_router_bwd", "moe_router_fwd", "moe_sgd_step", "EXPORTED_SYMBOLS",
+    "moe_router_bwd", "moe_router_fwd", "moe_sgd_step", "moe_mx_quantize", "EXPORTED_SYMBOLS",
 ]
 
 DETERMINISTIC = 0
@@ -28,7 +28,8 @@ _TORCH_TO_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.int32: 2, torch.uin
                   torch.int64: 4, torch.float64: 5}
 EXPORTED_SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_rows_cap", "moe_sched_elems",
                     "moe_workspace_size", "moe_stage_names", "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad",
-                    "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd", "moe_sgd_step")
+                    "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd", "moe_sgd_step",
+                    "moe_mx_quantize")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -89,9 +90,10 @@ def load_library() -> ctypes.CDLL:
     lib.moe_router_bwd.argtypes = [P, R, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp]
     lib.moe_router_fwd.argtypes = [P, vp, vp, vp, vp]
     lib.moe_sgd_step.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_float, vp, ctypes.c_int, vp]
+    lib.moe_mx_quantize.argtypes = [vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, vp, vp, ctypes.c_uint64, vp]
     for f in ("moe_rows_cap", "moe_sched_elems", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob",
               "moe_bwd_wgrad", "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd",
-              "moe_sgd_step"):
+              "moe_sgd_step", "moe_mx_quantize"):
         getattr(lib, f).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -320,6 +322,24 @@ def moe_sgd_step(master: torch.Tensor, grad: torch.Tensor, lr: float, runtime: t
     code = _TORCH_TO_CODE[runtime.dtype]
     _check(lib.moe_sgd_step(_ptr(master), _ptr(grad), n, lr, _ptr(runtime), code, _stream()), "moe_sgd_step")
     return master, runtime
+
+
+def moe_mx_quantize(t: torch.Tensor, codes=None, scales=None, shuffle_seed: int = 0):
+    """MXFP8 (E4M3 codes, E8M0 scales per 32 elements of the last dimension)
+    of a contiguous float32 or bf16 tensor.  Returns (codes uint8 with t's
+    shape, scales uint8 [..., cols/32])."""
+    lib = load_library()
+    if not t.is_contiguous() or t.dim() < 1:
+        raise MoeError("moe_mx_quantize needs a contiguous tensor")
+    cols = t.shape[-1]
+    rows = t.numel() // cols if cols else 0
+    if codes is None:
+        codes = torch.empty(t.shape, dtype=torch.uint8, device=t.device)
+    if scales is None:
+        scales = torch.empty(tuple(t.shape[:-1]) + (cols // 32,), dtype=torch.uint8, device=t.device)
+    _check(lib.moe_mx_quantize(_ptr(t), _TORCH_TO_CODE[t.dtype], rows, cols, _ptr(codes), _ptr(scales),
+                               shuffle_seed & 0xFFFFFFFFFFFFFFFF, _stream()), "moe_mx_quantize")
+    return codes, scales
 
 
 def moe_fingerprint(t: torch.Tensor, dtype: Optional[str] = None, chunk_elems: int = 65536,

@@ -178,6 +178,8 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_router_bwd(const RouterParams& P, bool bf16, hipStream_t st);
 hipError_t launch_router_fwd(const void* x, const void* wr, int64_t T, int E, int D, float* logits, bool bf16,
                              uint64_t seed, hipStream_t st);
+hipError_t launch_mx_quantize(const void* in, bool bf16, int64_t rows, int64_t cols, uint8_t* codes,
+                              uint8_t* scales, uint64_t seed, hipStream_t st);
 hipError_t launch_sgd(float* master, const float* grad, int64_t n, float lr, void* runtime, bool bf16,
                       hipStream_t st);
 hipError_t launch_dprob_combine(const float* part, const int32_t* slot_row, int64_t nslots, int n_tiles,

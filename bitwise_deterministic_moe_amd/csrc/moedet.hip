@@ -698,6 +698,19 @@ MOE_API moe_status moe_sgd_step(float* master, const float* grad, int64_t n, flo
              : MOE_ERR_HIP;
 }
 
+MOE_API moe_status moe_mx_quantize(const void* in, moe_dtype dtype, int64_t rows, int64_t cols, uint8_t* codes,
+                                   uint8_t* scales, uint64_t debug_shuffle_seed, void* stream) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (rows < 0 || cols <= 0 || cols % 32 != 0 || rows > (((int64_t)1 << 40) / cols)) return MOE_ERR_SHAPE;
+  if (rows == 0) return MOE_OK;
+  if (!in || !codes || !scales) return MOE_ERR_NULL;
+  if (((uintptr_t)in & 15) || ((uintptr_t)codes & 3)) return MOE_ERR_SHAPE;
+  return launch_mx_quantize(in, dtype == MOE_BF16, rows, cols, codes, scales, debug_shuffle_seed,
+                            (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
 MOE_API moe_status moe_fingerprint(const void* data, moe_dtype dtype, int ndim, const int64_t* shape,
                                    int64_t chunk_elems, uint64_t* chunk_hashes, uint64_t* total,
                                    void* stream) {

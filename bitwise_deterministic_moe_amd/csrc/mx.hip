@@ -1,0 +1,97 @@
+// MXFP8 block quantisation: the encoded form (E4M3 values and E8M0 block
+// scales) whose bytes the pages fingerprint for low-precision runs (French
+// article, section "Méthodologie de débogage du non-déterminisme").  Format
+// from the OCP Microscaling Formats (MX) Specification v1.0:
+//   block = 32 consecutive elements of a row; shared exponent
+//   se = floor(log2(max |v|)) - 8 clamped to [-127, 127] (-127 for a block
+//   whose largest magnitude is 0 or a float32 subnormal, where the clamp
+//   applies anyway); scale byte se + 127;
+//   element code = E4M3 of v * 2^-se, to nearest with ties to even, saturated
+//   at 448, sign kept.
+// v * 2^-se is exact in float32 whenever it can round to a nonzero code
+// (|v * 2^-se| < 512, and values that underflow float32 are far below the
+// smallest E4M3 subnormal, 2^-9).  The rounding is integer arithmetic on the
+// float32 bits; the block maximum is a max of bit patterns, so every output
+// byte is exact and independent of execution order.
+#include "common.h"
+#include "kernels.h"
+
+namespace moedet {
+
+// E4M3 code of y (|y| < 512 or saturated): see the header comment.
+DEV uint32_t e4m3_rne(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  uint32_t code;
+  if (a >= 0x43e00000u) {                 // |y| >= 448
+    code = 0x7e;
+  } else if (a >= 0x3c800000u) {          // |y| >= 2^-6: normal E4M3
+    const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;   // RNE to 3 mantissa bits
+    code = r - (120u << 3);               // rebias the exponent: 127 -> 7
+  } else {                                // subnormal E4M3: m * 2^-9, m in 0..8
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  }
+  return sign | code;
+}
+
+template <typename T>
+DEV void load4(const T* p, float (&v)[4]);
+template <>
+DEV void load4(const uint16_t* p, float (&v)[4]) {
+  const u32x2_t w = *(const u32x2_t*)p;
+  v[0] = bf16_to_f32(w[0] & 0xffffu);
+  v[1] = bf16_to_f32(w[0] >> 16);
+  v[2] = bf16_to_f32(w[1] & 0xffffu);
+  v[3] = bf16_to_f32(w[1] >> 16);
+}
+template <>
+DEV void load4(const float* p, float (&v)[4]) {
+  const f32x4_t w = *(const f32x4_t*)p;
+  v[0] = w[0];
+  v[1] = w[1];
+  v[2] = w[2];
+  v[3] = w[3];
+}
+
+// Thread: 4 consecutive elements; 8 consecutive threads: one block (the
+// blocks of a row are aligned because cols is a multiple of 32).
+template <typename T>
+__global__ __launch_bounds__(256) void mx_quantize_kernel(const T* in, int64_t rows, int64_t cols, uint8_t* codes,
+                                                          uint8_t* scales, uint64_t seed) {
+  const int64_t n4 = rows * cols / 4;
+  const int64_t u = map_unit(blockIdx.x, (n4 + 255) / 256, seed);
+  const int64_t i = (u < 0 ? n4 : u * 256 + threadIdx.x);
+  const bool live = i < n4;               // uniform over each 8-thread block
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  if (live) load4(in + 4 * i, v);
+  uint32_t m = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) m = max(m, __float_as_uint(v[q]) & 0x7fffffffu);
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+  const int ef = (int)(m >> 23);
+  const int se = ef == 0 ? -127 : min(127, max(-127, ef - 127 - 8));
+  const float f = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se, exact
+  uint32_t packed = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) packed |= e4m3_rne(v[q] * f) << (8 * q);
+  if (!live) return;
+  *(uint32_t*)(codes + 4 * i) = packed;
+  if ((threadIdx.x & 7) == 0) scales[(4 * i) / 32] = (uint8_t)(se + 127);
+}
+
+hipError_t launch_mx_quantize(const void* in, bool bf16, int64_t rows, int64_t cols, uint8_t* codes,
+                              uint8_t* scales, uint64_t seed, hipStream_t st) {
+  const int64_t n4 = rows * cols / 4;
+  if (n4 == 0) return hipSuccess;
+  const int64_t grid = grid_for_units((n4 + 255) / 256);
+  if (bf16)
+    mx_quantize_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)in, rows, cols, codes, scales, seed);
+  else
+    mx_quantize_kernel<float><<<grid, 256, 0, st>>>((const float*)in, rows, cols, codes, scales, seed);
+  return hipGetLastError();
+}
+
+}  // namespace moedet

@@ -302,6 +302,29 @@ moe_status moe_router_fwd(const moe_problem* p, const void* x, const void* w_rou
 moe_status moe_sgd_step(float* master, const float* grad, int64_t n, float lr, void* runtime, moe_dtype dtype,
                         void* stream);
 
+/* MXFP8 block quantisation: the encoded values and block scales that a
+ * low-precision run fingerprints (French article, section "Méthodologie de
+ * débogage du non-déterminisme": for MXFP8 the encoded values and the scale
+ * buffers are fingerprinted).  Format: OCP Microscaling Formats (MX) v1.0,
+ * E4M3 elements with an E8M0 scale per 32 consecutive elements of a row:
+ *   se    = floor(log2(max |v| over the block)) - 8, clamped to [-127, 127]
+ *           (-127 when the block's largest magnitude is 0 or subnormal)
+ *   scale = se + 127 (E8M0 byte)
+ *   code  = E4M3(v * 2^-se): nearest, ties to the even code, saturated at
+ *           +-448 (0x7E / 0xFE), sign kept (-0 -> 0x80)
+ *   in      DEVICE [rows, cols] of dtype (MOE_F32 or MOE_BF16), 16-byte aligned,
+ *           finite values
+ *   codes   DEVICE uint8 [rows, cols], 4-byte aligned, output
+ *   scales  DEVICE uint8 [rows, cols/32], output
+ *   debug_shuffle_seed  0, or a test-only seed that shuffles the launch order
+ * Every output byte is exact (integer rounding of exact values), so the
+ * outputs are bit-identical whatever the order.  Errors: MOE_ERR_DTYPE,
+ * MOE_ERR_SHAPE (rows < 0, cols not a positive multiple of 32, more than
+ * 2^40 elements, misaligned pointers), MOE_ERR_NULL; MOE_ERR_HIP for a
+ * launch failure. */
+moe_status moe_mx_quantize(const void* in, moe_dtype dtype, int64_t rows, int64_t cols, uint8_t* codes,
+                           uint8_t* scales, uint64_t debug_shuffle_seed, void* stream);
+
 /* Diagnostic for the measurement of the percent of bf16 dense peak: the
  * attainable MFMA rate of the device.  Enqueues on `stream` one launch of
  * `blocks` workgroups of 4 waves; every wave issues iters x 8 independent

@@ -163,3 +163,13 @@ def test_router_fwd_and_sgd_validation_return_before_enqueue(lib):
     assert lib.moe_sgd_step(fake, fake, -1, 0.1, fake, 1, None) == 2      # n < 0
     assert lib.moe_sgd_step(None, fake, 10, 0.1, fake, 1, None) == 1      # NULL master
     assert lib.moe_sgd_step(None, None, 0, 0.1, None, 1, None) == 0       # nothing to do
+
+
+def test_mx_quantize_validation_returns_before_enqueue(lib):
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.moe_mx_quantize(fake, 7, 4, 64, fake, fake, 0, None) == 3          # dtype
+    assert lib.moe_mx_quantize(fake, 1, 4, 48, fake, fake, 0, None) == 2          # cols not a multiple of 32
+    assert lib.moe_mx_quantize(fake, 1, -1, 64, fake, fake, 0, None) == 2         # rows < 0
+    assert lib.moe_mx_quantize(None, 1, 4, 64, fake, fake, 0, None) == 1          # NULL input
+    assert lib.moe_mx_quantize(ctypes.c_void_p(0x1008), 1, 4, 64, fake, fake, 0, None) == 2   # misaligned
+    assert lib.moe_mx_quantize(None, 1, 0, 64, None, None, 0, None) == 0          # empty
