@@ -177,6 +177,7 @@ def main():
     value = flops / (ms_det * 1e-3) / 1e12
     mfma_peak = measured_mfma_peak()
     router = measured_router_bwd(cfg, prob, routing, x, det.dprob) if cfg.combine and el == cfg.num_experts else None
+    mxq = measured_mx_quantize(det.dh[: R])
     result = {
         "metric": "MoE grouped-GEMM bwd TFLOP/s (det mode), % bf16 peak; determinism tax vs atomic",
         "value": round(value, 2),
@@ -203,6 +204,7 @@ def main():
             "interleaved_pairs": args.steps,
         },
         "router_bwd": router,
+        "mx_quantize": mxq,
         "stages_ms_det": {k: round(v, 5) for k, v in st_det.items()},
         "stages_ms_atomic": {k: round(v, 5) for k, v in st_atom.items()},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
@@ -276,6 +278,29 @@ def measured_router_bwd(cfg, prob, routing, x, dprob, reps=20):
             "tax": round(res["det"] / res["atomic"] - 1.0, 4), "hbm_bytes": hbm,
             "achieved_GBs": round(hbm / sec / 1e9, 1), "frac_hbm": round(hbm / sec / 1e9 / HBM_PEAK_GBS, 4),
             "gather_bytes": gather, "gather_GBs": round(gather / sec / 1e9, 1)}
+
+
+def measured_mx_quantize(t, reps=20):
+    """MXFP8 quantisation (E4M3 codes + E8M0 block scales) of the step's dh,
+    average over `reps` back-to-back launches, against HBM for its bytes
+    (read the tensor, write one code byte per element and one scale byte per
+    32 elements)."""
+    import torch
+    import bitwise_deterministic_moe_amd as moe
+    codes, scales = moe.moe_mx_quantize(t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        moe.moe_mx_quantize(t, codes, scales)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    n = t.numel()
+    hbm = n * t.element_size() + n + n // 32
+    return {"tensor": f"dh {list(t.shape)} {str(t.dtype).replace('torch.', '')}", "ms": round(ms, 5),
+            "hbm_bytes": hbm, "achieved_GBs": round(hbm / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(hbm / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def measured_traffic(stage):

@@ -704,7 +704,7 @@ MOE_API moe_status moe_mx_quantize(const void* in, moe_dtype dtype, int64_t rows
   if (rows < 0 || cols <= 0 || cols % 32 != 0 || rows > (((int64_t)1 << 40) / cols)) return MOE_ERR_SHAPE;
   if (rows == 0) return MOE_OK;
   if (!in || !codes || !scales) return MOE_ERR_NULL;
-  if (((uintptr_t)in & 15) || ((uintptr_t)codes & 3)) return MOE_ERR_SHAPE;
+  if (((uintptr_t)in & 15) || ((uintptr_t)codes & 7)) return MOE_ERR_SHAPE;
   return launch_mx_quantize(in, dtype == MOE_BF16, rows, cols, codes, scales, debug_shuffle_seed,
                             (hipStream_t)stream) == hipSuccess
              ? MOE_OK

@@ -36,57 +36,63 @@ DEV uint32_t e4m3_rne(float y) {
 }
 
 template <typename T>
-DEV void load4(const T* p, float (&v)[4]);
+DEV void load8(const T* p, float (&v)[8]);
 template <>
-DEV void load4(const uint16_t* p, float (&v)[4]) {
-  const u32x2_t w = *(const u32x2_t*)p;
-  v[0] = bf16_to_f32(w[0] & 0xffffu);
-  v[1] = bf16_to_f32(w[0] >> 16);
-  v[2] = bf16_to_f32(w[1] & 0xffffu);
-  v[3] = bf16_to_f32(w[1] >> 16);
+DEV void load8(const uint16_t* p, float (&v)[8]) {
+  const u32x4_t w = *(const u32x4_t*)p;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] = bf16_to_f32(w[q] & 0xffffu);
+    v[2 * q + 1] = bf16_to_f32(w[q] >> 16);
+  }
 }
 template <>
-DEV void load4(const float* p, float (&v)[4]) {
-  const f32x4_t w = *(const f32x4_t*)p;
-  v[0] = w[0];
-  v[1] = w[1];
-  v[2] = w[2];
-  v[3] = w[3];
+DEV void load8(const float* p, float (&v)[8]) {
+  const f32x4_t a = *(const f32x4_t*)p, b = *(const f32x4_t*)(p + 4);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[q] = a[q];
+    v[4 + q] = b[q];
+  }
 }
 
-// Thread: 4 consecutive elements; 8 consecutive threads: one block (the
+// Thread: 8 consecutive elements; 4 consecutive threads: one block (the
 // blocks of a row are aligned because cols is a multiple of 32).
 template <typename T>
 __global__ __launch_bounds__(256) void mx_quantize_kernel(const T* in, int64_t rows, int64_t cols, uint8_t* codes,
                                                           uint8_t* scales, uint64_t seed) {
-  const int64_t n4 = rows * cols / 4;
-  const int64_t u = map_unit(blockIdx.x, (n4 + 255) / 256, seed);
-  const int64_t i = (u < 0 ? n4 : u * 256 + threadIdx.x);
-  const bool live = i < n4;               // uniform over each 8-thread block
-  float v[4] = {0.f, 0.f, 0.f, 0.f};
-  if (live) load4(in + 4 * i, v);
+  const int64_t n8 = rows * cols / 8;
+  const int64_t u = map_unit(blockIdx.x, (n8 + 255) / 256, seed);
+  const int64_t i = (u < 0 ? n8 : u * 256 + threadIdx.x);
+  const bool live = i < n8;               // uniform over each 4-thread block
+  float v[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) v[q] = 0.f;
+  if (live) load8(in + 8 * i, v);
   uint32_t m = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) m = max(m, __float_as_uint(v[q]) & 0x7fffffffu);
+  for (int q = 0; q < 8; ++q) m = max(m, __float_as_uint(v[q]) & 0x7fffffffu);
   m = max(m, (uint32_t)__shfl_xor((int)m, 1));
   m = max(m, (uint32_t)__shfl_xor((int)m, 2));
-  m = max(m, (uint32_t)__shfl_xor((int)m, 4));
   const int ef = (int)(m >> 23);
   const int se = ef == 0 ? -127 : min(127, max(-127, ef - 127 - 8));
   const float f = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se, exact
-  uint32_t packed = 0;
+  uint32_t lo = 0, hi = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) packed |= e4m3_rne(v[q] * f) << (8 * q);
+  for (int q = 0; q < 4; ++q) {
+    lo |= e4m3_rne(v[q] * f) << (8 * q);
+    hi |= e4m3_rne(v[4 + q] * f) << (8 * q);
+  }
   if (!live) return;
-  *(uint32_t*)(codes + 4 * i) = packed;
-  if ((threadIdx.x & 7) == 0) scales[(4 * i) / 32] = (uint8_t)(se + 127);
+  *(u32x2_t*)(codes + 8 * i) = u32x2_t{lo, hi};
+  if ((threadIdx.x & 3) == 0) scales[(8 * i) / 32] = (uint8_t)(se + 127);
 }
 
 hipError_t launch_mx_quantize(const void* in, bool bf16, int64_t rows, int64_t cols, uint8_t* codes,
                               uint8_t* scales, uint64_t seed, hipStream_t st) {
-  const int64_t n4 = rows * cols / 4;
-  if (n4 == 0) return hipSuccess;
-  const int64_t grid = grid_for_units((n4 + 255) / 256);
+  const int64_t n8 = rows * cols / 8;
+  if (n8 == 0) return hipSuccess;
+  const int64_t grid = grid_for_units((n8 + 255) / 256);
   if (bf16)
     mx_quantize_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)in, rows, cols, codes, scales, seed);
   else

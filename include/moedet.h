@@ -314,7 +314,7 @@ moe_status moe_sgd_step(float* master, const float* grad, int64_t n, float lr, v
  *           +-448 (0x7E / 0xFE), sign kept (-0 -> 0x80)
  *   in      DEVICE [rows, cols] of dtype (MOE_F32 or MOE_BF16), 16-byte aligned,
  *           finite values
- *   codes   DEVICE uint8 [rows, cols], 4-byte aligned, output
+ *   codes   DEVICE uint8 [rows, cols], 8-byte aligned, output
  *   scales  DEVICE uint8 [rows, cols/32], output
  *   debug_shuffle_seed  0, or a test-only seed that shuffles the launch order
  * Every output byte is exact (integer rounding of exact values), so the
