@@ -17,7 +17,8 @@ __all__ = [
     "DETERMINISTIC", "ATOMIC", "Problem", "Routing", "MoeError", "MoeLibraryMissing",
     "load_library", "library_path", "moe_workspace_size", "moe_rows_cap", "moe_stage_names",
     "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad", "moe_fingerprint", "moe_sched_elems", "moe_mfma_rate",
-    "moe_router_bwd", "moe_router_fwd", "moe_sgd_step", "moe_mx_quantize", "EXPORTED_SYMBOLS",
+    "moe_router_bwd", "moe_router_fwd", "moe_sgd_step", "moe_mx_quantize", "moe_mx_dgrad_fc1",
+    "EXPORTED_SYMBOLS",
 ]
 
 DETERMINISTIC = 0
@@ -29,7 +30,7 @@ _TORCH_TO_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.int32: 2, torch.uin
 EXPORTED_SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_rows_cap", "moe_sched_elems",
                     "moe_workspace_size", "moe_stage_names", "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad",
                     "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd", "moe_sgd_step",
-                    "moe_mx_quantize")
+                    "moe_mx_quantize", "moe_mx_dgrad_fc1")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -91,9 +92,10 @@ def load_library() -> ctypes.CDLL:
     lib.moe_router_fwd.argtypes = [P, vp, vp, vp, vp]
     lib.moe_sgd_step.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_float, vp, ctypes.c_int, vp]
     lib.moe_mx_quantize.argtypes = [vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, vp, vp, ctypes.c_uint64, vp]
+    lib.moe_mx_dgrad_fc1.argtypes = [P, R, vp, vp, vp, vp, vp, vp]
     for f in ("moe_rows_cap", "moe_sched_elems", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob",
               "moe_bwd_wgrad", "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd",
-              "moe_sgd_step", "moe_mx_quantize"):
+              "moe_sgd_step", "moe_mx_quantize", "moe_mx_dgrad_fc1"):
         getattr(lib, f).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -340,6 +342,19 @@ def moe_mx_quantize(t: torch.Tensor, codes=None, scales=None, shuffle_seed: int 
     _check(lib.moe_mx_quantize(_ptr(t), _TORCH_TO_CODE[t.dtype], rows, cols, _ptr(codes), _ptr(scales),
                                shuffle_seed & 0xFFFFFFFFFFFFFFFF, _stream()), "moe_mx_quantize")
     return codes, scales
+
+
+def moe_mx_dgrad_fc1(prob: Problem, routing: Routing, dh_mx, w1_mx, dx_rows=None):
+    """MXFP8 fc1 data gradient: dx_rows [rows_cap, D] bf16 from (codes, scales)
+    of dh [rows_cap, F] and of W1 [num_local, D, F] (moe_mx_quantize outputs)."""
+    lib = load_library()
+    (dc, ds), (wc, wsc) = dh_mx, w1_mx
+    if dx_rows is None:
+        dx_rows = torch.empty((prob.rows_cap, prob.d_model), dtype=torch.bfloat16, device=dc.device)
+    cp, cr = prob.c(), routing.c()
+    _check(lib.moe_mx_dgrad_fc1(ctypes.byref(cp), ctypes.byref(cr), _ptr(dc), _ptr(ds), _ptr(wc), _ptr(wsc),
+                                _ptr(dx_rows), _stream()), "moe_mx_dgrad_fc1")
+    return dx_rows
 
 
 def moe_fingerprint(t: torch.Tensor, dtype: Optional[str] = None, chunk_elems: int = 65536,

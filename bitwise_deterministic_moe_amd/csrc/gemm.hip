@@ -26,6 +26,8 @@
 //  * wgrad split-K: chunk partials go to the output (chunk 0) and to
 //    workspace slots (chunks 1..S-1) and a later pass adds them in chunk
 //    order; the atomic mode adds all chunks atomically into a zeroed dW.
+#include <type_traits>
+
 #include "gemm_bf16.h"
 #include "gemm_f32.h"
 #include "kernels.h"
@@ -692,6 +694,150 @@ __global__ __launch_bounds__(256) void wgrad_pair_bf16_kernel(WgradParams P1, Wg
     wgrad_pair_unit<true, false>(P1, L, tiles1, lds, s_rowoff);
 }
 
+// ================================================================ MXFP8
+// Grouped row GEMM on MXFP8 operands (OCP MX v1.0: E4M3 codes, an E8M0 scale
+// per 32 consecutive k): C[r, n] = sum_k A[r, k] B_g[n, k] with both operands
+// K-contiguous (rows of codes, scales [rows][K/32]), through
+// v_mfma_scale_f32_32x32x64_f8f6f4; output bf16 rows.  A K slice is 64
+// codes, so a tile row of a slice is 64 bytes and the DMA loaders and the LDS
+// layout of the bf16 K-contiguous tiles carry over unchanged.  Lane layout of
+// the scaled MFMA (gfx950): lane l = 32h + i holds, for row i, the codes of k
+// = 16h .. 16h+15 in bytes 0..15 and k = 32+16h .. 32+16h+15 in bytes
+// 16..31, i.e. chunks h and 2+h of the row; the scale register of lane
+// 32kb + i carries the E8M0 byte of row i, k-block kb.  Each tile's scales
+// (256 rows x K/32 bytes per operand) are staged in LDS before the main loop.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t_ __attribute__((ext_vector_type(4)));
+
+struct MxFrags {
+  i32x8_t a[4], b[4];
+  int sa[4], sb[4];
+};
+
+DEV void mx_read_block(const uint8_t* op, const uint8_t* scales, int nkb, int kb, int row, int h, i32x8_t& f,
+                       int& sc) {
+  const int sw = bf::kc_swz(row);
+  const i32x4_t_ lo = *(const i32x4_t_*)(op + row * 64 + ((h ^ sw) << 4));
+  const i32x4_t_ hi = *(const i32x4_t_*)(op + row * 64 + (((2 + h) ^ sw) << 4));
+  f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  sc = scales[row * nkb + kb];
+}
+
+__global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sa[256 * (kMxMaxK / 32)];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sb[256 * (kMxMaxK / 32)];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t ring = bf::lds_base(lds);
+  const int wm = wave >> 1, wn = wave & 1;
+  RowTile t;
+  if (row_tile<bf::BM, bf::BN>(P, t) != kTileGemm) return;
+  const int nkb = P.K / 32;
+  const int64_t sg = (int64_t)t.g * P.b_sgstride;
+  // the tile's scales (rows past the tile's valid rows read row 0 of the
+  // tile: their codes load as zeros)
+  for (int idx = tid; idx < 256 * (nkb / 4); idx += 256) {
+    const int r = idx / (nkb / 4), q = idx % (nkb / 4);
+    const int ra = r < t.mvalid ? r : 0;
+    ((uint32_t*)s_sa)[idx] = ((const uint32_t*)(P.a_scales + (t.off + t.m0 + ra) * nkb))[q];
+    ((uint32_t*)s_sb)[idx] = ((const uint32_t*)(P.b_scales + sg + (int64_t)(t.n0 + r) * nkb))[q];
+  }
+  bf::KcOperand oa, ob;
+  oa.init(P.a, P.a_bytes, wave, lane, [&](int r) -> uint32_t {
+    return r < t.mvalid ? (uint32_t)((t.off + t.m0 + r) * P.lda) : bf::kOOB;
+  });
+  ob.init((const uint8_t*)P.b + (int64_t)t.g * P.b_gstride, P.b_bytes, wave, lane,
+          [&](int r) -> uint32_t { return (uint32_t)((t.n0 + r) * P.ldb); });
+  const int nsteps = P.K / 64;
+  // slice s: 64 codes = 64 bytes per row, the byte offset of a bf16 slice of 32
+  auto issue = [&](int s, uint32_t st, int i) __attribute__((always_inline)) {
+    if (i < bf::LOADS)
+      oa.issue1(st, wave, s * bf::BK, s < nsteps, i);
+    else
+      ob.issue1(st + bf::OPER * 2, wave, s * bf::BK, s < nsteps, i - bf::LOADS);
+  };
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  const int h = lane >> 5, r32 = lane & 31;
+  auto slot = [&](int s) { return (const uint8_t*)(lds + (s & 3) * bf::STAGE); };
+  auto slot_addr = [&](int s) { return ring + (uint32_t)(s & 3) * (bf::STAGE * 2); };
+  auto read = [&](MxFrags& f, int s, auto G) __attribute__((always_inline)) {   // group G: A block G (G < 4) or B block G-4
+    constexpr int g = decltype(G)::value;
+    const uint8_t* st = slot(s);
+    if constexpr (g < 4)
+      mx_read_block(st, s_sa, nkb, 2 * s + h, wm * 128 + g * 32 + r32, h, f.a[g], f.sa[g]);
+    else
+      mx_read_block(st + bf::OPER * 2, s_sb, nkb, 2 * s + h, wn * 128 + (g - 4) * 32 + r32, h, f.b[g - 4],
+                    f.sb[g - 4]);
+  };
+  auto mma = [&](const MxFrags& f, auto MB) __attribute__((always_inline)) {
+    constexpr int mb = decltype(MB)::value;
+    acc[mb][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[0], f.a[mb], acc[mb][0], 0, 0, 0, f.sb[0], 0, f.sa[mb]);
+    acc[mb][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[1], f.a[mb], acc[mb][1], 0, 0, 0, f.sb[1], 0, f.sa[mb]);
+    acc[mb][2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[2], f.a[mb], acc[mb][2], 0, 0, 0, f.sb[2], 0, f.sa[mb]);
+    acc[mb][3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[3], f.a[mb], acc[mb][3], 0, 0, 0, f.sb[3], 0, f.sa[mb]);
+  };
+  // prologue: slices 0..2 in flight
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) issue(s, slot_addr(s), i);
+  __syncthreads();   // the scale stores to LDS are visible
+  // step s: wait until this wave's loads of slice s landed (slices s+1, s+2
+  // stay in flight) and every wave is done with slice s-1, whose slot takes
+  // slice s+3; then the B blocks of slice s are read, and each A block is read
+  // and multiplied, with the loads of slice s+3 issued in between
+  MxFrags f;
+#pragma unroll 1
+  for (int s = 0; s < nsteps; ++s) {
+    asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    read(f, s, std::integral_constant<int, 4>{});
+    read(f, s, std::integral_constant<int, 5>{});
+    issue(s + 3, slot_addr(s + 3), 0);
+    issue(s + 3, slot_addr(s + 3), 1);
+    read(f, s, std::integral_constant<int, 6>{});
+    read(f, s, std::integral_constant<int, 7>{});
+    issue(s + 3, slot_addr(s + 3), 2);
+    issue(s + 3, slot_addr(s + 3), 3);
+    read(f, s, std::integral_constant<int, 0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    read(f, s, std::integral_constant<int, 1>{});
+    issue(s + 3, slot_addr(s + 3), 4);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f, std::integral_constant<int, 0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    read(f, s, std::integral_constant<int, 2>{});
+    issue(s + 3, slot_addr(s + 3), 5);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f, std::integral_constant<int, 1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    read(f, s, std::integral_constant<int, 3>{});
+    issue(s + 3, slot_addr(s + 3), 6);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f, std::integral_constant<int, 2>{});
+    __builtin_amdgcn_sched_barrier(0);
+    issue(s + 3, slot_addr(s + 3), 7);
+    mma(f, std::integral_constant<int, 3>{});
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  bf::block_barrier();
+  float* stage = (float*)lds;
+  NoPre none;
+  NoPre::Data nd[2];
+  const __amdgpu_buffer_rsrc_t rc = buf(P.c);
+  staged_epilogue<128>(stage, acc, wm, wn, lane, tid, t.mvalid, none, nd, false, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
+    if (m >= t.mvalid) return;  // uniform per wave
+    const uint32_t grow = (uint32_t)(t.off + t.m0 + m);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rc,
+                                          (grow * (uint32_t)P.ldc + t.n0 + col) * 2u, 0, kEpiNT);
+  });
+}
+
 // ================================================================= fp32
 template <bool B_MNC, int EPI>
 __global__ __launch_bounds__(256) void rowgemm_f32_kernel(RowGemmParams P) {
@@ -904,6 +1050,12 @@ hipError_t launch_wgrad(const WgradParams& P, int which, bool bf16, int64_t grid
 hipError_t launch_wgrad_pair(const WgradParams& P1, const WgradParams& P2, int ncu, int64_t grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
   wgrad_pair_bf16_kernel<<<grid, 256, 0, st>>>(P1, P2, ncu);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_rowgemm(const RowGemmParams& P, int64_t grid, hipStream_t st) {
+  if (grid <= 0) return hipSuccess;
+  mx_rowgemm_kernel<<<grid, 256, 0, st>>>(P);
   return hipGetLastError();
 }
 

@@ -61,7 +61,12 @@ struct RowGemmParams {
   int side_units;
   int64_t gemm_grid;
   uint64_t seed;
+  // MXFP8 row GEMM: E8M0 scales, one byte per 32 k, [rows][K/32]
+  const uint8_t* a_scales;
+  const uint8_t* b_scales;
+  int64_t b_sgstride;     // scale bytes between consecutive experts' B
 };
+constexpr int kMxMaxK = 2048;  // K bound of the MXFP8 row GEMM (its scales are staged in LDS)
 
 constexpr int kSideSlots = 1024;  // flat slots per side unit
 
@@ -178,6 +183,7 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_router_bwd(const RouterParams& P, bool bf16, hipStream_t st);
 hipError_t launch_router_fwd(const void* x, const void* wr, int64_t T, int E, int D, float* logits, bool bf16,
                              uint64_t seed, hipStream_t st);
+hipError_t launch_mx_rowgemm(const RowGemmParams& P, int64_t grid, hipStream_t st);
 hipError_t launch_mx_quantize(const void* in, bool bf16, int64_t rows, int64_t cols, uint8_t* codes,
                               uint8_t* scales, uint64_t seed, hipStream_t st);
 hipError_t launch_sgd(float* master, const float* grad, int64_t n, float lr, void* runtime, bool bf16,

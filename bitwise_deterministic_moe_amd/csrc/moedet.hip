@@ -711,6 +711,42 @@ MOE_API moe_status moe_mx_quantize(const void* in, moe_dtype dtype, int64_t rows
              : MOE_ERR_HIP;
 }
 
+MOE_API moe_status moe_mx_dgrad_fc1(const moe_problem* p, const moe_routing* routing, const uint8_t* dh_codes,
+                                    const uint8_t* dh_scales, const uint8_t* w1_codes, const uint8_t* w1_scales,
+                                    void* dx_rows, void* stream) {
+  Plan pl;
+  moe_status s = validate(p, &pl);
+  if (s != MOE_OK) return s;
+  if (!pl.bf16) return MOE_ERR_DTYPE;
+  if (pl.F > kMxMaxK || pl.F % 128) return MOE_ERR_SHAPE;
+  if (!routing || !routing->counts || !routing->offsets || !routing->sched) return MOE_ERR_NULL;
+  if (pl.rows_cap > 0 && (!dh_codes || !dh_scales || !w1_codes || !w1_scales || !dx_rows)) return MOE_ERR_NULL;
+  RowGemmParams G{};
+  G.counts = routing->counts;
+  G.offsets = routing->offsets;
+  G.groups = pl.el;
+  G.N = pl.D;
+  G.K = pl.F;
+  G.a = dh_codes;
+  G.lda = pl.F;  // bytes per row of codes
+  G.a_bytes = (uint32_t)(pl.rows_cap * pl.F);
+  G.b = w1_codes;
+  G.b_gstride = (int64_t)pl.D * pl.F;
+  G.ldb = pl.F;
+  G.b_bytes = (uint32_t)((int64_t)pl.D * pl.F);
+  G.c = dx_rows;
+  G.ldc = pl.D;
+  G.ncu = device_cu_count();
+  G.sched = routing->sched;
+  G.list_hdr = 0;
+  G.list_at = kSchedHeader;
+  G.a_scales = dh_scales;
+  G.b_scales = w1_scales;
+  G.b_sgstride = (int64_t)pl.D * (pl.F / 32);
+  G.seed = p->debug_shuffle_seed;
+  return launch_mx_rowgemm(G, rowgemm_grid(pl, pl.D), (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 MOE_API moe_status moe_fingerprint(const void* data, moe_dtype dtype, int ndim, const int64_t* shape,
                                    int64_t chunk_elems, uint64_t* chunk_hashes, uint64_t* total,
                                    void* stream) {

@@ -276,6 +276,27 @@ moe_status moe_router_bwd(const moe_problem* p, const moe_routing* routing, cons
                           const void* x, const void* w_router, float* dlogits, float* dw_router,
                           void* dx_router, moe_mode mode, void* stream);
 
+/* MXFP8 grouped GEMM, the low-precision variant of the fc1 data gradient:
+ *   dx_rows[r, :] = dequant(dh)[r, :] . dequant(W1_e)^T   (r a routed row of
+ *                   local expert e; dequant = E4M3 code * E8M0 block scale)
+ * through gfx950's v_mfma_scale_f32_32x32x64_f8f6f4, float32 accumulation
+ * in a fixed k order (64 k per MFMA, slices ascending), one rounding to bf16.
+ * The pages name MXFP8 runs and fingerprint their encoded values and scale
+ * buffers (French article, section "Méthodologie de débogage du
+ * non-déterminisme"); the format is OCP MX v1.0 (moe_mx_quantize).
+ *   dh_codes / dh_scales  DEVICE uint8 [rows_cap, F] / [rows_cap, F/32]
+ *                         (moe_mx_quantize of dh)
+ *   w1_codes / w1_scales  DEVICE uint8 [num_local, D, F] / [num_local, D, F/32]
+ *                         (moe_mx_quantize of W1 viewed as [num_local*D, F])
+ *   dx_rows               DEVICE bf16 [rows_cap, D] output; rows < R written
+ * routing: counts, offsets and sched as written by moe_fwd.  The problem must
+ * be bf16 with F a multiple of 128 and at most 2048 (the tile's scales are
+ * staged in LDS).  Errors: MOE_ERR_DTYPE, MOE_ERR_SHAPE, MOE_ERR_NULL before
+ * anything is enqueued; MOE_ERR_HIP for a launch failure. */
+moe_status moe_mx_dgrad_fc1(const moe_problem* p, const moe_routing* routing, const uint8_t* dh_codes,
+                            const uint8_t* dh_scales, const uint8_t* w1_codes, const uint8_t* w1_scales,
+                            void* dx_rows, void* stream);
+
 /* Router forward for a train step of the layer: logits[t,e] = sum over d
  * ascending of x[t,d] * w_router[e,d] in float32 fused multiply-adds, one
  * thread per logit (no reduction across threads, so bit-exact).  The router

@@ -14,4 +14,4 @@ from .fingerprint import fingerprint, mix64, DTYPE_CODE  # noqa: F401
 from .router import (  # noqa: F401
     router_logits, router_probs, router_dlogits, router_backward, router_loss,
 )
-from .mx import e4m3_decode, e4m3_encode, e8m0_decode, mx_quantize, mx_dequantize  # noqa: F401,E402
+from .mx import e4m3_decode, e4m3_encode, e8m0_decode, mx_quantize, mx_quantize_fast, mx_dequantize, mx_grouped_rows  # noqa: F401,E402

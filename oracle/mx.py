@@ -31,6 +31,7 @@ BLOCK = 32
 
 def e4m3_decode(code: int) -> float:
     """Value of an E4M3 code (NaN for S.1111.111)."""
+    code = int(code)
     s = -1.0 if code & 0x80 else 1.0
     e = (code >> 3) & 0xF
     m = code & 0x7
@@ -93,12 +94,52 @@ def mx_quantize(rows: np.ndarray):
     return codes, scales
 
 
+_DECODE = np.array([e4m3_decode(c) for c in range(256)])
+_POS_F64 = np.array([v for v, _ in _POS])            # increasing magnitudes of codes 0..126
+_POS_CODE = np.array([c for _, c in _POS], np.uint8)
+
+
+def mx_quantize_fast(rows: np.ndarray):
+    """mx_quantize in vectorised float64 (same definition, for large tensors;
+    pinned against mx_quantize).  Exactness: v * 2^-se is a power-of-two scaling
+    of a float32 value (exact in float64), and the two candidate magnitudes
+    around it lie within a factor of two of it, so their distances to it are
+    exact float64 differences."""
+    rows = np.asarray(rows, np.float64)
+    n, k = rows.shape
+    assert k % BLOCK == 0
+    blocks = rows.reshape(n, k // BLOCK, BLOCK)
+    amax = np.abs(blocks).max(axis=2)
+    _, ex = np.frexp(amax)                           # amax = m * 2^ex, m in [0.5, 1)
+    se = np.where(amax > 0, np.clip(ex - 1 - 8, -127, 127), -127).astype(np.int64)
+    y = np.ldexp(np.abs(blocks), -se[:, :, None])
+    i = np.searchsorted(_POS_F64, y, side="left")    # _POS_F64[i-1] < y <= _POS_F64[i]
+    lo = np.clip(i - 1, 0, len(_POS_F64) - 1)
+    hi = np.clip(i, 0, len(_POS_F64) - 1)
+    dlo, dhi = y - _POS_F64[lo], _POS_F64[hi] - y
+    clo, chi = _POS_CODE[lo], _POS_CODE[hi]
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (chi % 2 == 0) & (clo % 2 == 1))
+    code = np.where(pick_hi, chi, clo)
+    code = np.where(y >= E4M3_MAX, np.uint8(0x7E), code)
+    code = code | np.where(np.signbit(blocks), np.uint8(0x80), np.uint8(0))
+    return code.reshape(n, k).astype(np.uint8), (se + 127).astype(np.uint8)
+
+
 def mx_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """Values X * P_i as float64."""
+    """Values X * P_i as float64: the code's value times its block's scale
+    (codes [..., k], scales [..., k/32])."""
     codes = np.asarray(codes, np.uint8)
-    n, k = codes.shape
-    out = np.zeros((n, k))
-    for i in range(n):
-        for j in range(k):
-            out[i, j] = e4m3_decode(int(codes[i, j])) * e8m0_decode(int(scales[i, j // BLOCK]))
+    x = np.exp2(np.asarray(scales, np.float64) - 127.0)
+    return _DECODE[codes] * np.repeat(x, BLOCK, axis=-1)
+
+
+def mx_grouped_rows(a_codes, a_scales, b_codes, b_scales, offsets) -> np.ndarray:
+    """out[r] = dequant(A)[r] . dequant(B_e)^T for the rows r of group e
+    (offsets[e] <= r < offsets[e+1]); A [rows, K], B [groups, N, K]."""
+    A = mx_dequantize(a_codes, a_scales)
+    out = np.zeros((A.shape[0], b_codes.shape[1]))
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            out[lo:hi] = A[lo:hi] @ mx_dequantize(b_codes[e], b_scales[e]).T
     return out

@@ -173,3 +173,14 @@ def test_mx_quantize_validation_returns_before_enqueue(lib):
     assert lib.moe_mx_quantize(None, 1, 4, 64, fake, fake, 0, None) == 1          # NULL input
     assert lib.moe_mx_quantize(ctypes.c_void_p(0x1008), 1, 4, 64, fake, fake, 0, None) == 2   # misaligned
     assert lib.moe_mx_quantize(None, 1, 0, 64, None, None, 0, None) == 0          # empty
+
+
+def test_mx_dgrad_fc1_validation_returns_before_enqueue(lib):
+    fake = ctypes.c_void_p(0x1000)
+    r = moe._CRouting(*([0x2000] * 9))
+    big = moe.Problem(**{**BASE, "d_ffn": 4096}).c()
+    assert lib.moe_mx_dgrad_fc1(ctypes.byref(big), ctypes.byref(r), fake, fake, fake, fake, fake, None) == 2
+    f32 = moe.Problem(**{**BASE, "dtype": "f32"}).c()
+    assert lib.moe_mx_dgrad_fc1(ctypes.byref(f32), ctypes.byref(r), fake, fake, fake, fake, fake, None) == 3
+    cp = moe.Problem(**BASE).c()
+    assert lib.moe_mx_dgrad_fc1(ctypes.byref(cp), ctypes.byref(r), None, fake, fake, fake, fake, None) == 1

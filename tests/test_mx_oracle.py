@@ -125,3 +125,49 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     mid = (Fraction(v0) + Fraction(v1)) / 2
     away = max(c0, c1)                                  # ties away from zero
     assert mx.e4m3_encode(mid, False) != away or away % 2 == 0
+
+
+def test_vectorised_dequantise_equals_the_definition():
+    codes = np.arange(256, dtype=np.uint8).reshape(8, 32)
+    scales = np.array([[0], [1], [100], [126], [127], [128], [200], [254]], np.uint8)
+    got = mx.mx_dequantize(codes, scales)
+    for i in range(8):
+        for j in range(32):
+            want = mx.e4m3_decode(int(codes[i, j])) * mx.e8m0_decode(int(scales[i, 0]))
+            assert (np.isnan(want) and np.isnan(got[i, j])) or got[i, j] == want
+
+
+def test_grouped_rows_against_a_triple_loop():
+    rng = np.random.default_rng(2)
+    K, N = 64, 3
+    a = rng.standard_normal((5, K))
+    b = rng.standard_normal((2, N, K))
+    ac, asc = mx.mx_quantize(a)
+    bc, bsc = mx.mx_quantize(b.reshape(-1, K))
+    bc, bsc = bc.reshape(2, N, K), bsc.reshape(2, N, K // 32)
+    offsets = [0, 2, 5]
+    out = mx.mx_grouped_rows(ac, asc, bc, bsc, offsets)
+    for r in range(5):
+        e = 0 if r < 2 else 1
+        for n in range(N):
+            s = 0.0
+            for k in range(K):
+                s += (mx.e4m3_decode(int(ac[r, k])) * mx.e8m0_decode(int(asc[r, k // 32]))
+                      * mx.e4m3_decode(int(bc[e, n, k])) * mx.e8m0_decode(int(bsc[e, n, k // 32])))
+            assert abs(out[r, n] - s) <= 1e-12 * max(1.0, abs(s))
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_vectorised_quantise_equals_the_exact_one(seed):
+    rng = np.random.default_rng(100 + seed)
+    rows = (rng.standard_normal((16, 128)) * np.exp2(rng.uniform(-40, 40, (16, 1)))).astype(np.float32)
+    pos = sorted(mx.e4m3_decode(c) for c in range(0x7F))
+    mids = np.array([(u + v) / 2 for u, v in zip(pos, pos[1:])], np.float32)
+    rows[0, :32] = mids[-32:] * np.float32(2.0 ** -8)
+    rows[1, :32] = mids[:32] * np.float32(2.0 ** -8)
+    rows[2, :32] = -0.0
+    rows[3, :32] = np.float32(1.96875)
+    rows[4, :32] = np.float32(2.0 ** -149)
+    a, b = mx.mx_quantize(rows.astype(np.float64)), mx.mx_quantize_fast(rows.astype(np.float64))
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
