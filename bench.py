@@ -178,6 +178,7 @@ def main():
     mfma_peak = measured_mfma_peak()
     router = measured_router_bwd(cfg, prob, routing, x, det.dprob) if cfg.combine and el == cfg.num_experts else None
     mxq = measured_mx_quantize(det.dh[: R])
+    mxg = measured_mx_dgrad_fc1(cfg, prob, routing, det.dh, w1, st_det.get("fc1_dgrad_dprob_combine"))
     result = {
         "metric": "MoE grouped-GEMM bwd TFLOP/s (det mode), % bf16 peak; determinism tax vs atomic",
         "value": round(value, 2),
@@ -205,6 +206,7 @@ def main():
         },
         "router_bwd": router,
         "mx_quantize": mxq,
+        "mx_dgrad_fc1": mxg,
         "stages_ms_det": {k: round(v, 5) for k, v in st_det.items()},
         "stages_ms_atomic": {k: round(v, 5) for k, v in st_atom.items()},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
@@ -301,6 +303,37 @@ def measured_mx_quantize(t, reps=20):
     return {"tensor": f"dh {list(t.shape)} {str(t.dtype).replace('torch.', '')}", "ms": round(ms, 5),
             "hbm_bytes": hbm, "achieved_GBs": round(hbm / (ms * 1e-3) / 1e9, 1),
             "frac_hbm": round(hbm / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+FP8_PEAK_TFLOPS = 5033.2   # MI355X dense fp8 MFMA, vendor figure
+
+
+def measured_mx_dgrad_fc1(cfg, prob, routing, dh, w1, bf16_ms, reps=20):
+    """The MXFP8 variant of the fc1 data gradient (dx_rows = dh W1^T on E4M3
+    codes with E8M0 block scales) on the step's dh and W1, quantised once
+    outside the timed region; average of `reps` launches, against the dense
+    fp8 peak, beside the bf16 fc1 dgrad stage of the same step."""
+    import torch
+    import bitwise_deterministic_moe_amd as moe
+    if cfg.dtype != "bf16" or cfg.d_ffn > 2048:
+        return None
+    D, F, el = cfg.d_model, cfg.d_ffn, cfg.num_local
+    dmx = moe.moe_mx_quantize(dh)
+    wq = moe.moe_mx_quantize(w1.reshape(el * D, F))
+    wmx = (wq[0].reshape(el, D, F), wq[1].reshape(el, D, F // 32))
+    out = moe.moe_mx_dgrad_fc1(prob, routing, dmx, wmx)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        moe.moe_mx_dgrad_fc1(prob, routing, dmx, wmx, out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 2.0 * routing.rows * D * F
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 5), "tflops": round(tf, 1), "peak_fp8": FP8_PEAK_TFLOPS,
+            "frac": round(tf / FP8_PEAK_TFLOPS, 4), "bf16_stage_ms": None if bf16_ms is None else round(bf16_ms, 5)}
 
 
 def measured_traffic(stage):
