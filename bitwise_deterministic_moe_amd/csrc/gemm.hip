@@ -720,7 +720,7 @@ DEV void mx_read_block(const uint8_t* op, const uint8_t* scales, int nkb, int kb
   const i32x4_t_ lo = *(const i32x4_t_*)(op + row * 64 + ((h ^ sw) << 4));
   const i32x4_t_ hi = *(const i32x4_t_*)(op + row * 64 + (((2 + h) ^ sw) << 4));
   f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  sc = scales[row * nkb + kb];
+  sc = scales[row * nkb + (kb < nkb ? kb : nkb - 1)];
 }
 
 __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
@@ -782,48 +782,55 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
     acc[mb][2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[2], f.a[mb], acc[mb][2], 0, 0, 0, f.sb[2], 0, f.sa[mb]);
     acc[mb][3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[3], f.a[mb], acc[mb][3], 0, 0, 0, f.sb[3], 0, f.sa[mb]);
   };
-  // prologue: slices 0..2 in flight
+  // prologue: slices 0..2 in flight, slice 0 landed, its B blocks read
 #pragma unroll
   for (int s = 0; s < 3; ++s)
 #pragma unroll
     for (int i = 0; i < 8; ++i) issue(s, slot_addr(s), i);
-  __syncthreads();   // the scale stores to LDS are visible
-  // step s: wait until this wave's loads of slice s landed (slices s+1, s+2
-  // stay in flight) and every wave is done with slice s-1, whose slot takes
-  // slice s+3; then the B blocks of slice s are read, and each A block is read
-  // and multiplied, with the loads of slice s+3 issued in between
-  MxFrags f;
+  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  __syncthreads();   // slice 0 and the scale stores to LDS are visible
+  MxFrags f, fb;     // f: A blocks of slice s and B blocks in use; fb: B blocks of slice s+1
+  read(f, 0, std::integral_constant<int, 4>{});
+  read(f, 0, std::integral_constant<int, 5>{});
+  read(f, 0, std::integral_constant<int, 6>{});
+  read(f, 0, std::integral_constant<int, 7>{});
+  // step s: slice s+1 landed and every wave is done with slice s-1, whose slot
+  // takes slice s+3.  The A blocks of slice s are read one ahead of their
+  // MFMAs; the B blocks of slice s+1 (past the last slice: zero codes and a
+  // clamped scale index, never multiplied) are read in between.
 #pragma unroll 1
   for (int s = 0; s < nsteps; ++s) {
-    asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    read(f, s, std::integral_constant<int, 4>{});
-    read(f, s, std::integral_constant<int, 5>{});
-    issue(s + 3, slot_addr(s + 3), 0);
-    issue(s + 3, slot_addr(s + 3), 1);
-    read(f, s, std::integral_constant<int, 6>{});
-    read(f, s, std::integral_constant<int, 7>{});
-    issue(s + 3, slot_addr(s + 3), 2);
-    issue(s + 3, slot_addr(s + 3), 3);
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     read(f, s, std::integral_constant<int, 0>{});
-    __builtin_amdgcn_sched_barrier(0);
+    issue(s + 3, slot_addr(s + 3), 0);
     read(f, s, std::integral_constant<int, 1>{});
-    issue(s + 3, slot_addr(s + 3), 4);
+    issue(s + 3, slot_addr(s + 3), 1);
     __builtin_amdgcn_sched_barrier(0);
     mma(f, std::integral_constant<int, 0>{});
-    __builtin_amdgcn_sched_barrier(0);
+    read(fb, s + 1, std::integral_constant<int, 4>{});
     read(f, s, std::integral_constant<int, 2>{});
-    issue(s + 3, slot_addr(s + 3), 5);
+    issue(s + 3, slot_addr(s + 3), 2);
+    issue(s + 3, slot_addr(s + 3), 3);
     __builtin_amdgcn_sched_barrier(0);
     mma(f, std::integral_constant<int, 1>{});
-    __builtin_amdgcn_sched_barrier(0);
+    read(fb, s + 1, std::integral_constant<int, 5>{});
     read(f, s, std::integral_constant<int, 3>{});
-    issue(s + 3, slot_addr(s + 3), 6);
+    issue(s + 3, slot_addr(s + 3), 4);
+    issue(s + 3, slot_addr(s + 3), 5);
     __builtin_amdgcn_sched_barrier(0);
     mma(f, std::integral_constant<int, 2>{});
-    __builtin_amdgcn_sched_barrier(0);
+    read(fb, s + 1, std::integral_constant<int, 6>{});
+    read(fb, s + 1, std::integral_constant<int, 7>{});
+    issue(s + 3, slot_addr(s + 3), 6);
     issue(s + 3, slot_addr(s + 3), 7);
+    __builtin_amdgcn_sched_barrier(0);
     mma(f, std::integral_constant<int, 3>{});
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      f.b[nb] = fb.b[nb];
+      f.sb[nb] = fb.sb[nb];
+    }
   }
   bf::block_barrier();
   float* stage = (float*)lds;
