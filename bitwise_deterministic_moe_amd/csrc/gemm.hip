@@ -734,13 +734,19 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
   if (row_tile<bf::BM, bf::BN>(P, t) != kTileGemm) return;
   const int nkb = P.K / 32;
   const int64_t sg = (int64_t)t.g * P.b_sgstride;
-  // the tile's scales (rows past the tile's valid rows read row 0 of the
-  // tile: their codes load as zeros)
-  for (int idx = tid; idx < 256 * (nkb / 4); idx += 256) {
-    const int r = idx / (nkb / 4), q = idx % (nkb / 4);
+  // the tile's scales, 4-byte words, all loads issued up front (rows past the
+  // tile's valid rows read row 0 of the tile: their codes load as zeros); they
+  // are stored to LDS once the slice prologue below has been issued
+  constexpr int kSw = 256 * (kMxMaxK / 32) / 4 / 256;   // words per thread and operand, at most
+  const int nw = 256 * (nkb / 4);
+  uint32_t wa[kSw], wb[kSw];
+#pragma unroll
+  for (int q = 0; q < kSw; ++q) {
+    const int idx = tid + 256 * q;
+    const int r = idx / (nkb / 4), c = idx % (nkb / 4);
     const int ra = r < t.mvalid ? r : 0;
-    ((uint32_t*)s_sa)[idx] = ((const uint32_t*)(P.a_scales + (t.off + t.m0 + ra) * nkb))[q];
-    ((uint32_t*)s_sb)[idx] = ((const uint32_t*)(P.b_scales + sg + (int64_t)(t.n0 + r) * nkb))[q];
+    wa[q] = idx < nw ? ((const uint32_t*)(P.a_scales + (t.off + t.m0 + ra) * nkb))[c] : 0u;
+    wb[q] = idx < nw ? ((const uint32_t*)(P.b_scales + sg + (int64_t)(t.n0 + (idx < nw ? r : 0)) * nkb))[c] : 0u;
   }
   bf::KcOperand oa, ob;
   oa.init(P.a, P.a_bytes, wave, lane, [&](int r) -> uint32_t {
@@ -782,13 +788,22 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
     acc[mb][2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[2], f.a[mb], acc[mb][2], 0, 0, 0, f.sb[2], 0, f.sa[mb]);
     acc[mb][3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[3], f.a[mb], acc[mb][3], 0, 0, 0, f.sb[3], 0, f.sa[mb]);
   };
-  // prologue: slices 0..2 in flight, slice 0 landed, its B blocks read
+  // prologue: slices 0..2 in flight; the scale words (loaded before them)
+  // stored; slice 0 landed and the stores done in every wave; B blocks read
 #pragma unroll
   for (int s = 0; s < 3; ++s)
 #pragma unroll
     for (int i = 0; i < 8; ++i) issue(s, slot_addr(s), i);
-  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  __syncthreads();   // slice 0 and the scale stores to LDS are visible
+  asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+#pragma unroll
+  for (int q = 0; q < kSw; ++q) {
+    const int idx = tid + 256 * q;
+    if (idx < nw) {
+      ((uint32_t*)s_sa)[idx] = wa[q];
+      ((uint32_t*)s_sb)[idx] = wb[q];
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   MxFrags f, fb;     // f: A blocks of slice s and B blocks in use; fb: B blocks of slice s+1
   read(f, 0, std::integral_constant<int, 4>{});
   read(f, 0, std::integral_constant<int, 5>{});
