@@ -705,7 +705,8 @@ __global__ __launch_bounds__(256) void wgrad_pair_bf16_kernel(WgradParams P1, Wg
 // = 16h .. 16h+15 in bytes 0..15 and k = 32+16h .. 32+16h+15 in bytes
 // 16..31, i.e. chunks h and 2+h of the row; the scale register of lane
 // 32kb + i carries the E8M0 byte of row i, k-block kb.  Each tile's scales
-// (256 rows x K/32 bytes per operand) are staged in LDS before the main loop.
+// (up to 256 rows x K/32 bytes per operand) are staged in LDS before the main
+// loop.
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t_ __attribute__((ext_vector_type(4)));
 
@@ -723,7 +724,10 @@ DEV void mx_read_block(const uint8_t* op, const uint8_t* scales, int nkb, int kb
   sc = scales[row * nkb + (kb < nkb ? kb : nkb - 1)];
 }
 
+// BMV: tile rows (256, or 192 as two wave rows of 96: NA = 3 A blocks a wave).
+template <int BMV>
 __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
+  constexpr int WTM = BMV / 2, NA = WTM / 32;
   __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
   __shared__ __attribute__((aligned(16))) uint8_t s_sa[256 * (kMxMaxK / 32)];
   __shared__ __attribute__((aligned(16))) uint8_t s_sb[256 * (kMxMaxK / 32)];
@@ -731,7 +735,7 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
   const uint32_t ring = bf::lds_base(lds);
   const int wm = wave >> 1, wn = wave & 1;
   RowTile t;
-  if (row_tile<bf::BM, bf::BN>(P, t) != kTileGemm) return;
+  if (row_tile<BMV, bf::BN>(P, t) != kTileGemm) return;
   const int nkb = P.K / 32;
   const int64_t sg = (int64_t)t.g * P.b_sgstride;
   // the tile's scales, 4-byte words, all loads issued up front (rows past the
@@ -775,14 +779,15 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
   auto read = [&](MxFrags& f, int s, auto G) __attribute__((always_inline)) {   // group G: A block G (G < 4) or B block G-4
     constexpr int g = decltype(G)::value;
     const uint8_t* st = slot(s);
-    if constexpr (g < 4)
-      mx_read_block(st, s_sa, nkb, 2 * s + h, wm * 128 + g * 32 + r32, h, f.a[g], f.sa[g]);
-    else
+    if constexpr (g < NA)
+      mx_read_block(st, s_sa, nkb, 2 * s + h, wm * WTM + g * 32 + r32, h, f.a[g], f.sa[g]);
+    else if constexpr (g >= 4)
       mx_read_block(st + bf::OPER * 2, s_sb, nkb, 2 * s + h, wn * 128 + (g - 4) * 32 + r32, h, f.b[g - 4],
                     f.sb[g - 4]);
   };
   auto mma = [&](const MxFrags& f, auto MB) __attribute__((always_inline)) {
     constexpr int mb = decltype(MB)::value;
+    if constexpr (mb >= NA) return;
     acc[mb][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[0], f.a[mb], acc[mb][0], 0, 0, 0, f.sb[0], 0, f.sa[mb]);
     acc[mb][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[1], f.a[mb], acc[mb][1], 0, 0, 0, f.sb[1], 0, f.sa[mb]);
     acc[mb][2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[2], f.a[mb], acc[mb][2], 0, 0, 0, f.sb[2], 0, f.sa[mb]);
@@ -852,7 +857,7 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
   NoPre none;
   NoPre::Data nd[2];
   const __amdgpu_buffer_rsrc_t rc = buf(P.c);
-  staged_epilogue<128>(stage, acc, wm, wn, lane, tid, t.mvalid, none, nd, false, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
+  staged_epilogue<WTM>(stage, acc, wm, wn, lane, tid, t.mvalid, none, nd, false, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
     if (m >= t.mvalid) return;  // uniform per wave
     const uint32_t grow = (uint32_t)(t.off + t.m0 + m);
     __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rc,
@@ -1077,7 +1082,10 @@ hipError_t launch_wgrad_pair(const WgradParams& P1, const WgradParams& P2, int n
 
 hipError_t launch_mx_rowgemm(const RowGemmParams& P, int64_t grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
-  mx_rowgemm_kernel<<<grid, 256, 0, st>>>(P);
+  if (P.list_hdr == 2)
+    mx_rowgemm_kernel<kRowTile2><<<grid, 256, 0, st>>>(P);
+  else
+    mx_rowgemm_kernel<256><<<grid, 256, 0, st>>>(P);
   return hipGetLastError();
 }
 

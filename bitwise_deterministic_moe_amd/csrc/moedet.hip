@@ -738,13 +738,13 @@ MOE_API moe_status moe_mx_dgrad_fc1(const moe_problem* p, const moe_routing* rou
   G.ldc = pl.D;
   G.ncu = device_cu_count();
   G.sched = routing->sched;
-  G.list_hdr = 0;
-  G.list_at = kSchedHeader;
+  G.list_hdr = pl.fc1_list2 ? 2 : 0;   // the bf16 fc1 dgrad's row-tile list
+  G.list_at = pl.fc1_list2 ? pl.list2_at : kSchedHeader;
   G.a_scales = dh_scales;
   G.b_scales = w1_scales;
   G.b_sgstride = (int64_t)pl.D * (pl.F / 32);
   G.seed = p->debug_shuffle_seed;
-  return launch_mx_rowgemm(G, rowgemm_grid(pl, pl.D), (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  return launch_mx_rowgemm(G, rowgemm_grid(pl, pl.D, pl.fc1_list2), (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 MOE_API moe_status moe_fingerprint(const void* data, moe_dtype dtype, int ndim, const int64_t* shape,
