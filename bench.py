@@ -179,6 +179,7 @@ def main():
     router = measured_router_bwd(cfg, prob, routing, x, det.dprob) if cfg.combine and el == cfg.num_experts else None
     mxq = measured_mx_quantize(det.dh[: R])
     mxg = measured_mx_dgrad_fc1(cfg, prob, routing, det.dh, w1, st_det.get("fc1_dgrad_dprob_combine"))
+    mxg2 = measured_mx_dgrad_fc2(cfg, prob, routing, dy, w2, h, det.ws1, st_det.get("fc2_dgrad_dprob_partials"))
     result = {
         "metric": "MoE grouped-GEMM bwd TFLOP/s (det mode), % bf16 peak; determinism tax vs atomic",
         "value": round(value, 2),
@@ -207,6 +208,7 @@ def main():
         "router_bwd": router,
         "mx_quantize": mxq,
         "mx_dgrad_fc1": mxg,
+        "mx_dgrad_fc2": mxg2,
         "stages_ms_det": {k: round(v, 5) for k, v in st_det.items()},
         "stages_ms_atomic": {k: round(v, 5) for k, v in st_atom.items()},
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
@@ -327,6 +329,36 @@ def measured_mx_dgrad_fc1(cfg, prob, routing, dh, w1, bf16_ms, reps=20):
     e0.record()
     for _ in range(reps):
         moe.moe_mx_dgrad_fc1(prob, routing, dmx, wmx, out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 2.0 * routing.rows * D * F
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 5), "tflops": round(tf, 1), "peak_fp8": FP8_PEAK_TFLOPS,
+            "frac": round(tf / FP8_PEAK_TFLOPS, 4), "bf16_stage_ms": None if bf16_ms is None else round(bf16_ms, 5)}
+
+
+def measured_mx_dgrad_fc2(cfg, prob, routing, dy, w2, h, ws, bf16_ms, reps=20):
+    """The MXFP8 variant of the fc2 data gradient with its fused epilogue
+    (dprob partials and their fixed-order combine, dh, act_p) on the step's
+    dy, W2 and h, quantised once outside the timed region; deterministic
+    mode, average of `reps` calls (GEMM launch + combine launch), against the
+    dense fp8 peak, beside the bf16 fc2 dgrad stage (whose combine rides in
+    the next launch)."""
+    import torch
+    import bitwise_deterministic_moe_amd as moe
+    if cfg.dtype != "bf16" or cfg.d_model > 2048:
+        return None
+    D, F, el = cfg.d_model, cfg.d_ffn, cfg.num_local
+    dymx = moe.moe_mx_quantize(dy)
+    wq = moe.moe_mx_quantize(w2.reshape(el * F, D))
+    wmx = (wq[0].reshape(el, F, D), wq[1].reshape(el, F, D // 32))
+    dprob, dh, act_p = moe.moe_mx_dgrad_fc2(prob, routing, dymx, wmx, h, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        moe.moe_mx_dgrad_fc2(prob, routing, dymx, wmx, h, dprob=dprob, dh=dh, act_p=act_p, ws=ws)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps

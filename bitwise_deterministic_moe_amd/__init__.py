@@ -30,7 +30,7 @@ _TORCH_TO_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.int32: 2, torch.uin
 EXPORTED_SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_rows_cap", "moe_sched_elems",
                     "moe_workspace_size", "moe_stage_names", "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad",
                     "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd", "moe_sgd_step",
-                    "moe_mx_quantize", "moe_mx_dgrad_fc1")
+                    "moe_mx_quantize", "moe_mx_dgrad_fc1", "moe_mx_dgrad_fc2")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -93,9 +93,10 @@ def load_library() -> ctypes.CDLL:
     lib.moe_sgd_step.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_float, vp, ctypes.c_int, vp]
     lib.moe_mx_quantize.argtypes = [vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, vp, vp, ctypes.c_uint64, vp]
     lib.moe_mx_dgrad_fc1.argtypes = [P, R, vp, vp, vp, vp, vp, vp]
+    lib.moe_mx_dgrad_fc2.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
     for f in ("moe_rows_cap", "moe_sched_elems", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob",
               "moe_bwd_wgrad", "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd",
-              "moe_sgd_step", "moe_mx_quantize", "moe_mx_dgrad_fc1"):
+              "moe_sgd_step", "moe_mx_quantize", "moe_mx_dgrad_fc1", "moe_mx_dgrad_fc2"):
         getattr(lib, f).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -355,6 +356,29 @@ def moe_mx_dgrad_fc1(prob: Problem, routing: Routing, dh_mx, w1_mx, dx_rows=None
     _check(lib.moe_mx_dgrad_fc1(ctypes.byref(cp), ctypes.byref(cr), _ptr(dc), _ptr(ds), _ptr(wc), _ptr(wsc),
                                 _ptr(dx_rows), _stream()), "moe_mx_dgrad_fc1")
     return dx_rows
+
+
+def moe_mx_dgrad_fc2(prob: Problem, routing: Routing, dy_mx, w2_mx, h, mode: int = DETERMINISTIC, dprob=None,
+                     dh=None, act_p=None, ws=None):
+    """MXFP8 fc2 data gradient with the fused dprob / dh / act_p epilogue, from
+    (codes, scales) of dy [T, D] and of W2 [num_local, F, D] (moe_mx_quantize
+    outputs) and the saved h.  Returns (dprob float32 [T, k], dh, act_p bf16
+    [rows_cap, F]).  The workspace is the dgrad one (moe_workspace_size)."""
+    lib = load_library()
+    (dc, ds), (wc, wsc) = dy_mx, w2_mx
+    dev = h.device
+    if dprob is None:
+        dprob = torch.empty((prob.tokens, prob.top_k), dtype=torch.float32, device=dev)
+    if dh is None:
+        dh = torch.empty((prob.rows_cap, prob.d_ffn), dtype=torch.bfloat16, device=dev)
+    if act_p is None:
+        act_p = torch.empty((prob.rows_cap, prob.d_ffn), dtype=torch.bfloat16, device=dev)
+    ws = _ws(moe_workspace_size(prob, mode)[1], ws, dev)
+    cp, cr = prob.c(), routing.c()
+    _check(lib.moe_mx_dgrad_fc2(ctypes.byref(cp), ctypes.byref(cr), _ptr(dc), _ptr(ds), _ptr(wc), _ptr(wsc), _ptr(h),
+                                _ptr(dprob), _ptr(dh), _ptr(act_p), _ptr(ws), ws.numel(), mode, _stream()),
+           "moe_mx_dgrad_fc2")
+    return dprob, dh, act_p
 
 
 def moe_fingerprint(t: torch.Tensor, dtype: Optional[str] = None, chunk_elems: int = 65536,

@@ -439,6 +439,67 @@ constexpr int kQsumOff = kStageBytes;                     // float [BM][16]
 constexpr int kProbOff = kQsumOff + bf::BM * 16 * 4;      // float [BM]
 static_assert(kProbOff + bf::BM * 4 <= bf::ring_bytes<kRowNS>, "epilogue scratch must fit in the ring");
 
+// fc2 dgrad epilogue (shared by the bf16 and the MXFP8 row GEMMs):
+// v = G = dy W2^T at (row, columns col..col+3 of this N-tile).
+//   part[row][nt] = sum over the tile's 256 columns of G * relu(h)^2:
+//                   4 columns in order inside a lane, a DPP butterfly over
+//                   the lane quad (16 columns), then the 16 quad sums of
+//                   the row in quad order (through LDS);
+//   dh = (2 p G) * relu(h);  act_p = p * relu(h)^2.
+// h of a pass is loaded one pass ahead; the row probabilities come from
+// LDS.  lds: the main-loop ring, free (the main loop ended with a barrier).
+template <int WTM>
+DEV void dgrad2_epilogue(const RowGemmParams& P, const RowTile& t, uint16_t* lds, f32x16_t (&acc)[4][4], int wm,
+                         int wn, int lane, int tid, float my_prob) {
+  float* stage = (float*)lds;
+  float* s_qsum = (float*)((char*)lds + kQsumOff);  // [tile row][quad]
+  float* s_prob = (float*)((char*)lds + kProbOff);
+  s_prob[tid] = my_prob;  // the main loop ended with a barrier: the ring is free
+  lds_barrier();
+  HPre hpre{P, t, tid};
+  HPre::Data hd[2];
+  const __amdgpu_buffer_rsrc_t rc = buf(P.c), rc2 = buf(P.c2);
+  staged_epilogue<WTM>(stage, acc, wm, wn, lane, tid, t.mvalid, hpre, hd, false, [&](int m, int col, float (&g)[4], HPre::Data& d, int st) {
+    const bool valid = m < t.mvalid;   // uniform across the wave (one row per wave)
+    if (!valid) return;
+    const int64_t grow = t.off + t.m0 + m;
+    const float p = s_prob[m];
+    const float p2 = 2.f * p;
+    float hv[4], dh[4], pa[4];
+    hv[0] = bf16_to_f32(d.h[st][0] & 0xffffu);
+    hv[1] = bf16_to_f32(d.h[st][0] >> 16);
+    hv[2] = bf16_to_f32(d.h[st][1] & 0xffffu);
+    hv[3] = bf16_to_f32(d.h[st][1] >> 16);
+    float part = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float rh = relu(hv[q]);
+      const float a = rh * rh;
+      part = __builtin_fmaf(g[q], a, part);
+      dh[q] = (p2 * g[q]) * rh;
+      pa[q] = p * a;
+    }
+    const uint32_t o = (uint32_t)grow * 2u * (uint32_t)P.ldc + (t.n0 + col) * 2u;
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(dh[0], dh[1]), pack_bf16x2(dh[2], dh[3])}, rc, o, 0, kEpiNT);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(pa[0], pa[1]), pack_bf16x2(pa[2], pa[3])}, rc2,
+                                          (uint32_t)grow * 2u * (uint32_t)P.ldc2 + (t.n0 + col) * 2u, 0, kEpiNT);
+    part = quad_sum(part);
+    if ((lane & 3) == 0) s_qsum[m * 16 + (lane >> 2)] = part;
+  });
+  __syncthreads();
+  // one thread per tile row: the 16 quad sums in order
+  if (tid < t.mvalid) {
+    float v = s_qsum[tid * 16];
+#pragma unroll
+    for (int q = 1; q < 16; ++q) v = v + s_qsum[tid * 16 + q];
+    const int64_t grow = t.off + t.m0 + tid;
+    if (P.atomic)
+      atomicAdd(P.dprob + P.row_src[grow], v);
+    else
+      P.part[grow * P.n_tiles + t.nt] = v;
+  }
+}
+
 // BMV: tile rows (256, or 192 as two wave rows of 96).
 template <int BL, int EPI, int BMV>
 __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
@@ -526,60 +587,7 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
       }
     });
   } else {
-    // fc2 dgrad: v = G = dy W2^T at (row, columns col..col+3 of this N-tile).
-    //   part[row][nt] = sum over the tile's 256 columns of G * relu(h)^2:
-    //                   4 columns in order inside a lane, a DPP butterfly over
-    //                   the lane quad (16 columns), then the 16 quad sums of
-    //                   the row in quad order (through LDS);
-    //   dh = (2 p G) * relu(h);  act_p = p * relu(h)^2.
-    // h of a pass is loaded one pass ahead; the row probabilities come from
-    // LDS.
-    float* s_qsum = (float*)((char*)lds + kQsumOff);  // [tile row][quad]
-    float* s_prob = (float*)((char*)lds + kProbOff);
-    s_prob[tid] = my_prob;  // the main loop ended with a barrier: the ring is free
-    lds_barrier();
-    HPre hpre{P, t, tid};
-    HPre::Data hd[2];
-    const __amdgpu_buffer_rsrc_t rc = buf(P.c), rc2 = buf(P.c2);
-    staged_epilogue<WTM>(stage, acc, wm, wn, lane, tid, t.mvalid, hpre, hd, false, [&](int m, int col, float (&g)[4], HPre::Data& d, int st) {
-      const bool valid = m < t.mvalid;   // uniform across the wave (one row per wave)
-      if (!valid) return;
-      const int64_t grow = t.off + t.m0 + m;
-      const float p = s_prob[m];
-      const float p2 = 2.f * p;
-      float hv[4], dh[4], pa[4];
-      hv[0] = bf16_to_f32(d.h[st][0] & 0xffffu);
-      hv[1] = bf16_to_f32(d.h[st][0] >> 16);
-      hv[2] = bf16_to_f32(d.h[st][1] & 0xffffu);
-      hv[3] = bf16_to_f32(d.h[st][1] >> 16);
-      float part = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float rh = relu(hv[q]);
-        const float a = rh * rh;
-        part = __builtin_fmaf(g[q], a, part);
-        dh[q] = (p2 * g[q]) * rh;
-        pa[q] = p * a;
-      }
-      const uint32_t o = (uint32_t)grow * 2u * (uint32_t)P.ldc + (t.n0 + col) * 2u;
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(dh[0], dh[1]), pack_bf16x2(dh[2], dh[3])}, rc, o, 0, kEpiNT);
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(pa[0], pa[1]), pack_bf16x2(pa[2], pa[3])}, rc2,
-                                            (uint32_t)grow * 2u * (uint32_t)P.ldc2 + (t.n0 + col) * 2u, 0, kEpiNT);
-      part = quad_sum(part);
-      if ((lane & 3) == 0) s_qsum[m * 16 + (lane >> 2)] = part;
-    });
-    __syncthreads();
-    // one thread per tile row: the 16 quad sums in order
-    if (tid < t.mvalid) {
-      float v = s_qsum[tid * 16];
-#pragma unroll
-      for (int q = 1; q < 16; ++q) v = v + s_qsum[tid * 16 + q];
-      const int64_t grow = t.off + t.m0 + tid;
-      if (P.atomic)
-        atomicAdd(P.dprob + P.row_src[grow], v);
-      else
-        P.part[grow * P.n_tiles + t.nt] = v;
-    }
+    dgrad2_epilogue<WTM>(P, t, lds, acc, wm, wn, lane, tid, my_prob);
   }
 }
 
@@ -724,8 +732,12 @@ DEV void mx_read_block(const uint8_t* op, const uint8_t* scales, int nkb, int kb
   sc = scales[row * nkb + (kb < nkb ? kb : nkb - 1)];
 }
 
-// BMV: tile rows (256, or 192 as two wave rows of 96: NA = 3 A blocks a wave).
-template <int BMV>
+// BMV: tile rows (256, or 192 as two wave rows of 96: NA = 3 A blocks a
+// wave).  EPI: kEpiStore (bf16 rows of C) or kEpiDgrad2 (the fc2 dgrad
+// epilogue on G = C).  With P.a_rows, A row r is row a_rows[r] of the codes
+// and of the scales (the fc2 dgrad gathers dy by token).
+static_assert(kProbOff + bf::BM * 4 <= bf::LDS_BYTES, "fc2 dgrad epilogue scratch must fit in the MXFP8 ring");
+template <int BMV, int EPI>
 __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
   constexpr int WTM = BMV / 2, NA = WTM / 32;
   __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
@@ -736,8 +748,13 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
   const int wm = wave >> 1, wn = wave & 1;
   RowTile t;
   if (row_tile<BMV, bf::BN>(P, t) != kTileGemm) return;
+  float my_prob = 0.f;
+  if constexpr (EPI == kEpiDgrad2) my_prob = tid < t.mvalid ? P.row_prob[t.off + t.m0 + tid] : 0.f;
   const int nkb = P.K / 32;
   const int64_t sg = (int64_t)t.g * P.b_sgstride;
+  auto arow = [&](int r) -> int64_t {   // source row of tile row r < t.mvalid
+    return P.a_rows ? (int64_t)P.a_rows[t.off + t.m0 + r] : t.off + t.m0 + r;
+  };
   // the tile's scales, 4-byte words, all loads issued up front (rows past the
   // tile's valid rows read row 0 of the tile: their codes load as zeros); they
   // are stored to LDS once the slice prologue below has been issued
@@ -749,12 +766,13 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
     const int idx = tid + 256 * q;
     const int r = idx / (nkb / 4), c = idx % (nkb / 4);
     const int ra = r < t.mvalid ? r : 0;
-    wa[q] = idx < nw ? ((const uint32_t*)(P.a_scales + (t.off + t.m0 + ra) * nkb))[c] : 0u;
+    wa[q] = idx < nw ? ((const uint32_t*)(P.a_scales + arow(ra) * nkb))[c] : 0u;
     wb[q] = idx < nw ? ((const uint32_t*)(P.b_scales + sg + (int64_t)(t.n0 + (idx < nw ? r : 0)) * nkb))[c] : 0u;
   }
   bf::KcOperand oa, ob;
-  oa.init(P.a, P.a_bytes, wave, lane, [&](int r) -> uint32_t {
-    return r < t.mvalid ? (uint32_t)((t.off + t.m0 + r) * P.lda) : bf::kOOB;
+  oa.init(P.a, P.a_bytes, wave, lane, [&](int r) -> uint32_t {   // branch-free, as in the bf16 kernel
+    const int64_t row = arow(r < t.mvalid ? r : t.mvalid - 1);
+    return r < t.mvalid ? (uint32_t)(row * P.lda) : bf::kOOB;
   });
   ob.init((const uint8_t*)P.b + (int64_t)t.g * P.b_gstride, P.b_bytes, wave, lane,
           [&](int r) -> uint32_t { return (uint32_t)((t.n0 + r) * P.ldb); });
@@ -853,16 +871,20 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
     }
   }
   bf::block_barrier();
-  float* stage = (float*)lds;
-  NoPre none;
-  NoPre::Data nd[2];
-  const __amdgpu_buffer_rsrc_t rc = buf(P.c);
-  staged_epilogue<WTM>(stage, acc, wm, wn, lane, tid, t.mvalid, none, nd, false, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
-    if (m >= t.mvalid) return;  // uniform per wave
-    const uint32_t grow = (uint32_t)(t.off + t.m0 + m);
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rc,
-                                          (grow * (uint32_t)P.ldc + t.n0 + col) * 2u, 0, kEpiNT);
-  });
+  if constexpr (EPI == kEpiDgrad2) {
+    dgrad2_epilogue<WTM>(P, t, lds, acc, wm, wn, lane, tid, my_prob);
+  } else {
+    float* stage = (float*)lds;
+    NoPre none;
+    NoPre::Data nd[2];
+    const __amdgpu_buffer_rsrc_t rc = buf(P.c);
+    staged_epilogue<WTM>(stage, acc, wm, wn, lane, tid, t.mvalid, none, nd, false, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
+      if (m >= t.mvalid) return;  // uniform per wave
+      const uint32_t grow = (uint32_t)(t.off + t.m0 + m);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rc,
+                                            (grow * (uint32_t)P.ldc + t.n0 + col) * 2u, 0, kEpiNT);
+    });
+  }
 }
 
 // ================================================================= fp32
@@ -1080,12 +1102,16 @@ hipError_t launch_wgrad_pair(const WgradParams& P1, const WgradParams& P2, int n
   return hipGetLastError();
 }
 
-hipError_t launch_mx_rowgemm(const RowGemmParams& P, int64_t grid, hipStream_t st) {
+hipError_t launch_mx_rowgemm(const RowGemmParams& P, int kind, int64_t grid, hipStream_t st) {
   if (grid <= 0) return hipSuccess;
-  if (P.list_hdr == 2)
-    mx_rowgemm_kernel<kRowTile2><<<grid, 256, 0, st>>>(P);
+  if (kind == kGemmFc2Dgrad)
+    mx_rowgemm_kernel<256, kEpiDgrad2><<<grid, 256, 0, st>>>(P);
+  else if (kind != kGemmFc1Dgrad)
+    return hipErrorInvalidValue;
+  else if (P.list_hdr == 2)
+    mx_rowgemm_kernel<kRowTile2, kEpiStore><<<grid, 256, 0, st>>>(P);
   else
-    mx_rowgemm_kernel<256><<<grid, 256, 0, st>>>(P);
+    mx_rowgemm_kernel<256, kEpiStore><<<grid, 256, 0, st>>>(P);
   return hipGetLastError();
 }
 

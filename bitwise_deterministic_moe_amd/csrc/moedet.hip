@@ -744,7 +744,75 @@ MOE_API moe_status moe_mx_dgrad_fc1(const moe_problem* p, const moe_routing* rou
   G.b_scales = w1_scales;
   G.b_sgstride = (int64_t)pl.D * (pl.F / 32);
   G.seed = p->debug_shuffle_seed;
-  return launch_mx_rowgemm(G, rowgemm_grid(pl, pl.D, pl.fc1_list2), (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  return launch_mx_rowgemm(G, kGemmFc1Dgrad, rowgemm_grid(pl, pl.D, pl.fc1_list2), (hipStream_t)stream) ==
+                 hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+MOE_API moe_status moe_mx_dgrad_fc2(const moe_problem* p, const moe_routing* routing, const uint8_t* dy_codes,
+                                    const uint8_t* dy_scales, const uint8_t* w2_codes, const uint8_t* w2_scales,
+                                    const void* h, float* dprob, void* dh, void* act_p, void* ws, size_t ws_bytes,
+                                    moe_mode mode, void* stream) {
+  Plan pl;
+  moe_status s = validate(p, &pl);
+  if (s != MOE_OK) return s;
+  if (!pl.bf16) return MOE_ERR_DTYPE;
+  if (mode != MOE_DETERMINISTIC && mode != MOE_ATOMIC) return MOE_ERR_MODE;
+  if (pl.D > kMxMaxK) return MOE_ERR_SHAPE;
+  const bool at = mode == MOE_ATOMIC;
+  if (!routing || !routing->counts || !routing->offsets || !routing->sched) return MOE_ERR_NULL;
+  if (pl.T > 0 && (!dy_codes || !dy_scales || !dprob || !routing->slot_row)) return MOE_ERR_NULL;
+  if (pl.rows_cap > 0 && (!w2_codes || !w2_scales || !h || !dh || !act_p || !routing->row_src ||
+                          !routing->row_tok || !routing->row_prob))
+    return MOE_ERR_NULL;
+  // the partials region of the dgrad workspace (same layout as moe_bwd_dgrad_dprob)
+  const DgradWs L = dgrad_layout(pl, p->combine, at);
+  s = check_ws(ws, ws_bytes, L.total);
+  if (s != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  const uint64_t seed = p->debug_shuffle_seed;
+  float* part = (float*)((char*)ws + L.part);
+  if (at && launch_zero(dprob, pl.nslot, st) != hipSuccess) return MOE_ERR_HIP;
+  RowGemmParams G{};
+  G.counts = routing->counts;
+  G.offsets = routing->offsets;
+  G.groups = pl.el;
+  G.ncu = device_cu_count();
+  G.sched = routing->sched;
+  G.list_hdr = 0;
+  G.list_at = kSchedHeader;
+  G.seed = seed;
+  // G = dequant(dy)[row_tok] dequant(W2_g)^T; W2 codes [F][D] read as [N=F][K=D]
+  G.N = pl.F;
+  G.K = pl.D;
+  G.a = dy_codes;
+  G.lda = pl.D;  // bytes per row of codes
+  G.a_bytes = (uint32_t)(pl.T * pl.D);
+  G.a_rows = routing->row_tok;
+  G.a_scales = dy_scales;
+  G.b = w2_codes;
+  G.b_gstride = (int64_t)pl.F * pl.D;
+  G.ldb = pl.D;
+  G.b_bytes = (uint32_t)G.b_gstride;
+  G.b_scales = w2_scales;
+  G.b_sgstride = (int64_t)pl.F * (pl.D / 32);
+  G.c = dh;
+  G.ldc = pl.F;
+  G.c2 = act_p;
+  G.ldc2 = pl.F;
+  G.h = h;
+  G.ldh = pl.F;
+  G.row_prob = routing->row_prob;
+  G.row_src = routing->row_src;
+  G.part = part;
+  G.n_tiles = pl.n_tiles;
+  G.dprob = dprob;
+  G.atomic = at;
+  if (launch_mx_rowgemm(G, kGemmFc2Dgrad, rowgemm_grid(pl, pl.F), st) != hipSuccess) return MOE_ERR_HIP;
+  if (!at && launch_dprob_combine(part, routing->slot_row, pl.nslot, pl.n_tiles, dprob, seed, st) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
 }
 
 MOE_API moe_status moe_fingerprint(const void* data, moe_dtype dtype, int ndim, const int64_t* shape,

@@ -297,6 +297,39 @@ moe_status moe_mx_dgrad_fc1(const moe_problem* p, const moe_routing* routing, co
                             const uint8_t* dh_scales, const uint8_t* w1_codes, const uint8_t* w1_scales,
                             void* dx_rows, void* stream);
 
+/* MXFP8 grouped GEMM, the low-precision variant of the fc2 data gradient, with
+ * the fused epilogue of moe_bwd_dgrad_dprob's first stage:
+ *   G[r, :]  = dequant(dy)[row_tok[r], :] . dequant(W2_e)^T   (r a routed row
+ *              of local expert e), float32 accumulation in a fixed k order
+ *              (64 k per scaled MFMA, slices ascending);
+ *   dprob[t, j] = sum_f G[r, f] relu(h[r, f])^2 for the row r of slot (t, j)
+ *              (0 for slots routed to non-local experts);
+ *   dh[r, :]    = bf16(2 p_r G[r, :] relu(h[r, :]));
+ *   act_p[r, :] = bf16(p_r relu(h[r, :])^2)   (p_r = the row's topk_prob).
+ * This is the layer backward of moe_bwd_dgrad_dprob with dy and W2 replaced
+ * by their MXFP8 values; the pages name MXFP8 runs and fingerprint their
+ * encoded values and scale buffers (French article, section "Méthodologie de
+ * débogage du non-déterminisme"); format OCP MX v1.0 (moe_mx_quantize).
+ *   dy_codes / dy_scales  DEVICE uint8 [T, D] / [T, D/32] (moe_mx_quantize of dy)
+ *   w2_codes / w2_scales  DEVICE uint8 [num_local, F, D] / [num_local, F, D/32]
+ *                         (moe_mx_quantize of W2 viewed as [num_local*F, D])
+ *   h                     DEVICE bf16 [rows_cap, F], as saved by moe_fwd
+ *   dprob                 DEVICE float32 [T, k] output
+ *   dh, act_p             DEVICE bf16 [rows_cap, F] outputs; rows < R written
+ *   ws, ws_bytes          the dgrad workspace of moe_workspace_size (mode)
+ *   mode                  MOE_DETERMINISTIC: per-(row, N-tile) partials in the
+ *                         workspace, then the fixed-tree combine of
+ *                         moe_bwd_dgrad_dprob (bits independent of scheduling);
+ *                         MOE_ATOMIC: dprob zeroed, partials added with atomics
+ * routing: as written by moe_fwd.  The problem must be bf16 with D at most
+ * 2048 (the tile's scales are staged in LDS).  Errors: MOE_ERR_DTYPE,
+ * MOE_ERR_SHAPE, MOE_ERR_MODE, MOE_ERR_NULL, MOE_ERR_WORKSPACE before anything
+ * is enqueued; MOE_ERR_HIP for a launch failure. */
+moe_status moe_mx_dgrad_fc2(const moe_problem* p, const moe_routing* routing, const uint8_t* dy_codes,
+                            const uint8_t* dy_scales, const uint8_t* w2_codes, const uint8_t* w2_scales,
+                            const void* h, float* dprob, void* dh, void* act_p, void* ws, size_t ws_bytes,
+                            moe_mode mode, void* stream);
+
 /* Router forward for a train step of the layer: logits[t,e] = sum over d
  * ascending of x[t,d] * w_router[e,d] in float32 fused multiply-adds, one
  * thread per logit (no reduction across threads, so bit-exact).  The router

@@ -184,3 +184,19 @@ def test_mx_dgrad_fc1_validation_returns_before_enqueue(lib):
     assert lib.moe_mx_dgrad_fc1(ctypes.byref(f32), ctypes.byref(r), fake, fake, fake, fake, fake, None) == 3
     cp = moe.Problem(**BASE).c()
     assert lib.moe_mx_dgrad_fc1(ctypes.byref(cp), ctypes.byref(r), None, fake, fake, fake, fake, None) == 1
+
+
+def test_mx_dgrad_fc2_validation_returns_before_enqueue(lib):
+    fake = ctypes.c_void_p(0x1000)
+    r = moe._CRouting(*([0x2000] * 9))
+    cp = moe.Problem(**BASE).c()
+
+    def call(prob, dy=fake, mode=0, ws=ctypes.c_void_p(0x100000), ws_bytes=1 << 40):
+        return lib.moe_mx_dgrad_fc2(ctypes.byref(prob), ctypes.byref(r), dy, fake, fake, fake, fake, fake, fake,
+                                    fake, ws, ws_bytes, mode, None)
+    assert call(moe.Problem(**{**BASE, "d_model": 4096}).c()) == 2        # D beyond the staged scales
+    assert call(moe.Problem(**{**BASE, "dtype": "f32"}).c()) == 3
+    assert call(cp, mode=7) == 5
+    assert call(cp, dy=None) == 1
+    assert call(cp, ws_bytes=16) == 4                                      # workspace too small
+    assert call(cp, ws=ctypes.c_void_p(0x100008)) == 4                     # misaligned

@@ -17,6 +17,16 @@ from test_gpu_parity import EDGE
 
 pytestmark = pytest.mark.gpu
 
+# The scaled MFMA does not return the exactly rounded float32 sum of its 64
+# products.  On a single-wave probe (1024 outputs, E4M3 codes over the whole
+# range, block scales over 2^-7 .. 2^2) its result differed from the exact sum
+# by a median 1.6e-5 and at most 1.6e-4 of the sum of |products|, where a
+# float32-exact sum stays within 64 * 2^-24 = 3.8e-6.  So the float32 dprob of
+# the MXFP8 path is held to 2e-4 of its sum of |terms| element by element, and
+# to 1e-4 in rel-L2, instead of the 1e-5 of float32-accumulated outputs.
+MX_DPROB_TOL = 1e-4
+MX_TERM_BOUND = 2e-4
+
 
 def _case(name):
     cfg = CONFIGS.get(name) or EDGE[name]
@@ -64,3 +74,81 @@ def test_mx_dgrad_fc1_bits_identical_under_shuffles():
         fp = moe.moe_fingerprint(out[:R].contiguous())[1]
         ref = fp if ref is None else ref
         assert fp == ref, seed
+
+
+# ---------------------------------------------------------------- fc2 dgrad
+# The MXFP8 fc2 data gradient is the layer backward with dy and W2 replaced by
+# their MXFP8 values, so the oracle is oracle.backward on the oracle's own
+# dequantised operands; h is a seeded input shared by both sides.
+def _fc2_case(name):
+    cfg = CONFIGS.get(name) or EDGE[name]
+    di = device_inputs(cfg)
+    prob = moe.Problem.from_config(cfg)
+    routing, _, _ = moe.moe_fwd(prob, di.logits, di.x, di.w1, di.w2)
+    rng = np.random.default_rng([cfg.seed, 78])
+    h_bits = f32_to_bf16_bits((rng.standard_normal((prob.rows_cap, cfg.d_ffn)) * 0.5).astype(np.float32))
+    h = torch.from_numpy(h_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    D, F, el = cfg.d_model, cfg.d_ffn, cfg.num_local
+    dymx = moe.moe_mx_quantize(di.dy)
+    wq = moe.moe_mx_quantize(di.w2.reshape(el * F, D))
+    w2mx = (wq[0].reshape(el, F, D), wq[1].reshape(el, F, D // 32))
+    return cfg, di, prob, routing, h_bits, h, dymx, w2mx
+
+
+def _fc2_oracle(cfg, di, h_bits):
+    D, F, el, k = cfg.d_model, cfg.d_ffn, cfg.num_local, cfg.top_k
+    idx, topk_prob = oracle.route(di.host["logits"], k)
+    perm = oracle.permute(idx, cfg.expert_begin, el)
+    R = int(perm["offsets"][-1])
+    deq = lambda a: oracle.mx_dequantize(*oracle.mx_quantize_fast(a))  # noqa: E731
+    dy = deq(oracle.decode(di.host["dy"], "bf16"))
+    w2 = deq(oracle.decode(di.host["w2"], "bf16").reshape(el * F, D)).reshape(el, F, D)
+    x = oracle.decode(di.host["x"], "bf16")
+    w1 = oracle.decode(di.host["w1"], "bf16")
+    h = bf16_bits_to_f32(h_bits[:R]).astype(np.float64)
+    ref = oracle.backward(x, w1, w2, h, dy, topk_prob, perm, k, combine=False)
+    # sum over f and k of |dy[tok, k] W2[f, k] relu(h[f])^2| per slot: the
+    # scale of dprob's rounding bound
+    off, row_tok = perm["offsets"], perm["row_tok"]
+    a = np.maximum(h, 0.0) ** 2
+    mag = np.zeros(R)
+    for e in range(el):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            mag[lo:hi] = np.sum((np.abs(dy[row_tok[lo:hi]]) @ np.abs(w2[e]).T) * a[lo:hi], axis=1)
+    ref["dprob_mag"] = np.zeros(cfg.tokens * k)
+    ref["dprob_mag"][perm["row_src"]] = mag
+    return R, ref
+
+
+@pytest.mark.parametrize("name,mode", [("ragged_bf16", moe.DETERMINISTIC), ("ragged_bf16", moe.ATOMIC),
+                                       ("shard_bf16", moe.DETERMINISTIC), ("empty_experts_bf16", moe.DETERMINISTIC),
+                                       ("bf16_e8k2", moe.DETERMINISTIC), ("bf16_e8k2", moe.ATOMIC)])
+def test_mx_dgrad_fc2_parity(name, mode):
+    print(f"mx dgrad fc2 {name} mode {mode}", flush=True)
+    cfg, di, prob, routing, h_bits, h, dymx, w2mx = _fc2_case(name)
+    dprob, dh, act_p = moe.moe_mx_dgrad_fc2(prob, routing, dymx, w2mx, h, mode)
+    torch.cuda.synchronize()
+    R, ref = _fc2_oracle(cfg, di, h_bits)
+    e_dprob = rel_l2(dprob.cpu().numpy(), ref["dprob"])
+    e_dh = rel_l2(to_host(dh[:R]), ref["dh"])
+    e_ap = rel_l2(to_host(act_p[:R]), ref["act_p"])
+    print(f"  rel-L2 dprob {e_dprob:.3e} dh {e_dh:.3e} act_p {e_ap:.3e}", flush=True)
+    assert e_dh <= 2e-2 and e_ap <= 2e-2
+    assert e_dprob <= MX_DPROB_TOL
+    err = np.abs(dprob.cpu().numpy().astype(np.float64).ravel() - ref["dprob"].ravel())
+    assert np.all(err <= MX_TERM_BOUND * ref["dprob_mag"] + 1e-30), float(np.max(err / (ref["dprob_mag"] + 1e-30)))
+    # slots routed to non-local experts are exactly 0
+    local = (ref["dprob"] != 0)
+    assert np.all(dprob.cpu().numpy()[~local] == 0)
+
+
+def test_mx_dgrad_fc2_bits_identical_under_shuffles():
+    cfg, di, prob, routing, h_bits, h, dymx, w2mx = _fc2_case("bf16_e8k2")
+    R = routing.rows
+    ref = None
+    for seed in (0, 3, 0xBEEF):
+        dprob, dh, act_p = moe.moe_mx_dgrad_fc2(prob.with_seed(seed), routing, dymx, w2mx, h)
+        fps = tuple(moe.moe_fingerprint(t.contiguous())[1] for t in (dprob, dh[:R], act_p[:R]))
+        ref = fps if ref is None else ref
+        assert fps == ref, seed
