@@ -236,6 +236,13 @@ def moe_fwd(prob: Problem, logits, x, w1, w2, mode: int = DETERMINISTIC, routing
         y = torch.empty((prob.tokens if prob.combine else prob.rows_cap, prob.d_model), dtype=dt, device=dev)
     need = moe_workspace_size(prob, mode)[0]
     ws = _ws(need, ws, dev)
+    T, E, D, F, el, rc = prob.tokens, prob.num_experts, prob.d_model, prob.d_ffn, prob.local, prob.rows_cap
+    _need(logits, T * E, torch.float32, "moe_fwd logits")
+    _need(x, T * D, dt, "moe_fwd x")
+    _need(w1, el * D * F, dt, "moe_fwd w1")
+    _need(w2, el * F * D, dt, "moe_fwd w2")
+    _need(h, rc * F, dt, "moe_fwd h")
+    _need(y, (T if prob.combine else rc) * D, dt, "moe_fwd y")
     cp, cr = prob.c(events), routing.c()
     _check(lib.moe_fwd(ctypes.byref(cp), _ptr(logits), _ptr(x), _ptr(w1), _ptr(w2), ctypes.byref(cr), _ptr(h),
                        _ptr(y), _ptr(ws), ws.numel(), mode, _stream()), "moe_fwd")
@@ -259,6 +266,15 @@ def moe_bwd_dgrad_dprob(prob: Problem, routing: Routing, dy, w1, w2, h, mode: in
         act_p = torch.empty((prob.rows_cap, prob.d_ffn), dtype=dt, device=dev)
     need = moe_workspace_size(prob, mode)[1]
     ws = _ws(need, ws, dev)
+    T, k, D, F, el, rc = prob.tokens, prob.top_k, prob.d_model, prob.d_ffn, prob.local, prob.rows_cap
+    _need(dy, T * D, dt, "moe_bwd_dgrad_dprob dy")
+    _need(w1, el * D * F, dt, "moe_bwd_dgrad_dprob w1")
+    _need(w2, el * F * D, dt, "moe_bwd_dgrad_dprob w2")
+    _need(h, rc * F, dt, "moe_bwd_dgrad_dprob h")
+    _need(dx, (T if prob.combine else rc) * D, dt, "moe_bwd_dgrad_dprob dx")
+    _need(dprob, T * k, torch.float32, "moe_bwd_dgrad_dprob dprob")
+    _need(dh, rc * F, dt, "moe_bwd_dgrad_dprob dh")
+    _need(act_p, rc * F, dt, "moe_bwd_dgrad_dprob act_p")
     cp, cr = prob.c(events), routing.c()
     _check(lib.moe_bwd_dgrad_dprob(ctypes.byref(cp), ctypes.byref(cr), _ptr(dy), _ptr(w1), _ptr(w2), _ptr(h),
                                    _ptr(dx), _ptr(dprob), _ptr(dh), _ptr(act_p), _ptr(ws), ws.numel(), mode,
@@ -278,6 +294,14 @@ def moe_bwd_wgrad(prob: Problem, routing: Routing, x, dy, dh, act_p, mode: int =
         dw2 = torch.empty((el, F, D), dtype=torch.float32, device=dev)
     need = moe_workspace_size(prob, mode)[2]
     ws = _ws(need, ws, dev)
+    dt = TORCH_DTYPE[prob.dtype]
+    T, rc = prob.tokens, prob.rows_cap
+    _need(x, T * D, dt, "moe_bwd_wgrad x")
+    _need(dy, T * D, dt, "moe_bwd_wgrad dy")
+    _need(dh, rc * F, dt, "moe_bwd_wgrad dh")
+    _need(act_p, rc * F, dt, "moe_bwd_wgrad act_p")
+    _need(dw1, el * D * F, torch.float32, "moe_bwd_wgrad dw1")
+    _need(dw2, el * F * D, torch.float32, "moe_bwd_wgrad dw2")
     cp, cr = prob.c(events), routing.c()
     _check(lib.moe_bwd_wgrad(ctypes.byref(cp), ctypes.byref(cr), _ptr(x), _ptr(dy), _ptr(dh), _ptr(act_p), _ptr(dw1),
                              _ptr(dw2), _ptr(ws), ws.numel(), mode, _stream()), "moe_bwd_wgrad")
@@ -327,6 +351,14 @@ def moe_sgd_step(master: torch.Tensor, grad: torch.Tensor, lr: float, runtime: t
     return master, runtime
 
 
+def _need(t: torch.Tensor, numel: int, dtype, what: str):
+    """Argument check before a raw pointer crosses the boundary: the kernels
+    behind it take sizes from the problem, not from the tensor."""
+    if t.dtype != dtype or not t.is_contiguous() or t.numel() != numel:
+        raise MoeError(f"{what}: need a contiguous {dtype} tensor of {numel} elements, "
+                       f"got {t.dtype} {tuple(t.shape)} (contiguous={t.is_contiguous()})")
+
+
 def moe_mx_quantize(t: torch.Tensor, codes=None, scales=None, shuffle_seed: int = 0):
     """MXFP8 (E4M3 codes, E8M0 scales per 32 elements of the last dimension)
     of a contiguous float32 or bf16 tensor.  Returns (codes uint8 with t's
@@ -340,6 +372,8 @@ def moe_mx_quantize(t: torch.Tensor, codes=None, scales=None, shuffle_seed: int 
         codes = torch.empty(t.shape, dtype=torch.uint8, device=t.device)
     if scales is None:
         scales = torch.empty(tuple(t.shape[:-1]) + (cols // 32,), dtype=torch.uint8, device=t.device)
+    _need(codes, t.numel(), torch.uint8, "moe_mx_quantize codes")
+    _need(scales, rows * (cols // 32), torch.uint8, "moe_mx_quantize scales")
     _check(lib.moe_mx_quantize(_ptr(t), _TORCH_TO_CODE[t.dtype], rows, cols, _ptr(codes), _ptr(scales),
                                shuffle_seed & 0xFFFFFFFFFFFFFFFF, _stream()), "moe_mx_quantize")
     return codes, scales
@@ -352,6 +386,12 @@ def moe_mx_dgrad_fc1(prob: Problem, routing: Routing, dh_mx, w1_mx, dx_rows=None
     (dc, ds), (wc, wsc) = dh_mx, w1_mx
     if dx_rows is None:
         dx_rows = torch.empty((prob.rows_cap, prob.d_model), dtype=torch.bfloat16, device=dc.device)
+    rc, D, F, el = prob.rows_cap, prob.d_model, prob.d_ffn, prob.local
+    _need(dc, rc * F, torch.uint8, "moe_mx_dgrad_fc1 dh codes")
+    _need(ds, rc * (F // 32), torch.uint8, "moe_mx_dgrad_fc1 dh scales")
+    _need(wc, el * D * F, torch.uint8, "moe_mx_dgrad_fc1 W1 codes")
+    _need(wsc, el * D * (F // 32), torch.uint8, "moe_mx_dgrad_fc1 W1 scales")
+    _need(dx_rows, rc * D, torch.bfloat16, "moe_mx_dgrad_fc1 dx_rows")
     cp, cr = prob.c(), routing.c()
     _check(lib.moe_mx_dgrad_fc1(ctypes.byref(cp), ctypes.byref(cr), _ptr(dc), _ptr(ds), _ptr(wc), _ptr(wsc),
                                 _ptr(dx_rows), _stream()), "moe_mx_dgrad_fc1")
@@ -374,6 +414,15 @@ def moe_mx_dgrad_fc2(prob: Problem, routing: Routing, dy_mx, w2_mx, h, mode: int
     if act_p is None:
         act_p = torch.empty((prob.rows_cap, prob.d_ffn), dtype=torch.bfloat16, device=dev)
     ws = _ws(moe_workspace_size(prob, mode)[1], ws, dev)
+    T, k, rc, D, F, el = prob.tokens, prob.top_k, prob.rows_cap, prob.d_model, prob.d_ffn, prob.local
+    _need(dc, T * D, torch.uint8, "moe_mx_dgrad_fc2 dy codes")
+    _need(ds, T * (D // 32), torch.uint8, "moe_mx_dgrad_fc2 dy scales")
+    _need(wc, el * F * D, torch.uint8, "moe_mx_dgrad_fc2 W2 codes")
+    _need(wsc, el * F * (D // 32), torch.uint8, "moe_mx_dgrad_fc2 W2 scales")
+    _need(h, rc * F, torch.bfloat16, "moe_mx_dgrad_fc2 h")
+    _need(dprob, T * k, torch.float32, "moe_mx_dgrad_fc2 dprob")
+    _need(dh, rc * F, torch.bfloat16, "moe_mx_dgrad_fc2 dh")
+    _need(act_p, rc * F, torch.bfloat16, "moe_mx_dgrad_fc2 act_p")
     cp, cr = prob.c(), routing.c()
     _check(lib.moe_mx_dgrad_fc2(ctypes.byref(cp), ctypes.byref(cr), _ptr(dc), _ptr(ds), _ptr(wc), _ptr(wsc), _ptr(h),
                                 _ptr(dprob), _ptr(dh), _ptr(act_p), _ptr(ws), ws.numel(), mode, _stream()),

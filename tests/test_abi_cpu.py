@@ -200,3 +200,20 @@ def test_mx_dgrad_fc2_validation_returns_before_enqueue(lib):
     assert call(cp, dy=None) == 1
     assert call(cp, ws_bytes=16) == 4                                      # workspace too small
     assert call(cp, ws=ctypes.c_void_p(0x100008)) == 4                     # misaligned
+
+
+def test_mx_bindings_check_tensor_sizes_before_the_call():
+    # CPU tensors of the wrong size: the binding raises before any pointer
+    # reaches the library
+    import torch
+    p = moe.Problem(tokens=64, d_model=256, d_ffn=256, num_experts=4, top_k=2)
+    rc, D, F, el = p.rows_cap, p.d_model, p.d_ffn, p.local
+    u8 = lambda n: torch.zeros(n, dtype=torch.uint8)  # noqa: E731
+    r = moe.Routing(*[torch.zeros(1, dtype=torch.int32)] * 9)
+    with pytest.raises(moe.MoeError, match="dh scales"):
+        moe.moe_mx_dgrad_fc1(p, r, (u8(rc * F), u8(rc * F // 32 - 1)), (u8(el * D * F), u8(el * D * F // 32)))
+    with pytest.raises(moe.MoeError, match="W2 codes"):
+        moe.moe_mx_dgrad_fc2(p, r, (u8(64 * D), u8(64 * D // 32)), (u8(el * F * D + 1), u8(el * F * D // 32)),
+                             torch.zeros(rc * F, dtype=torch.bfloat16))
+    with pytest.raises(moe.MoeError, match="scales"):
+        moe.moe_mx_quantize(torch.zeros(4, 64), scales=u8(3))
