@@ -321,6 +321,13 @@ def moe_router_bwd(prob: Problem, routing: Routing, dprob, x, w_router, mode: in
         dw_router = torch.empty((E, D), dtype=torch.float32, device=dev)
     if dx_router is None:
         dx_router = torch.empty((T, D), dtype=TORCH_DTYPE[prob.dtype], device=dev)
+    dt = TORCH_DTYPE[prob.dtype]
+    _need(dprob, T * prob.top_k, torch.float32, "moe_router_bwd dprob")
+    _need(x, T * D, dt, "moe_router_bwd x")
+    _need(w_router, E * D, dt, "moe_router_bwd w_router")
+    _need(dlogits, T * E, torch.float32, "moe_router_bwd dlogits")
+    _need(dw_router, E * D, torch.float32, "moe_router_bwd dw_router")
+    _need(dx_router, T * D, dt, "moe_router_bwd dx_router")
     cp, cr = prob.c(), routing.c()
     _check(lib.moe_router_bwd(ctypes.byref(cp), ctypes.byref(cr), _ptr(dprob), _ptr(x), _ptr(w_router), _ptr(dlogits),
                               _ptr(dw_router), _ptr(dx_router), mode, _stream()), "moe_router_bwd")
@@ -332,6 +339,10 @@ def moe_router_fwd(prob: Problem, x, w_router, logits=None):
     lib = load_library()
     if logits is None:
         logits = torch.empty((prob.tokens, prob.num_experts), dtype=torch.float32, device=w_router.device)
+    dt = TORCH_DTYPE[prob.dtype]
+    _need(x, prob.tokens * prob.d_model, dt, "moe_router_fwd x")
+    _need(w_router, prob.num_experts * prob.d_model, dt, "moe_router_fwd w_router")
+    _need(logits, prob.tokens * prob.num_experts, torch.float32, "moe_router_fwd logits")
     cp = prob.c()
     _check(lib.moe_router_fwd(ctypes.byref(cp), _ptr(x), _ptr(w_router), _ptr(logits), _stream()), "moe_router_fwd")
     return logits
