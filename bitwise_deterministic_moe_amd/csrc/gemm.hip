@@ -803,13 +803,14 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
       mx_read_block(st + bf::OPER * 2, s_sb, nkb, 2 * s + h, wn * 128 + (g - 4) * 32 + r32, h, f.b[g - 4],
                     f.sb[g - 4]);
   };
-  auto mma = [&](const MxFrags& f, auto MB) __attribute__((always_inline)) {
+  // A block mb of fa against the four B blocks of fb
+  auto mma = [&](const MxFrags& fa, const MxFrags& fb, auto MB) __attribute__((always_inline)) {
     constexpr int mb = decltype(MB)::value;
     if constexpr (mb >= NA) return;
-    acc[mb][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[0], f.a[mb], acc[mb][0], 0, 0, 0, f.sb[0], 0, f.sa[mb]);
-    acc[mb][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[1], f.a[mb], acc[mb][1], 0, 0, 0, f.sb[1], 0, f.sa[mb]);
-    acc[mb][2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[2], f.a[mb], acc[mb][2], 0, 0, 0, f.sb[2], 0, f.sa[mb]);
-    acc[mb][3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[3], f.a[mb], acc[mb][3], 0, 0, 0, f.sb[3], 0, f.sa[mb]);
+    acc[mb][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb.b[0], fa.a[mb], acc[mb][0], 0, 0, 0, fb.sb[0], 0, fa.sa[mb]);
+    acc[mb][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb.b[1], fa.a[mb], acc[mb][1], 0, 0, 0, fb.sb[1], 0, fa.sa[mb]);
+    acc[mb][2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb.b[2], fa.a[mb], acc[mb][2], 0, 0, 0, fb.sb[2], 0, fa.sa[mb]);
+    acc[mb][3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb.b[3], fa.a[mb], acc[mb][3], 0, 0, 0, fb.sb[3], 0, fa.sa[mb]);
   };
   // prologue: slices 0..2 in flight; the scale words (loaded before them)
   // stored; slice 0 landed and the stores done in every wave; B blocks read
@@ -827,7 +828,7 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
     }
   }
   asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  MxFrags f, fb;     // f: A blocks of slice s and B blocks in use; fb: B blocks of slice s+1
+  MxFrags f, g;      // f.a: A blocks of the current slice; f.b and g.b: B blocks, alternating by step
   read(f, 0, std::integral_constant<int, 4>{});
   read(f, 0, std::integral_constant<int, 5>{});
   read(f, 0, std::integral_constant<int, 6>{});
@@ -835,40 +836,41 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
   // step s: slice s+1 landed and every wave is done with slice s-1, whose slot
   // takes slice s+3.  The A blocks of slice s are read one ahead of their
   // MFMAs; the B blocks of slice s+1 (past the last slice: zero codes and a
-  // clamped scale index, never multiplied) are read in between.
-#pragma unroll 1
-  for (int s = 0; s < nsteps; ++s) {
+  // clamped scale index, never multiplied) are read into the other B set in
+  // between, so the sets swap roles each step and nothing is copied.
+  auto step = [&](int s, const MxFrags& bcur, MxFrags& bnext) __attribute__((always_inline)) {
     asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     read(f, s, std::integral_constant<int, 0>{});
     issue(s + 3, slot_addr(s + 3), 0);
     read(f, s, std::integral_constant<int, 1>{});
     issue(s + 3, slot_addr(s + 3), 1);
     __builtin_amdgcn_sched_barrier(0);
-    mma(f, std::integral_constant<int, 0>{});
-    read(fb, s + 1, std::integral_constant<int, 4>{});
+    mma(f, bcur, std::integral_constant<int, 0>{});
+    read(bnext, s + 1, std::integral_constant<int, 4>{});
     read(f, s, std::integral_constant<int, 2>{});
     issue(s + 3, slot_addr(s + 3), 2);
     issue(s + 3, slot_addr(s + 3), 3);
     __builtin_amdgcn_sched_barrier(0);
-    mma(f, std::integral_constant<int, 1>{});
-    read(fb, s + 1, std::integral_constant<int, 5>{});
+    mma(f, bcur, std::integral_constant<int, 1>{});
+    read(bnext, s + 1, std::integral_constant<int, 5>{});
     read(f, s, std::integral_constant<int, 3>{});
     issue(s + 3, slot_addr(s + 3), 4);
     issue(s + 3, slot_addr(s + 3), 5);
     __builtin_amdgcn_sched_barrier(0);
-    mma(f, std::integral_constant<int, 2>{});
-    read(fb, s + 1, std::integral_constant<int, 6>{});
-    read(fb, s + 1, std::integral_constant<int, 7>{});
+    mma(f, bcur, std::integral_constant<int, 2>{});
+    read(bnext, s + 1, std::integral_constant<int, 6>{});
+    read(bnext, s + 1, std::integral_constant<int, 7>{});
     issue(s + 3, slot_addr(s + 3), 6);
     issue(s + 3, slot_addr(s + 3), 7);
     __builtin_amdgcn_sched_barrier(0);
-    mma(f, std::integral_constant<int, 3>{});
+    mma(f, bcur, std::integral_constant<int, 3>{});
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      f.b[nb] = fb.b[nb];
-      f.sb[nb] = fb.sb[nb];
-    }
+  };
+  // the number of slices is even (K is a multiple of 128)
+#pragma unroll 1
+  for (int s = 0; s < nsteps; s += 2) {
+    step(s, f, g);
+    step(s + 1, g, f);
   }
   bf::block_barrier();
   if constexpr (EPI == kEpiDgrad2) {
