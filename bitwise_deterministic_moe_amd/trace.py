@@ -25,6 +25,10 @@ One train step on the layer (all device work through the library's C ABI):
     dlogits, dwr, dx_router = moe_router_bwd(dprob)
     SGD on the float32 masters of W1, W2, wr; bf16 (or f32) runtime copies
     rebuilt by the same kernel (moe_sgd_step).
+With mx=True (bf16 layers) the two data gradients run on MXFP8 operands
+(moe_mx_dgrad_fc2 on dy and W2, moe_mx_dgrad_fc1 on dh and W1, each
+quantised by moe_mx_quantize), and the op-level trace fingerprints each
+encoded tensor and its scale buffer, as the pages do for low-precision runs.
 Metrics (loss, gradient norms) are summed on the host in float64 in a fixed
 order, so they are deterministic too.
 """
@@ -37,7 +41,8 @@ import numpy as np
 import torch
 
 from . import (MoeError, Problem, TORCH_DTYPE, moe_bwd_dgrad_dprob, moe_bwd_wgrad, moe_fingerprint,
-               moe_fwd, moe_router_bwd, moe_router_fwd, moe_sgd_step)
+               moe_fwd, moe_mx_dgrad_fc1, moe_mx_dgrad_fc2, moe_mx_quantize, moe_router_bwd, moe_router_fwd,
+               moe_sgd_step)
 
 LEVELS = {"metrics": 0, "phases": 1, "ops": 2}
 
@@ -173,11 +178,19 @@ def _host_sum_sq(t: torch.Tensor) -> float:
     return float(math.fsum((a * a).tolist())) if a.size < 1 << 20 else float(np.sum(a * a))
 
 
-def train_step(cfg, st: TrainState, tracer: Tracer, hook: Optional[Callable] = None):
+def _mx(t, rows: int, cols: int):
+    """MXFP8 codes and scales of t viewed as [rows, cols]."""
+    return moe_mx_quantize(t.reshape(rows, cols))
+
+
+def train_step(cfg, st: TrainState, tracer: Tracer, hook: Optional[Callable] = None, mx: bool = False):
     """One step at st.step; advances st.step.  ``hook(step, where, st)`` may
-    change the state at "before_forward" (a fault injector for tests)."""
+    change the state at "before_forward" (a fault injector for tests).  With
+    ``mx`` the data gradients run on MXFP8 operands."""
     if cfg.combine != 1 or cfg.num_local != cfg.num_experts:
         raise MoeError("the train step covers the full layer (token layout, all experts local)")
+    if mx and (cfg.dtype != "bf16" or cfg.d_model > 2048 or cfg.d_ffn > 2048):
+        raise MoeError("the MXFP8 train step needs a bf16 layer with d_model and d_ffn at most 2048")
     s, prob = st.step, st.prob
     x, dy = _device_batch(cfg, s)
     if hook:
@@ -185,7 +198,17 @@ def train_step(cfg, st: TrainState, tracer: Tracer, hook: Optional[Callable] = N
     R = st.runtime
     logits = moe_router_fwd(prob, x, R["wr"])
     routing, h, y = moe_fwd(prob, logits, x, R["w1"], R["w2"])
-    dx, dprob, dh, act_p = moe_bwd_dgrad_dprob(prob, routing, dy, R["w1"], R["w2"], h)
+    enc = {}
+    if mx:
+        el, D, F = cfg.num_local, cfg.d_model, cfg.d_ffn
+        enc["dy"], enc["w2"] = _mx(dy, cfg.tokens, D), _mx(R["w2"], el * F, D)
+        w2mx = (enc["w2"][0].reshape(el, F, D), enc["w2"][1].reshape(el, F, D // 32))
+        dprob, dh, act_p = moe_mx_dgrad_fc2(prob, routing, enc["dy"], w2mx, h)
+        enc["dh"], enc["w1"] = _mx(dh, prob.rows_cap, F), _mx(R["w1"], el * D, F)
+        w1mx = (enc["w1"][0].reshape(el, D, F), enc["w1"][1].reshape(el, D, F // 32))
+        dx = moe_mx_dgrad_fc1(prob, routing, enc["dh"], w1mx)     # per routed row
+    else:
+        dx, dprob, dh, act_p = moe_bwd_dgrad_dprob(prob, routing, dy, R["w1"], R["w2"], h)
     dw1, dw2 = moe_bwd_wgrad(prob, routing, x, dy, dh, act_p)
     dlogits, dwr, dxr = moe_router_bwd(prob, routing, dprob, x, R["wr"])
     torch.cuda.synchronize()
@@ -198,10 +221,22 @@ def train_step(cfg, st: TrainState, tracer: Tracer, hook: Optional[Callable] = N
     T.tensor(s, "forward", "moe_fwd", "h", h, 2)
     T.tensor(s, "forward", "moe_fwd", "y", y, 1)
     # backward
-    T.tensor(s, "backward", "moe_bwd_dgrad_dprob", "dprob", dprob, 1)
-    T.tensor(s, "backward", "moe_bwd_dgrad_dprob", "dh", dh, 2)
-    T.tensor(s, "backward", "moe_bwd_dgrad_dprob", "act_p", act_p, 2)
-    T.tensor(s, "backward", "moe_bwd_dgrad_dprob", "dx", dx, 1)
+    if mx:
+        for n in ("dy", "w2"):
+            T.tensor(s, "backward", "moe_mx_quantize", f"{n}_codes", enc[n][0], 2)
+            T.tensor(s, "backward", "moe_mx_quantize", f"{n}_scales", enc[n][1], 2)
+        T.tensor(s, "backward", "moe_mx_dgrad_fc2", "dprob", dprob, 1)
+        T.tensor(s, "backward", "moe_mx_dgrad_fc2", "dh", dh, 2)
+        T.tensor(s, "backward", "moe_mx_dgrad_fc2", "act_p", act_p, 2)
+        for n in ("dh", "w1"):
+            T.tensor(s, "backward", "moe_mx_quantize", f"{n}_codes", enc[n][0], 2)
+            T.tensor(s, "backward", "moe_mx_quantize", f"{n}_scales", enc[n][1], 2)
+        T.tensor(s, "backward", "moe_mx_dgrad_fc1", "dx_rows", dx[: routing.rows], 1)
+    else:
+        T.tensor(s, "backward", "moe_bwd_dgrad_dprob", "dprob", dprob, 1)
+        T.tensor(s, "backward", "moe_bwd_dgrad_dprob", "dh", dh, 2)
+        T.tensor(s, "backward", "moe_bwd_dgrad_dprob", "act_p", act_p, 2)
+        T.tensor(s, "backward", "moe_bwd_dgrad_dprob", "dx", dx, 1)
     T.tensor(s, "backward", "moe_bwd_wgrad", "dw1", dw1, 1)
     T.tensor(s, "backward", "moe_bwd_wgrad", "dw2", dw2, 1)
     T.tensor(s, "router", "moe_router_bwd", "dlogits", dlogits, 2)
@@ -222,12 +257,12 @@ def train_step(cfg, st: TrainState, tracer: Tracer, hook: Optional[Callable] = N
 
 
 def run(cfg, steps: int, level: str = "phases", window: Optional[range] = None, st: Optional[TrainState] = None,
-        hook: Optional[Callable] = None, lr: float = 0.05):
+        hook: Optional[Callable] = None, lr: float = 0.05, mx: bool = False):
     """Train from st (or the initial state) until st.step == steps."""
     st = st or initial_state(cfg, lr)
     tr = Tracer(level, window)
     while st.step < steps:
-        train_step(cfg, st, tr, hook)
+        train_step(cfg, st, tr, hook, mx)
     return st, tr
 
 
@@ -275,6 +310,7 @@ def main(argv=None):
     ap.add_argument("--level", default="phases", choices=list(LEVELS))
     ap.add_argument("--out", help="write the trace (JSON lines)")
     ap.add_argument("--compare", nargs=2, metavar=("A", "B"), help="report the first divergence of two traces")
+    ap.add_argument("--mx", action="store_true", help="data gradients on MXFP8 operands (bf16 layers)")
     a = ap.parse_args(argv)
     if a.compare:
         d = first_divergence(Tracer.load(a.compare[0]), Tracer.load(a.compare[1]))
@@ -282,7 +318,7 @@ def main(argv=None):
                                                  "b": d[2] and d[2].__dict__}))
         return
     from synth import CONFIGS
-    _, tr = run(CONFIGS[a.config], a.steps, a.level)
+    _, tr = run(CONFIGS[a.config], a.steps, a.level, mx=a.mx)
     if a.out:
         tr.save(a.out)
     print(json.dumps({"records": len(tr.records), "steps": a.steps, "level": a.level}))

@@ -134,3 +134,18 @@ def _rne32(q: fractions.Fraction) -> np.float32:
     best = min(cands, key=lambda c: (abs(fractions.Fraction(c.item()) - q),
                                      int(np.array([c], np.float32).view(np.int32)[0]) & 1))
     return best
+
+
+def test_mx_train_steps_are_bit_identical_and_fingerprint_the_encoded_buffers():
+    cfg = EDGE["ragged_bf16"]
+    print("trace mx reproducibility", flush=True)
+    _, a = trace.run(cfg, 3, "ops", mx=True)
+    _, b = trace.run(cfg, 3, "ops", mx=True)
+    assert trace.first_divergence(a.records, b.records) is None
+    enc = {r.name for r in a.records if r.op == "moe_mx_quantize"}
+    assert enc == {f"{n}_{k}" for n in ("dy", "w2", "dh", "w1") for k in ("codes", "scales")}
+    assert all(r.dtype == "u8" for r in a.records if r.op == "moe_mx_quantize")
+    # a different computation from the bf16 step: the traces part at step 0's backward
+    _, c = trace.run(cfg, 3, "ops")
+    d = trace.first_divergence(a.records, c.records)
+    assert d is not None and d[1].step == 0 and d[1].phase == "backward"
