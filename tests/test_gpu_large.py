@@ -219,3 +219,65 @@ def test_large_parity_and_determinism(name):
     fp1 = fingerprints(out2, cfg.combine)
     diff = [n for n in fp0 if fp0[n] != fp1[n]]
     assert not diff, f"outputs differ under a shuffled launch order: {diff}"
+
+
+def test_large_mx_data_gradients_on_sampled_experts():
+    """The MXFP8 data gradients at LatentMoE size (512 experts, 2 GiB of W1
+    codes): every row of sampled experts against the oracle on its own
+    dequantised operands.  h and dh are seeded inputs of both sides; dprob is
+    held to the MXFP8 tolerance (1e-4 rel-L2, see test_gpu_mx_gemm.py)."""
+    cfg = CONFIGS["latent_e512k22"]
+    print("[latent mx] drawing inputs", flush=True)
+    host = make_inputs(cfg)
+    di = DeviceInputs(cfg, host)
+    prob = moe.Problem.from_config(cfg)
+    D, F, el = cfg.d_model, cfg.d_ffn, cfg.num_local
+    routing, _, _ = moe.moe_fwd(prob, di.logits, di.x, di.w1, di.w2)
+    rng = np.random.default_rng([cfg.seed, 79])
+    from synth.inputs import f32_to_bf16_bits, bf16_bits_to_f32
+    h_bits = f32_to_bf16_bits((rng.standard_normal((prob.rows_cap, F)) * 0.5).astype(np.float32))
+    dh_bits = f32_to_bf16_bits((rng.standard_normal((prob.rows_cap, F)) * 0.01).astype(np.float32))
+    up = lambda b: torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)  # noqa: E731
+    h, dh = up(h_bits), up(dh_bits)
+    print("[latent mx] HIP path", flush=True)
+    dymx = moe.moe_mx_quantize(di.dy)
+    wq2 = moe.moe_mx_quantize(di.w2.reshape(el * F, D))
+    dprob, g_dh, g_ap = moe.moe_mx_dgrad_fc2(prob, routing, dymx, (wq2[0].reshape(el, F, D),
+                                                                  wq2[1].reshape(el, F, D // 32)), h)
+    del wq2
+    wq1 = moe.moe_mx_quantize(di.w1.reshape(el * D, F))
+    dx_rows = moe.moe_mx_dgrad_fc1(prob, routing, moe.moe_mx_quantize(dh), (wq1[0].reshape(el, D, F),
+                                                                           wq1[1].reshape(el, D, F // 32)))
+    torch.cuda.synchronize()
+    del wq1
+
+    idx, p = oracle.route(host["logits"], cfg.top_k)
+    perm = oracle.permute(idx, cfg.expert_begin, el)
+    off, row_tok, row_src = perm["offsets"], perm["row_tok"], perm["row_src"]
+    p_rows = p.reshape(-1)[row_src]
+    deq = lambda a: oracle.mx_dequantize(*oracle.mx_quantize_fast(a))  # noqa: E731
+    x = oracle.decode(host["x"], "bf16")
+    dy = oracle.decode(host["dy"], "bf16")
+    experts = _sample_experts(perm["counts"], np.random.default_rng([cfg.seed, 98]))
+    print(f"[latent mx] oracle on experts {experts}", flush=True)
+    got = {n: [] for n in ("dprob", "dh", "act_p", "dx_rows")}
+    ref = {n: [] for n in got}
+    g_dprob = to_host(dprob).reshape(-1)
+    for e in experts:
+        s, t = int(off[e]), int(off[e + 1])
+        if t == s:
+            continue
+        w1, w2 = _weights(cfg, host, e)
+        w2q = deq(w2)                                      # W2_e [F, D], blocks along D
+        hr = bf16_bits_to_f32(h_bits[s:t]).astype(np.float64)
+        b = oracle.expert_backward(x[row_tok[s:t]], deq(dy[row_tok[s:t]]), p_rows[s:t], hr, w1, w2q)
+        dhq = deq(bf16_bits_to_f32(dh_bits[s:t]).astype(np.float64))
+        for n, gv, rv in (("dprob", g_dprob[row_src[s:t]], b["dprob"]), ("dh", to_host(g_dh[s:t]), b["dh"]),
+                          ("act_p", to_host(g_ap[s:t]), b["act_p"]),
+                          ("dx_rows", to_host(dx_rows[s:t]), dhq @ deq(w1).T)):
+            got[n].append(np.asarray(gv).ravel())
+            ref[n].append(np.asarray(rv).ravel())
+    errs = {n: rel_l2(np.concatenate(got[n]), np.concatenate(ref[n])) for n in got}
+    print(f"[latent mx] rel-L2 {errs}", flush=True)
+    assert errs["dprob"] <= 1e-4
+    assert all(errs[n] <= 2e-2 for n in ("dh", "act_p", "dx_rows"))
