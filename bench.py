@@ -50,7 +50,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs the layer on one GPU; --gpus must be 1"}))
         sys.exit(2)
     import numpy as np
     import torch
