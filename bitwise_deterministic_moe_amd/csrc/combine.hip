@@ -64,14 +64,28 @@ __global__ __launch_bounds__(256) void gather_combine_kernel(const T* rows, cons
   float acc[V];
 #pragma unroll
   for (int q = 0; q < V; ++q) acc[q] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int32_t r = slot_row[t * k + j];
-    if (r < 0) continue;
-    const float w = weights ? weights[t * k + j] : 1.f;
-    float f[V];
-    Vec<T>::load(rows + (int64_t)r * D + d, f);
+  // slots in groups of 4: the group's row indices, then its rows, are loaded
+  // together (one memory round trip each instead of one per slot); they are
+  // added in slot order, so the result is the j-ascending sum either way
+  constexpr int G = 4;
+  for (int j0 = 0; j0 < k; j0 += G) {
+    int32_t r[G];
+    float w[G];
 #pragma unroll
-    for (int q = 0; q < V; ++q) acc[q] = weights ? __builtin_fmaf(w, f[q], acc[q]) : acc[q] + f[q];
+    for (int i = 0; i < G; ++i) {
+      r[i] = j0 + i < k ? slot_row[t * k + j0 + i] : -1;
+      w[i] = weights && j0 + i < k ? weights[t * k + j0 + i] : 1.f;
+    }
+    float f[G][V];
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+      if (r[i] >= 0) Vec<T>::load(rows + (int64_t)r[i] * D + d, f[i]);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (r[i] < 0) continue;
+#pragma unroll
+      for (int q = 0; q < V; ++q) acc[q] = weights ? __builtin_fmaf(w[i], f[i][q], acc[q]) : acc[q] + f[i][q];
+    }
   }
   Vec<T>::store(out + t * D + d, acc);
 }
