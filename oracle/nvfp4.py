@@ -16,7 +16,9 @@ follows NVIDIA's public description of NVFP4:
 The decisions are taken in float32 steps, written out here so that a kernel
 can take the same ones (where float arithmetic decides a code, both sides
 decide in the same precision):
-  g  = f32(amax) / 2688                       (1 if amax == 0)
+  g  = f32(amax) / 2688                       (1 if that is 0: an all-zero
+                                              tensor, or one so small that
+                                              g underflows)
   t  = f32(6 * g);  x = f32(amax_b / t)       block scale code sb = E4M3(x)
   d  = f32(value(sb) * g)                     element code = E2M1(f32(v / d))
                                               (0 codes, sign kept, if d == 0)
@@ -70,7 +72,9 @@ def nvfp4_quantize(rows: np.ndarray):
     assert k % BLOCK == 0
     f32 = np.float32
     amax = f32(np.max(np.abs(rows))) if rows.size else f32(0)
-    g = f32(amax / f32(2688.0)) if amax > 0 else f32(1.0)
+    g = f32(amax / f32(2688.0))
+    if not g > 0:
+        g = f32(1.0)
     t = f32(f32(6.0) * g)
     codes = np.zeros((n, k), np.uint8)
     scales = np.zeros((n, k // BLOCK), np.uint8)

@@ -53,13 +53,20 @@ def test_a_block_worked_by_hand():
     assert packed[0, 8] == (0x7 | (0xB << 4))
     zero = nvfp4.nvfp4_quantize(np.zeros((2, 16), np.float32))
     assert zero[2] == np.float32(1.0) and not zero[0].any() and not zero[1].any()
+    # a tensor whose scale amax / 2688 underflows: g = 1, and every code and
+    # scale is zero (the sign bits kept)
+    tiny = np.full((1, 16), np.float32(2.0 ** -140))
+    tiny[0, 1] = -tiny[0, 1]
+    t = nvfp4.nvfp4_quantize(tiny)
+    assert t[2] == np.float32(1.0) and not t[1].any() and t[0][0, 0] == 0x80
 
 
 def _brute(rows):
     """Same float32 steps, encoders replaced by a scan over every code."""
     f32 = np.float32
     amax = f32(np.max(np.abs(rows)))
-    g = f32(amax / f32(2688.0)) if amax > 0 else f32(1.0)
+    g = f32(amax / f32(2688.0))
+    g = g if g > 0 else f32(1.0)
     t = f32(f32(6.0) * g)
     e4 = [(mx.e4m3_decode(c), c) for c in range(0x7F)]
     e2 = [(nvfp4.e2m1_decode(c), c) for c in range(8)]
