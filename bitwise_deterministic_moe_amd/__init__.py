@@ -30,7 +30,8 @@ _TORCH_TO_CODE = {torch.float32: 0, torch.bfloat16: 1, torch.int32: 2, torch.uin
 EXPORTED_SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_rows_cap", "moe_sched_elems",
                     "moe_workspace_size", "moe_stage_names", "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad",
                     "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd", "moe_sgd_step",
-                    "moe_mx_quantize", "moe_mx_dgrad_fc1", "moe_mx_dgrad_fc2")
+                    "moe_mx_quantize", "moe_mx_dgrad_fc1", "moe_mx_dgrad_fc2",
+                    "moe_nvfp4_quantize")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -93,10 +94,12 @@ def load_library() -> ctypes.CDLL:
     lib.moe_sgd_step.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_float, vp, ctypes.c_int, vp]
     lib.moe_mx_quantize.argtypes = [vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, vp, vp, ctypes.c_uint64, vp]
     lib.moe_mx_dgrad_fc1.argtypes = [P, R, vp, vp, vp, vp, vp, vp]
+    lib.moe_nvfp4_quantize.argtypes = [vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, vp, vp, vp, ctypes.c_uint64,
+                                       vp]
     lib.moe_mx_dgrad_fc2.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
     for f in ("moe_rows_cap", "moe_sched_elems", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob",
               "moe_bwd_wgrad", "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd",
-              "moe_sgd_step", "moe_mx_quantize", "moe_mx_dgrad_fc1", "moe_mx_dgrad_fc2"):
+              "moe_sgd_step", "moe_mx_quantize", "moe_mx_dgrad_fc1", "moe_mx_dgrad_fc2", "moe_nvfp4_quantize"):
         getattr(lib, f).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -388,6 +391,23 @@ def moe_mx_quantize(t: torch.Tensor, codes=None, scales=None, shuffle_seed: int 
     _check(lib.moe_mx_quantize(_ptr(t), _TORCH_TO_CODE[t.dtype], rows, cols, _ptr(codes), _ptr(scales),
                                shuffle_seed & 0xFFFFFFFFFFFFFFFF, _stream()), "moe_mx_quantize")
     return codes, scales
+
+
+def moe_nvfp4_quantize(t: torch.Tensor, shuffle_seed: int = 0):
+    """NVFP4 of a contiguous float32 or bf16 tensor (blocks of 16 along the
+    last dimension).  Returns (packed codes uint8 [..., cols/2], block scales
+    uint8 [..., cols/16], tensor scale float32 [1])."""
+    lib = load_library()
+    if not t.is_contiguous() or t.dim() < 1:
+        raise MoeError("moe_nvfp4_quantize needs a contiguous tensor")
+    cols = t.shape[-1]
+    rows = t.numel() // cols if cols else 0
+    codes = torch.empty(tuple(t.shape[:-1]) + (cols // 2,), dtype=torch.uint8, device=t.device)
+    scales = torch.empty(tuple(t.shape[:-1]) + (cols // 16,), dtype=torch.uint8, device=t.device)
+    g = torch.empty(1, dtype=torch.float32, device=t.device)
+    _check(lib.moe_nvfp4_quantize(_ptr(t), _TORCH_TO_CODE[t.dtype], rows, cols, _ptr(codes), _ptr(scales), _ptr(g),
+                                  shuffle_seed & 0xFFFFFFFFFFFFFFFF, _stream()), "moe_nvfp4_quantize")
+    return codes, scales, g
 
 
 def moe_mx_dgrad_fc1(prob: Problem, routing: Routing, dh_mx, w1_mx, dx_rows=None):

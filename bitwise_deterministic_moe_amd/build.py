@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoedet.so")
-SOURCES = ["moedet.hip", "route.hip", "gemm.hip", "combine.hip", "fingerprint.hip", "mfma_rate.hip", "router.hip", "train.hip", "mx.hip"]
+SOURCES = ["moedet.hip", "route.hip", "gemm.hip", "combine.hip", "fingerprint.hip", "mfma_rate.hip", "router.hip", "train.hip", "mx.hip", "nvfp4.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

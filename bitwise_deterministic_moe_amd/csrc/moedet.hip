@@ -711,6 +711,20 @@ MOE_API moe_status moe_mx_quantize(const void* in, moe_dtype dtype, int64_t rows
              : MOE_ERR_HIP;
 }
 
+MOE_API moe_status moe_nvfp4_quantize(const void* in, moe_dtype dtype, int64_t rows, int64_t cols, uint8_t* codes,
+                                      uint8_t* scales, float* global_scale, uint64_t debug_shuffle_seed,
+                                      void* stream) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (rows < 0 || cols <= 0 || cols % 16 != 0 || rows > (((int64_t)1 << 40) / cols)) return MOE_ERR_SHAPE;
+  if (!global_scale) return MOE_ERR_NULL;
+  if (rows > 0 && (!in || !codes || !scales)) return MOE_ERR_NULL;
+  if (((uintptr_t)in & 15) || ((uintptr_t)codes & 3)) return MOE_ERR_SHAPE;
+  return launch_nvfp4_quantize(in, dtype == MOE_BF16, rows, cols, codes, scales, global_scale, debug_shuffle_seed,
+                               (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
 MOE_API moe_status moe_mx_dgrad_fc1(const moe_problem* p, const moe_routing* routing, const uint8_t* dh_codes,
                                     const uint8_t* dh_scales, const uint8_t* w1_codes, const uint8_t* w1_scales,
                                     void* dx_rows, void* stream) {

@@ -276,6 +276,27 @@ moe_status moe_router_bwd(const moe_problem* p, const moe_routing* routing, cons
                           const void* x, const void* w_router, float* dlogits, float* dw_router,
                           void* dx_router, moe_mode mode, void* stream);
 
+/* NVFP4 block quantisation of a row-major [rows, cols] tensor, the second
+ * low-precision form whose encoded values and scale buffers the pages
+ * fingerprint (French article, section "Méthodologie de débogage du
+ * non-déterminisme").  The pages do not define it; this follows NVIDIA's
+ * public description: E2M1 element codes, an E4M3 scale per 16 consecutive
+ * elements of a row, a float32 scale g for the tensor.  Decisions in float32:
+ *   g = amax / 2688 (1 if that is 0);  block scale sb = E4M3(amax_block / (6 g));
+ *   element code = E2M1(|v| / (value(sb) g)) with v's sign (0 if the divisor is 0);
+ * E4M3 / E2M1 round to nearest, ties to the even code, saturating at 448 / 6.
+ *   in            DEVICE float32 or bf16 [rows, cols], 16-byte aligned;
+ *                 cols a multiple of 16; finite values
+ *   codes         DEVICE uint8 [rows, cols/2] output, 4-byte aligned: element
+ *                 2j in the low nibble of byte j, 2j+1 in the high nibble
+ *   scales        DEVICE uint8 [rows, cols/16] output (E4M3 codes)
+ *   global_scale  DEVICE float32 [1] output: g
+ * Three launches on `stream`; every output byte is independent of the launch
+ * order.  Errors: MOE_ERR_DTYPE, MOE_ERR_SHAPE, MOE_ERR_NULL before anything
+ * is enqueued; MOE_ERR_HIP for a launch failure. */
+moe_status moe_nvfp4_quantize(const void* in, moe_dtype dtype, int64_t rows, int64_t cols, uint8_t* codes,
+                              uint8_t* scales, float* global_scale, uint64_t debug_shuffle_seed, void* stream);
+
 /* MXFP8 grouped GEMM, the low-precision variant of the fc1 data gradient:
  *   dx_rows[r, :] = dequant(dh)[r, :] . dequant(W1_e)^T   (r a routed row of
  *                   local expert e; dequant = E4M3 code * E8M0 block scale)

@@ -217,3 +217,12 @@ def test_mx_bindings_check_tensor_sizes_before_the_call():
                              torch.zeros(rc * F, dtype=torch.bfloat16))
     with pytest.raises(moe.MoeError, match="scales"):
         moe.moe_mx_quantize(torch.zeros(4, 64), scales=u8(3))
+
+
+def test_nvfp4_quantize_validation_returns_before_enqueue(lib):
+    fake, g = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x3000)
+    assert lib.moe_nvfp4_quantize(fake, 2, 4, 64, fake, fake, g, 0, None) == 3             # i32 input
+    assert lib.moe_nvfp4_quantize(fake, 1, 4, 40, fake, fake, g, 0, None) == 2             # cols % 16
+    assert lib.moe_nvfp4_quantize(fake, 1, 4, 64, fake, fake, None, 0, None) == 1          # no tensor scale
+    assert lib.moe_nvfp4_quantize(None, 1, 4, 64, fake, fake, g, 0, None) == 1
+    assert lib.moe_nvfp4_quantize(ctypes.c_void_p(0x1008), 1, 4, 64, fake, fake, g, 0, None) == 2   # misaligned
