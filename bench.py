@@ -178,6 +178,7 @@ def main():
     mfma_peak = measured_mfma_peak()
     router = measured_router_bwd(cfg, prob, routing, x, det.dprob) if cfg.combine and el == cfg.num_experts else None
     mxq = measured_mx_quantize(det.dh[: R])
+    nvq = measured_nvfp4_quantize(det.dh[: R])
     mxg = measured_mx_dgrad_fc1(cfg, prob, routing, det.dh, w1, st_det.get("fc1_dgrad_dprob_combine"))
     mxg2 = measured_mx_dgrad_fc2(cfg, prob, routing, dy, w2, h, det.ws1, st_det.get("fc2_dgrad_dprob_partials"))
     result = {
@@ -207,6 +208,7 @@ def main():
         },
         "router_bwd": router,
         "mx_quantize": mxq,
+        "nvfp4_quantize": nvq,
         "mx_dgrad_fc1": mxg,
         "mx_dgrad_fc2": mxg2,
         "stages_ms_det": {k: round(v, 5) for k, v in st_det.items()},
@@ -282,6 +284,29 @@ def measured_router_bwd(cfg, prob, routing, x, dprob, reps=20):
             "tax": round(res["det"] / res["atomic"] - 1.0, 4), "hbm_bytes": hbm,
             "achieved_GBs": round(hbm / sec / 1e9, 1), "frac_hbm": round(hbm / sec / 1e9 / HBM_PEAK_GBS, 4),
             "gather_bytes": gather, "gather_GBs": round(gather / sec / 1e9, 1)}
+
+
+def measured_nvfp4_quantize(t, reps=20):
+    """NVFP4 quantisation (tensor amax pass, then E2M1 codes + E4M3 block
+    scales) of the step's dh, average over `reps` calls (three launches each),
+    against HBM for its bytes (read the tensor twice, write half a byte per
+    element and one scale byte per 16 elements)."""
+    import torch
+    import bitwise_deterministic_moe_amd as moe
+    moe.moe_nvfp4_quantize(t)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        moe.moe_nvfp4_quantize(t)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    n = t.numel()
+    hbm = 2 * n * t.element_size() + n // 2 + n // 16
+    return {"tensor": f"dh {list(t.shape)} {str(t.dtype).replace('torch.', '')}", "ms": round(ms, 5),
+            "hbm_bytes": hbm, "achieved_GBs": round(hbm / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(hbm / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def measured_mx_quantize(t, reps=20):

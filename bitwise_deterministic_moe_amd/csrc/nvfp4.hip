@@ -34,20 +34,28 @@ DEV float e4m3_value(uint32_t c) {
   return e == 0 ? (float)m * 0x1p-9f : (float)(8u + m) * __uint_as_float((e + 117u) << 23);   // (8+m) 2^(e-10)
 }
 
+// Grid-stride over 8-element groups; the workgroup's max (waves, then LDS)
+// goes to the word with one atomic per workgroup, so at most kAmaxBlocks
+// atomics meet at one address.
+constexpr int kAmaxBlocks = 1024;
 template <typename T>
-__global__ __launch_bounds__(256) void nvfp4_amax_kernel(const T* in, int64_t n8, uint32_t* amax_bits, uint64_t seed) {
-  const int64_t u = map_unit(blockIdx.x, (n8 + 255) / 256, seed);
-  const int64_t i = (u < 0 ? n8 : u * 256 + threadIdx.x);
-  float v[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) v[q] = 0.f;
-  if (i < n8) load8(in + 8 * i, v);
+__global__ __launch_bounds__(256) void nvfp4_amax_kernel(const T* in, int64_t n8, uint32_t* amax_bits) {
+  __shared__ uint32_t s_m[4];
   uint32_t m = 0;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    float v[8];
+    load8(in + 8 * i, v);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) m = max(m, __float_as_uint(v[q]) & 0x7fffffffu);
+    for (int q = 0; q < 8; ++q) m = max(m, __float_as_uint(v[q]) & 0x7fffffffu);
+  }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-  if ((threadIdx.x & 63) == 0 && m != 0) atomicMax(amax_bits, m);
+  if ((threadIdx.x & 63) == 0) s_m[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(s_m[0], s_m[1]), max(s_m[2], s_m[3]));
+    if (m != 0) atomicMax(amax_bits, m);
+  }
 }
 
 __global__ void nvfp4_tensor_scale_kernel(float* g) {
@@ -94,10 +102,11 @@ hipError_t launch_nvfp4_quantize(const void* in, bool bf16, int64_t rows, int64_
   if (e != hipSuccess) return e;
   const int64_t grid = grid_for_units((n8 + 255) / 256);
   if (n8 > 0) {
+    const int64_t ag = grid < kAmaxBlocks ? grid : kAmaxBlocks;
     if (bf16)
-      nvfp4_amax_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)in, n8, (uint32_t*)global_scale, seed);
+      nvfp4_amax_kernel<uint16_t><<<ag, 256, 0, st>>>((const uint16_t*)in, n8, (uint32_t*)global_scale);
     else
-      nvfp4_amax_kernel<float><<<grid, 256, 0, st>>>((const float*)in, n8, (uint32_t*)global_scale, seed);
+      nvfp4_amax_kernel<float><<<ag, 256, 0, st>>>((const float*)in, n8, (uint32_t*)global_scale);
   }
   nvfp4_tensor_scale_kernel<<<1, 1, 0, st>>>(global_scale);
   if (n8 > 0) {
