@@ -28,7 +28,8 @@ One train step on the layer (all device work through the library's C ABI):
 With mx=True (bf16 layers) the two data gradients run on MXFP8 operands
 (moe_mx_dgrad_fc2 on dy and W2, moe_mx_dgrad_fc1 on dh and W1, each
 quantised by moe_mx_quantize), and the op-level trace fingerprints each
-encoded tensor and its scale buffer, as the pages do for low-precision runs.
+encoded tensor and its scale buffer, as the pages do for low-precision runs;
+it also records dh's NVFP4 encoding (codes, block scales, tensor scale).
 Metrics (loss, gradient norms) are summed on the host in float64 in a fixed
 order, so they are deterministic too.
 """
@@ -41,8 +42,8 @@ import numpy as np
 import torch
 
 from . import (MoeError, Problem, TORCH_DTYPE, moe_bwd_dgrad_dprob, moe_bwd_wgrad, moe_fingerprint,
-               moe_fwd, moe_mx_dgrad_fc1, moe_mx_dgrad_fc2, moe_mx_quantize, moe_router_bwd, moe_router_fwd,
-               moe_sgd_step)
+               moe_fwd, moe_mx_dgrad_fc1, moe_mx_dgrad_fc2, moe_mx_quantize, moe_nvfp4_quantize, moe_router_bwd,
+               moe_router_fwd, moe_sgd_step)
 
 LEVELS = {"metrics": 0, "phases": 1, "ops": 2}
 
@@ -232,6 +233,9 @@ def train_step(cfg, st: TrainState, tracer: Tracer, hook: Optional[Callable] = N
             T.tensor(s, "backward", "moe_mx_quantize", f"{n}_codes", enc[n][0], 2)
             T.tensor(s, "backward", "moe_mx_quantize", f"{n}_scales", enc[n][1], 2)
         T.tensor(s, "backward", "moe_mx_dgrad_fc1", "dx_rows", dx[: routing.rows], 1)
+        nv = moe_nvfp4_quantize(dh)
+        for n, t in zip(("dh_codes", "dh_scales", "dh_tensor_scale"), nv):
+            T.tensor(s, "backward", "moe_nvfp4_quantize", n, t, 2)
     else:
         T.tensor(s, "backward", "moe_bwd_dgrad_dprob", "dprob", dprob, 1)
         T.tensor(s, "backward", "moe_bwd_dgrad_dprob", "dh", dh, 2)

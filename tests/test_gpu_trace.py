@@ -145,6 +145,8 @@ def test_mx_train_steps_are_bit_identical_and_fingerprint_the_encoded_buffers():
     enc = {r.name for r in a.records if r.op == "moe_mx_quantize"}
     assert enc == {f"{n}_{k}" for n in ("dy", "w2", "dh", "w1") for k in ("codes", "scales")}
     assert all(r.dtype == "u8" for r in a.records if r.op == "moe_mx_quantize")
+    nv = [r.name for r in a.records if r.op == "moe_nvfp4_quantize" and r.step == 0]
+    assert nv == ["dh_codes", "dh_scales", "dh_tensor_scale"]
     # a different computation from the bf16 step: the traces part at step 0's backward
     _, c = trace.run(cfg, 3, "ops")
     d = trace.first_divergence(a.records, c.records)
