@@ -84,7 +84,7 @@ def load_library() -> ctypes.CDLL:
     lib.moe_stage_names.restype = ctypes.c_char_p
     lib.moe_stage_names.argtypes = [P, ctypes.c_int, ctypes.c_int]
     lib.moe_fwd.argtypes = [P, vp, vp, vp, vp, R, vp, vp, vp, sz, ctypes.c_int, vp]
-    lib.moe_bwd_dgrad_dprob.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
+    lib.moe_bwd_dgrad_dprob.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
     lib.moe_bwd_wgrad.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
     lib.moe_fingerprint.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
                                     vp, vp, vp]
@@ -96,7 +96,7 @@ def load_library() -> ctypes.CDLL:
     lib.moe_mx_dgrad_fc1.argtypes = [P, R, vp, vp, vp, vp, vp, vp]
     lib.moe_nvfp4_quantize.argtypes = [vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, vp, vp, vp, ctypes.c_uint64,
                                        vp]
-    lib.moe_mx_dgrad_fc2.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
+    lib.moe_mx_dgrad_fc2.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
     for f in ("moe_rows_cap", "moe_sched_elems", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob",
               "moe_bwd_wgrad", "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd",
               "moe_sgd_step", "moe_mx_quantize", "moe_mx_dgrad_fc1", "moe_mx_dgrad_fc2", "moe_nvfp4_quantize"):
@@ -253,9 +253,9 @@ def moe_fwd(prob: Problem, logits, x, w1, w2, mode: int = DETERMINISTIC, routing
 
 
 def moe_bwd_dgrad_dprob(prob: Problem, routing: Routing, dy, w1, w2, h, mode: int = DETERMINISTIC,
-                        dx=None, dprob=None, dh=None, act_p=None, ws=None, events=None):
+                        dx=None, dprob=None, dh=None, ws=None, events=None):
     """fc2 dgrad with dprob + fc1 dgrad + dx combine.
-    Returns (dx_or_rows, dprob, dh, act_p)."""
+    Returns (dx_or_rows, dprob, dh)."""
     lib = load_library()
     dev = h.device
     dt = TORCH_DTYPE[prob.dtype]
@@ -265,8 +265,6 @@ def moe_bwd_dgrad_dprob(prob: Problem, routing: Routing, dy, w1, w2, h, mode: in
         dprob = torch.empty((prob.tokens, prob.top_k), dtype=torch.float32, device=dev)
     if dh is None:
         dh = torch.empty((prob.rows_cap, prob.d_ffn), dtype=dt, device=dev)
-    if act_p is None:
-        act_p = torch.empty((prob.rows_cap, prob.d_ffn), dtype=dt, device=dev)
     need = moe_workspace_size(prob, mode)[1]
     ws = _ws(need, ws, dev)
     T, k, D, F, el, rc = prob.tokens, prob.top_k, prob.d_model, prob.d_ffn, prob.local, prob.rows_cap
@@ -277,17 +275,17 @@ def moe_bwd_dgrad_dprob(prob: Problem, routing: Routing, dy, w1, w2, h, mode: in
     _need(dx, (T if prob.combine else rc) * D, dt, "moe_bwd_dgrad_dprob dx")
     _need(dprob, T * k, torch.float32, "moe_bwd_dgrad_dprob dprob")
     _need(dh, rc * F, dt, "moe_bwd_dgrad_dprob dh")
-    _need(act_p, rc * F, dt, "moe_bwd_dgrad_dprob act_p")
     cp, cr = prob.c(events), routing.c()
     _check(lib.moe_bwd_dgrad_dprob(ctypes.byref(cp), ctypes.byref(cr), _ptr(dy), _ptr(w1), _ptr(w2), _ptr(h),
-                                   _ptr(dx), _ptr(dprob), _ptr(dh), _ptr(act_p), _ptr(ws), ws.numel(), mode,
-                                   _stream()), "moe_bwd_dgrad_dprob")
-    return dx, dprob, dh, act_p
+                                   _ptr(dx), _ptr(dprob), _ptr(dh), _ptr(ws), ws.numel(), mode, _stream()),
+           "moe_bwd_dgrad_dprob")
+    return dx, dprob, dh
 
 
-def moe_bwd_wgrad(prob: Problem, routing: Routing, x, dy, dh, act_p, mode: int = DETERMINISTIC, dw1=None,
+def moe_bwd_wgrad(prob: Problem, routing: Routing, x, dy, h, dh, mode: int = DETERMINISTIC, dw1=None,
                   dw2=None, ws=None, events=None):
-    """Expert weight gradients (float32).  Returns (dw1, dw2)."""
+    """Expert weight gradients (float32) from the layer input x, the upstream
+    gradient dy, the saved h and dh.  Returns (dw1, dw2)."""
     lib = load_library()
     dev = dh.device
     el, D, F = prob.local, prob.d_model, prob.d_ffn
@@ -301,12 +299,12 @@ def moe_bwd_wgrad(prob: Problem, routing: Routing, x, dy, dh, act_p, mode: int =
     T, rc = prob.tokens, prob.rows_cap
     _need(x, T * D, dt, "moe_bwd_wgrad x")
     _need(dy, T * D, dt, "moe_bwd_wgrad dy")
+    _need(h, rc * F, dt, "moe_bwd_wgrad h")
     _need(dh, rc * F, dt, "moe_bwd_wgrad dh")
-    _need(act_p, rc * F, dt, "moe_bwd_wgrad act_p")
     _need(dw1, el * D * F, torch.float32, "moe_bwd_wgrad dw1")
     _need(dw2, el * F * D, torch.float32, "moe_bwd_wgrad dw2")
     cp, cr = prob.c(events), routing.c()
-    _check(lib.moe_bwd_wgrad(ctypes.byref(cp), ctypes.byref(cr), _ptr(x), _ptr(dy), _ptr(dh), _ptr(act_p), _ptr(dw1),
+    _check(lib.moe_bwd_wgrad(ctypes.byref(cp), ctypes.byref(cr), _ptr(x), _ptr(dy), _ptr(h), _ptr(dh), _ptr(dw1),
                              _ptr(dw2), _ptr(ws), ws.numel(), mode, _stream()), "moe_bwd_wgrad")
     return dw1, dw2
 
@@ -430,10 +428,10 @@ def moe_mx_dgrad_fc1(prob: Problem, routing: Routing, dh_mx, w1_mx, dx_rows=None
 
 
 def moe_mx_dgrad_fc2(prob: Problem, routing: Routing, dy_mx, w2_mx, h, mode: int = DETERMINISTIC, dprob=None,
-                     dh=None, act_p=None, ws=None):
-    """MXFP8 fc2 data gradient with the fused dprob / dh / act_p epilogue, from
+                     dh=None, ws=None):
+    """MXFP8 fc2 data gradient with the fused dprob / dh epilogue, from
     (codes, scales) of dy [T, D] and of W2 [num_local, F, D] (moe_mx_quantize
-    outputs) and the saved h.  Returns (dprob float32 [T, k], dh, act_p bf16
+    outputs) and the saved h.  Returns (dprob float32 [T, k], dh bf16
     [rows_cap, F]).  The workspace is the dgrad one (moe_workspace_size)."""
     lib = load_library()
     (dc, ds), (wc, wsc) = dy_mx, w2_mx
@@ -442,8 +440,6 @@ def moe_mx_dgrad_fc2(prob: Problem, routing: Routing, dy_mx, w2_mx, h, mode: int
         dprob = torch.empty((prob.tokens, prob.top_k), dtype=torch.float32, device=dev)
     if dh is None:
         dh = torch.empty((prob.rows_cap, prob.d_ffn), dtype=torch.bfloat16, device=dev)
-    if act_p is None:
-        act_p = torch.empty((prob.rows_cap, prob.d_ffn), dtype=torch.bfloat16, device=dev)
     ws = _ws(moe_workspace_size(prob, mode)[1], ws, dev)
     T, k, rc, D, F, el = prob.tokens, prob.top_k, prob.rows_cap, prob.d_model, prob.d_ffn, prob.local
     _need(dc, T * D, torch.uint8, "moe_mx_dgrad_fc2 dy codes")
@@ -453,12 +449,11 @@ def moe_mx_dgrad_fc2(prob: Problem, routing: Routing, dy_mx, w2_mx, h, mode: int
     _need(h, rc * F, torch.bfloat16, "moe_mx_dgrad_fc2 h")
     _need(dprob, T * k, torch.float32, "moe_mx_dgrad_fc2 dprob")
     _need(dh, rc * F, torch.bfloat16, "moe_mx_dgrad_fc2 dh")
-    _need(act_p, rc * F, torch.bfloat16, "moe_mx_dgrad_fc2 act_p")
     cp, cr = prob.c(), routing.c()
     _check(lib.moe_mx_dgrad_fc2(ctypes.byref(cp), ctypes.byref(cr), _ptr(dc), _ptr(ds), _ptr(wc), _ptr(wsc), _ptr(h),
-                                _ptr(dprob), _ptr(dh), _ptr(act_p), _ptr(ws), ws.numel(), mode, _stream()),
+                                _ptr(dprob), _ptr(dh), _ptr(ws), ws.numel(), mode, _stream()),
            "moe_mx_dgrad_fc2")
-    return dprob, dh, act_p
+    return dprob, dh
 
 
 def moe_fingerprint(t: torch.Tensor, dtype: Optional[str] = None, chunk_elems: int = 65536,

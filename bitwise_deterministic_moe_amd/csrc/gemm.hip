@@ -5,12 +5,14 @@
 //                         epilogue stores h and a = relu(h)^2;
 //           fc2 forward   A = a, B = W2_g [F][D];
 //           fc2 dgrad     A = dy[row_tok], B = W2_g read as [N=F][K=D],
-//                         epilogue: dprob partial, dh, p*relu(h)^2;
+//                         epilogue: dprob partial and dh;
 //           fc1 dgrad     A = dh, B = W1_g read as [N=D][K=F].
 //  wgrad    dW_g[M, N] = sum over the expert's rows of A_row^T B_row (both
 //           operands contiguous along M/N), rows split into chunks whose size
 //           depends on shapes only:
-//           dW1 = x[row_tok]^T dh,   dW2 = (p relu(h)^2)^T dy[row_tok].
+//           dW1 = x[row_tok]^T dh,   dW2 = act_p^T dy[row_tok], where
+//           act_p = p relu(h)^2 is rebuilt from h by the weight-gradient
+//           prologue kernel.
 //
 // Expert row counts live on the device: the permute scan turns them into
 // the routing work list (row tiles longest first, weight-gradient units),
@@ -194,7 +196,7 @@ DEV void row_epilogue(const RowGemmParams& P, const RowTile& t, f32x16_t (&acc)[
     // fc2 dgrad: acc = G = dy W2^T for rows m, columns f of this N-tile.
     //   part[row][nt] = sum_f G * relu(h)^2   (fixed order: nb, i, q inside a
     //                   lane; then the lane pair; then waves wn = 0, 1, ...)
-    //   dh = (2 p G) * relu(h);   pa = p * relu(h)^2
+    //   dh = (2 p G) * relu(h)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int m = wm * WTM + mb * 32 + r32;
@@ -206,25 +208,21 @@ DEV void row_epilogue(const RowGemmParams& P, const RowTile& t, f32x16_t (&acc)[
         const int64_t col = t.n0 + wn * WTN;
         const T* hrow = (const T*)P.h + grow * P.ldh + col;
         T* drow = (T*)P.c + grow * P.ldc + col;
-        T* arow = (T*)P.c2 + grow * P.ldc2 + col;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int n = nb * 32 + 8 * i + 4 * half;
-            float hv[4], dh[4], pa[4];
+            float hv[4], dh[4];
             load4(hrow + n, hv);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const float gq = acc[mb][nb][4 * i + q];
               const float rh = relu(hv[q]);
-              const float a = rh * rh;
-              part = __builtin_fmaf(gq, a, part);
+              part = __builtin_fmaf(gq, rh * rh, part);
               dh[q] = (p2 * gq) * rh;
-              pa[q] = p * a;
             }
             store4(drow + n, dh);
-            store4(arow + n, pa);
           }
       }
       // lanes l and l^32 hold the two column halves of the same row;
@@ -445,7 +443,7 @@ static_assert(kProbOff + bf::BM * 4 <= bf::ring_bytes<kRowNS>, "epilogue scratch
 //                   4 columns in order inside a lane, a DPP butterfly over
 //                   the lane quad (16 columns), then the 16 quad sums of
 //                   the row in quad order (through LDS);
-//   dh = (2 p G) * relu(h);  act_p = p * relu(h)^2.
+//   dh = (2 p G) * relu(h).
 // h of a pass is loaded one pass ahead; the row probabilities come from
 // LDS.  lds: the main-loop ring, free (the main loop ended with a barrier).
 template <int WTM>
@@ -458,14 +456,13 @@ DEV void dgrad2_epilogue(const RowGemmParams& P, const RowTile& t, uint16_t* lds
   lds_barrier();
   HPre hpre{P, t, tid};
   HPre::Data hd[2];
-  const __amdgpu_buffer_rsrc_t rc = buf(P.c), rc2 = buf(P.c2);
+  const __amdgpu_buffer_rsrc_t rc = buf(P.c);
   staged_epilogue<WTM>(stage, acc, wm, wn, lane, tid, t.mvalid, hpre, hd, false, [&](int m, int col, float (&g)[4], HPre::Data& d, int st) {
     const bool valid = m < t.mvalid;   // uniform across the wave (one row per wave)
     if (!valid) return;
     const int64_t grow = t.off + t.m0 + m;
-    const float p = s_prob[m];
-    const float p2 = 2.f * p;
-    float hv[4], dh[4], pa[4];
+    const float p2 = 2.f * s_prob[m];
+    float hv[4], dh[4];
     hv[0] = bf16_to_f32(d.h[st][0] & 0xffffu);
     hv[1] = bf16_to_f32(d.h[st][0] >> 16);
     hv[2] = bf16_to_f32(d.h[st][1] & 0xffffu);
@@ -474,15 +471,11 @@ DEV void dgrad2_epilogue(const RowGemmParams& P, const RowTile& t, uint16_t* lds
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float rh = relu(hv[q]);
-      const float a = rh * rh;
-      part = __builtin_fmaf(g[q], a, part);
+      part = __builtin_fmaf(g[q], rh * rh, part);
       dh[q] = (p2 * g[q]) * rh;
-      pa[q] = p * a;
     }
     const uint32_t o = (uint32_t)grow * 2u * (uint32_t)P.ldc + (t.n0 + col) * 2u;
     __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(dh[0], dh[1]), pack_bf16x2(dh[2], dh[3])}, rc, o, 0, kEpiNT);
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(pa[0], pa[1]), pack_bf16x2(pa[2], pa[3])}, rc2,
-                                          (uint32_t)grow * 2u * (uint32_t)P.ldc2 + (t.n0 + col) * 2u, 0, kEpiNT);
     part = quad_sum(part);
     if ((lane & 3) == 0) s_qsum[m * 16 + (lane >> 2)] = part;
   });
@@ -663,6 +656,47 @@ DEV void wgrad_bf16_tile(const WgradParams& P, const WgradTile& t, float* dst, u
   });
 }
 
+// Ordered split-K reduction of one dW tile, run by the chunk that finishes
+// last (deterministic mode).  Every chunk of a split expert has stored its
+// partial tile (chunk 0 into dW itself, chunk s >= 1 into slot
+// first_slot + s - 1), made the stores visible at device scope and taken an
+// integer ticket for the tile; integer addition is exact, so the ticket
+// count does not depend on arrival order, and the chunk that takes the last
+// ticket adds the partials in chunk order:
+//   dW = ((part_0 + part_1) + part_2) + ... + part_{S-1}
+// Which workgroup does the adding changes nothing in the sum.  No workgroup
+// waits on another, and the tickets were zeroed by the prologue launch.
+DEV void wgrad_ordered_tail(const WgradParams& P, const WgradTile& t, int S, int first_slot, int tile, int tiles,
+                            int* s_flag) {
+  __threadfence();  // release this workgroup's partial stores
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = atomicAdd(P.tickets + (int64_t)first_slot * tiles + tile, 1);
+    s_flag[0] = old == S - 1;
+  }
+  __syncthreads();
+  if (!s_flag[0]) return;
+  __threadfence();  // acquire the other chunks' partials
+  const int64_t MN = (int64_t)P.M * P.N;
+  float* out = P.dw + (int64_t)t.g * MN;
+  const float* sl = P.slots + (int64_t)first_slot * MN;
+  // 256 x 256 floats: thread tid adds 4 consecutive columns of 64 rows
+#pragma unroll 4
+  for (int q = 0; q < 64; ++q) {
+    const int m = q * 4 + (threadIdx.x >> 6);
+    const int64_t o = (int64_t)(t.m0 + m) * P.N + t.n0 + 4 * (threadIdx.x & 63);
+    f32x4_t v = *(const f32x4_t*)(out + o);
+    for (int s = 1; s < S; ++s) {
+      const f32x4_t w = *(const f32x4_t*)(sl + (int64_t)(s - 1) * MN + o);
+      v[0] = v[0] + w[0];
+      v[1] = v[1] + w[1];
+      v[2] = v[2] + w[2];
+      v[3] = v[3] + w[3];
+    }
+    *(f32x4_t*)(out + o) = v;
+  }
+}
+
 // Unit L of one of the two weight gradients of the paired launch: tile
 // L % tiles of weight-gradient unit L / tiles of the routing work list.
 template <bool A_GATHER, bool B_GATHER>
@@ -682,6 +716,11 @@ DEV void wgrad_pair_unit(const WgradParams& P, int64_t L, int tiles, uint16_t* l
   t.n0 = (tile % nN) * bf::BN;
   float* dst = (!P.atomic && slot >= 0) ? P.slots + (int64_t)slot * P.M * P.N : P.dw + (int64_t)t.g * P.M * P.N;
   wgrad_bf16_tile<A_GATHER, B_GATHER>(P, t, dst, lds, s_rowoff);
+  if (!P.atomic && t.S > 1) {
+    const int4 ax = ((const int4*)(P.units + P.aux_at))[u];   // {S, chunk, first slot, 0}
+    wgrad_ordered_tail(P, t, __builtin_amdgcn_readfirstlane(ax.x), __builtin_amdgcn_readfirstlane(ax.z), tile,
+                       tiles, (int*)lds);
+  }
 }
 
 // Both weight gradients in one launch: units [0, U1) are dW1 tiles (rows of
@@ -993,9 +1032,16 @@ __global__ __launch_bounds__(256) void wgrad_f32_kernel(WgradParams P) {
 }
 
 // ============================================================ prep/reduce
-// Schedule for wgrad: unit_start[g] = sum_{g'<g} S_g' and slot_base[g] =
-// sum_{g'<g} (S_g' - 1), S_g = max(1, ceil(cnt_g / kc)).  Atomic mode also
-// zeroes dW of every expert that is split (S_g >= 2).
+// Prologue of moe_bwd_wgrad.
+//  * act_p = p * relu(h)^2 for every routed row r < R (R = offsets[G]), in
+//    the same float32 steps as the forward's activation: rh = max(h, 0),
+//    a = rh * rh, act_p = RNE(p * a);
+//  * block 0, float32 path only: unit_start[g] = sum_{g'<g} S_g' and
+//    slot_base[g] = sum_{g'<g} (S_g' - 1), S_g = max(1, ceil(cnt_g / kc));
+//  * the arrival tickets of the split tiles are zeroed;
+//  * atomic mode zeroes dW of every split expert (S_g >= 2), whose chunks
+//    then add into it.
+template <typename T>
 __global__ __launch_bounds__(256) void wgrad_prep_kernel(WgradPrepParams P) {
   __shared__ int s_pre[kMaxExperts + 1];
   __shared__ int s_tmp[8];
@@ -1004,12 +1050,48 @@ __global__ __launch_bounds__(256) void wgrad_prep_kernel(WgradPrepParams P) {
     const int c = P.counts[g];
     return c > P.kc ? (c + P.kc - 1) / P.kc : 1;
   };
-  if (blockIdx.x == 0) {
+  if (P.sched && blockIdx.x == 0) {
     block_exclusive_scan<256>(s_pre, s_tmp, G, nsplit);
     for (int g = threadIdx.x; g <= G; g += 256) P.sched[g] = s_pre[g];
     __syncthreads();
     block_exclusive_scan<256>(s_pre, s_tmp, G, [&](int g) { return nsplit(g) - 1; });
     for (int g = threadIdx.x; g <= G; g += 256) P.sched[G + 1 + g] = s_pre[g];
+  }
+  const int64_t gtid = (int64_t)blockIdx.x * 256 + threadIdx.x, gstride = (int64_t)gridDim.x * 256;
+  for (int64_t i = gtid; i < P.n_tickets; i += gstride) P.tickets[i] = 0;
+  // R * N elements of the storage type are below 2^31 bytes (validated on
+  // the host), so 32-bit indices suffice
+  constexpr int V = 16 / sizeof(T);
+  const int per_row = P.N / V;
+  const int nvec = P.offsets[G] * per_row;
+  for (int v = (int)gtid; v < nvec; v += (int)gstride) {
+    const int r = v / per_row;
+    const int e0 = v * V;
+    const float p = P.row_prob[r];
+    float hv[V], a[V];
+    if constexpr (sizeof(T) == 2) {
+      const u32x4_t x = __builtin_nontemporal_load((const u32x4_t*)((const uint16_t*)P.h + e0));
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        hv[2 * w] = bf16_to_f32(x[w] & 0xffffu);
+        hv[2 * w + 1] = bf16_to_f32(x[w] >> 16);
+      }
+    } else {
+      const f32x4_t x = __builtin_nontemporal_load((const f32x4_t*)((const float*)P.h + e0));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hv[q] = x[q];
+    }
+#pragma unroll
+    for (int q = 0; q < V; ++q) {
+      const float rh = relu(hv[q]);
+      a[q] = p * (rh * rh);
+    }
+    if constexpr (sizeof(T) == 2) {
+      *(u32x4_t*)((uint16_t*)P.act_p + e0) =
+          u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7])};
+    } else {
+      *(f32x4_t*)((float*)P.act_p + e0) = f32x4_t{a[0], a[1], a[2], a[3]};
+    }
   }
   if (P.atomic) {
     const int64_t per = (int64_t)P.M * P.N / 4;
@@ -1017,7 +1099,7 @@ __global__ __launch_bounds__(256) void wgrad_prep_kernel(WgradPrepParams P) {
       if (nsplit(g) < 2) continue;
       f32x4_t* d1 = (f32x4_t*)(P.dw1 + (int64_t)g * P.M * P.N);
       f32x4_t* d2 = (f32x4_t*)(P.dw2 + (int64_t)g * P.M * P.N);
-      for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < per; i += (int64_t)gridDim.x * 256) {
+      for (int64_t i = gtid; i < per; i += gstride) {
         d1[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         d2[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
@@ -1117,8 +1199,12 @@ hipError_t launch_mx_rowgemm(const RowGemmParams& P, int kind, int64_t grid, hip
   return hipGetLastError();
 }
 
-hipError_t launch_wgrad_prep(const WgradPrepParams& P, int64_t grid, hipStream_t st) {
-  wgrad_prep_kernel<<<grid, 256, 0, st>>>(P);
+hipError_t launch_wgrad_prep(const WgradPrepParams& P, bool bf16, int64_t grid, hipStream_t st) {
+  if (grid <= 0) return hipSuccess;
+  if (bf16)
+    wgrad_prep_kernel<uint16_t><<<grid, 256, 0, st>>>(P);
+  else
+    wgrad_prep_kernel<float><<<grid, 256, 0, st>>>(P);
   return hipGetLastError();
 }
 

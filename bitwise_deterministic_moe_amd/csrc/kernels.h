@@ -76,6 +76,8 @@ struct WgradParams {
   const int32_t* row_tok;
   const int32_t* units;  // routing.sched: [1] = unit count; entries at `units_at`
   int64_t units_at;
+  int64_t aux_at;        // routing.sched: {S, chunk, first slot, 0} per unit
+  int32_t* tickets;      // [wslots][tiles] arrival counters of split tiles (zeroed by the prologue)
   const int32_t* sched;  // unit_start[G+1], slot_base[G+1]
   int groups;
   int M, N;
@@ -111,9 +113,14 @@ struct RouterParams {
   uint64_t seed;
 };
 
+// Prologue of moe_bwd_wgrad (one launch): act_p = p relu(h)^2 over the
+// routed rows, the float32 path's split-K schedule (block 0, when sched is
+// set), zeroed arrival tickets, and in atomic mode zeroed dW of every split
+// expert.
 struct WgradPrepParams {
   const int32_t* counts;
-  int32_t* sched;
+  const int32_t* offsets;
+  int32_t* sched;        // float32 path: unit_start[G+1], slot_base[G+1]; else null
   int groups;
   int M, N;
   int kc;
@@ -122,6 +129,11 @@ struct WgradPrepParams {
   float* dw2;
   const float* slots1;
   const float* slots2;
+  const void* h;         // [rows_cap, N] saved pre-activation (N = F)
+  const float* row_prob;
+  void* act_p;           // [rows_cap, N] output
+  int32_t* tickets;
+  int64_t n_tickets;
 };
 
 struct RouteParams {
@@ -148,13 +160,15 @@ struct RouteParams {
   int kc;            // weight-gradient K chunk (rows)
   int64_t mt_cap;    // capacity of the row-tile list
   int64_t list2_at;  // int32 offset of the second row-tile list
+  int64_t aux_at;    // int32 offset of the weight-gradient unit side table
 };
 
 // routing.sched: [0] row tiles of bm rows, [1] weight-gradient units,
 // [2] row tiles of bm2 rows, [3] 0; then mt_cap row-tile entries {expert,
 // first row in the expert, first row overall, rows}, wu_cap weight-gradient
-// unit entries {expert | split << 30, first row, rows, partial slot or -1}
-// and mt_cap2 row-tile entries of bm2 rows, four int32 each.
+// unit entries {expert | split << 30, first row, rows, partial slot or -1},
+// mt_cap2 row-tile entries of bm2 rows, and wu_cap unit side entries
+// {S, chunk, first partial slot of the expert, 0}, four int32 each.
 constexpr int kSchedHeader = 4;
 constexpr int kRowTile2 = 192;  // bf16 fc1 dgrad row tile: two waves of 96 rows
 
@@ -164,7 +178,7 @@ hipError_t launch_permute_scatter(const RouteParams& P, hipStream_t st);
 
 hipError_t launch_rowgemm(const RowGemmParams& P, int kind, bool bf16, int64_t grid, hipStream_t st);
 hipError_t launch_wgrad(const WgradParams& P, int which, bool bf16, int64_t grid, hipStream_t st);
-hipError_t launch_wgrad_prep(const WgradPrepParams& P, int64_t grid, hipStream_t st);
+hipError_t launch_wgrad_prep(const WgradPrepParams& P, bool bf16, int64_t grid, hipStream_t st);
 hipError_t launch_wgrad_reduce(const WgradPrepParams& P, int64_t grid, hipStream_t st);
 // bf16: both weight gradients (P1: dW1, P2: dW2) in one launch, schedule computed in-kernel
 hipError_t launch_wgrad_pair(const WgradParams& P1, const WgradParams& P2, int ncu, int64_t grid, hipStream_t st);

@@ -35,6 +35,7 @@ struct Plan {
   int bm2;            // height of the second row-tile list
   int64_t mt_cap2;    // routing.sched: row-tile entries (bm2 rows)
   int64_t list2_at;   // routing.sched: int32 offset of the bm2 list
+  int64_t aux_at;     // routing.sched: int32 offset of the unit side table
   bool fc1_list2;     // the fc1 dgrad runs the bm2 list
   int64_t sched_elems;
   size_t esize;
@@ -111,7 +112,8 @@ moe_status validate(const moe_problem* p, Plan* pl) {
     pl->fc1_list2 = bf16 && mean >= 512.0;
     pl->mt_cap2 = (pl->rows_cap + pl->bm2 - 1) / pl->bm2 + pl->el;
     pl->list2_at = kSchedHeader + 4 * (pl->mt_cap + pl->wu_cap);
-    pl->sched_elems = pl->list2_at + 4 * pl->mt_cap2;
+    pl->aux_at = pl->list2_at + 4 * pl->mt_cap2;
+    pl->sched_elems = pl->aux_at + 4 * pl->wu_cap;
     pl->esize = bf16 ? 2 : 4;
   }
   return MOE_OK;
@@ -125,7 +127,8 @@ struct DgradWs {
   size_t part, dxrows, dx32, total;
 };
 struct WgradWs {
-  size_t sched, slots1, slots2, total;
+  size_t sched, slots1, slots2, tickets, actp, total;
+  int64_t n_tickets;  // per weight gradient
 };
 
 FwdWs fwd_layout(const Plan& pl, int combine, bool atomic) {
@@ -158,6 +161,10 @@ DgradWs dgrad_layout(const Plan& pl, int combine, bool atomic) {
   return w;
 }
 
+// wgrad: the float32 path's split schedule, the split-K partial slots of
+// both weight gradients (deterministic mode), the arrival tickets of split
+// tiles (deterministic bf16: one int per partial slot and 256x256 tile, per
+// weight gradient) and act_p = p relu(h)^2 [rows_cap, F].
 WgradWs wgrad_layout(const Plan& pl, bool atomic) {
   WgradWs w{};
   size_t o = 0;
@@ -168,6 +175,11 @@ WgradWs wgrad_layout(const Plan& pl, bool atomic) {
   if (!atomic) o += slot_bytes;
   w.slots2 = o;
   if (!atomic) o += slot_bytes;
+  w.n_tickets = (!atomic && pl.bf16) ? pl.wslots * (int64_t)(pl.D / pl.bm) * (pl.F / pl.bn) : 0;
+  w.tickets = o;
+  o += align_up((size_t)2 * w.n_tickets * 4);
+  w.actp = o;
+  o += align_up((size_t)pl.rows_cap * pl.F * pl.esize);
   w.total = o;
   return w;
 }
@@ -292,11 +304,12 @@ MOE_API const char* moe_stage_names(const moe_problem* p, moe_mode mode, int cal
       Plan pl;
       validate(p, &pl);
       if (!pl.bf16) {
-        if (at) return "wgrad_prep_zero,wgrad_fc1,wgrad_fc2";
-        return pl.may_split ? "wgrad_prep,wgrad_fc1,wgrad_fc2,wgrad_reduce" : "wgrad_prep,wgrad_fc1,wgrad_fc2";
+        if (at) return "wgrad_prep_act_p_zero,wgrad_fc1,wgrad_fc2";
+        return pl.may_split ? "wgrad_prep_act_p,wgrad_fc1,wgrad_fc2,wgrad_reduce"
+                            : "wgrad_prep_act_p,wgrad_fc1,wgrad_fc2";
       }
-      if (at) return pl.may_split ? "wgrad_prep_zero,wgrad_fc1_fc2" : "wgrad_fc1_fc2";
-      return pl.may_split ? "wgrad_fc1_fc2,wgrad_reduce" : "wgrad_fc1_fc2";
+      if (at) return "wgrad_prep_act_p_zero,wgrad_fc1_fc2";
+      return "wgrad_prep_act_p,wgrad_fc1_fc2_ordered";
     }
   }
   return nullptr;
@@ -345,6 +358,7 @@ MOE_API moe_status moe_fwd(const moe_problem* p, const float* logits, const void
   R.bm = pl.bm;
   R.bm2 = pl.bm2;
   R.list2_at = pl.list2_at;
+  R.aux_at = pl.aux_at;
   R.kc = pl.kc;
   R.mt_cap = pl.mt_cap;
   R.nchunk = pl.nchunk;
@@ -422,23 +436,49 @@ MOE_API moe_status moe_fwd(const moe_problem* p, const float* logits, const void
   return sg.err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* routing, const void* dy,
-                                       const void* w1, const void* w2, const void* h, void* dx_or_rows,
-                                       float* dprob, void* dh, void* act_p, void* ws, size_t ws_bytes,
-                                       moe_mode mode, void* stream) {
-  Plan pl;
-  moe_status s = validate(p, &pl);
+namespace {
+
+// Argument checks of moe_bwd_dgrad_dprob (and its no-allocation variant),
+// before the workspace is known.
+moe_status dgrad_check(const moe_problem* p, Plan* pl, const moe_routing* routing, const void* dy, const void* w1,
+                       const void* w2, const void* h, void* dx_or_rows, float* dprob, void* dh, moe_mode mode) {
+  moe_status s = validate(p, pl);
   if (s != MOE_OK) return s;
   if (mode != MOE_DETERMINISTIC && mode != MOE_ATOMIC) return MOE_ERR_MODE;
-  const bool at = mode == MOE_ATOMIC;
-  const bool has_tok = pl.T > 0, has_rows = pl.rows_cap > 0;
+  const bool has_tok = pl->T > 0, has_rows = pl->rows_cap > 0;
   if (!routing || !w1 || !w2 || !routing->counts || !routing->offsets || !routing->sched) return MOE_ERR_NULL;
   if (has_tok && (!dy || !dx_or_rows || !dprob || !routing->slot_row || !routing->topk_prob)) return MOE_ERR_NULL;
-  if (has_rows && (!h || !dh || !act_p || !routing->row_src || !routing->row_tok || !routing->row_prob))
+  if (has_rows && (!h || !dh || !routing->row_src || !routing->row_tok || !routing->row_prob))
     return MOE_ERR_NULL;
-  const DgradWs L = dgrad_layout(pl, p->combine, at);
-  s = check_ws(ws, ws_bytes, L.total);
+  return MOE_OK;
+}
+
+// The launch sequence of moe_bwd_dgrad_dprob on a checked problem and a
+// workspace of at least dgrad_layout(...).total bytes.
+moe_status dgrad_enqueue(const moe_problem* p, const Plan& pl, const moe_routing* routing, const void* dy,
+                         const void* w1, const void* w2, const void* h, void* dx_or_rows, float* dprob, void* dh,
+                         void* ws, moe_mode mode, void* stream);
+
+}  // namespace
+
+MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* routing, const void* dy,
+                                       const void* w1, const void* w2, const void* h, void* dx_or_rows,
+                                       float* dprob, void* dh, void* ws, size_t ws_bytes, moe_mode mode,
+                                       void* stream) {
+  Plan pl;
+  moe_status s = dgrad_check(p, &pl, routing, dy, w1, w2, h, dx_or_rows, dprob, dh, mode);
   if (s != MOE_OK) return s;
+  s = check_ws(ws, ws_bytes, dgrad_layout(pl, p->combine, mode == MOE_ATOMIC).total);
+  if (s != MOE_OK) return s;
+  return dgrad_enqueue(p, pl, routing, dy, w1, w2, h, dx_or_rows, dprob, dh, ws, mode, stream);
+}
+
+namespace {
+moe_status dgrad_enqueue(const moe_problem* p, const Plan& pl, const moe_routing* routing, const void* dy,
+                         const void* w1, const void* w2, const void* h, void* dx_or_rows, float* dprob, void* dh,
+                         void* ws, moe_mode mode, void* stream) {
+  const bool at = mode == MOE_ATOMIC;
+  const DgradWs L = dgrad_layout(pl, p->combine, at);
   hipStream_t st = (hipStream_t)stream;
   char* wsb = (char*)ws;
   const uint64_t seed = p->debug_shuffle_seed;
@@ -474,8 +514,6 @@ MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* 
   G.b_bytes = (uint32_t)(G.b_gstride * pl.esize);
   G.c = dh;
   G.ldc = pl.F;
-  G.c2 = act_p;
-  G.ldc2 = pl.F;
   G.h = h;
   G.ldh = pl.F;
   G.row_prob = routing->row_prob;
@@ -539,9 +577,10 @@ MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* 
   sg.mark();
   return sg.err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
+}  // namespace
 
 MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routing, const void* x,
-                                 const void* dy, const void* dh, const void* act_p, float* dw1, float* dw2,
+                                 const void* dy, const void* h, const void* dh, float* dw1, float* dw2,
                                  void* ws, size_t ws_bytes, moe_mode mode, void* stream) {
   Plan pl;
   moe_status s = validate(p, &pl);
@@ -551,7 +590,7 @@ MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routin
   const bool has_tok = pl.T > 0, has_rows = pl.rows_cap > 0;
   if (!routing || !dw1 || !dw2 || !routing->counts || !routing->offsets || !routing->sched) return MOE_ERR_NULL;
   if (has_tok && (!x || !dy)) return MOE_ERR_NULL;
-  if (has_rows && (!dh || !act_p || !routing->row_tok)) return MOE_ERR_NULL;
+  if (has_rows && (!h || !dh || !routing->row_tok || !routing->row_prob)) return MOE_ERR_NULL;
   const WgradWs L = wgrad_layout(pl, at);
   s = check_ws(ws, ws_bytes, L.total);
   if (s != MOE_OK) return s;
@@ -562,19 +601,27 @@ MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routin
   int32_t* sched = (int32_t*)(wsb + L.sched);
   float* slots1 = (float*)(wsb + L.slots1);
   float* slots2 = (float*)(wsb + L.slots2);
+  int32_t* tickets = (int32_t*)(wsb + L.tickets);
+  void* act_p = wsb + L.actp;
 
   WgradPrepParams Q{};
   Q.counts = routing->counts;
-  Q.sched = sched;
+  Q.offsets = routing->offsets;
+  Q.sched = pl.bf16 ? nullptr : sched;
   Q.groups = pl.el;
   Q.M = pl.D;
   Q.N = pl.F;
   Q.kc = pl.kc;
-  Q.atomic = at;
+  Q.atomic = at && pl.may_split;
   Q.dw1 = dw1;
   Q.dw2 = dw2;
   Q.slots1 = slots1;
   Q.slots2 = slots2;
+  Q.h = h;
+  Q.row_prob = routing->row_prob;
+  Q.act_p = act_p;
+  Q.tickets = tickets;
+  Q.n_tickets = 2 * L.n_tickets;
 
   WgradParams W1{};
   W1.counts = routing->counts;
@@ -582,6 +629,7 @@ MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routin
   W1.row_tok = routing->row_tok;
   W1.units = routing->sched;
   W1.units_at = kSchedHeader + 4 * pl.mt_cap;
+  W1.aux_at = pl.aux_at;
   W1.sched = sched;
   W1.groups = pl.el;
   W1.kc = pl.kc;
@@ -601,7 +649,8 @@ MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routin
   W1.b_bytes = rows_f_bytes;
   W1.dw = dw1;
   W1.slots = slots1;
-  // dW2_g [F][D] = (p relu(h)^2)^T dy[row_tok]
+  W1.tickets = tickets;
+  // dW2_g [F][D] = act_p^T dy[row_tok], act_p = p relu(h)^2 from the prologue
   W2.M = pl.F;
   W2.N = pl.D;
   W2.a = act_p;
@@ -612,27 +661,30 @@ MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routin
   W2.b_bytes = tok_d_bytes;
   W2.dw = dw2;
   W2.slots = slots2;
+  W2.tickets = tickets + L.n_tickets;
 
+  // prologue grid: one 16-byte vector of act_p per thread and iteration
+  const int64_t nvec = pl.rows_cap * pl.F / (pl.bf16 ? 8 : 4);
+  int64_t pgrid = (nvec + 255) / 256;
+  if (pgrid > 8192) pgrid = 8192;
+  if (pgrid < 1) pgrid = 1;
+  sg.mark();
+  HIP_TRY(launch_wgrad_prep(Q, pl.bf16, pgrid, st));
   if (pl.bf16) {
-    // atomic mode zeroes dW of split experts before their chunks add into it
-    if (at && pl.may_split) {
-      sg.mark();
-      HIP_TRY(launch_wgrad_prep(Q, 1024, st));
-    }
+    // both weight gradients in one launch; split tiles are reduced in chunk
+    // order by the chunk that finishes last (deterministic mode)
     const int64_t units = (int64_t)(pl.el + pl.wslots) * (pl.D / pl.bm) * (pl.F / pl.bn);
     sg.mark();
     HIP_TRY(launch_wgrad_pair(W1, W2, device_cu_count(), grid_for_unit_rounds(2 * units), st));
   } else {
     sg.mark();
-    HIP_TRY(launch_wgrad_prep(Q, at ? 1024 : 1, st));
-    sg.mark();
     HIP_TRY(launch_wgrad(W1, 1, pl.bf16, wgrad_grid(pl, pl.D, pl.F), st));
     sg.mark();
     HIP_TRY(launch_wgrad(W2, 2, pl.bf16, wgrad_grid(pl, pl.F, pl.D), st));
-  }
-  if (!at && pl.may_split) {
-    sg.mark();
-    HIP_TRY(launch_wgrad_reduce(Q, 1024, st));
+    if (!at && pl.may_split) {
+      sg.mark();
+      HIP_TRY(launch_wgrad_reduce(Q, 1024, st));
+    }
   }
   sg.mark();
   return sg.err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
@@ -766,7 +818,7 @@ MOE_API moe_status moe_mx_dgrad_fc1(const moe_problem* p, const moe_routing* rou
 
 MOE_API moe_status moe_mx_dgrad_fc2(const moe_problem* p, const moe_routing* routing, const uint8_t* dy_codes,
                                     const uint8_t* dy_scales, const uint8_t* w2_codes, const uint8_t* w2_scales,
-                                    const void* h, float* dprob, void* dh, void* act_p, void* ws, size_t ws_bytes,
+                                    const void* h, float* dprob, void* dh, void* ws, size_t ws_bytes,
                                     moe_mode mode, void* stream) {
   Plan pl;
   moe_status s = validate(p, &pl);
@@ -777,7 +829,7 @@ MOE_API moe_status moe_mx_dgrad_fc2(const moe_problem* p, const moe_routing* rou
   const bool at = mode == MOE_ATOMIC;
   if (!routing || !routing->counts || !routing->offsets || !routing->sched) return MOE_ERR_NULL;
   if (pl.T > 0 && (!dy_codes || !dy_scales || !dprob || !routing->slot_row)) return MOE_ERR_NULL;
-  if (pl.rows_cap > 0 && (!w2_codes || !w2_scales || !h || !dh || !act_p || !routing->row_src ||
+  if (pl.rows_cap > 0 && (!w2_codes || !w2_scales || !h || !dh || !routing->row_src ||
                           !routing->row_tok || !routing->row_prob))
     return MOE_ERR_NULL;
   // the partials region of the dgrad workspace (same layout as moe_bwd_dgrad_dprob)
@@ -813,8 +865,6 @@ MOE_API moe_status moe_mx_dgrad_fc2(const moe_problem* p, const moe_routing* rou
   G.b_sgstride = (int64_t)pl.F * (pl.D / 32);
   G.c = dh;
   G.ldc = pl.F;
-  G.c2 = act_p;
-  G.ldc2 = pl.F;
   G.h = h;
   G.ldh = pl.F;
   G.row_prob = routing->row_prob;

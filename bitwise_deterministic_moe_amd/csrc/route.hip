@@ -148,7 +148,8 @@ DEV int row_tile_list(const RouteParams& P, int4* mt, int BM, const int* s_cnt, 
 //   units leaves the smallest tiles for its last round;
 //   weight-gradient units: expert g in S_g = max(1, ceil(cnt_g / kc)) chunks,
 //   chunk s covering rows [s cnt/S, (s+1) cnt/S); chunks s >= 1 of a split
-//   expert own partial slot sum_{g'<g} (S_g' - 1) + s - 1.
+//   expert own partial slot sum_{g'<g} (S_g' - 1) + s - 1; the side table
+//   holds {S_g, s, sum_{g'<g} (S_g' - 1), 0} for the ordered reduction.
 __global__ __launch_bounds__(1024) void permute_scan_kernel(RouteParams P) {
   __shared__ int s_pre[kMaxExperts + 1];
   __shared__ int s_tmp[16];
@@ -196,10 +197,12 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(RouteParams P) {
   block_exclusive_scan<1024>(s_pre, s_tmp, P.el, [&](int g) { return nsplit(g) - 1; });
   if (e < P.el) {
     int4* wu = (int4*)(P.sched + kSchedHeader) + P.mt_cap;
+    int4* aux = (int4*)(P.sched + P.aux_at);
     const int S = nsplit(e);
     for (int sc = 0; sc < S; ++sc) {
       const int lo = (int)((int64_t)sc * total / S), hi = (int)((int64_t)(sc + 1) * total / S);
       wu[ubase + sc] = int4{e | (S > 1 ? 1 << 30 : 0), off_e + lo, hi - lo, sc > 0 ? s_pre[e] + sc - 1 : -1};
+      aux[ubase + sc] = int4{S, sc, s_pre[e], 0};
     }
   }
   if (e == 0) P.sched[1] = nunits;

@@ -20,8 +20,8 @@ One train step on the layer (all device work through the library's C ABI):
     logits = moe_router_fwd(x, wr)              router (linear, no bias)
     routing, h, y = moe_fwd(logits, x, W1, W2)
     loss = sum_t <dy_t, y_t>                    (dy: the step's batch)
-    dx, dprob, dh, act_p = moe_bwd_dgrad_dprob(dy)
-    dW1, dW2 = moe_bwd_wgrad(...)
+    dx, dprob, dh = moe_bwd_dgrad_dprob(dy)
+    dW1, dW2 = moe_bwd_wgrad(x, dy, h, dh)
     dlogits, dwr, dx_router = moe_router_bwd(dprob)
     SGD on the float32 masters of W1, W2, wr; bf16 (or f32) runtime copies
     rebuilt by the same kernel (moe_sgd_step).
@@ -71,7 +71,7 @@ class Tracer:
     """Ordered log of fingerprints.  ``level``: "metrics" (loss and gradient
     norms per step), "phases" (also every call's outputs at phase level: the
     tensors that leave forward, backward, router and optimizer) or "ops"
-    (also the intermediate tensors of each call: routing maps, h, dh, act_p,
+    (also the intermediate tensors of each call: routing maps, h, dh,
     dlogits ...).  ``window``: steps traced above metric level (None = all)."""
 
     def __init__(self, level: str = "phases", window: Optional[range] = None):
@@ -204,13 +204,13 @@ def train_step(cfg, st: TrainState, tracer: Tracer, hook: Optional[Callable] = N
         el, D, F = cfg.num_local, cfg.d_model, cfg.d_ffn
         enc["dy"], enc["w2"] = _mx(dy, cfg.tokens, D), _mx(R["w2"], el * F, D)
         w2mx = (enc["w2"][0].reshape(el, F, D), enc["w2"][1].reshape(el, F, D // 32))
-        dprob, dh, act_p = moe_mx_dgrad_fc2(prob, routing, enc["dy"], w2mx, h)
+        dprob, dh = moe_mx_dgrad_fc2(prob, routing, enc["dy"], w2mx, h)
         enc["dh"], enc["w1"] = _mx(dh, prob.rows_cap, F), _mx(R["w1"], el * D, F)
         w1mx = (enc["w1"][0].reshape(el, D, F), enc["w1"][1].reshape(el, D, F // 32))
         dx = moe_mx_dgrad_fc1(prob, routing, enc["dh"], w1mx)     # per routed row
     else:
-        dx, dprob, dh, act_p = moe_bwd_dgrad_dprob(prob, routing, dy, R["w1"], R["w2"], h)
-    dw1, dw2 = moe_bwd_wgrad(prob, routing, x, dy, dh, act_p)
+        dx, dprob, dh = moe_bwd_dgrad_dprob(prob, routing, dy, R["w1"], R["w2"], h)
+    dw1, dw2 = moe_bwd_wgrad(prob, routing, x, dy, h, dh)
     dlogits, dwr, dxr = moe_router_bwd(prob, routing, dprob, x, R["wr"])
     torch.cuda.synchronize()
 
@@ -228,7 +228,6 @@ def train_step(cfg, st: TrainState, tracer: Tracer, hook: Optional[Callable] = N
             T.tensor(s, "backward", "moe_mx_quantize", f"{n}_scales", enc[n][1], 2)
         T.tensor(s, "backward", "moe_mx_dgrad_fc2", "dprob", dprob, 1)
         T.tensor(s, "backward", "moe_mx_dgrad_fc2", "dh", dh, 2)
-        T.tensor(s, "backward", "moe_mx_dgrad_fc2", "act_p", act_p, 2)
         for n in ("dh", "w1"):
             T.tensor(s, "backward", "moe_mx_quantize", f"{n}_codes", enc[n][0], 2)
             T.tensor(s, "backward", "moe_mx_quantize", f"{n}_scales", enc[n][1], 2)
@@ -239,7 +238,6 @@ def train_step(cfg, st: TrainState, tracer: Tracer, hook: Optional[Callable] = N
     else:
         T.tensor(s, "backward", "moe_bwd_dgrad_dprob", "dprob", dprob, 1)
         T.tensor(s, "backward", "moe_bwd_dgrad_dprob", "dh", dh, 2)
-        T.tensor(s, "backward", "moe_bwd_dgrad_dprob", "act_p", act_p, 2)
         T.tensor(s, "backward", "moe_bwd_dgrad_dprob", "dx", dx, 1)
     T.tensor(s, "backward", "moe_bwd_wgrad", "dw1", dw1, 1)
     T.tensor(s, "backward", "moe_bwd_wgrad", "dw2", dw2, 1)

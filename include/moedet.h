@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -171,7 +171,14 @@ moe_status moe_rows_cap(const moe_problem* p, int64_t* rows_cap);
 moe_status moe_sched_elems(const moe_problem* p, int64_t* elems);
 
 /* Workspace bytes needed by each call for problem p in `mode` (upper bounds
- * from shapes only).  Any of the output pointers may be NULL. */
+ * from shapes only; no routing is read and nothing is enqueued).  The pages
+ * describe no interface; the regions are this library's: routing histograms
+ * and activation rows (fwd); the per-(row, N-tile) dprob partials, which are
+ * the private output slots of the fix the English digest describes
+ * ("Interpretation"), and the dx rows (dgrad); the split-K partial slots,
+ * their arrival tickets and act_p = p relu(h)^2 (wgrad).  Any of the output
+ * pointers may be NULL.  Errors: those of the problem's validation
+ * (MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_MODE). */
 moe_status moe_workspace_size(const moe_problem* p, moe_mode mode, size_t* fwd_bytes,
                               size_t* dgrad_bytes, size_t* wgrad_bytes);
 
@@ -181,7 +188,17 @@ moe_status moe_workspace_size(const moe_problem* p, moe_mode mode, size_t* fwd_b
 const char* moe_stage_names(const moe_problem* p, moe_mode mode, int call);
 
 /* Forward: routing, stable permute, expert MLP and (combine=1) weighted
- * combine.
+ * combine.  It produces the routing state and the saved activation that the
+ * backward calls read.  Sources: the expert shapes follow the LatentMoE
+ * description of the Nemotron 3 Ultra notes (section of concepts: a
+ * 2048-wide latent, 512 experts, 22 selected); the combine is a gather over
+ * the k slots in a fixed order, the reduction-order rule of the English
+ * digest ("Interpretation") applied to the top-k combine.  The router's
+ * tie-break, the softmax over the selected logits and the ReLU^2 expert MLP
+ * are this library's readings (the pages state none of them).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_MODE,
+ * MOE_ERR_WORKSPACE before anything is enqueued; MOE_ERR_HIP for a launch
+ * failure.
  *   logits     [T,E] float32
  *   x          [T,D] dtype
  *   w1         [El,D,F] dtype (local experts in order)
@@ -198,9 +215,17 @@ moe_status moe_fwd(const moe_problem* p, const float* logits, const void* x, con
                    void* ws, size_t ws_bytes, moe_mode mode, void* stream);
 
 /* Backward, data path: fc2 dgrad with the dprob epilogue, fc1 dgrad and the
- * dx combine.
+ * dx combine.  This is the site of the fault and the fix in the English
+ * digest ("Interpretation"): in the grouped-GEMM epilogue several N-tiles
+ * added into the same dprob[token] address in arrival order; here every
+ * N-tile writes a private float32 slot and the slots are combined in a fixed
+ * order once all writers have finished (also the French article,
+ * "Optimisation pour le Nemotron à mille milliards de paramètres": private
+ * output slots for the grouped-GEMM writers).  The dx combine gathers the k
+ * slots in a fixed order instead of scatter-adding.
  *   dy         [T,D] dtype upstream gradient of y (token layout also for the
  *              shard: row r reads dy[row_tok[r]])
+ *   w1, w2     [El,D,F], [El,F,D] dtype, as given to moe_fwd
  *   h          [rows_cap,F] saved pre-activation from moe_fwd
  *   dx_or_rows combine=1: [T,D] dx_t = sum_j dx_(t,j), slots ascending;
  *              combine=0: [rows_cap,D] per-row dx
@@ -211,24 +236,41 @@ moe_status moe_fwd(const moe_problem* p, const float* logits, const void* x, con
  *              adds its partial atomically.
  *   dh         [rows_cap,F] dtype output, p * (dy W2^T) * 2 relu(h); input of
  *              moe_bwd_wgrad
- *   act_p      [rows_cap,F] dtype output, p * relu(h)^2 recomputed from h in
- *              the same epilogue; input of moe_bwd_wgrad */
+ *   ws         workspace of at least moe_workspace_size(...).dgrad_bytes
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_MODE,
+ * MOE_ERR_WORKSPACE before anything is enqueued; MOE_ERR_HIP for a launch
+ * failure. */
 moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* routing, const void* dy,
                                const void* w1, const void* w2, const void* h, void* dx_or_rows,
-                               float* dprob, void* dh, void* act_p, void* ws, size_t ws_bytes,
-                               moe_mode mode, void* stream);
+                               float* dprob, void* dh, void* ws, size_t ws_bytes, moe_mode mode,
+                               void* stream);
 
 /* Backward, weight gradients (float32 outputs, exact zeros for experts
- * without rows), from the outputs of moe_bwd_dgrad_dprob:
+ * without rows):
  *   dw1 [El,D,F] = sum over the expert's rows of x_row^T dh_row
- *   dw2 [El,F,D] = sum over the expert's rows of act_p_row^T dy_row
- *                  (act_p = p * relu(h)^2)
- * An expert with many rows is split along its rows into chunks whose size is
- * a function of the problem shapes only.  MOE_DETERMINISTIC: the chunk
- * partials go to the workspace and are added in chunk order.  MOE_ATOMIC:
- * they are added atomically. */
+ *   dw2 [El,F,D] = sum over the expert's rows of act_p_row^T dy_row,
+ *                  act_p = p * relu(h)^2, rebuilt from h into the workspace
+ *                  by the call's first kernel
+ * The pages name the weight-gradient path as one of the deterministic
+ * paths that were optimised (English digest, "Interpretation"; French
+ * article, "Optimisation pour le Nemotron à mille milliards de
+ * paramètres"), and their rule -- a fixed reduction order -- is applied here
+ * to the split-K sum.  An expert with many rows is split along its rows into
+ * chunks whose size is a function of the problem shapes only.
+ * MOE_DETERMINISTIC: chunk 0 stores its partial into dW, the other chunks
+ * into workspace slots, and the chunk that finishes last (an integer ticket
+ * per tile) adds them in chunk order, ((p0 + p1) + p2) + ...; which chunk
+ * does the adding does not change the bits.  MOE_ATOMIC: the chunks are
+ * added atomically into a zeroed dW.
+ *   x, dy      [T,D] dtype (the layer input and the upstream gradient)
+ *   h          [rows_cap,F] saved pre-activation from moe_fwd
+ *   dh         [rows_cap,F] from moe_bwd_dgrad_dprob
+ *   ws         workspace of at least moe_workspace_size(...).wgrad_bytes
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_MODE,
+ * MOE_ERR_WORKSPACE before anything is enqueued; MOE_ERR_HIP for a launch
+ * failure. */
 moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routing, const void* x,
-                         const void* dy, const void* dh, const void* act_p, float* dw1, float* dw2,
+                         const void* dy, const void* h, const void* dh, float* dw1, float* dw2,
                          void* ws, size_t ws_bytes, moe_mode mode, void* stream);
 
 /* Chunk-wise tensor fingerprint (integer arithmetic; bit-exact).
@@ -325,8 +367,7 @@ moe_status moe_mx_dgrad_fc1(const moe_problem* p, const moe_routing* routing, co
  *              (64 k per scaled MFMA, slices ascending);
  *   dprob[t, j] = sum_f G[r, f] relu(h[r, f])^2 for the row r of slot (t, j)
  *              (0 for slots routed to non-local experts);
- *   dh[r, :]    = bf16(2 p_r G[r, :] relu(h[r, :]));
- *   act_p[r, :] = bf16(p_r relu(h[r, :])^2)   (p_r = the row's topk_prob).
+ *   dh[r, :]    = bf16(2 p_r G[r, :] relu(h[r, :]))   (p_r = the row's topk_prob).
  * This is the layer backward of moe_bwd_dgrad_dprob with dy and W2 replaced
  * by their MXFP8 values; the pages name MXFP8 runs and fingerprint their
  * encoded values and scale buffers (French article, section "Méthodologie de
@@ -336,7 +377,7 @@ moe_status moe_mx_dgrad_fc1(const moe_problem* p, const moe_routing* routing, co
  *                         (moe_mx_quantize of W2 viewed as [num_local*F, D])
  *   h                     DEVICE bf16 [rows_cap, F], as saved by moe_fwd
  *   dprob                 DEVICE float32 [T, k] output
- *   dh, act_p             DEVICE bf16 [rows_cap, F] outputs; rows < R written
+ *   dh                    DEVICE bf16 [rows_cap, F] output; rows < R written
  *   ws, ws_bytes          the dgrad workspace of moe_workspace_size (mode)
  *   mode                  MOE_DETERMINISTIC: per-(row, N-tile) partials in the
  *                         workspace, then the fixed-tree combine of
@@ -348,7 +389,7 @@ moe_status moe_mx_dgrad_fc1(const moe_problem* p, const moe_routing* routing, co
  * is enqueued; MOE_ERR_HIP for a launch failure. */
 moe_status moe_mx_dgrad_fc2(const moe_problem* p, const moe_routing* routing, const uint8_t* dy_codes,
                             const uint8_t* dy_scales, const uint8_t* w2_codes, const uint8_t* w2_scales,
-                            const void* h, float* dprob, void* dh, void* act_p, void* ws, size_t ws_bytes,
+                            const void* h, float* dprob, void* dh, void* ws, size_t ws_bytes,
                             moe_mode mode, void* stream);
 
 /* Router forward for a train step of the layer: logits[t,e] = sum over d

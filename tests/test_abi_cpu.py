@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert names == set(moe.EXPORTED_SYMBOLS)
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -80,11 +80,14 @@ def test_null_and_workspace_errors_return_before_enqueue(lib):
     # misaligned workspace
     assert lib.moe_bwd_wgrad(ctypes.byref(cp), ctypes.byref(r), fake, fake, fake, fake, fake, fake,
                              ctypes.c_void_p(0x1008), 1 << 40, 0, None) == 4
-    assert lib.moe_bwd_dgrad_dprob(None, ctypes.byref(r), fake, fake, fake, fake, fake, fake, fake, fake, fake, 0,
+    assert lib.moe_bwd_dgrad_dprob(None, ctypes.byref(r), fake, fake, fake, fake, fake, fake, fake, fake, 0,
                                    0, None) == 1
-    # NULL act_p
-    assert lib.moe_bwd_dgrad_dprob(ctypes.byref(cp), ctypes.byref(r), fake, fake, fake, fake, fake, fake, fake, None,
+    # NULL dh
+    assert lib.moe_bwd_dgrad_dprob(ctypes.byref(cp), ctypes.byref(r), fake, fake, fake, fake, fake, fake, None,
                                    fake, 1 << 40, 0, None) == 1
+    # NULL h for the weight gradients
+    assert lib.moe_bwd_wgrad(ctypes.byref(cp), ctypes.byref(r), fake, fake, None, fake, fake, fake, fake, 1 << 40, 0,
+                             None) == 1
     # fingerprint argument checks
     shape = (ctypes.c_int64 * 1)(10)
     assert lib.moe_fingerprint(fake, 9, 1, shape, 4, fake, fake, None) == 3
@@ -100,30 +103,37 @@ def test_workspace_sizes_and_rows_cap():
     # dprob partials: rows_cap x (F / 256) floats
     assert dg >= 8192 * 8 * 4
     fa, da, wa = moe.moe_workspace_size(p, moe.ATOMIC)
-    # chunk 4 * mean rows = 4096 >= tokens: no expert can split, no partial slots
+    # chunk 4 * mean rows = 4096 >= tokens: no expert can split, no partial
+    # slots; both modes hold act_p [rows_cap, F] bf16
     assert wa == wg and da >= 4096 * 1024 * 4
-    assert moe.moe_stage_names(p, 0, 2) == ["wgrad_fc1_fc2"]
+    assert wg >= 8192 * 2048 * 2
+    assert moe.moe_stage_names(p, 0, 2) == ["wgrad_prep_act_p", "wgrad_fc1_fc2_ordered"]
     # 512 experts top-22: 32768 weight-gradient tiles, so no expert is split
     # (chunk 4096 = tokens): no slots, no ordered reduction
     latent = moe.Problem(4096, 2048, 2048, 512, 22)
     _, _, wl = moe.moe_workspace_size(latent, moe.DETERMINISTIC)
     _, _, wla = moe.moe_workspace_size(latent, moe.ATOMIC)
     assert wl == wla
-    assert moe.moe_stage_names(latent, 0, 2) == ["wgrad_fc1_fc2"]
-    assert moe.moe_stage_names(latent, 1, 2) == ["wgrad_fc1_fc2"]
+    assert moe.moe_stage_names(latent, 0, 2) == ["wgrad_prep_act_p", "wgrad_fc1_fc2_ordered"]
+    assert moe.moe_stage_names(latent, 1, 2) == ["wgrad_prep_act_p_zero", "wgrad_fc1_fc2"]
     # 8 experts, 16384 tokens top-2: 128 tiles, chunk 4096 < tokens: split
     # slots (rows_cap / chunk = 8 per weight gradient) in the deterministic workspace
     wide = moe.Problem(16384, 1024, 1024, 8, 2)
     _, _, ww = moe.moe_workspace_size(wide, moe.DETERMINISTIC)
     _, _, wwa = moe.moe_workspace_size(wide, moe.ATOMIC)
     assert ww - wwa >= 2 * 8 * 1024 * 1024 * 4
-    assert moe.moe_stage_names(wide, 0, 2) == ["wgrad_fc1_fc2", "wgrad_reduce"]
-    assert moe.moe_stage_names(wide, 1, 2) == ["wgrad_prep_zero", "wgrad_fc1_fc2"]
+    # the ordered reduction rides in the pair launch: the same two launches
+    # in both modes
+    assert moe.moe_stage_names(wide, 0, 2) == ["wgrad_prep_act_p", "wgrad_fc1_fc2_ordered"]
+    assert moe.moe_stage_names(wide, 1, 2) == ["wgrad_prep_act_p_zero", "wgrad_fc1_fc2"]
+    # the float32 path keeps its separate ordered reduction
+    wide32 = moe.Problem(16384, 64, 64, 8, 2, dtype="f32")
+    assert moe.moe_stage_names(wide32, 0, 2) == ["wgrad_prep_act_p", "wgrad_fc1", "wgrad_fc2", "wgrad_reduce"]
     shard = moe.Problem(16384, 2048, 2048, 512, 22, 0, 4, "bf16", 0)
     assert moe.moe_rows_cap(shard) == 16384 * 4
     assert moe.moe_stage_names(p, 0, 1) == ["fc2_dgrad_dprob_partials", "fc1_dgrad_dprob_combine",
                                             "dx_combine_gather"]
-    assert moe.moe_stage_names(p, 1, 2) == ["wgrad_fc1_fc2"]
+    assert moe.moe_stage_names(p, 1, 2) == ["wgrad_prep_act_p_zero", "wgrad_fc1_fc2"]
 
 
 def test_mfma_rate_validation_returns_before_enqueue(lib):
@@ -193,7 +203,7 @@ def test_mx_dgrad_fc2_validation_returns_before_enqueue(lib):
 
     def call(prob, dy=fake, mode=0, ws=ctypes.c_void_p(0x100000), ws_bytes=1 << 40):
         return lib.moe_mx_dgrad_fc2(ctypes.byref(prob), ctypes.byref(r), dy, fake, fake, fake, fake, fake, fake,
-                                    fake, ws, ws_bytes, mode, None)
+                                    ws, ws_bytes, mode, None)
     assert call(moe.Problem(**{**BASE, "d_model": 4096}).c()) == 2        # D beyond the staged scales
     assert call(moe.Problem(**{**BASE, "dtype": "f32"}).c()) == 3
     assert call(cp, mode=7) == 5

@@ -130,14 +130,13 @@ def _fc2_oracle(cfg, di, h_bits):
 def test_mx_dgrad_fc2_parity(name, mode):
     print(f"mx dgrad fc2 {name} mode {mode}", flush=True)
     cfg, di, prob, routing, h_bits, h, dymx, w2mx = _fc2_case(name)
-    dprob, dh, act_p = moe.moe_mx_dgrad_fc2(prob, routing, dymx, w2mx, h, mode)
+    dprob, dh = moe.moe_mx_dgrad_fc2(prob, routing, dymx, w2mx, h, mode)
     torch.cuda.synchronize()
     R, ref = _fc2_oracle(cfg, di, h_bits)
     e_dprob = rel_l2(dprob.cpu().numpy(), ref["dprob"])
     e_dh = rel_l2(to_host(dh[:R]), ref["dh"])
-    e_ap = rel_l2(to_host(act_p[:R]), ref["act_p"])
-    print(f"  rel-L2 dprob {e_dprob:.3e} dh {e_dh:.3e} act_p {e_ap:.3e}", flush=True)
-    assert e_dh <= 2e-2 and e_ap <= 2e-2
+    print(f"  rel-L2 dprob {e_dprob:.3e} dh {e_dh:.3e}", flush=True)
+    assert e_dh <= 2e-2
     assert e_dprob <= MX_DPROB_TOL
     err = np.abs(dprob.cpu().numpy().astype(np.float64).ravel() - ref["dprob"].ravel())
     assert np.all(err <= MX_TERM_BOUND * ref["dprob_mag"] + 1e-30), float(np.max(err / (ref["dprob_mag"] + 1e-30)))
@@ -151,7 +150,7 @@ def test_mx_dgrad_fc2_bits_identical_under_shuffles():
     R = routing.rows
     ref = None
     for seed in (0, 3, 0xBEEF):
-        dprob, dh, act_p = moe.moe_mx_dgrad_fc2(prob.with_seed(seed), routing, dymx, w2mx, h)
-        fps = tuple(moe.moe_fingerprint(t.contiguous())[1] for t in (dprob, dh[:R], act_p[:R]))
+        dprob, dh = moe.moe_mx_dgrad_fc2(prob.with_seed(seed), routing, dymx, w2mx, h)
+        fps = tuple(moe.moe_fingerprint(t.contiguous())[1] for t in (dprob, dh[:R]))
         ref = fps if ref is None else ref
         assert fps == ref, seed

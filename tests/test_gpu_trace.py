@@ -106,8 +106,8 @@ def test_one_step_against_the_oracle():
     R = st.runtime
     logits = moe.moe_router_fwd(prob, x, R["wr"])
     routing, h, _ = moe.moe_fwd(prob, logits, x, R["w1"], R["w2"])
-    _, dprob, dh, act_p = moe.moe_bwd_dgrad_dprob(prob, routing, dy, R["w1"], R["w2"], h)
-    dw1, dw2 = moe.moe_bwd_wgrad(prob, routing, x, dy, dh, act_p)
+    _, dprob, dh = moe.moe_bwd_dgrad_dprob(prob, routing, dy, R["w1"], R["w2"], h)
+    dw1, dw2 = moe.moe_bwd_wgrad(prob, routing, x, dy, h, dh)
     _, dwr, _ = moe.moe_router_bwd(prob, routing, dprob, x, R["wr"])
     torch.cuda.synchronize()
     grads = {n: t.cpu().numpy().ravel().copy() for n, t in (("w1", dw1), ("w2", dw2), ("wr", dwr))}
