@@ -28,6 +28,10 @@ EDGE = {
     # (three full tiles and a ragged one per expert), the fc2 dgrad 256-row tiles
     "rows192_bf16": Config("rows192_bf16", 1500, 256, 512, 4, 2, 0, 4, "bf16", 1, 22),
     "ragged_fp32": Config("ragged_fp32", 37, 64, 192, 3, 2, 0, 3, "f32", 1, 20),
+    # float32 storage with experts above the chunk (4 x 128 mean rows = 512):
+    # the float32 weight-gradient kernels' partial slots and ordered reduction
+    "split_k_fp32": Config("split_k_fp32", 2048, 64, 128, 16, 1, 0, 16, "f32", 1, 23, skew="zipf",
+                           zipf_beta=2.0, zipf_empty=2),
     "shard_fp32": Config("shard_fp32", 90, 128, 64, 8, 3, 2, 4, "f32", 0, 21),
 }
 
@@ -67,20 +71,22 @@ def test_edge_parity(name):
     print(name, compare_layer(cfg, out, ref))
 
 
-@pytest.mark.parametrize("name", ["ragged_bf16", "split_k_bf16", "shard_bf16"])
+@pytest.mark.parametrize("name", ["ragged_bf16", "split_k_bf16", "split_k_fp32", "shard_bf16"])
 def test_edge_parity_atomic(name):
     cfg = EDGE[name]
     out, ref = _run(cfg, moe.ATOMIC)
     print(name, compare_layer_unordered(cfg, out, ref))
 
 
-def test_split_config_really_splits():
-    """The split-K path is exercised: some expert holds more rows than the chunk."""
+@pytest.mark.parametrize("name", ["split_k_bf16", "split_k_fp32"])
+def test_split_config_really_splits(name):
+    """The split-K path is exercised: some expert holds more than twice the
+    chunk (4 x mean rows = 512), so it is reduced over at least three chunks."""
+    import numpy as np
     from oracle import route
     from synth import make_inputs
-    cfg = EDGE["split_k_bf16"]
+    cfg = EDGE[name]
     idx, _ = route(make_inputs(cfg, parts=("logits",))["logits"], cfg.top_k)
-    import numpy as np
     counts = np.bincount(idx.reshape(-1), minlength=cfg.num_experts)
-    kc = 512  # chunk for this shape: 4 * mean rows (128) -> 512
+    kc = 512
     assert counts.max() > 2 * kc, counts
