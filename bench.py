@@ -4,18 +4,24 @@ MI355X.
 
 A step is one backward of the expert layer: moe_bwd_dgrad_dprob followed by
 moe_bwd_wgrad (fc2 dgrad with the dprob partial epilogue, the fixed-order
-dprob combine, fc1 dgrad, the fixed-order dx combine, both split-K weight
-gradients and their ordered reduction) on the default workload: 4096 tokens,
-d_model 1024, 8 experts, top-2, expert MLP 1024 -> 2048 -> 1024 with ReLU^2,
-bf16 storage, float32 accumulation and float32 dprob / dW.  The inputs are
-seeded synthetic tensors already resident in HBM, and routing and the saved h
-come from one untimed moe_fwd.
+dprob combine, fc1 dgrad, the fixed-order dx combine, act_p rebuilt from h,
+both weight gradients with their ordered split-K reduction).  The headline
+workload is the largest single-GPU one, the LatentMoE-shaped layer: 4096
+tokens, latent 2048, 512 experts top-22 (90,112 routed rows), expert MLP
+2048 -> 2048 -> 2048 ReLU^2, bf16 storage, float32 accumulation and float32
+dprob / dW.  The inputs are seeded synthetic tensors already resident in HBM;
+routing and the saved h come from one untimed moe_fwd.
 
 Prints one JSON line.  ``value`` is 8*R*D*F / (time of one deterministic
-step), in TFLOP/s.  The determinism tax compares deterministic with atomic
-steps, which are interleaved step by step.
+step), in TFLOP/s, from K steps back to back between synchronisations.  The
+line also carries, per workload: cold-cache (512 MB written between steps)
+and warm per-step medians, the determinism tax (deterministic and atomic
+steps interleaved A B B A, medians and IQR, and the tax of the GEMM launches
+alone), the forward time, per-kernel times, and each kernel's roofline
+(algorithmic FLOPs and bytes against the bf16 MFMA and HBM peaks; the bound is
+whichever takes longer).
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--config NAME] [--sub-configs A,B|none]
 """
 import argparse
 import json
@@ -28,7 +34,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA, vendor figure
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+HEADLINE = "latent_e512k22"
+SUBS = "bf16_e8k2,skewed_e512k22,shard_e512k22_l4"
 
 
 def parse():
@@ -36,23 +44,301 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="bf16_e8k2")
+    ap.add_argument("--config", default=HEADLINE)
+    ap.add_argument("--sub-configs", default=SUBS, help="comma-separated workloads reported beside the headline, "
+                                                         "or 'none'")
     ap.add_argument("--stage-reps", type=int, default=10)
+    ap.add_argument("--flush-mb", type=int, default=512, help="bytes written between cold-cache steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the router / MXFP8 / NVFP4 legs")
     ap.add_argument("--profile-only", action="store_true",
-                    help="run warmup + timed steps only (for rocprofv3 runs)")
+                    help="run warmup + timed steps of the headline workload only (for rocprofv3 runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against known bytes)")
     return ap.parse_args()
 
 
+# ------------------------------------------------------------ algorithmic cost
+def stage_cost(stage: str, cfg, R: int) -> dict:
+    """Algorithmic FLOPs and compulsory HBM bytes of one launch of a stage:
+    every operand read once, every output written once (gathered rows count
+    once per distinct row of the source).  R: routed rows held here."""
+    T, D, F, El, k = cfg.tokens, cfg.d_model, cfg.d_ffn, cfg.num_local, cfg.top_k
+    es = 2 if cfg.dtype == "bf16" else 4
+    nT = F // 256 if cfg.dtype == "bf16" else F // 64
+    tok = min(T, R) * D * es              # x or dy: the distinct token rows read (at most R)
+    rowsF, rowsD = R * F * es, R * D * es
+    w = El * D * F * es                   # W1 or W2
+    if stage.startswith("fc2_dgrad"):     # dy rows, W2, h -> dh, per-N-tile partials
+        return dict(flops=2.0 * R * D * F, bytes=tok + w + rowsF + rowsF + R * nT * 4 + R * 4)
+    if stage.startswith("fc1_dgrad"):     # dh, W1 -> dx rows; the dprob combine (partials -> dprob)
+        return dict(flops=2.0 * R * D * F, bytes=rowsF + w + rowsD + R * nT * 4 + T * k * 4)
+    if stage.startswith("dx_combine"):    # dx rows -> dx
+        return dict(flops=0.0, bytes=rowsD + tok + T * k * 4)
+    if stage.startswith("wgrad_prep"):    # h, p -> act_p
+        return dict(flops=0.0, bytes=2 * rowsF + R * 4)
+    if stage.startswith("wgrad_fc1_fc2"):  # x, dy, dh, act_p -> dW1, dW2 (float32)
+        return dict(flops=4.0 * R * D * F, bytes=2 * tok + 2 * rowsF + 2 * El * D * F * 4)
+    if stage in ("wgrad_fc1", "wgrad_fc2"):
+        return dict(flops=2.0 * R * D * F, bytes=tok + rowsF + El * D * F * 4)
+    if stage in ("fc1_fwd", "fc2_fwd"):
+        return dict(flops=2.0 * R * D * F, bytes=tok + w + 2 * rowsF)
+    if stage.startswith("combine_gather"):
+        return dict(flops=0.0, bytes=rowsD + tok + T * k * 8)
+    return dict(flops=0.0, bytes=0.0)
+
+
+def roofline(stage: str, ms: float, cfg, R: int) -> dict:
+    """Roofline of one launch: the bound is whichever of the FLOP time at the
+    bf16 MFMA peak and the byte time at the HBM peak is longer; ``achieved``
+    and ``peak`` are in that bound's unit and ``frac`` = achieved / peak
+    (= bound time / measured time)."""
+    c = stage_cost(stage, cfg, R)
+    t_f = c["flops"] / (BF16_PEAK_TFLOPS * 1e12)
+    t_b = c["bytes"] / (HBM_PEAK_GBS * 1e9)
+    sec = ms * 1e-3
+    if t_f >= t_b:
+        ach = c["flops"] / sec / 1e12
+        return {"kernel": stage, "bound": "mfma", "achieved": round(ach, 2), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "flops_per_launch": c["flops"],
+                "bytes_per_launch": c["bytes"], "ms_per_launch": round(ms, 5),
+                "hbm_frac": round(c["bytes"] / sec / 1e9 / HBM_PEAK_GBS, 4)}
+    ach = c["bytes"] / sec / 1e9
+    return {"kernel": stage, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "flops_per_launch": c["flops"], "bytes_per_launch": c["bytes"],
+            "ms_per_launch": round(ms, 5), "mfma_frac": round(c["flops"] / sec / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ------------------------------------------------------------------ one workload
+class Workload:
+    """Device inputs, routing, saved h and output buffers of one workload."""
+
+    def __init__(self, cfg):
+        import numpy as np
+        import torch
+        import bitwise_deterministic_moe_amd as moe
+        from synth import make_inputs
+        self.cfg, self.moe, self.torch = cfg, moe, torch
+        self.prob = moe.Problem.from_config(cfg)
+        self.host = make_inputs(cfg)
+        dev = "cuda"
+
+        def up(a, dt):
+            if dt == "bf16":
+                return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        self.logits = torch.from_numpy(self.host["logits"]).to(dev)
+        self.x, self.w1, self.w2, self.dy = (up(self.host[n], cfg.dtype) for n in ("x", "w1", "w2", "dy"))
+        self.fwd_ws = torch.empty(max(moe.moe_workspace_size(self.prob)[0], 1), dtype=torch.uint8, device=dev)
+        self.routing, self.h, self.y = moe.moe_fwd(self.prob, self.logits, self.x, self.w1, self.w2,
+                                                   moe.DETERMINISTIC, ws=self.fwd_ws)
+        torch.cuda.synchronize()
+        self.R = self.routing.rows
+        D, F, el = cfg.d_model, cfg.d_ffn, cfg.num_local
+        dt = moe.TORCH_DTYPE[cfg.dtype]
+        out_rows = cfg.tokens if cfg.combine else self.prob.rows_cap
+        self.bufs = {}
+        for mode in (moe.DETERMINISTIC, moe.ATOMIC):
+            sz = moe.moe_workspace_size(self.prob, mode)
+            self.bufs[mode] = dict(
+                dx=torch.empty((out_rows, D), dtype=dt, device=dev),
+                dprob=torch.empty((cfg.tokens, cfg.top_k), dtype=torch.float32, device=dev),
+                dh=torch.empty((self.prob.rows_cap, F), dtype=dt, device=dev),
+                dw1=torch.empty((el, D, F), dtype=torch.float32, device=dev),
+                dw2=torch.empty((el, F, D), dtype=torch.float32, device=dev),
+                ws1=torch.empty(max(sz[1], 1), dtype=torch.uint8, device=dev),
+                ws2=torch.empty(max(sz[2], 1), dtype=torch.uint8, device=dev))
+
+    def step(self, mode, ev1=None, ev2=None):
+        moe, b = self.moe, self.bufs[mode]
+        moe.moe_bwd_dgrad_dprob(self.prob, self.routing, self.dy, self.w1, self.w2, self.h, mode, dx=b["dx"],
+                                dprob=b["dprob"], dh=b["dh"], ws=b["ws1"], events=ev1)
+        moe.moe_bwd_wgrad(self.prob, self.routing, self.x, self.dy, self.h, b["dh"], mode, dw1=b["dw1"],
+                          dw2=b["dw2"], ws=b["ws2"], events=ev2)
+
+    def fwd(self, ev=None):
+        self.moe.moe_fwd(self.prob, self.logits, self.x, self.w1, self.w2, self.moe.DETERMINISTIC,
+                         routing=self.routing, h=self.h, y=self.y, ws=self.fwd_ws, events=ev)
+
+
+def _ev():
+    import torch
+    return torch.cuda.Event(enable_timing=True)
+
+
+def _iqr(v):
+    if len(v) < 2:
+        return 0.0
+    q = statistics.quantiles(v, n=4)
+    return q[2] - q[0]
+
+
+def _busy():
+    """A short spin kernel, so that the host has enqueued the next work before
+    the GPU reaches it (no host-enqueue gap inside a timed step)."""
+    import torch
+    torch.cuda._sleep(100_000)
+
+
+def measure(wl: "Workload", args, flush) -> dict:
+    """Every timing of one workload (deterministic step back to back, cold and
+    warm per-step medians, ABBA determinism tax, per-kernel stage times in
+    both modes, forward)."""
+    torch, moe, cfg = wl.torch, wl.moe, wl.cfg
+    DET, ATOM = moe.DETERMINISTIC, moe.ATOMIC
+    R, D, F = wl.R, cfg.d_model, cfg.d_ffn
+    flops = 8.0 * R * D * F
+    for _ in range(args.warmup):
+        wl.step(DET)
+        wl.step(ATOM)
+    torch.cuda.synchronize()
+
+    # K deterministic steps back to back (the headline number)
+    t0, t1 = _ev(), _ev()
+    torch.cuda.synchronize()
+    _busy()
+    t0.record()
+    for _ in range(args.steps):
+        wl.step(DET)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_det = t0.elapsed_time(t1) / args.steps
+
+    # per-step medians, cold (flush written before every step) and warm
+    def per_step(mode, cold):
+        ts = []
+        evs = []
+        _busy()
+        for _ in range(args.steps):
+            if cold:
+                flush.add_(1)
+            e0, e1 = _ev(), _ev()
+            e0.record()
+            wl.step(mode)
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(b) for a, b in evs]
+        return statistics.median(ts), _iqr(ts)
+
+    cold_med, cold_iqr = per_step(DET, True)
+    warm_med, warm_iqr = per_step(DET, False)
+
+    # determinism tax: deterministic (A) and atomic (B) steps interleaved A B B A,
+    # one continuous stream of work (no synchronisation between steps), cold
+    td, ta = [], []
+    evs = []
+    _busy()
+    for i in range(args.steps):
+        order = (DET, ATOM) if i % 2 == 0 else (ATOM, DET)
+        for mode in order:
+            flush.add_(1)
+            e0, e1 = _ev(), _ev()
+            e0.record()
+            wl.step(mode)
+            e1.record()
+            evs.append((mode, e0, e1))
+    torch.cuda.synchronize()
+    for mode, a, b in evs:
+        (td if mode == DET else ta).append(a.elapsed_time(b))
+    med_d, med_a = statistics.median(td), statistics.median(ta)
+
+    # per-kernel times (library stage events), cold, both modes
+    def stage_times(mode):
+        names1 = moe.moe_stage_names(wl.prob, mode, 1)
+        names2 = moe.moe_stage_names(wl.prob, mode, 2)
+        acc = {}
+        for _ in range(args.stage_reps):
+            ev1 = [_ev() for _ in range(len(names1) + 1)]
+            ev2 = [_ev() for _ in range(len(names2) + 1)]
+            for e in ev1 + ev2:   # materialise the events before handing them to the library
+                e.record()
+            flush.add_(1)
+            _busy()
+            wl.step(mode, ev1, ev2)
+            torch.cuda.synchronize()
+            for names, ev in ((names1, ev1), (names2, ev2)):
+                for i, n in enumerate(names):
+                    acc.setdefault(n, []).append(ev[i].elapsed_time(ev[i + 1]))
+        return {n: statistics.median(v) for n, v in acc.items()}
+
+    st_det = stage_times(DET)
+    st_atom = stage_times(ATOM)
+    gemm = ("fc2_dgrad", "fc1_dgrad", "wgrad_fc1")
+    g_det = sum(v for n, v in st_det.items() if n.startswith(gemm))
+    g_atom = sum(v for n, v in st_atom.items() if n.startswith(gemm))
+
+    # forward (deterministic), warm, back to back
+    for _ in range(2):
+        wl.fwd()
+    torch.cuda.synchronize()
+    f0, f1 = _ev(), _ev()
+    _busy()
+    f0.record()
+    for _ in range(args.steps):
+        wl.fwd()
+    f1.record()
+    torch.cuda.synchronize()
+    ms_fwd = f0.elapsed_time(f1) / args.steps
+    names0 = moe.moe_stage_names(wl.prob, DET, 0)
+    ev0 = [_ev() for _ in range(len(names0) + 1)]
+    for e in ev0:
+        e.record()
+    _busy()
+    wl.fwd(ev0)
+    torch.cuda.synchronize()
+    st_fwd = {n: ev0[i].elapsed_time(ev0[i + 1]) for i, n in enumerate(names0)}
+
+    stage_roof = {n: roofline(n, v, cfg, R) for n, v in st_det.items()}
+    dom = max((n for n in st_det if stage_cost(n, cfg, R)["flops"] > 0), key=lambda n: st_det[n])
+    return {
+        "routed_rows": R, "flops_per_step": flops,
+        "ms_per_step": ms_det, "tflops": flops / (ms_det * 1e-3) / 1e12,
+        "cold_ms_median": cold_med, "cold_ms_iqr": cold_iqr, "warm_ms_median": warm_med, "warm_ms_iqr": warm_iqr,
+        "tax": {"tax": med_d / med_a - 1.0, "det_ms_median": med_d, "det_ms_iqr": _iqr(td),
+                "atomic_ms_median": med_a, "atomic_ms_iqr": _iqr(ta), "pairs_abba": args.steps,
+                "gemm_launches_tax": g_det / g_atom - 1.0, "gemm_launches_det_ms": g_det,
+                "gemm_launches_atomic_ms": g_atom},
+        "stages_ms_det": st_det, "stages_ms_atomic": st_atom, "stage_roofline": stage_roof,
+        "dominant": dom,
+        "fwd": {"ms": ms_fwd, "tflops": 4.0 * R * D * F / (ms_fwd * 1e-3) / 1e12, "stages_ms": st_fwd},
+    }
+
+
+def _r(v, n=5):
+    if isinstance(v, float):
+        return round(v, n)
+    if isinstance(v, dict):
+        return {k: _r(x, n) for k, x in v.items()}
+    return v
+
+
+def workload_desc(cfg, R) -> str:
+    lay = "token layout" if cfg.combine else f"expert shard: experts {cfg.expert_begin}..{cfg.expert_begin + cfg.num_local - 1} of {cfg.num_experts}, row layout"
+    skew = ", Zipf(1.1) routing skew" if cfg.skew else ""
+    return (f"{cfg.name}: {cfg.tokens} tokens, d_model {cfg.d_model}, {cfg.num_experts} experts top-{cfg.top_k}{skew}, "
+            f"{R} routed rows, expert MLP {cfg.d_model}->{cfg.d_ffn}->{cfg.d_model} ReLU^2, {cfg.dtype} storage, "
+            f"fp32 dprob/dW, {lay}")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "the benchmark runs the layer on one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark measures one GPU's share of the layer; it takes --gpus 1 only "
+                                   "(no multi-GPU path is built)"}))
         sys.exit(2)
-    import numpy as np
     import torch
 
     if args.copy_calibration:
@@ -66,121 +352,31 @@ def main():
         return
 
     import bitwise_deterministic_moe_amd as moe
-    from synth import CONFIGS, make_inputs
+    from synth import CONFIGS
 
     moe.load_library()
     cfg = CONFIGS[args.config]
-    prob = moe.Problem.from_config(cfg)
-    host = make_inputs(cfg)
-    dev = "cuda"
-
-    def up(a, dt):
-        if dt == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    logits = torch.from_numpy(host["logits"]).to(dev)
-    x, w1, w2, dy = (up(host[n], cfg.dtype) for n in ("x", "w1", "w2", "dy"))
-    routing, h, _ = moe.moe_fwd(prob, logits, x, w1, w2, moe.DETERMINISTIC)
-    torch.cuda.synchronize()
-    R = routing.rows
-    D, F, el = cfg.d_model, cfg.d_ffn, cfg.num_local
-    flops = 8.0 * R * D * F
-    gemm_flops = 2.0 * R * D * F
-    dt = moe.TORCH_DTYPE[cfg.dtype]
-    out_rows = cfg.tokens if cfg.combine else prob.rows_cap
-
-    class Bufs:
-        def __init__(self, mode):
-            self.mode = mode
-            self.dx = torch.empty((out_rows, D), dtype=dt, device=dev)
-            self.dprob = torch.empty((cfg.tokens, cfg.top_k), dtype=torch.float32, device=dev)
-            self.dh = torch.empty((prob.rows_cap, F), dtype=dt, device=dev)
-            self.act_p = torch.empty((prob.rows_cap, F), dtype=dt, device=dev)
-            self.dw1 = torch.empty((el, D, F), dtype=torch.float32, device=dev)
-            self.dw2 = torch.empty((el, F, D), dtype=torch.float32, device=dev)
-            sz = moe.moe_workspace_size(prob, mode)
-            self.ws1 = torch.empty(max(sz[1], 1), dtype=torch.uint8, device=dev)
-            self.ws2 = torch.empty(max(sz[2], 1), dtype=torch.uint8, device=dev)
-
-    def step(b, ev1=None, ev2=None):
-        moe.moe_bwd_dgrad_dprob(prob, routing, dy, w1, w2, h, b.mode, dx=b.dx, dprob=b.dprob, dh=b.dh,
-                                act_p=b.act_p, ws=b.ws1, events=ev1)
-        moe.moe_bwd_wgrad(prob, routing, x, dy, b.dh, b.act_p, b.mode, dw1=b.dw1, dw2=b.dw2, ws=b.ws2, events=ev2)
-
-    det, atom = Bufs(moe.DETERMINISTIC), Bufs(moe.ATOMIC)
-    for _ in range(args.warmup):
-        step(det)
-        step(atom)
-    torch.cuda.synchronize()
-
-    # ---- timed region: K deterministic steps back to back
-    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    t0, t1 = E(), E()
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(args.steps):
-        step(det)
-    t1.record()
-    torch.cuda.synchronize()
-    ms_det = t0.elapsed_time(t1) / args.steps
+    wl = Workload(cfg)
     if args.profile_only:
-        print(json.dumps({"profile_only": True, "ms_per_step": ms_det}))
-        return
-
-    # ---- determinism tax: det and atomic steps interleaved, per-step events
-    td, ta = [], []
-    for _ in range(args.steps):
-        e = [E() for _ in range(3)]
-        e[0].record()
-        step(det)
-        e[1].record()
-        step(atom)
-        e[2].record()
+        for _ in range(args.warmup):
+            wl.step(moe.DETERMINISTIC)
         torch.cuda.synchronize()
-        td.append(e[0].elapsed_time(e[1]))
-        ta.append(e[1].elapsed_time(e[2]))
-    med_d, med_a = statistics.median(td), statistics.median(ta)
-
-    def iqr(v):
-        q = statistics.quantiles(v, n=4)
-        return q[2] - q[0]
-
-    # ---- per-kernel times through the library's stage-event hook
-    def stage_times(mode, b):
-        names1 = moe.moe_stage_names(prob, mode, 1)
-        names2 = moe.moe_stage_names(prob, mode, 2)
-        acc = {}
-        for _ in range(args.stage_reps):
-            ev1 = [E() for _ in range(len(names1) + 1)]
-            ev2 = [E() for _ in range(len(names2) + 1)]
-            for e in ev1 + ev2:   # materialise the events before handing them to the library
-                e.record()
-            step(b, ev1, ev2)
-            torch.cuda.synchronize()
-            for names, ev in ((names1, ev1), (names2, ev2)):
-                for i, n in enumerate(names):
-                    acc.setdefault(n, []).append(ev[i].elapsed_time(ev[i + 1]))
-        return {n: statistics.mean(v) for n, v in acc.items()}
-
-    st_det = stage_times(moe.DETERMINISTIC, det)
-    st_atom = stage_times(moe.ATOMIC, atom)
-    # grouped GEMMs per launch of each GEMM stage (both weight gradients share one launch for bf16)
-    gemms_in = {"fc2_dgrad_dprob_partials": 1, "fc1_dgrad_dprob_combine": 1, "wgrad_fc1": 1, "wgrad_fc2": 1,
-                "wgrad_fc1_fc2": 2}
-    gemm_stages = [n for n in gemms_in if n in st_det]
-    dom = max(gemm_stages, key=lambda n: st_det[n])
-    dom_ms = st_det[dom]
-    dom_flops = gemms_in[dom] * gemm_flops
-    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
-
-    value = flops / (ms_det * 1e-3) / 1e12
+        t0, t1 = _ev(), _ev()
+        t0.record()
+        for _ in range(args.steps):
+            wl.step(moe.DETERMINISTIC)
+        t1.record()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_only": True, "config": cfg.name, "ms_per_step": t0.elapsed_time(t1) / args.steps}))
+        return
+    flush = torch.empty(args.flush_mb * (1 << 20) // 4, dtype=torch.float32, device="cuda").zero_()
+    m = measure(wl, args, flush)
+    R = m["routed_rows"]
+    dom = m["dominant"]
+    roof = dict(m["stage_roofline"][dom])
+    roof["traffic"] = measured_traffic(cfg.name, dom)
+    value = m["tflops"]
     mfma_peak = measured_mfma_peak()
-    router = measured_router_bwd(cfg, prob, routing, x, det.dprob) if cfg.combine and el == cfg.num_experts else None
-    mxq = measured_mx_quantize(det.dh[: R])
-    nvq = measured_nvfp4_quantize(det.dh[: R])
-    mxg = measured_mx_dgrad_fc1(cfg, prob, routing, det.dh, w1, st_det.get("fc1_dgrad_dprob_combine"))
-    mxg2 = measured_mx_dgrad_fc2(cfg, prob, routing, dy, w2, h, det.ws1, st_det.get("fc2_dgrad_dprob_partials"))
     result = {
         "metric": "MoE grouped-GEMM bwd TFLOP/s (det mode), % bf16 peak; determinism tax vs atomic",
         "value": round(value, 2),
@@ -188,40 +384,96 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_det, 5),
+        "ms_per_step": round(m["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: {cfg.tokens} tokens, d_model {D}, {cfg.num_experts} experts top-{cfg.top_k}, "
-                               f"expert MLP {D}->{F}->{D} ReLU^2, {cfg.dtype} storage, fp32 dprob/dW",
-                   "tokens": cfg.tokens, "d_model": D, "d_ffn": F, "experts": cfg.num_experts,
-                   "top_k": cfg.top_k, "routed_rows": R, "mode": "deterministic", "parallelism": "single GPU"},
+        "config": {"workload": workload_desc(cfg, R), "tokens": cfg.tokens, "d_model": cfg.d_model,
+                   "d_ffn": cfg.d_ffn, "experts": cfg.num_experts, "top_k": cfg.top_k, "local_experts": cfg.num_local,
+                   "routed_rows": R, "mode": "deterministic", "parallelism": "single GPU"},
         "pct_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
         "mfma_peak_measured": dict(mfma_peak, pct_of_measured=round(100.0 * value / mfma_peak["tflops"], 2)),
-        "determinism_tax": {
-            "tax": round(med_d / med_a - 1.0, 4),
-            "det_ms_median": round(med_d, 5), "det_ms_iqr": round(iqr(td), 5),
-            "atomic_ms_median": round(med_a, 5), "atomic_ms_iqr": round(iqr(ta), 5),
-            "interleaved_pairs": args.steps,
-        },
-        "router_bwd": router,
-        "mx_quantize": mxq,
-        "nvfp4_quantize": nvq,
-        "mx_dgrad_fc1": mxg,
-        "mx_dgrad_fc2": mxg2,
-        "stages_ms_det": {k: round(v, 5) for k, v in st_det.items()},
-        "stages_ms_atomic": {k: round(v, 5) for k, v in st_atom.items()},
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(dom) if args.config == "bf16_e8k2" else None,
-                     "flops_per_launch": dom_flops, "ms_per_launch": round(dom_ms, 5)},
+        "step_roofline": _r(step_roofline(m, cfg), 4),
+        "cold_cache": _r({"flush_mb": args.flush_mb, "ms_median": m["cold_ms_median"], "ms_iqr": m["cold_ms_iqr"],
+                          "tflops": m["flops_per_step"] / (m["cold_ms_median"] * 1e-3) / 1e12}),
+        "warm_cache": _r({"ms_median": m["warm_ms_median"], "ms_iqr": m["warm_ms_iqr"],
+                          "tflops": m["flops_per_step"] / (m["warm_ms_median"] * 1e-3) / 1e12}),
+        "determinism_tax": _r(m["tax"], 5),
+        "forward": _r(m["fwd"], 5),
+        "stages_ms_det": _r(m["stages_ms_det"]),
+        "stages_ms_atomic": _r(m["stages_ms_atomic"]),
+        "stage_roofline": m["stage_roofline"],
+        "roofline": roof,
     }
-
+    if not args.no_extras:
+        b = wl.bufs[moe.DETERMINISTIC]
+        st = m["stages_ms_det"]
+        if cfg.combine and cfg.num_local == cfg.num_experts:
+            result["router_bwd"] = measured_router_bwd(cfg, wl.prob, wl.routing, wl.x, b["dprob"])
+        result["mx_quantize"] = measured_mx_quantize(b["dh"][:R])
+        result["nvfp4_quantize"] = measured_nvfp4_quantize(b["dh"][:R])
+        result["mx_dgrad_fc1"] = measured_mx_dgrad_fc1(cfg, wl.prob, wl.routing, b["dh"], wl.w1,
+                                                       st.get("fc1_dgrad_dprob_combine"))
+        result["mx_dgrad_fc2"] = measured_mx_dgrad_fc2(cfg, wl.prob, wl.routing, wl.dy, wl.w2, wl.h, b["ws1"],
+                                                       st.get("fc2_dgrad_dprob_partials"))
+        result["fingerprint"] = measured_fingerprint(b["dw1"])
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, host, flops)
+        result["cpu_baseline"] = cpu_baseline(cfg, wl.host, R)
+    del wl
+    torch.cuda.empty_cache()
+    subs = {}
+    if args.sub_configs and args.sub_configs != "none":
+        for name in args.sub_configs.split(","):
+            if name == cfg.name:
+                continue
+            c = CONFIGS[name]
+            w = Workload(c)
+            s = measure(w, args, flush)
+            d = s["dominant"]
+            subs[name] = _r({"workload": workload_desc(c, s["routed_rows"]), "ms_per_step": s["ms_per_step"],
+                             "tflops": s["tflops"], "pct_bf16_peak": 100.0 * s["tflops"] / BF16_PEAK_TFLOPS,
+                             "step_roofline": step_roofline(s, c),
+                             "cold_ms_median": s["cold_ms_median"], "warm_ms_median": s["warm_ms_median"],
+                             "determinism_tax": s["tax"], "forward": s["fwd"], "stages_ms_det": s["stages_ms_det"],
+                             "stages_ms_atomic": s["stages_ms_atomic"],
+                             "roofline": dict(s["stage_roofline"][d], traffic=measured_traffic(name, d))}, 5)
+            del w
+            torch.cuda.empty_cache()
+    result["other_workloads"] = subs
     print(json.dumps(result), flush=True)
+
+
+def step_roofline(m, cfg) -> dict:
+    """The whole step against its bound: the sum over its launches of
+    max(FLOP time, byte time), divided by the measured step time."""
+    R = m["routed_rows"]
+    t_bound = 0.0
+    for n in m["stages_ms_det"]:
+        c = stage_cost(n, cfg, R)
+        t_bound += max(c["flops"] / (BF16_PEAK_TFLOPS * 1e12), c["bytes"] / (HBM_PEAK_GBS * 1e9))
+    return {"bound_ms": t_bound * 1e3, "frac": t_bound * 1e3 / m["ms_per_step"]}
+
+
+def measured_fingerprint(t, reps=5):
+    """moe_fingerprint of a float32 weight gradient (chunks of 65536): average
+    of `reps` calls against HBM for one read of the tensor."""
+    import torch
+    import bitwise_deterministic_moe_amd as moe
+    moe.moe_fingerprint(t, sync=False)
+    torch.cuda.synchronize()
+    e0, e1 = _ev(), _ev()
+    e0.record()
+    for _ in range(reps):
+        moe.moe_fingerprint(t, sync=False)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nb = t.numel() * t.element_size()
+    return {"tensor": f"dW1 {list(t.shape)} float32", "ms": round(ms, 5), "bytes": nb,
+            "achieved_GBs": round(nb / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "elements_per_s": round(t.numel() / (ms * 1e-3), 1)}
 
 
 def measured_mfma_peak(iters=20000, reps=5):
@@ -365,7 +617,7 @@ def measured_mx_dgrad_fc1(cfg, prob, routing, dh, w1, bf16_ms, reps=20):
 
 def measured_mx_dgrad_fc2(cfg, prob, routing, dy, w2, h, ws, bf16_ms, reps=20):
     """The MXFP8 variant of the fc2 data gradient with its fused epilogue
-    (dprob partials and their fixed-order combine, dh, act_p) on the step's
+    (dprob partials and their fixed-order combine, dh) on the step's
     dy, W2 and h, quantised once outside the timed region; deterministic
     mode, average of `reps` calls (GEMM launch + combine launch), against the
     dense fp8 peak, beside the bf16 fc2 dgrad stage (whose combine rides in
@@ -378,12 +630,12 @@ def measured_mx_dgrad_fc2(cfg, prob, routing, dy, w2, h, ws, bf16_ms, reps=20):
     dymx = moe.moe_mx_quantize(dy)
     wq = moe.moe_mx_quantize(w2.reshape(el * F, D))
     wmx = (wq[0].reshape(el, F, D), wq[1].reshape(el, F, D // 32))
-    dprob, dh, act_p = moe.moe_mx_dgrad_fc2(prob, routing, dymx, wmx, h, ws=ws)
+    dprob, dh = moe.moe_mx_dgrad_fc2(prob, routing, dymx, wmx, h, ws=ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
-        moe.moe_mx_dgrad_fc2(prob, routing, dymx, wmx, h, dprob=dprob, dh=dh, act_p=act_p, ws=ws)
+        moe.moe_mx_dgrad_fc2(prob, routing, dymx, wmx, h, dprob=dprob, dh=dh, ws=ws)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
@@ -393,13 +645,13 @@ def measured_mx_dgrad_fc2(cfg, prob, routing, dy, w2, h, ws, bf16_ms, reps=20):
             "frac": round(tf / FP8_PEAK_TFLOPS, 4), "bf16_stage_ms": None if bf16_ms is None else round(bf16_ms, 5)}
 
 
-def measured_traffic(stage):
-    """HBM bytes per launch of `stage` from profiles/bench_bf16_e8k2_hbm_traffic.txt
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of `stage` from profiles/<workload>_hbm_traffic.txt
     (rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by a plain-copy calibration), or
     None when the library source changed since those counters were taken."""
     import glob
     import hashlib
-    path = os.path.join(ROOT, "profiles", "bench_bf16_e8k2_hbm_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     m = hashlib.sha256()
@@ -420,8 +672,13 @@ def measured_traffic(stage):
     return fields.get(("stage", stage))
 
 
-def cpu_baseline(cfg, host, gpu_flops):
-    """The oracle's backward (float64 numpy, as it stands) on the same inputs."""
+def cpu_baseline(cfg, host, R):
+    """The oracle's backward (numpy, as it stands) on the same inputs, on this
+    host's cores: oracle.expert_backward over every local expert in order
+    (what oracle.backward does, one expert's float64 weights at a time, so
+    that the 512-expert layer needs no 34 GB of float64 weights).  The saved
+    h comes from oracle.expert_forward outside the timed calls.  Also the
+    same code on float32 arrays over the first experts (a bounded sample)."""
     import numpy as np
     try:
         from threadpoolctl import threadpool_info
@@ -431,21 +688,40 @@ def cpu_baseline(cfg, host, gpu_flops):
     import oracle
     idx, p = oracle.route(host["logits"], cfg.top_k)
     perm = oracle.permute(idx, cfg.expert_begin, cfg.num_local)
-    x, w1, w2, dy = (oracle.decode(host[n], cfg.dtype) for n in ("x", "w1", "w2", "dy"))
-    h = oracle.forward(x, w1, w2, p, perm, cfg.top_k, combine=bool(cfg.combine))["h"]
-    times = []
-    t_end = time.perf_counter() + 10.0
-    while len(times) < 3 and (not times or time.perf_counter() < t_end):
-        t = time.perf_counter()
-        oracle.backward(x, w1, w2, h, dy, p, perm, cfg.top_k, combine=bool(cfg.combine))
-        times.append(time.perf_counter() - t)
-    sec = statistics.median(times)
-    R = int(perm["offsets"][-1])
-    fl = 8.0 * R * cfg.d_model * cfg.d_ffn
-    return {"value": round(fl / sec / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"full float64 oracle backward of {cfg.name} (all {cfg.num_local} experts, {R} rows), "
-                      f"median of {len(times)} runs, {sec:.2f} s each",
-            "seconds_per_step": round(sec, 3)}
+    off, row_tok, row_src = perm["offsets"], perm["row_tok"], perm["row_src"]
+    p_rows = p.reshape(-1)[row_src]
+    x = oracle.decode(host["x"], cfg.dtype)
+    dy = oracle.decode(host["dy"], cfg.dtype)
+
+    def run(dtype, experts):
+        sec, rows = 0.0, 0
+        for e in experts:
+            s, t = int(off[e]), int(off[e + 1])
+            if t == s:
+                continue
+            w1 = oracle.decode(host["w1"][e], cfg.dtype).astype(dtype)
+            w2 = oracle.decode(host["w2"][e], cfg.dtype).astype(dtype)
+            xr, dyr, pr = x[row_tok[s:t]].astype(dtype), dy[row_tok[s:t]].astype(dtype), p_rows[s:t].astype(dtype)
+            h, _ = oracle.expert_forward(xr, w1, w2)
+            t0 = time.perf_counter()
+            oracle.expert_backward(xr, dyr, pr, h, w1, w2)
+            sec += time.perf_counter() - t0
+            rows += t - s
+        return sec, rows
+
+    el = cfg.num_local
+    sec64, rows64 = run(np.float64, range(el))
+    n32 = min(el, 64)
+    sec32, rows32 = run(np.float32, range(n32))
+    fl = lambda rows: 8.0 * rows * cfg.d_model * cfg.d_ffn  # noqa: E731
+    return {"value": round(fl(rows64) / sec64 / 1e12, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_logical_cpus": os.cpu_count(),
+            "sample": f"float64 oracle backward (oracle.expert_backward) over all {el} local experts of "
+                      f"{cfg.name}, {rows64} routed rows, {sec64:.2f} s of timed calls",
+            "seconds_per_step": round(sec64, 3),
+            "fp32_variant": {"value": round(fl(rows32) / sec32 / 1e12, 5), "unit": "TFLOP/s",
+                             "sample": f"the same calls on float32 arrays, first {n32} experts ({rows32} rows), "
+                                       f"{sec32:.2f} s"}}
 
 
 if __name__ == "__main__":
