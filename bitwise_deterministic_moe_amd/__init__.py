@@ -18,7 +18,7 @@ __all__ = [
     "load_library", "library_path", "moe_workspace_size", "moe_rows_cap", "moe_stage_names",
     "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad", "moe_fingerprint", "moe_sched_elems", "moe_mfma_rate",
     "moe_router_bwd", "moe_router_fwd", "moe_sgd_step", "moe_mx_quantize", "moe_mx_dgrad_fc1",
-    "EXPORTED_SYMBOLS",
+    "moe_bwd_dgrad_dprob_noalloc", "EXPORTED_SYMBOLS",
 ]
 
 DETERMINISTIC = 0
@@ -31,7 +31,7 @@ EXPORTED_SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_rows_cap", "moe
                     "moe_workspace_size", "moe_stage_names", "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad",
                     "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd", "moe_sgd_step",
                     "moe_mx_quantize", "moe_mx_dgrad_fc1", "moe_mx_dgrad_fc2",
-                    "moe_nvfp4_quantize")
+                    "moe_nvfp4_quantize", "moe_bwd_dgrad_dprob_noalloc")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -86,6 +86,7 @@ def load_library() -> ctypes.CDLL:
     lib.moe_fwd.argtypes = [P, vp, vp, vp, vp, R, vp, vp, vp, sz, ctypes.c_int, vp]
     lib.moe_bwd_dgrad_dprob.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
     lib.moe_bwd_wgrad.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
+    lib.moe_bwd_dgrad_dprob_noalloc.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp]
     lib.moe_fingerprint.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
                                     vp, vp, vp]
     lib.moe_mfma_rate.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_float, vp, vp]
@@ -98,6 +99,7 @@ def load_library() -> ctypes.CDLL:
                                        vp]
     lib.moe_mx_dgrad_fc2.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
     for f in ("moe_rows_cap", "moe_sched_elems", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob",
+              "moe_bwd_dgrad_dprob_noalloc",
               "moe_bwd_wgrad", "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd",
               "moe_sgd_step", "moe_mx_quantize", "moe_mx_dgrad_fc1", "moe_mx_dgrad_fc2", "moe_nvfp4_quantize"):
         getattr(lib, f).restype = ctypes.c_int
@@ -279,6 +281,31 @@ def moe_bwd_dgrad_dprob(prob: Problem, routing: Routing, dy, w1, w2, h, mode: in
     _check(lib.moe_bwd_dgrad_dprob(ctypes.byref(cp), ctypes.byref(cr), _ptr(dy), _ptr(w1), _ptr(w2), _ptr(h),
                                    _ptr(dx), _ptr(dprob), _ptr(dh), _ptr(ws), ws.numel(), mode, _stream()),
            "moe_bwd_dgrad_dprob")
+    return dx, dprob, dh
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES of moedet.h
+
+
+def moe_bwd_dgrad_dprob_noalloc(prob: Problem, routing: Routing, dy, w1, w2, h, dx, dprob, dh,
+                                mode: int = DETERMINISTIC, events=None):
+    """moe_bwd_dgrad_dprob with the library's static per-GPU workspace: the
+    caller passes inputs and preallocated outputs, nothing is allocated.
+    Returns (dx_or_rows, dprob, dh)."""
+    lib = load_library()
+    dt = TORCH_DTYPE[prob.dtype]
+    T, k, D, F, el, rc = prob.tokens, prob.top_k, prob.d_model, prob.d_ffn, prob.local, prob.rows_cap
+    _need(dy, T * D, dt, "moe_bwd_dgrad_dprob_noalloc dy")
+    _need(w1, el * D * F, dt, "moe_bwd_dgrad_dprob_noalloc w1")
+    _need(w2, el * F * D, dt, "moe_bwd_dgrad_dprob_noalloc w2")
+    _need(h, rc * F, dt, "moe_bwd_dgrad_dprob_noalloc h")
+    _need(dx, (T if prob.combine else rc) * D, dt, "moe_bwd_dgrad_dprob_noalloc dx")
+    _need(dprob, T * k, torch.float32, "moe_bwd_dgrad_dprob_noalloc dprob")
+    _need(dh, rc * F, dt, "moe_bwd_dgrad_dprob_noalloc dh")
+    cp, cr = prob.c(events), routing.c()
+    _check(lib.moe_bwd_dgrad_dprob_noalloc(ctypes.byref(cp), ctypes.byref(cr), _ptr(dy), _ptr(w1), _ptr(w2), _ptr(h),
+                                           _ptr(dx), _ptr(dprob), _ptr(dh), mode, _stream()),
+           "moe_bwd_dgrad_dprob_noalloc")
     return dx, dprob, dh
 
 

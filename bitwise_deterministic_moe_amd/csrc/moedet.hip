@@ -6,6 +6,8 @@
 // workspaces from shape upper bounds only, so nothing here waits for the GPU.
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moedet.h"
 #include "kernels.h"
 
@@ -469,6 +471,53 @@ MOE_API moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* 
   moe_status s = dgrad_check(p, &pl, routing, dy, w1, w2, h, dx_or_rows, dprob, dh, mode);
   if (s != MOE_OK) return s;
   s = check_ws(ws, ws_bytes, dgrad_layout(pl, p->combine, mode == MOE_ATOMIC).total);
+  if (s != MOE_OK) return s;
+  return dgrad_enqueue(p, pl, routing, dy, w1, w2, h, dx_or_rows, dprob, dh, ws, mode, stream);
+}
+
+// ---------------------------------------------------- no-allocation variant
+// The dgrad workspace of moe_bwd_dgrad_dprob_noalloc lives in this
+// file-scope device array: every GPU the library runs on holds its own copy
+// of kScratchBytes until the process ends.  In host code `scratch` is only a
+// stand-in for the symbol; the device address of a GPU's copy comes from
+// hipGetSymbolAddress with that GPU current, and only that address is ever
+// handed to kernels.
+namespace {
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+// Device address of the current GPU's scratch array, looked up once per
+// device (with that device current, as the call runs on it).
+moe_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = ptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return MOE_ERR_HIP;
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+MOE_API moe_status moe_bwd_dgrad_dprob_noalloc(const moe_problem* p, const moe_routing* routing, const void* dy,
+                                               const void* w1, const void* w2, const void* h, void* dx_or_rows,
+                                               float* dprob, void* dh, moe_mode mode, void* stream) {
+  Plan pl;
+  moe_status s = dgrad_check(p, &pl, routing, dy, w1, w2, h, dx_or_rows, dprob, dh, mode);
+  if (s != MOE_OK) return s;
+  if (dgrad_layout(pl, p->combine, mode == MOE_ATOMIC).total > kScratchBytes) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  s = scratch_for_current_device(&ws);
   if (s != MOE_OK) return s;
   return dgrad_enqueue(p, pl, routing, dy, w1, w2, h, dx_or_rows, dprob, dh, ws, mode, stream);
 }

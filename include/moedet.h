@@ -245,6 +245,34 @@ moe_status moe_bwd_dgrad_dprob(const moe_problem* p, const moe_routing* routing,
                                float* dprob, void* dh, void* ws, size_t ws_bytes, moe_mode mode,
                                void* stream);
 
+/* Bytes of the device array that holds the workspace of
+ * moe_bwd_dgrad_dprob_noalloc (one copy per GPU the library runs on). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* moe_bwd_dgrad_dprob for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels, with the dgrad workspace taken from a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES per GPU (its device address is looked up once per
+ * GPU, on the first call there) instead of a caller buffer.  The call
+ * allocates and frees nothing.  Arguments and outputs are those of
+ * moe_bwd_dgrad_dprob without ws / ws_bytes; the outputs are bit-identical
+ * to moe_bwd_dgrad_dprob's in MOE_DETERMINISTIC mode.
+ * Limit: the problem's dgrad workspace (moe_workspace_size(...).dgrad_bytes
+ * for `mode`) must fit in MOE_NOALLOC_SCRATCH_BYTES, else MOE_ERR_WORKSPACE
+ * is returned before anything is enqueued (for example the 4096-token,
+ * 1024-wide, 8-expert top-2 layer needs 17 MB in MOE_DETERMINISTIC mode; a
+ * 512-expert top-22 layer of 4096 tokens at width 2048 needs 372 MB and is
+ * rejected).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other threads) race on it and must be serialised by the
+ * caller.  The array keeps the last call's contents; nothing in it needs to
+ * start at zero (what must be zeroed, the call zeroes itself).
+ * Errors: those of moe_bwd_dgrad_dprob, plus MOE_ERR_WORKSPACE for a problem
+ * beyond the limit and MOE_ERR_HIP if the array's address cannot be found. */
+moe_status moe_bwd_dgrad_dprob_noalloc(const moe_problem* p, const moe_routing* routing, const void* dy,
+                                       const void* w1, const void* w2, const void* h, void* dx_or_rows,
+                                       float* dprob, void* dh, moe_mode mode, void* stream);
+
 /* Backward, weight gradients (float32 outputs, exact zeros for experts
  * without rows):
  *   dw1 [El,D,F] = sum over the expert's rows of x_row^T dh_row
