@@ -493,18 +493,15 @@ DEV void dgrad2_epilogue(const RowGemmParams& P, const RowTile& t, uint16_t* lds
   }
 }
 
-// BMV: tile rows (256, or 192 as two wave rows of 96).
-template <int BL, int EPI, int BMV>
-__global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
-  constexpr int WTM = BMV / 2;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[bf::ring_bytes<kRowNS> / 2];
+// One row tile of the bf16 row GEMM, with WTM rows per wave row (128, or 96
+// for a tile of at most 192 rows: then both wave rows hold three 32-row
+// blocks instead of four and at most two, so the slower wave does three
+// quarters of the MFMAs).  The tile's LDS A operand always has 256 rows.
+template <int BL, int EPI, int WTM>
+DEV void rowgemm_bf16_tile(const RowGemmParams& P, const RowTile& t, uint16_t* lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t ring = bf::lds_base(lds);
   const int wm = wave >> 1, wn = wave & 1;
-  RowTile t;
-  const int kind = row_tile<BMV, bf::BN>(P, t);
-  if (kind == kTileSide) dprob_side(P, t.nt);
-  if (kind != kTileGemm) return;
   // routing probability of each tile row (fc2 dgrad epilogue); loaded now,
   // stored to LDS once the ring is free
   float my_prob = 0.f;
@@ -581,6 +578,27 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
     });
   } else {
     dgrad2_epilogue<WTM>(P, t, lds, acc, wm, wn, lane, tid, my_prob);
+  }
+}
+
+
+// BMV: tile rows (256, or 192 as two wave rows of 96).  A 256-row tile that
+// holds at most 192 rows runs the 96-row wave layout (a choice made per tile
+// from its row count; the MFMA order per output element is the same).
+template <int BL, int EPI, int BMV>
+__global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[bf::ring_bytes<kRowNS> / 2];
+  RowTile t;
+  const int kind = row_tile<BMV, bf::BN>(P, t);
+  if (kind == kTileSide) dprob_side(P, t.nt);
+  if (kind != kTileGemm) return;
+  if constexpr (BMV == 256) {
+    if (t.mvalid <= kRowTile2)
+      rowgemm_bf16_tile<BL, EPI, kRowTile2 / 2>(P, t, lds);
+    else
+      rowgemm_bf16_tile<BL, EPI, 128>(P, t, lds);
+  } else {
+    rowgemm_bf16_tile<BL, EPI, BMV / 2>(P, t, lds);
   }
 }
 

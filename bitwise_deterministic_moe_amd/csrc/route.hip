@@ -8,9 +8,10 @@
 // slot index t*k+j, so the row order inside an expert -- the K order of the
 // weight-gradient reduction -- is fixed by the routing alone.
 //
-//  route_kernel    one wave per token: k rounds of a wave-wide argmax, then
-//                  the softmax; per-chunk histogram of local experts in LDS
-//                  (integer atomics: exact in any order).
+//  route_kernel    one wave per token (16 waves per chunk of 64 tokens): k
+//                  rounds of a wave-wide argmax, then the softmax; per-chunk
+//                  histogram of local experts in LDS (integer atomics: exact
+//                  in any order).
 //  scan_kernel     per-expert exclusive bases of every chunk and the expert
 //                  offsets (one workgroup, sequential over chunks).
 //  scatter_kernel  one wave per chunk walks its slots in order, 64 at a
@@ -37,16 +38,19 @@ DEV bool better(const Cand& a, const Cand& b) {
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void route_kernel(RouteParams P) {
+// PER logits per lane (E <= 64 * PER); kRouteWaves waves per chunk of
+// kRouteChunk tokens, one token per wave at a time.
+constexpr int kRouteWaves = 16;
+template <int PER>
+__global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(RouteParams P) {
   __shared__ int s_hist[kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t b = blockIdx.x;  // chunk index (fixed: the histogram is per chunk)
   if (P.seed) shuffle_delay(P.seed, b);
-  for (int i = tid; i < P.el; i += 256) s_hist[i] = 0;
+  for (int i = tid; i < P.el; i += kRouteWaves * 64) s_hist[i] = 0;
   __syncthreads();
   const int E = P.E, k = P.k;
-  constexpr int PER = kMaxExperts / kWave;
-  for (int tt = w; tt < kRouteChunk; tt += 4) {
+  for (int tt = w; tt < kRouteChunk; tt += kRouteWaves) {
     const int64_t t = b * kRouteChunk + tt;
     if (t >= P.T) break;
     const float* row = P.logits + t * E;
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteParams P) {
     }
   }
   __syncthreads();
-  for (int i = tid; i < P.el; i += 256) P.hist[b * P.el + i] = s_hist[i];
+  for (int i = tid; i < P.el; i += kRouteWaves * 64) P.hist[b * P.el + i] = s_hist[i];
 }
 
 // Row tiles of height BM over the experts' rows, longest first: the full
@@ -254,7 +258,17 @@ __global__ __launch_bounds__(64) void permute_scatter_kernel(RouteParams P) {
 
 hipError_t launch_route(const RouteParams& P, hipStream_t st) {
   if (P.nchunk <= 0) return hipSuccess;
-  route_kernel<<<P.nchunk, 256, 0, st>>>(P);
+  const dim3 blk(kRouteWaves * 64);
+  if (P.E <= 64)
+    route_kernel<1><<<P.nchunk, blk, 0, st>>>(P);
+  else if (P.E <= 128)
+    route_kernel<2><<<P.nchunk, blk, 0, st>>>(P);
+  else if (P.E <= 256)
+    route_kernel<4><<<P.nchunk, blk, 0, st>>>(P);
+  else if (P.E <= 512)
+    route_kernel<8><<<P.nchunk, blk, 0, st>>>(P);
+  else
+    route_kernel<kMaxExperts / kWave><<<P.nchunk, blk, 0, st>>>(P);
   return hipGetLastError();
 }
 
