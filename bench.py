@@ -418,6 +418,7 @@ def main():
                                                        st.get("fc1_dgrad_dprob_combine"))
         result["mx_dgrad_fc2"] = measured_mx_dgrad_fc2(cfg, wl.prob, wl.routing, wl.dy, wl.w2, wl.h, b["ws1"],
                                                        st.get("fc2_dgrad_dprob_partials"))
+        result["mx_fwd"] = measured_mx_fwd(cfg, wl, m["fwd"]["stages_ms"])
         result["fingerprint"] = measured_fingerprint(b["dw1"])
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, wl.host, R)
@@ -643,6 +644,40 @@ def measured_mx_dgrad_fc2(cfg, prob, routing, dy, w2, h, ws, bf16_ms, reps=20):
     tf = flops / (ms * 1e-3) / 1e12
     return {"ms": round(ms, 5), "tflops": round(tf, 1), "peak_fp8": FP8_PEAK_TFLOPS,
             "frac": round(tf / FP8_PEAK_TFLOPS, 4), "bf16_stage_ms": None if bf16_ms is None else round(bf16_ms, 5)}
+
+
+def measured_mx_fwd(cfg, wl, bf16_stages, reps=20):
+    """The MXFP8 forward GEMMs on the workload's x, W1 and W2 (quantised once
+    outside the timed region, the weights along their contraction axis):
+    fc1 (h and relu(h)^2) and fc2 with the fixed-order combine, average of
+    `reps` calls each, against the dense fp8 peak, beside the bf16 forward
+    stages."""
+    import torch
+    import bitwise_deterministic_moe_amd as moe
+    if cfg.dtype != "bf16" or cfg.d_model > 2048 or cfg.d_ffn > 2048:
+        return None
+    xmx, w1t, w2t = moe.moe_mx_quantize(wl.x), moe.moe_mx_quantize_t(wl.w1), moe.moe_mx_quantize_t(wl.w2)
+    h, act = moe.moe_mx_fwd_fc1(wl.prob, wl.routing, xmx, w1t)
+    amx = moe.moe_mx_quantize(act)
+    y = moe.moe_mx_fwd_fc2(wl.prob, wl.routing, amx, w2t, ws=wl.fwd_ws)
+    torch.cuda.synchronize()
+    res = {}
+    flops = 2.0 * wl.R * cfg.d_model * cfg.d_ffn
+    for name, fn in (("fc1", lambda: moe.moe_mx_fwd_fc1(wl.prob, wl.routing, xmx, w1t, h=h, act=act)),
+                     ("fc2_combine", lambda: moe.moe_mx_fwd_fc2(wl.prob, wl.routing, amx, w2t, y=y, ws=wl.fwd_ws))):
+        e0, e1 = _ev(), _ev()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = flops / (ms * 1e-3) / 1e12
+        res[name] = {"ms": round(ms, 5), "tflops": round(tf, 1), "frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
+    res["fc1"]["bf16_stage_ms"] = round(bf16_stages.get("fc1_fwd", float("nan")), 5)
+    res["fc2_combine"]["bf16_stage_ms"] = round(bf16_stages.get("fc2_fwd", float("nan")) +
+                                                bf16_stages.get("combine_gather", 0.0), 5)
+    return res
 
 
 def measured_traffic(workload, stage):

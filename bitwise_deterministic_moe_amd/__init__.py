@@ -18,7 +18,7 @@ __all__ = [
     "load_library", "library_path", "moe_workspace_size", "moe_rows_cap", "moe_stage_names",
     "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad", "moe_fingerprint", "moe_sched_elems", "moe_mfma_rate",
     "moe_router_bwd", "moe_router_fwd", "moe_sgd_step", "moe_mx_quantize", "moe_mx_dgrad_fc1",
-    "moe_bwd_dgrad_dprob_noalloc", "EXPORTED_SYMBOLS",
+    "moe_bwd_dgrad_dprob_noalloc", "moe_mx_quantize_t", "moe_mx_fwd_fc1", "moe_mx_fwd_fc2", "EXPORTED_SYMBOLS",
 ]
 
 DETERMINISTIC = 0
@@ -31,7 +31,8 @@ EXPORTED_SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_rows_cap", "moe
                     "moe_workspace_size", "moe_stage_names", "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad",
                     "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd", "moe_sgd_step",
                     "moe_mx_quantize", "moe_mx_dgrad_fc1", "moe_mx_dgrad_fc2",
-                    "moe_nvfp4_quantize", "moe_bwd_dgrad_dprob_noalloc")
+                    "moe_nvfp4_quantize", "moe_bwd_dgrad_dprob_noalloc", "moe_mx_quantize_t", "moe_mx_fwd_fc1",
+                    "moe_mx_fwd_fc2")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -98,8 +99,12 @@ def load_library() -> ctypes.CDLL:
     lib.moe_nvfp4_quantize.argtypes = [vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, vp, vp, vp, ctypes.c_uint64,
                                        vp]
     lib.moe_mx_dgrad_fc2.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
+    lib.moe_mx_quantize_t.argtypes = [vp, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp, vp,
+                                      ctypes.c_uint64, vp]
+    lib.moe_mx_fwd_fc1.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp]
+    lib.moe_mx_fwd_fc2.argtypes = [P, R, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
     for f in ("moe_rows_cap", "moe_sched_elems", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob",
-              "moe_bwd_dgrad_dprob_noalloc",
+              "moe_bwd_dgrad_dprob_noalloc", "moe_mx_quantize_t", "moe_mx_fwd_fc1", "moe_mx_fwd_fc2",
               "moe_bwd_wgrad", "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd",
               "moe_sgd_step", "moe_mx_quantize", "moe_mx_dgrad_fc1", "moe_mx_dgrad_fc2", "moe_nvfp4_quantize"):
         getattr(lib, f).restype = ctypes.c_int
@@ -481,6 +486,73 @@ def moe_mx_dgrad_fc2(prob: Problem, routing: Routing, dy_mx, w2_mx, h, mode: int
                                 _ptr(dprob), _ptr(dh), _ptr(ws), ws.numel(), mode, _stream()),
            "moe_mx_dgrad_fc2")
     return dprob, dh
+
+
+def moe_mx_quantize_t(t: torch.Tensor, codes=None, scales=None, shuffle_seed: int = 0):
+    """MXFP8 of the transpose of each [rows, cols] matrix of a contiguous
+    [groups, rows, cols] (or [rows, cols]) float32 / bf16 tensor: blocks of 32
+    consecutive rows of a column.  Returns (codes uint8 [groups, cols, rows],
+    scales uint8 [groups, cols, rows/32]) (without the group axis for 2-D input)."""
+    lib = load_library()
+    if not t.is_contiguous() or t.dim() not in (2, 3):
+        raise MoeError("moe_mx_quantize_t needs a contiguous [groups,] rows, cols tensor")
+    g, rows, cols = (1,) + tuple(t.shape) if t.dim() == 2 else tuple(t.shape)
+    shp = (cols, rows) if t.dim() == 2 else (g, cols, rows)
+    if codes is None:
+        codes = torch.empty(shp, dtype=torch.uint8, device=t.device)
+    if scales is None:
+        scales = torch.empty(shp[:-1] + (rows // 32,), dtype=torch.uint8, device=t.device)
+    _need(codes, g * rows * cols, torch.uint8, "moe_mx_quantize_t codes")
+    _need(scales, g * cols * (rows // 32), torch.uint8, "moe_mx_quantize_t scales")
+    _check(lib.moe_mx_quantize_t(_ptr(t), _TORCH_TO_CODE[t.dtype], g, rows, cols, _ptr(codes), _ptr(scales),
+                                 shuffle_seed & 0xFFFFFFFFFFFFFFFF, _stream()), "moe_mx_quantize_t")
+    return codes, scales
+
+
+def moe_mx_fwd_fc1(prob: Problem, routing: Routing, x_mx, w1t_mx, h=None, act=None):
+    """MXFP8 forward fc1: h and act = relu(h)^2 (bf16 [rows_cap, F]) from the
+    (codes, scales) of x [T, D] (moe_mx_quantize) and of W1 transposed
+    [num_local, F, D] (moe_mx_quantize_t of W1).  Returns (h, act)."""
+    lib = load_library()
+    (xc, xs), (wc, wsc) = x_mx, w1t_mx
+    rc, T, D, F, el = prob.rows_cap, prob.tokens, prob.d_model, prob.d_ffn, prob.local
+    if h is None:
+        h = torch.empty((rc, F), dtype=torch.bfloat16, device=xc.device)
+    if act is None:
+        act = torch.empty((rc, F), dtype=torch.bfloat16, device=xc.device)
+    _need(xc, T * D, torch.uint8, "moe_mx_fwd_fc1 x codes")
+    _need(xs, T * (D // 32), torch.uint8, "moe_mx_fwd_fc1 x scales")
+    _need(wc, el * F * D, torch.uint8, "moe_mx_fwd_fc1 W1^T codes")
+    _need(wsc, el * F * (D // 32), torch.uint8, "moe_mx_fwd_fc1 W1^T scales")
+    _need(h, rc * F, torch.bfloat16, "moe_mx_fwd_fc1 h")
+    _need(act, rc * F, torch.bfloat16, "moe_mx_fwd_fc1 act")
+    cp, cr = prob.c(), routing.c()
+    _check(lib.moe_mx_fwd_fc1(ctypes.byref(cp), ctypes.byref(cr), _ptr(xc), _ptr(xs), _ptr(wc), _ptr(wsc), _ptr(h),
+                              _ptr(act), _stream()), "moe_mx_fwd_fc1")
+    return h, act
+
+
+def moe_mx_fwd_fc2(prob: Problem, routing: Routing, act_mx, w2t_mx, mode: int = DETERMINISTIC, y=None, ws=None):
+    """MXFP8 forward fc2 and the combine: y [T, D] (combine=1) or the o rows
+    [rows_cap, D] (bf16) from the (codes, scales) of act [rows_cap, F]
+    (moe_mx_quantize) and of W2 transposed [num_local, D, F] (moe_mx_quantize_t
+    of W2).  The workspace is the forward one (moe_workspace_size)."""
+    lib = load_library()
+    (ac, asc), (wc, wsc) = act_mx, w2t_mx
+    rc, T, D, F, el = prob.rows_cap, prob.tokens, prob.d_model, prob.d_ffn, prob.local
+    out_rows = T if prob.combine else rc
+    if y is None:
+        y = torch.empty((out_rows, D), dtype=torch.bfloat16, device=ac.device)
+    ws = _ws(moe_workspace_size(prob, mode)[0], ws, ac.device)
+    _need(ac, rc * F, torch.uint8, "moe_mx_fwd_fc2 act codes")
+    _need(asc, rc * (F // 32), torch.uint8, "moe_mx_fwd_fc2 act scales")
+    _need(wc, el * D * F, torch.uint8, "moe_mx_fwd_fc2 W2^T codes")
+    _need(wsc, el * D * (F // 32), torch.uint8, "moe_mx_fwd_fc2 W2^T scales")
+    _need(y, out_rows * D, torch.bfloat16, "moe_mx_fwd_fc2 y")
+    cp, cr = prob.c(), routing.c()
+    _check(lib.moe_mx_fwd_fc2(ctypes.byref(cp), ctypes.byref(cr), _ptr(ac), _ptr(asc), _ptr(wc), _ptr(wsc), _ptr(y),
+                              _ptr(ws), ws.numel(), mode, _stream()), "moe_mx_fwd_fc2")
+    return y
 
 
 def moe_fingerprint(t: torch.Tensor, dtype: Optional[str] = None, chunk_elems: int = 65536,

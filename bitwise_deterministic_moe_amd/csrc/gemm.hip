@@ -790,8 +790,8 @@ DEV void mx_read_block(const uint8_t* op, const uint8_t* scales, int nkb, int kb
 }
 
 // BMV: tile rows (256, or 192 as two wave rows of 96: NA = 3 A blocks a
-// wave).  EPI: kEpiStore (bf16 rows of C) or kEpiDgrad2 (the fc2 dgrad
-// epilogue on G = C).  With P.a_rows, A row r is row a_rows[r] of the codes
+// wave).  EPI: kEpiStore (bf16 rows of C), kEpiStoreAct (also relu(C)^2 of
+// the rounded C, into c2) or kEpiDgrad2 (the fc2 dgrad epilogue on G = C).  With P.a_rows, A row r is row a_rows[r] of the codes
 // and of the scales (the fc2 dgrad gathers dy by token).
 static_assert(kProbOff + bf::BM * 4 <= bf::LDS_BYTES, "fc2 dgrad epilogue scratch must fit in the MXFP8 ring");
 template <int BMV, int EPI>
@@ -936,12 +936,23 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
     float* stage = (float*)lds;
     NoPre none;
     NoPre::Data nd[2];
-    const __amdgpu_buffer_rsrc_t rc = buf(P.c);
+    const __amdgpu_buffer_rsrc_t rc = buf(P.c), rc2 = buf(P.c2);
     staged_epilogue<WTM>(stage, acc, wm, wn, lane, tid, t.mvalid, none, nd, false, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
       if (m >= t.mvalid) return;  // uniform per wave
       const uint32_t grow = (uint32_t)(t.off + t.m0 + m);
       __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rc,
                                             (grow * (uint32_t)P.ldc + t.n0 + col) * 2u, 0, kEpiNT);
+      if constexpr (EPI == kEpiStoreAct) {
+        // activation of the stored (rounded) h, as in the bf16 forward
+        float a[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float r = relu(round_t<uint16_t>(v[q]));
+          a[q] = r * r;
+        }
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])}, rc2,
+                                              (grow * (uint32_t)P.ldc2 + t.n0 + col) * 2u, 0, kEpiNT);
+      }
     });
   }
 }
@@ -1208,7 +1219,9 @@ hipError_t launch_mx_rowgemm(const RowGemmParams& P, int kind, int64_t grid, hip
   if (grid <= 0) return hipSuccess;
   if (kind == kGemmFc2Dgrad)
     mx_rowgemm_kernel<256, kEpiDgrad2><<<grid, 256, 0, st>>>(P);
-  else if (kind != kGemmFc1Dgrad)
+  else if (kind == kGemmFc1Fwd)
+    mx_rowgemm_kernel<256, kEpiStoreAct><<<grid, 256, 0, st>>>(P);
+  else if (kind != kGemmFc1Dgrad && kind != kGemmFc2Fwd)
     return hipErrorInvalidValue;
   else if (P.list_hdr == 2)
     mx_rowgemm_kernel<kRowTile2, kEpiStore><<<grid, 256, 0, st>>>(P);

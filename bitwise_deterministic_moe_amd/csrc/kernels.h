@@ -197,13 +197,16 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t st);
 hipError_t launch_router_bwd(const RouterParams& P, bool bf16, hipStream_t st);
 hipError_t launch_router_fwd(const void* x, const void* wr, int64_t T, int E, int D, float* logits, bool bf16,
                              uint64_t seed, hipStream_t st);
-// MXFP8 row GEMM: kind kGemmFc1Dgrad (bf16 rows of C; P.list_hdr 2 selects the
-// 192-row tiles) or kGemmFc2Dgrad (the fc2 dgrad epilogue; 256-row tiles).
+// MXFP8 row GEMM: kind kGemmFc1Dgrad or kGemmFc2Fwd (bf16 rows of C; P.list_hdr
+// 2 selects the 192-row tiles), kGemmFc2Dgrad (the fc2 dgrad epilogue) or
+// kGemmFc1Fwd (h and relu(h)^2 rows); 256-row tiles unless stated.
 hipError_t launch_mx_rowgemm(const RowGemmParams& P, int kind, int64_t grid, hipStream_t st);
 hipError_t launch_nvfp4_quantize(const void* in, bool bf16, int64_t rows, int64_t cols, uint8_t* codes,
                                  uint8_t* scales, float* global_scale, uint64_t seed, hipStream_t st);
 hipError_t launch_mx_quantize(const void* in, bool bf16, int64_t rows, int64_t cols, uint8_t* codes,
                               uint8_t* scales, uint64_t seed, hipStream_t st);
+hipError_t launch_mx_quantize_t(const void* in, bool bf16, int64_t groups, int64_t rows, int64_t cols,
+                                uint8_t* codes, uint8_t* scales, uint64_t seed, hipStream_t st);
 hipError_t launch_sgd(float* master, const float* grad, int64_t n, float lr, void* runtime, bool bf16,
                       hipStream_t st);
 hipError_t launch_dprob_combine(const float* part, const int32_t* slot_row, int64_t nslots, int n_tiles,

@@ -928,6 +928,126 @@ MOE_API moe_status moe_mx_dgrad_fc2(const moe_problem* p, const moe_routing* rou
   return MOE_OK;
 }
 
+MOE_API moe_status moe_mx_quantize_t(const void* in, moe_dtype dtype, int64_t groups, int64_t rows, int64_t cols,
+                                     uint8_t* codes, uint8_t* scales, uint64_t debug_shuffle_seed, void* stream) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (groups < 0 || rows <= 0 || rows % 32 != 0 || cols <= 0) return MOE_ERR_SHAPE;
+  if (groups > (((int64_t)1 << 40) / rows) / cols) return MOE_ERR_SHAPE;
+  if (groups == 0) return MOE_OK;
+  if (!in || !codes || !scales) return MOE_ERR_NULL;
+  if ((uintptr_t)codes & 15) return MOE_ERR_SHAPE;
+  return launch_mx_quantize_t(in, dtype == MOE_BF16, groups, rows, cols, codes, scales, debug_shuffle_seed,
+                              (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+MOE_API moe_status moe_mx_fwd_fc1(const moe_problem* p, const moe_routing* routing, const uint8_t* x_codes,
+                                  const uint8_t* x_scales, const uint8_t* w1t_codes, const uint8_t* w1t_scales,
+                                  void* h, void* act, void* stream) {
+  Plan pl;
+  moe_status s = validate(p, &pl);
+  if (s != MOE_OK) return s;
+  if (!pl.bf16) return MOE_ERR_DTYPE;
+  if (pl.D > kMxMaxK || pl.D % 128) return MOE_ERR_SHAPE;
+  if (!routing || !routing->counts || !routing->offsets || !routing->sched) return MOE_ERR_NULL;
+  if (pl.rows_cap > 0 && (!x_codes || !x_scales || !w1t_codes || !w1t_scales || !h || !act || !routing->row_tok))
+    return MOE_ERR_NULL;
+  RowGemmParams G{};
+  G.counts = routing->counts;
+  G.offsets = routing->offsets;
+  G.groups = pl.el;
+  G.ncu = device_cu_count();
+  G.sched = routing->sched;
+  G.list_hdr = 0;
+  G.list_at = kSchedHeader;
+  G.seed = p->debug_shuffle_seed;
+  // h = dequant(x)[row_tok] dequant(W1_g^T)^T; W1^T codes [F][D] read as [N=F][K=D]
+  G.N = pl.F;
+  G.K = pl.D;
+  G.a = x_codes;
+  G.lda = pl.D;  // bytes per row of codes
+  G.a_bytes = (uint32_t)(pl.T * pl.D);
+  G.a_rows = routing->row_tok;
+  G.a_scales = x_scales;
+  G.b = w1t_codes;
+  G.b_gstride = (int64_t)pl.F * pl.D;
+  G.ldb = pl.D;
+  G.b_bytes = (uint32_t)G.b_gstride;
+  G.b_scales = w1t_scales;
+  G.b_sgstride = (int64_t)pl.F * (pl.D / 32);
+  G.c = h;
+  G.ldc = pl.F;
+  G.c2 = act;
+  G.ldc2 = pl.F;
+  return launch_mx_rowgemm(G, kGemmFc1Fwd, rowgemm_grid(pl, pl.F), (hipStream_t)stream) == hipSuccess ? MOE_OK
+                                                                                                     : MOE_ERR_HIP;
+}
+
+MOE_API moe_status moe_mx_fwd_fc2(const moe_problem* p, const moe_routing* routing, const uint8_t* act_codes,
+                                  const uint8_t* act_scales, const uint8_t* w2t_codes, const uint8_t* w2t_scales,
+                                  void* y_or_rows, void* ws, size_t ws_bytes, moe_mode mode, void* stream) {
+  Plan pl;
+  moe_status s = validate(p, &pl);
+  if (s != MOE_OK) return s;
+  if (!pl.bf16) return MOE_ERR_DTYPE;
+  if (mode != MOE_DETERMINISTIC && mode != MOE_ATOMIC) return MOE_ERR_MODE;
+  if (pl.F > kMxMaxK || pl.F % 128) return MOE_ERR_SHAPE;
+  const bool at = mode == MOE_ATOMIC;
+  if (!routing || !routing->counts || !routing->offsets || !routing->sched) return MOE_ERR_NULL;
+  if (pl.T > 0 && (!y_or_rows || !routing->slot_row || !routing->topk_prob)) return MOE_ERR_NULL;
+  if (pl.rows_cap > 0 && (!act_codes || !act_scales || !w2t_codes || !w2t_scales || !routing->row_tok ||
+                          !routing->row_prob))
+    return MOE_ERR_NULL;
+  const FwdWs L = fwd_layout(pl, p->combine, at);
+  s = check_ws(ws, ws_bytes, L.total);
+  if (s != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  const uint64_t seed = p->debug_shuffle_seed;
+  void* orows = p->combine ? (void*)(wsb + L.orows) : y_or_rows;
+  RowGemmParams G{};
+  G.counts = routing->counts;
+  G.offsets = routing->offsets;
+  G.groups = pl.el;
+  G.ncu = device_cu_count();
+  G.sched = routing->sched;
+  G.list_hdr = 0;
+  G.list_at = kSchedHeader;
+  G.seed = seed;
+  // o = dequant(act) dequant(W2_g^T)^T; W2^T codes [D][F] read as [N=D][K=F]
+  G.N = pl.D;
+  G.K = pl.F;
+  G.a = act_codes;
+  G.lda = pl.F;
+  G.a_bytes = (uint32_t)(pl.rows_cap * pl.F);
+  G.a_scales = act_scales;
+  G.b = w2t_codes;
+  G.b_gstride = (int64_t)pl.D * pl.F;
+  G.ldb = pl.F;
+  G.b_bytes = (uint32_t)G.b_gstride;
+  G.b_scales = w2t_scales;
+  G.b_sgstride = (int64_t)pl.D * (pl.F / 32);
+  G.c = orows;
+  G.ldc = pl.D;
+  if (launch_mx_rowgemm(G, kGemmFc2Fwd, rowgemm_grid(pl, pl.D), st) != hipSuccess) return MOE_ERR_HIP;
+  if (p->combine) {
+    if (!at) {
+      if (launch_gather_combine(orows, routing->slot_row, routing->topk_prob, pl.T, pl.k, pl.D, y_or_rows, pl.bf16,
+                                seed, st) != hipSuccess)
+        return MOE_ERR_HIP;
+    } else {
+      float* y32 = (float*)(wsb + L.y32);
+      if (launch_zero(y32, pl.T * pl.D, st) != hipSuccess ||
+          launch_scatter_add(orows, routing->offsets, pl.el, routing->row_tok, routing->row_prob, pl.rows_cap, pl.D,
+                             y32, pl.bf16, seed, st) != hipSuccess ||
+          launch_cast(y32, y_or_rows, pl.T * pl.D, pl.bf16, st) != hipSuccess)
+        return MOE_ERR_HIP;
+    }
+  }
+  return MOE_OK;
+}
+
 MOE_API moe_status moe_fingerprint(const void* data, moe_dtype dtype, int ndim, const int64_t* shape,
                                    int64_t chunk_elems, uint64_t* chunk_hashes, uint64_t* total,
                                    void* stream) {

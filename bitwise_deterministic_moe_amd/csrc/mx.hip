@@ -51,6 +51,63 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const T* in, int64_t r
   if ((threadIdx.x & 3) == 0) scales[(8 * i) / 32] = (uint8_t)(se + 127);
 }
 
+// MXFP8 of the transpose of each group's [rows, cols] matrix: a block is 32
+// consecutive rows of one column, and the codes of column c are written as
+// row c of the output (codes [groups][cols][rows], scales
+// [groups][cols][rows/32]).  Same encoding as mx_quantize_kernel.  One thread
+// per (column, 32-row block): the 32 loads of a row step are contiguous over
+// the wave's 64 columns, and each thread writes its block's 32 codes as two
+// 16-byte stores.
+template <typename T>
+__global__ __launch_bounds__(256) void mx_quantize_t_kernel(const T* in, int64_t groups, int64_t rows, int64_t cols,
+                                                            uint8_t* codes, uint8_t* scales, uint64_t seed) {
+  const int64_t ncb = (cols + 255) / 256, nrb = rows / 32;
+  const int64_t u = map_unit(blockIdx.x, groups * nrb * ncb, seed);
+  if (u < 0) return;
+  const int64_t g = u / (nrb * ncb), rb = (u / ncb) % nrb, cb = u % ncb;
+  const int64_t c = cb * 256 + threadIdx.x;
+  if (c >= cols) return;
+  const T* src = in + (g * rows + rb * 32) * cols + c;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    if constexpr (sizeof(T) == 2)
+      v[i] = bf16_to_f32(src[(int64_t)i * cols]);
+    else
+      v[i] = src[(int64_t)i * cols];
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(v[i]) & 0x7fffffffu);
+  const int ef = (int)(m >> 23);
+  const int se = ef == 0 ? -127 : min(127, max(-127, ef - 127 - 8));
+  const float f = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se, exact
+  uint32_t w[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    w[q] = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) w[q] |= e4m3_rne(v[4 * q + b] * f) << (8 * b);
+  }
+  uint8_t* dst = codes + (g * cols + c) * rows + rb * 32;
+  *(u32x4_t*)dst = u32x4_t{w[0], w[1], w[2], w[3]};
+  *(u32x4_t*)(dst + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
+  scales[(g * cols + c) * nrb + rb] = (uint8_t)(se + 127);
+}
+
+hipError_t launch_mx_quantize_t(const void* in, bool bf16, int64_t groups, int64_t rows, int64_t cols,
+                                uint8_t* codes, uint8_t* scales, uint64_t seed, hipStream_t st) {
+  const int64_t units = groups * (rows / 32) * ((cols + 255) / 256);
+  if (units == 0) return hipSuccess;
+  const int64_t grid = grid_for_units(units);
+  if (bf16)
+    mx_quantize_t_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)in, groups, rows, cols, codes, scales,
+                                                         seed);
+  else
+    mx_quantize_t_kernel<float><<<grid, 256, 0, st>>>((const float*)in, groups, rows, cols, codes, scales, seed);
+  return hipGetLastError();
+}
+
 hipError_t launch_mx_quantize(const void* in, bool bf16, int64_t rows, int64_t cols, uint8_t* codes,
                               uint8_t* scales, uint64_t seed, hipStream_t st) {
   const int64_t n8 = rows * cols / 8;

@@ -469,6 +469,66 @@ moe_status moe_sgd_step(float* master, const float* grad, int64_t n, float lr, v
 moe_status moe_mx_quantize(const void* in, moe_dtype dtype, int64_t rows, int64_t cols, uint8_t* codes,
                            uint8_t* scales, uint64_t debug_shuffle_seed, void* stream);
 
+/* MXFP8 block quantisation along the other axis: for each of `groups`
+ * row-major [rows, cols] matrices, the E4M3 codes and E8M0 scales of its
+ * transpose, i.e. a block is 32 consecutive ROWS of one column, and the
+ * codes of column c form row c of the output.  Same encoding as
+ * moe_mx_quantize (OCP MX v1.0).  This is the form the forward GEMMs read
+ * the weights in, contiguous along the contraction (the d_model axis of W1,
+ * the d_ffn axis of W2), as MXFP8 training keeps a copy quantised along each
+ * axis a GEMM contracts (French article, section "Méthodologie de débogage
+ * du non-déterminisme": MXFP8 runs fingerprint their encoded values and
+ * scale buffers).
+ *   in      DEVICE [groups, rows, cols] of dtype (MOE_F32 or MOE_BF16); rows a
+ *           positive multiple of 32; finite values
+ *   codes   DEVICE uint8 [groups, cols, rows], 16-byte aligned, output
+ *   scales  DEVICE uint8 [groups, cols, rows/32], output
+ * Every output byte is exact, so the outputs are bit-identical whatever the
+ * order.  Errors: MOE_ERR_DTYPE, MOE_ERR_SHAPE (rows not a positive multiple
+ * of 32, cols <= 0, more than 2^40 elements, misaligned codes), MOE_ERR_NULL;
+ * MOE_ERR_HIP for a launch failure. */
+moe_status moe_mx_quantize_t(const void* in, moe_dtype dtype, int64_t groups, int64_t rows, int64_t cols,
+                             uint8_t* codes, uint8_t* scales, uint64_t debug_shuffle_seed, void* stream);
+
+/* MXFP8 grouped GEMM, the low-precision variant of the forward's fc1:
+ *   h[r, :]   = bf16(dequant(x)[row_tok[r], :] . dequant(W1_e^T)^T)   (r a
+ *               routed row of local expert e), float32 accumulation in a fixed
+ *               k order (64 k per scaled MFMA, slices ascending);
+ *   act[r, :] = bf16(relu(h[r, :])^2) of the rounded h (the input of fc2).
+ * Format and sources as moe_mx_quantize / moe_mx_quantize_t.
+ *   x_codes / x_scales    DEVICE uint8 [T, D] / [T, D/32] (moe_mx_quantize of x)
+ *   w1t_codes / w1t_scales DEVICE uint8 [num_local, F, D] / [num_local, F, D/32]
+ *                         (moe_mx_quantize_t of W1 [num_local, D, F])
+ *   h, act                DEVICE bf16 [rows_cap, F] outputs; rows < R written
+ * routing: as written by moe_fwd (top-k, permutation and work list).  The
+ * problem must be bf16 with D a multiple of 128 and at most 2048.  Errors:
+ * MOE_ERR_DTYPE, MOE_ERR_SHAPE, MOE_ERR_NULL before anything is enqueued;
+ * MOE_ERR_HIP for a launch failure. */
+moe_status moe_mx_fwd_fc1(const moe_problem* p, const moe_routing* routing, const uint8_t* x_codes,
+                          const uint8_t* x_scales, const uint8_t* w1t_codes, const uint8_t* w1t_scales, void* h,
+                          void* act, void* stream);
+
+/* MXFP8 grouped GEMM, the low-precision variant of the forward's fc2, with
+ * the forward's combine:
+ *   o[r, :] = bf16(dequant(act)[r, :] . dequant(W2_e^T)^T), float32
+ *             accumulation in a fixed k order;
+ *   combine=1: y_t = sum_j p_tj o_(t,j), slots j ascending, float32
+ *             accumulation from 0, rounded once (MOE_DETERMINISTIC; MOE_ATOMIC:
+ *             the scatter-add control); combine=0: the o rows.
+ *   act_codes / act_scales DEVICE uint8 [rows_cap, F] / [rows_cap, F/32]
+ *                         (moe_mx_quantize of moe_mx_fwd_fc1's act)
+ *   w2t_codes / w2t_scales DEVICE uint8 [num_local, D, F] / [num_local, D, F/32]
+ *                         (moe_mx_quantize_t of W2 [num_local, F, D])
+ *   y_or_rows             DEVICE bf16 [T, D] (combine=1) or [rows_cap, D]
+ *   ws, ws_bytes          the forward workspace of moe_workspace_size (mode)
+ * The problem must be bf16 with F a multiple of 128 and at most 2048.
+ * Errors: MOE_ERR_DTYPE, MOE_ERR_SHAPE, MOE_ERR_MODE, MOE_ERR_NULL,
+ * MOE_ERR_WORKSPACE before anything is enqueued; MOE_ERR_HIP for a launch
+ * failure. */
+moe_status moe_mx_fwd_fc2(const moe_problem* p, const moe_routing* routing, const uint8_t* act_codes,
+                          const uint8_t* act_scales, const uint8_t* w2t_codes, const uint8_t* w2t_scales,
+                          void* y_or_rows, void* ws, size_t ws_bytes, moe_mode mode, void* stream);
+
 /* Diagnostic for the measurement of the percent of bf16 dense peak: the
  * attainable MFMA rate of the device.  Enqueues on `stream` one launch of
  * `blocks` workgroups of 4 waves; every wave issues iters x 8 independent

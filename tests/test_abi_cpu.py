@@ -236,3 +236,29 @@ def test_nvfp4_quantize_validation_returns_before_enqueue(lib):
     assert lib.moe_nvfp4_quantize(fake, 1, 4, 64, fake, fake, None, 0, None) == 1          # no tensor scale
     assert lib.moe_nvfp4_quantize(None, 1, 4, 64, fake, fake, g, 0, None) == 1
     assert lib.moe_nvfp4_quantize(ctypes.c_void_p(0x1008), 1, 4, 64, fake, fake, g, 0, None) == 2   # misaligned
+
+
+def test_mx_forward_validation_returns_before_enqueue(lib):
+    fake = ctypes.c_void_p(0x1000)
+    r = moe._CRouting(*([0x2000] * 9))
+    cp = moe.Problem(**BASE).c()
+    # transposing quantiser: dtype, rows not a multiple of 32, NULL, misaligned codes, empty
+    assert lib.moe_mx_quantize_t(fake, 2, 1, 64, 64, fake, fake, 0, None) == 3
+    assert lib.moe_mx_quantize_t(fake, 1, 1, 48, 64, fake, fake, 0, None) == 2
+    assert lib.moe_mx_quantize_t(None, 1, 1, 64, 64, fake, fake, 0, None) == 1
+    assert lib.moe_mx_quantize_t(fake, 1, 1, 64, 64, ctypes.c_void_p(0x1008), fake, 0, None) == 2
+    assert lib.moe_mx_quantize_t(None, 1, 0, 64, 64, None, None, 0, None) == 0
+    # fc1: D beyond the staged scales, float32 problem, NULL operand
+    big = moe.Problem(**{**BASE, "d_model": 4096}).c()
+    assert lib.moe_mx_fwd_fc1(ctypes.byref(big), ctypes.byref(r), fake, fake, fake, fake, fake, fake, None) == 2
+    f32 = moe.Problem(**{**BASE, "dtype": "f32"}).c()
+    assert lib.moe_mx_fwd_fc1(ctypes.byref(f32), ctypes.byref(r), fake, fake, fake, fake, fake, fake, None) == 3
+    assert lib.moe_mx_fwd_fc1(ctypes.byref(cp), ctypes.byref(r), None, fake, fake, fake, fake, fake, None) == 1
+    # fc2: F beyond the staged scales, mode, workspace too small
+    bigf = moe.Problem(**{**BASE, "d_ffn": 4096}).c()
+    assert lib.moe_mx_fwd_fc2(ctypes.byref(bigf), ctypes.byref(r), fake, fake, fake, fake, fake, fake, 1 << 40, 0,
+                              None) == 2
+    assert lib.moe_mx_fwd_fc2(ctypes.byref(cp), ctypes.byref(r), fake, fake, fake, fake, fake,
+                              ctypes.c_void_p(0x100000), 1 << 40, 7, None) == 5
+    assert lib.moe_mx_fwd_fc2(ctypes.byref(cp), ctypes.byref(r), fake, fake, fake, fake, fake,
+                              ctypes.c_void_p(0x100000), 16, 0, None) == 4
