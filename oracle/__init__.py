@@ -14,5 +14,8 @@ from .fingerprint import fingerprint, mix64, DTYPE_CODE  # noqa: F401
 from .router import (  # noqa: F401
     router_logits, router_probs, router_dlogits, router_backward, router_loss,
 )
-from .mx import e4m3_decode, e4m3_encode, e8m0_decode, mx_quantize, mx_quantize_fast, mx_dequantize, mx_grouped_rows  # noqa: F401,E402
+from .mx import (  # noqa: F401,E402
+    e4m3_decode, e4m3_encode, e8m0_decode, mx_quantize, mx_quantize_fast, mx_dequantize, mx_grouped_rows,
+    MXW_PAD, mx_pad_offsets, mx_quantize_expert_rows, act_p_f32, mx_wgrad,
+)
 from .nvfp4 import e2m1_decode, e2m1_encode, nvfp4_quantize, nvfp4_dequantize  # noqa: F401,E402

@@ -143,3 +143,82 @@ def mx_grouped_rows(a_codes, a_scales, b_codes, b_scales, offsets) -> np.ndarray
         if hi > lo:
             out[lo:hi] = A[lo:hi] @ mx_dequantize(b_codes[e], b_scales[e]).T
     return out
+
+
+# ------------------------------------------------------------ weight gradients
+# The weight gradients contract over the routed rows of one expert,
+#   dW1_e = X_e^T dH_e   and   dW2_e = A_e^T dY_e,   A = p relu(h)^2,
+# where X_e and dY_e are the rows of the expert's tokens.  A block scale
+# factors out of a product only if it is constant along the contraction, so
+# these four operands are quantised along the rows: a block is 32
+# consecutive routed rows of one expert in one column, the first block
+# starting at the expert's first row and the last one completed with zero
+# rows.  The pages name the format only; this layout is the reading of this
+# library.  Each expert's rows are laid out in a multiple of MXW_PAD rows
+# (two blocks: one 64-element step of the scaled product), zero past its
+# count.
+
+MXW_PAD = 64
+
+
+def mx_pad_offsets(counts, pad: int = MXW_PAD) -> np.ndarray:
+    """First padded row of each expert (and the total at the end): the row
+    counts rounded up to a multiple of ``pad``, prefix-summed."""
+    c = np.asarray(counts, np.int64)
+    padded = (c + pad - 1) // pad * pad
+    return np.concatenate([[0], np.cumsum(padded)]).astype(np.int64)
+
+
+def mx_quantize_expert_rows(values: np.ndarray, offsets, pad: int = MXW_PAD):
+    """MXFP8 of each expert's rows along the row axis.
+
+    values: float64 [R, M], the exact input values of the routed rows,
+    expert-major (rows offsets[e]..offsets[e+1] belong to expert e).
+    Returns (codes uint8 [M, P], scales uint8 [M, P/32], poff): column j of
+    expert e's range poff[e] <= j < poff[e+1] holds its routed row
+    offsets[e] + (j - poff[e]), transposed; columns past its count are zero
+    rows (code 0; a block of them alone takes scale byte 0)."""
+    values = np.asarray(values, np.float64)
+    offsets = np.asarray(offsets, np.int64)
+    M = values.shape[1]
+    poff = mx_pad_offsets(np.diff(offsets), pad)
+    P = int(poff[-1])
+    codes = np.zeros((M, P), np.uint8)
+    scales = np.zeros((M, P // BLOCK), np.uint8)
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        p0, p1 = int(poff[e]), int(poff[e + 1])
+        if p1 == p0:
+            continue
+        block = np.zeros((M, p1 - p0))
+        block[:, : hi - lo] = values[lo:hi].T
+        c, s = mx_quantize_fast(block)
+        codes[:, p0:p1] = c
+        scales[:, p0 // BLOCK: p1 // BLOCK] = s
+    return codes, scales, poff
+
+
+def act_p_f32(h, p) -> np.ndarray:
+    """p * relu(h)^2 as the weight-gradient quantiser forms it, in float32:
+    r = h where h > 0, else +0; then r * r and that times p, each product
+    rounded to float32 (p: one routing weight per row, h [rows, F])."""
+    h = np.asarray(h, np.float32)
+    p = np.asarray(p, np.float32).reshape(-1, 1)
+    r = np.where(h > 0, h, np.float32(0.0)).astype(np.float32)
+    return (p * (r * r)).astype(np.float32)
+
+
+def mx_wgrad(a_codes, a_scales, b_codes, b_scales, poff, experts=None):
+    """Yields (e, dW_e) with dW_e = dequant(A_e) dequant(B_e)^T in float64,
+    A_e / B_e the columns poff[e]..poff[e+1] of the row-quantised operands
+    ([M, P] and [N, P]); an expert without rows gets zeros."""
+    poff = np.asarray(poff, np.int64)
+    M, N = a_codes.shape[0], b_codes.shape[0]
+    for e in (range(len(poff) - 1) if experts is None else experts):
+        p0, p1 = int(poff[e]), int(poff[e + 1])
+        if p1 == p0:
+            yield e, np.zeros((M, N))
+            continue
+        a = mx_dequantize(a_codes[:, p0:p1], a_scales[:, p0 // BLOCK: p1 // BLOCK])
+        b = mx_dequantize(b_codes[:, p0:p1], b_scales[:, p0 // BLOCK: p1 // BLOCK])
+        yield e, a @ b.T

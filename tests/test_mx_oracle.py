@@ -171,3 +171,156 @@ def test_vectorised_quantise_equals_the_exact_one(seed):
     a, b = mx.mx_quantize(rows.astype(np.float64)), mx.mx_quantize_fast(rows.astype(np.float64))
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1], b[1])
+
+
+# ------------------------------------------------------------ weight gradients
+def _blocks_by_hand(values, lo, hi, pad):
+    """Codes and scales of one expert built block by block with the exact
+    quantiser: block b of column m is rows lo + 32 b .. of column m, zeros
+    past hi."""
+    n = hi - lo
+    P = (n + pad - 1) // pad * pad
+    M = values.shape[1]
+    codes = np.zeros((M, P), np.uint8)
+    scales = np.zeros((M, P // 32), np.uint8)
+    for m in range(M):
+        for b in range(P // 32):
+            blk = [values[lo + 32 * b + j, m] if 32 * b + j < n else 0.0 for j in range(32)]
+            c, s = mx.mx_quantize(np.array([blk]))
+            codes[m, 32 * b: 32 * b + 32] = c[0]
+            scales[m, b] = s[0, 0]
+    return codes, scales
+
+
+def test_pad_offsets():
+    np.testing.assert_array_equal(mx.mx_pad_offsets([0, 1, 64, 65, 128, 0]), [0, 0, 64, 128, 256, 384, 384])
+    np.testing.assert_array_equal(mx.mx_pad_offsets([5, 40], pad=32), [0, 32, 96])
+
+
+def test_expert_rows_one_expert_is_the_transposed_row_quantiser():
+    rng = np.random.default_rng(31)
+    v = rng.standard_normal((128, 48)) * np.exp2(rng.integers(-10, 10, (128, 48)))
+    codes, scales, poff = mx.mx_quantize_expert_rows(v, [0, 128])
+    rc, rs = mx.mx_quantize_fast(v.T)
+    np.testing.assert_array_equal(poff, [0, 128])
+    np.testing.assert_array_equal(codes, rc)
+    np.testing.assert_array_equal(scales, rs)
+
+
+def test_expert_rows_blocks_start_at_each_experts_first_row():
+    rng = np.random.default_rng(32)
+    counts = [5, 0, 40, 64, 1, 70]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    v = rng.standard_normal((off[-1], 3)) * np.exp2(rng.integers(-6, 6, (off[-1], 1)))
+    codes, scales, poff = mx.mx_quantize_expert_rows(v, off)
+    for e in range(len(counts)):
+        c, s = _blocks_by_hand(v, off[e], off[e + 1], 64)
+        np.testing.assert_array_equal(codes[:, poff[e]:poff[e + 1]], c, err_msg=str(e))
+        np.testing.assert_array_equal(scales[:, poff[e] // 32: poff[e + 1] // 32], s, err_msg=str(e))
+    # a block shifted by one row (blocks counted from the start of all rows
+    # instead of the expert's) gives other bytes
+    shifted = _blocks_by_hand(v, off[2] - 1, off[3] - 1, 64)
+    assert not np.array_equal(codes[:, poff[2]:poff[3]], shifted[0])
+
+
+def test_expert_rows_depend_only_on_their_own_rows():
+    rng = np.random.default_rng(33)
+    off = np.array([0, 30, 100, 101])
+    v = rng.standard_normal((101, 8))
+    c0, s0, poff = mx.mx_quantize_expert_rows(v, off)
+    w = v.copy()
+    w[30:100] *= 1000.0
+    c1, s1, _ = mx.mx_quantize_expert_rows(w, off)
+    keep = np.r_[poff[0]:poff[1], poff[2]:poff[3]]
+    np.testing.assert_array_equal(c0[:, keep], c1[:, keep])
+    np.testing.assert_array_equal(s0[:, keep[::32] // 32], s1[:, keep[::32] // 32])
+    assert not np.array_equal(s0[:, poff[1] // 32: poff[2] // 32], s1[:, poff[1] // 32: poff[2] // 32])
+
+
+def test_padding_rows_are_zero_codes_and_an_empty_block_takes_scale_zero():
+    v = np.full((3, 4), 5.0)
+    codes, scales, poff = mx.mx_quantize_expert_rows(v, [0, 3])
+    assert codes.shape == (4, 64) and scales.shape == (4, 2)
+    assert np.all(codes[:, 3:] == 0) and np.all(scales[:, 1] == 0)
+    assert np.all(scales[:, 0] == 127 + 2 - 8)             # floor(log2 5) - 8
+    assert np.all(mx.mx_dequantize(codes, scales)[:, :3] == 5.0)
+
+
+def _small_ints(rng, shape):
+    """Integers in [-8, 8]: with any block maximum among them, every element
+    times 2^-scale is an E4M3 value, so quantisation is exact."""
+    return rng.integers(-8, 9, shape).astype(np.float64)
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_wgrad_equals_the_exact_product_on_representable_values(seed):
+    rng = np.random.default_rng(40 + seed)
+    counts = [37, 0, 64, 100]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    R, D, F = int(off[-1]), 32, 48
+    x = _small_ints(rng, (R, D)) * 2.0 ** -7
+    dh = _small_ints(rng, (R, F)) * 2.0 ** 5
+    xc, xs, poff = mx.mx_quantize_expert_rows(x, off)
+    hc, hs, _ = mx.mx_quantize_expert_rows(dh, off)
+    np.testing.assert_array_equal(mx.mx_dequantize(xc, xs)[:, poff[0]:poff[0] + 37], x[:37].T)
+    for e, dw in mx.mx_wgrad(xc, xs, hc, hs, poff):
+        lo, hi = off[e], off[e + 1]
+        want = x[lo:hi].T @ dh[lo:hi]                        # exact: small dyadic integers
+        assert dw.shape == (D, F)
+        np.testing.assert_array_equal(dw, want, err_msg=str(e))
+    # planted mistakes: blocks of another expert, or the operands swapped
+    bad = poff.copy()
+    bad[2:] += 32
+    bad[-1] = min(bad[-1], xc.shape[1])
+    assert not np.array_equal(dict(mx.mx_wgrad(xc, xs, hc, hs, bad))[2], x[off[2]:off[3]].T @ dh[off[2]:off[3]])
+    assert dict(mx.mx_wgrad(hc, hs, xc, xs, poff))[0].shape == (F, D)
+
+
+def test_wgrad_within_the_quantisation_bound_on_gaussian_rows():
+    rng = np.random.default_rng(44)
+    off = np.array([0, 150])
+    a, b = rng.standard_normal((150, 16)), rng.standard_normal((150, 16))
+    ac, as_, poff = mx.mx_quantize_expert_rows(a, off)
+    bc, bs, _ = mx.mx_quantize_expert_rows(b, off)
+    dw = dict(mx.mx_wgrad(ac, as_, bc, bs, poff))[0]
+    exact = a.T @ b
+
+    def elem_bound(v, sc):
+        # half an E4M3 step: 2^-4 relative for normals, 2^-10 of the block
+        # scale for subnormals
+        x = np.repeat(2.0 ** (sc.astype(np.int64) - 127), 32, axis=1)[:, :150].T
+        return np.abs(v) * 2.0 ** -4 + x * 2.0 ** -10
+
+    ea, eb = elem_bound(a, as_), elem_bound(b, bs)
+    bound = ea.T @ np.abs(b) + np.abs(a).T @ eb + ea.T @ eb
+    assert np.all(np.abs(dw - exact) <= bound * (1 + 1e-12))
+
+
+def test_act_p_f32():
+    h = np.array([[2.0 ** -3, -1.0, -0.0, 0.0, 3.0]], np.float32)
+    p = np.array([0.25], np.float32)
+    a = mx.act_p_f32(h, p)
+    np.testing.assert_array_equal(a, [[2.0 ** -8, 0.0, 0.0, 0.0, 2.25]])
+    assert not np.any(np.signbit(a))                         # relu gives +0
+    rng = np.random.default_rng(45)
+    h = rng.standard_normal((64, 32)).astype(np.float32)
+    p = rng.uniform(0.01, 1.0, 64).astype(np.float32)
+    a = mx.act_p_f32(h, p).astype(np.float64)
+    exact = p.astype(np.float64)[:, None] * np.maximum(h.astype(np.float64), 0.0) ** 2
+    assert np.all(np.abs(a - exact) <= exact * 2.0 ** -23)   # two float32 roundings
+    assert a.dtype == np.float64 and mx.act_p_f32(h, p).dtype == np.float32
+
+
+def test_act_p_f32_squares_before_scaling():
+    """The order of the two roundings is fixed (it decides codes): r * r
+    first, then times p; find inputs where the other order differs."""
+    rng = np.random.default_rng(46)
+    h = rng.uniform(0.5, 2.0, 4096).astype(np.float32)
+    p = rng.uniform(0.1, 1.0, 4096).astype(np.float32)
+    other = (p * h) * h
+    a = mx.act_p_f32(h.reshape(-1, 1), p)[:, 0]
+    differ = a != other
+    assert differ.any()
+    r64 = h.astype(np.float64) ** 2
+    sq = r64.astype(np.float32).astype(np.float64)             # r * r rounded once
+    np.testing.assert_array_equal(a, (sq * p.astype(np.float64)).astype(np.float32))
