@@ -419,6 +419,8 @@ def main():
         result["mx_dgrad_fc2"] = measured_mx_dgrad_fc2(cfg, wl.prob, wl.routing, wl.dy, wl.w2, wl.h, b["ws1"],
                                                        st.get("fc2_dgrad_dprob_partials"))
         result["mx_fwd"] = measured_mx_fwd(cfg, wl, m["fwd"]["stages_ms"])
+        result["mx_wgrad"] = measured_mx_wgrad(cfg, wl, b["dh"], st.get("wgrad_prep_act_p", 0.0) +
+                                               st.get("wgrad_fc1_fc2_ordered", float("nan")))
         result["fingerprint"] = measured_fingerprint(b["dw1"])
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, wl.host, R)
@@ -678,6 +680,54 @@ def measured_mx_fwd(cfg, wl, bf16_stages, reps=20):
     res["fc2_combine"]["bf16_stage_ms"] = round(bf16_stages.get("fc2_fwd", float("nan")) +
                                                 bf16_stages.get("combine_gather", 0.0), 5)
     return res
+
+
+def measured_mx_wgrad(cfg, wl, dh, bf16_ms, reps=10):
+    """The MXFP8 weight gradients on the workload's x, dY, saved h and the
+    backward's dh: the four row-quantised encodings (moe_mx_quantize_wgrad)
+    and the GEMM of both dW (moe_mx_wgrad), average of `reps` calls each,
+    beside the bf16 weight-gradient stages.  The GEMM stores 2 El D F float32
+    and reads each operand about once from HBM; its bound is
+    max(FLOP time at the fp8 peak, those bytes at HBM peak)."""
+    import torch
+    import bitwise_deterministic_moe_amd as moe
+    if cfg.dtype != "bf16":
+        return None
+    D, F, el = cfg.d_model, cfg.d_ffn, cfg.num_local
+    srcs = (("x", wl.x, moe.MXW_TOKEN), ("dh", dh, moe.MXW_ROW), ("act", wl.h, moe.MXW_ACT_P),
+            ("dy", wl.dy, moe.MXW_TOKEN))
+    enc = {n: moe.moe_mx_quantize_wgrad(wl.prob, wl.routing, t, k) for n, t, k in srcs}
+    dw1, dw2 = moe.moe_mx_wgrad(wl.prob, wl.routing, enc["x"], enc["dh"], enc["act"], enc["dy"])
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        e0, e1 = _ev(), _ev()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def quantise_all():
+        for n, t, k in srcs:
+            moe.moe_mx_quantize_wgrad(wl.prob, wl.routing, t, k, *enc[n])
+
+    q_ms = timed(quantise_all)
+    g_ms = timed(lambda: moe.moe_mx_wgrad(wl.prob, wl.routing, enc["x"], enc["dh"], enc["act"], enc["dy"],
+                                          dw1=dw1, dw2=dw2))
+    rp = moe.moe_mx_wgrad_cols(wl.prob)
+    counts = wl.routing.counts.long()
+    P = int(((counts + 63) // 64 * 64).sum().item())
+    flops = 4.0 * wl.R * D * F
+    out_bytes = 2.0 * el * D * F * 4
+    in_bytes = 2.0 * (D + F) * P * (1 + 1 / 32)
+    bound_ms = max(flops / (FP8_PEAK_TFLOPS * 1e12), (out_bytes + in_bytes) / (HBM_PEAK_GBS * 1e9)) * 1e3
+    return {"gemm_ms": round(g_ms, 5), "gemm_tflops": round(flops / (g_ms * 1e-3) / 1e12, 1),
+            "gemm_GBs": round((out_bytes + in_bytes) / (g_ms * 1e-3) / 1e9, 1),
+            "gemm_bound_ms": round(bound_ms, 5), "gemm_frac_of_bound": round(bound_ms / g_ms, 4),
+            "quantise_ms": round(q_ms, 5), "padded_rows": P, "rows": wl.R, "rpad_cap": rp,
+            "bf16_wgrad_ms": round(bf16_ms, 5), "total_ms": round(q_ms + g_ms, 5)}
 
 
 def measured_traffic(workload, stage):

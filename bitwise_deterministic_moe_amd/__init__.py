@@ -19,6 +19,8 @@ __all__ = [
     "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad", "moe_fingerprint", "moe_sched_elems", "moe_mfma_rate",
     "moe_router_bwd", "moe_router_fwd", "moe_sgd_step", "moe_mx_quantize", "moe_mx_dgrad_fc1",
     "moe_bwd_dgrad_dprob_noalloc", "moe_mx_quantize_t", "moe_mx_fwd_fc1", "moe_mx_fwd_fc2", "EXPORTED_SYMBOLS",
+    "moe_mx_wgrad_cols", "moe_mx_quantize_wgrad", "moe_mx_wgrad", "MXW_TOKEN", "MXW_ROW", "MXW_ACT_P",
+    "moe_route",
 ]
 
 DETERMINISTIC = 0
@@ -32,7 +34,9 @@ EXPORTED_SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_rows_cap", "moe
                     "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd", "moe_sgd_step",
                     "moe_mx_quantize", "moe_mx_dgrad_fc1", "moe_mx_dgrad_fc2",
                     "moe_nvfp4_quantize", "moe_bwd_dgrad_dprob_noalloc", "moe_mx_quantize_t", "moe_mx_fwd_fc1",
-                    "moe_mx_fwd_fc2")
+                    "moe_mx_fwd_fc2", "moe_mx_wgrad_cols", "moe_mx_quantize_wgrad", "moe_mx_wgrad", "moe_route")
+# rows read by moe_mx_quantize_wgrad (moe_mxw_src)
+MXW_TOKEN, MXW_ROW, MXW_ACT_P = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -103,7 +107,11 @@ def load_library() -> ctypes.CDLL:
                                       ctypes.c_uint64, vp]
     lib.moe_mx_fwd_fc1.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_mx_fwd_fc2.argtypes = [P, R, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
-    for f in ("moe_rows_cap", "moe_sched_elems", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob",
+    lib.moe_mx_wgrad_cols.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+    lib.moe_route.argtypes = [P, vp, R, vp, sz, ctypes.c_int, vp]
+    lib.moe_mx_quantize_wgrad.argtypes = [P, R, vp, ctypes.c_int, vp, vp, vp]
+    lib.moe_mx_wgrad.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    for f in ("moe_route", "moe_mx_wgrad_cols", "moe_mx_quantize_wgrad", "moe_mx_wgrad", "moe_rows_cap", "moe_sched_elems", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob",
               "moe_bwd_dgrad_dprob_noalloc", "moe_mx_quantize_t", "moe_mx_fwd_fc1", "moe_mx_fwd_fc2",
               "moe_bwd_wgrad", "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd",
               "moe_sgd_step", "moe_mx_quantize", "moe_mx_dgrad_fc1", "moe_mx_dgrad_fc2", "moe_nvfp4_quantize"):
@@ -257,6 +265,20 @@ def moe_fwd(prob: Problem, logits, x, w1, w2, mode: int = DETERMINISTIC, routing
     _check(lib.moe_fwd(ctypes.byref(cp), _ptr(logits), _ptr(x), _ptr(w1), _ptr(w2), ctypes.byref(cr), _ptr(h),
                        _ptr(y), _ptr(ws), ws.numel(), mode, _stream()), "moe_fwd")
     return routing, h, y
+
+
+def moe_route(prob: Problem, logits, mode: int = DETERMINISTIC, routing: Routing = None, ws=None, events=None):
+    """The routing stage of moe_fwd alone (top-k, permutation, work list).
+    Returns the routing."""
+    lib = load_library()
+    dev = logits.device
+    routing = routing or Routing.empty(prob, dev)
+    ws = _ws(moe_workspace_size(prob, mode)[0], ws, dev)
+    _need(logits, prob.tokens * prob.num_experts, torch.float32, "moe_route logits")
+    cp, cr = prob.c(events), routing.c()
+    _check(lib.moe_route(ctypes.byref(cp), _ptr(logits), ctypes.byref(cr), _ptr(ws), ws.numel(), mode, _stream()),
+           "moe_route")
+    return routing
 
 
 def moe_bwd_dgrad_dprob(prob: Problem, routing: Routing, dy, w1, w2, h, mode: int = DETERMINISTIC,
@@ -553,6 +575,62 @@ def moe_mx_fwd_fc2(prob: Problem, routing: Routing, act_mx, w2t_mx, mode: int = 
     _check(lib.moe_mx_fwd_fc2(ctypes.byref(cp), ctypes.byref(cr), _ptr(ac), _ptr(asc), _ptr(wc), _ptr(wsc), _ptr(y),
                               _ptr(ws), ws.numel(), mode, _stream()), "moe_mx_fwd_fc2")
     return y
+
+
+def moe_mx_wgrad_cols(prob: Problem) -> int:
+    """rpad_cap: columns of the MXFP8 weight-gradient operands (each expert's
+    routed rows padded to a multiple of 64)."""
+    v = ctypes.c_int64()
+    _check(load_library().moe_mx_wgrad_cols(ctypes.byref(prob.c()), ctypes.byref(v)), "moe_mx_wgrad_cols")
+    return v.value
+
+
+def moe_mx_quantize_wgrad(prob: Problem, routing: Routing, src: torch.Tensor, kind: int, codes=None, scales=None):
+    """MXFP8 of a weight-gradient operand along each expert's routed rows.
+    kind MXW_TOKEN: src [T, D] gathered by token (x, dY); MXW_ROW: src
+    [rows_cap, F] (dH); MXW_ACT_P: src = h [rows_cap, F], encodes
+    p relu(h)^2.  Returns (codes uint8 [cols, rpad_cap], scales uint8
+    [rpad_cap / 64, cols, 2]); columns past the padded total are not written."""
+    lib = load_library()
+    rp = moe_mx_wgrad_cols(prob)
+    cols = prob.d_model if kind == MXW_TOKEN else prob.d_ffn
+    rows = prob.tokens if kind == MXW_TOKEN else prob.rows_cap
+    _need(src, rows * cols, torch.bfloat16, "moe_mx_quantize_wgrad src")
+    if codes is None:
+        codes = torch.empty((cols, rp), dtype=torch.uint8, device=src.device)
+    if scales is None:
+        scales = torch.empty((rp // 64, cols, 2), dtype=torch.uint8, device=src.device)
+    _need(codes, cols * rp, torch.uint8, "moe_mx_quantize_wgrad codes")
+    _need(scales, cols * (rp // 32), torch.uint8, "moe_mx_quantize_wgrad scales")
+    cp, cr = prob.c(), routing.c()
+    _check(lib.moe_mx_quantize_wgrad(ctypes.byref(cp), ctypes.byref(cr), _ptr(src), kind, _ptr(codes), _ptr(scales),
+                                     _stream()), "moe_mx_quantize_wgrad")
+    return codes, scales
+
+
+def moe_mx_wgrad(prob: Problem, routing: Routing, x_mx, dh_mx, act_mx, dy_mx, dw1=None, dw2=None):
+    """MXFP8 weight gradients dW1 [num_local, D, F] and dW2 [num_local, F, D]
+    (float32) from the moe_mx_quantize_wgrad encodings of x (MXW_TOKEN), dH
+    (MXW_ROW), h (MXW_ACT_P) and dY (MXW_TOKEN)."""
+    lib = load_library()
+    rp = moe_mx_wgrad_cols(prob)
+    D, F, el = prob.d_model, prob.d_ffn, prob.local
+    ops = []
+    for (c, s), n, name in ((x_mx, D, "x"), (dh_mx, F, "dh"), (act_mx, F, "act"), (dy_mx, D, "dy")):
+        _need(c, n * rp, torch.uint8, f"moe_mx_wgrad {name} codes")
+        _need(s, n * (rp // 32), torch.uint8, f"moe_mx_wgrad {name} scales")
+        ops += [_ptr(c), _ptr(s)]
+    dev = x_mx[0].device
+    if dw1 is None:
+        dw1 = torch.empty((el, D, F), dtype=torch.float32, device=dev)
+    if dw2 is None:
+        dw2 = torch.empty((el, F, D), dtype=torch.float32, device=dev)
+    _need(dw1, el * D * F, torch.float32, "moe_mx_wgrad dw1")
+    _need(dw2, el * F * D, torch.float32, "moe_mx_wgrad dw2")
+    cp, cr = prob.c(), routing.c()
+    _check(lib.moe_mx_wgrad(ctypes.byref(cp), ctypes.byref(cr), *ops, _ptr(dw1), _ptr(dw2), _stream()),
+           "moe_mx_wgrad")
+    return dw1, dw2
 
 
 def moe_fingerprint(t: torch.Tensor, dtype: Optional[str] = None, chunk_elems: int = 65536,

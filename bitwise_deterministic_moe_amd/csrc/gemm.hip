@@ -789,6 +789,154 @@ DEV void mx_read_block(const uint8_t* op, const uint8_t* scales, int nkb, int kb
   sc = scales[row * nkb + (kb < nkb ? kb : nkb - 1)];
 }
 
+// E8M0 scales of an MXFP8 operand pair streamed through LDS with the codes,
+// for operands whose scales are laid out slice-major ([slices][rows][2]: the
+// two 32-code block scales of each row in each 64-code slice), so that the
+// 512 bytes of a 256-row tile's slice are contiguous.  Each wave issues one
+// 16-byte DMA per slice: wave 0 the A scales and wave 1 the B scales (lanes
+// 0..31), every other lane and wave a load past the buffer end, whose zeros
+// land in the wave's own KiB of the slot.  Slot layout: A scales at 0 (row
+// r: bytes 2r, 2r + 1), B scales at 1024.
+constexpr int kMxScaleSlot = 4096;
+struct MxRingScales {
+  bf::i32x4_t rs;
+  uint32_t voff;     // byte offset of this lane's 16 bytes of slice 0, or kOOB
+  uint32_t sstride;  // bytes per slice of the operand this wave loads
+  DEV void init(int wave, int lane, const uint8_t* a, uint32_t a_bytes, uint32_t a_off, uint32_t a_stride,
+                const uint8_t* b, uint32_t b_bytes, uint32_t b_off, uint32_t b_stride) {
+    const bool is_b = wave == 1;
+    rs = bf::make_rsrc(is_b ? b : a, is_b ? b_bytes : a_bytes);
+    sstride = is_b ? b_stride : a_stride;
+    voff = (wave < 2 && lane < 32) ? (is_b ? b_off : a_off) + (uint32_t)lane * 16u : bf::kOOB;
+  }
+  DEV void issue(uint32_t slot, int wave, int s, bool live) const {
+    bf::dma16(rs, slot + (uint32_t)wave * 1024u, live ? voff : bf::kOOB, live ? (uint32_t)s * sstride : 0u);
+  }
+};
+
+// Pipelined MXFP8 main loop of one 256-column tile over nsteps slices of 64
+// codes (nsteps even), accumulated into acc in a fixed order: slice by
+// slice, and within a slice A block by A block against B blocks 0..3.
+// Slices at or past nlive load as zeros; slice s reads operand bytes
+// (kslice0 + s) * 64 onward of each row.
+// Scales, RS == false: the scale of tile row r and 32-code block kb of the
+// call is s_sa[r * nkb + kb] (s_sb for B; kb past nkb - 1 reads nkb - 1,
+// and every byte read must be a finite scale); store_scales() writes those
+// LDS arrays from registers the caller loaded before the call: it runs
+// once the loads of slices 0..2 have been issued and every load issued
+// before them has landed.  RS == true: the scales come through the ring
+// (MxRingScales rsc, 4 slots of kMxScaleSlot bytes at s_sa), slice
+// kslice0 + s with the codes of slice s.
+// On return loads past the last slice may still be in flight and other
+// waves may still read LDS: the caller drains and synchronises before
+// reusing it.
+template <int NA, int WTM, bool RS, class StoreScales>
+DEV void mx_mainloop(uint16_t* lds, const bf::KcOperand& oa, const bf::KcOperand& ob, const MxRingScales& rsc,
+                     int kslice0, int nsteps, int nlive, const uint8_t* s_sa, const uint8_t* s_sb, int nkb,
+                     StoreScales store_scales, f32x16_t (&acc)[4][4], int wave, int lane, int wm, int wn) {
+  const uint32_t ring = bf::lds_base(lds);
+  const uint32_t sring = bf::lds_base(s_sa);
+  constexpr int NL = RS ? 9 : 8;   // loads per slice and thread
+  // slice s: 64 codes = 64 bytes per row, the byte offset of a bf16 slice of 32
+  auto issue = [&](int s, int i) __attribute__((always_inline)) {
+    const uint32_t st = ring + (uint32_t)(s & 3) * (bf::STAGE * 2);
+    if (i < bf::LOADS)
+      oa.issue1(st, wave, (kslice0 + s) * bf::BK, s < nlive, i);
+    else if (i < 2 * bf::LOADS)
+      ob.issue1(st + bf::OPER * 2, wave, (kslice0 + s) * bf::BK, s < nlive, i - bf::LOADS);
+    else
+      rsc.issue(sring + (uint32_t)(s & 3) * kMxScaleSlot, wave, kslice0 + s, s < nlive);
+  };
+  const int h = lane >> 5, r32 = lane & 31;
+  auto slot = [&](int s) { return (const uint8_t*)(lds + (s & 3) * bf::STAGE); };
+  auto read = [&](MxFrags& f, int s, auto G) __attribute__((always_inline)) {   // group G: A block G (G < 4) or B block G-4
+    constexpr int g = decltype(G)::value;
+    const uint8_t* st = slot(s);
+    if constexpr (RS) {
+      const uint8_t* ss = s_sa + (s & 3) * kMxScaleSlot;
+      if constexpr (g < NA)
+        mx_read_block(st, ss, 2, h, wm * WTM + g * 32 + r32, h, f.a[g], f.sa[g]);
+      else if constexpr (g >= 4)
+        mx_read_block(st + bf::OPER * 2, ss + 1024, 2, h, wn * 128 + (g - 4) * 32 + r32, h, f.b[g - 4], f.sb[g - 4]);
+    } else {
+      if constexpr (g < NA)
+        mx_read_block(st, s_sa, nkb, 2 * s + h, wm * WTM + g * 32 + r32, h, f.a[g], f.sa[g]);
+      else if constexpr (g >= 4)
+        mx_read_block(st + bf::OPER * 2, s_sb, nkb, 2 * s + h, wn * 128 + (g - 4) * 32 + r32, h, f.b[g - 4],
+                      f.sb[g - 4]);
+    }
+  };
+  // A block mb of fa against the four B blocks of fb
+  auto mma = [&](const MxFrags& fa, const MxFrags& fb, auto MB) __attribute__((always_inline)) {
+    constexpr int mb = decltype(MB)::value;
+    if constexpr (mb >= NA) return;
+    acc[mb][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb.b[0], fa.a[mb], acc[mb][0], 0, 0, 0, fb.sb[0], 0, fa.sa[mb]);
+    acc[mb][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb.b[1], fa.a[mb], acc[mb][1], 0, 0, 0, fb.sb[1], 0, fa.sa[mb]);
+    acc[mb][2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb.b[2], fa.a[mb], acc[mb][2], 0, 0, 0, fb.sb[2], 0, fa.sa[mb]);
+    acc[mb][3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb.b[3], fa.a[mb], acc[mb][3], 0, 0, 0, fb.sb[3], 0, fa.sa[mb]);
+  };
+  // prologue: slices 0..2 in flight; the scale words (loaded before them)
+  // stored; slice 0 landed and the stores done in every wave; B blocks read
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+#pragma unroll
+    for (int i = 0; i < NL; ++i) issue(s, i);
+  if constexpr (RS) {
+    asm volatile("s_waitcnt vmcnt(18)\n\ts_barrier" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+    store_scales();
+    asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  MxFrags f, g;      // f.a: A blocks of the current slice; f.b and g.b: B blocks, alternating by step
+  read(f, 0, std::integral_constant<int, 4>{});
+  read(f, 0, std::integral_constant<int, 5>{});
+  read(f, 0, std::integral_constant<int, 6>{});
+  read(f, 0, std::integral_constant<int, 7>{});
+  // step s: slice s+1 landed and every wave is done with slice s-1, whose slot
+  // takes slice s+3.  The A blocks of slice s are read one ahead of their
+  // MFMAs; the B blocks of slice s+1 (past the last slice: zero codes and a
+  // clamped scale index, never multiplied) are read into the other B set in
+  // between, so the sets swap roles each step and nothing is copied.
+  auto step = [&](int s, const MxFrags& bcur, MxFrags& bnext) __attribute__((always_inline)) {
+    if constexpr (RS)
+      asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    read(f, s, std::integral_constant<int, 0>{});
+    issue(s + 3, 0);
+    read(f, s, std::integral_constant<int, 1>{});
+    issue(s + 3, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f, bcur, std::integral_constant<int, 0>{});
+    read(bnext, s + 1, std::integral_constant<int, 4>{});
+    read(f, s, std::integral_constant<int, 2>{});
+    issue(s + 3, 2);
+    issue(s + 3, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f, bcur, std::integral_constant<int, 1>{});
+    read(bnext, s + 1, std::integral_constant<int, 5>{});
+    read(f, s, std::integral_constant<int, 3>{});
+    issue(s + 3, 4);
+    issue(s + 3, 5);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f, bcur, std::integral_constant<int, 2>{});
+    read(bnext, s + 1, std::integral_constant<int, 6>{});
+    read(bnext, s + 1, std::integral_constant<int, 7>{});
+    issue(s + 3, 6);
+    issue(s + 3, 7);
+    if constexpr (RS) issue(s + 3, 8);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f, bcur, std::integral_constant<int, 3>{});
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll 1
+  for (int s = 0; s < nsteps; s += 2) {
+    step(s, f, g);
+    step(s + 1, g, f);
+  }
+}
+
 // BMV: tile rows (256, or 192 as two wave rows of 96: NA = 3 A blocks a
 // wave).  EPI: kEpiStore (bf16 rows of C), kEpiStoreAct (also relu(C)^2 of
 // the rounded C, into c2) or kEpiDgrad2 (the fc2 dgrad epilogue on G = C).  With P.a_rows, A row r is row a_rows[r] of the codes
@@ -801,7 +949,6 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
   __shared__ __attribute__((aligned(16))) uint8_t s_sa[256 * (kMxMaxK / 32)];
   __shared__ __attribute__((aligned(16))) uint8_t s_sb[256 * (kMxMaxK / 32)];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t ring = bf::lds_base(lds);
   const int wm = wave >> 1, wn = wave & 1;
   RowTile t;
   if (row_tile<BMV, bf::BN>(P, t) != kTileGemm) return;
@@ -814,7 +961,7 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
   };
   // the tile's scales, 4-byte words, all loads issued up front (rows past the
   // tile's valid rows read row 0 of the tile: their codes load as zeros); they
-  // are stored to LDS once the slice prologue below has been issued
+  // are stored to LDS once the slice prologue has been issued
   constexpr int kSw = 256 * (kMxMaxK / 32) / 4 / 256;   // words per thread and operand, at most
   const int nw = 256 * (nkb / 4);
   uint32_t wa[kSw], wb[kSw];
@@ -833,14 +980,6 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
   });
   ob.init((const uint8_t*)P.b + (int64_t)t.g * P.b_gstride, P.b_bytes, wave, lane,
           [&](int r) -> uint32_t { return (uint32_t)((t.n0 + r) * P.ldb); });
-  const int nsteps = P.K / 64;
-  // slice s: 64 codes = 64 bytes per row, the byte offset of a bf16 slice of 32
-  auto issue = [&](int s, uint32_t st, int i) __attribute__((always_inline)) {
-    if (i < bf::LOADS)
-      oa.issue1(st, wave, s * bf::BK, s < nsteps, i);
-    else
-      ob.issue1(st + bf::OPER * 2, wave, s * bf::BK, s < nsteps, i - bf::LOADS);
-  };
   f32x16_t acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -848,87 +987,19 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-  const int h = lane >> 5, r32 = lane & 31;
-  auto slot = [&](int s) { return (const uint8_t*)(lds + (s & 3) * bf::STAGE); };
-  auto slot_addr = [&](int s) { return ring + (uint32_t)(s & 3) * (bf::STAGE * 2); };
-  auto read = [&](MxFrags& f, int s, auto G) __attribute__((always_inline)) {   // group G: A block G (G < 4) or B block G-4
-    constexpr int g = decltype(G)::value;
-    const uint8_t* st = slot(s);
-    if constexpr (g < NA)
-      mx_read_block(st, s_sa, nkb, 2 * s + h, wm * WTM + g * 32 + r32, h, f.a[g], f.sa[g]);
-    else if constexpr (g >= 4)
-      mx_read_block(st + bf::OPER * 2, s_sb, nkb, 2 * s + h, wn * 128 + (g - 4) * 32 + r32, h, f.b[g - 4],
-                    f.sb[g - 4]);
-  };
-  // A block mb of fa against the four B blocks of fb
-  auto mma = [&](const MxFrags& fa, const MxFrags& fb, auto MB) __attribute__((always_inline)) {
-    constexpr int mb = decltype(MB)::value;
-    if constexpr (mb >= NA) return;
-    acc[mb][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb.b[0], fa.a[mb], acc[mb][0], 0, 0, 0, fb.sb[0], 0, fa.sa[mb]);
-    acc[mb][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb.b[1], fa.a[mb], acc[mb][1], 0, 0, 0, fb.sb[1], 0, fa.sa[mb]);
-    acc[mb][2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb.b[2], fa.a[mb], acc[mb][2], 0, 0, 0, fb.sb[2], 0, fa.sa[mb]);
-    acc[mb][3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb.b[3], fa.a[mb], acc[mb][3], 0, 0, 0, fb.sb[3], 0, fa.sa[mb]);
-  };
-  // prologue: slices 0..2 in flight; the scale words (loaded before them)
-  // stored; slice 0 landed and the stores done in every wave; B blocks read
-#pragma unroll
-  for (int s = 0; s < 3; ++s)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) issue(s, slot_addr(s), i);
-  asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-#pragma unroll
-  for (int q = 0; q < kSw; ++q) {
-    const int idx = tid + 256 * q;
-    if (idx < nw) {
-      ((uint32_t*)s_sa)[idx] = wa[q];
-      ((uint32_t*)s_sb)[idx] = wb[q];
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  MxFrags f, g;      // f.a: A blocks of the current slice; f.b and g.b: B blocks, alternating by step
-  read(f, 0, std::integral_constant<int, 4>{});
-  read(f, 0, std::integral_constant<int, 5>{});
-  read(f, 0, std::integral_constant<int, 6>{});
-  read(f, 0, std::integral_constant<int, 7>{});
-  // step s: slice s+1 landed and every wave is done with slice s-1, whose slot
-  // takes slice s+3.  The A blocks of slice s are read one ahead of their
-  // MFMAs; the B blocks of slice s+1 (past the last slice: zero codes and a
-  // clamped scale index, never multiplied) are read into the other B set in
-  // between, so the sets swap roles each step and nothing is copied.
-  auto step = [&](int s, const MxFrags& bcur, MxFrags& bnext) __attribute__((always_inline)) {
-    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    read(f, s, std::integral_constant<int, 0>{});
-    issue(s + 3, slot_addr(s + 3), 0);
-    read(f, s, std::integral_constant<int, 1>{});
-    issue(s + 3, slot_addr(s + 3), 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(f, bcur, std::integral_constant<int, 0>{});
-    read(bnext, s + 1, std::integral_constant<int, 4>{});
-    read(f, s, std::integral_constant<int, 2>{});
-    issue(s + 3, slot_addr(s + 3), 2);
-    issue(s + 3, slot_addr(s + 3), 3);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(f, bcur, std::integral_constant<int, 1>{});
-    read(bnext, s + 1, std::integral_constant<int, 5>{});
-    read(f, s, std::integral_constant<int, 3>{});
-    issue(s + 3, slot_addr(s + 3), 4);
-    issue(s + 3, slot_addr(s + 3), 5);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(f, bcur, std::integral_constant<int, 2>{});
-    read(bnext, s + 1, std::integral_constant<int, 6>{});
-    read(bnext, s + 1, std::integral_constant<int, 7>{});
-    issue(s + 3, slot_addr(s + 3), 6);
-    issue(s + 3, slot_addr(s + 3), 7);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(f, bcur, std::integral_constant<int, 3>{});
-    __builtin_amdgcn_sched_barrier(0);
-  };
   // the number of slices is even (K is a multiple of 128)
-#pragma unroll 1
-  for (int s = 0; s < nsteps; s += 2) {
-    step(s, f, g);
-    step(s + 1, g, f);
-  }
+  const int nsteps = P.K / 64;
+  const MxRingScales none{};
+  mx_mainloop<NA, WTM, false>(lds, oa, ob, none, 0, nsteps, nsteps, s_sa, s_sb, nkb, [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < kSw; ++q) {
+      const int idx = tid + 256 * q;
+      if (idx < nw) {
+        ((uint32_t*)s_sa)[idx] = wa[q];
+        ((uint32_t*)s_sb)[idx] = wb[q];
+      }
+    }
+  }, acc, wave, lane, wm, wn);
   bf::block_barrier();
   if constexpr (EPI == kEpiDgrad2) {
     dgrad2_epilogue<WTM>(P, t, lds, acc, wm, wn, lane, tid, my_prob);
@@ -955,6 +1026,73 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
       }
     });
   }
+}
+
+// MXFP8 weight gradients, both matrices in one launch.  Unit (g, matrix,
+// 256x256 tile): dW1_g tiles take A = X^T codes (rows over d_model) and
+// B = dH^T codes (rows over d_ffn), dW2_g tiles A = act^T and B = dY^T; K
+// runs over the expert's padded routed rows, whose count is even in 64-code
+// slices or completed by one slice of zeros.  One workgroup accumulates a
+// tile over the whole K range in slice order and stores it once, so the
+// result does not depend on the launch order and needs no reduction.  The
+// scales (slice-major) stream through LDS with the codes.  An expert
+// without rows gets a zero tile.
+template <class T>
+DEV T pick(int c, T a, T b) {
+  return c ? a : b;
+}
+__global__ __launch_bounds__(256) void mx_wgrad_kernel(MxWgradParams P) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sc[4 * kMxScaleSlot];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles = (P.D / 256) * (P.F / 256);
+  const int64_t L = map_unit(blockIdx.x, (int64_t)P.groups * 2 * tiles, P.seed);
+  if (L < 0) return;
+  const int g = (int)(L / (2 * tiles)), mat = (int)(L / tiles) & 1, tile = (int)(L % tiles);
+  // selections on copies: a conditional over two members of the kernel
+  // argument is an lvalue and would move the argument to scratch
+  const int M = pick(mat, P.F, P.D), N = pick(mat, P.D, P.F);
+  const int m0 = (tile / (N / 256)) * 256, n0 = (tile % (N / 256)) * 256;
+  const uint8_t* ac = pick(mat, P.act_codes, P.x_codes);
+  const uint8_t* as = pick(mat, P.act_scales, P.x_scales);
+  const uint8_t* bc = pick(mat, P.dy_codes, P.dh_codes);
+  const uint8_t* bs = pick(mat, P.dy_scales, P.dh_scales);
+  float* dst = pick(mat, P.dw2, P.dw1) + (int64_t)g * P.D * P.F;
+  const int p0 = P.poff[g], nsl = (P.poff[g + 1] - p0) / 64;
+  bf::KcOperand oa, ob;
+  oa.init(ac, (uint32_t)(M * P.rpad), wave, lane, [&](int r) -> uint32_t { return (uint32_t)((m0 + r) * P.rpad + p0); });
+  ob.init(bc, (uint32_t)(N * P.rpad), wave, lane, [&](int r) -> uint32_t { return (uint32_t)((n0 + r) * P.rpad + p0); });
+  // slice-major scales: slice j of operand rows R at byte (j R + row) 2
+  MxRingScales rsc;
+  rsc.init(wave, lane, as, (uint32_t)(M * P.rpad / 32), (uint32_t)(((int64_t)(p0 / 64) * M + m0) * 2), (uint32_t)(2 * M),
+           bs, (uint32_t)(N * P.rpad / 32), (uint32_t)(((int64_t)(p0 / 64) * N + n0) * 2), (uint32_t)(2 * N));
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  mx_mainloop<4, 128, true>(lds, oa, ob, rsc, 0, (nsl + 1) & ~1, nsl, s_sc, s_sc, 2, [] {}, acc, wave, lane, wm, wn);
+  // every load (those of the zero slices past the end included) landed and
+  // every wave done with the ring before the epilogue stages through it
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  bf::block_barrier();
+  NoPre none;
+  NoPre::Data nd[2];
+  const __amdgpu_buffer_rsrc_t rd = buf(dst);
+  staged_epilogue((float*)lds, acc, wm, wn, lane, tid, bf::BM, none, nd, false, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
+    const uint32_t o = ((uint32_t)(m0 + m) * (uint32_t)N + n0 + col) * 4u;
+    __builtin_amdgcn_raw_buffer_store_b128(f32x4_t{v[0], v[1], v[2], v[3]}, rd, o, 0, kEpiNT);
+  });
+}
+
+hipError_t launch_mx_wgrad(const MxWgradParams& P, hipStream_t st) {
+  const int64_t units = (int64_t)P.groups * 2 * (P.D / 256) * (P.F / 256);
+  if (units == 0) return hipSuccess;
+  mx_wgrad_kernel<<<grid_for_units(units), 256, 0, st>>>(P);
+  return hipGetLastError();
 }
 
 // ================================================================= fp32

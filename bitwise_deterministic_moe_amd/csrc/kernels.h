@@ -67,6 +67,45 @@ struct RowGemmParams {
   int64_t b_sgstride;     // scale bytes between consecutive experts' B
 };
 constexpr int kMxMaxK = 2048;  // K bound of the MXFP8 row GEMM (its scales are staged in LDS)
+// MXFP8 weight-gradient operands: each expert's rows padded to a multiple of
+// kMxPad (two 32-row blocks, one 64-element step of the scaled MFMA)
+constexpr int kMxPad = 64;
+
+// MXFP8 weight gradients: dW1_g = X_g^T dH_g and dW2_g = A_g^T dY_g from
+// operands quantised along the routed rows (codes [cols][rpad], scales
+// slice-major [rpad / 64][cols][2]; expert g owns columns poff[g] ..
+// poff[g+1]).
+struct MxWgradParams {
+  const int32_t* poff;    // el + 1 padded row offsets (routing.sched)
+  int groups;             // local experts
+  int D, F;
+  int64_t rpad;           // bytes per codes row
+  const uint8_t* x_codes; const uint8_t* x_scales;      // [D][rpad]
+  const uint8_t* dh_codes; const uint8_t* dh_scales;    // [F][rpad]
+  const uint8_t* act_codes; const uint8_t* act_scales;  // [F][rpad]
+  const uint8_t* dy_codes; const uint8_t* dy_scales;    // [D][rpad]
+  float* dw1;             // [groups][D][F]
+  float* dw2;             // [groups][F][D]
+  uint64_t seed;
+};
+
+// Rows the weight-gradient quantiser reads (moe_mxw_src of the C ABI).
+enum { kMxwToken = 0, kMxwRow = 1, kMxwActP = 2 };
+struct MxWgradQuantParams {
+  const uint16_t* src;    // bf16: [tokens][cols] (token), [rows_cap][cols] (row, act_p: h)
+  int kind;
+  int64_t cols;
+  int64_t rpad;
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* poff;
+  int el;
+  const int32_t* row_tok;
+  const float* row_prob;
+  uint8_t* codes;         // [cols][rpad]
+  uint8_t* scales;        // [rpad / 64][cols][2]
+  uint64_t seed;
+};
 
 constexpr int kSideSlots = 1024;  // flat slots per side unit
 
@@ -161,6 +200,7 @@ struct RouteParams {
   int64_t mt_cap;    // capacity of the row-tile list
   int64_t list2_at;  // int32 offset of the second row-tile list
   int64_t aux_at;    // int32 offset of the weight-gradient unit side table
+  int64_t pad_at;    // int32 offset of the padded row offsets
 };
 
 // routing.sched: [0] row tiles of bm rows, [1] weight-gradient units,
@@ -168,7 +208,10 @@ struct RouteParams {
 // first row in the expert, first row overall, rows}, wu_cap weight-gradient
 // unit entries {expert | split << 30, first row, rows, partial slot or -1},
 // mt_cap2 row-tile entries of bm2 rows, and wu_cap unit side entries
-// {S, chunk, first partial slot of the expert, 0}, four int32 each.
+// {S, chunk, first partial slot of the expert, 0}, four int32 each; then
+// el + 1 padded row offsets: each expert's row count rounded up to a
+// multiple of kMxPad, prefix-summed (the column ranges of the MXFP8
+// weight-gradient operands).
 constexpr int kSchedHeader = 4;
 constexpr int kRowTile2 = 192;  // bf16 fc1 dgrad row tile: two waves of 96 rows
 
@@ -201,6 +244,8 @@ hipError_t launch_router_fwd(const void* x, const void* wr, int64_t T, int E, in
 // 2 selects the 192-row tiles), kGemmFc2Dgrad (the fc2 dgrad epilogue) or
 // kGemmFc1Fwd (h and relu(h)^2 rows); 256-row tiles unless stated.
 hipError_t launch_mx_rowgemm(const RowGemmParams& P, int kind, int64_t grid, hipStream_t st);
+hipError_t launch_mx_wgrad(const MxWgradParams& P, hipStream_t st);
+hipError_t launch_mx_quantize_wgrad(const MxWgradQuantParams& P, hipStream_t st);
 hipError_t launch_nvfp4_quantize(const void* in, bool bf16, int64_t rows, int64_t cols, uint8_t* codes,
                                  uint8_t* scales, float* global_scale, uint64_t seed, hipStream_t st);
 hipError_t launch_mx_quantize(const void* in, bool bf16, int64_t rows, int64_t cols, uint8_t* codes,

@@ -38,6 +38,8 @@ struct Plan {
   int64_t mt_cap2;    // routing.sched: row-tile entries (bm2 rows)
   int64_t list2_at;   // routing.sched: int32 offset of the bm2 list
   int64_t aux_at;     // routing.sched: int32 offset of the unit side table
+  int64_t pad_at;     // routing.sched: int32 offset of the padded row offsets
+  int64_t rpad_cap;   // MXFP8 weight-gradient operands: padded rows (bytes per codes row)
   bool fc1_list2;     // the fc1 dgrad runs the bm2 list
   int64_t sched_elems;
   size_t esize;
@@ -115,7 +117,10 @@ moe_status validate(const moe_problem* p, Plan* pl) {
     pl->mt_cap2 = (pl->rows_cap + pl->bm2 - 1) / pl->bm2 + pl->el;
     pl->list2_at = kSchedHeader + 4 * (pl->mt_cap + pl->wu_cap);
     pl->aux_at = pl->list2_at + 4 * pl->mt_cap2;
-    pl->sched_elems = pl->aux_at + 4 * pl->wu_cap;
+    pl->pad_at = pl->aux_at + 4 * pl->wu_cap;
+    pl->sched_elems = pl->pad_at + pl->el + 1;
+    // sum over experts of round_up(cnt, kMxPad) <= rows_cap + el (kMxPad - 1)
+    pl->rpad_cap = (pl->rows_cap + (int64_t)pl->el * (kMxPad - 1) + kMxPad - 1) / kMxPad * kMxPad;
     pl->esize = bf16 ? 2 : 4;
   }
   return MOE_OK;
@@ -313,32 +318,19 @@ MOE_API const char* moe_stage_names(const moe_problem* p, moe_mode mode, int cal
       if (at) return "wgrad_prep_act_p_zero,wgrad_fc1_fc2";
       return "wgrad_prep_act_p,wgrad_fc1_fc2_ordered";
     }
+    case 3:
+      return at ? "route,permute_scan,permute_scatter_atomic" : "route,permute_scan,permute_scatter";
   }
   return nullptr;
 }
 
-MOE_API moe_status moe_fwd(const moe_problem* p, const float* logits, const void* x, const void* w1,
-                           const void* w2, const moe_routing* routing, void* h, void* y_or_rows,
-                           void* ws, size_t ws_bytes, moe_mode mode, void* stream) {
-  Plan pl;
-  moe_status s = validate(p, &pl);
-  if (s != MOE_OK) return s;
-  if (mode != MOE_DETERMINISTIC && mode != MOE_ATOMIC) return MOE_ERR_MODE;
-  const bool at = mode == MOE_ATOMIC;
-  const bool has_tok = pl.T > 0, has_rows = pl.rows_cap > 0;
-  if (!routing || !w1 || !w2 || !routing->counts || !routing->offsets || !routing->sched) return MOE_ERR_NULL;
-  if (has_tok && (!logits || !x || !y_or_rows || !routing->topk_idx || !routing->topk_prob ||
-                  !routing->slot_row))
-    return MOE_ERR_NULL;
-  if (has_rows && (!h || !routing->row_src || !routing->row_tok || !routing->row_prob)) return MOE_ERR_NULL;
-  const FwdWs L = fwd_layout(pl, p->combine, at);
-  s = check_ws(ws, ws_bytes, L.total);
-  if (s != MOE_OK) return s;
-  hipStream_t st = (hipStream_t)stream;
-  char* wsb = (char*)ws;
-  const uint64_t seed = p->debug_shuffle_seed;
-  Stager sg{p, st};
+namespace {
 
+// Top-k routing, the stable permutation and the backward work list (the
+// first three kernels of moe_fwd) into `routing`, with the forward
+// workspace's histogram and cursor regions.
+hipError_t route_enqueue(const moe_problem* p, const Plan& pl, const float* logits, const moe_routing* routing,
+                         char* wsb, const FwdWs& L, bool at, Stager& sg, hipStream_t st) {
   RouteParams R{};
   R.logits = logits;
   R.T = pl.T;
@@ -361,17 +353,69 @@ MOE_API moe_status moe_fwd(const moe_problem* p, const float* logits, const void
   R.bm2 = pl.bm2;
   R.list2_at = pl.list2_at;
   R.aux_at = pl.aux_at;
+  R.pad_at = pl.pad_at;
   R.kc = pl.kc;
   R.mt_cap = pl.mt_cap;
   R.nchunk = pl.nchunk;
   R.atomic = at;
-  R.seed = seed;
+  R.seed = p->debug_shuffle_seed;
+  hipError_t e;
   sg.mark();
-  HIP_TRY(launch_route(R, st));
+  if ((e = launch_route(R, st)) != hipSuccess) return e;
   sg.mark();
-  HIP_TRY(launch_permute_scan(R, st));
+  if ((e = launch_permute_scan(R, st)) != hipSuccess) return e;
   sg.mark();
-  HIP_TRY(launch_permute_scatter(R, st));
+  return launch_permute_scatter(R, st);
+}
+
+// Argument checks shared by moe_fwd and moe_route.
+moe_status route_check(const moe_problem* p, Plan* pl, const float* logits, const moe_routing* routing,
+                       moe_mode mode) {
+  moe_status s = validate(p, pl);
+  if (s != MOE_OK) return s;
+  if (mode != MOE_DETERMINISTIC && mode != MOE_ATOMIC) return MOE_ERR_MODE;
+  if (!routing || !routing->counts || !routing->offsets || !routing->sched) return MOE_ERR_NULL;
+  if (pl->T > 0 && (!logits || !routing->topk_idx || !routing->topk_prob || !routing->slot_row)) return MOE_ERR_NULL;
+  if (pl->rows_cap > 0 && (!routing->row_src || !routing->row_tok || !routing->row_prob)) return MOE_ERR_NULL;
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API moe_status moe_route(const moe_problem* p, const float* logits, const moe_routing* routing, void* ws,
+                             size_t ws_bytes, moe_mode mode, void* stream) {
+  Plan pl;
+  moe_status s = route_check(p, &pl, logits, routing, mode);
+  if (s != MOE_OK) return s;
+  const bool at = mode == MOE_ATOMIC;
+  const FwdWs L = fwd_layout(pl, p->combine, at);
+  s = check_ws(ws, ws_bytes, L.total);
+  if (s != MOE_OK) return s;
+  Stager sg{p, (hipStream_t)stream};
+  const hipError_t e = route_enqueue(p, pl, logits, routing, (char*)ws, L, at, sg, (hipStream_t)stream);
+  sg.mark();
+  return e == hipSuccess && sg.err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+MOE_API moe_status moe_fwd(const moe_problem* p, const float* logits, const void* x, const void* w1,
+                           const void* w2, const moe_routing* routing, void* h, void* y_or_rows,
+                           void* ws, size_t ws_bytes, moe_mode mode, void* stream) {
+  Plan pl;
+  moe_status s = route_check(p, &pl, logits, routing, mode);
+  if (s != MOE_OK) return s;
+  const bool at = mode == MOE_ATOMIC;
+  const bool has_tok = pl.T > 0, has_rows = pl.rows_cap > 0;
+  if (!w1 || !w2) return MOE_ERR_NULL;
+  if (has_tok && (!x || !y_or_rows)) return MOE_ERR_NULL;
+  if (has_rows && !h) return MOE_ERR_NULL;
+  const FwdWs L = fwd_layout(pl, p->combine, at);
+  s = check_ws(ws, ws_bytes, L.total);
+  if (s != MOE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  char* wsb = (char*)ws;
+  const uint64_t seed = p->debug_shuffle_seed;
+  Stager sg{p, st};
+  HIP_TRY(route_enqueue(p, pl, logits, routing, wsb, L, at, sg, st));
 
   void* orows = p->combine ? (void*)(wsb + L.orows) : y_or_rows;
   RowGemmParams G{};
@@ -1046,6 +1090,87 @@ MOE_API moe_status moe_mx_fwd_fc2(const moe_problem* p, const moe_routing* routi
     }
   }
   return MOE_OK;
+}
+
+MOE_API moe_status moe_mx_wgrad_cols(const moe_problem* p, int64_t* rpad_cap) {
+  Plan pl;
+  moe_status s = validate(p, &pl);
+  if (s != MOE_OK) return s;
+  if (!rpad_cap) return MOE_ERR_NULL;
+  *rpad_cap = pl.rpad_cap;
+  return MOE_OK;
+}
+
+static bool mx_wgrad_fits(const Plan& pl) {
+  return (int64_t)(pl.D > pl.F ? pl.D : pl.F) * pl.rpad_cap < ((int64_t)1 << 31);
+}
+
+MOE_API moe_status moe_mx_quantize_wgrad(const moe_problem* p, const moe_routing* routing, const void* src,
+                                         moe_mxw_src kind, uint8_t* codes, uint8_t* scales, void* stream) {
+  Plan pl;
+  moe_status s = validate(p, &pl);
+  if (s != MOE_OK) return s;
+  if (!pl.bf16) return MOE_ERR_DTYPE;
+  if (kind != MOE_MXW_TOKEN && kind != MOE_MXW_ROW && kind != MOE_MXW_ACT_P) return MOE_ERR_SHAPE;
+  if (!mx_wgrad_fits(pl)) return MOE_ERR_SHAPE;
+  if (!routing || !routing->counts || !routing->offsets || !routing->sched) return MOE_ERR_NULL;
+  if (pl.rows_cap == 0) return MOE_OK;
+  if (!src || !codes || !scales) return MOE_ERR_NULL;
+  if (kind == MOE_MXW_TOKEN && !routing->row_tok) return MOE_ERR_NULL;
+  if (kind == MOE_MXW_ACT_P && !routing->row_prob) return MOE_ERR_NULL;
+  if ((uintptr_t)codes & 15) return MOE_ERR_SHAPE;
+  MxWgradQuantParams Q{};
+  Q.src = (const uint16_t*)src;
+  Q.kind = (int)kind;
+  Q.cols = kind == MOE_MXW_TOKEN ? pl.D : pl.F;
+  Q.rpad = pl.rpad_cap;
+  Q.counts = routing->counts;
+  Q.offsets = routing->offsets;
+  Q.poff = routing->sched + pl.pad_at;
+  Q.el = pl.el;
+  Q.row_tok = routing->row_tok;
+  Q.row_prob = routing->row_prob;
+  Q.codes = codes;
+  Q.scales = scales;
+  Q.seed = p->debug_shuffle_seed;
+  return launch_mx_quantize_wgrad(Q, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+MOE_API moe_status moe_mx_wgrad(const moe_problem* p, const moe_routing* routing, const uint8_t* x_codes,
+                                const uint8_t* x_scales, const uint8_t* dh_codes, const uint8_t* dh_scales,
+                                const uint8_t* act_codes, const uint8_t* act_scales, const uint8_t* dy_codes,
+                                const uint8_t* dy_scales, float* dw1, float* dw2, void* stream) {
+  Plan pl;
+  moe_status s = validate(p, &pl);
+  if (s != MOE_OK) return s;
+  if (!pl.bf16) return MOE_ERR_DTYPE;
+  if (!mx_wgrad_fits(pl)) return MOE_ERR_SHAPE;
+  if (!routing || !routing->sched || !dw1 || !dw2) return MOE_ERR_NULL;
+  const uint8_t* ops[8] = {x_codes, x_scales, dh_codes, dh_scales, act_codes, act_scales, dy_codes, dy_scales};
+  if (pl.rows_cap > 0) {
+    for (int i = 0; i < 8; ++i) {
+      if (!ops[i]) return MOE_ERR_NULL;
+      if ((uintptr_t)ops[i] & 15) return MOE_ERR_SHAPE;
+    }
+  }
+  MxWgradParams W{};
+  W.poff = routing->sched + pl.pad_at;
+  W.groups = pl.el;
+  W.D = pl.D;
+  W.F = pl.F;
+  W.rpad = pl.rpad_cap;
+  W.x_codes = x_codes;
+  W.x_scales = x_scales;
+  W.dh_codes = dh_codes;
+  W.dh_scales = dh_scales;
+  W.act_codes = act_codes;
+  W.act_scales = act_scales;
+  W.dy_codes = dy_codes;
+  W.dy_scales = dy_scales;
+  W.dw1 = dw1;
+  W.dw2 = dw2;
+  W.seed = p->debug_shuffle_seed;
+  return launch_mx_wgrad(W, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 MOE_API moe_status moe_fingerprint(const void* data, moe_dtype dtype, int ndim, const int64_t* shape,

@@ -95,6 +95,90 @@ __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const T* in, int64_t
   scales[(g * cols + c) * nrb + rb] = (uint8_t)(se + 127);
 }
 
+// MXFP8 operands of the weight gradients: quantised along the routed rows
+// of each expert (the contraction axis of dW1 = X^T dH and dW2 = A^T dY).
+// Expert g's rows occupy the padded columns poff[g] .. poff[g+1] of the
+// output (its row count rounded up to kMxPad); a block is 32 consecutive
+// padded rows of one column, so blocks start at the expert's first row and
+// its last block is completed with zeros.  Padded row j of expert g is
+// routed row offsets[g] + (j - poff[g]) while below its count, and reads
+//   token: src[row_tok[r]] (x or dY, gathered by token),
+//   row:   src[r] (dH),
+//   act_p: p_r * (relu(h_r))^2 from h = src[r], relu(v) = v > 0 ? v : +0,
+//          the square rounded to float32 and then the product.
+// Same encoding as mx_quantize_t_kernel; one thread per (column, block).
+// Scales are stored slice-major, [rpad / 64][cols][2], so that the weight-
+// gradient GEMM streams a tile's scales of one 64-row slice as one
+// contiguous run.  Blocks at or past poff[el] are not written.
+template <int KIND>
+__global__ __launch_bounds__(256) void mx_quantize_wgrad_kernel(MxWgradQuantParams P) {
+  const int64_t ncb = (P.cols + 255) / 256, nrb = P.rpad / 32;
+  const int64_t u = map_unit(blockIdx.x, nrb * ncb, P.seed);
+  if (u < 0) return;
+  const int64_t rb = u / ncb, cb = u % ncb;
+  const int64_t c = cb * 256 + threadIdx.x;
+  const int j0 = (int)(rb * 32);
+  if (c >= P.cols || j0 >= P.poff[P.el]) return;
+  // the expert holding padded row j0: the last g with poff[g] <= j0
+  int lo = 0, hi = P.el - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (P.poff[mid] <= j0) lo = mid; else hi = mid - 1;
+  }
+  const int local0 = j0 - P.poff[lo];
+  const int live = P.counts[lo] - local0;   // rows of the block below the count (uniform)
+  const int r0 = P.offsets[lo] + local0;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    if (i < live) {
+      const int64_t srcrow = KIND == kMxwToken ? (int64_t)P.row_tok[r0 + i] : (int64_t)(r0 + i);
+      v[i] = bf16_to_f32(P.src[srcrow * P.cols + c]);
+    } else {
+      v[i] = 0.f;
+    }
+  }
+  if constexpr (KIND == kMxwActP) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float rl = v[i] > 0.f ? v[i] : 0.f;
+      const float sq = rl * rl;
+      v[i] = i < live ? P.row_prob[r0 + i] * sq : 0.f;
+    }
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(v[i]) & 0x7fffffffu);
+  const int ef = (int)(m >> 23);
+  const int se = ef == 0 ? -127 : min(127, max(-127, ef - 127 - 8));
+  const float f = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se, exact
+  uint32_t w[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    w[q] = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) w[q] |= e4m3_rne(v[4 * q + b] * f) << (8 * b);
+  }
+  uint8_t* dst = P.codes + c * P.rpad + j0;
+  *(u32x4_t*)dst = u32x4_t{w[0], w[1], w[2], w[3]};
+  *(u32x4_t*)(dst + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
+  // slice-major scales: the two blocks of each 64-row slice of a column together
+  P.scales[((rb >> 1) * P.cols + c) * 2 + (rb & 1)] = (uint8_t)(se + 127);
+}
+
+hipError_t launch_mx_quantize_wgrad(const MxWgradQuantParams& P, hipStream_t st) {
+  const int64_t units = (P.rpad / 32) * ((P.cols + 255) / 256);
+  if (units == 0) return hipSuccess;
+  const int64_t grid = grid_for_units(units);
+  if (P.kind == kMxwToken)
+    mx_quantize_wgrad_kernel<kMxwToken><<<grid, 256, 0, st>>>(P);
+  else if (P.kind == kMxwRow)
+    mx_quantize_wgrad_kernel<kMxwRow><<<grid, 256, 0, st>>>(P);
+  else
+    mx_quantize_wgrad_kernel<kMxwActP><<<grid, 256, 0, st>>>(P);
+  return hipGetLastError();
+}
+
 hipError_t launch_mx_quantize_t(const void* in, bool bf16, int64_t groups, int64_t rows, int64_t cols,
                                 uint8_t* codes, uint8_t* scales, uint64_t seed, hipStream_t st) {
   const int64_t units = groups * (rows / 32) * ((cols + 255) / 256);

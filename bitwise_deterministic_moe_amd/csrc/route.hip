@@ -173,7 +173,9 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(RouteParams P) {
     s_cnt[e] = total;
   }
   block_exclusive_scan<1024>(s_pre, s_tmp, P.el, [&](int g) { return s_cnt[g]; });
-  if (e <= P.el) P.offsets[e] = s_pre[e];
+  // el may be the block size (1024): thread 0 also writes the total
+  if (e < P.el) P.offsets[e] = s_pre[e];
+  if (e == 0) P.offsets[P.el] = s_pre[P.el];
   const int off_e = e < P.el ? s_pre[e] : 0;
   if (e < P.el) {
     s_off[e] = off_e;
@@ -210,6 +212,11 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(RouteParams P) {
     }
   }
   if (e == 0) P.sched[1] = nunits;
+  __syncthreads();
+  // padded row offsets of the MXFP8 weight-gradient operands
+  block_exclusive_scan<1024>(s_pre, s_tmp, P.el, [&](int g) { return (s_cnt[g] + kMxPad - 1) / kMxPad * kMxPad; });
+  if (e < P.el) P.sched[P.pad_at + e] = s_pre[e];
+  if (e == 0) P.sched[P.pad_at + P.el] = s_pre[P.el];
 }
 
 __global__ __launch_bounds__(64) void permute_scatter_kernel(RouteParams P) {

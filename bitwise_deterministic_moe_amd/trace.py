@@ -25,11 +25,15 @@ One train step on the layer (all device work through the library's C ABI):
     dlogits, dwr, dx_router = moe_router_bwd(dprob)
     SGD on the float32 masters of W1, W2, wr; bf16 (or f32) runtime copies
     rebuilt by the same kernel (moe_sgd_step).
-With mx=True (bf16 layers) the two data gradients run on MXFP8 operands
-(moe_mx_dgrad_fc2 on dy and W2, moe_mx_dgrad_fc1 on dh and W1, each
-quantised by moe_mx_quantize), and the op-level trace fingerprints each
-encoded tensor and its scale buffer, as the pages do for low-precision runs;
-it also records dh's NVFP4 encoding (codes, block scales, tensor scale).
+With mx=True (bf16 layers) every expert GEMM runs on MXFP8 operands: the
+routing stage alone (moe_route), then moe_mx_fwd_fc1 / moe_mx_fwd_fc2 on x,
+act and the transposed weights (moe_mx_quantize, moe_mx_quantize_t), the
+data gradients moe_mx_dgrad_fc2 / moe_mx_dgrad_fc1 on dy, dh and the
+weights, and the weight gradients moe_mx_wgrad on x, dh, p relu(h)^2 and dy
+quantised along the routed rows (moe_mx_quantize_wgrad).  The op-level
+trace fingerprints every encoded tensor and its scale buffer, as the pages
+do for low-precision runs; it also records dh's NVFP4 encoding (codes,
+block scales, tensor scale).
 Metrics (loss, gradient norms) are summed on the host in float64 in a fixed
 order, so they are deterministic too.
 """
@@ -41,9 +45,10 @@ from typing import Callable, List, Optional
 import numpy as np
 import torch
 
-from . import (MoeError, Problem, TORCH_DTYPE, moe_bwd_dgrad_dprob, moe_bwd_wgrad, moe_fingerprint,
-               moe_fwd, moe_mx_dgrad_fc1, moe_mx_dgrad_fc2, moe_mx_quantize, moe_nvfp4_quantize, moe_router_bwd,
-               moe_router_fwd, moe_sgd_step)
+from . import (MXW_ACT_P, MXW_ROW, MXW_TOKEN, MoeError, Problem, TORCH_DTYPE, moe_bwd_dgrad_dprob,
+               moe_bwd_wgrad, moe_fingerprint, moe_fwd, moe_mx_dgrad_fc1, moe_mx_dgrad_fc2, moe_mx_fwd_fc1,
+               moe_mx_fwd_fc2, moe_mx_quantize, moe_mx_quantize_t, moe_mx_quantize_wgrad, moe_mx_wgrad,
+               moe_nvfp4_quantize, moe_route, moe_router_bwd, moe_router_fwd, moe_sgd_step)
 
 LEVELS = {"metrics": 0, "phases": 1, "ops": 2}
 
@@ -187,7 +192,7 @@ def _mx(t, rows: int, cols: int):
 def train_step(cfg, st: TrainState, tracer: Tracer, hook: Optional[Callable] = None, mx: bool = False):
     """One step at st.step; advances st.step.  ``hook(step, where, st)`` may
     change the state at "before_forward" (a fault injector for tests).  With
-    ``mx`` the data gradients run on MXFP8 operands."""
+    ``mx`` every expert GEMM runs on MXFP8 operands."""
     if cfg.combine != 1 or cfg.num_local != cfg.num_experts:
         raise MoeError("the train step covers the full layer (token layout, all experts local)")
     if mx and (cfg.dtype != "bf16" or cfg.d_model > 2048 or cfg.d_ffn > 2048):
@@ -198,8 +203,16 @@ def train_step(cfg, st: TrainState, tracer: Tracer, hook: Optional[Callable] = N
         hook(s, "before_forward", st)
     R = st.runtime
     logits = moe_router_fwd(prob, x, R["wr"])
-    routing, h, y = moe_fwd(prob, logits, x, R["w1"], R["w2"])
-    enc = {}
+    enc, fwd_enc, wg_enc = {}, {}, {}
+    if mx:
+        el, D, F = cfg.num_local, cfg.d_model, cfg.d_ffn
+        routing = moe_route(prob, logits)
+        fwd_enc["x"], fwd_enc["w1t"] = moe_mx_quantize(x), moe_mx_quantize_t(R["w1"].reshape(el, D, F))
+        h, act = moe_mx_fwd_fc1(prob, routing, fwd_enc["x"], fwd_enc["w1t"])
+        fwd_enc["act"], fwd_enc["w2t"] = moe_mx_quantize(act), moe_mx_quantize_t(R["w2"].reshape(el, F, D))
+        y = moe_mx_fwd_fc2(prob, routing, fwd_enc["act"], fwd_enc["w2t"])
+    else:
+        routing, h, y = moe_fwd(prob, logits, x, R["w1"], R["w2"])
     if mx:
         el, D, F = cfg.num_local, cfg.d_model, cfg.d_ffn
         enc["dy"], enc["w2"] = _mx(dy, cfg.tokens, D), _mx(R["w2"], el * F, D)
@@ -208,9 +221,12 @@ def train_step(cfg, st: TrainState, tracer: Tracer, hook: Optional[Callable] = N
         enc["dh"], enc["w1"] = _mx(dh, prob.rows_cap, F), _mx(R["w1"], el * D, F)
         w1mx = (enc["w1"][0].reshape(el, D, F), enc["w1"][1].reshape(el, D, F // 32))
         dx = moe_mx_dgrad_fc1(prob, routing, enc["dh"], w1mx)     # per routed row
+        for n, src, kind in (("x", x, MXW_TOKEN), ("dh", dh, MXW_ROW), ("act", h, MXW_ACT_P), ("dy", dy, MXW_TOKEN)):
+            wg_enc[n] = moe_mx_quantize_wgrad(prob, routing, src, kind)
+        dw1, dw2 = moe_mx_wgrad(prob, routing, wg_enc["x"], wg_enc["dh"], wg_enc["act"], wg_enc["dy"])
     else:
         dx, dprob, dh = moe_bwd_dgrad_dprob(prob, routing, dy, R["w1"], R["w2"], h)
-    dw1, dw2 = moe_bwd_wgrad(prob, routing, x, dy, h, dh)
+        dw1, dw2 = moe_bwd_wgrad(prob, routing, x, dy, h, dh)
     dlogits, dwr, dxr = moe_router_bwd(prob, routing, dprob, x, R["wr"])
     torch.cuda.synchronize()
 
@@ -219,8 +235,18 @@ def train_step(cfg, st: TrainState, tracer: Tracer, hook: Optional[Callable] = N
     T.tensor(s, "forward", "moe_router_fwd", "logits", logits, 1)
     for n in ("topk_idx", "topk_prob", "counts", "offsets", "row_src", "slot_row"):
         T.tensor(s, "forward", "moe_fwd", n, getattr(routing, n), 2)
-    T.tensor(s, "forward", "moe_fwd", "h", h, 2)
-    T.tensor(s, "forward", "moe_fwd", "y", y, 1)
+    if mx:
+        for n, op in (("x", "moe_mx_quantize"), ("w1t", "moe_mx_quantize_t")):
+            T.tensor(s, "forward", op, f"{n}_codes", fwd_enc[n][0], 2)
+            T.tensor(s, "forward", op, f"{n}_scales", fwd_enc[n][1], 2)
+        T.tensor(s, "forward", "moe_mx_fwd_fc1", "h", h, 2)
+        for n, op in (("act", "moe_mx_quantize"), ("w2t", "moe_mx_quantize_t")):
+            T.tensor(s, "forward", op, f"{n}_codes", fwd_enc[n][0], 2)
+            T.tensor(s, "forward", op, f"{n}_scales", fwd_enc[n][1], 2)
+        T.tensor(s, "forward", "moe_mx_fwd_fc2", "y", y, 1)
+    else:
+        T.tensor(s, "forward", "moe_fwd", "h", h, 2)
+        T.tensor(s, "forward", "moe_fwd", "y", y, 1)
     # backward
     if mx:
         for n in ("dy", "w2"):
@@ -235,12 +261,21 @@ def train_step(cfg, st: TrainState, tracer: Tracer, hook: Optional[Callable] = N
         nv = moe_nvfp4_quantize(dh)
         for n, t in zip(("dh_codes", "dh_scales", "dh_tensor_scale"), nv):
             T.tensor(s, "backward", "moe_nvfp4_quantize", n, t, 2)
+        # the written part of the weight-gradient encodings: each expert's
+        # rows padded to 64
+        P = int(((routing.counts.long() + 63) // 64 * 64).sum().item())
+        for n in ("x", "dh", "act", "dy"):
+            codes, scales = wg_enc[n]
+            T.tensor(s, "backward", "moe_mx_quantize_wgrad", f"{n}_codes", codes[:, :P].contiguous(), 2)
+            T.tensor(s, "backward", "moe_mx_quantize_wgrad", f"{n}_scales", scales[: P // 64].contiguous(), 2)
+        T.tensor(s, "backward", "moe_mx_wgrad", "dw1", dw1, 1)
+        T.tensor(s, "backward", "moe_mx_wgrad", "dw2", dw2, 1)
     else:
         T.tensor(s, "backward", "moe_bwd_dgrad_dprob", "dprob", dprob, 1)
         T.tensor(s, "backward", "moe_bwd_dgrad_dprob", "dh", dh, 2)
         T.tensor(s, "backward", "moe_bwd_dgrad_dprob", "dx", dx, 1)
-    T.tensor(s, "backward", "moe_bwd_wgrad", "dw1", dw1, 1)
-    T.tensor(s, "backward", "moe_bwd_wgrad", "dw2", dw2, 1)
+        T.tensor(s, "backward", "moe_bwd_wgrad", "dw1", dw1, 1)
+        T.tensor(s, "backward", "moe_bwd_wgrad", "dw2", dw2, 1)
     T.tensor(s, "router", "moe_router_bwd", "dlogits", dlogits, 2)
     T.tensor(s, "router", "moe_router_bwd", "dwr", dwr, 1)
     T.tensor(s, "router", "moe_router_bwd", "dx_router", dxr, 1)
@@ -312,7 +347,7 @@ def main(argv=None):
     ap.add_argument("--level", default="phases", choices=list(LEVELS))
     ap.add_argument("--out", help="write the trace (JSON lines)")
     ap.add_argument("--compare", nargs=2, metavar=("A", "B"), help="report the first divergence of two traces")
-    ap.add_argument("--mx", action="store_true", help="data gradients on MXFP8 operands (bf16 layers)")
+    ap.add_argument("--mx", action="store_true", help="every expert GEMM on MXFP8 operands (bf16 layers)")
     a = ap.parse_args(argv)
     if a.compare:
         d = first_divergence(Tracer.load(a.compare[0]), Tracer.load(a.compare[1]))

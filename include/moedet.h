@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -184,7 +184,8 @@ moe_status moe_workspace_size(const moe_problem* p, moe_mode mode, size_t* fwd_b
 
 /* Names of the kernels a call enqueues, in order, comma-separated, for the
  * stage_events hook.  call: 0 = moe_fwd, 1 = moe_bwd_dgrad_dprob,
- * 2 = moe_bwd_wgrad.  Returns NULL for an invalid call or problem. */
+ * 2 = moe_bwd_wgrad, 3 = moe_route.  Returns NULL for an invalid call or
+ * problem. */
 const char* moe_stage_names(const moe_problem* p, moe_mode mode, int call);
 
 /* Forward: routing, stable permute, expert MLP and (combine=1) weighted
@@ -213,6 +214,18 @@ const char* moe_stage_names(const moe_problem* p, moe_mode mode, int call);
 moe_status moe_fwd(const moe_problem* p, const float* logits, const void* x, const void* w1,
                    const void* w2, const moe_routing* routing, void* h, void* y_or_rows,
                    void* ws, size_t ws_bytes, moe_mode mode, void* stream);
+
+/* The routing stage of moe_fwd alone (its first three kernels): top-k
+ * selection with probabilities renormalised over the chosen experts, the
+ * stable permutation of the (token, slot) pairs by local expert and the
+ * backward work list, written to `routing` exactly as moe_fwd writes them
+ * (same arguments, same workspace: the forward one of moe_workspace_size).
+ * For callers that run the expert GEMMs through another path (the MXFP8
+ * forward).  Errors: MOE_ERR_MODE, MOE_ERR_NULL, MOE_ERR_WORKSPACE and the
+ * problem's validation before anything is enqueued; MOE_ERR_HIP for a
+ * launch failure. */
+moe_status moe_route(const moe_problem* p, const float* logits, const moe_routing* routing, void* ws,
+                     size_t ws_bytes, moe_mode mode, void* stream);
 
 /* Backward, data path: fc2 dgrad with the dprob epilogue, fc1 dgrad and the
  * dx combine.  This is the site of the fault and the fix in the English
@@ -528,6 +541,68 @@ moe_status moe_mx_fwd_fc1(const moe_problem* p, const moe_routing* routing, cons
 moe_status moe_mx_fwd_fc2(const moe_problem* p, const moe_routing* routing, const uint8_t* act_codes,
                           const uint8_t* act_scales, const uint8_t* w2t_codes, const uint8_t* w2t_scales,
                           void* y_or_rows, void* ws, size_t ws_bytes, moe_mode mode, void* stream);
+
+/* Rows read by moe_mx_quantize_wgrad (cols: the operand's width). */
+typedef enum moe_mxw_src {
+  MOE_MXW_TOKEN = 0, /* src bf16 [T, D]: row r of the output is src[row_tok[r]] (x or dY), cols = D */
+  MOE_MXW_ROW = 1,   /* src bf16 [rows_cap, F]: routed row r (dH), cols = F */
+  MOE_MXW_ACT_P = 2  /* src bf16 h [rows_cap, F]: p_r relu(h_r)^2 formed in float32 (the
+                        square rounded, then the product; relu(v) = v > 0 ? v : +0), cols = F */
+} moe_mxw_src;
+
+/* Columns of the MXFP8 weight-gradient operands for problem p: rpad_cap =
+ * rows_cap + num_local * 63 rounded up to a multiple of 64 (each expert's
+ * routed rows padded to a multiple of 64).  Errors: those of the problem's
+ * validation, MOE_ERR_NULL. */
+moe_status moe_mx_wgrad_cols(const moe_problem* p, int64_t* rpad_cap);
+
+/* MXFP8 encoding of a weight-gradient operand, quantised along the routed
+ * rows: the contraction axis of dW1_e = X_e^T dH_e and dW2_e = A_e^T dY_e
+ * (A = p relu(h)^2; the English digest's backward of the expert MLP), so
+ * that a block scale is constant along each product.  The format is
+ * moe_mx_quantize's (the French article, section on the method for
+ * debugging non-determinism, fingerprints the encoded values and the scale
+ * buffers; OCP MX v1.0: E4M3 codes, one E8M0 scale per 32 elements).
+ * Layout: expert e owns columns poff[e] .. poff[e+1] of every output row,
+ * poff the prefix sum of its routed row counts rounded up to a multiple of
+ * 64; column poff[e] + i holds its routed row offsets[e] + i, transposed,
+ * for i below its count, and zero past it.  A block is 32 consecutive
+ * columns of one row, so blocks start at an expert's first row.  The
+ * scales are stored slice-major: the scale of row c, block b is byte
+ * ((b / 2) * cols + c) * 2 + b % 2 (the two blocks of each 64-column slice
+ * of a row side by side, slices outermost), so that the GEMM reads a tile's
+ * scales of one slice as one contiguous run.
+ *   src            DEVICE bf16, as moe_mxw_src describes
+ *   codes          DEVICE uint8 [cols, rpad_cap], 16-byte aligned
+ *   scales         DEVICE uint8 [rpad_cap / 64, cols, 2]
+ * Columns from poff[num_local] on are not written.  routing: as written by
+ * moe_fwd.  The problem must be bf16 with max(D, F) * rpad_cap < 2^31.
+ * Deterministic: every byte depends on the inputs only.  Errors:
+ * MOE_ERR_DTYPE, MOE_ERR_SHAPE (sizes, alignment, kind), MOE_ERR_NULL before
+ * anything is enqueued; MOE_ERR_HIP for a launch failure. */
+moe_status moe_mx_quantize_wgrad(const moe_problem* p, const moe_routing* routing, const void* src,
+                                 moe_mxw_src kind, uint8_t* codes, uint8_t* scales, void* stream);
+
+/* MXFP8 weight gradients, both matrices, from operands encoded by
+ * moe_mx_quantize_wgrad (x: MOE_MXW_TOKEN of X, dh: MOE_MXW_ROW of dH,
+ * act: MOE_MXW_ACT_P of h, dy: MOE_MXW_TOKEN of dY):
+ *   dW1[e] = dequant(x_e) . dequant(dh_e)^T   [D, F] per local expert,
+ *   dW2[e] = dequant(act_e) . dequant(dy_e)^T [F, D],
+ * over expert e's padded columns.  Each output tile is accumulated in
+ * float32 by one workgroup over all of the expert's rows in a fixed order
+ * (64 rows per scaled MFMA, ascending) and stored once: the result is
+ * bitwise reproducible with no reduction step (there is no atomic mode).
+ * An expert without rows gets zeros.
+ *   *_codes        DEVICE uint8 [D or F, rpad_cap], 16-byte aligned
+ *   *_scales       DEVICE uint8 [rpad_cap / 64, D or F, 2], 16-byte aligned
+ *   dw1, dw2       DEVICE float32 [num_local, D, F] / [num_local, F, D]
+ * The problem must be bf16 with max(D, F) * rpad_cap < 2^31.  Errors:
+ * MOE_ERR_DTYPE, MOE_ERR_SHAPE, MOE_ERR_NULL before anything is enqueued;
+ * MOE_ERR_HIP for a launch failure. */
+moe_status moe_mx_wgrad(const moe_problem* p, const moe_routing* routing, const uint8_t* x_codes,
+                        const uint8_t* x_scales, const uint8_t* dh_codes, const uint8_t* dh_scales,
+                        const uint8_t* act_codes, const uint8_t* act_scales, const uint8_t* dy_codes,
+                        const uint8_t* dy_scales, float* dw1, float* dw2, void* stream);
 
 /* Diagnostic for the measurement of the percent of bf16 dense peak: the
  * attainable MFMA rate of the device.  Enqueues on `stream` one launch of

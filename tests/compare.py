@@ -211,3 +211,72 @@ def compare_full(dtype: str, got: dict, ref: dict, combine: bool, k: int, rows=N
     errs["dprob_worst_z"] = sb.worst
     assert not fails, f"{fails} (all: {errs})"
     return errs
+
+
+def fp32_sum_bound(abs_terms, k: int):
+    """Largest error of a float32 accumulation of k exactly representable
+    products whose magnitudes sum to ``abs_terms`` (per element): each of
+    the k - 1 additions errs by at most one float32 ulp (2^-23 relative) of
+    a partial sum, whatever the rounding rule of the adder (so truncating
+    matrix units are covered too), and each partial sum is at most
+    abs_terms; plus half an ulp for the final value."""
+    return (max(k - 1, 0) * 2.0 ** -23 + 2.0 ** -24) * np.asarray(abs_terms, dtype=np.float64)
+
+
+class ElementBound:
+    """Per-element check |got - ref| <= bound; tracks the worst ratio."""
+
+    def __init__(self, name: str):
+        self.name = name
+        self.worst = 0.0
+        self.worst_at = None
+
+    def add(self, got, ref, bound, label=None):
+        got = np.asarray(got, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        bound = np.asarray(bound, dtype=np.float64)
+        err = np.abs(got - ref)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
+        if ratio.size:
+            i = int(np.argmax(ratio))
+            if ratio.flat[i] > self.worst or self.worst_at is None:
+                self.worst = float(ratio.flat[i])
+                self.worst_at = (label, np.unravel_index(i, ratio.shape))
+        return self
+
+    def failures(self) -> list:
+        if self.worst <= 1.0:
+            return []
+        return [f"{self.name}: error {self.worst:.3g} x the bound at {self.worst_at}"]
+
+
+# The scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4) does not return the
+# exactly rounded float32 sum of its 64 products.  On a single-wave probe
+# (1024 outputs, E4M3 codes over the whole range, block scales over
+# 2^-7 .. 2^2) its result differed from the exact sum by a median 1.6e-5 and
+# at most 1.6e-4 of the sum of |products|, where a float32-exact sum stays
+# within 64 * 2^-24 = 3.8e-6; no model of float32 adds (sequential, per
+# instruction, truncating to 16..26 bits) reproduces its bits.  So the
+# float32 outputs of the MXFP8 path are held to MX_TERM_BOUND of their sum
+# of |terms| element by element, and to MX_REL_TOL in rel-L2, instead of
+# the float32 bounds above.
+MX_TERM_BOUND = 2e-4
+MX_REL_TOL = 1e-4
+# Where a block's products are much smaller than its scale allows (sparse
+# blocks such as p relu(h)^2, or few routed rows), the error is better
+# described against the scale: measured on the weight gradients, it stays
+# below 2^-12.5 of the block's largest representable product
+# 448^2 * 2^(sa + sb) (the instruction accumulates each block in fixed point
+# relative to its scale).  mx_block_bound allows 2^-10 of that per block.
+MX_BLOCK_TAU = 2.0 ** -10
+
+
+def mx_block_bound(a_scales, b_scales):
+    """Per-element error bound of a scaled-MFMA product from the E8M0 scale
+    bytes of its operands (a_scales [M, nb], b_scales [N, nb], block b of
+    row i and column j meeting in element (i, j)):
+    MX_BLOCK_TAU * 448^2 * sum_b 2^(sa_ib + sb_jb)."""
+    ea = np.exp2(np.asarray(a_scales, dtype=np.float64) - 127.0)
+    eb = np.exp2(np.asarray(b_scales, dtype=np.float64) - 127.0)
+    return MX_BLOCK_TAU * 448.0 ** 2 * (ea @ eb.T)

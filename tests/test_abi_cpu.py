@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert names == set(moe.EXPORTED_SYMBOLS)
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -262,3 +262,47 @@ def test_mx_forward_validation_returns_before_enqueue(lib):
                               ctypes.c_void_p(0x100000), 1 << 40, 7, None) == 5
     assert lib.moe_mx_fwd_fc2(ctypes.byref(cp), ctypes.byref(r), fake, fake, fake, fake, fake,
                               ctypes.c_void_p(0x100000), 16, 0, None) == 4
+
+
+def test_mx_wgrad_cols_and_validation_return_before_enqueue(lib):
+    p = moe.Problem(**BASE)
+    rc, el = moe.moe_rows_cap(p), p.local
+    # each expert's rows rounded up to 64: at most rows_cap + 63 per expert
+    assert moe.moe_mx_wgrad_cols(p) == (rc + 63 * el + 63) // 64 * 64
+    fake = ctypes.c_void_p(0x1000)
+    r = moe._CRouting(*([0x2000] * 9))
+    cp = p.c()
+    f32 = moe.Problem(**{**BASE, "dtype": "f32"}).c()
+    # quantiser: float32 problem, unknown kind, NULL source, NULL row_tok for
+    # the token gather, misaligned codes
+    assert lib.moe_mx_quantize_wgrad(ctypes.byref(f32), ctypes.byref(r), fake, 0, fake, fake, None) == 3
+    assert lib.moe_mx_quantize_wgrad(ctypes.byref(cp), ctypes.byref(r), fake, 3, fake, fake, None) == 2
+    assert lib.moe_mx_quantize_wgrad(ctypes.byref(cp), ctypes.byref(r), None, 1, fake, fake, None) == 1
+    no_tok = moe._CRouting(*([0x2000] * 5 + [0] + [0x2000] * 3))
+    assert lib.moe_mx_quantize_wgrad(ctypes.byref(cp), ctypes.byref(no_tok), fake, 0, fake, fake, None) == 1
+    assert lib.moe_mx_quantize_wgrad(ctypes.byref(cp), ctypes.byref(r), fake, 1, ctypes.c_void_p(0x1008), fake,
+                                     None) == 2
+    # operands beyond 32-bit buffer offsets: max(D, F) * rpad_cap >= 2^31
+    huge = moe.Problem(**{**BASE, "tokens": 1 << 20, "d_ffn": 4096}).c()
+    assert lib.moe_mx_quantize_wgrad(ctypes.byref(huge), ctypes.byref(r), fake, 1, fake, fake, None) == 2
+    ops = [fake] * 8
+    assert lib.moe_mx_wgrad(ctypes.byref(f32), ctypes.byref(r), *ops, fake, fake, None) == 3
+    assert lib.moe_mx_wgrad(ctypes.byref(huge), ctypes.byref(r), *ops, fake, fake, None) == 2
+    assert lib.moe_mx_wgrad(ctypes.byref(cp), ctypes.byref(r), *ops, None, fake, None) == 1
+    assert lib.moe_mx_wgrad(ctypes.byref(cp), ctypes.byref(r), *([fake] * 7 + [None]), fake, fake, None) == 1
+    # scales must be 16-byte aligned (they are streamed with 16-byte loads)
+    assert lib.moe_mx_wgrad(ctypes.byref(cp), ctypes.byref(r), *([fake] * 3 + [ctypes.c_void_p(0x1002)] +
+                                                                 [fake] * 4), fake, fake, None) == 2
+
+
+def test_route_validation_and_stage_names(lib):
+    p = moe.Problem(**BASE)
+    assert moe.moe_stage_names(p, 0, 3) == ["route", "permute_scan", "permute_scatter"]
+    assert moe.moe_stage_names(p, 1, 3) == ["route", "permute_scan", "permute_scatter_atomic"]
+    fake = ctypes.c_void_p(0x1000)
+    r = moe._CRouting(*([0x2000] * 9))
+    cp = p.c()
+    assert lib.moe_route(ctypes.byref(cp), fake, ctypes.byref(r), fake, 1 << 40, 9, None) == 5
+    assert lib.moe_route(ctypes.byref(cp), None, ctypes.byref(r), fake, 1 << 40, 0, None) == 1
+    assert lib.moe_route(ctypes.byref(cp), fake, ctypes.byref(r), ctypes.c_void_p(0x100000), 16, 0, None) == 4
+    assert lib.moe_route(None, fake, ctypes.byref(r), fake, 1 << 40, 0, None) == 1

@@ -140,3 +140,49 @@ def test_shard_row_outputs_checked_per_row(shard):
     bad["dx"][3] *= 1.5
     with pytest.raises(AssertionError, match="dx: worst row"):
         compare_full(cfg.dtype, bad, ref, False, cfg.top_k)
+
+
+def _f32_accumulate(terms, truncate=False):
+    """Sequential float32 accumulation (round to nearest, or toward zero)."""
+    s = np.float32(0.0)
+    for t in terms:
+        exact = float(s) + float(t)
+        r = np.float32(exact)
+        if truncate and abs(float(r)) > abs(exact):
+            r = np.nextafter(r, np.float32(0.0))
+        s = r
+    return float(s)
+
+
+def test_fp32_sum_bound_covers_nearest_and_truncating_accumulation():
+    from compare import fp32_sum_bound
+    rng = np.random.default_rng(7)
+    for k in (1, 2, 64, 700):
+        terms = (rng.standard_normal(k) * np.exp2(rng.integers(-8, 8, k))).astype(np.float32)
+        exact = float(np.sum(terms.astype(np.float64)))
+        bound = float(fp32_sum_bound(np.sum(np.abs(terms.astype(np.float64))), k))
+        for trunc in (False, True):
+            assert abs(_f32_accumulate(terms, trunc) - exact) <= bound, (k, trunc)
+    # a missing block of 32 terms out of 700 breaks it
+    terms = np.abs(rng.standard_normal(700)).astype(np.float32)
+    bound = float(fp32_sum_bound(np.sum(terms.astype(np.float64)), 700))
+    assert abs(_f32_accumulate(terms[32:]) - float(np.sum(terms.astype(np.float64)))) > bound
+
+
+def test_element_bound_reports_the_worst_ratio():
+    from compare import ElementBound
+    c = ElementBound("t")
+    c.add([1.0, 2.0], [1.0, 2.5], [0.1, 1.0], "a")
+    assert not c.failures() and abs(c.worst - 0.5) < 1e-12
+    c.add([0.0, 1.0], [0.0, 0.0], [0.0, 0.5], "b")
+    assert c.failures() and c.worst_at[0] == "b"
+
+
+def test_mx_block_bound_by_hand():
+    from compare import MX_BLOCK_TAU, mx_block_bound
+    a = np.array([[127, 130]], np.uint8)          # scales 2^0, 2^3
+    b = np.array([[127, 125], [0, 0]], np.uint8)  # 2^0, 2^-2; 2^-127 twice
+    got = mx_block_bound(a, b)
+    want0 = MX_BLOCK_TAU * 448.0 ** 2 * (1.0 + 2.0 ** 1)
+    assert got.shape == (1, 2) and abs(got[0, 0] - want0) <= 1e-12 * want0
+    assert 0 < got[0, 1] < 1e-30

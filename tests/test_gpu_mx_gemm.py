@@ -12,20 +12,15 @@ import bitwise_deterministic_moe_amd as moe
 import oracle
 from synth import CONFIGS
 from synth.inputs import f32_to_bf16_bits, bf16_bits_to_f32
+from compare import MX_REL_TOL, MX_TERM_BOUND
 from harness import device_inputs, rel_l2, to_host
 from test_gpu_parity import EDGE
 
 pytestmark = pytest.mark.gpu
 
-# The scaled MFMA does not return the exactly rounded float32 sum of its 64
-# products.  On a single-wave probe (1024 outputs, E4M3 codes over the whole
-# range, block scales over 2^-7 .. 2^2) its result differed from the exact sum
-# by a median 1.6e-5 and at most 1.6e-4 of the sum of |products|, where a
-# float32-exact sum stays within 64 * 2^-24 = 3.8e-6.  So the float32 dprob of
-# the MXFP8 path is held to 2e-4 of its sum of |terms| element by element, and
-# to 1e-4 in rel-L2, instead of the 1e-5 of float32-accumulated outputs.
-MX_DPROB_TOL = 1e-4
-MX_TERM_BOUND = 2e-4
+# the float32 dprob of the MXFP8 path: tests/compare.py MX_TERM_BOUND (per
+# slot, of its sum of |terms|) and MX_REL_TOL (rel-L2)
+MX_DPROB_TOL = MX_REL_TOL
 
 
 def _case(name):

@@ -27,6 +27,9 @@ EDGE = {
     # mean 750 rows per expert: the fc1 dgrad runs the 192-row tile list
     # (three full tiles and a ragged one per expert), the fc2 dgrad 256-row tiles
     "rows192_bf16": Config("rows192_bf16", 1500, 256, 512, 4, 2, 0, 4, "bf16", 1, 22),
+    # the widest router the library takes: 1024 experts, all local (the
+    # routing scan's block holds exactly one thread per expert)
+    "max_experts_bf16": Config("max_experts_bf16", 300, 256, 256, 1024, 8, 0, 1024, "bf16", 1, 24),
     "ragged_fp32": Config("ragged_fp32", 37, 64, 192, 3, 2, 0, 3, "f32", 1, 20),
     # float32 storage with experts above the chunk (4 x 128 mean rows = 512):
     # the float32 weight-gradient kernels' partial slots and ordered reduction

@@ -142,12 +142,24 @@ def test_mx_train_steps_are_bit_identical_and_fingerprint_the_encoded_buffers():
     _, a = trace.run(cfg, 3, "ops", mx=True)
     _, b = trace.run(cfg, 3, "ops", mx=True)
     assert trace.first_divergence(a.records, b.records) is None
-    enc = {r.name for r in a.records if r.op == "moe_mx_quantize"}
-    assert enc == {f"{n}_{k}" for n in ("dy", "w2", "dh", "w1") for k in ("codes", "scales")}
-    assert all(r.dtype == "u8" for r in a.records if r.op == "moe_mx_quantize")
+    def names(op):
+        return {r.name for r in a.records if r.op == op}
+
+    def both(*ns):
+        return {f"{n}_{k}" for n in ns for k in ("codes", "scales")}
+
+    assert names("moe_mx_quantize") == both("x", "act", "dy", "w2", "dh", "w1")
+    assert names("moe_mx_quantize_t") == both("w1t", "w2t")
+    assert names("moe_mx_quantize_wgrad") == both("x", "dh", "act", "dy")
+    assert names("moe_mx_fwd_fc1") == {"h"} and names("moe_mx_fwd_fc2") == {"y"}
+    assert names("moe_mx_wgrad") == {"dw1", "dw2"} and not names("moe_fwd") - {
+        "topk_idx", "topk_prob", "counts", "offsets", "row_src", "slot_row"}
+    assert not names("moe_bwd_wgrad") and not names("moe_bwd_dgrad_dprob")
+    assert all(r.dtype == "u8" for r in a.records if r.op.startswith("moe_mx_quantize"))
     nv = [r.name for r in a.records if r.op == "moe_nvfp4_quantize" and r.step == 0]
     assert nv == ["dh_codes", "dh_scales", "dh_tensor_scale"]
-    # a different computation from the bf16 step: the traces part at step 0's backward
+    # a different computation from the bf16 step: the traces part at step 0's
+    # forward (same routing, then the MXFP8 encodings)
     _, c = trace.run(cfg, 3, "ops")
     d = trace.first_divergence(a.records, c.records)
-    assert d is not None and d[1].step == 0 and d[1].phase == "backward"
+    assert d is not None and d[1].step == 0 and d[1].phase == "forward"
