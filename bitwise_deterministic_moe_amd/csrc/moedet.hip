@@ -1118,7 +1118,7 @@ MOE_API moe_status moe_mx_quantize_wgrad(const moe_problem* p, const moe_routing
   if (!src || !codes || !scales) return MOE_ERR_NULL;
   if (kind == MOE_MXW_TOKEN && !routing->row_tok) return MOE_ERR_NULL;
   if (kind == MOE_MXW_ACT_P && !routing->row_prob) return MOE_ERR_NULL;
-  if ((uintptr_t)codes & 15) return MOE_ERR_SHAPE;
+  if (((uintptr_t)codes | (uintptr_t)src) & 15) return MOE_ERR_SHAPE;
   MxWgradQuantParams Q{};
   Q.src = (const uint16_t*)src;
   Q.kind = (int)kind;

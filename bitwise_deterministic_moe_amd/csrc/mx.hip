@@ -51,6 +51,27 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const T* in, int64_t r
   if ((threadIdx.x & 3) == 0) scales[(8 * i) / 32] = (uint8_t)(se + 127);
 }
 
+// Encode one block of 32 float32 values (the definition above) and store
+// its 32 codes (two 16-byte stores) and its scale byte.
+DEV void mx_encode_block_store(const float (&v)[32], uint8_t* codes, uint8_t* scale) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(v[i]) & 0x7fffffffu);
+  const int ef = (int)(m >> 23);
+  const int se = ef == 0 ? -127 : min(127, max(-127, ef - 127 - 8));
+  const float f = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se, exact
+  uint32_t w[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    w[q] = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[q] |= e4m3_rne(v[4 * q + e] * f) << (8 * e);
+  }
+  *(u32x4_t*)codes = u32x4_t{w[0], w[1], w[2], w[3]};
+  *(u32x4_t*)(codes + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
+  *scale = (uint8_t)(se + 127);
+}
+
 // MXFP8 of the transpose of each group's [rows, cols] matrix: a block is 32
 // consecutive rows of one column, and the codes of column c are written as
 // row c of the output (codes [groups][cols][rows], scales
@@ -76,23 +97,7 @@ __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const T* in, int64_t
     else
       v[i] = src[(int64_t)i * cols];
   }
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(v[i]) & 0x7fffffffu);
-  const int ef = (int)(m >> 23);
-  const int se = ef == 0 ? -127 : min(127, max(-127, ef - 127 - 8));
-  const float f = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se, exact
-  uint32_t w[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    w[q] = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) w[q] |= e4m3_rne(v[4 * q + b] * f) << (8 * b);
-  }
-  uint8_t* dst = codes + (g * cols + c) * rows + rb * 32;
-  *(u32x4_t*)dst = u32x4_t{w[0], w[1], w[2], w[3]};
-  *(u32x4_t*)(dst + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
-  scales[(g * cols + c) * nrb + rb] = (uint8_t)(se + 127);
+  mx_encode_block_store(v, codes + (g * cols + c) * rows + rb * 32, scales + (g * cols + c) * nrb + rb);
 }
 
 // MXFP8 operands of the weight gradients: quantised along the routed rows
@@ -106,68 +111,109 @@ __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const T* in, int64_t
 //   row:   src[r] (dH),
 //   act_p: p_r * (relu(h_r))^2 from h = src[r], relu(v) = v > 0 ? v : +0,
 //          the square rounded to float32 and then the product.
-// Same encoding as mx_quantize_t_kernel; one thread per (column, block).
-// Scales are stored slice-major, [rpad / 64][cols][2], so that the weight-
-// gradient GEMM streams a tile's scales of one 64-row slice as one
-// contiguous run.  Blocks at or past poff[el] are not written.
+// Same encoding as mx_quantize_t_kernel.  Scales are stored slice-major,
+// [rpad / 64][cols][2], so that the weight-gradient GEMM streams a tile's
+// scales of one 64-row slice as one contiguous run.  Blocks at or past
+// poff[el] are not written.
+//
+// Workgroup: 128 padded rows (four blocks: one 128-byte line of codes per
+// column) by 256 columns, in four chunks of 64.  The padded and routed row
+// offsets are copied to LDS once (one memory round trip) and each of the
+// 128 rows finds its expert by binary search there, then its source row
+// (and p) once; per chunk the rows are loaded 16 bytes a lane (eight lanes
+// a row) into LDS as float32, thread (column, block) encodes its 32 values,
+// and the four threads of a column store its 128-byte line.
+constexpr int kQwRows = 128, kQwCols = 64, kQwChunks = 4;
 template <int KIND>
 __global__ __launch_bounds__(256) void mx_quantize_wgrad_kernel(MxWgradQuantParams P) {
-  const int64_t ncb = (P.cols + 255) / 256, nrb = P.rpad / 32;
+  __shared__ float s_v[kQwRows][kQwCols + 1];
+  __shared__ int s_poff[kMaxExperts + 1];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int64_t s_src[kQwRows];   // source row of each tile row, -1: padding
+  __shared__ float s_p[kQwRows];
+  const int64_t ncb = P.cols / (kQwCols * kQwChunks), nrb = (P.rpad + kQwRows - 1) / kQwRows;
   const int64_t u = map_unit(blockIdx.x, nrb * ncb, P.seed);
   if (u < 0) return;
-  const int64_t rb = u / ncb, cb = u % ncb;
-  const int64_t c = cb * 256 + threadIdx.x;
-  const int j0 = (int)(rb * 32);
-  if (c >= P.cols || j0 >= P.poff[P.el]) return;
-  // the expert holding padded row j0: the last g with poff[g] <= j0
-  int lo = 0, hi = P.el - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (P.poff[mid] <= j0) lo = mid; else hi = mid - 1;
+  const int j0 = (int)((u / ncb) * kQwRows);
+  const int64_t cbase = (u % ncb) * (kQwCols * kQwChunks);
+  const int total = P.poff[P.el];
+  if (j0 >= total) return;
+  const int tid = threadIdx.x;
+  for (int g = tid; g <= P.el; g += 256) {
+    s_poff[g] = P.poff[g];
+    s_off[g] = P.offsets[g];
   }
-  const int local0 = j0 - P.poff[lo];
-  const int live = P.counts[lo] - local0;   // rows of the block below the count (uniform)
-  const int r0 = P.offsets[lo] + local0;
-  float v[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    if (i < live) {
-      const int64_t srcrow = KIND == kMxwToken ? (int64_t)P.row_tok[r0 + i] : (int64_t)(r0 + i);
-      v[i] = bf16_to_f32(P.src[srcrow * P.cols + c]);
-    } else {
-      v[i] = 0.f;
+  __syncthreads();
+  if (tid < kQwRows) {
+    // routed row of padded row j (padding: none), its expert being the last
+    // g with poff[g] <= j
+    const int j = j0 + tid;
+    int64_t src = -1;
+    float p = 0.f;
+    if (j < total) {
+      int lo = 0, hi = P.el - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_poff[mid] <= j) lo = mid; else hi = mid - 1;
+      }
+      const int local = j - s_poff[lo];
+      if (local < s_off[lo + 1] - s_off[lo]) {
+        const int r = s_off[lo] + local;
+        src = KIND == kMxwToken ? (int64_t)P.row_tok[r] : (int64_t)r;
+        if constexpr (KIND == kMxwActP) p = P.row_prob[r];
+      }
     }
+    s_src[tid] = src;
+    s_p[tid] = p;
   }
-  if constexpr (KIND == kMxwActP) {
+  __syncthreads();
+  const int cc = (tid & 7) * 8;   // this lane's 8 columns of a row
+  const int c = tid >> 2, b = tid & 3;
+  const int jb = j0 + 32 * b;
+#pragma unroll 1
+  for (int chunk = 0; chunk < kQwChunks; ++chunk) {
+    const int64_t c0 = cbase + chunk * kQwCols;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float rl = v[i] > 0.f ? v[i] : 0.f;
-      const float sq = rl * rl;
-      v[i] = i < live ? P.row_prob[r0 + i] * sq : 0.f;
+    for (int pass = 0; pass < kQwRows / 32; ++pass) {
+      const int i = pass * 32 + (tid >> 3);
+      const int64_t srow = s_src[i];
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = 0.f;
+      if (srow >= 0) {
+        const u32x4_t x = *(const u32x4_t*)(P.src + srow * P.cols + c0 + cc);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          v[2 * w] = bf16_to_f32(x[w] & 0xffffu);
+          v[2 * w + 1] = bf16_to_f32(x[w] >> 16);
+        }
+        if constexpr (KIND == kMxwActP) {
+          const float pr = s_p[i];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float rl = v[q] > 0.f ? v[q] : 0.f;
+            const float sq = rl * rl;
+            v[q] = pr * sq;
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s_v[i][cc + q] = v[q];
     }
+    __syncthreads();
+    if (jb < total) {
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[i] = s_v[32 * b + i][c];
+      mx_encode_block_store(v, P.codes + (c0 + c) * P.rpad + jb,
+                            P.scales + (((int64_t)(jb / 32) >> 1) * P.cols + c0 + c) * 2 + ((jb / 32) & 1));
+    }
+    __syncthreads();
   }
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) m = max(m, __float_as_uint(v[i]) & 0x7fffffffu);
-  const int ef = (int)(m >> 23);
-  const int se = ef == 0 ? -127 : min(127, max(-127, ef - 127 - 8));
-  const float f = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se, exact
-  uint32_t w[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    w[q] = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) w[q] |= e4m3_rne(v[4 * q + b] * f) << (8 * b);
-  }
-  uint8_t* dst = P.codes + c * P.rpad + j0;
-  *(u32x4_t*)dst = u32x4_t{w[0], w[1], w[2], w[3]};
-  *(u32x4_t*)(dst + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
-  // slice-major scales: the two blocks of each 64-row slice of a column together
-  P.scales[((rb >> 1) * P.cols + c) * 2 + (rb & 1)] = (uint8_t)(se + 127);
 }
 
 hipError_t launch_mx_quantize_wgrad(const MxWgradQuantParams& P, hipStream_t st) {
-  const int64_t units = (P.rpad / 32) * ((P.cols + 255) / 256);
+  const int64_t units = ((P.rpad + kQwRows - 1) / kQwRows) * (P.cols / (kQwCols * kQwChunks));
   if (units == 0) return hipSuccess;
   const int64_t grid = grid_for_units(units);
   if (P.kind == kMxwToken)

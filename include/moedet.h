@@ -572,7 +572,7 @@ moe_status moe_mx_wgrad_cols(const moe_problem* p, int64_t* rpad_cap);
  * ((b / 2) * cols + c) * 2 + b % 2 (the two blocks of each 64-column slice
  * of a row side by side, slices outermost), so that the GEMM reads a tile's
  * scales of one slice as one contiguous run.
- *   src            DEVICE bf16, as moe_mxw_src describes
+ *   src            DEVICE bf16, as moe_mxw_src describes, 16-byte aligned
  *   codes          DEVICE uint8 [cols, rpad_cap], 16-byte aligned
  *   scales         DEVICE uint8 [rpad_cap / 64, cols, 2]
  * Columns from poff[num_local] on are not written.  routing: as written by

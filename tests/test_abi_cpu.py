@@ -306,3 +306,11 @@ def test_route_validation_and_stage_names(lib):
     assert lib.moe_route(ctypes.byref(cp), None, ctypes.byref(r), fake, 1 << 40, 0, None) == 1
     assert lib.moe_route(ctypes.byref(cp), fake, ctypes.byref(r), ctypes.c_void_p(0x100000), 16, 0, None) == 4
     assert lib.moe_route(None, fake, ctypes.byref(r), fake, 1 << 40, 0, None) == 1
+
+
+def test_mx_quantize_wgrad_needs_an_aligned_source(lib):
+    r = moe._CRouting(*([0x2000] * 9))
+    cp = moe.Problem(**BASE).c()
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.moe_mx_quantize_wgrad(ctypes.byref(cp), ctypes.byref(r), ctypes.c_void_p(0x1002), 1, fake, fake,
+                                     None) == 2
