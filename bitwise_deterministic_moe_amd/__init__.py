@@ -589,15 +589,16 @@ def moe_mx_quantize_wgrad(prob: Problem, routing: Routing, src: torch.Tensor, ki
     """MXFP8 of a weight-gradient operand along each expert's routed rows.
     kind MXW_TOKEN: src [T, D] gathered by token (x, dY); MXW_ROW: src
     [rows_cap, F] (dH); MXW_ACT_P: src = h [rows_cap, F], encodes
-    p relu(h)^2.  Returns (codes uint8 [cols, rpad_cap], scales uint8
-    [rpad_cap / 64, cols, 2]); columns past the padded total are not written."""
+    p relu(h)^2.  Returns (codes uint8 [rpad_cap / 64, cols, 64], scales
+    uint8 [rpad_cap / 64, cols, 2]), slice-major; slices past the padded
+    total are not written."""
     lib = load_library()
     rp = moe_mx_wgrad_cols(prob)
     cols = prob.d_model if kind == MXW_TOKEN else prob.d_ffn
     rows = prob.tokens if kind == MXW_TOKEN else prob.rows_cap
     _need(src, rows * cols, torch.bfloat16, "moe_mx_quantize_wgrad src")
     if codes is None:
-        codes = torch.empty((cols, rp), dtype=torch.uint8, device=src.device)
+        codes = torch.empty((rp // 64, cols, 64), dtype=torch.uint8, device=src.device)
     if scales is None:
         scales = torch.empty((rp // 64, cols, 2), dtype=torch.uint8, device=src.device)
     _need(codes, cols * rp, torch.uint8, "moe_mx_quantize_wgrad codes")

@@ -817,8 +817,9 @@ struct MxRingScales {
 // Pipelined MXFP8 main loop of one 256-column tile over nsteps slices of 64
 // codes (nsteps even), accumulated into acc in a fixed order: slice by
 // slice, and within a slice A block by A block against B blocks 0..3.
-// Slices at or past nlive load as zeros; slice s reads operand bytes
-// (kslice0 + s) * 64 onward of each row.
+// Slices at or past nlive load as zeros; slice s of an operand starts
+// (kslice0 + s) * a_sstride (b_sstride) bytes past its tile rows' offsets:
+// 64 for codes stored K-contiguous, rows * 64 for slice-major codes.
 // Scales, RS == false: the scale of tile row r and 32-code block kb of the
 // call is s_sa[r * nkb + kb] (s_sb for B; kb past nkb - 1 reads nkb - 1,
 // and every byte read must be a finite scale); store_scales() writes those
@@ -831,19 +832,20 @@ struct MxRingScales {
 // waves may still read LDS: the caller drains and synchronises before
 // reusing it.
 template <int NA, int WTM, bool RS, class StoreScales>
-DEV void mx_mainloop(uint16_t* lds, const bf::KcOperand& oa, const bf::KcOperand& ob, const MxRingScales& rsc,
-                     int kslice0, int nsteps, int nlive, const uint8_t* s_sa, const uint8_t* s_sb, int nkb,
-                     StoreScales store_scales, f32x16_t (&acc)[4][4], int wave, int lane, int wm, int wn) {
+DEV void mx_mainloop(uint16_t* lds, const bf::KcOperand& oa, const bf::KcOperand& ob, uint32_t a_sstride,
+                     uint32_t b_sstride, const MxRingScales& rsc, int kslice0, int nsteps, int nlive,
+                     const uint8_t* s_sa, const uint8_t* s_sb, int nkb, StoreScales store_scales,
+                     f32x16_t (&acc)[4][4], int wave, int lane, int wm, int wn) {
   const uint32_t ring = bf::lds_base(lds);
   const uint32_t sring = bf::lds_base(s_sa);
   constexpr int NL = RS ? 9 : 8;   // loads per slice and thread
-  // slice s: 64 codes = 64 bytes per row, the byte offset of a bf16 slice of 32
+  // slice s: 64 codes = 64 bytes per row, the size of a bf16 slice of 32
   auto issue = [&](int s, int i) __attribute__((always_inline)) {
     const uint32_t st = ring + (uint32_t)(s & 3) * (bf::STAGE * 2);
     if (i < bf::LOADS)
-      oa.issue1(st, wave, (kslice0 + s) * bf::BK, s < nlive, i);
+      oa.issue1_bytes(st, wave, (uint32_t)(kslice0 + s) * a_sstride, s < nlive, i);
     else if (i < 2 * bf::LOADS)
-      ob.issue1(st + bf::OPER * 2, wave, (kslice0 + s) * bf::BK, s < nlive, i - bf::LOADS);
+      ob.issue1_bytes(st + bf::OPER * 2, wave, (uint32_t)(kslice0 + s) * b_sstride, s < nlive, i - bf::LOADS);
     else
       rsc.issue(sring + (uint32_t)(s & 3) * kMxScaleSlot, wave, kslice0 + s, s < nlive);
   };
@@ -990,7 +992,7 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
   // the number of slices is even (K is a multiple of 128)
   const int nsteps = P.K / 64;
   const MxRingScales none{};
-  mx_mainloop<NA, WTM, false>(lds, oa, ob, none, 0, nsteps, nsteps, s_sa, s_sb, nkb, [&]() __attribute__((always_inline)) {
+  mx_mainloop<NA, WTM, false>(lds, oa, ob, 64u, 64u, none, 0, nsteps, nsteps, s_sa, s_sb, nkb, [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < kSw; ++q) {
       const int idx = tid + 256 * q;
@@ -1034,9 +1036,10 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
 // runs over the expert's padded routed rows, whose count is even in 64-code
 // slices or completed by one slice of zeros.  One workgroup accumulates a
 // tile over the whole K range in slice order and stores it once, so the
-// result does not depend on the launch order and needs no reduction.  The
-// scales (slice-major) stream through LDS with the codes.  An expert
-// without rows gets a zero tile.
+// result does not depend on the launch order and needs no reduction.  Codes
+// and scales are slice-major (a tile's slice is one contiguous run of 16 KiB
+// of codes and 512 bytes of scales); the scales stream through LDS with the
+// codes.  An expert without rows gets a zero tile.
 template <class T>
 DEV T pick(int c, T a, T b) {
   return c ? a : b;
@@ -1060,9 +1063,12 @@ __global__ __launch_bounds__(256) void mx_wgrad_kernel(MxWgradParams P) {
   const uint8_t* bs = pick(mat, P.dy_scales, P.dh_scales);
   float* dst = pick(mat, P.dw2, P.dw1) + (int64_t)g * P.D * P.F;
   const int p0 = P.poff[g], nsl = (P.poff[g + 1] - p0) / 64;
+  // slice-major codes: slice j of operand rows R at byte (j R + row) 64
   bf::KcOperand oa, ob;
-  oa.init(ac, (uint32_t)(M * P.rpad), wave, lane, [&](int r) -> uint32_t { return (uint32_t)((m0 + r) * P.rpad + p0); });
-  ob.init(bc, (uint32_t)(N * P.rpad), wave, lane, [&](int r) -> uint32_t { return (uint32_t)((n0 + r) * P.rpad + p0); });
+  oa.init(ac, (uint32_t)(M * P.rpad), wave, lane,
+          [&](int r) -> uint32_t { return (uint32_t)(((int64_t)(p0 / 64) * M + m0 + r) * 64); });
+  ob.init(bc, (uint32_t)(N * P.rpad), wave, lane,
+          [&](int r) -> uint32_t { return (uint32_t)(((int64_t)(p0 / 64) * N + n0 + r) * 64); });
   // slice-major scales: slice j of operand rows R at byte (j R + row) 2
   MxRingScales rsc;
   rsc.init(wave, lane, as, (uint32_t)(M * P.rpad / 32), (uint32_t)(((int64_t)(p0 / 64) * M + m0) * 2), (uint32_t)(2 * M),
@@ -1074,7 +1080,8 @@ __global__ __launch_bounds__(256) void mx_wgrad_kernel(MxWgradParams P) {
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-  mx_mainloop<4, 128, true>(lds, oa, ob, rsc, 0, (nsl + 1) & ~1, nsl, s_sc, s_sc, 2, [] {}, acc, wave, lane, wm, wn);
+  mx_mainloop<4, 128, true>(lds, oa, ob, (uint32_t)(64 * M), (uint32_t)(64 * N), rsc, 0, (nsl + 1) & ~1, nsl, s_sc,
+                            s_sc, 2, [] {}, acc, wave, lane, wm, wn);
   // every load (those of the zero slices past the end included) landed and
   // every wave done with the ring before the epilogue stages through it
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

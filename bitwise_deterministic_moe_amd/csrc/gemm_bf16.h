@@ -194,7 +194,11 @@ struct KcOperand {
   // of the operand's tile in the slot (uniform); live == false issues the
   // load past the buffer end.
   DEV void issue1(uint32_t lds, int wave, int k0, bool live, int i) const {
-    dma16(rs, lds + (wave * LOADS + i) * 1024, live ? voff[i] : kOOB, live ? (uint32_t)k0 * 2u : 0u);
+    issue1_bytes(lds, wave, (uint32_t)k0 * 2u, live, i);
+  }
+  // The same with the slice's byte offset from the tile's rows given directly.
+  DEV void issue1_bytes(uint32_t lds, int wave, uint32_t soff, bool live, int i) const {
+    dma16(rs, lds + (wave * LOADS + i) * 1024, live ? voff[i] : kOOB, live ? soff : 0u);
   }
 };
 

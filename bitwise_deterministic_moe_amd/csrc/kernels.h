@@ -72,14 +72,14 @@ constexpr int kMxMaxK = 2048;  // K bound of the MXFP8 row GEMM (its scales are 
 constexpr int kMxPad = 64;
 
 // MXFP8 weight gradients: dW1_g = X_g^T dH_g and dW2_g = A_g^T dY_g from
-// operands quantised along the routed rows (codes [cols][rpad], scales
-// slice-major [rpad / 64][cols][2]; expert g owns columns poff[g] ..
-// poff[g+1]).
+// operands quantised along the routed rows, stored slice-major (codes
+// [rpad / 64][cols][64], scales [rpad / 64][cols][2]; expert g owns padded
+// rows poff[g] .. poff[g+1]).
 struct MxWgradParams {
   const int32_t* poff;    // el + 1 padded row offsets (routing.sched)
   int groups;             // local experts
   int D, F;
-  int64_t rpad;           // bytes per codes row
+  int64_t rpad;           // padded rows (a multiple of 64)
   const uint8_t* x_codes; const uint8_t* x_scales;      // [D][rpad]
   const uint8_t* dh_codes; const uint8_t* dh_scales;    // [F][rpad]
   const uint8_t* act_codes; const uint8_t* act_scales;  // [F][rpad]
@@ -102,7 +102,7 @@ struct MxWgradQuantParams {
   int el;
   const int32_t* row_tok;
   const float* row_prob;
-  uint8_t* codes;         // [cols][rpad]
+  uint8_t* codes;         // [rpad / 64][cols][64]
   uint8_t* scales;        // [rpad / 64][cols][2]
   uint64_t seed;
 };

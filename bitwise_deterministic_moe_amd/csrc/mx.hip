@@ -10,8 +10,9 @@
 //   at 448, sign kept.
 // v * 2^-se is exact in float32 whenever it can round to a nonzero code
 // (|v * 2^-se| < 512, and values that underflow float32 are far below the
-// smallest E4M3 subnormal, 2^-9).  The rounding is integer arithmetic on the
-// float32 bits; the block maximum is a max of bit patterns, so every output
+// smallest E4M3 subnormal, 2^-9).  The rounding is the hardware conversion
+// on values clamped to +-448 (e4m3x4, equal to the integer rounding
+// e4m3_rne); the block maximum is a max of bit patterns, so every output
 // byte is exact and independent of execution order.
 #include "common.h"
 #include "kernels.h"
@@ -40,12 +41,8 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const T* in, int64_t r
   const int ef = (int)(m >> 23);
   const int se = ef == 0 ? -127 : min(127, max(-127, ef - 127 - 8));
   const float f = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se, exact
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    lo |= e4m3_rne(v[q] * f) << (8 * q);
-    hi |= e4m3_rne(v[4 + q] * f) << (8 * q);
-  }
+  const uint32_t lo = e4m3x4(v[0] * f, v[1] * f, v[2] * f, v[3] * f);
+  const uint32_t hi = e4m3x4(v[4] * f, v[5] * f, v[6] * f, v[7] * f);
   if (!live) return;
   *(u32x2_t*)(codes + 8 * i) = u32x2_t{lo, hi};
   if ((threadIdx.x & 3) == 0) scales[(8 * i) / 32] = (uint8_t)(se + 127);
@@ -62,11 +59,7 @@ DEV void mx_encode_block_store(const float (&v)[32], uint8_t* codes, uint8_t* sc
   const float f = __uint_as_float((uint32_t)(127 - se) << 23);   // 2^-se, exact
   uint32_t w[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    w[q] = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[q] |= e4m3_rne(v[4 * q + e] * f) << (8 * e);
-  }
+  for (int q = 0; q < 8; ++q) w[q] = e4m3x4(v[4 * q] * f, v[4 * q + 1] * f, v[4 * q + 2] * f, v[4 * q + 3] * f);
   *(u32x4_t*)codes = u32x4_t{w[0], w[1], w[2], w[3]};
   *(u32x4_t*)(codes + 16) = u32x4_t{w[4], w[5], w[6], w[7]};
   *scale = (uint8_t)(se + 127);
@@ -111,18 +104,20 @@ __global__ __launch_bounds__(256) void mx_quantize_t_kernel(const T* in, int64_t
 //   row:   src[r] (dH),
 //   act_p: p_r * (relu(h_r))^2 from h = src[r], relu(v) = v > 0 ? v : +0,
 //          the square rounded to float32 and then the product.
-// Same encoding as mx_quantize_t_kernel.  Scales are stored slice-major,
-// [rpad / 64][cols][2], so that the weight-gradient GEMM streams a tile's
-// scales of one 64-row slice as one contiguous run.  Blocks at or past
-// poff[el] are not written.
+// Same encoding as mx_quantize_t_kernel.  Codes and scales are stored
+// slice-major, [rpad / 64][cols][64] and [rpad / 64][cols][2]: the 64 codes
+// (and two scales) of one column and 64-row slice, columns side by side, so
+// that the weight-gradient GEMM reads a tile's slice as one contiguous run
+// and this kernel writes whole runs.  Blocks at or past poff[el] are not
+// written.
 //
-// Workgroup: 128 padded rows (four blocks: one 128-byte line of codes per
-// column) by 256 columns, in four chunks of 64.  The padded and routed row
-// offsets are copied to LDS once (one memory round trip) and each of the
-// 128 rows finds its expert by binary search there, then its source row
-// (and p) once; per chunk the rows are loaded 16 bytes a lane (eight lanes
-// a row) into LDS as float32, thread (column, block) encodes its 32 values,
-// and the four threads of a column store its 128-byte line.
+// Workgroup: 128 padded rows (two slices) by 256 columns, in four chunks of
+// 64.  The padded and routed row offsets are copied to LDS once (one memory
+// round trip) and each of the 128 rows finds its expert by binary search
+// there, then its source row (and p) once; per chunk the rows are loaded 16
+// bytes a lane (eight lanes a row) into LDS as float32 and thread (column,
+// block) encodes its 32 values: a wave stores two contiguous 1 KiB runs of
+// codes (16 columns of each slice).
 constexpr int kQwRows = 128, kQwCols = 64, kQwChunks = 4;
 template <int KIND>
 __global__ __launch_bounds__(256) void mx_quantize_wgrad_kernel(MxWgradQuantParams P) {
@@ -170,31 +165,37 @@ __global__ __launch_bounds__(256) void mx_quantize_wgrad_kernel(MxWgradQuantPara
   const int cc = (tid & 7) * 8;   // this lane's 8 columns of a row
   const int c = tid >> 2, b = tid & 3;
   const int jb = j0 + 32 * b;
-#pragma unroll 1
+  // every chunk's loads issued up front: 4 rows x 16 bytes per chunk a lane
+  constexpr int kPass = kQwRows / 32;
+  u32x4_t raw[kQwChunks][kPass];
+#pragma unroll
+  for (int chunk = 0; chunk < kQwChunks; ++chunk)
+#pragma unroll
+    for (int pass = 0; pass < kPass; ++pass) {
+      const int64_t srow = s_src[pass * 32 + (tid >> 3)];
+      raw[chunk][pass] = srow >= 0 ? *(const u32x4_t*)(P.src + srow * P.cols + cbase + chunk * kQwCols + cc)
+                                   : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
   for (int chunk = 0; chunk < kQwChunks; ++chunk) {
     const int64_t c0 = cbase + chunk * kQwCols;
 #pragma unroll
-    for (int pass = 0; pass < kQwRows / 32; ++pass) {
+    for (int pass = 0; pass < kPass; ++pass) {
       const int i = pass * 32 + (tid >> 3);
-      const int64_t srow = s_src[i];
       float v[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = 0.f;
-      if (srow >= 0) {
-        const u32x4_t x = *(const u32x4_t*)(P.src + srow * P.cols + c0 + cc);
+      for (int w = 0; w < 4; ++w) {
+        v[2 * w] = bf16_to_f32(raw[chunk][pass][w] & 0xffffu);
+        v[2 * w + 1] = bf16_to_f32(raw[chunk][pass][w] >> 16);
+      }
+      if constexpr (KIND == kMxwActP) {
+        // padding rows hold zeros (p = 0 there), which stay +0
+        const float pr = s_p[i];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          v[2 * w] = bf16_to_f32(x[w] & 0xffffu);
-          v[2 * w + 1] = bf16_to_f32(x[w] >> 16);
-        }
-        if constexpr (KIND == kMxwActP) {
-          const float pr = s_p[i];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const float rl = v[q] > 0.f ? v[q] : 0.f;
-            const float sq = rl * rl;
-            v[q] = pr * sq;
-          }
+        for (int q = 0; q < 8; ++q) {
+          const float rl = v[q] > 0.f ? v[q] : 0.f;
+          const float sq = rl * rl;
+          v[q] = pr * sq;
         }
       }
 #pragma unroll
@@ -205,8 +206,8 @@ __global__ __launch_bounds__(256) void mx_quantize_wgrad_kernel(MxWgradQuantPara
       float v[32];
 #pragma unroll
       for (int i = 0; i < 32; ++i) v[i] = s_v[32 * b + i][c];
-      mx_encode_block_store(v, P.codes + (c0 + c) * P.rpad + jb,
-                            P.scales + (((int64_t)(jb / 32) >> 1) * P.cols + c0 + c) * 2 + ((jb / 32) & 1));
+      const int64_t at = ((int64_t)(jb / 64) * P.cols + c0 + c) * 2 + ((jb / 32) & 1);   // (slice, column, block)
+      mx_encode_block_store(v, P.codes + at * 32, P.scales + at);
     }
     __syncthreads();
   }

@@ -266,7 +266,7 @@ def train_step(cfg, st: TrainState, tracer: Tracer, hook: Optional[Callable] = N
         P = int(((routing.counts.long() + 63) // 64 * 64).sum().item())
         for n in ("x", "dh", "act", "dy"):
             codes, scales = wg_enc[n]
-            T.tensor(s, "backward", "moe_mx_quantize_wgrad", f"{n}_codes", codes[:, :P].contiguous(), 2)
+            T.tensor(s, "backward", "moe_mx_quantize_wgrad", f"{n}_codes", codes[: P // 64].contiguous(), 2)
             T.tensor(s, "backward", "moe_mx_quantize_wgrad", f"{n}_scales", scales[: P // 64].contiguous(), 2)
         T.tensor(s, "backward", "moe_mx_wgrad", "dw1", dw1, 1)
         T.tensor(s, "backward", "moe_mx_wgrad", "dw2", dw2, 1)

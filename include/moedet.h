@@ -563,19 +563,19 @@ moe_status moe_mx_wgrad_cols(const moe_problem* p, int64_t* rpad_cap);
  * moe_mx_quantize's (the French article, section on the method for
  * debugging non-determinism, fingerprints the encoded values and the scale
  * buffers; OCP MX v1.0: E4M3 codes, one E8M0 scale per 32 elements).
- * Layout: expert e owns columns poff[e] .. poff[e+1] of every output row,
- * poff the prefix sum of its routed row counts rounded up to a multiple of
- * 64; column poff[e] + i holds its routed row offsets[e] + i, transposed,
- * for i below its count, and zero past it.  A block is 32 consecutive
- * columns of one row, so blocks start at an expert's first row.  The
- * scales are stored slice-major: the scale of row c, block b is byte
- * ((b / 2) * cols + c) * 2 + b % 2 (the two blocks of each 64-column slice
- * of a row side by side, slices outermost), so that the GEMM reads a tile's
- * scales of one slice as one contiguous run.
+ * Layout: expert e owns padded rows poff[e] .. poff[e+1], poff the prefix
+ * sum of its routed row counts rounded up to a multiple of 64; padded row
+ * poff[e] + i is its routed row offsets[e] + i for i below its count, and
+ * zeros past it.  A block is 32 consecutive padded rows of one column, so
+ * blocks start at an expert's first row.  Codes and scales are stored
+ * slice-major: the 64 codes and two scales of column c in 64-row slice j
+ * are codes[j][c][0..63] and scales[j][c][0..1] (slices outermost, columns
+ * side by side), so that the GEMM reads a tile's slice as one contiguous
+ * run.
  *   src            DEVICE bf16, as moe_mxw_src describes, 16-byte aligned
- *   codes          DEVICE uint8 [cols, rpad_cap], 16-byte aligned
+ *   codes          DEVICE uint8 [rpad_cap / 64, cols, 64], 16-byte aligned
  *   scales         DEVICE uint8 [rpad_cap / 64, cols, 2]
- * Columns from poff[num_local] on are not written.  routing: as written by
+ * Slices from poff[num_local] / 64 on are not written.  routing: as written by
  * moe_fwd.  The problem must be bf16 with max(D, F) * rpad_cap < 2^31.
  * Deterministic: every byte depends on the inputs only.  Errors:
  * MOE_ERR_DTYPE, MOE_ERR_SHAPE (sizes, alignment, kind), MOE_ERR_NULL before
@@ -593,7 +593,7 @@ moe_status moe_mx_quantize_wgrad(const moe_problem* p, const moe_routing* routin
  * (64 rows per scaled MFMA, ascending) and stored once: the result is
  * bitwise reproducible with no reduction step (there is no atomic mode).
  * An expert without rows gets zeros.
- *   *_codes        DEVICE uint8 [D or F, rpad_cap], 16-byte aligned
+ *   *_codes        DEVICE uint8 [rpad_cap / 64, D or F, 64], 16-byte aligned
  *   *_scales       DEVICE uint8 [rpad_cap / 64, D or F, 2], 16-byte aligned
  *   dw1, dw2       DEVICE float32 [num_local, D, F] / [num_local, F, D]
  * The problem must be bf16 with max(D, F) * rpad_cap < 2^31.  Errors:

@@ -84,10 +84,10 @@ class Case:
         return oracle.act_p_f32(bf16_bits_to_f32(self.h_bits[rows]), self.p[rows]).astype(np.float64)
 
 
-def _slice_major(scales_cm):
-    """Oracle scales [cols, P/32] -> the library's [P/64, cols, 2]."""
-    cols, nb = scales_cm.shape
-    return scales_cm.reshape(cols, nb // 2, 2).transpose(1, 0, 2)
+def _slice_major(a, per):
+    """Oracle codes [cols, P] (per = 64) or scales [cols, P/32] (per = 2) ->
+    the library's slice-major [P/64, cols, per]."""
+    return a.reshape(a.shape[0], -1, per).transpose(1, 0, 2)
 
 
 def _u8(t):
@@ -104,9 +104,9 @@ def test_mx_quantize_wgrad_bytes_equal_the_oracle(name):
         torch.cuda.synchronize()
         rc, rs, poff = oracle.mx_quantize_expert_rows(case.oracle_values(op), off)
         P = int(poff[-1])
-        assert P <= codes.shape[1]
-        assert np.array_equal(_u8(codes[:, :P]), rc), op
-        assert np.array_equal(_u8(scales[: P // 64]), _slice_major(rs)), op
+        assert P // 64 <= codes.shape[0]
+        assert np.array_equal(_u8(codes[: P // 64]), _slice_major(rc, 64)), op
+        assert np.array_equal(_u8(scales[: P // 64]), _slice_major(rs, 2)), op
 
 
 def _expert_check(checks, e, got1, got2, enc, p0, p1):
@@ -177,14 +177,14 @@ def test_mx_wgrad_bits_identical_under_shuffles_and_poisoned_buffers():
         for op in ("x", "dh", "act", "dy"):
             cols = cfg.d_model if op in ("x", "dy") else cfg.d_ffn
             rp = moe.moe_mx_wgrad_cols(ps)
-            c = torch.full((cols, rp), fill, dtype=torch.uint8, device="cuda")
+            c = torch.full((rp // 64, cols, 64), fill, dtype=torch.uint8, device="cuda")
             s = torch.full((rp // 64, cols, 2), fill, dtype=torch.uint8, device="cuda")
             ops.append(moe.moe_mx_quantize_wgrad(ps, case.routing, case.src(op), KINDS[op], c, s))
         dw1 = torch.full((ps.local, cfg.d_model, cfg.d_ffn), float(fill), device="cuda")
         dw2 = torch.full((ps.local, cfg.d_ffn, cfg.d_model), float(fill), device="cuda")
         moe.moe_mx_wgrad(ps, case.routing, *ops, dw1=dw1, dw2=dw2)
         P = int(oracle.mx_pad_offsets(case.perm["counts"])[-1])
-        fps = [moe.moe_fingerprint(c[:, :P].contiguous())[1] for c, _ in ops]
+        fps = [moe.moe_fingerprint(c[: P // 64].contiguous())[1] for c, _ in ops]
         fps += [moe.moe_fingerprint(s[: P // 64].contiguous())[1] for _, s in ops]
         fps += [moe.moe_fingerprint(dw1)[1], moe.moe_fingerprint(dw2)[1]]
         ref = fps if ref is None else ref
@@ -206,7 +206,7 @@ def test_mx_wgrad_full_size_latent_streamed():
     off = case.perm["offsets"].astype(np.int64)
     poff = oracle.mx_pad_offsets(counts)
     P = int(poff[-1])
-    host = {op: (_u8(c[:, :P]), _u8(s[: P // 64])) for op, (c, s) in ops.items()}
+    host = {op: (_u8(c[: P // 64]), _u8(s[: P // 64])) for op, (c, s) in ops.items()}
     checks = _new_checks()
 
     def oracle_expert(e):
@@ -220,7 +220,7 @@ def test_mx_wgrad_full_size_latent_streamed():
             for e, enc in pool.map(oracle_expert, range(b0, min(b0 + 64, cfg.num_local))):
                 p0, p1 = int(poff[e]), int(poff[e + 1])
                 for op in KINDS:
-                    assert np.array_equal(host[op][0][:, p0:p1], enc[op][0]), (e, op)
-                    assert np.array_equal(host[op][1][p0 // 64: p1 // 64], _slice_major(enc[op][1])), (e, op)
+                    assert np.array_equal(host[op][0][p0 // 64: p1 // 64], _slice_major(enc[op][0], 64)), (e, op)
+                    assert np.array_equal(host[op][1][p0 // 64: p1 // 64], _slice_major(enc[op][1], 2)), (e, op)
                 _expert_check(checks, e, dw1[e], dw2[e], enc, 0, p1 - p0)
     _report(checks, "[latent mx wgrad]")

@@ -44,12 +44,23 @@ def _ties():
     return rows
 
 
-@pytest.mark.parametrize("case", ["binades", "ties", "zero", "tiny"])
+@pytest.mark.parametrize("case", ["binades", "near_binades", "ties", "zero", "tiny", "subnormal_g"])
 def test_nvfp4_f32_bytes_equal_the_oracle(case):
+    """binades: row scales over 60 binades (rows far below the tensor amax
+    get block scale 0); near_binades: row scales within 2^12 of the tensor
+    amax, so every row reaches the E2M1 encoder; subnormal_g: amax near
+    2^-120, so the tensor scale g = amax / 2688 and the decode scales are
+    float32 subnormals."""
     print(f"nvfp4 {case}", flush=True)
     rng = np.random.default_rng(11)
     if case == "binades":
         rows = (rng.standard_normal((64, 512)) * np.exp2(rng.uniform(-30, 30, (64, 1)))).astype(np.float32)
+    elif case == "near_binades":
+        rows = (rng.standard_normal((64, 512)) * np.exp2(rng.uniform(-12, 0, (64, 1)) + 5)).astype(np.float32)
+    elif case == "subnormal_g":
+        rows = (rng.standard_normal((16, 64)) * np.exp2(rng.uniform(-8, 0, (16, 1)) - 122)).astype(np.float32)
+        g = np.float32(np.abs(rows).max()) / np.float32(2688)
+        assert 0 < g < np.finfo(np.float32).tiny
     elif case == "ties":
         rows = _ties()
     elif case == "zero":
