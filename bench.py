@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--no-extras", action="store_true", help="skip the router / MXFP8 / NVFP4 legs")
     ap.add_argument("--profile-only", action="store_true",
                     help="run warmup + timed steps of the headline workload only (for rocprofv3 runs)")
+    ap.add_argument("--profile-mx-wgrad", action="store_true",
+                    help="with --profile-only: time the MXFP8 weight gradients (the four row quantisations "
+                         "and the GEMM) instead of the bf16 backward step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (calibrates the "
                          "FETCH_SIZE / WRITE_SIZE counters against known bytes)")
@@ -358,13 +361,14 @@ def main():
     cfg = CONFIGS[args.config]
     wl = Workload(cfg)
     if args.profile_only:
+        run = mx_wgrad_runner(wl) if args.profile_mx_wgrad else (lambda: wl.step(moe.DETERMINISTIC))
         for _ in range(args.warmup):
-            wl.step(moe.DETERMINISTIC)
+            run()
         torch.cuda.synchronize()
         t0, t1 = _ev(), _ev()
         t0.record()
         for _ in range(args.steps):
-            wl.step(moe.DETERMINISTIC)
+            run()
         t1.record()
         torch.cuda.synchronize()
         print(json.dumps({"profile_only": True, "config": cfg.name, "ms_per_step": t0.elapsed_time(t1) / args.steps}))
@@ -682,6 +686,26 @@ def measured_mx_fwd(cfg, wl, bf16_stages, reps=20):
     return res
 
 
+def mx_wgrad_runner(wl):
+    """A closure running the MXFP8 weight gradients once on the workload:
+    dh from one deterministic bf16 data-gradient call, then the four row
+    quantisations and the GEMM into preallocated buffers."""
+    import bitwise_deterministic_moe_amd as moe
+    b = wl.bufs[moe.DETERMINISTIC]
+    moe.moe_bwd_dgrad_dprob(wl.prob, wl.routing, wl.dy, wl.w1, wl.w2, wl.h, moe.DETERMINISTIC, dx=b["dx"],
+                            dprob=b["dprob"], dh=b["dh"], ws=b["ws1"])
+    srcs = (("x", wl.x, moe.MXW_TOKEN), ("dh", b["dh"], moe.MXW_ROW), ("act", wl.h, moe.MXW_ACT_P),
+            ("dy", wl.dy, moe.MXW_TOKEN))
+    enc = {n: moe.moe_mx_quantize_wgrad(wl.prob, wl.routing, t, k) for n, t, k in srcs}
+
+    def run():
+        for n, t, k in srcs:
+            moe.moe_mx_quantize_wgrad(wl.prob, wl.routing, t, k, *enc[n])
+        moe.moe_mx_wgrad(wl.prob, wl.routing, enc["x"], enc["dh"], enc["act"], enc["dy"], dw1=b["dw1"],
+                         dw2=b["dw2"])
+    return run
+
+
 def measured_mx_wgrad(cfg, wl, dh, bf16_ms, reps=10):
     """The MXFP8 weight gradients on the workload's x, dY, saved h and the
     backward's dh: the four row-quantised encodings (moe_mx_quantize_wgrad)
@@ -716,7 +740,7 @@ def measured_mx_wgrad(cfg, wl, dh, bf16_ms, reps=10):
     q_ms = timed(quantise_all)
     g_ms = timed(lambda: moe.moe_mx_wgrad(wl.prob, wl.routing, enc["x"], enc["dh"], enc["act"], enc["dy"],
                                           dw1=dw1, dw2=dw2))
-    rp = moe.moe_mx_wgrad_cols(wl.prob)
+    rp = moe.moe_mx_wgrad_rows(wl.prob)
     counts = wl.routing.counts.long()
     P = int(((counts + 63) // 64 * 64).sum().item())
     flops = 4.0 * wl.R * D * F
@@ -725,6 +749,7 @@ def measured_mx_wgrad(cfg, wl, dh, bf16_ms, reps=10):
     bound_ms = max(flops / (FP8_PEAK_TFLOPS * 1e12), (out_bytes + in_bytes) / (HBM_PEAK_GBS * 1e9)) * 1e3
     return {"gemm_ms": round(g_ms, 5), "gemm_tflops": round(flops / (g_ms * 1e-3) / 1e12, 1),
             "gemm_GBs": round((out_bytes + in_bytes) / (g_ms * 1e-3) / 1e9, 1),
+            "gemm_traffic": measured_traffic(cfg.name, "mx_wgrad"),
             "gemm_bound_ms": round(bound_ms, 5), "gemm_frac_of_bound": round(bound_ms / g_ms, 4),
             "quantise_ms": round(q_ms, 5), "padded_rows": P, "rows": wl.R, "rpad_cap": rp,
             "bf16_wgrad_ms": round(bf16_ms, 5), "total_ms": round(q_ms + g_ms, 5)}

@@ -19,7 +19,7 @@ __all__ = [
     "moe_fwd", "moe_bwd_dgrad_dprob", "moe_bwd_wgrad", "moe_fingerprint", "moe_sched_elems", "moe_mfma_rate",
     "moe_router_bwd", "moe_router_fwd", "moe_sgd_step", "moe_mx_quantize", "moe_mx_dgrad_fc1",
     "moe_bwd_dgrad_dprob_noalloc", "moe_mx_quantize_t", "moe_mx_fwd_fc1", "moe_mx_fwd_fc2", "EXPORTED_SYMBOLS",
-    "moe_mx_wgrad_cols", "moe_mx_quantize_wgrad", "moe_mx_wgrad", "MXW_TOKEN", "MXW_ROW", "MXW_ACT_P",
+    "moe_mx_wgrad_rows", "moe_mx_quantize_wgrad", "moe_mx_wgrad", "MXW_TOKEN", "MXW_ROW", "MXW_ACT_P",
     "moe_route",
 ]
 
@@ -34,7 +34,7 @@ EXPORTED_SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_rows_cap", "moe
                     "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd", "moe_sgd_step",
                     "moe_mx_quantize", "moe_mx_dgrad_fc1", "moe_mx_dgrad_fc2",
                     "moe_nvfp4_quantize", "moe_bwd_dgrad_dprob_noalloc", "moe_mx_quantize_t", "moe_mx_fwd_fc1",
-                    "moe_mx_fwd_fc2", "moe_mx_wgrad_cols", "moe_mx_quantize_wgrad", "moe_mx_wgrad", "moe_route")
+                    "moe_mx_fwd_fc2", "moe_mx_wgrad_rows", "moe_mx_quantize_wgrad", "moe_mx_wgrad", "moe_route")
 # rows read by moe_mx_quantize_wgrad (moe_mxw_src)
 MXW_TOKEN, MXW_ROW, MXW_ACT_P = 0, 1, 2
 
@@ -107,11 +107,11 @@ def load_library() -> ctypes.CDLL:
                                       ctypes.c_uint64, vp]
     lib.moe_mx_fwd_fc1.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_mx_fwd_fc2.argtypes = [P, R, vp, vp, vp, vp, vp, vp, sz, ctypes.c_int, vp]
-    lib.moe_mx_wgrad_cols.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
+    lib.moe_mx_wgrad_rows.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
     lib.moe_route.argtypes = [P, vp, R, vp, sz, ctypes.c_int, vp]
     lib.moe_mx_quantize_wgrad.argtypes = [P, R, vp, ctypes.c_int, vp, vp, vp]
     lib.moe_mx_wgrad.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-    for f in ("moe_route", "moe_mx_wgrad_cols", "moe_mx_quantize_wgrad", "moe_mx_wgrad", "moe_rows_cap", "moe_sched_elems", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob",
+    for f in ("moe_route", "moe_mx_wgrad_rows", "moe_mx_quantize_wgrad", "moe_mx_wgrad", "moe_rows_cap", "moe_sched_elems", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob",
               "moe_bwd_dgrad_dprob_noalloc", "moe_mx_quantize_t", "moe_mx_fwd_fc1", "moe_mx_fwd_fc2",
               "moe_bwd_wgrad", "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd",
               "moe_sgd_step", "moe_mx_quantize", "moe_mx_dgrad_fc1", "moe_mx_dgrad_fc2", "moe_nvfp4_quantize"):
@@ -577,11 +577,11 @@ def moe_mx_fwd_fc2(prob: Problem, routing: Routing, act_mx, w2t_mx, mode: int = 
     return y
 
 
-def moe_mx_wgrad_cols(prob: Problem) -> int:
-    """rpad_cap: columns of the MXFP8 weight-gradient operands (each expert's
-    routed rows padded to a multiple of 64)."""
+def moe_mx_wgrad_rows(prob: Problem) -> int:
+    """rpad_cap: padded rows of the MXFP8 weight-gradient operands (each
+    expert's routed rows padded to a multiple of 64)."""
     v = ctypes.c_int64()
-    _check(load_library().moe_mx_wgrad_cols(ctypes.byref(prob.c()), ctypes.byref(v)), "moe_mx_wgrad_cols")
+    _check(load_library().moe_mx_wgrad_rows(ctypes.byref(prob.c()), ctypes.byref(v)), "moe_mx_wgrad_rows")
     return v.value
 
 
@@ -593,7 +593,7 @@ def moe_mx_quantize_wgrad(prob: Problem, routing: Routing, src: torch.Tensor, ki
     uint8 [rpad_cap / 64, cols, 2]), slice-major; slices past the padded
     total are not written."""
     lib = load_library()
-    rp = moe_mx_wgrad_cols(prob)
+    rp = moe_mx_wgrad_rows(prob)
     cols = prob.d_model if kind == MXW_TOKEN else prob.d_ffn
     rows = prob.tokens if kind == MXW_TOKEN else prob.rows_cap
     _need(src, rows * cols, torch.bfloat16, "moe_mx_quantize_wgrad src")
@@ -614,7 +614,7 @@ def moe_mx_wgrad(prob: Problem, routing: Routing, x_mx, dh_mx, act_mx, dy_mx, dw
     (float32) from the moe_mx_quantize_wgrad encodings of x (MXW_TOKEN), dH
     (MXW_ROW), h (MXW_ACT_P) and dY (MXW_TOKEN)."""
     lib = load_library()
-    rp = moe_mx_wgrad_cols(prob)
+    rp = moe_mx_wgrad_rows(prob)
     D, F, el = prob.d_model, prob.d_ffn, prob.local
     ops = []
     for (c, s), n, name in ((x_mx, D, "x"), (dh_mx, F, "dh"), (act_mx, F, "act"), (dy_mx, D, "dy")):

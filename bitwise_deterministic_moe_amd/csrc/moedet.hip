@@ -1092,7 +1092,7 @@ MOE_API moe_status moe_mx_fwd_fc2(const moe_problem* p, const moe_routing* routi
   return MOE_OK;
 }
 
-MOE_API moe_status moe_mx_wgrad_cols(const moe_problem* p, int64_t* rpad_cap) {
+MOE_API moe_status moe_mx_wgrad_rows(const moe_problem* p, int64_t* rpad_cap) {
   Plan pl;
   moe_status s = validate(p, &pl);
   if (s != MOE_OK) return s;

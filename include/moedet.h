@@ -550,11 +550,11 @@ typedef enum moe_mxw_src {
                         square rounded, then the product; relu(v) = v > 0 ? v : +0), cols = F */
 } moe_mxw_src;
 
-/* Columns of the MXFP8 weight-gradient operands for problem p: rpad_cap =
- * rows_cap + num_local * 63 rounded up to a multiple of 64 (each expert's
- * routed rows padded to a multiple of 64).  Errors: those of the problem's
- * validation, MOE_ERR_NULL. */
-moe_status moe_mx_wgrad_cols(const moe_problem* p, int64_t* rpad_cap);
+/* Padded rows of the MXFP8 weight-gradient operands for problem p:
+ * rpad_cap = rows_cap + num_local * 63 rounded up to a multiple of 64 (each
+ * expert's routed rows padded to a multiple of 64).  Errors: those of the
+ * problem's validation, MOE_ERR_NULL. */
+moe_status moe_mx_wgrad_rows(const moe_problem* p, int64_t* rpad_cap);
 
 /* MXFP8 encoding of a weight-gradient operand, quantised along the routed
  * rows: the contraction axis of dW1_e = X_e^T dH_e and dW2_e = A_e^T dY_e
@@ -588,7 +588,7 @@ moe_status moe_mx_quantize_wgrad(const moe_problem* p, const moe_routing* routin
  * act: MOE_MXW_ACT_P of h, dy: MOE_MXW_TOKEN of dY):
  *   dW1[e] = dequant(x_e) . dequant(dh_e)^T   [D, F] per local expert,
  *   dW2[e] = dequant(act_e) . dequant(dy_e)^T [F, D],
- * over expert e's padded columns.  Each output tile is accumulated in
+ * over expert e's padded rows.  Each output tile is accumulated in
  * float32 by one workgroup over all of the expert's rows in a fixed order
  * (64 rows per scaled MFMA, ascending) and stored once: the result is
  * bitwise reproducible with no reduction step (there is no atomic mode).

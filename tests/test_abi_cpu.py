@@ -268,7 +268,7 @@ def test_mx_wgrad_cols_and_validation_return_before_enqueue(lib):
     p = moe.Problem(**BASE)
     rc, el = moe.moe_rows_cap(p), p.local
     # each expert's rows rounded up to 64: at most rows_cap + 63 per expert
-    assert moe.moe_mx_wgrad_cols(p) == (rc + 63 * el + 63) // 64 * 64
+    assert moe.moe_mx_wgrad_rows(p) == (rc + 63 * el + 63) // 64 * 64
     fake = ctypes.c_void_p(0x1000)
     r = moe._CRouting(*([0x2000] * 9))
     cp = p.c()

@@ -176,7 +176,7 @@ def test_mx_wgrad_bits_identical_under_shuffles_and_poisoned_buffers():
         ops = []
         for op in ("x", "dh", "act", "dy"):
             cols = cfg.d_model if op in ("x", "dy") else cfg.d_ffn
-            rp = moe.moe_mx_wgrad_cols(ps)
+            rp = moe.moe_mx_wgrad_rows(ps)
             c = torch.full((rp // 64, cols, 64), fill, dtype=torch.uint8, device="cuda")
             s = torch.full((rp // 64, cols, 2), fill, dtype=torch.uint8, device="cuda")
             ops.append(moe.moe_mx_quantize_wgrad(ps, case.routing, case.src(op), KINDS[op], c, s))
