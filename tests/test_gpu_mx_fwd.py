@@ -23,7 +23,7 @@ from test_gpu_parity import EDGE
 pytestmark = pytest.mark.gpu
 
 SMALL = ["ragged_bf16", "many_experts_bf16", "rows192_bf16", "single_token_bf16", "no_tokens_bf16",
-         "empty_experts_bf16", "shard_bf16", "bf16_e8k2"]
+         "empty_experts_bf16", "shard_bf16", "max_experts_bf16", "bf16_e8k2"]
 
 
 @pytest.fixture(scope="module", autouse=True)

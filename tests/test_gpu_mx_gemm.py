@@ -35,7 +35,7 @@ def _case(name):
 
 
 @pytest.mark.parametrize("name", ["ragged_bf16", "many_experts_bf16", "rows192_bf16", "single_token_bf16",
-                                  "no_tokens_bf16", "bf16_e8k2"])
+                                  "no_tokens_bf16", "max_experts_bf16", "bf16_e8k2"])
 def test_mx_dgrad_fc1_parity(name):
     print(f"mx dgrad fc1 {name}", flush=True)
     cfg, di, prob, routing, dh_bits, dh = _case(name)
@@ -120,7 +120,7 @@ def _fc2_oracle(cfg, di, h_bits):
 @pytest.mark.parametrize("name,mode", [("ragged_bf16", moe.DETERMINISTIC), ("ragged_bf16", moe.ATOMIC),
                                        ("shard_bf16", moe.DETERMINISTIC), ("empty_experts_bf16", moe.DETERMINISTIC),
                                        ("single_token_bf16", moe.DETERMINISTIC), ("no_tokens_bf16", moe.DETERMINISTIC),
-                                       ("rows192_bf16", moe.ATOMIC),
+                                       ("rows192_bf16", moe.ATOMIC), ("max_experts_bf16", moe.DETERMINISTIC),
                                        ("bf16_e8k2", moe.DETERMINISTIC), ("bf16_e8k2", moe.ATOMIC)])
 def test_mx_dgrad_fc2_parity(name, mode):
     print(f"mx dgrad fc2 {name} mode {mode}", flush=True)
