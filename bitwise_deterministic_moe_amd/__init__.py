@@ -111,7 +111,8 @@ def load_library() -> ctypes.CDLL:
     lib.moe_route.argtypes = [P, vp, R, vp, sz, ctypes.c_int, vp]
     lib.moe_mx_quantize_wgrad.argtypes = [P, R, vp, ctypes.c_int, vp, vp, vp]
     lib.moe_mx_wgrad.argtypes = [P, R, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-    for f in ("moe_route", "moe_mx_wgrad_rows", "moe_mx_quantize_wgrad", "moe_mx_wgrad", "moe_rows_cap", "moe_sched_elems", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob",
+    for f in ("moe_route", "moe_mx_wgrad_rows", "moe_mx_quantize_wgrad", "moe_mx_wgrad", "moe_rows_cap",
+              "moe_sched_elems", "moe_workspace_size", "moe_fwd", "moe_bwd_dgrad_dprob",
               "moe_bwd_dgrad_dprob_noalloc", "moe_mx_quantize_t", "moe_mx_fwd_fc1", "moe_mx_fwd_fc2",
               "moe_bwd_wgrad", "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd",
               "moe_sgd_step", "moe_mx_quantize", "moe_mx_dgrad_fc1", "moe_mx_dgrad_fc2", "moe_nvfp4_quantize"):

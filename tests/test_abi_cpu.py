@@ -264,7 +264,7 @@ def test_mx_forward_validation_returns_before_enqueue(lib):
                               ctypes.c_void_p(0x100000), 16, 0, None) == 4
 
 
-def test_mx_wgrad_cols_and_validation_return_before_enqueue(lib):
+def test_mx_wgrad_rows_and_validation_return_before_enqueue(lib):
     p = moe.Problem(**BASE)
     rc, el = moe.moe_rows_cap(p), p.local
     # each expert's rows rounded up to 64: at most rows_cap + 63 per expert
