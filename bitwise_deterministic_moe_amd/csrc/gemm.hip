@@ -60,11 +60,19 @@ DEV void store4(uint16_t* p, const float (&v)[4]) {
 }
 DEV void store4(float* p, const float (&v)[4]) { *(f32x4_t*)p = f32x4_t{v[0], v[1], v[2], v[3]}; }
 
-// Buffer resource covering [p, p + 2^31): outputs and saved activations are
-// below 2 GiB (validated on the host); offsets >= 2^31 are dropped on store
-// and read as zero on load.
+// Buffer resource covering [p, p + 2^31); offsets >= 2^31 are dropped on
+// store and read as zero on load.  Arrays indexed by routed row can exceed
+// 2 GiB, so their resources start at the first row a tile touches
+// (tile_rows), and offsets within a tile stay far below 2^31.
 DEV __amdgpu_buffer_rsrc_t buf(const void* p) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7fffffff, 0x00020000);
+}
+// Row `row` of a row-major array of `ld` elements of `es` bytes per row.
+DEV const void* row_ptr(const void* p, int64_t row, int64_t ld, int es) {
+  return (const char*)p + row * ld * es;
+}
+DEV __amdgpu_buffer_rsrc_t tile_rows(const void* p, int64_t row0, int64_t ld, int es) {
+  return buf(row_ptr(p, row0, ld, es));
 }
 constexpr uint32_t kNoRow = 0x80000000u;
 // Cache policy of the epilogue's loads and stores: non-temporal.  Each
@@ -417,14 +425,13 @@ struct HPre {
   const RowTile& t;
   int tid;
   DEV void load(Data& d, int p) {
-    const __amdgpu_buffer_rsrc_t rh = buf(P.h);
+    const __amdgpu_buffer_rsrc_t rh = tile_rows(P.h, t.off + t.m0, P.ldh, 2);
 #pragma unroll
     for (int st = 0; st < 16; ++st) {
       const int m = staged_row(p, st, tid);
       const bool ok = m < t.mvalid;
-      const uint32_t grow = (uint32_t)(t.off + t.m0 + (ok ? m : 0));
       d.h[st] = __builtin_amdgcn_raw_buffer_load_b64(
-          rh, ok ? (grow * (uint32_t)P.ldh + t.n0 + staged_col(tid)) * 2u : kNoRow, 0, kEpiNT);
+          rh, ok ? ((uint32_t)m * (uint32_t)P.ldh + t.n0 + staged_col(tid)) * 2u : kNoRow, 0, kEpiNT);
     }
   }
 };
@@ -456,11 +463,10 @@ DEV void dgrad2_epilogue(const RowGemmParams& P, const RowTile& t, uint16_t* lds
   lds_barrier();
   HPre hpre{P, t, tid};
   HPre::Data hd[2];
-  const __amdgpu_buffer_rsrc_t rc = buf(P.c);
+  const __amdgpu_buffer_rsrc_t rc = tile_rows(P.c, t.off + t.m0, P.ldc, 2);
   staged_epilogue<WTM>(stage, acc, wm, wn, lane, tid, t.mvalid, hpre, hd, false, [&](int m, int col, float (&g)[4], HPre::Data& d, int st) {
     const bool valid = m < t.mvalid;   // uniform across the wave (one row per wave)
     if (!valid) return;
-    const int64_t grow = t.off + t.m0 + m;
     const float p2 = 2.f * s_prob[m];
     float hv[4], dh[4];
     hv[0] = bf16_to_f32(d.h[st][0] & 0xffffu);
@@ -474,7 +480,7 @@ DEV void dgrad2_epilogue(const RowGemmParams& P, const RowTile& t, uint16_t* lds
       part = __builtin_fmaf(g[q], rh * rh, part);
       dh[q] = (p2 * g[q]) * rh;
     }
-    const uint32_t o = (uint32_t)grow * 2u * (uint32_t)P.ldc + (t.n0 + col) * 2u;
+    const uint32_t o = (uint32_t)m * 2u * (uint32_t)P.ldc + (t.n0 + col) * 2u;
     __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(dh[0], dh[1]), pack_bf16x2(dh[2], dh[3])}, rc, o, 0, kEpiNT);
     part = quad_sum(part);
     if ((lane & 3) == 0) s_qsum[m * 16 + (lane >> 2)] = part;
@@ -508,11 +514,16 @@ DEV void rowgemm_bf16_tile(const RowGemmParams& P, const RowTile& t, uint16_t* l
   if constexpr (EPI == kEpiDgrad2) my_prob = tid < t.mvalid ? P.row_prob[t.off + t.m0 + tid] : 0.f;
 
   bf::KcOperand oa;
-  // Branch-free so that the four row-index loads of a thread are in flight
-  // together (the tile holds at least one valid row).
-  oa.init(P.a, P.a_bytes, wave, lane, [&](int r) -> uint32_t {
+  // A gathered by token: rows of a[T][lda] (below 2 GiB); else the tile's own
+  // rows, addressed from the first.  Branch-free so that the four row-index
+  // loads of a thread are in flight together (the tile holds at least one
+  // valid row).
+  const bool gathered = P.a_rows != nullptr;
+  const int64_t row0 = t.off + t.m0;
+  oa.init(gathered ? P.a : row_ptr(P.a, row0, P.lda, 2),
+          gathered ? P.a_bytes : (uint32_t)(t.mvalid * P.lda * 2), wave, lane, [&](int r) -> uint32_t {
     const int rc = r < t.mvalid ? r : t.mvalid - 1;
-    const int64_t row = P.a_rows ? (int64_t)P.a_rows[t.off + t.m0 + rc] : t.off + t.m0 + rc;
+    const int64_t row = gathered ? (int64_t)P.a_rows[row0 + rc] : rc;
     return r < t.mvalid ? (uint32_t)(row * P.lda * 2) : bf::kOOB;
   });
   const uint16_t* Bg = (const uint16_t*)P.b + (int64_t)t.g * P.b_gstride;
@@ -558,12 +569,12 @@ DEV void rowgemm_bf16_tile(const RowGemmParams& P, const RowTile& t, uint16_t* l
   if constexpr (EPI == kEpiStore || EPI == kEpiStoreAct) {
     NoPre none;
     NoPre::Data nd[2];
-    const __amdgpu_buffer_rsrc_t rc = buf(P.c), rc2 = buf(P.c2);
+    const __amdgpu_buffer_rsrc_t rc = tile_rows(P.c, row0, P.ldc, 2);
+    const __amdgpu_buffer_rsrc_t rc2 = tile_rows(P.c2, row0, P.ldc2, 2);
     staged_epilogue<WTM>(stage, acc, wm, wn, lane, tid, t.mvalid, none, nd, false, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
       if (m >= t.mvalid) return;  // uniform per wave
-      const uint32_t grow = (uint32_t)(t.off + t.m0 + m);
       __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rc,
-                                            (grow * (uint32_t)P.ldc + t.n0 + col) * 2u, 0, kEpiNT);
+                                            ((uint32_t)m * (uint32_t)P.ldc + t.n0 + col) * 2u, 0, kEpiNT);
       if constexpr (EPI == kEpiStoreAct) {
         // activation of the stored (rounded) h, the value the backward sees
         float a[4];
@@ -573,7 +584,7 @@ DEV void rowgemm_bf16_tile(const RowGemmParams& P, const RowTile& t, uint16_t* l
           a[q] = r * r;
         }
         __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])}, rc2,
-                                              (grow * (uint32_t)P.ldc2 + t.n0 + col) * 2u, 0, kEpiNT);
+                                              ((uint32_t)m * (uint32_t)P.ldc2 + t.n0 + col) * 2u, 0, kEpiNT);
       }
     });
   } else {
@@ -622,9 +633,14 @@ DEV void wgrad_bf16_tile(const WgradParams& P, const WgradTile& t, float* dst, u
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  // The direct operand (rows of dh or act_p, which can exceed 2 GiB) is
+  // addressed from the chunk's first row; the gathered one (x or dy, by
+  // token) from its start.
+  const void* dbase = row_ptr(A_GATHER ? P.b : P.a, t.row0, A_GATHER ? P.ldb : P.lda, 2);
+  const uint32_t dbytes = (uint32_t)t.klen * ld_direct;
   bf::MncOperand oa, ob;
-  oa.init(P.a, P.a_bytes, wave, lane, t.m0);
-  ob.init(P.b, P.b_bytes, wave, lane, t.n0);
+  oa.init(A_GATHER ? P.a : dbase, A_GATHER ? P.a_bytes : dbytes, wave, lane, t.m0);
+  ob.init(A_GATHER ? dbase : P.b, A_GATHER ? dbytes : P.b_bytes, wave, lane, t.n0);
   const int nsteps = (t.klen + bf::BK - 1) / bf::BK;
   // Per load j of a slice, this lane's k row is krow(j) + 32 s.  The direct
   // operand's row offset advances by a scalar per slice; the gathered
@@ -636,7 +652,7 @@ DEV void wgrad_bf16_tile(const WgradParams& P, const WgradTile& t, float* dst, u
 #pragma unroll
   for (int j = 0; j < bf::LOADS; ++j) {
     kr[j] = bf::MncOperand::krow(wave, lane, j);
-    dir[j] = (uint32_t)(t.row0 + kr[j]) * ld_direct;
+    dir[j] = (uint32_t)kr[j] * ld_direct;
   }
   const int last = t.klen > 0 ? t.klen - 1 : 0;
   auto fetch = [&](int s) {
@@ -975,10 +991,15 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
     wa[q] = idx < nw ? ((const uint32_t*)(P.a_scales + arow(ra) * nkb))[c] : 0u;
     wb[q] = idx < nw ? ((const uint32_t*)(P.b_scales + sg + (int64_t)(t.n0 + (idx < nw ? r : 0)) * nkb))[c] : 0u;
   }
+  // codes gathered by token from the start of a[T][lda]; otherwise the
+  // tile's own rows from the first (arrays of routed rows can exceed 2 GiB)
+  const bool gathered = P.a_rows != nullptr;
+  const int64_t row0 = t.off + t.m0;
   bf::KcOperand oa, ob;
-  oa.init(P.a, P.a_bytes, wave, lane, [&](int r) -> uint32_t {   // branch-free, as in the bf16 kernel
+  oa.init(gathered ? P.a : row_ptr(P.a, row0, P.lda, 1), gathered ? P.a_bytes : (uint32_t)(t.mvalid * P.lda), wave,
+          lane, [&](int r) -> uint32_t {   // branch-free, as in the bf16 kernel
     const int64_t row = arow(r < t.mvalid ? r : t.mvalid - 1);
-    return r < t.mvalid ? (uint32_t)(row * P.lda) : bf::kOOB;
+    return r < t.mvalid ? (uint32_t)((gathered ? row : row - row0) * P.lda) : bf::kOOB;
   });
   ob.init((const uint8_t*)P.b + (int64_t)t.g * P.b_gstride, P.b_bytes, wave, lane,
           [&](int r) -> uint32_t { return (uint32_t)((t.n0 + r) * P.ldb); });
@@ -1009,12 +1030,12 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
     float* stage = (float*)lds;
     NoPre none;
     NoPre::Data nd[2];
-    const __amdgpu_buffer_rsrc_t rc = buf(P.c), rc2 = buf(P.c2);
+    const __amdgpu_buffer_rsrc_t rc = tile_rows(P.c, row0, P.ldc, 2);
+    const __amdgpu_buffer_rsrc_t rc2 = tile_rows(P.c2, row0, P.ldc2, 2);
     staged_epilogue<WTM>(stage, acc, wm, wn, lane, tid, t.mvalid, none, nd, false, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
       if (m >= t.mvalid) return;  // uniform per wave
-      const uint32_t grow = (uint32_t)(t.off + t.m0 + m);
       __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])}, rc,
-                                            (grow * (uint32_t)P.ldc + t.n0 + col) * 2u, 0, kEpiNT);
+                                            ((uint32_t)m * (uint32_t)P.ldc + t.n0 + col) * 2u, 0, kEpiNT);
       if constexpr (EPI == kEpiStoreAct) {
         // activation of the stored (rounded) h, as in the bf16 forward
         float a[4];
@@ -1024,7 +1045,7 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
           a[q] = r * r;
         }
         __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])}, rc2,
-                                              (grow * (uint32_t)P.ldc2 + t.n0 + col) * 2u, 0, kEpiNT);
+                                              ((uint32_t)m * (uint32_t)P.ldc2 + t.n0 + col) * 2u, 0, kEpiNT);
       }
     });
   }
@@ -1063,16 +1084,19 @@ __global__ __launch_bounds__(256) void mx_wgrad_kernel(MxWgradParams P) {
   const uint8_t* bs = pick(mat, P.dy_scales, P.dh_scales);
   float* dst = pick(mat, P.dw2, P.dw1) + (int64_t)g * P.D * P.F;
   const int p0 = P.poff[g], nsl = (P.poff[g + 1] - p0) / 64;
-  // slice-major codes: slice j of operand rows R at byte (j R + row) 64
+  // slice-major codes: slice j of operand rows R at byte (j R + row) 64,
+  // addressed from the expert's first slice (the encodings of all routed
+  // rows can exceed 2 GiB; one expert's slices stay far below)
+  const int64_t j0 = p0 / 64;
   bf::KcOperand oa, ob;
-  oa.init(ac, (uint32_t)(M * P.rpad), wave, lane,
-          [&](int r) -> uint32_t { return (uint32_t)(((int64_t)(p0 / 64) * M + m0 + r) * 64); });
-  ob.init(bc, (uint32_t)(N * P.rpad), wave, lane,
-          [&](int r) -> uint32_t { return (uint32_t)(((int64_t)(p0 / 64) * N + n0 + r) * 64); });
+  oa.init(ac + j0 * M * 64, (uint32_t)(nsl * M * 64), wave, lane,
+          [&](int r) -> uint32_t { return (uint32_t)((m0 + r) * 64); });
+  ob.init(bc + j0 * N * 64, (uint32_t)(nsl * N * 64), wave, lane,
+          [&](int r) -> uint32_t { return (uint32_t)((n0 + r) * 64); });
   // slice-major scales: slice j of operand rows R at byte (j R + row) 2
   MxRingScales rsc;
-  rsc.init(wave, lane, as, (uint32_t)(M * P.rpad / 32), (uint32_t)(((int64_t)(p0 / 64) * M + m0) * 2), (uint32_t)(2 * M),
-           bs, (uint32_t)(N * P.rpad / 32), (uint32_t)(((int64_t)(p0 / 64) * N + n0) * 2), (uint32_t)(2 * N));
+  rsc.init(wave, lane, as + j0 * M * 2, (uint32_t)(nsl * M * 2), (uint32_t)(m0 * 2), (uint32_t)(2 * M),
+           bs + j0 * N * 2, (uint32_t)(nsl * N * 2), (uint32_t)(n0 * 2), (uint32_t)(2 * N));
   f32x16_t acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -1233,14 +1257,15 @@ __global__ __launch_bounds__(256) void wgrad_prep_kernel(WgradPrepParams P) {
   }
   const int64_t gtid = (int64_t)blockIdx.x * 256 + threadIdx.x, gstride = (int64_t)gridDim.x * 256;
   for (int64_t i = gtid; i < P.n_tickets; i += gstride) P.tickets[i] = 0;
-  // R * N elements of the storage type are below 2^31 bytes (validated on
-  // the host), so 32-bit indices suffice
+  // R * N elements of the storage type are below 2^35 bytes (validated on
+  // the host), so the number of 16-byte vectors fits 32 bits; element
+  // offsets are 64-bit
   constexpr int V = 16 / sizeof(T);
   const int per_row = P.N / V;
   const int nvec = P.offsets[G] * per_row;
   for (int v = (int)gtid; v < nvec; v += (int)gstride) {
     const int r = v / per_row;
-    const int e0 = v * V;
+    const int64_t e0 = (int64_t)v * V;
     const float p = P.row_prob[r];
     float hv[V], a[V];
     if constexpr (sizeof(T) == 2) {

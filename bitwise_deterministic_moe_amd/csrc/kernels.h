@@ -27,7 +27,8 @@ struct RowGemmParams {
   int N, K;
   const void* a;
   int64_t lda;
-  uint32_t a_bytes;       // extent of a (buffer range check)
+  uint32_t a_bytes;       // extent of a when gathered by a_rows (buffer range check);
+                          // unread otherwise: a tile's own rows are addressed from its first
   const int32_t* a_rows;  // A row r reads a[a_rows[r]] when set, a[r] otherwise
   const void* b;
   int64_t b_gstride;      // elements between consecutive experts' B
@@ -120,6 +121,9 @@ struct WgradParams {
   const int32_t* sched;  // unit_start[G+1], slot_base[G+1]
   int groups;
   int M, N;
+  // the operand gathered by token (x or dy) has an extent (a_bytes or
+  // b_bytes, below 2 GiB); the routed-row one (dh or act_p) is addressed
+  // from each chunk's first row and its extent field is unread
   const void* a;
   int64_t lda;
   uint32_t a_bytes;

@@ -63,11 +63,14 @@ moe_status validate(const moe_problem* p, Plan* pl) {
   if (p->d_ffn / bn > 64) return MOE_ERR_SHAPE;  // dprob partials per row
   if ((int64_t)p->d_model * p->d_ffn >= (int64_t)1 << 31) return MOE_ERR_SHAPE;
   {
-    // every operand is addressed with 32-bit buffer offsets below 2^31
+    // Token arrays ([T, D]: x, dy, y, dx) are gathered through 32-bit buffer
+    // offsets and stay below 2 GiB; arrays of routed rows ([rows_cap,
+    // max(D, F)]) are addressed from each tile's first row and may reach
+    // 32 GiB (so the act_p prologue's 16-byte vectors number below 2^31).
     const int64_t es = bf16 ? 2 : 4;
     const int64_t rc = p->tokens * (int64_t)(p->top_k < p->num_local ? p->top_k : p->num_local);
     const int64_t wmax = p->d_model > p->d_ffn ? p->d_model : p->d_ffn;
-    if (p->tokens * p->d_model * es >= ((int64_t)1 << 31) || rc * wmax * es >= ((int64_t)1 << 31))
+    if (p->tokens * p->d_model * es >= ((int64_t)1 << 31) || rc * wmax * es >= ((int64_t)1 << 35))
       return MOE_ERR_SHAPE;
   }
   if (p->n_stage_events < 0 || (p->n_stage_events > 0 && !p->stage_events)) return MOE_ERR_NULL;
@@ -450,7 +453,7 @@ MOE_API moe_status moe_fwd(const moe_problem* p, const float* logits, const void
   G.K = pl.F;
   G.a = arows;
   G.lda = pl.F;
-  G.a_bytes = (uint32_t)(pl.rows_cap * pl.F * pl.esize);
+  G.a_bytes = 0;  // rows of the tile, addressed from its first
   G.a_rows = nullptr;
   G.b = w2;
   G.b_gstride = (int64_t)pl.F * pl.D;
@@ -631,7 +634,7 @@ moe_status dgrad_enqueue(const moe_problem* p, const Plan& pl, const moe_routing
   G2.K = pl.F;
   G2.a = dh;
   G2.lda = pl.F;
-  G2.a_bytes = (uint32_t)(pl.rows_cap * pl.F * pl.esize);
+  G2.a_bytes = 0;  // rows of the tile, addressed from its first
   G2.a_rows = nullptr;
   G2.b = w1;
   G2.b_gstride = (int64_t)pl.D * pl.F;
@@ -728,7 +731,7 @@ MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routin
   W1.kc = pl.kc;
   W1.atomic = at;
   W1.seed = seed;
-  const uint32_t rows_f_bytes = (uint32_t)(pl.rows_cap * pl.F * pl.esize);
+  const uint32_t rows_f_bytes = 0;  // routed-row operands: addressed per chunk in the kernel
   const uint32_t tok_d_bytes = (uint32_t)(pl.T * pl.D * pl.esize);
   WgradParams W2 = W1;
   // dW1_g [D][F] = x[row_tok]^T dh
@@ -888,7 +891,7 @@ MOE_API moe_status moe_mx_dgrad_fc1(const moe_problem* p, const moe_routing* rou
   G.K = pl.F;
   G.a = dh_codes;
   G.lda = pl.F;  // bytes per row of codes
-  G.a_bytes = (uint32_t)(pl.rows_cap * pl.F);
+  G.a_bytes = 0;  // rows of the tile, addressed from its first
   G.b = w1_codes;
   G.b_gstride = (int64_t)pl.D * pl.F;
   G.ldb = pl.F;
@@ -1064,7 +1067,7 @@ MOE_API moe_status moe_mx_fwd_fc2(const moe_problem* p, const moe_routing* routi
   G.K = pl.F;
   G.a = act_codes;
   G.lda = pl.F;
-  G.a_bytes = (uint32_t)(pl.rows_cap * pl.F);
+  G.a_bytes = 0;  // rows of the tile, addressed from its first
   G.a_scales = act_scales;
   G.b = w2t_codes;
   G.b_gstride = (int64_t)pl.D * pl.F;
@@ -1101,9 +1104,9 @@ MOE_API moe_status moe_mx_wgrad_rows(const moe_problem* p, int64_t* rpad_cap) {
   return MOE_OK;
 }
 
-static bool mx_wgrad_fits(const Plan& pl) {
-  return (int64_t)(pl.D > pl.F ? pl.D : pl.F) * pl.rpad_cap < ((int64_t)1 << 31);
-}
+// Padded rows are indexed with 32-bit integers; byte offsets into the
+// encodings are 64-bit or taken from an expert's first slice.
+static bool mx_wgrad_fits(const Plan& pl) { return pl.rpad_cap < ((int64_t)1 << 31); }
 
 MOE_API moe_status moe_mx_quantize_wgrad(const moe_problem* p, const moe_routing* routing, const void* src,
                                          moe_mxw_src kind, uint8_t* codes, uint8_t* scales, void* stream) {

@@ -94,7 +94,8 @@ typedef enum moe_mode { MOE_DETERMINISTIC = 0, MOE_ATOMIC = 1 } moe_mode;
  *   expert_begin, num_local
  *                 the experts held here: [expert_begin, expert_begin+num_local)
  *   dtype         MOE_F32 (D, F multiples of 64) or MOE_BF16 (multiples of 256);
- *                 every [T,D] and [rows_cap,max(D,F)] array below 2 GiB
+ *                 every [T,D] array below 2 GiB (T < 512K tokens at a bf16
+ *                 D of 2048) and every [rows_cap,max(D,F)] array below 32 GiB
  *   combine       1: full layer, outputs in token layout ([T,D]; requires
  *                 num_local == num_experts);
  *                 0: expert shard, outputs in row layout ([rows_cap,D]) as an
@@ -576,7 +577,7 @@ moe_status moe_mx_wgrad_rows(const moe_problem* p, int64_t* rpad_cap);
  *   codes          DEVICE uint8 [rpad_cap / 64, cols, 64], 16-byte aligned
  *   scales         DEVICE uint8 [rpad_cap / 64, cols, 2]
  * Slices from poff[num_local] / 64 on are not written.  routing: as written by
- * moe_fwd.  The problem must be bf16 with max(D, F) * rpad_cap < 2^31.
+ * moe_fwd.  The problem must be bf16.
  * Deterministic: every byte depends on the inputs only.  Errors:
  * MOE_ERR_DTYPE, MOE_ERR_SHAPE (sizes, alignment, kind), MOE_ERR_NULL before
  * anything is enqueued; MOE_ERR_HIP for a launch failure. */
@@ -596,7 +597,7 @@ moe_status moe_mx_quantize_wgrad(const moe_problem* p, const moe_routing* routin
  *   *_codes        DEVICE uint8 [rpad_cap / 64, D or F, 64], 16-byte aligned
  *   *_scales       DEVICE uint8 [rpad_cap / 64, D or F, 2], 16-byte aligned
  *   dw1, dw2       DEVICE float32 [num_local, D, F] / [num_local, F, D]
- * The problem must be bf16 with max(D, F) * rpad_cap < 2^31.  Errors:
+ * The problem must be bf16.  Errors:
  * MOE_ERR_DTYPE, MOE_ERR_SHAPE, MOE_ERR_NULL before anything is enqueued;
  * MOE_ERR_HIP for a launch failure. */
 moe_status moe_mx_wgrad(const moe_problem* p, const moe_routing* routing, const uint8_t* x_codes,

@@ -48,11 +48,22 @@ BASE = dict(tokens=4096, d_model=1024, d_ffn=2048, num_experts=8, top_k=2)
     dict(top_k=0), dict(top_k=9), dict(num_experts=2000, top_k=2), dict(d_model=1000), dict(d_ffn=64),
     dict(tokens=-1), dict(expert_begin=7, num_local=2, combine=0), dict(num_local=4),  # combine=1 needs all experts
     dict(d_ffn=256 * 65), dict(top_k=65, num_experts=100),
+    # token arrays [T, D] of 2 GiB; routed-row arrays [rows_cap, max(D, F)] of 32 GiB
+    dict(tokens=1 << 20, d_model=1024), dict(tokens=1 << 19, d_model=256, d_ffn=4096, top_k=8),
 ])
 def test_shape_validation(bad):
     p = moe.Problem(**{**BASE, **bad})
     with pytest.raises(moe.MoeError, match="status 2"):
         moe.moe_workspace_size(p)
+
+
+def test_routed_row_arrays_beyond_2gib_are_accepted():
+    # 65536 tokens top-8 of 8 experts at d_ffn 4096: h, dh and act_p are 4 GiB
+    # each, addressed from each tile's first row
+    p = moe.Problem(**{**BASE, "tokens": 1 << 16, "d_ffn": 4096, "top_k": 8})
+    assert moe.moe_rows_cap(p) * 4096 * 2 == 4 << 30
+    fwd, dgrad, wgrad = moe.moe_workspace_size(p)
+    assert wgrad >= 4 << 30 and dgrad > 0 and fwd >= 4 << 30
 
 
 def test_dtype_and_mode_validation(lib):
@@ -282,8 +293,8 @@ def test_mx_wgrad_rows_and_validation_return_before_enqueue(lib):
     assert lib.moe_mx_quantize_wgrad(ctypes.byref(cp), ctypes.byref(no_tok), fake, 0, fake, fake, None) == 1
     assert lib.moe_mx_quantize_wgrad(ctypes.byref(cp), ctypes.byref(r), fake, 1, ctypes.c_void_p(0x1008), fake,
                                      None) == 2
-    # operands beyond 32-bit buffer offsets: max(D, F) * rpad_cap >= 2^31
-    huge = moe.Problem(**{**BASE, "tokens": 1 << 20, "d_ffn": 4096}).c()
+    # routed-row arrays of 32 GiB and more are rejected by every call
+    huge = moe.Problem(**{**BASE, "tokens": 1 << 19, "d_model": 256, "d_ffn": 4096, "top_k": 8}).c()
     assert lib.moe_mx_quantize_wgrad(ctypes.byref(huge), ctypes.byref(r), fake, 1, fake, fake, None) == 2
     ops = [fake] * 8
     assert lib.moe_mx_wgrad(ctypes.byref(f32), ctypes.byref(r), *ops, fake, fake, None) == 3

@@ -185,6 +185,37 @@ def test_large_full_parity_and_determinism(name):
     print(f"[{name}] {n} runs bit-identical to the first", flush=True)
 
 
+def test_routed_rows_beyond_2gib():
+    """A layer whose arrays of routed rows exceed 2 GiB (80000 tokens top-2 of
+    8 experts at d_ffn 8192: h, dh and act_p are 2.6 GB each), so that rows
+    past the first 2 GiB are reached only through the tiles' own base
+    addresses: every routed row, every dW element (each expert's 20000 rows
+    split into ordered K chunks) and every token against the oracle, then
+    bit identity over repeats and shuffled launch orders."""
+    from synth import Config
+    cfg = Config("rows_2gib_e8k2", 80000, 256, 8192, 8, 2, 0, 8, "bf16", 1, 31)
+    prob = moe.Problem.from_config(cfg)
+    assert prob.rows_cap * cfg.d_ffn * 2 > (2 << 30)
+    print("[rows > 2 GiB] drawing inputs", flush=True)
+    host = make_inputs(cfg)
+    di = DeviceInputs(cfg, host)
+    runner = LayerRunner(prob, di)
+    out = runner.run(0)
+    idx, p = oracle.route(host["logits"], cfg.top_k)
+    perm = oracle.permute(idx, cfg.expert_begin, cfg.num_local)
+    compare_routing(out["routing"], dict(topk_idx=idx, topk_prob=p, perm=perm))
+    assert int(perm["offsets"][-1]) == cfg.tokens * cfg.top_k
+    # the last expert's rows start past 2 GiB of h
+    assert int(perm["offsets"][-2]) * cfg.d_ffn * 2 > (2 << 30)
+    print("[rows > 2 GiB] oracle over all experts", flush=True)
+    errs = _stream_check(cfg, host, perm, p, out)
+    errs.update(_euler(cfg, di, out, out["routing"]))
+    print(f"[rows > 2 GiB] errors {errs}", flush=True)
+    assert errs["euler_w1"] <= 2e-2 and errs["euler_w2"] <= 2e-2 and errs["euler_x"] <= 2e-2, errs
+    n = determinism_runs(runner, cfg.combine, repeats=4, label="rows > 2 GiB")
+    print(f"[rows > 2 GiB] {n} runs bit-identical to the first", flush=True)
+
+
 def test_large_mx_data_gradients_streamed():
     """The MXFP8 data gradients at LatentMoE size (512 experts, 2 GiB of W1
     codes): every routed row of every expert against the oracle on its own
