@@ -1104,9 +1104,14 @@ MOE_API moe_status moe_mx_wgrad_rows(const moe_problem* p, int64_t* rpad_cap) {
   return MOE_OK;
 }
 
-// Padded rows are indexed with 32-bit integers; byte offsets into the
-// encodings are 64-bit or taken from an expert's first slice.
-static bool mx_wgrad_fits(const Plan& pl) { return pl.rpad_cap < ((int64_t)1 << 31); }
+// Padded rows are indexed with 32-bit integers, and the GEMM addresses an
+// expert's encodings from its first slice with 32-bit offsets: an expert
+// holds at most T rows, so (T rounded up to 64) x max(D, F) bytes must stay
+// below 2^31.
+static bool mx_wgrad_fits(const Plan& pl) {
+  const int64_t rows_e = (pl.T + kMxPad - 1) / kMxPad * kMxPad;
+  return pl.rpad_cap < ((int64_t)1 << 31) && rows_e * (pl.D > pl.F ? pl.D : pl.F) < ((int64_t)1 << 31);
+}
 
 MOE_API moe_status moe_mx_quantize_wgrad(const moe_problem* p, const moe_routing* routing, const void* src,
                                          moe_mxw_src kind, uint8_t* codes, uint8_t* scales, void* stream) {

@@ -577,7 +577,8 @@ moe_status moe_mx_wgrad_rows(const moe_problem* p, int64_t* rpad_cap);
  *   codes          DEVICE uint8 [rpad_cap / 64, cols, 64], 16-byte aligned
  *   scales         DEVICE uint8 [rpad_cap / 64, cols, 2]
  * Slices from poff[num_local] / 64 on are not written.  routing: as written by
- * moe_fwd.  The problem must be bf16.
+ * moe_fwd.  The problem must be bf16 with max(D, F) * (T rounded up to 64)
+ * < 2^31 (one expert's encodings, which can hold every token).
  * Deterministic: every byte depends on the inputs only.  Errors:
  * MOE_ERR_DTYPE, MOE_ERR_SHAPE (sizes, alignment, kind), MOE_ERR_NULL before
  * anything is enqueued; MOE_ERR_HIP for a launch failure. */
@@ -597,7 +598,8 @@ moe_status moe_mx_quantize_wgrad(const moe_problem* p, const moe_routing* routin
  *   *_codes        DEVICE uint8 [rpad_cap / 64, D or F, 64], 16-byte aligned
  *   *_scales       DEVICE uint8 [rpad_cap / 64, D or F, 2], 16-byte aligned
  *   dw1, dw2       DEVICE float32 [num_local, D, F] / [num_local, F, D]
- * The problem must be bf16.  Errors:
+ * The problem must be bf16 with max(D, F) * (T rounded up to 64) < 2^31.
+ * Errors:
  * MOE_ERR_DTYPE, MOE_ERR_SHAPE, MOE_ERR_NULL before anything is enqueued;
  * MOE_ERR_HIP for a launch failure. */
 moe_status moe_mx_wgrad(const moe_problem* p, const moe_routing* routing, const uint8_t* x_codes,

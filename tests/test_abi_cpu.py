@@ -299,6 +299,11 @@ def test_mx_wgrad_rows_and_validation_return_before_enqueue(lib):
     ops = [fake] * 8
     assert lib.moe_mx_wgrad(ctypes.byref(f32), ctypes.byref(r), *ops, fake, fake, None) == 3
     assert lib.moe_mx_wgrad(ctypes.byref(huge), ctypes.byref(r), *ops, fake, fake, None) == 2
+    # a valid layer whose single expert could hold T rows of 2^31 encoded bytes
+    wide = moe.Problem(**{**BASE, "tokens": 1 << 18, "d_model": 256, "d_ffn": 8192}).c()
+    moe.moe_workspace_size(moe.Problem(**{**BASE, "tokens": 1 << 18, "d_model": 256, "d_ffn": 8192}))
+    assert lib.moe_mx_quantize_wgrad(ctypes.byref(wide), ctypes.byref(r), fake, 1, fake, fake, None) == 2
+    assert lib.moe_mx_wgrad(ctypes.byref(wide), ctypes.byref(r), *ops, fake, fake, None) == 2
     assert lib.moe_mx_wgrad(ctypes.byref(cp), ctypes.byref(r), *ops, None, fake, None) == 1
     assert lib.moe_mx_wgrad(ctypes.byref(cp), ctypes.byref(r), *([fake] * 7 + [None]), fake, fake, None) == 1
     # scales must be 16-byte aligned (they are streamed with 16-byte loads)
