@@ -1086,7 +1086,8 @@ __global__ __launch_bounds__(256) void mx_wgrad_kernel(MxWgradParams P) {
   const int p0 = P.poff[g], nsl = (P.poff[g + 1] - p0) / 64;
   // slice-major codes: slice j of operand rows R at byte (j R + row) 64,
   // addressed from the expert's first slice (the encodings of all routed
-  // rows can exceed 2 GiB; one expert's slices stay far below)
+  // rows can exceed 2 GiB; one expert's, at most T rows, stay below 2^31
+  // bytes, which the host checks)
   const int64_t j0 = p0 / 64;
   bf::KcOperand oa, ob;
   oa.init(ac + j0 * M * 64, (uint32_t)(nsl * M * 64), wave, lane,
