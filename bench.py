@@ -394,6 +394,7 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic",
+        "library_source_hash": moe.moe_source_hash(),
         "config": {"workload": workload_desc(cfg, R), "tokens": cfg.tokens, "d_model": cfg.d_model,
                    "d_ffn": cfg.d_ffn, "experts": cfg.num_experts, "top_k": cfg.top_k, "local_experts": cfg.num_local,
                    "routed_rows": R, "mode": "deterministic", "parallelism": "single GPU"},
@@ -758,16 +759,12 @@ def measured_mx_wgrad(cfg, wl, dh, bf16_ms, reps=10):
 def measured_traffic(workload, stage):
     """HBM bytes per launch of `stage` from profiles/<workload>_hbm_traffic.txt
     (rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by a plain-copy calibration), or
-    None when the library source changed since those counters were taken."""
-    import glob
-    import hashlib
+    None when the running library was built from other sources than the
+    profiled one."""
+    import bitwise_deterministic_moe_amd as moe
     path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
-    m = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "bitwise_deterministic_moe_amd", "csrc", "*"))):
-        m.update(os.path.basename(f).encode())
-        m.update(open(f, "rb").read())
     fields = {}
     for line in open(path):
         parts = line.split()
@@ -777,7 +774,7 @@ def measured_traffic(workload, stage):
             fields[("stage", parts[1])] = float(parts[7])
         elif len(parts) == 2:
             fields[parts[0]] = parts[1]
-    if fields.get("csrc_sha256") != m.hexdigest()[:16]:
+    if fields.get("source_hash") != moe.moe_source_hash():
         return None
     return fields.get(("stage", stage))
 

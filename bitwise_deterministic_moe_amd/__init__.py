@@ -34,7 +34,8 @@ EXPORTED_SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_rows_cap", "moe
                     "moe_fingerprint", "moe_mfma_rate", "moe_router_bwd", "moe_router_fwd", "moe_sgd_step",
                     "moe_mx_quantize", "moe_mx_dgrad_fc1", "moe_mx_dgrad_fc2",
                     "moe_nvfp4_quantize", "moe_bwd_dgrad_dprob_noalloc", "moe_mx_quantize_t", "moe_mx_fwd_fc1",
-                    "moe_mx_fwd_fc2", "moe_mx_wgrad_rows", "moe_mx_quantize_wgrad", "moe_mx_wgrad", "moe_route")
+                    "moe_mx_fwd_fc2", "moe_mx_wgrad_rows", "moe_mx_quantize_wgrad", "moe_mx_wgrad", "moe_route",
+                    "moe_source_hash")
 # rows read by moe_mx_quantize_wgrad (moe_mxw_src)
 MXW_TOKEN, MXW_ROW, MXW_ACT_P = 0, 1, 2
 
@@ -48,6 +49,10 @@ class MoeError(RuntimeError):
 
 class MoeLibraryMissing(MoeError):
     pass
+
+
+class MoeLibraryStale(MoeError):
+    """The in-tree libmoedet.so was built from other sources than the tree's."""
 
 
 class _CProblem(ctypes.Structure):
@@ -81,6 +86,15 @@ def load_library() -> ctypes.CDLL:
     P = ctypes.POINTER(_CProblem)
     R = ctypes.POINTER(_CRouting)
     lib.moe_abi_version.restype = ctypes.c_int
+    lib.moe_source_hash.restype = ctypes.c_char_p
+    lib.moe_source_hash.argtypes = []
+    if "MOEDET_LIB" not in os.environ and os.path.isdir(os.path.join(_HERE, "csrc")):
+        # the in-tree library must have been built from the tree's sources
+        from .build import source_hash
+        built, tree = lib.moe_source_hash().decode(), source_hash()
+        if built != tree:
+            raise MoeLibraryStale(f"{path} was built from sources {built}, the tree holds {tree}; rebuild it with "
+                                  "python -m bitwise_deterministic_moe_amd.build")
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_rows_cap.argtypes = [P, ctypes.POINTER(ctypes.c_int64)]
@@ -119,6 +133,11 @@ def load_library() -> ctypes.CDLL:
         getattr(lib, f).restype = ctypes.c_int
     _LIB = lib
     return lib
+
+
+def moe_source_hash() -> str:
+    """Hash of the sources the loaded library was built from."""
+    return load_library().moe_source_hash().decode()
 
 
 def _check(status: int, what: str):

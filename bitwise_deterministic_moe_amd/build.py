@@ -2,12 +2,15 @@
 
     python -m bitwise_deterministic_moe_amd.build
 """
+import glob
+import hashlib
 import os
 import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+HEADER = os.path.join(HERE, "..", "include", "moedet.h")
 LIB = os.path.join(HERE, "libmoedet.so")
 SOURCES = ["moedet.hip", "route.hip", "gemm.hip", "combine.hip", "fingerprint.hip", "mfma_rate.hip", "router.hip", "train.hip", "mx.hip", "nvfp4.hip"]
 
@@ -30,6 +33,18 @@ FLAGS = [
 ]
 
 
+def source_hash() -> str:
+    """First 16 hex digits of SHA-256 over the library's sources (every file
+    of csrc/ in name order, each name then its bytes, then the C header),
+    compiled into the library as moe_source_hash()."""
+    m = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))) + [HEADER]:
+        m.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            m.update(fh.read())
+    return m.hexdigest()[:16]
+
+
 def _scratch_kernels(stderr: str) -> list:
     """Kernels whose resource report shows per-lane scratch (register spills
     or stack), from the compiler's kernel-resource-usage remarks."""
@@ -47,7 +62,8 @@ def _scratch_kernels(stderr: str) -> list:
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp"
-    cmd = [hipcc] + FLAGS + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+    cmd = ([hipcc] + FLAGS + [f'-DMOEDET_SOURCE_HASH="{source_hash()}"'] + [os.path.join(CSRC, s) for s in SOURCES]
+           + ["-o", tmp])
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

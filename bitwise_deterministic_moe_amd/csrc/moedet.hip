@@ -251,6 +251,11 @@ using namespace moedet;
 
 MOE_API int moe_abi_version(void) { return MOE_ABI_VERSION; }
 
+#ifndef MOEDET_SOURCE_HASH
+#define MOEDET_SOURCE_HASH "unknown"
+#endif
+MOE_API const char* moe_source_hash(void) { return MOEDET_SOURCE_HASH; }
+
 MOE_API const char* moe_status_string(moe_status s) {
   switch (s) {
     case MOE_OK: return "ok";

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -161,6 +161,12 @@ typedef struct moe_routing {
 
 /* ABI version (MOE_ABI_VERSION of the build). */
 int moe_abi_version(void);
+
+/* Hash of the sources the library was built from (16 hex digits of
+ * SHA-256 over the csrc files and this header, as computed by the build
+ * script), or "unknown" for a build that did not supply it.  Static string,
+ * owned by the library. */
+const char* moe_source_hash(void);
 
 /* Static description of a status code. */
 const char* moe_status_string(moe_status s);

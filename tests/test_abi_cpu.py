@@ -33,7 +33,15 @@ def test_every_declared_symbol_is_exported(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert names == set(moe.EXPORTED_SYMBOLS)
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
+
+
+def test_library_is_built_from_the_tree(lib):
+    # the loader refuses an in-tree library built from other sources; the
+    # hash it carries is the build script's hash of the tree
+    from bitwise_deterministic_moe_amd.build import source_hash
+    assert len(source_hash()) == 16
+    assert moe.moe_source_hash() == source_hash()
 
 
 def test_status_strings(lib):
