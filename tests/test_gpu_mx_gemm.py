@@ -57,6 +57,41 @@ def test_mx_dgrad_fc1_parity(name):
     assert err <= 2e-2
 
 
+def test_mx_dgrad_fc1_codes_beyond_2gib():
+    """dh codes past 2 GiB (600000 tokens top-2 of 64 experts at d_ffn
+    2048: 2.5 GB of codes, read from each tile's first row): the first
+    expert's and the last two experts' dx rows against the oracle.  dh rows
+    repeat one seeded 4096-row block."""
+    from synth import Config
+    cfg = Config("mx_fc1_2gib_e64k2", 600000, 256, 2048, 64, 2, 0, 64, "bf16", 1, 36)
+    di = device_inputs(cfg)
+    prob = moe.Problem.from_config(cfg)
+    routing = moe.moe_route(prob, di.logits)
+    D, F, el, rc = cfg.d_model, cfg.d_ffn, cfg.num_local, prob.rows_cap
+    rng = np.random.default_rng([cfg.seed, 77])
+    reps = (rc + 4095) // 4096
+    dh_bits = np.tile(f32_to_bf16_bits((rng.standard_normal((4096, F)) * 0.01).astype(np.float32)), (reps, 1))[:rc]
+    dh = torch.from_numpy(dh_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    dmx = moe.moe_mx_quantize(dh)
+    wmx = moe.moe_mx_quantize(di.w1.reshape(el * D, F))
+    wmx = (wmx[0].reshape(el, D, F), wmx[1].reshape(el, D, F // 32))
+    out = moe.moe_mx_dgrad_fc1(prob, routing, dmx, wmx)
+    torch.cuda.synchronize()
+    idx, _ = oracle.route(di.host["logits"], cfg.top_k)
+    perm = oracle.permute(idx, cfg.expert_begin, el)
+    off = perm["offsets"]
+    assert int(off[-2]) * F > (2 << 30)
+    w1 = oracle.decode(di.host["w1"], "bf16")
+    for e in (0, el - 2, el - 1):
+        lo, hi = int(off[e]), int(off[e + 1])
+        ac, asc = oracle.mx_quantize_fast(bf16_bits_to_f32(dh_bits[lo:hi]).astype(np.float64))
+        bc, bsc = oracle.mx_quantize_fast(w1[e])
+        ref = oracle.mx_grouped_rows(ac, asc, bc[None], bsc[None], np.array([0, hi - lo]))
+        err = rel_l2(to_host(out[lo:hi]), ref)
+        print(f"  expert {e} rows {lo}..{hi} rel-L2 {err:.3e}", flush=True)
+        assert err <= 2e-2
+
+
 def test_mx_dgrad_fc1_bits_identical_under_shuffles():
     cfg, di, prob, routing, dh_bits, dh = _case("bf16_e8k2")
     D, F, el = cfg.d_model, cfg.d_ffn, cfg.num_local

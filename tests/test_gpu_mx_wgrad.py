@@ -191,6 +191,57 @@ def test_mx_wgrad_bits_identical_under_shuffles_and_poisoned_buffers():
         assert fps == ref, seed
 
 
+def test_mx_wgrad_encodings_beyond_2gib():
+    """Encodings of routed rows past 2 GiB (160000 tokens top-2 of 64 experts
+    at d_ffn 8192: the dh and act codes are 2.6 GB each): the quantiser's
+    bytes and dW1 / dW2 of the first expert and of the last two, whose
+    slices start past 2 GiB, against the oracle.  h and dh rows repeat one
+    seeded 4096-row block (both sides read the same rows)."""
+    cfg = Config("mx_2gib_e64k2", 160000, 256, 8192, 64, 2, 0, 64, "bf16", 1, 35)
+    prob = moe.Problem.from_config(cfg)
+    di = device_inputs(cfg)
+    routing = moe.moe_route(prob, di.logits)
+    rc, F = prob.rows_cap, cfg.d_ffn
+    rng = np.random.default_rng([cfg.seed, 85])
+    reps = (rc + 4095) // 4096
+    h_bits = np.tile(f32_to_bf16_bits((rng.standard_normal((4096, F)) * 0.5).astype(np.float32)), (reps, 1))[:rc]
+    dh_bits = np.tile(f32_to_bf16_bits((rng.standard_normal((4096, F)) * 0.01).astype(np.float32)), (reps, 1))[:rc]
+    p = rng.uniform(0.02, 1.0, rc).astype(np.float32)
+    routing.row_prob.copy_(torch.from_numpy(p).cuda())
+    h, dh = _bits_dev(h_bits), _bits_dev(dh_bits)
+    print("[mx > 2 GiB] HIP path", flush=True)
+    ops = {op: moe.moe_mx_quantize_wgrad(prob, routing, {"x": di.x, "dy": di.dy, "dh": dh, "act": h}[op], KINDS[op])
+           for op in ("x", "dh", "act", "dy")}
+    dw1, dw2 = moe.moe_mx_wgrad(prob, routing, ops["x"], ops["dh"], ops["act"], ops["dy"])
+    torch.cuda.synchronize()
+    idx, _ = oracle.route(di.host["logits"], cfg.top_k)
+    perm = oracle.permute(idx, cfg.expert_begin, cfg.num_local)
+    off = perm["offsets"].astype(np.int64)
+    poff = oracle.mx_pad_offsets(perm["counts"].astype(np.int64))
+    assert int(poff[-1]) * F > (2 << 30) and int(poff[-2]) * F > (2 << 30)
+
+    def values(op, lo, hi):
+        tok = perm["row_tok"][lo:hi]
+        if op in ("x", "dy"):
+            return oracle.decode(di.host[op][tok], "bf16")
+        if op == "dh":
+            return bf16_bits_to_f32(dh_bits[lo:hi]).astype(np.float64)
+        return oracle.act_p_f32(bf16_bits_to_f32(h_bits[lo:hi]), p[lo:hi]).astype(np.float64)
+
+    checks = _new_checks()
+    for e in (0, cfg.num_local - 2, cfg.num_local - 1):
+        print(f"[mx > 2 GiB] expert {e}", flush=True)
+        lo, hi = int(off[e]), int(off[e + 1])
+        p0, p1 = int(poff[e]), int(poff[e + 1])
+        enc = {op: oracle.mx_quantize_expert_rows(values(op, lo, hi), np.array([0, hi - lo])) for op in KINDS}
+        for op in KINDS:
+            c, s = ops[op]
+            assert np.array_equal(_u8(c[p0 // 64: p1 // 64]), _slice_major(enc[op][0], 64)), (e, op)
+            assert np.array_equal(_u8(s[p0 // 64: p1 // 64]), _slice_major(enc[op][1], 2)), (e, op)
+        _expert_check(checks, e, dw1[e], dw2[e], enc, 0, p1 - p0)
+    _report(checks, "[mx > 2 GiB]")
+
+
 def test_mx_wgrad_full_size_latent_streamed():
     """The 512-expert top-22 layer at its full size, in the launch the bench
     times: every expert's operand bytes and dW1 / dW2 against the oracle,
