@@ -8,7 +8,7 @@ namespace moedet {
 
 constexpr int kMaxExperts = 1024;     // router width handled by the routing kernels
 constexpr int kMaxTopK = 64;          // one lane per selected expert
-constexpr int kRouteChunk = 64;       // tokens per routing/permutation chunk
+constexpr int kRouteChunk = 16;       // tokens per routing/permutation chunk (two per wave of a route workgroup)
 constexpr int kMaxChunkRows = 4096;   // upper bound on the wgrad K chunk (rows)
 constexpr int64_t kManyWgradTiles = 8192;  // weight-gradient tiles above which no expert is split
 

@@ -8,12 +8,13 @@
 // slot index t*k+j, so the row order inside an expert -- the K order of the
 // weight-gradient reduction -- is fixed by the routing alone.
 //
-//  route_kernel    one wave per token (16 waves per chunk of 64 tokens): k
+//  route_kernel    one wave per token (8 waves per chunk of 16 tokens): k
 //                  rounds of a wave-wide argmax, then the softmax; per-chunk
 //                  histogram of local experts in LDS (integer atomics: exact
 //                  in any order).
 //  scan_kernel     per-expert exclusive bases of every chunk and the expert
-//                  offsets (one workgroup, sequential over chunks).
+//                  offsets (one workgroup; each expert's chunks split over
+//                  several threads, their loads issued in batches).
 //  scatter_kernel  one wave per chunk walks its slots in order, 64 at a
 //                  time; a lane's rank among equal experts comes from ballots,
 //                  so the result is the stable order.  Atomic mode claims rows
@@ -40,7 +41,7 @@ DEV bool better(const Cand& a, const Cand& b) {
 
 // PER logits per lane (E <= 64 * PER); kRouteWaves waves per chunk of
 // kRouteChunk tokens, one token per wave at a time.
-constexpr int kRouteWaves = 16;
+constexpr int kRouteWaves = 8;
 template <int PER>
 __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(RouteParams P) {
   __shared__ int s_hist[kMaxExperts];
@@ -160,27 +161,61 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(RouteParams P) {
   __shared__ int s_cnt[kMaxExperts];
   __shared__ int s_off[kMaxExperts];
   __shared__ uint32_t s_key[1024];
+  __shared__ int s_part[1024];
   const int e = threadIdx.x;
-  int total = 0;
-  if (e < P.el) {
-    for (int c = 0; c < P.nchunk; ++c) {
-      int32_t* h = P.hist + (int64_t)c * P.el + e;
-      const int v = *h;
-      *h = total;
-      total += v;
+  // Chunk counts hist[c][g] -> row bases: expert g's chunks are split over
+  // tpe threads (the largest power of two with tpe * el <= 1024), thread
+  // (g, part) taking a contiguous range.  Pass 1 sums each range; the ranges'
+  // exclusive prefix within the expert and the experts' offsets follow; pass
+  // 2 writes offsets[g] + (rows of g in earlier chunks) into hist.  Loads
+  // are issued 16 at a time.  Integer sums: exact in any grouping.
+  int tpe = 1;
+  while (tpe * 2 * P.el <= 1024) tpe *= 2;
+  const int g = e / tpe, part = e % tpe;
+  const bool active = g < P.el;
+  const int per = (P.nchunk + tpe - 1) / tpe;
+  const int c0 = min(P.nchunk, part * per), c1 = min(P.nchunk, c0 + per);
+  constexpr int kBatch = 16;
+  int sum = 0;
+  if (active) {
+    for (int c = c0; c < c1; c += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) v[q] = P.hist[(int64_t)min(c + q, c1 - 1) * P.el + g];  // branch-free
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) sum += c + q < c1 ? v[q] : 0;
     }
+  }
+  s_part[e] = sum;
+  __syncthreads();
+  int total = 0;  // rows of expert e (thread e as an expert from here on)
+  if (e < P.el) {
+    for (int q = 0; q < tpe; ++q) total += s_part[e * tpe + q];
     P.counts[e] = total;
     s_cnt[e] = total;
   }
-  block_exclusive_scan<1024>(s_pre, s_tmp, P.el, [&](int g) { return s_cnt[g]; });
+  block_exclusive_scan<1024>(s_pre, s_tmp, P.el, [&](int x) { return s_cnt[x]; });
   // el may be the block size (1024): thread 0 also writes the total
   if (e < P.el) P.offsets[e] = s_pre[e];
   if (e == 0) P.offsets[P.el] = s_pre[P.el];
   const int off_e = e < P.el ? s_pre[e] : 0;
   if (e < P.el) {
     s_off[e] = off_e;
-    for (int c = 0; c < P.nchunk; ++c) P.hist[(int64_t)c * P.el + e] += off_e;
     if (P.atomic) P.cursor[e] = off_e;
+  }
+  if (active) {
+    int run = s_pre[g];
+    for (int q = 0; q < part; ++q) run += s_part[g * tpe + q];
+    for (int c = c0; c < c1; c += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) v[q] = P.hist[(int64_t)min(c + q, c1 - 1) * P.el + g];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        if (c + q < c1) P.hist[(int64_t)(c + q) * P.el + g] = run;
+        run += v[q];
+      }
+    }
   }
   __syncthreads();
 
