@@ -26,16 +26,22 @@ namespace moedet {
 
 namespace {
 
-struct Cand {
-  float v;
-  int e;  // INT_MAX: none
-};
-
-DEV bool better(const Cand& a, const Cand& b) {
-  if (b.e == 0x7fffffff) return a.e != 0x7fffffff;
-  if (a.e == 0x7fffffff) return false;
-  return a.v > b.v || (a.v == b.v && a.e < b.e);
+// Candidate (logit v, expert e) as one unsigned 64-bit key, larger = better:
+// the high word orders floats (-0.0 taken as +0.0, so the two compare equal),
+// the low word is ~e (a lower expert wins a tie).  0 stands for "none": every
+// finite or infinite logit maps above it.  A single unsigned comparison then
+// decides, without branches.
+DEV uint64_t cand_key(float v, int e) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) == 0u) u = 0u;
+  const uint32_t s = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)s << 32) | (uint32_t)~e;
 }
+DEV float key_value(uint64_t key) {
+  const uint32_t s = (uint32_t)(key >> 32);
+  return __uint_as_float((s & 0x80000000u) ? (s & 0x7fffffffu) : ~s);
+}
+DEV int key_expert(uint64_t key) { return (int)~(uint32_t)key; }
 
 }  // namespace
 
@@ -55,38 +61,37 @@ __global__ __launch_bounds__(kRouteWaves * 64) void route_kernel(RouteParams P) 
     const int64_t t = b * kRouteChunk + tt;
     if (t >= P.T) break;
     const float* row = P.logits + t * E;
-    float v[PER];
-    uint32_t avail = 0;
+    // this lane's candidates; taken ones are set to 0 (none)
+    uint64_t key[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int e = lane + kWave * i;
-      v[i] = 0.f;
-      if (e < E) {
-        v[i] = row[e];
-        avail |= 1u << i;
-      }
+      key[i] = e < E ? cand_key(row[e], e) : 0ull;
     }
     float vmax = 0.f, my_v = 0.f;
     int my_e = -1;
     for (int j = 0; j < k; ++j) {
-      Cand best{0.f, 0x7fffffff};
+      uint64_t best = 0ull;
 #pragma unroll
-      for (int i = 0; i < PER; ++i)
-        if ((avail >> i) & 1u) {
-          Cand c{v[i], lane + kWave * i};
-          if (better(c, best)) best = c;
-        }
+      for (int i = 0; i < PER; ++i) best = key[i] > best ? key[i] : best;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) {
-        Cand o{__shfl_xor(best.v, off, 64), __shfl_xor(best.e, off, 64)};
-        if (better(o, best)) best = o;
+        const uint64_t o = ((uint64_t)(uint32_t)__shfl_xor((int)(best >> 32), off, 64) << 32) |
+                           (uint32_t)__shfl_xor((int)(uint32_t)best, off, 64);
+        best = o > best ? o : best;
       }
-      // best is identical in every lane: (value, index) is a strict total order.
-      if ((best.e & (kWave - 1)) == lane) avail &= ~(1u << (best.e / kWave));
-      if (j == 0) vmax = best.v;
+      // best is identical in every lane (the keys are distinct)
+      const int be = key_expert(best);
+      const float bv = key_value(best);
+      if ((be & (kWave - 1)) == lane) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+          if (i == be / kWave) key[i] = 0ull;
+      }
+      if (j == 0) vmax = bv;
       if (lane == j) {
-        my_v = best.v;
-        my_e = best.e;
+        my_v = bv;
+        my_e = be;
       }
     }
     float ex = lane < k ? expf(my_v - vmax) : 0.f;
