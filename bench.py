@@ -89,6 +89,14 @@ def stage_cost(stage: str, cfg, R: int) -> dict:
         return dict(flops=2.0 * R * D * F, bytes=tok + w + 2 * rowsF)
     if stage.startswith("combine_gather"):
         return dict(flops=0.0, bytes=rowsD + tok + T * k * 8)
+    # routing: chunk histograms of 16 tokens per local expert
+    hist = (T + 15) // 16 * El * 4
+    if stage == "route":                  # logits -> top-k indices and probabilities, chunk histograms
+        return dict(flops=0.0, bytes=T * cfg.num_experts * 4 + T * k * 8 + hist)
+    if stage == "permute_scan":           # histograms read twice, chunk bases written
+        return dict(flops=0.0, bytes=3 * hist)
+    if stage.startswith("permute_scatter"):  # top-k and bases -> slot_row, row_src, row_tok, row_prob
+        return dict(flops=0.0, bytes=T * k * 8 + hist + T * k * 4 + R * 12)
     return dict(flops=0.0, bytes=0.0)
 
 
@@ -316,7 +324,8 @@ def measure(wl: "Workload", args, flush) -> dict:
                 "gemm_launches_atomic_ms": g_atom},
         "stages_ms_det": st_det, "stages_ms_atomic": st_atom, "stage_roofline": stage_roof,
         "dominant": dom,
-        "fwd": {"ms": ms_fwd, "tflops": 4.0 * R * D * F / (ms_fwd * 1e-3) / 1e12, "stages_ms": st_fwd},
+        "fwd": {"ms": ms_fwd, "tflops": 4.0 * R * D * F / (ms_fwd * 1e-3) / 1e12, "stages_ms": st_fwd,
+                "stage_roofline": {n: roofline(n, v, cfg, R) for n, v in st_fwd.items()}},
     }
 
 
