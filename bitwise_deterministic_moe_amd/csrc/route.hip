@@ -123,10 +123,14 @@ DEV int row_tile_list(const RouteParams& P, int4* mt, int BM, const int* s_cnt, 
     for (int i = 0; i < total / BM; ++i) mt[s_pre[e] + i] = int4{e, i * BM, off_e + i * BM, BM};
   s_key[e] = (e < P.el && total % BM) ? ((uint32_t)(BM - total % BM) << 10) | (uint32_t)e : 0xffffffffu;
   __syncthreads();
-  for (int k = 2; k <= 1024; k <<= 1)
+  // bitonic sort of the first N = next_pow2(el) keys (the rest are sentinels
+  // already in place)
+  int N = 1;
+  while (N < P.el) N <<= 1;
+  for (int k = 2; k <= N; k <<= 1)
     for (int j = k >> 1; j > 0; j >>= 1) {
       const int o = e ^ j;
-      if (o > e) {
+      if (e < N && o > e) {
         const uint32_t a = s_key[e], b = s_key[o];
         if ((a > b) == ((e & k) == 0)) {
           s_key[e] = b;
