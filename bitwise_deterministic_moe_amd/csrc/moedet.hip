@@ -736,7 +736,6 @@ MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routin
   W1.kc = pl.kc;
   W1.atomic = at;
   W1.seed = seed;
-  const uint32_t rows_f_bytes = 0;  // routed-row operands: addressed per chunk in the kernel
   const uint32_t tok_d_bytes = (uint32_t)(pl.T * pl.D * pl.esize);
   WgradParams W2 = W1;
   // dW1_g [D][F] = x[row_tok]^T dh
@@ -747,7 +746,7 @@ MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routin
   W1.a_bytes = tok_d_bytes;
   W1.b = dh;
   W1.ldb = pl.F;
-  W1.b_bytes = rows_f_bytes;
+  W1.b_bytes = 0;  // routed rows: addressed from each chunk's first row in the kernel
   W1.dw = dw1;
   W1.slots = slots1;
   W1.tickets = tickets;
@@ -756,7 +755,7 @@ MOE_API moe_status moe_bwd_wgrad(const moe_problem* p, const moe_routing* routin
   W2.N = pl.D;
   W2.a = act_p;
   W2.lda = pl.F;
-  W2.a_bytes = rows_f_bytes;
+  W2.a_bytes = 0;  // routed rows: addressed from each chunk's first row in the kernel
   W2.b = dy;
   W2.ldb = pl.D;
   W2.b_bytes = tok_d_bytes;
