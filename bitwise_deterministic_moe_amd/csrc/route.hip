@@ -8,10 +8,10 @@
 // slot index t*k+j, so the row order inside an expert -- the K order of the
 // weight-gradient reduction -- is fixed by the routing alone.
 //
-//  route_kernel    one wave per token (8 waves per chunk of 16 tokens): k
-//                  rounds of a wave-wide argmax, then the softmax; per-chunk
-//                  histogram of local experts in LDS (integer atomics: exact
-//                  in any order).
+//  route_kernel    one wave per token at a time (8 waves per chunk of 16
+//                  tokens, two tokens each): k rounds of a wave-wide argmax,
+//                  then the softmax; per-chunk histogram of local experts in
+//                  LDS (integer atomics: exact in any order).
 //  scan_kernel     per-expert exclusive bases of every chunk and the expert
 //                  offsets (one workgroup; each expert's chunks split over
 //                  several threads, their loads issued in batches).
