@@ -171,6 +171,7 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(RouteParams P) {
   __shared__ int s_off[kMaxExperts];
   __shared__ uint32_t s_key[1024];
   __shared__ int s_part[1024];
+  __shared__ int s_ppre[1025];
   const int e = threadIdx.x;
   // Chunk counts hist[c][g] -> row bases: expert g's chunks are split over
   // tpe threads (the largest power of two with tpe * el <= 1024), thread
@@ -197,9 +198,12 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(RouteParams P) {
   }
   s_part[e] = sum;
   __syncthreads();
+  // prefix over the (expert, range) sums in that order: an expert's total
+  // and each range's offset inside its expert are differences of it
+  block_exclusive_scan<1024>(s_ppre, s_tmp, 1024, [&](int x) { return s_part[x]; });
   int total = 0;  // rows of expert e (thread e as an expert from here on)
   if (e < P.el) {
-    for (int q = 0; q < tpe; ++q) total += s_part[e * tpe + q];
+    total = s_ppre[(e + 1) * tpe] - s_ppre[e * tpe];
     P.counts[e] = total;
     s_cnt[e] = total;
   }
@@ -213,8 +217,7 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(RouteParams P) {
     if (P.atomic) P.cursor[e] = off_e;
   }
   if (active) {
-    int run = s_pre[g];
-    for (int q = 0; q < part; ++q) run += s_part[g * tpe + q];
+    int run = s_pre[g] + (s_ppre[e] - s_ppre[g * tpe]);
     for (int c = c0; c < c1; c += kBatch) {
       int v[kBatch];
 #pragma unroll
