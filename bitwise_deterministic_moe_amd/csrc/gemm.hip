@@ -884,14 +884,17 @@ DEV void mx_mainloop(uint16_t* lds, const bf::KcOperand& oa, const bf::KcOperand
                       f.sb[g - 4]);
     }
   };
-  // A block mb of fa against the four B blocks of fb
-  auto mma = [&](const MxFrags& fa, const MxFrags& fb, auto MB) __attribute__((always_inline)) {
+  // A block mb of fa against the four B blocks of fb; the tile's first slice
+  // (FIRST) takes a zero accumulator input instead of zeroed registers
+  auto mma = [&](const MxFrags& fa, const MxFrags& fb, auto MB, auto FIRST) __attribute__((always_inline)) {
     constexpr int mb = decltype(MB)::value;
+    constexpr bool first = decltype(FIRST)::value;
     if constexpr (mb >= NA) return;
-    acc[mb][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb.b[0], fa.a[mb], acc[mb][0], 0, 0, 0, fb.sb[0], 0, fa.sa[mb]);
-    acc[mb][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb.b[1], fa.a[mb], acc[mb][1], 0, 0, 0, fb.sb[1], 0, fa.sa[mb]);
-    acc[mb][2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb.b[2], fa.a[mb], acc[mb][2], 0, 0, 0, fb.sb[2], 0, fa.sa[mb]);
-    acc[mb][3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb.b[3], fa.a[mb], acc[mb][3], 0, 0, 0, fb.sb[3], 0, fa.sa[mb]);
+    const f32x16_t zero = {};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[mb][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb.b[j], fa.a[mb], first ? zero : acc[mb][j], 0, 0, 0,
+                                                                   fb.sb[j], 0, fa.sa[mb]);
   };
   // prologue: slices 0..2 in flight; the scale words (loaded before them)
   // stored; slice 0 landed and the stores done in every wave; B blocks read
@@ -916,7 +919,7 @@ DEV void mx_mainloop(uint16_t* lds, const bf::KcOperand& oa, const bf::KcOperand
   // MFMAs; the B blocks of slice s+1 (past the last slice: zero codes and a
   // clamped scale index, never multiplied) are read into the other B set in
   // between, so the sets swap roles each step and nothing is copied.
-  auto step = [&](int s, const MxFrags& bcur, MxFrags& bnext) __attribute__((always_inline)) {
+  auto step = [&](int s, const MxFrags& bcur, MxFrags& bnext, auto first) __attribute__((always_inline)) {
     if constexpr (RS)
       asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     else
@@ -926,32 +929,35 @@ DEV void mx_mainloop(uint16_t* lds, const bf::KcOperand& oa, const bf::KcOperand
     read(f, s, std::integral_constant<int, 1>{});
     issue(s + 3, 1);
     __builtin_amdgcn_sched_barrier(0);
-    mma(f, bcur, std::integral_constant<int, 0>{});
+    mma(f, bcur, std::integral_constant<int, 0>{}, first);
     read(bnext, s + 1, std::integral_constant<int, 4>{});
     read(f, s, std::integral_constant<int, 2>{});
     issue(s + 3, 2);
     issue(s + 3, 3);
     __builtin_amdgcn_sched_barrier(0);
-    mma(f, bcur, std::integral_constant<int, 1>{});
+    mma(f, bcur, std::integral_constant<int, 1>{}, first);
     read(bnext, s + 1, std::integral_constant<int, 5>{});
     read(f, s, std::integral_constant<int, 3>{});
     issue(s + 3, 4);
     issue(s + 3, 5);
     __builtin_amdgcn_sched_barrier(0);
-    mma(f, bcur, std::integral_constant<int, 2>{});
+    mma(f, bcur, std::integral_constant<int, 2>{}, first);
     read(bnext, s + 1, std::integral_constant<int, 6>{});
     read(bnext, s + 1, std::integral_constant<int, 7>{});
     issue(s + 3, 6);
     issue(s + 3, 7);
     if constexpr (RS) issue(s + 3, 8);
     __builtin_amdgcn_sched_barrier(0);
-    mma(f, bcur, std::integral_constant<int, 3>{});
+    mma(f, bcur, std::integral_constant<int, 3>{}, first);
     __builtin_amdgcn_sched_barrier(0);
   };
+  if (nsteps <= 0) return;
+  step(0, f, g, std::true_type{});
+  step(1, g, f, std::false_type{});
 #pragma unroll 1
-  for (int s = 0; s < nsteps; s += 2) {
-    step(s, f, g);
-    step(s + 1, g, f);
+  for (int s = 2; s < nsteps; s += 2) {
+    step(s, f, g, std::false_type{});
+    step(s + 1, g, f, std::false_type{});
   }
 }
 

@@ -44,6 +44,11 @@ constexpr uint32_t kOOB = 0x80000000u;        // offset beyond any num_records: 
 
 enum { KC = 0, MNC = 1 };
 
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 DEV int kc_swz(int r) { return (r >> 2) & 3; }
@@ -151,12 +156,17 @@ DEV void load_frag(Frags& f, const uint16_t* st, int kk, int wm, int wn, int lan
   }
 }
 
-template <int NMB = 4>
+// FIRST: the tile's first k-half, whose MFMAs take a zero accumulator input
+// (the same +0.0 the accumulators would hold), so no zeroing of the 256
+// accumulator registers has to run after slice 0 has landed.
+template <int NMB = 4, bool FIRST = false>
 DEV void mma2(const Frags& f, f32x16_t (&acc)[4][4], int g) {
   const int mb = kGrpM[g], nb = kGrpN[g];
   if (mb >= NMB) return;
-  acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[nb], f.a[mb], acc[mb][nb], 0, 0, 0);
-  acc[mb][nb + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[nb + 1], f.a[mb], acc[mb][nb + 1], 0, 0, 0);
+  const f32x16_t zero = {};
+  acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[nb], f.a[mb], FIRST ? zero : acc[mb][nb], 0, 0, 0);
+  acc[mb][nb + 1] =
+      __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[nb + 1], f.a[mb], FIRST ? zero : acc[mb][nb + 1], 0, 0, 0);
 }
 
 DEV void mma16(const Frags& f, f32x16_t (&acc)[4][4]) {
@@ -262,18 +272,31 @@ DEV void mainloop(const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f
   Frags f0, f1;
 #pragma unroll
   for (int g = 0; g < 8; ++g) load_frag<AL, BL, NMB, WTM>(f0, lds, 0, wm, wn, lane, g);
-#pragma unroll 1
-  for (int s = 0; s < nsteps - 1; ++s) {
+  if (nsteps == 1) {
+#pragma unroll
+    for (int g = 0; g < 8; ++g) load_frag<AL, BL, NMB, WTM>(f1, lds, 1, wm, wn, lane, g);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) mma2<NMB, true>(f0, acc, g);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) mma2<NMB>(f1, acc, g);
+    block_barrier();
+    return;
+  }
+  // phase 1 of step s (the MFMAs of slice s / k-half 0)
+  auto phase1 = [&](int s, auto first) __attribute__((always_inline)) {
     const uint16_t* cur = slot(s);
-    const uint16_t* nxt = slot(s + 1);
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       if (g & 1) issue(s + NS - 2, slot_addr(s + NS - 2), 4 + (g >> 1));
       load_frag<AL, BL, NMB, WTM>(f1, cur, 1, wm, wn, lane, g);
       __builtin_amdgcn_sched_barrier(0);
-      mma2<NMB>(f0, acc, g);
+      mma2<NMB, decltype(first)::value>(f0, acc, g);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  // wait, then phase 2 of step s (the MFMAs of slice s / k-half 1)
+  auto phase2 = [&](int s) __attribute__((always_inline)) {
+    const uint16_t* nxt = slot(s + 1);
     wait_barrier<8 * (NS - 3)>();  // slice s+1 landed; slot of slice s-1 free
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
@@ -283,6 +306,13 @@ DEV void mainloop(const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f
       mma2<NMB>(f1, acc, g);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  phase1(0, BoolC<true>{});
+  phase2(0);
+#pragma unroll 1
+  for (int s = 1; s < nsteps - 1; ++s) {
+    phase1(s, BoolC<false>{});
+    phase2(s);
   }
 #pragma unroll
   for (int g = 0; g < 8; ++g) load_frag<AL, BL, NMB, WTM>(f1, slot(nsteps - 1), 1, wm, wn, lane, g);
