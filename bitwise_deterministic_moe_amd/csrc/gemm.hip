@@ -111,8 +111,9 @@ DEV int row_tile(const RowGemmParams& P, RowTile& t) {
   const int64_t U = (int64_t)P.sched[P.list_hdr] * nN;
   const int64_t L = map_unit_rounds(blockIdx.x, U, P.ncu, P.seed);
   if (L < 0) return kTileNone;
-  const int64_t mt = L / nN;
-  t.nt = (int)(L % nN);
+  // L < 2^31 (one unit per workgroup of the grid): 32-bit division
+  const int64_t mt = (uint32_t)L / (uint32_t)nN;
+  t.nt = (int)((uint32_t)L % (uint32_t)nN);
   const int4 en = ((const int4*)(P.sched + P.list_at))[mt];
   t.g = __builtin_amdgcn_readfirstlane(en.x);
   t.m0 = __builtin_amdgcn_readfirstlane(en.y);
@@ -291,8 +292,8 @@ DEV bool wgrad_tile(const WgradParams& P, WgradTile& t) {
   const int64_t U = (int64_t)unit_start[G] * tiles;
   const int64_t L = map_unit(blockIdx.x, U, P.seed);
   if (L < 0) return false;
-  const int64_t u = L / tiles;
-  const int tile = (int)(L % tiles);
+  const int64_t u = (uint32_t)L / (uint32_t)tiles;  // L < 2^31
+  const int tile = (int)((uint32_t)L % (uint32_t)tiles);
   t.g = find_group(unit_start, G, u);
   t.s = (int)(u - unit_start[t.g]);
   const int cnt = P.counts[t.g];
@@ -535,6 +536,10 @@ DEV void rowgemm_bf16_tile(const RowGemmParams& P, const RowTile& t, uint16_t* l
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
   const int nsteps = P.K / bf::BK;
+  // K is a positive multiple of 256 (checked at the boundary), so the main
+  // loop's first MFMAs always run and the zeros above stay only in blocks of
+  // rows past the tile's end
+  __builtin_assume(nsteps > 0);
   // 32-row A blocks of this wave that hold rows (wave-uniform)
   const int nmb = max(0, min(WTM / 32, (t.mvalid - wm * WTM + 31) / 32));
   if constexpr (BL == bf::KC) {
@@ -674,20 +679,22 @@ DEV void wgrad_bf16_tile(const WgradParams& P, const WgradTile& t, float* dst, u
       ob.issue1(st + bf::OPER * 2, wave, ok ? (B_GATHER ? gat[j] : d) : bf::kOOB, j);
     if (i == 2 * bf::LOADS - 1) fetch(s + 1);
   }, acc, wm, wn, lane);
-  const bool atomic_add = P.atomic && t.S > 1;
   NoPre none;
   const __amdgpu_buffer_rsrc_t rd = buf(dst);
   NoPre::Data nd[2];
-  staged_epilogue((float*)lds, acc, wm, wn, lane, tid, bf::BM, none, nd, false, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
-    const uint32_t o = ((uint32_t)(t.m0 + m) * (uint32_t)P.N + t.n0 + col) * 4u;
-    if (atomic_add) {
-      float* po = dst + o / 4u;
+  auto offset = [&](int m, int col) { return ((uint32_t)(t.m0 + m) * (uint32_t)P.N + t.n0 + col) * 4u; };
+  // two instantiations, so that the store loop carries no per-store branch
+  if (P.atomic && t.S > 1) {
+    staged_epilogue((float*)lds, acc, wm, wn, lane, tid, bf::BM, none, nd, false, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
+      float* po = dst + offset(m, col) / 4u;
 #pragma unroll
       for (int q = 0; q < 4; ++q) atomicAdd(po + q, v[q]);
-    } else {
-      __builtin_amdgcn_raw_buffer_store_b128(f32x4_t{v[0], v[1], v[2], v[3]}, rd, o, 0, kEpiNT);
-    }
-  });
+    });
+  } else {
+    staged_epilogue((float*)lds, acc, wm, wn, lane, tid, bf::BM, none, nd, false, [&](int m, int col, float (&v)[4], NoPre::Data&, int) {
+      __builtin_amdgcn_raw_buffer_store_b128(f32x4_t{v[0], v[1], v[2], v[3]}, rd, offset(m, col), 0, kEpiNT);
+    });
+  }
 }
 
 // Ordered split-K reduction of one dW tile, run by the chunk that finishes
@@ -736,8 +743,8 @@ DEV void wgrad_ordered_tail(const WgradParams& P, const WgradTile& t, int S, int
 template <bool A_GATHER, bool B_GATHER>
 DEV void wgrad_pair_unit(const WgradParams& P, int64_t L, int tiles, uint16_t* lds, uint32_t* s_rowoff) {
   const int nN = P.N / bf::BN;
-  const int64_t u = L / tiles;
-  const int tile = (int)(L % tiles);
+  const int64_t u = (uint32_t)L / (uint32_t)tiles;  // L < 2^31 (one unit per workgroup)
+  const int tile = (int)((uint32_t)L % (uint32_t)tiles);
   const int4 en = ((const int4*)(P.units + P.units_at))[u];
   WgradTile t;
   t.g = __builtin_amdgcn_readfirstlane(en.x & 0x3fffffff);
@@ -1018,6 +1025,7 @@ __global__ __launch_bounds__(256) void mx_rowgemm_kernel(RowGemmParams P) {
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
   // the number of slices is even (K is a multiple of 128)
   const int nsteps = P.K / 64;
+  __builtin_assume(nsteps > 0);  // K is a positive multiple of 128 (checked at the boundary)
   const MxRingScales none{};
   mx_mainloop<NA, WTM, false>(lds, oa, ob, 64u, 64u, none, 0, nsteps, nsteps, s_sa, s_sb, nkb, [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -1079,7 +1087,8 @@ __global__ __launch_bounds__(256) void mx_wgrad_kernel(MxWgradParams P) {
   const int tiles = (P.D / 256) * (P.F / 256);
   const int64_t L = map_unit(blockIdx.x, (int64_t)P.groups * 2 * tiles, P.seed);
   if (L < 0) return;
-  const int g = (int)(L / (2 * tiles)), mat = (int)(L / tiles) & 1, tile = (int)(L % tiles);
+  const uint32_t Lu = (uint32_t)L;  // L < 2^31 (one unit per workgroup)
+  const int g = (int)(Lu / (2u * tiles)), mat = (int)(Lu / (uint32_t)tiles) & 1, tile = (int)(Lu % (uint32_t)tiles);
   // selections on copies: a conditional over two members of the kernel
   // argument is an lvalue and would move the argument to scratch
   const int M = pick(mat, P.F, P.D), N = pick(mat, P.D, P.F);
