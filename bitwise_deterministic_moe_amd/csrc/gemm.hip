@@ -618,6 +618,12 @@ __global__ __launch_bounds__(256) void rowgemm_bf16_kernel(RowGemmParams P) {
   }
 }
 
+// Entries of the gathered-row table past a chunk of klen rows: the main loop
+// reads rows up to (ceil(klen / 32) + NS - 2) * 32 - 1 < klen + 128 (the last
+// slice and those prefetched past it, NS = 4 slots).
+constexpr int kRowoffPad = 160;
+static_assert(bf::NSTAGE == 4, "row table padding sized for a 4-slot ring");
+
 // One weight-gradient tile: dW[m0:m0+256, n0:n0+256] of expert t.g over the
 // rows of chunk t.s, into dst (dW itself, or a split-K partial slot).
 template <bool A_GATHER, bool B_GATHER>
@@ -628,7 +634,10 @@ DEV void wgrad_bf16_tile(const WgradParams& P, const WgradTile& t, float* dst, u
   static_assert(A_GATHER != B_GATHER, "exactly one operand is gathered by token");
   const uint32_t ld_gather = (uint32_t)(A_GATHER ? P.lda : P.ldb) * 2u;
   const uint32_t ld_direct = (uint32_t)(A_GATHER ? P.ldb : P.lda) * 2u;
-  for (int i = tid; i < t.klen; i += 256) s_rowoff[i] = (uint32_t)P.row_tok[t.row0 + i] * ld_gather;
+  // entries past the chunk (read by the loads of its last slice and of the
+  // slices prefetched past it) hold kOOB, so those rows read zeros
+  for (int i = tid; i < t.klen + kRowoffPad; i += 256)
+    s_rowoff[i] = i < t.klen ? (uint32_t)P.row_tok[t.row0 + i] * ld_gather : bf::kOOB;
   __syncthreads();
 
   f32x16_t acc[4][4];
@@ -648,10 +657,11 @@ DEV void wgrad_bf16_tile(const WgradParams& P, const WgradTile& t, float* dst, u
   ob.init(A_GATHER ? dbase : P.b, A_GATHER ? dbytes : P.b_bytes, wave, lane, t.n0);
   const int nsteps = (t.klen + bf::BK - 1) / bf::BK;
   // Per load j of a slice, this lane's k row is krow(j) + 32 s.  The direct
-  // operand's row offset advances by a scalar per slice; the gathered
-  // operand's offsets of slice s+1 are read from LDS right after slice s is
-  // issued, so an issue never waits on that read.  (Rows past the chunk read
-  // an in-range entry and are masked at issue.)
+  // operand's row offset advances by a scalar per slice, and its rows past
+  // the chunk lie past the buffer's num_records (the chunk's own rows), so
+  // they read zeros; the gathered operand's offsets of slice s+1 are read
+  // from LDS right after slice s is issued, so an issue never waits on that
+  // read.
   uint32_t dir[bf::LOADS], gat[bf::LOADS];
   int kr[bf::LOADS];
 #pragma unroll
@@ -659,24 +669,19 @@ DEV void wgrad_bf16_tile(const WgradParams& P, const WgradTile& t, float* dst, u
     kr[j] = bf::MncOperand::krow(wave, lane, j);
     dir[j] = (uint32_t)kr[j] * ld_direct;
   }
-  const int last = t.klen > 0 ? t.klen - 1 : 0;
   auto fetch = [&](int s) {
 #pragma unroll
-    for (int j = 0; j < bf::LOADS; ++j) {
-      const int kk = s * bf::BK + kr[j];
-      gat[j] = s_rowoff[kk < t.klen ? kk : last];
-    }
+    for (int j = 0; j < bf::LOADS; ++j) gat[j] = s_rowoff[s * bf::BK + kr[j]];
   };
   fetch(0);
   const uint32_t dir_step = (uint32_t)bf::BK * ld_direct;
   bf::mainloop<bf::MNC, bf::MNC>(lds, ring, nsteps, [&](int s, uint32_t st, int i) {
     const int j = i & (bf::LOADS - 1);
-    const bool ok = kr[j] < t.klen - s * bf::BK;
     const uint32_t d = dir[j] + (uint32_t)s * dir_step;
     if (i < bf::LOADS)
-      oa.issue1(st, wave, ok ? (A_GATHER ? gat[j] : d) : bf::kOOB, j);
+      oa.issue1(st, wave, A_GATHER ? gat[j] : d, j);
     else
-      ob.issue1(st + bf::OPER * 2, wave, ok ? (B_GATHER ? gat[j] : d) : bf::kOOB, j);
+      ob.issue1(st + bf::OPER * 2, wave, B_GATHER ? gat[j] : d, j);
     if (i == 2 * bf::LOADS - 1) fetch(s + 1);
   }, acc, wm, wn, lane);
   NoPre none;
@@ -770,7 +775,7 @@ DEV void wgrad_pair_unit(const WgradParams& P, int64_t L, int tiles, uint16_t* l
 // list.
 __global__ __launch_bounds__(256) void wgrad_pair_bf16_kernel(WgradParams P1, WgradParams P2, int ncu) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[bf::LDS_BYTES / 2];
-  __shared__ uint32_t s_rowoff[kMaxChunkRows];  // byte offset of each gathered row of the chunk
+  __shared__ uint32_t s_rowoff[kMaxChunkRows + kRowoffPad];  // byte offset of each gathered row of the chunk
   const int tiles1 = (P1.M / bf::BM) * (P1.N / bf::BN), tiles2 = (P2.M / bf::BM) * (P2.N / bf::BN);
   const int64_t units = P1.units[1];
   const int64_t U1 = units * tiles1, U2 = units * tiles2;

@@ -228,9 +228,10 @@ struct MncOperand {
   // krowoff(k) -> byte offset of k row (k relative to the stage start) or kOOB
   // k row handled by this lane in load i
   DEV static int krow(int wave, int lane, int i) { return 2 * (wave * LOADS + i) + (lane >> 5); }
-  // Load i; ro: byte offset of k row krow(i) of the slice, or kOOB.
+  // Load i; ro: byte offset of k row krow(i) of the slice, or kOOB (then
+  // ro + mnoff[i] stays at or past 2^31, beyond any num_records here).
   DEV void issue1(uint32_t lds, int wave, uint32_t ro, int i) const {
-    dma16(rs, lds + (wave * LOADS + i) * 1024, ro == kOOB ? kOOB : ro + mnoff[i], 0u);
+    dma16(rs, lds + (wave * LOADS + i) * 1024, ro + mnoff[i], 0u);
   }
 };
 
