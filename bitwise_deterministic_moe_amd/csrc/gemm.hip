@@ -675,7 +675,7 @@ DEV void wgrad_bf16_tile(const WgradParams& P, const WgradTile& t, float* dst, u
   };
   fetch(0);
   const uint32_t dir_step = (uint32_t)bf::BK * ld_direct;
-  bf::mainloop<bf::MNC, bf::MNC>(lds, ring, nsteps, [&](int s, uint32_t st, int i) {
+  bf::mainloop<bf::MNC, bf::MNC, 4, bf::NSTAGE, 128, true>(lds, ring, nsteps, [&](int s, uint32_t st, int i) {
     const int j = i & (bf::LOADS - 1);
     const uint32_t d = dir[j] + (uint32_t)s * dir_step;
     if (i < bf::LOADS)

@@ -133,6 +133,45 @@ struct Frags {
   bf16x8_t a[4], b[4];
 };
 
+// Fragment read addresses of an MNC x MNC tile for the unrolled main loop:
+// per lane, the LDS byte addresses of the 16 transpose reads of k-half 0 in
+// slot 0 (blocks A0..A3 then B0..B3, each a read of rows k and k+4), and the
+// same addresses + 64 KiB.  A read of slot sl, k-half kh is then one of
+// them plus (sl % 2) * 32 KiB + kh * 8 KiB, an offset that fits the
+// instruction's 16-bit field, so no address arithmetic runs per read (rows
+// k + 16 share the swizzle of rows k).  The second set goes through an asm
+// add so that the compiler keeps it as registers instead of rebuilding
+// addresses past the offset field.
+struct MncAddr {
+  uint32_t s0[16], s1[16];
+};
+
+template <int WTM>
+DEV void mnc_addr_init(MncAddr& m, uint32_t ring, int wm, int wn, int lane) {
+  const int g4 = lane >> 4, i = lane & 15;
+  const int k = 8 * (g4 >> 1) + (i >> 2);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int col = (b >= 4 ? wn * 128 : wm * WTM) + (b & 3) * 32 + 16 * (g4 & 1) + 4 * (i & 3);
+    const uint32_t base = ring + (b >= 4 ? (uint32_t)OPER * 2u : 0u);
+    m.s0[2 * b] = base + 2u * (uint32_t)mnc_off(k, col);
+    m.s0[2 * b + 1] = base + 2u * (uint32_t)mnc_off(k + 4, col);
+  }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) asm("v_add_u32 %0, 0x10000, %1" : "=v"(m.s1[j]) : "v"(m.s0[j]));
+}
+
+DEV bf16x8_t frag_mnc_at(const MncAddr& m, int b, int sl, int kh) {
+  const uint32_t* set = sl >= 2 ? m.s1 : m.s0;
+  const uint32_t off = (uint32_t)(sl & 1) * 32768u + (uint32_t)kh * 8192u;
+  const LDS_AS char* plo = (const LDS_AS char*)(uintptr_t)set[2 * b];
+  const LDS_AS char* phi = (const LDS_AS char*)(uintptr_t)set[2 * b + 1];
+  v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(plo + off));
+  v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(phi + off));
+  u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{l2[0], l2[1], h2[0], h2[1]});
+}
+
 // Fragment reads and MFMAs of a k-half in 8 groups.  Group g reads block
 // A0 B0 B1 A1 B2 B3 A2 A3 [g] and issues MFMA pair g:
 //   (A0;B0,B1) (A1;B0,B1) (A0;B2,B3) (A1;B2,B3) (A2;B0,B1) (A2;B2,B3) (A3;B0,B1) (A3;B2,B3)
@@ -167,6 +206,15 @@ DEV void mma2(const Frags& f, f32x16_t (&acc)[4][4], int g) {
   acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[nb], f.a[mb], FIRST ? zero : acc[mb][nb], 0, 0, 0);
   acc[mb][nb + 1] =
       __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[nb + 1], f.a[mb], FIRST ? zero : acc[mb][nb + 1], 0, 0, 0);
+}
+
+template <int NMB>
+DEV void load_frag_at(Frags& f, const MncAddr& m, int sl, int kh, int g) {
+  if (kGrpA[g] >= 0) {
+    if (kGrpA[g] < NMB) f.a[kGrpA[g]] = frag_mnc_at(m, kGrpA[g], sl, kh);
+  } else {
+    f.b[kGrpB[g]] = frag_mnc_at(m, 4 + kGrpB[g], sl, kh);
+  }
 }
 
 DEV void mma16(const Frags& f, f32x16_t (&acc)[4][4]) {
@@ -256,7 +304,12 @@ struct MncOperand {
 //    is then done with slice s-1, whose slot takes slice s+NS-1);
 //  phase 2: fragments of slice s+1 / k-half 0 are read and loads 0..3 of
 //    slice s+NS-1 issued, while the MFMAs of k-half 1 run.
-template <int AL, int BL, int NMB = 4, int NS = NSTAGE, int WTM = 128, class Issue>
+// UNR: the steady-state loop is unrolled NS times, so that every slot
+// index, and with it every LDS address offset, is a compile-time constant
+// (the fragment reads then take the slot in their immediate offset instead of
+// an add per read); the up to NS - 1 steps left after the unrolled rounds
+// start at slot 1 as well.
+template <int AL, int BL, int NMB = 4, int NS = NSTAGE, int WTM = 128, bool UNR = false, class Issue>
 DEV void mainloop(const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f32x16_t (&acc)[4][4], int wm,
                   int wn, int lane) {
   static_assert(NS == 4 || NS == 5, "ring slots");
@@ -283,37 +336,68 @@ DEV void mainloop(const uint16_t* lds, uint32_t ring, int nsteps, Issue issue, f
     block_barrier();
     return;
   }
-  // phase 1 of step s (the MFMAs of slice s / k-half 0)
-  auto phase1 = [&](int s, auto first) __attribute__((always_inline)) {
-    const uint16_t* cur = slot(s);
+  static_assert(!UNR || (AL == MNC && BL == MNC && NS == 4), "unrolled loop: MNC x MNC tiles, 4 slots");
+  MncAddr ma;
+  if constexpr (UNR) mnc_addr_init<WTM>(ma, ring, wm, wn, lane);
+  // phase 1 of step s, whose slice sits in slot sl = s % NS (the MFMAs of
+  // slice s / k-half 0)
+  auto phase1 = [&](int s, auto first, int sl) __attribute__((always_inline)) {
+    const uint16_t* cur = lds + sl * STAGE;
+    const int si = sl >= 2 ? sl - 2 : sl + NS - 2;  // slot of slice s + NS - 2
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
-      if (g & 1) issue(s + NS - 2, slot_addr(s + NS - 2), 4 + (g >> 1));
-      load_frag<AL, BL, NMB, WTM>(f1, cur, 1, wm, wn, lane, g);
+      if (g & 1) issue(s + NS - 2, ring + (uint32_t)si * (STAGE * 2), 4 + (g >> 1));
+      if constexpr (UNR)
+        load_frag_at<NMB>(f1, ma, sl, 1, g);
+      else
+        load_frag<AL, BL, NMB, WTM>(f1, cur, 1, wm, wn, lane, g);
       __builtin_amdgcn_sched_barrier(0);
       mma2<NMB, decltype(first)::value>(f0, acc, g);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
   // wait, then phase 2 of step s (the MFMAs of slice s / k-half 1)
-  auto phase2 = [&](int s) __attribute__((always_inline)) {
-    const uint16_t* nxt = slot(s + 1);
+  auto phase2 = [&](int s, int sl) __attribute__((always_inline)) {
+    const uint16_t* nxt = lds + (sl + 1 == NS ? 0 : sl + 1) * STAGE;
+    const int si = sl >= 1 ? sl - 1 : NS - 1;  // slot of slice s + NS - 1
     wait_barrier<8 * (NS - 3)>();  // slice s+1 landed; slot of slice s-1 free
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
-      if (g & 1) issue(s + NS - 1, slot_addr(s + NS - 1), g >> 1);
-      load_frag<AL, BL, NMB, WTM>(f0, nxt, 0, wm, wn, lane, g);
+      if (g & 1) issue(s + NS - 1, ring + (uint32_t)si * (STAGE * 2), g >> 1);
+      if constexpr (UNR)
+        load_frag_at<NMB>(f0, ma, sl + 1 == NS ? 0 : sl + 1, 0, g);
+      else
+        load_frag<AL, BL, NMB, WTM>(f0, nxt, 0, wm, wn, lane, g);
       __builtin_amdgcn_sched_barrier(0);
       mma2<NMB>(f1, acc, g);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  phase1(0, BoolC<true>{});
-  phase2(0);
+  phase1(0, BoolC<true>{}, 0);
+  phase2(0, 0);
+  if constexpr (UNR) {
+    int s = 1;
 #pragma unroll 1
-  for (int s = 1; s < nsteps - 1; ++s) {
-    phase1(s, BoolC<false>{});
-    phase2(s);
+    for (; s + NS <= nsteps - 1; s += NS) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        phase1(s + j, BoolC<false>{}, (1 + j) % NS);
+        phase2(s + j, (1 + j) % NS);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) {
+      if (s + j < nsteps - 1) {
+        phase1(s + j, BoolC<false>{}, (1 + j) % NS);
+        phase2(s + j, (1 + j) % NS);
+      }
+    }
+  } else {
+#pragma unroll 1
+    for (int s = 1; s < nsteps - 1; ++s) {
+      phase1(s, BoolC<false>{}, s % NS);
+      phase2(s, s % NS);
+    }
   }
 #pragma unroll
   for (int g = 0; g < 8; ++g) load_frag<AL, BL, NMB, WTM>(f1, slot(nsteps - 1), 1, wm, wn, lane, g);
