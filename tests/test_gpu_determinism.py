@@ -36,7 +36,7 @@ def test_det_bits_identical_20_repeats_and_4_shuffles(name):
 
 
 @pytest.mark.parametrize("name", ["split_k_bf16", "split_k_fp32", "shard_bf16", "empty_experts_bf16",
-                                  "max_experts_bf16"])
+                                  "max_experts_bf16", "max_chunk_split_bf16"])
 def test_det_bits_identical_across_repeats_and_shuffles(name):
     cfg = CONFIGS.get(name) or EDGE[name]
     determinism_runs(LayerRunner(moe.Problem.from_config(cfg), device_inputs(cfg)), cfg.combine, repeats=4,

@@ -36,6 +36,11 @@ EDGE = {
     "split_k_fp32": Config("split_k_fp32", 2048, 64, 128, 16, 1, 0, 16, "f32", 1, 23, skew="zipf",
                            zipf_beta=2.0, zipf_empty=2),
     "shard_fp32": Config("shard_fp32", 90, 128, 64, 8, 3, 2, 4, "f32", 0, 21),
+    # one expert holding the largest weight-gradient chunk (4096 rows) whole,
+    # and one holding two such chunks (8192 rows: split, ordered reduction):
+    # the gathered-row table is filled to its last padded entry
+    "max_chunk_bf16": Config("max_chunk_bf16", 4096, 256, 256, 1, 1, 0, 1, "bf16", 1, 25),
+    "max_chunk_split_bf16": Config("max_chunk_split_bf16", 8192, 256, 256, 1, 1, 0, 1, "bf16", 1, 26),
 }
 
 
