@@ -868,14 +868,18 @@ DEV void mx_mainloop(uint16_t* lds, const bf::KcOperand& oa, const bf::KcOperand
   const uint32_t sring = bf::lds_base(s_sa);
   constexpr int NL = RS ? 9 : 8;   // loads per slice and thread
   // slice s: 64 codes = 64 bytes per row, the size of a bf16 slice of 32
+  // With RS the operands are slice-major and their buffers end after slice
+  // nlive - 1, so a slice past it lies past num_records and reads zeros with
+  // no per-load select; K-contiguous rows would run into the next row.
   auto issue = [&](int s, int i) __attribute__((always_inline)) {
     const uint32_t st = ring + (uint32_t)(s & 3) * (bf::STAGE * 2);
+    const bool live = RS || s < nlive;
     if (i < bf::LOADS)
-      oa.issue1_bytes(st, wave, (uint32_t)(kslice0 + s) * a_sstride, s < nlive, i);
+      oa.issue1_bytes(st, wave, (uint32_t)(kslice0 + s) * a_sstride, live, i);
     else if (i < 2 * bf::LOADS)
-      ob.issue1_bytes(st + bf::OPER * 2, wave, (uint32_t)(kslice0 + s) * b_sstride, s < nlive, i - bf::LOADS);
+      ob.issue1_bytes(st + bf::OPER * 2, wave, (uint32_t)(kslice0 + s) * b_sstride, live, i - bf::LOADS);
     else
-      rsc.issue(sring + (uint32_t)(s & 3) * kMxScaleSlot, wave, kslice0 + s, s < nlive);
+      rsc.issue(sring + (uint32_t)(s & 3) * kMxScaleSlot, wave, kslice0 + s, live);
   };
   const int h = lane >> 5, r32 = lane & 31;
   auto slot = [&](int s) { return (const uint8_t*)(lds + (s & 3) * bf::STAGE); };
