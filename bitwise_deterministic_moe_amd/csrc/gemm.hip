@@ -634,10 +634,26 @@ DEV void wgrad_bf16_tile(const WgradParams& P, const WgradTile& t, float* dst, u
   static_assert(A_GATHER != B_GATHER, "exactly one operand is gathered by token");
   const uint32_t ld_gather = (uint32_t)(A_GATHER ? P.lda : P.ldb) * 2u;
   const uint32_t ld_direct = (uint32_t)(A_GATHER ? P.ldb : P.lda) * 2u;
-  // entries past the chunk (read by the loads of its last slice and of the
-  // slices prefetched past it) hold kOOB, so those rows read zeros
-  for (int i = tid; i < t.klen + kRowoffPad; i += 256)
-    s_rowoff[i] = i < t.klen ? (uint32_t)P.row_tok[t.row0 + i] * ld_gather : bf::kOOB;
+  // Entries past the chunk (read by the loads of its last slice and of the
+  // slices prefetched past it) hold kOOB, so those rows read zeros.  Eight
+  // entries per thread are loaded before any is stored, so a long chunk
+  // waits on one load latency per 2048 rows instead of one per 256.
+  // (The loads read a clamped index unconditionally, so that they are not
+  // split into branches that each wait for their load.)
+  const int nrow = t.klen + kRowoffPad, last = t.klen - 1;
+  for (int i0 = 0; i0 < nrow; i0 += 8 * 256) {
+    int v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 256 + tid;
+      if (i0 + u * 256 < t.klen) v[u] = P.row_tok[t.row0 + (i < t.klen ? i : last)];  // uniform test
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * 256 + tid;
+      if (i < nrow) s_rowoff[i] = i < t.klen ? (uint32_t)v[u] * ld_gather : bf::kOOB;
+    }
+  }
   __syncthreads();
 
   f32x16_t acc[4][4];
