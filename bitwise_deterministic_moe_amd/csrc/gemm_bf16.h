@@ -276,8 +276,10 @@ struct MncOperand {
   // krowoff(k) -> byte offset of k row (k relative to the stage start) or kOOB
   // k row handled by this lane in load i
   DEV static int krow(int wave, int lane, int i) { return 2 * (wave * LOADS + i) + (lane >> 5); }
-  // Load i; ro: byte offset of k row krow(i) of the slice, or kOOB (then
-  // ro + mnoff[i] stays at or past 2^31, beyond any num_records here).
+  // Load i; ro: byte offset of k row krow(i) of the slice, or kOOB.  Then
+  // ro + mnoff[i] is at or past 2^31: past num_records of any buffer under
+  // 2 GiB, which reads zeros; in a larger weight buffer it reads in-range
+  // data into a slot that is never read (slices past the last one).
   DEV void issue1(uint32_t lds, int wave, uint32_t ro, int i) const {
     dma16(rs, lds + (wave * LOADS + i) * 1024, ro + mnoff[i], 0u);
   }
